@@ -1,0 +1,149 @@
+"""fp64 CPU oracle for the RDA gated delta rule -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the bench's ``cpu_baseline``
+leg may import this package.  The product path (the HIP library and its
+Python binding) never imports, links or executes anything here, and this
+package imports nothing from the product path.
+
+The arithmetic lives in ``oracle.c`` (plain C, double precision): the gated
+delta rule as the page "Raon-1 nano" (ai.satyajit.si), section "The other
+1.5B: a hybrid built to forget", describes its recurrent step -- decay the
+state, form the error between the value and the decayed state's prediction
+for the key, write it back with strength beta -- and read-out o_t = S_t q_t
+after the update.  This module only marshals NumPy arrays into that library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_default = None
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
+    """Compile an oracle C source into a shared library with gcc (OpenMP)."""
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared",
+               "-Wall", "-Wextra", "-o", tmp, src]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out)
+    return out
+
+
+class Oracle:
+    """ctypes handle on one build of the oracle library."""
+
+    def __init__(self, lib_path: str = _LIB):
+        if lib_path == _LIB and not os.path.exists(lib_path):
+            build(force=False)
+        lib = ctypes.CDLL(lib_path)
+        p = ctypes.c_void_p
+        i32 = ctypes.c_int32
+        lib.oracle_rda_prefill.argtypes = [p, p, p, p, p, p, i32, ctypes.c_int64,
+                                           i32, i32, i32, p, p, p, i32]
+        lib.oracle_rda_prefill.restype = ctypes.c_int
+        lib.oracle_rda_decode_step.argtypes = [p, p, p, p, p, i32, i32, i32, i32,
+                                               p, p, i32]
+        lib.oracle_rda_decode_step.restype = ctypes.c_int
+        lib.oracle_threads.argtypes = [i32]
+        lib.oracle_threads.restype = ctypes.c_int
+        self.lib = lib
+
+    def threads_used(self, threads: int = 0) -> int:
+        return int(self.lib.oracle_threads(int(threads)))
+
+    def prefill(self, q, k, v, a, b, cu_seqlens=None, S0=None, threads: int = 0):
+        return _prefill(self.lib, q, k, v, a, b, cu_seqlens, S0, threads)
+
+    def decode_step(self, q, k, v, a, b, S, threads: int = 0):
+        return _decode_step(self.lib, q, k, v, a, b, S, threads)
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def _f32(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+
+
+def _f64(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(x):
+    return None if x is None else x.ctypes.data_as(ctypes.c_void_p)
+
+
+def threads_used(threads: int = 0) -> int:
+    return default().threads_used(threads)
+
+
+def prefill(q, k, v, a, b, cu_seqlens=None, S0=None, threads: int = 0):
+    """Sequential fp64 prefill with the default oracle build (see _prefill)."""
+    return default().prefill(q, k, v, a, b, cu_seqlens, S0, threads)
+
+
+def decode_step(q, k, v, a, b, S, threads: int = 0):
+    """One in-place fp64 decode step with the default build (see _decode_step)."""
+    return default().decode_step(q, k, v, a, b, S, threads)
+
+
+def _prefill(lib, q, k, v, a, b, cu_seqlens=None, S0=None, threads: int = 0):
+    """Sequential fp64 prefill.
+
+    q, k: [T, H, dk]; v: [T, H, dv]; a, b: [T, H] -- any float dtype that is
+    exactly representable in fp32 (fp32 or bf16 values widened to fp32).
+    cu_seqlens: int32 [N+1] or None (one sequence); S0: [N, H, dv, dk] or None.
+    Returns (o [T, H, dv] float64, S_final [N, H, dv, dk] float64).
+    """
+    q, k, v, a, b = (_f32(x) for x in (q, k, v, a, b))
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    assert k.shape == (T, H, dk) and v.shape[:2] == (T, H)
+    assert a.shape == (T, H) and b.shape == (T, H)
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        N = cu.shape[0] - 1
+    else:
+        cu, N = None, 1
+    if S0 is not None:
+        S0 = _f64(S0)
+        assert S0.shape == (N, H, dv, dk)
+    o = np.zeros((T, H, dv), dtype=np.float64)
+    S_final = np.zeros((N, H, dv, dk), dtype=np.float64)
+    rc = lib.oracle_rda_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                                _ptr(cu), N, T, H, dk, dv, _ptr(S0), _ptr(o),
+                                _ptr(S_final), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_rda_prefill failed with code {rc}")
+    return o, S_final
+
+
+def _decode_step(lib, q, k, v, a, b, S, threads: int = 0):
+    """One in-place fp64 decode step on S [B, H, dv, dk] (float64, modified).
+
+    Returns o [B, H, dv] float64.
+    """
+    q, k, v, a, b = (_f32(x) for x in (q, k, v, a, b))
+    B, H, dk = q.shape
+    dv = v.shape[2]
+    assert isinstance(S, np.ndarray) and S.dtype == np.float64 and S.flags.c_contiguous
+    assert S.shape == (B, H, dv, dk)
+    o = np.zeros((B, H, dv), dtype=np.float64)
+    rc = lib.oracle_rda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                                    B, H, dk, dv, _ptr(S), _ptr(o), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_rda_decode_step failed with code {rc}")
+    return o

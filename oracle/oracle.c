@@ -1,0 +1,199 @@
+/*
+ * oracle.c -- plain fp64 CPU reference for the RDA gated delta rule.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file; only the tests, the smoke check and the bench's CPU
+ * baseline leg use it.  It shares no code, header or table with the HIP
+ * library.
+ *
+ * What it computes.  RDA ("Raon Delta Attention") is described on the page
+ * "Raon-1 nano" (ai.satyajit.si), section "The other 1.5B: a hybrid built to
+ * forget", as a gated delta-rule linear attention whose recurrent step first
+ * decays the matrix state, then forms the error between the value and what
+ * the decayed state predicts for the key, and writes that error back with
+ * strength beta.  The same page, section "The cache is small if the runtime
+ * keeps it small", fixes the state as one 128 x 128 fp32 matrix per head.
+ * With a scalar decay a_t in (0,1] and write strength b_t in [0,1] per token
+ * and head, that step is the gated delta rule
+ *
+ *     S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T ,   o_t = S_t q_t
+ *
+ * written here in the page's order of operations:
+ *
+ *     S'  = a_t S_{t-1}            (decay)
+ *     e   = v_t - S' k_t           (error against the decayed state)
+ *     S_t = S' + b_t e k_t^T       (write with strength b_t)
+ *     o_t = S_t q_t                (read-out after the update)
+ *
+ * which equals the product form exactly in real arithmetic.  The state is
+ * stored row-major as S[i][j] with i the value channel (0..dv-1) and j the
+ * key channel (0..dk-1).  Tokens are laid out [T, H, d]; gates [T, H].
+ * No query scale and no normalisation happen here: q and k are used exactly
+ * as given.  Tokens are processed strictly in order, one at a time; the only
+ * parallelism is across independent (sequence, head) pairs.
+ *
+ * Every input is widened exactly to double before use; all arithmetic is
+ * double.
+ */
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG 1
+#define ORACLE_ERR_NOMEM 2
+
+int oracle_version(void) { return 1; }
+
+/* One token of the recurrence on one head's state S[dv][dk] (see header). */
+static void oracle_token(double* S, double* e, int dk, int dv,
+                         const float* q, const float* k, const float* v,
+                         double a, double b, double* o) {
+    /* decay */
+    for (int i = 0; i < dv; ++i)
+        for (int j = 0; j < dk; ++j)
+            S[(size_t)i * dk + j] *= a;
+    /* error against the decayed state: e = v - S k */
+    for (int i = 0; i < dv; ++i) {
+        double pred = 0.0;
+        for (int j = 0; j < dk; ++j)
+            pred += S[(size_t)i * dk + j] * (double)k[j];
+        e[i] = (double)v[i] - pred;
+    }
+    /* write with strength b: S += b e k^T */
+    for (int i = 0; i < dv; ++i)
+        for (int j = 0; j < dk; ++j)
+            S[(size_t)i * dk + j] += b * e[i] * (double)k[j];
+    /* read-out with the updated state: o = S q */
+    if (o) {
+        for (int i = 0; i < dv; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < dk; ++j)
+                acc += S[(size_t)i * dk + j] * (double)q[j];
+            o[i] = acc;
+        }
+    }
+}
+
+/*
+ * Prefill over packed variable-length sequences.
+ *   q, k   : [total_tokens, H, dk] fp32 (bf16 inputs arrive widened exactly)
+ *   v      : [total_tokens, H, dv] fp32
+ *   a, b   : [total_tokens, H] fp32
+ *   cu     : [num_seqs + 1] int32 token offsets, cu[0] = 0, non-decreasing,
+ *            cu[num_seqs] = total_tokens; NULL means one sequence of all tokens
+ *   S0     : [num_seqs, H, dv, dk] double, or NULL for zero initial states
+ *   o      : [total_tokens, H, dv] double (output)
+ *   S_final: [num_seqs, H, dv, dk] double (output, may be NULL)
+ *   threads: OpenMP threads over (sequence, head) pairs; <= 0 means default
+ * Returns 0, or a nonzero code for invalid arguments / allocation failure.
+ */
+int oracle_rda_prefill(const float* q, const float* k, const float* v,
+                       const float* a, const float* b,
+                       const int32_t* cu, int32_t num_seqs, int64_t total_tokens,
+                       int32_t H, int32_t dk, int32_t dv,
+                       const double* S0, double* o, double* S_final,
+                       int32_t threads) {
+    if (!q || !k || !v || !a || !b || !o) return ORACLE_ERR_ARG;
+    if (H <= 0 || dk <= 0 || dv <= 0 || total_tokens < 0) return ORACLE_ERR_ARG;
+    int32_t n_seq = cu ? num_seqs : 1;
+    if (n_seq <= 0) return ORACLE_ERR_ARG;
+    if (cu) {
+        if (cu[0] != 0 || cu[n_seq] != total_tokens) return ORACLE_ERR_ARG;
+        for (int32_t n = 0; n < n_seq; ++n)
+            if (cu[n + 1] < cu[n]) return ORACLE_ERR_ARG;
+    }
+    const size_t dd = (size_t)dv * dk;
+    const int64_t units = (int64_t)n_seq * H;
+    int err = ORACLE_OK;
+#ifdef _OPENMP
+    int nt = threads > 0 ? threads : omp_get_max_threads();
+#pragma omp parallel num_threads(nt)
+#endif
+    {
+        double* S = (double*)malloc(dd * sizeof(double));
+        double* e = (double*)malloc((size_t)dv * sizeof(double));
+        if (!S || !e) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            err = ORACLE_ERR_NOMEM;
+        } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+            for (int64_t u = 0; u < units; ++u) {
+                const int32_t n = (int32_t)(u / H), h = (int32_t)(u % H);
+                const int64_t t0 = cu ? cu[n] : 0;
+                const int64_t t1 = cu ? cu[n + 1] : total_tokens;
+                if (S0) memcpy(S, S0 + (size_t)u * dd, dd * sizeof(double));
+                else memset(S, 0, dd * sizeof(double));
+                for (int64_t t = t0; t < t1; ++t) {
+                    const size_t th = (size_t)t * H + h;
+                    oracle_token(S, e, dk, dv, q + th * dk, k + th * dk, v + th * dv,
+                                 (double)a[th], (double)b[th], o + th * dv);
+                }
+                if (S_final) memcpy(S_final + (size_t)u * dd, S, dd * sizeof(double));
+            }
+        }
+        free(S);
+        free(e);
+    }
+    return err;
+}
+
+/*
+ * One decode step: the same recurrence for a single token per (batch, head),
+ * applied in place to the fp64 state.
+ *   q, k : [B, H, dk] fp32;  v : [B, H, dv] fp32;  a, b : [B, H] fp32
+ *   S    : [B, H, dv, dk] double, in/out
+ *   o    : [B, H, dv] double, output
+ */
+int oracle_rda_decode_step(const float* q, const float* k, const float* v,
+                           const float* a, const float* b,
+                           int32_t B, int32_t H, int32_t dk, int32_t dv,
+                           double* S, double* o, int32_t threads) {
+    if (!q || !k || !v || !a || !b || !S || !o) return ORACLE_ERR_ARG;
+    if (B < 0 || H <= 0 || dk <= 0 || dv <= 0) return ORACLE_ERR_ARG;
+    const size_t dd = (size_t)dv * dk;
+    const int64_t units = (int64_t)B * H;
+    int err = ORACLE_OK;
+#ifdef _OPENMP
+    int nt = threads > 0 ? threads : omp_get_max_threads();
+#pragma omp parallel num_threads(nt)
+#endif
+    {
+        double* e = (double*)malloc((size_t)dv * sizeof(double));
+        if (!e) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            err = ORACLE_ERR_NOMEM;
+        } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 16)
+#endif
+            for (int64_t u = 0; u < units; ++u) {
+                oracle_token(S + (size_t)u * dd, e, dk, dv, q + (size_t)u * dk,
+                             k + (size_t)u * dk, v + (size_t)u * dv,
+                             (double)a[u], (double)b[u], o + (size_t)u * dv);
+            }
+        }
+        free(e);
+    }
+    return err;
+}
+
+/* Number of OpenMP threads a call with `threads` would use. */
+int oracle_threads(int32_t threads) {
+#ifdef _OPENMP
+    return threads > 0 ? threads : omp_get_max_threads();
+#else
+    (void)threads;
+    return 1;
+#endif
+}

@@ -1,0 +1,319 @@
+"""Pins for the fp64 oracle: checks against what the mathematics fixes.
+
+Each ``pin_*`` takes an oracle handle (anything with ``prefill`` and
+``decode_step`` like ``oracle.Oracle``) and raises AssertionError when the
+handle disagrees with a result fixed independently of the oracle's code:
+
+* the unrolled product form of the recurrence (brute force, T <= 4),
+* exact rational arithmetic on dyadic inputs (bitwise),
+* invariants the recurrence must satisfy (identity gates, read-back with
+  orthonormal keys, pure decay, linearity, rotation and permutation
+  equivariance, the state-norm bound),
+* structural identities (resume = one call, packed varlen = separate calls,
+  decode steps = prefill).
+
+The recurrence, per the "Raon-1 nano" teardown (section "The other 1.5B: a
+hybrid built to forget"): decay the state, take the error of the value
+against the decayed state's prediction for the key, write it with strength
+beta; read out o_t = S_t q_t.  As a product: S_t = S_{t-1} A_t + b_t v_t k_t^T
+with A_t = a_t (I - b_t k_t k_t^T).  The module is shared by
+``test_oracle_pins.py`` (real oracle) and ``test_oracle_mutants.py``
+(builds of the oracle with a planted mistake, which must fail some pin).
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+
+RNG_KEY = 777
+
+
+def _rng(i):
+    return np.random.default_rng([RNG_KEY, i])
+
+
+def _close(x, y, rtol=1e-12, what=""):
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    assert x.shape == y.shape, (what, x.shape, y.shape)
+    scale = max(1.0, float(np.max(np.abs(y))) if y.size else 1.0)
+    err = float(np.max(np.abs(x - y))) if y.size else 0.0
+    assert err <= rtol * scale, f"{what}: max abs err {err:.3e} > {rtol:.1e} * {scale:.3e}"
+
+
+def _f32(x):
+    return np.asarray(x, dtype=np.float32)
+
+
+def _d(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def random_case(rng, T, H, dk, dv, unit_keys=True, s0=True):
+    q = rng.standard_normal((T, H, dk))
+    k = rng.standard_normal((T, H, dk))
+    if unit_keys:
+        q /= np.linalg.norm(q, axis=-1, keepdims=True)
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, H, dv))
+    a = rng.uniform(0.05, 1.0, (T, H))
+    b = rng.uniform(0.0, 1.0, (T, H))
+    S0 = rng.standard_normal((1, H, dv, dk)) if s0 else None
+    return [_f32(x) for x in (q, k, v, a, b)] + [S0]
+
+
+# --------------------------------------------------------------------------
+# brute force: unrolled product form
+# --------------------------------------------------------------------------
+def product_form(q, k, v, a, b, S0):
+    """One head: S_t = S0 A_1..A_t + sum_{s<=t} b_s v_s k_s^T A_{s+1}..A_t.
+
+    Inputs are float64 arrays q,k [T,dk], v [T,dv], a,b [T], S0 [dv,dk].
+    Returns (o [T,dv], S_T [dv,dk]).
+    """
+    T, dk = k.shape
+    I = np.eye(dk)
+    A = [a[t] * (I - b[t] * np.outer(k[t], k[t])) for t in range(T)]
+
+    def chain(i, j):  # A_i ... A_j (1-based, inclusive); identity if empty
+        P = np.eye(dk)
+        for s in range(i, j + 1):
+            P = P @ A[s - 1]
+        return P
+
+    o = np.zeros((T, v.shape[1]))
+    S = None
+    for t in range(1, T + 1):
+        S = S0 @ chain(1, t)
+        for s in range(1, t + 1):
+            S = S + b[s - 1] * np.outer(v[s - 1], k[s - 1]) @ chain(s + 1, t)
+        o[t - 1] = S @ q[t - 1]
+    return o, S
+
+
+def pin_bruteforce(orc):
+    cases = [(1, 1, 4, 4, True), (2, 2, 6, 4, False), (3, 2, 8, 8, True),
+             (4, 3, 5, 7, False), (4, 2, 128, 128, True)]
+    for i, (T, H, dk, dv, unit) in enumerate(cases):
+        q, k, v, a, b, S0 = random_case(_rng(i), T, H, dk, dv, unit_keys=unit)
+        o, Sf = orc.prefill(q, k, v, a, b, S0=S0)
+        for h in range(H):
+            ro, rS = product_form(*(_d(x[:, h]) for x in (q, k, v, a, b)),
+                                  S0[0, h])
+            _close(o[:, h], ro, 1e-12, f"brute force o case {i} head {h}")
+            _close(Sf[0, h], rS, 1e-12, f"brute force S case {i} head {h}")
+
+
+# --------------------------------------------------------------------------
+# exact rational arithmetic on dyadic inputs
+# --------------------------------------------------------------------------
+def _frac_matmul(A, B):
+    return [[sum(A[i][m] * B[m][j] for m in range(len(B))) for j in range(len(B[0]))]
+            for i in range(len(A))]
+
+
+def exact_product_form(q, k, v, a, b, S0):
+    """Product form in Fractions for one head (lists of Fractions)."""
+    T, dk = len(k), len(k[0])
+    S = [row[:] for row in S0]
+    outs = []
+    for t in range(T):
+        A = [[a[t] * ((1 if i == j else 0) - b[t] * k[t][i] * k[t][j]) for j in range(dk)]
+             for i in range(dk)]
+        S = _frac_matmul(S, A)
+        S = [[S[i][j] + b[t] * v[t][i] * k[t][j] for j in range(dk)] for i in range(len(S))]
+        outs.append([sum(S[i][j] * q[t][j] for j in range(dk)) for i in range(len(S))])
+    return outs, S
+
+
+def pin_exact_dyadic(orc):
+    """Dyadic inputs with few bits: every intermediate is exact in fp64, so
+    the oracle must equal exact rational arithmetic bit for bit."""
+    F = Fraction
+    q = [[F(1, 2), F(-1, 4)], [F(0), F(1)], [F(3, 4), F(1, 2)]]
+    k = [[F(1), F(0)], [F(1, 2), F(1, 2)], [F(-1, 4), F(3, 4)]]
+    v = [[F(5), F(6), F(-2)], [F(1, 2), F(-3), F(1)], [F(2), F(1, 4), F(-1, 2)]]
+    a = [F(1, 2), F(3, 4), F(1)]
+    b = [F(1, 2), F(1, 4), F(1)]
+    S0 = [[F(1), F(2)], [F(3), F(4)], [F(-1, 2), F(1, 4)]]
+    eo, eS = exact_product_form(q, k, v, a, b, S0)
+    tof = lambda m: np.array([[float(x) for x in r] for r in m])
+    o, Sf = orc.prefill(tof(q)[:, None], tof(k)[:, None], tof(v)[:, None],
+                        np.array([[float(x)] for x in a]), np.array([[float(x)] for x in b]),
+                        S0=tof(S0)[None, None])
+    assert np.array_equal(o[:, 0], tof(eo)), (o[:, 0], tof(eo))
+    assert np.array_equal(Sf[0, 0], tof(eS)), (Sf[0, 0], tof(eS))
+
+
+def pin_hand_example(orc):
+    """Worked by hand: S0 = [[1,2],[3,4]], k = (1,0), q = (0,1), v = (5,6),
+    a = b = 1/2.  Decay: [[.5,1],[1.5,2]]; prediction (.5,1.5); error
+    (4.5,4.5); write .5*error*k^T: S = [[2.75,1],[3.75,2]]; o = S q = (1,2)."""
+    o, Sf = orc.prefill(np.array([[[0.0, 1.0]]]), np.array([[[1.0, 0.0]]]),
+                        np.array([[[5.0, 6.0]]]), np.array([[0.5]]), np.array([[0.5]]),
+                        S0=np.array([[[[1.0, 2.0], [3.0, 4.0]]]]))
+    assert np.array_equal(Sf[0, 0], [[2.75, 1.0], [3.75, 2.0]]), Sf[0, 0]
+    assert np.array_equal(o[0, 0], [1.0, 2.0]), o[0, 0]
+
+
+# --------------------------------------------------------------------------
+# invariants and closed forms
+# --------------------------------------------------------------------------
+def pin_identity_gates(orc):
+    """a = 1, b = 0 leaves S unchanged and reads o_t = S0 q_t."""
+    q, k, v, a, b, S0 = random_case(_rng(10), 9, 2, 6, 5)
+    a[:] = 1.0
+    b[:] = 0.0
+    o, Sf = orc.prefill(q, k, v, a, b, S0=S0)
+    assert np.array_equal(Sf, S0), "S changed under a=1, b=0"
+    for h in range(2):
+        _close(o[:, h], _d(q[:, h]) @ S0[0, h].T, 1e-13, "o under a=1,b=0")
+
+
+def pin_readback(orc):
+    """a = 1, b = 1 and orthonormal keys: after writing v_s under key k_s the
+    state maps k_s to v_s, so querying an earlier key reads its value."""
+    rng = _rng(11)
+    T, dk, dv = 10, 16, 6
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    k = Qm[:, :T].T.copy()                       # orthonormal rows
+    v = rng.standard_normal((T, dv))
+    src = [t // 2 for t in range(T)]             # query an earlier (or same) key
+    q = k[src]
+    S0 = rng.standard_normal((1, 1, dv, dk))
+    # the oracle consumes fp32 inputs; use the rounded values for the check
+    k32, q32, v32 = _f32(k), _f32(q), _f32(v)
+    o, Sf = orc.prefill(q32[:, None], k32[:, None], v32[:, None],
+                        np.ones((T, 1)), np.ones((T, 1)), S0=S0)
+    # fp32-rounded keys are orthonormal to ~1e-7, so the read-back holds to ~1e-6
+    _close(o[:, 0], _d(v32)[src], 2e-6, "read-back of written values")
+    _close(Sf[0, 0] @ _d(k32).T, _d(v32).T, 2e-6, "S k_s = v_s")
+
+
+def pin_pure_decay(orc):
+    """b = 0: S_t = (prod_{s<=t} a_s) S0 and o_t = (prod a) S0 q_t."""
+    q, k, v, a, b, S0 = random_case(_rng(12), 7, 2, 5, 4)
+    b[:] = 0.0
+    o, Sf = orc.prefill(q, k, v, a, b, S0=S0)
+    for h in range(2):
+        cum = np.cumprod(_d(a[:, h]))
+        _close(Sf[0, h], cum[-1] * S0[0, h], 1e-13, "pure decay S")
+        _close(o[:, h], cum[:, None] * (_d(q[:, h]) @ S0[0, h].T), 1e-13, "pure decay o")
+
+
+def pin_single_step(orc):
+    """T = 1 from S0 = 0 with q = k: o = b v (k . k)."""
+    rng = _rng(13)
+    k = _f32(rng.standard_normal((1, 3, 8)))
+    v = _f32(rng.standard_normal((1, 3, 5)))
+    a = _f32(rng.uniform(0.1, 1, (1, 3)))
+    b = _f32(rng.uniform(0, 1, (1, 3)))
+    o, Sf = orc.prefill(k, k, v, a, b)
+    kk = np.sum(_d(k) ** 2, axis=-1)
+    _close(o[0], _d(b)[0, :, None] * _d(v[0]) * kk[0, :, None], 1e-13,
+           "T=1 closed form")
+
+
+def pin_linearity(orc):
+    """(S0, V) -> (O, S_T) is linear for fixed q, k, a, b."""
+    rng = _rng(14)
+    q, k, v1, a, b, S01 = random_case(rng, 12, 2, 6, 5)
+    v2 = _f32(rng.standard_normal(v1.shape))
+    S02 = rng.standard_normal(S01.shape)
+    al, be = 0.75, -1.25   # exact in fp32, so the combined v is exact too
+    v3 = _f32(_d(v1) * al + _d(v2) * be)
+    o1, s1 = orc.prefill(q, k, v1, a, b, S0=S01)
+    o2, s2 = orc.prefill(q, k, v2, a, b, S0=S02)
+    o3, s3 = orc.prefill(q, k, v3, a, b, S0=al * S01 + be * S02)
+    # v3 is rounded to fp32: allow that rounding (~6e-8 relative)
+    _close(o3, al * o1 + be * o2, 1e-6, "linearity o")
+    _close(s3, al * s1 + be * s2, 1e-6, "linearity S")
+
+
+def pin_rotation(orc):
+    """q -> R q, k -> R k, S0 -> S0 R^T gives the same o and S_T -> S_T R^T."""
+    rng = _rng(15)
+    q, k, v, a, b, S0 = random_case(rng, 11, 2, 8, 6)
+    R, _ = np.linalg.qr(rng.standard_normal((8, 8)))
+    o1, s1 = orc.prefill(q, k, v, a, b, S0=S0)
+    qr = _f32(_d(q) @ R.T)
+    kr = _f32(_d(k) @ R.T)
+    o2, s2 = orc.prefill(qr, kr, v, a, b, S0=S0 @ R.T)
+    # rotated inputs are rounded to fp32, so agreement is to ~1e-6
+    _close(o2, o1, 1e-5, "rotation o")
+    _close(s2, s1 @ R.T, 1e-5, "rotation S")
+
+
+def pin_permutation(orc):
+    """Permuting value channels permutes rows of S and channels of o."""
+    rng = _rng(16)
+    q, k, v, a, b, S0 = random_case(rng, 9, 2, 6, 7)
+    p = rng.permutation(7)
+    o1, s1 = orc.prefill(q, k, v, a, b, S0=S0)
+    o2, s2 = orc.prefill(q, k, v[:, :, p], a, b, S0=S0[:, :, p, :])
+    assert np.array_equal(o2, o1[:, :, p]) and np.array_equal(s2, s1[:, :, p, :])
+
+
+def pin_norm_bound(orc):
+    """||S_t||_2 <= a_t ||S_{t-1}||_2 + b_t ||v_t|| ||k_t|| for unit keys."""
+    q, k, v, a, b, S0 = random_case(_rng(17), 20, 1, 6, 6)
+    S = np.ascontiguousarray(S0.copy())
+    prev = np.linalg.norm(S[0, 0], 2)
+    for t in range(20):
+        orc.decode_step(q[t:t + 1], k[t:t + 1], v[t:t + 1], a[t:t + 1], b[t:t + 1], S)
+        cur = np.linalg.norm(S[0, 0], 2)
+        bound = a[t, 0] * prev + b[t, 0] * np.linalg.norm(v[t, 0]) * np.linalg.norm(k[t, 0])
+        assert cur <= bound * (1 + 1e-12) + 1e-12, (t, cur, bound)
+        prev = cur
+
+
+# --------------------------------------------------------------------------
+# structural identities
+# --------------------------------------------------------------------------
+def pin_resume(orc):
+    """prefill(x) = prefill(x[t1:], S0 = prefill(x[:t1]).S_final)."""
+    q, k, v, a, b, S0 = random_case(_rng(18), 30, 2, 8, 8)
+    o, s = orc.prefill(q, k, v, a, b, S0=S0)
+    for t1 in (1, 13, 29):
+        oa, sa = orc.prefill(q[:t1], k[:t1], v[:t1], a[:t1], b[:t1], S0=S0)
+        ob, sb = orc.prefill(q[t1:], k[t1:], v[t1:], a[t1:], b[t1:], S0=sa)
+        _close(np.concatenate([oa, ob]), o, 1e-13, f"resume o at {t1}")
+        _close(sb, s, 1e-13, f"resume S at {t1}")
+
+
+def pin_varlen(orc):
+    """A packed batch equals separate calls per sequence; an empty sequence
+    returns its S0 unchanged."""
+    rng = _rng(19)
+    lens = [5, 0, 9, 1, 0, 4]
+    T = sum(lens)
+    q, k, v, a, b, _ = random_case(rng, T, 2, 6, 5)
+    S0 = rng.standard_normal((len(lens), 2, 5, 6))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    o, s = orc.prefill(q, k, v, a, b, cu_seqlens=cu, S0=S0)
+    for n, L in enumerate(lens):
+        t0, t1 = cu[n], cu[n + 1]
+        if L == 0:
+            assert np.array_equal(s[n], S0[n])
+            continue
+        on, sn = orc.prefill(q[t0:t1], k[t0:t1], v[t0:t1], a[t0:t1], b[t0:t1], S0=S0[n:n + 1])
+        _close(o[t0:t1], on, 1e-14, f"varlen o seq {n}")
+        _close(s[n], sn[0], 1e-14, f"varlen S seq {n}")
+
+
+def pin_decode_equals_prefill(orc):
+    """T single-token decode steps equal one T-token prefill."""
+    q, k, v, a, b, S0 = random_case(_rng(20), 12, 3, 6, 5)
+    o, s = orc.prefill(q, k, v, a, b, S0=S0)
+    S = np.ascontiguousarray(S0[0][None].repeat(1, axis=0))   # [1, H, dv, dk]
+    for t in range(12):
+        ot = orc.decode_step(q[t:t + 1], k[t:t + 1], v[t:t + 1], a[t:t + 1], b[t:t + 1], S)
+        _close(ot[0], o[t], 1e-13, f"decode o step {t}")
+    _close(S, s, 1e-13, "decode final state")
+
+
+ALL_PINS = [pin_bruteforce, pin_exact_dyadic, pin_hand_example, pin_identity_gates,
+            pin_readback, pin_pure_decay, pin_single_step, pin_linearity, pin_rotation,
+            pin_permutation, pin_norm_bound, pin_resume, pin_varlen,
+            pin_decode_equals_prefill]

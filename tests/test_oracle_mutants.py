@@ -1,0 +1,76 @@
+"""Plant plausible mistakes in copies of the oracle source (CPU only) and
+check that every one of them fails at least one pin.  This shows the pins
+constrain each term, sign, index and operand of the recurrence."""
+import os
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+import pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, exact text in oracle.c, replacement)
+MUTANTS = [
+    ("no_decay", "S[(size_t)i * dk + j] *= a;", "(void)a;"),
+    ("error_sign", "e[i] = (double)v[i] - pred;", "e[i] = (double)v[i] + pred;"),
+    ("error_vs_undecayed_state",
+     "pred += S[(size_t)i * dk + j] * (double)k[j];",
+     "pred += S[(size_t)i * dk + j] / a * (double)k[j];"),
+    ("transposed_prediction",
+     "pred += S[(size_t)i * dk + j] * (double)k[j];",
+     "pred += S[(size_t)j * dk + i] * (double)k[j];"),
+    ("write_without_beta", "S[(size_t)i * dk + j] += b * e[i] * (double)k[j];",
+     "S[(size_t)i * dk + j] += e[i] * (double)k[j];"),
+    ("write_value_not_error", "S[(size_t)i * dk + j] += b * e[i] * (double)k[j];",
+     "S[(size_t)i * dk + j] += b * (double)v[i] * (double)k[j];"),
+    ("write_with_query", "S[(size_t)i * dk + j] += b * e[i] * (double)k[j];",
+     "S[(size_t)i * dk + j] += b * e[i] * (double)q[j];"),
+    ("readout_with_key", "acc += S[(size_t)i * dk + j] * (double)q[j];",
+     "acc += S[(size_t)i * dk + j] * (double)k[j];"),
+    ("readout_transposed", "acc += S[(size_t)i * dk + j] * (double)q[j];",
+     "acc += S[(size_t)j * dk + i] * (double)q[j];"),
+    ("ignore_S0", "if (S0) memcpy(S, S0 + (size_t)u * dd, dd * sizeof(double));",
+     "if (S0 && 0) memcpy(S, S0, dd * sizeof(double));"),
+    ("skip_first_token", "const int64_t t0 = cu ? cu[n] : 0;",
+     "const int64_t t0 = (cu ? cu[n] : 0) + 1;"),
+    ("wrong_head", "const size_t th = (size_t)t * H + h;",
+     "const size_t th = (size_t)t * H + (H - 1 - h);"),
+    ("decode_state_of_head0", "oracle_token(S + (size_t)u * dd, e,",
+     "oracle_token(S + (size_t)(u - u % H) * dd, e,"),
+]
+
+
+@pytest.fixture(scope="module")
+def workdir():
+    d = tempfile.mkdtemp(prefix="oracle_mutants_")
+    yield d
+    shutil.rmtree(d, ignore_errors=True)
+
+
+def test_mutations_apply_exactly():
+    src = open(SRC).read()
+    for name, old, new in MUTANTS:
+        assert src.count(old) == 1, f"mutation {name}: pattern found {src.count(old)} times"
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_fails_a_pin(workdir, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1
+    msrc = os.path.join(workdir, f"{name}.c")
+    with open(msrc, "w") as f:
+        f.write(src.replace(old, new))
+    lib = os.path.join(workdir, f"lib_{name}.so")
+    oracle.build(force=True, src=msrc, out=lib)
+    orc = oracle.Oracle(lib)
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError, IndexError):
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
