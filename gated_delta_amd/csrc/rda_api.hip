@@ -1,0 +1,207 @@
+// rda_api.hip -- the C ABI declared in include/rda.h: argument validation,
+// workspace sizing and the launch sequence of each entry point.  Validation
+// is pure host code and runs before anything is enqueued, so every error
+// path returns a status without touching the device.
+#include <climits>
+#include <cstdint>
+
+#include "rda_internal.h"
+
+using namespace rda;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range rng(const void* p, size_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + bytes};
+}
+
+bool overlap(Range x, Range y) {
+    if (x.lo == x.hi || y.lo == y.hi || x.lo == 0 || y.lo == 0) return false;
+    return x.lo < y.hi && y.lo < x.hi;
+}
+
+constexpr int kWalkSlices = kD / 16;  // value-channel slices per (sequence, head)
+
+rda_status check_dims(int32_t heads, int32_t dk, int32_t dv) {
+    if (heads <= 0 || dk <= 0 || dv <= 0) return RDA_ERR_SHAPE;
+    if (dk != kD || dv != kD) return RDA_ERR_UNSUPPORTED;
+    return RDA_OK;
+}
+
+rda_status record(hipEvent_t const* ev, int idx, hipStream_t stream) {
+    if (ev && ev[idx]) {
+        if (hipEventRecord(ev[idx], stream) != hipSuccess) return RDA_ERR_HIP;
+    }
+    return RDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rda_abi_version(void) { return RDA_ABI_VERSION; }
+
+const char* rda_status_string(int status) {
+    switch (status) {
+        case RDA_OK: return "ok";
+        case RDA_ERR_NULL: return "a required pointer is NULL";
+        case RDA_ERR_SHAPE: return "invalid size argument";
+        case RDA_ERR_UNSUPPORTED: return "unsupported shape (only dk = dv = 128 is implemented)";
+        case RDA_ERR_DTYPE: return "unknown dtype";
+        case RDA_ERR_WORKSPACE: return "workspace missing or too small";
+        case RDA_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case RDA_ERR_HIP: return "HIP launch error";
+        case RDA_ERR_ALIAS: return "output buffers overlap other arguments";
+        default: return "unknown status";
+    }
+}
+
+int32_t rda_max_chunks(int32_t num_seqs, int32_t total_tokens) {
+    if (num_seqs < 1 || total_tokens < 0) return -1;
+    const int64_t m = (int64_t(total_tokens) + int64_t(kC - 1) * num_seqs) / kC;
+    if (m > INT32_MAX) return -1;
+    return int32_t(m);
+}
+
+size_t rda_prefill_workspace_bytes(int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                                   int32_t dk, int32_t dv) {
+    if (check_dims(num_heads, dk, dv) != RDA_OK) return 0;
+    const int32_t mc = rda_max_chunks(num_seqs, total_tokens);
+    if (mc < 0) return 0;
+    const TableLayout tl = table_layout(mc, num_seqs);
+    return align256(tl.bytes) + size_t(mc) * size_t(num_heads) * kChunkHeadBytes;
+}
+
+rda_status rda_prefill_profiled(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
+                                const float* a, const float* b, const int32_t* cu_seqlens,
+                                int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                                int32_t dk, int32_t dv, const float* S0, float* o, float* S_final,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                hipEvent_t const* stage_events) {
+    if (qkv_dtype != RDA_BF16 && qkv_dtype != RDA_FP32) return RDA_ERR_DTYPE;
+    if (total_tokens < 0 || num_seqs < 1) return RDA_ERR_SHAPE;
+    if (!cu_seqlens && num_seqs != 1) return RDA_ERR_SHAPE;
+    rda_status st = check_dims(num_heads, dk, dv);
+    if (st != RDA_OK) return st;
+    const int32_t mc = rda_max_chunks(num_seqs, total_tokens);
+    if (mc < 0) return RDA_ERR_SHAPE;
+    if (int64_t(mc) * num_heads > INT32_MAX || int64_t(num_seqs) * num_heads * kWalkSlices > INT32_MAX)
+        return RDA_ERR_SHAPE;
+    if (total_tokens > 0 && (!q || !k || !v || !a || !b || !o)) return RDA_ERR_NULL;
+    if (!workspace) return RDA_ERR_WORKSPACE;
+    const size_t need = rda_prefill_workspace_bytes(num_seqs, total_tokens, num_heads, dk, dv);
+    if (workspace_bytes < need) return RDA_ERR_WORKSPACE;
+    for (const void* p : {q, k, v, static_cast<const void*>(a), static_cast<const void*>(b),
+                          static_cast<const void*>(S0), static_cast<const void*>(o),
+                          static_cast<const void*>(S_final), static_cast<const void*>(workspace)})
+        if (p && !aligned16(p)) return RDA_ERR_ALIGN;
+    if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return RDA_ERR_ALIGN;
+
+    const size_t esz = qkv_dtype == RDA_BF16 ? 2 : 4;
+    const size_t th = size_t(total_tokens) * num_heads;
+    const size_t sbytes = size_t(num_seqs) * num_heads * kD * kD * sizeof(float);
+    const Range rq = rng(q, th * kD * esz), rk = rng(k, th * kD * esz), rv = rng(v, th * kD * esz);
+    const Range ra = rng(a, th * 4), rb = rng(b, th * 4);
+    const Range ro = rng(o, th * kD * 4), rs0 = rng(S0, S0 ? sbytes : 0);
+    const Range rsf = rng(S_final, S_final ? sbytes : 0), rws = rng(workspace, need);
+    const Range rcu = rng(cu_seqlens, cu_seqlens ? size_t(num_seqs + 1) * 4 : 0);
+    for (Range in : {rq, rk, rv, ra, rb, rs0, rcu, rsf, rws})
+        if (overlap(ro, in)) return RDA_ERR_ALIAS;
+    for (Range in : {rq, rk, rv, ra, rb, rcu, rws})
+        if (overlap(rsf, in)) return RDA_ERR_ALIAS;
+    if (S0 && S_final && S0 != S_final && overlap(rs0, rsf)) return RDA_ERR_ALIAS;
+    for (Range in : {rq, rk, rv, ra, rb, rs0, rcu})
+        if (overlap(rws, in)) return RDA_ERR_ALIAS;
+
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    const TableLayout tl = table_layout(mc, num_seqs);
+    int32_t* rec = reinterpret_cast<int32_t*>(ws + tl.rec_off);
+    int32_t* seq_off = reinterpret_cast<int32_t*>(ws + tl.seq_off_off);
+    int32_t* nch = reinterpret_cast<int32_t*>(ws + tl.num_off);
+    unsigned char* factors = ws + align256(tl.bytes);
+
+    if ((st = record(stage_events, 2 * RDA_STAGE_TABLE, stream)) != RDA_OK) return st;
+    if (launch_chunk_table(cu_seqlens, num_seqs, total_tokens, mc, rec, seq_off, nch, stream) !=
+        hipSuccess)
+        return RDA_ERR_HIP;
+    if ((st = record(stage_events, 2 * RDA_STAGE_TABLE + 1, stream)) != RDA_OK) return st;
+
+    if ((st = record(stage_events, 2 * RDA_STAGE_PREP, stream)) != RDA_OK) return st;
+    if (mc > 0 && total_tokens > 0) {
+        if (launch_prep(q, k, v, qkv_dtype, a, b, num_heads, mc, rec, nch, factors, stream) !=
+            hipSuccess)
+            return RDA_ERR_HIP;
+    }
+    if ((st = record(stage_events, 2 * RDA_STAGE_PREP + 1, stream)) != RDA_OK) return st;
+
+    if ((st = record(stage_events, 2 * RDA_STAGE_WALK, stream)) != RDA_OK) return st;
+    if (launch_walk(qkv_dtype, num_seqs, num_heads, rec, seq_off, nch, factors, S0, o, S_final,
+                    stream) != hipSuccess)
+        return RDA_ERR_HIP;
+    if ((st = record(stage_events, 2 * RDA_STAGE_WALK + 1, stream)) != RDA_OK) return st;
+    return RDA_OK;
+}
+
+rda_status rda_prefill(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
+                       const float* a, const float* b, const int32_t* cu_seqlens, int32_t num_seqs,
+                       int32_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
+                       const float* S0, float* o, float* S_final, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+    return rda_prefill_profiled(q, k, v, qkv_dtype, a, b, cu_seqlens, num_seqs, total_tokens,
+                                num_heads, dk, dv, S0, o, S_final, workspace, workspace_bytes,
+                                stream, nullptr);
+}
+
+rda_status rda_decode_step(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
+                           const float* a, const float* b, int32_t batch, int32_t num_heads,
+                           int32_t dk, int32_t dv, float* S, float* o, hipStream_t stream) {
+    if (qkv_dtype != RDA_BF16 && qkv_dtype != RDA_FP32) return RDA_ERR_DTYPE;
+    if (batch < 0) return RDA_ERR_SHAPE;
+    rda_status st = check_dims(num_heads, dk, dv);
+    if (st != RDA_OK) return st;
+    if (int64_t(batch) * num_heads > INT32_MAX) return RDA_ERR_SHAPE;
+    if (batch == 0) return RDA_OK;
+    if (!q || !k || !v || !a || !b || !S || !o) return RDA_ERR_NULL;
+    for (const void* p : {q, k, v, static_cast<const void*>(a), static_cast<const void*>(b),
+                          static_cast<const void*>(S), static_cast<const void*>(o)})
+        if (!aligned16(p)) return RDA_ERR_ALIGN;
+    const size_t esz = qkv_dtype == RDA_BF16 ? 2 : 4;
+    const size_t bh = size_t(batch) * num_heads;
+    const Range rq = rng(q, bh * kD * esz), rk = rng(k, bh * kD * esz), rv = rng(v, bh * kD * esz);
+    const Range ra = rng(a, bh * 4), rb = rng(b, bh * 4);
+    const Range rS = rng(S, bh * kD * kD * 4), ro = rng(o, bh * kD * 4);
+    for (Range in : {rq, rk, rv, ra, rb, rS})
+        if (overlap(ro, in)) return RDA_ERR_ALIAS;
+    for (Range in : {rq, rk, rv, ra, rb})
+        if (overlap(rS, in)) return RDA_ERR_ALIAS;
+    if (launch_decode(q, k, v, qkv_dtype, a, b, batch, num_heads, S, o, stream) != hipSuccess)
+        return RDA_ERR_HIP;
+    return RDA_OK;
+}
+
+rda_status rda_chunk_table(const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                           int32_t* out, int32_t* out_seq_offsets, int32_t* out_num_chunks,
+                           hipStream_t stream) {
+    if (total_tokens < 0 || num_seqs < 1) return RDA_ERR_SHAPE;
+    if (!cu_seqlens && num_seqs != 1) return RDA_ERR_SHAPE;
+    const int32_t mc = rda_max_chunks(num_seqs, total_tokens);
+    if (mc < 0) return RDA_ERR_SHAPE;
+    if (!out_seq_offsets || !out_num_chunks || (mc > 0 && !out)) return RDA_ERR_NULL;
+    for (const void* p : {static_cast<const void*>(cu_seqlens), static_cast<const void*>(out),
+                          static_cast<const void*>(out_seq_offsets),
+                          static_cast<const void*>(out_num_chunks)})
+        if (p && (reinterpret_cast<uintptr_t>(p) & 3u)) return RDA_ERR_ALIGN;
+    if (launch_chunk_table(cu_seqlens, num_seqs, total_tokens, mc, out, out_seq_offsets,
+                           out_num_chunks, stream) != hipSuccess)
+        return RDA_ERR_HIP;
+    return RDA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// rda_device.h -- small device helpers for the gfx950 kernels: vector types,
+// bf16 conversion and hi/lo splitting, 16-lane DPP reductions, input loads.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace rda {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+// bf16 bit pattern -> fp32 (exact)
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+    return __uint_as_float(uint32_t(h) << 16);
+}
+
+// fp32 -> bf16 bit pattern, round to nearest even (finite inputs)
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+// x ~= hi + lo with hi = bf16(x), lo = bf16(x - hi): the pair carries ~16
+// mantissa bits, so an MFMA product of pairs (hi*hi + hi*lo + lo*hi) is
+// accurate to ~2^-16 relative.
+__device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
+    hi = f32_to_bf16_bits(x);
+    lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+}
+
+// Sum over each 16-lane row of the wavefront with DPP (every lane of the
+// row receives the row's sum): xor 1, xor 2 (quad permutes), then the half-
+// and full-row mirrors pair up quads and half rows.
+__device__ __forceinline__ float dpp_sum16(float x) {
+    int v = __float_as_int(x);
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));  // quad [1,0,3,2]
+    v = __float_as_int(x);
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));  // quad [2,3,0,1]
+    v = __float_as_int(x);
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false)); // row_half_mirror
+    v = __float_as_int(x);
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false)); // row_mirror
+    return x;
+}
+
+// Load 4 consecutive input elements as fp32 (bf16 bits or fp32).
+__device__ __forceinline__ void load4_bf16(const uint16_t* p, float out[4]) {
+    u16x4 h = *reinterpret_cast<const u16x4*>(p);
+    out[0] = bf16_bits_to_f32(h[0]);
+    out[1] = bf16_bits_to_f32(h[1]);
+    out[2] = bf16_bits_to_f32(h[2]);
+    out[3] = bf16_bits_to_f32(h[3]);
+}
+
+__device__ __forceinline__ void load4_f32(const float* p, float out[4]) {
+    f32x4 x = *reinterpret_cast<const f32x4*>(p);
+    out[0] = x[0];
+    out[1] = x[1];
+    out[2] = x[2];
+    out[3] = x[3];
+}
+
+template <typename T>
+__device__ __forceinline__ void load4(const T* p, float out[4]);
+template <>
+__device__ __forceinline__ void load4<uint16_t>(const uint16_t* p, float out[4]) { load4_bf16(p, out); }
+template <>
+__device__ __forceinline__ void load4<float>(const float* p, float out[4]) { load4_f32(p, out); }
+
+template <typename T>
+__device__ __forceinline__ float load1(const T* p);
+template <>
+__device__ __forceinline__ float load1<uint16_t>(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+template <>
+__device__ __forceinline__ float load1<float>(const float* p) { return *p; }
+
+}  // namespace rda

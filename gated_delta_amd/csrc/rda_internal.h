@@ -1,0 +1,80 @@
+// rda_internal.h -- declarations shared by the library's translation units
+// (launchers, workspace layout).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/rda.h"
+
+namespace rda {
+
+constexpr int kC = RDA_CHUNK;      // tokens per chunk
+constexpr int kD = RDA_HEAD_DIM;   // dk = dv
+
+// ---------------------------------------------------------------------------
+// Workspace layout of rda_prefill (all offsets 256-byte aligned):
+//
+//   [table]     int32 rec[max_chunks][4]   (seq, token start, valid len, chunk-in-seq)
+//               int32 seq_off[num_seqs+1]  first chunk of each sequence
+//               int32 num_chunks[1]
+//   [factors]   per (chunk, head), kChunkHeadBytes each, chunk-major:
+//                 Wpk  bf16 hi/lo of W, packed as the walk's MFMA A operand
+//                 Qpk  bf16 hi/lo of Q' = diag(gamma) Q - A W, same packing
+//                 Up   fp32 U' = T diag(b) V, in the walk's accumulator order
+//                 Op   fp32 O' = A U', same order
+//                 Kt   bf16 K^T packed as the walk's state-update A operand
+//                      (second plane: lo parts, used for fp32 inputs only)
+//                 gsc  fp32 gamma_C / gamma_i for i < 64, then gamma_C
+// ---------------------------------------------------------------------------
+constexpr size_t kPackBytes = size_t(kC) * kD * 2 * 2;   // hi + lo bf16, 64 x 128
+constexpr size_t kF32Bytes = size_t(kC) * kD * 4;        // 64 x 128 fp32
+constexpr size_t kKtBytes = size_t(kC) * kD * 2 * 2;     // 64 x 128 bf16, hi and lo planes
+constexpr size_t kGscBytes = 512;                        // 65 floats, padded
+constexpr size_t kOffW = 0;
+constexpr size_t kOffQ = kOffW + kPackBytes;
+constexpr size_t kOffU = kOffQ + kPackBytes;
+constexpr size_t kOffO = kOffU + kF32Bytes;
+constexpr size_t kOffK = kOffO + kF32Bytes;
+constexpr size_t kOffG = kOffK + kKtBytes;
+constexpr size_t kChunkHeadBytes = kOffG + kGscBytes;
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct TableLayout {
+    size_t rec_off, seq_off_off, num_off, bytes;
+};
+
+inline TableLayout table_layout(int32_t max_chunks, int32_t num_seqs) {
+    TableLayout t;
+    t.rec_off = 0;
+    t.seq_off_off = align256(size_t(max_chunks) * 4 * sizeof(int32_t));
+    t.num_off = t.seq_off_off + align256(size_t(num_seqs + 1) * sizeof(int32_t));
+    t.bytes = t.num_off + 256;
+    return t;
+}
+
+// ---------------------------------------------------------------------------
+// launchers (each returns the hipGetLastError() of its launch)
+// ---------------------------------------------------------------------------
+hipError_t launch_chunk_table(const int32_t* cu, int32_t num_seqs, int32_t total_tokens,
+                              int32_t max_chunks, int32_t* rec, int32_t* seq_off,
+                              int32_t* num_chunks, hipStream_t stream);
+
+hipError_t launch_decode(const void* q, const void* k, const void* v, rda_dtype dt,
+                         const float* a, const float* b, int32_t batch, int32_t heads,
+                         float* S, float* o, hipStream_t stream);
+
+hipError_t launch_prep(const void* q, const void* k, const void* v, rda_dtype dt,
+                       const float* a, const float* b, int32_t heads, int32_t max_chunks,
+                       const int32_t* rec, const int32_t* num_chunks, unsigned char* factors,
+                       hipStream_t stream);
+
+hipError_t launch_walk(rda_dtype dt, int32_t num_seqs, int32_t heads, const int32_t* rec,
+                       const int32_t* seq_off, const int32_t* num_chunks,
+                       const unsigned char* factors, const float* S0, float* o, float* S_final,
+                       hipStream_t stream);
+
+}  // namespace rda

@@ -1,0 +1,267 @@
+"""Thin Python binding of librda.so (argument marshalling only).
+
+Every function here has the name of the C entry point it calls (see
+``include/rda.h``) and does no arithmetic of its own: it checks tensor
+dtypes, devices and shapes, allocates outputs and the workspace with
+``torch.empty`` on the caller's device, validates ``cu_seqlens`` on a host
+copy, and passes raw device pointers plus the current HIP stream.  If the
+library is not built, the first call raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch  # imported before librda.so so both share one HIP runtime
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librda.so")
+_lib = None
+
+RDA_BF16 = 0
+RDA_FP32 = 1
+RDA_CHUNK = 64
+RDA_HEAD_DIM = 128
+RDA_NUM_STAGES = 3
+STAGES = ("table", "prep", "walk")
+
+
+class RdaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = int(status)
+        super().__init__(f"{where}: status {status} ({rda_status_string(status)})")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is not built; run `python -m gated_delta_amd.build` "
+                "(the RDA kernels have no non-HIP fallback)")
+        lib = ctypes.CDLL(_LIB_PATH)
+        p, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        lib.rda_abi_version.argtypes = []
+        lib.rda_abi_version.restype = ctypes.c_int
+        lib.rda_status_string.argtypes = [ctypes.c_int]
+        lib.rda_status_string.restype = ctypes.c_char_p
+        lib.rda_max_chunks.argtypes = [i32, i32]
+        lib.rda_max_chunks.restype = i32
+        lib.rda_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        lib.rda_prefill_workspace_bytes.restype = sz
+        pre = [p, p, p, ctypes.c_int, p, p, p, i32, i32, i32, i32, i32, p, p, p, p, sz, p]
+        lib.rda_prefill.argtypes = pre
+        lib.rda_prefill.restype = ctypes.c_int
+        lib.rda_prefill_profiled.argtypes = pre + [p]
+        lib.rda_prefill_profiled.restype = ctypes.c_int
+        lib.rda_decode_step.argtypes = [p, p, p, ctypes.c_int, p, p, i32, i32, i32, i32, p, p, p]
+        lib.rda_decode_step.restype = ctypes.c_int
+        lib.rda_chunk_table.argtypes = [p, i32, i32, p, p, p, p]
+        lib.rda_chunk_table.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def lib():
+    """The loaded ctypes library (loads it on first use)."""
+    return _load()
+
+
+# ---------------------------------------------------------------------------
+# plain queries
+# ---------------------------------------------------------------------------
+def rda_abi_version() -> int:
+    return int(_load().rda_abi_version())
+
+
+def rda_status_string(status: int) -> str:
+    return _load().rda_status_string(int(status)).decode()
+
+
+def rda_max_chunks(num_seqs: int, total_tokens: int) -> int:
+    return int(_load().rda_max_chunks(int(num_seqs), int(total_tokens)))
+
+
+def rda_prefill_workspace_bytes(num_seqs: int, total_tokens: int, num_heads: int,
+                                dk: int = RDA_HEAD_DIM, dv: int = RDA_HEAD_DIM) -> int:
+    return int(_load().rda_prefill_workspace_bytes(int(num_seqs), int(total_tokens),
+                                                   int(num_heads), int(dk), int(dv)))
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _qkv_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return RDA_BF16
+    if t.dtype == torch.float32:
+        return RDA_FP32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def check_cu_seqlens(cu, total_tokens: int) -> np.ndarray:
+    """Host-side validation of packed-sequence offsets; returns int32 array."""
+    if isinstance(cu, torch.Tensor):
+        cu = cu.detach().to("cpu").numpy()
+    cu = np.asarray(cu)
+    if cu.ndim != 1 or cu.shape[0] < 2:
+        raise ValueError("cu_seqlens must be 1-D with at least 2 entries")
+    if not np.issubdtype(cu.dtype, np.integer):
+        raise TypeError("cu_seqlens must be integers")
+    cu64 = cu.astype(np.int64)
+    if cu64[0] != 0:
+        raise ValueError("cu_seqlens[0] must be 0")
+    if np.any(np.diff(cu64) < 0):
+        raise ValueError("cu_seqlens must be non-decreasing")
+    if cu64[-1] != total_tokens:
+        raise ValueError(f"cu_seqlens[-1] = {cu64[-1]} != total tokens {total_tokens}")
+    if cu64[-1] > np.iinfo(np.int32).max:
+        raise ValueError("cu_seqlens exceeds int32")
+    return cu64.astype(np.int32)
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+def rda_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, a: torch.Tensor,
+                b: torch.Tensor, cu_seqlens=None, S0: Optional[torch.Tensor] = None, *,
+                o: Optional[torch.Tensor] = None, S_final: Optional[torch.Tensor] = None,
+                want_state: bool = True, workspace: Optional[torch.Tensor] = None,
+                stream=None, stage_events: Optional[Sequence] = None):
+    """Chunked RDA prefill (C entry point ``rda_prefill``).
+
+    q, k [T, H, 128] and v [T, H, 128] (bf16 or fp32, same dtype), a, b
+    [T, H] fp32, cu_seqlens (host or device int offsets, [N+1]) or None,
+    S0 [N, H, 128, 128] fp32 or None.  Returns (o [T, H, 128] fp32,
+    S_final [N, H, 128, 128] fp32 or None).  ``S_final`` may be passed as
+    the same tensor as ``S0`` to resume in place.  ``stage_events``: six
+    recorded-once torch.cuda.Event objects (start/stop per stage) to time
+    the kernels on the launch stream.
+    """
+    lib_ = _load()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a GPU tensor")
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _qkv_dtype(q)
+    _need(q, "q", q.dtype, (T, H, dk), dev)
+    _need(k, "k", q.dtype, (T, H, dk), dev)
+    _need(v, "v", q.dtype, (T, H, dv), dev)
+    _need(a, "a", torch.float32, (T, H), dev)
+    _need(b, "b", torch.float32, (T, H), dev)
+    if cu_seqlens is not None:
+        cu_host = check_cu_seqlens(cu_seqlens, T)
+        N = cu_host.shape[0] - 1
+        if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.device == dev \
+                and cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous():
+            cu_dev = cu_seqlens
+        else:
+            cu_dev = torch.from_numpy(cu_host).to(dev)
+    else:
+        N, cu_dev = 1, None
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (N, H, dv, dk), dev)
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=torch.float32, device=dev)
+    _need(o, "o", torch.float32, (T, H, dv), dev)
+    if S_final is None and want_state:
+        S_final = torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev)
+    if S_final is not None:
+        _need(S_final, "S_final", torch.float32, (N, H, dv, dk), dev)
+    need = rda_prefill_workspace_bytes(N, T, H, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    args = [_ptr(q), _ptr(k), _ptr(v), dt, _ptr(a), _ptr(b), _ptr(cu_dev), N, T, H, dk, dv,
+            _ptr(S0), _ptr(o), _ptr(S_final), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream_handle(stream)]
+    if stage_events is not None:
+        if len(stage_events) != 2 * RDA_NUM_STAGES:
+            raise ValueError("stage_events needs 2 events per stage")
+        arr = (ctypes.c_void_p * (2 * RDA_NUM_STAGES))(
+            *[None if e is None else ctypes.c_void_p(e.cuda_event) for e in stage_events])
+        st = lib_.rda_prefill_profiled(*args, arr)
+    else:
+        st = lib_.rda_prefill(*args)
+    if st != 0:
+        raise RdaError(st, "rda_prefill")
+    return o, S_final
+
+
+def rda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, a: torch.Tensor,
+                    b: torch.Tensor, S: torch.Tensor, *, o: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """One in-place decode step (C entry point ``rda_decode_step``).
+
+    q, k, v [B, H, 128] (bf16 or fp32), a, b [B, H] fp32, S [B, H, 128, 128]
+    fp32 (updated in place).  Returns o [B, H, 128] fp32.
+    """
+    lib_ = _load()
+    dev = q.device
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _qkv_dtype(q)
+    _need(q, "q", q.dtype, (B, H, dk), dev)
+    _need(k, "k", q.dtype, (B, H, dk), dev)
+    _need(v, "v", q.dtype, (B, H, dv), dev)
+    _need(a, "a", torch.float32, (B, H), dev)
+    _need(b, "b", torch.float32, (B, H), dev)
+    _need(S, "S", torch.float32, (B, H, dv, dk), dev)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=torch.float32, device=dev)
+    _need(o, "o", torch.float32, (B, H, dv), dev)
+    st = lib_.rda_decode_step(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(a), _ptr(b), B, H, dk, dv,
+                              _ptr(S), _ptr(o), _stream_handle(stream))
+    if st != 0:
+        raise RdaError(st, "rda_decode_step")
+    return o
+
+
+def rda_chunk_table(cu_seqlens, num_seqs: int, total_tokens: int, device="cuda",
+                    stream=None):
+    """The chunk table rda_prefill builds (C entry point ``rda_chunk_table``).
+
+    cu_seqlens: device int32 tensor [N+1] or None.  Returns device tensors
+    (rec [max_chunks, 4], seq_offsets [N+1], num_chunks [1]).  The offsets
+    are NOT validated here, so malformed tables can be inspected.
+    """
+    lib_ = _load()
+    mc = rda_max_chunks(num_seqs, total_tokens)
+    if mc < 0:
+        raise ValueError("bad sizes")
+    rec = torch.empty((max(mc, 1), 4), dtype=torch.int32, device=device)
+    seq_off = torch.empty((num_seqs + 1,), dtype=torch.int32, device=device)
+    nch = torch.empty((1,), dtype=torch.int32, device=device)
+    st = lib_.rda_chunk_table(_ptr(cu_seqlens), int(num_seqs), int(total_tokens), _ptr(rec),
+                              _ptr(seq_off), _ptr(nch), _stream_handle(stream))
+    if st != 0:
+        raise RdaError(st, "rda_chunk_table")
+    return rec[:mc], seq_off, nch

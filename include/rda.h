@@ -1,0 +1,168 @@
+/*
+ * rda.h -- C ABI of librda.so: the RDA gated-delta token mixer on MI355X.
+ *
+ * RDA ("Raon Delta Attention") is the linear-attention token mixer of the
+ * Raon-1 models.  The "Raon-1 nano" teardown page (ai.satyajit.si), section
+ * "The other 1.5B: a hybrid built to forget", describes its recurrent step:
+ * decay the matrix state, form the error between the value and what the
+ * decayed state predicts for the key, and write that error back with
+ * strength beta.  Section "The cache is small if the runtime keeps it small"
+ * of the same page fixes the state as 16 heads x 128 x 128 fp32 per layer,
+ * carried across calls; the "Raon-1-nano-gguf" page's spec table gives the
+ * 16 heads of dimension 128, and its Transformers section notes that the
+ * plain PyTorch path walks prompt tokens one at a time.  With a scalar decay
+ * a_t and write strength b_t per token and head the step is the gated delta
+ * rule
+ *
+ *     S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,   o_t = S_t q_t
+ *
+ * (read-out after the update; no query scale; q and k are used as given --
+ * callers L2-normalise them).  rda_prefill evaluates it for whole prompts in
+ * chunks of 64 tokens (WY / UT-transform form on bf16 MFMA); rda_decode_step
+ * applies one token in place.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers to contiguous row-major memory,
+ *   16-byte aligned.  The caller owns every buffer; the library allocates no
+ *   device memory (rda_prefill takes a caller-provided workspace).
+ * - Layouts: tokens q, k [T, H, dk], v [T, H, dv]; gates a, b [T, H] fp32;
+ *   states [N, H, dv, dk] fp32 with S[i][j], i = value channel (row),
+ *   j = key channel (column); outputs o [T, H, dv] fp32.
+ * - Only dk = dv = 128 is supported (RDA_ERR_UNSUPPORTED otherwise).
+ * - Work is enqueued asynchronously on `stream` (0 = the null stream); no
+ *   entry point synchronises the host.  Argument checks run on the host
+ *   before anything is enqueued; on an error nothing is launched.  Launch
+ *   failures return RDA_ERR_HIP.  Nothing aborts, throws or prints.
+ * - Gates must satisfy a in (0, 1] and b in [0, 1]; other values are not
+ *   checked and give unspecified (but memory-safe) results.
+ * - Entry points hold no mutable global state and are thread-safe.
+ */
+#ifndef RDA_H
+#define RDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RDA_ABI_VERSION 1
+#define RDA_CHUNK 64      /* tokens per prefill chunk */
+#define RDA_HEAD_DIM 128  /* the only supported dk = dv */
+
+typedef enum {
+    RDA_OK = 0,
+    RDA_ERR_NULL = 1,        /* a required pointer is NULL */
+    RDA_ERR_SHAPE = 2,       /* a size is negative / zero where not allowed / overflows */
+    RDA_ERR_UNSUPPORTED = 3, /* a valid shape this build does not implement (dk, dv != 128) */
+    RDA_ERR_DTYPE = 4,       /* unknown rda_dtype */
+    RDA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than rda_prefill_workspace_bytes */
+    RDA_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned */
+    RDA_ERR_HIP = 7,         /* a HIP launch reported an error */
+    RDA_ERR_ALIAS = 8        /* outputs overlap inputs (other than S_final == S0) */
+} rda_status;
+
+typedef enum { RDA_BF16 = 0, RDA_FP32 = 1 } rda_dtype;
+
+/* Stages of one rda_prefill call, in launch order (for rda_prefill_profiled). */
+typedef enum {
+    RDA_STAGE_TABLE = 0, /* chunk table from cu_seqlens */
+    RDA_STAGE_PREP = 1,  /* per-chunk intra-chunk solve and WY products (parallel) */
+    RDA_STAGE_WALK = 2,  /* inter-chunk state passing and outputs (sequential per sequence) */
+    RDA_NUM_STAGES = 3
+} rda_stage;
+
+/* RDA_ABI_VERSION of the loaded library. */
+int rda_abi_version(void);
+
+/* Static English text for a status code (never NULL). */
+const char* rda_status_string(int status);
+
+/* Upper bound on the number of 64-token chunks of a packed batch:
+ * floor((total_tokens + 63 * num_seqs) / 64).  Returns -1 on bad sizes. */
+int32_t rda_max_chunks(int32_t num_seqs, int32_t total_tokens);
+
+/* Workspace bytes rda_prefill needs for these sizes (0 on bad sizes).  The
+ * workspace holds the chunk table and the per-chunk WY factors; its contents
+ * need no initialisation and are garbage after the call. */
+size_t rda_prefill_workspace_bytes(int32_t num_seqs, int32_t total_tokens,
+                                   int32_t num_heads, int32_t dk, int32_t dv);
+
+/*
+ * Chunked prefill over a packed batch of variable-length sequences.
+ *
+ *   q, k        [total_tokens, H, dk], v [total_tokens, H, dv], dtype qkv_dtype
+ *               (RDA_BF16 or RDA_FP32; fp32 values are fed to MFMA as exact
+ *               bf16 hi + lo pairs)
+ *   a, b        [total_tokens, H] fp32 gates
+ *   cu_seqlens  device int32 [num_seqs + 1] token offsets, or NULL for one
+ *               sequence of total_tokens (then num_seqs must be 1).  Contents
+ *               are trusted (cu[0] = 0, non-decreasing, cu[N] = total_tokens;
+ *               the Python binding checks this on a host copy) but never read
+ *               or used out of bounds.  Zero-length sequences are allowed and
+ *               return S_final = S0.
+ *   S0          [num_seqs, H, dv, dk] fp32 initial states, or NULL for zeros
+ *   o           [total_tokens, H, dv] fp32 output
+ *   S_final     [num_seqs, H, dv, dk] fp32 output, or NULL to skip; may be the
+ *               same pointer as S0 (in-place resume), no other overlap allowed
+ *   workspace   device scratch of at least rda_prefill_workspace_bytes(...)
+ * total_tokens = 0 is allowed (only S_final is written).
+ */
+rda_status rda_prefill(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
+                       const float* a, const float* b,
+                       const int32_t* cu_seqlens, int32_t num_seqs,
+                       int32_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
+                       const float* S0, float* o, float* S_final,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * rda_prefill with per-stage timing events: when `stage_events` is non-NULL
+ * it points to 2 * RDA_NUM_STAGES events; stage s records stage_events[2s]
+ * before its kernel and stage_events[2s+1] after it, on `stream` (NULL
+ * entries are skipped).  Results are identical to rda_prefill.
+ */
+rda_status rda_prefill_profiled(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
+                                const float* a, const float* b,
+                                const int32_t* cu_seqlens, int32_t num_seqs,
+                                int32_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
+                                const float* S0, float* o, float* S_final,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                hipEvent_t const* stage_events);
+
+/*
+ * One decode step: the recurrence for a single token per (batch, head),
+ * updating the state in place in one read-modify-write pass over it.
+ *
+ *   q, k [batch, H, dk], v [batch, H, dv] (qkv_dtype); a, b [batch, H] fp32
+ *   S    [batch, H, dv, dk] fp32, read and overwritten with the new state
+ *   o    [batch, H, dv] fp32 output (o = S_new q)
+ * batch = 0 is allowed (nothing is launched).
+ */
+rda_status rda_decode_step(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
+                           const float* a, const float* b,
+                           int32_t batch, int32_t num_heads, int32_t dk, int32_t dv,
+                           float* S, float* o, hipStream_t stream);
+
+/*
+ * Test hook: the chunk table rda_prefill builds from cu_seqlens.
+ *   out               device int32 [rda_max_chunks(...), 4]; row c =
+ *                     (sequence, first token, valid length 1..64, chunk index
+ *                     within its sequence) for c < *num_chunks, (-1, 0, 0, 0) after
+ *   out_seq_offsets   device int32 [num_seqs + 1]: first chunk of each sequence
+ *                     (exclusive prefix sum of ceil(len / 64)); required
+ *   out_num_chunks    device int32 [1]: number of chunks
+ * cu_seqlens may be NULL (one sequence of total_tokens, num_seqs = 1).
+ */
+rda_status rda_chunk_table(const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                           int32_t* out, int32_t* out_seq_offsets, int32_t* out_num_chunks,
+                           hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RDA_H */

@@ -1,0 +1,144 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point the
+public header declares, sizes workspaces, and rejects bad arguments with the
+documented status before anything reaches a device (no compute calls)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import table_ref
+from gated_delta_amd import rda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rda.h")
+
+OK, NULL, SHAPE, UNSUP, DTYPE, WS, ALIGN, HIPERR, ALIAS = range(9)
+P = 1 << 40          # fake, well-aligned device addresses: never dereferenced
+GiB = 1 << 30
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rda.library_path()):
+        import gated_delta_amd.build as b
+        b.build()
+    return rda.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rda_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("rda_prefill", "rda_decode_step", "rda_prefill_workspace_bytes",
+              "rda_chunk_table", "rda_abi_version", "rda_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"librda.so does not export {name}"
+
+
+def test_version_and_status_strings(lib):
+    assert rda.rda_abi_version() == 1
+    for s in range(9):
+        assert rda.rda_status_string(s) and rda.rda_status_string(s) != "unknown status"
+    assert rda.rda_status_string(99) == "unknown status"
+
+
+def test_max_chunks_matches_reference(lib):
+    for N, T in [(1, 0), (1, 1), (1, 64), (1, 65), (8, 32768), (3, 5), (1000, 123457)]:
+        assert rda.rda_max_chunks(N, T) == table_ref.max_chunks(N, T)
+    assert rda.rda_max_chunks(0, 5) == -1 and rda.rda_max_chunks(1, -1) == -1
+
+
+def test_workspace_bytes(lib):
+    w1 = rda.rda_prefill_workspace_bytes(1, 16384, 16)
+    w2 = rda.rda_prefill_workspace_bytes(1, 16384, 8)
+    assert w1 > w2 > 0 and w1 % 256 == 0
+    assert rda.rda_prefill_workspace_bytes(1, 16384, 16, 64, 64) == 0
+    assert rda.rda_prefill_workspace_bytes(1, 0, 16) > 0
+
+
+def _prefill(lib, q=P, k=P + GiB, v=P + 2 * GiB, dt=0, a=P + 3 * GiB, b=P + 4 * GiB,
+             cu=None, N=1, T=128, H=2, dk=128, dv=128, S0=None, o=P + 5 * GiB,
+             Sf=P + 6 * GiB, ws=P + 7 * GiB, wsb=None):
+    if wsb is None:
+        wsb = rda.rda_prefill_workspace_bytes(N, T, H, 128, 128) if (dk, dv) == (128, 128) else 1 << 30
+    return lib.rda_prefill(q, k, v, dt, a, b, cu, N, T, H, dk, dv, S0, o, Sf, ws, wsb, None)
+
+
+def test_prefill_rejects_bad_arguments(lib):
+    assert _prefill(lib, q=None) == NULL
+    assert _prefill(lib, o=None) == NULL
+    assert _prefill(lib, dt=7) == DTYPE
+    assert _prefill(lib, T=-1) == SHAPE
+    assert _prefill(lib, N=0) == SHAPE
+    assert _prefill(lib, N=2) == SHAPE           # several sequences need cu_seqlens
+    assert _prefill(lib, H=0) == SHAPE
+    assert _prefill(lib, dk=64) == UNSUP
+    assert _prefill(lib, dk=128, dv=256) == UNSUP
+    assert _prefill(lib, ws=None) == WS
+    assert _prefill(lib, wsb=1024) == WS
+    assert _prefill(lib, q=P + 8) == ALIGN
+    assert _prefill(lib, Sf=P + 6 * GiB + 4) == ALIGN
+    assert _prefill(lib, cu=P + 9 * GiB + 2, N=2) == ALIGN
+    assert _prefill(lib, o=P + 16) == ALIAS             # o overlaps q
+    assert _prefill(lib, Sf=P + 2 * GiB) == ALIAS       # S_final overlaps v
+    assert _prefill(lib, ws=P + 5 * GiB + 256) == ALIAS  # workspace overlaps o
+    # S0 == S_final (in-place resume) is allowed to pass validation; a partial
+    # overlap is not
+    assert _prefill(lib, S0=P + 6 * GiB + 1024, Sf=P + 6 * GiB) == ALIAS
+
+
+def test_decode_rejects_bad_arguments(lib):
+    def dec(q=P, k=P + GiB, v=P + 2 * GiB, dt=0, a=P + 3 * GiB, b=P + 4 * GiB, B=4, H=2,
+            dk=128, dv=128, S=P + 5 * GiB, o=P + 6 * GiB):
+        return lib.rda_decode_step(q, k, v, dt, a, b, B, H, dk, dv, S, o, None)
+    assert dec(B=0) == OK                      # nothing to do: no launch
+    assert dec(S=None) == NULL
+    assert dec(dt=3) == DTYPE
+    assert dec(B=-1) == SHAPE
+    assert dec(dk=96) == UNSUP
+    assert dec(o=P + 4) == ALIGN
+    assert dec(o=P + 5 * GiB + 512) == ALIAS      # o inside S
+    assert dec(S=P + 2 * GiB) == ALIAS            # S over v
+
+
+def test_chunk_table_rejects_bad_arguments(lib):
+    assert lib.rda_chunk_table(None, 2, 10, P, P + GiB, P + 2 * GiB, None) == SHAPE
+    assert lib.rda_chunk_table(None, 1, -3, P, P + GiB, P + 2 * GiB, None) == SHAPE
+    assert lib.rda_chunk_table(None, 1, 10, P, None, P + 2 * GiB, None) == NULL
+    assert lib.rda_chunk_table(P + 2, 1, 10, P, P + GiB, P + 2 * GiB, None) == ALIGN
+
+
+def test_cu_seqlens_host_validation():
+    assert list(rda.check_cu_seqlens([0, 3, 3, 10], 10)) == [0, 3, 3, 10]
+    for bad, T in [([1, 10], 10), ([0, 5, 4, 10], 10), ([0, 9], 10), ([0], 0),
+                   (np.array([0.0, 10.0]), 10)]:
+        with pytest.raises((ValueError, TypeError)):
+            rda.check_cu_seqlens(bad, T)
+
+
+def test_table_reference_brute_force():
+    rng = np.random.default_rng(3)
+    for _ in range(50):
+        N = int(rng.integers(1, 9))
+        lens = rng.integers(0, 300, size=N)
+        cu = np.concatenate([[0], np.cumsum(lens)])
+        T = int(cu[-1])
+        rec, off, nch = table_ref.chunk_table(cu, N, T)
+        assert nch == sum(-(-int(x) // 64) for x in lens) <= table_ref.max_chunks(N, T)
+        covered = np.zeros(T, dtype=int)
+        for c in range(nch):
+            n, s, L, j = rec[c]
+            assert 1 <= L <= 64 and cu[n] <= s and s + L <= cu[n + 1] and s == cu[n] + 64 * j
+            covered[s:s + L] += 1
+        assert np.all(covered == 1)
+        assert np.all(rec[nch:, 0] == -1)

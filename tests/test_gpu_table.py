@@ -1,0 +1,60 @@
+"""The GPU chunk table equals the integer CPU reference bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import table_ref
+from gated_delta_amd import rda, synth
+from gpu_util import need_gpu, say, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return need_gpu()
+
+
+def check(cu, N, T, dev):
+    say(f"[table] N={N} T={T}")
+    cud = None if cu is None else torch.from_numpy(np.asarray(cu, np.int32)).to(dev)
+    rec, off, nch = rda.rda_chunk_table(cud, N, T, device=dev)
+    torch.cuda.synchronize()
+    rrec, roff, rn = table_ref.chunk_table(cu, N, T)
+    assert int(to_host(nch)[0]) == rn
+    assert np.array_equal(to_host(off), roff)
+    assert np.array_equal(to_host(rec), rrec)
+
+
+@pytest.mark.parametrize("T", [0, 1, 63, 64, 65, 16384])
+def test_single_sequence_null_offsets(dev, T):
+    check(None, 1, T, dev)
+
+
+def test_varlen_workload_table(dev):
+    L = synth.config4_lengths()
+    check(synth.cu_from_lengths(L), len(L), int(L.sum()), dev)
+
+
+def test_random_varlen_tables(dev):
+    rng = np.random.default_rng(300)
+    for trial in range(20):
+        N = int(rng.integers(1, 3000)) if trial % 5 == 0 else int(rng.integers(1, 40))
+        lens = rng.integers(0, 400, size=N) * (rng.random(N) > 0.2)
+        cu = synth.cu_from_lengths(lens)
+        check(cu, N, int(cu[-1]), dev)
+
+
+def test_malformed_offsets_stay_in_bounds(dev):
+    """Unvalidated, non-monotone offsets: the kernel clamps and caps, so the
+    table stays within its bound and every record lies inside [0, T)."""
+    T, N = 300, 4
+    cu = np.array([0, 290, 10, 300, 300], np.int32)
+    say("[table] malformed offsets")
+    cud = torch.from_numpy(cu).to(dev)
+    rec, off, nch = rda.rda_chunk_table(cud, N, T, device=dev)
+    torch.cuda.synchronize()
+    rec, n = to_host(rec), int(to_host(nch)[0])
+    assert 0 <= n <= table_ref.max_chunks(N, T)
+    for r in rec[:n]:
+        assert 0 <= r[0] < N and 0 <= r[1] and 1 <= r[2] <= 64 and r[1] + r[2] <= T
