@@ -1,0 +1,253 @@
+"""Benchmark of the RDA token mixer hot path on one MI355X.
+
+One step = one rda_prefill over the long-prompt workload (T = 16384 tokens,
+H = 16 heads, d = 128, bf16 q/k/v, fp32 gates, S0 ~ N(0, 0.02)) plus one
+rda_decode_step over the decode batch (B = 256 sequences x 16 heads, fp32
+128 x 128 states updated in place; step i uses the (i mod 128)-th of 128
+pre-drawn bf16 tokens).  Inputs are resident in HBM before the timed region.
+
+Prints ONE JSON line:
+  value      prefill tokens/s on the long-prompt workload (whole call)
+  decode     decode state bandwidth (algorithmic bytes / kernel time)
+  roofline   the kernel with the largest time per step, against its bound
+  kernels    every kernel's average duration (HIP events on its stream)
+  cpu_baseline  the fp64 oracle on the same prefill inputs, host cores
+  parity     rel-L2 / max-abs of this run's prefill output vs the oracle
+
+Usage: python bench.py [--gpus 1] [--steps 128] [--warmup 5] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("RDA prefill tokens/s (H=16,d=128,T=16384) + decode state HBM GB/s, 1 GPU")
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, vendor figure
+D = 128
+C = 64
+# Algorithmic work per unit (token-head for prefill, (batch, head) for decode)
+PREFILL_IN_BYTES = 3 * D * 2 + 2 * 4        # bf16 q, k, v + fp32 a, b   = 776
+PREFILL_OUT_BYTES = D * 4                   # fp32 o                     = 512
+PREFILL_BYTES = PREFILL_IN_BYTES + PREFILL_OUT_BYTES          # 1288
+STATE_BYTES = D * D * 4                     # one fp32 state             = 65536
+PREFILL_FLOPS = 6 * D * D + 5 * C * D + C * C // 3            # 140,629 (triangle-aware)
+DECODE_BYTES = 2 * STATE_BYTES + PREFILL_IN_BYTES + PREFILL_OUT_BYTES   # 132,360
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0 = all)")
+    ap.add_argument("--mode", choices=["bench", "prefill", "decode", "copy"], default="bench",
+                    help="prefill/decode: run only that part (for profiling); copy: a plain "
+                         "device copy of known size (counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "gated_delta_amd", "csrc", "*"))):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the summary is missing or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        line = line.strip()
+        if line and not line.startswith("#") and "=" in line:
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != kernel_source_hash():
+        return None
+    val = kv.get(f"{kernel}.bytes_per_launch")
+    return float(val) if val else None
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): the RDA "
+              "path here is a single-GPU kernel set; multi-GPU sharding is a design note, "
+              "not a runnable mode.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from gated_delta_amd import rda, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    if args.mode == "copy":
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n, "launches": 5}))
+        return
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # ---- inputs (host draw, then resident on the device) --------------------
+    t = time.time()
+    p = synth.config3()
+    T, H = p.total_tokens, p.num_heads
+    q = torch.from_numpy(p.q).to(torch.bfloat16).to(dev)
+    k = torch.from_numpy(p.k).to(torch.bfloat16).to(dev)
+    v = torch.from_numpy(p.v).to(torch.bfloat16).to(dev)
+    a = torch.from_numpy(p.a).to(dev)
+    b = torch.from_numpy(p.b).to(dev)
+    S0 = torch.from_numpy(p.S0).to(dev)
+    o = torch.empty((T, H, D), dtype=torch.float32, device=dev)
+    Sf = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(rda.rda_prefill_workspace_bytes(1, T, H), dtype=torch.uint8, device=dev)
+    log(f"prefill inputs ready ({time.time() - t:.1f}s)")
+
+    B, DH, NTOK = 256, 16, 128
+    do_decode = args.mode in ("bench", "decode")
+    do_prefill = args.mode in ("bench", "prefill")
+    if do_decode:
+        t = time.time()
+        S_dec = torch.from_numpy(synth.decode_state(B, DH)).to(dev)
+        toks = []
+        for i in range(NTOK):
+            x = synth.decode_step_inputs(i, B, DH)
+            toks.append(tuple(torch.from_numpy(getattr(x, n)).to(torch.bfloat16).to(dev)
+                              for n in "qkv") + (torch.from_numpy(x.a).to(dev),
+                                                 torch.from_numpy(x.b).to(dev)))
+        o_dec = torch.empty((B, DH, D), dtype=torch.float32, device=dev)
+        log(f"decode inputs ready ({time.time() - t:.1f}s)")
+
+    def make_events(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in evs:
+            e.record(stream)      # materialise the underlying HIP events
+        return evs
+
+    K, W = args.steps, args.warmup
+
+    def one_step(i, stage_ev=None, dec_ev=None):
+        if do_prefill:
+            rda.rda_prefill(q, k, v, a, b, S0=S0, o=o, S_final=Sf, workspace=ws,
+                            stage_events=stage_ev)
+        if do_decode:
+            qt, kt, vt, at, bt = toks[i % NTOK]
+            if dec_ev is not None:
+                dec_ev[0].record(stream)
+            rda.rda_decode_step(qt, kt, vt, at, bt, S_dec, o=o_dec)
+            if dec_ev is not None:
+                dec_ev[1].record(stream)
+
+    for i in range(W):
+        one_step(i)
+    torch.cuda.synchronize()
+
+    stage_evs = [make_events(2 * rda.RDA_NUM_STAGES) for _ in range(K)]
+    dec_evs = [make_events(2) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        one_step(W + i, stage_evs[i] if do_prefill else None, dec_evs[i] if do_decode else None)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    out = {"metric": METRIC, "n_gpus": 1, "steps": K, "warmup": W,
+           "ms_per_step": wall * 1e3 / K, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "RDA long-prompt prefill T=16384 H=16 d=128 (bf16 q/k/v, "
+                                  "fp32 gates, S0~N(0,0.02)) + RDA decode step B=256 H=16 "
+                                  "d=128 (fp32 states in place)",
+                      "prefill": {"T": T, "H": H, "d": D, "chunk": C, "qkv": "bf16",
+                                  "state": "fp32", "o": "fp32"},
+                      "decode": {"B": B, "H": DH, "d": D, "tokens_cycled": NTOK}}}
+
+    kernels = {}
+    if do_prefill:
+        st = np.array([[stage_evs[i][2 * s].elapsed_time(stage_evs[i][2 * s + 1])
+                        for s in range(rda.RDA_NUM_STAGES)] for i in range(K)])   # ms
+        call = np.array([stage_evs[i][0].elapsed_time(stage_evs[i][-1]) for i in range(K)])
+        units = T * H
+        call_s = float(np.mean(call)) * 1e-3
+        out["value"] = T / call_s
+        out["unit"] = "tokens/s"
+        out["prefill"] = {"ms_per_call": call_s * 1e3, "tokens_per_s": T / call_s,
+                          "hbm_roofline_tokens_per_s": PEAK_HBM_GBPS * 1e9 / (PREFILL_BYTES * H),
+                          "algorithmic_TFLOPs": PREFILL_FLOPS * units / call_s / 1e12,
+                          "mfma_frac_algorithmic": PREFILL_FLOPS * units / call_s / 1e12
+                          / PEAK_BF16_TFLOPS,
+                          "hbm_frac_algorithmic": (PREFILL_BYTES * units + 2 * H * STATE_BYTES)
+                          / call_s / 1e9 / PEAK_HBM_GBPS}
+        names = {0: "rda_chunk_table", 1: "rda_prep", 2: "rda_walk"}
+        kb = {0: 0.0, 1: PREFILL_IN_BYTES * units,
+              2: PREFILL_OUT_BYTES * units + 2 * H * STATE_BYTES}
+        for s in range(rda.RDA_NUM_STAGES):
+            ms = float(np.mean(st[:, s]))
+            kernels[names[s]] = {"avg_us": ms * 1e3, "alg_bytes": kb[s]}
+    if do_decode:
+        dms = np.array([dec_evs[i][0].elapsed_time(dec_evs[i][1]) for i in range(K)])
+        dsec = float(np.mean(dms)) * 1e-3
+        dbytes = DECODE_BYTES * B * DH
+        gbps = dbytes / dsec / 1e9
+        out["decode"] = {"value": gbps, "unit": "GB/s", "us_per_step": dsec * 1e6,
+                         "frac_of_peak": gbps / PEAK_HBM_GBPS, "bytes_per_step": dbytes,
+                         "tokens_per_s": B / dsec}
+        kernels["rda_decode_step"] = {"avg_us": dsec * 1e6, "alg_bytes": dbytes}
+        if "value" not in out:
+            out["value"], out["unit"] = gbps, "GB/s"
+    out["kernels"] = kernels
+
+    # roofline of the kernel with the largest time per step
+    dom = max(kernels, key=lambda n: kernels[n]["avg_us"])
+    kd = kernels[dom]
+    ach = kd["alg_bytes"] / (kd["avg_us"] * 1e-6) / 1e9
+    tr = read_traffic(dom)
+    out["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS,
+                       "unit": "GB/s", "frac": ach / PEAK_HBM_GBPS, "traffic": tr}
+
+    if do_prefill:
+        o_h = o.cpu().numpy().astype(np.float64)
+        S_h = Sf.cpu().numpy().astype(np.float64)
+    if do_prefill and not args.no_cpu:
+        import oracle
+        thr = oracle.threads_used(args.cpu_threads)
+        t = time.perf_counter()
+        ro, rS = oracle.prefill(p.q, p.k, p.v, p.a, p.b, S0=p.S0, threads=args.cpu_threads)
+        cpu_s = time.perf_counter() - t
+        out["cpu_baseline"] = {"value": T / cpu_s, "unit": "tokens/s", "cores": thr,
+                               "kind": "oracle",
+                               "sample": f"the full long-prompt prefill (T={T}, H={H}, d={D}, "
+                                         f"fp64 sequential recurrence, OpenMP over the {H} "
+                                         f"heads), {cpu_s:.1f} s on {os.cpu_count()} visible "
+                                         "host CPUs"}
+        out["parity"] = {"o_rel_l2": float(np.linalg.norm(o_h - ro) / np.linalg.norm(ro)),
+                         "o_max_abs": float(np.max(np.abs(o_h - ro))),
+                         "S_rel_l2": float(np.linalg.norm(S_h - rS) / np.linalg.norm(rS))}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

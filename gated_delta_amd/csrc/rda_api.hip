@@ -135,15 +135,15 @@ rda_status rda_prefill_profiled(const void* q, const void* k, const void* v, rda
 
     if ((st = record(stage_events, 2 * RDA_STAGE_PREP, stream)) != RDA_OK) return st;
     if (mc > 0 && total_tokens > 0) {
-        if (launch_prep(q, k, v, qkv_dtype, a, b, num_heads, mc, rec, nch, factors, stream) !=
+        if (launch_prep(q, k, qkv_dtype, a, b, num_heads, mc, rec, nch, factors, stream) !=
             hipSuccess)
             return RDA_ERR_HIP;
     }
     if ((st = record(stage_events, 2 * RDA_STAGE_PREP + 1, stream)) != RDA_OK) return st;
 
     if ((st = record(stage_events, 2 * RDA_STAGE_WALK, stream)) != RDA_OK) return st;
-    if (launch_walk(qkv_dtype, num_seqs, num_heads, rec, seq_off, nch, factors, S0, o, S_final,
-                    stream) != hipSuccess)
+    if (launch_walk(q, k, v, qkv_dtype, num_seqs, num_heads, rec, seq_off, nch, factors, S0, o,
+                    S_final, stream) != hipSuccess)
         return RDA_ERR_HIP;
     if ((st = record(stage_events, 2 * RDA_STAGE_WALK + 1, stream)) != RDA_OK) return st;
     return RDA_OK;

@@ -32,6 +32,19 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) 
     lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Split two fp32 values into packed bf16 hi and lo pairs (element 0 in the
+// low half): hi = bf16(x), lo = bf16(x - hi), both round-to-nearest-even.
+// Compiles to two v_cvt_pk_bf16_f32 plus four VALU ops for the pair.
+__device__ __forceinline__ void split_pk(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+    const f32x2 v = {x0, x1};
+    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    const f32x2 hf = {__uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u)};
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(v - hf, bf16x2));
+}
+
 // Sum over each 16-lane row of the wavefront with DPP (every lane of the
 // row receives the row's sum): xor 1, xor 2 (quad permutes), then the half-
 // and full-row mirrors pair up quads and half rows.

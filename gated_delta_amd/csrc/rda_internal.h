@@ -21,25 +21,20 @@ constexpr int kD = RDA_HEAD_DIM;   // dk = dv
 //               int32 seq_off[num_seqs+1]  first chunk of each sequence
 //               int32 num_chunks[1]
 //   [factors]   per (chunk, head), kChunkHeadBytes each, chunk-major:
-//                 Wpk  bf16 hi/lo of W, packed as the walk's MFMA A operand
-//                 Qpk  bf16 hi/lo of Q' = diag(gamma) Q - A W, same packing
-//                 Up   fp32 U' = T diag(b) V, in the walk's accumulator order
-//                 Op   fp32 O' = A U', same order
-//                 Kt   bf16 K^T packed as the walk's state-update A operand
-//                      (second plane: lo parts, used for fp32 inputs only)
-//                 gsc  fp32 gamma_C / gamma_i for i < 64, then gamma_C
+//                 Tb   bf16 hi/lo of T diag(b), T = (I + L)^-1, packed as the
+//                      walk's MFMA A operand (rows = tokens, K dim = tokens)
+//                 Am   bf16 hi/lo of A = lower(Q K^T . Gamma), same packing
+//                 G    fp32 gamma_i (64), gamma_C / gamma_i (64), gamma_C
 // ---------------------------------------------------------------------------
-constexpr size_t kPackBytes = size_t(kC) * kD * 2 * 2;   // hi + lo bf16, 64 x 128
-constexpr size_t kF32Bytes = size_t(kC) * kD * 4;        // 64 x 128 fp32
-constexpr size_t kKtBytes = size_t(kC) * kD * 2 * 2;     // 64 x 128 bf16, hi and lo planes
-constexpr size_t kGscBytes = 512;                        // 65 floats, padded
-constexpr size_t kOffW = 0;
-constexpr size_t kOffQ = kOffW + kPackBytes;
-constexpr size_t kOffU = kOffQ + kPackBytes;
-constexpr size_t kOffO = kOffU + kF32Bytes;
-constexpr size_t kOffK = kOffO + kF32Bytes;
-constexpr size_t kOffG = kOffK + kKtBytes;
-constexpr size_t kChunkHeadBytes = kOffG + kGscBytes;
+constexpr size_t kPackBytes = size_t(kC) * kC * 2 * 2;   // hi + lo bf16, 64 x 64
+constexpr size_t kGBytes = 1024;
+constexpr size_t kOffTb = 0;
+constexpr size_t kOffA = kOffTb + kPackBytes;
+constexpr size_t kOffG = kOffA + kPackBytes;
+constexpr size_t kChunkHeadBytes = kOffG + kGBytes;
+constexpr int kGGam = 0;     // float offsets inside G
+constexpr int kGScale = 64;
+constexpr int kGC = 128;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -67,12 +62,13 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, rda_dtype 
                          const float* a, const float* b, int32_t batch, int32_t heads,
                          float* S, float* o, hipStream_t stream);
 
-hipError_t launch_prep(const void* q, const void* k, const void* v, rda_dtype dt,
+hipError_t launch_prep(const void* q, const void* k, rda_dtype dt,
                        const float* a, const float* b, int32_t heads, int32_t max_chunks,
                        const int32_t* rec, const int32_t* num_chunks, unsigned char* factors,
                        hipStream_t stream);
 
-hipError_t launch_walk(rda_dtype dt, int32_t num_seqs, int32_t heads, const int32_t* rec,
+hipError_t launch_walk(const void* q, const void* k, const void* v, rda_dtype dt,
+                       int32_t num_seqs, int32_t heads, const int32_t* rec,
                        const int32_t* seq_off, const int32_t* num_chunks,
                        const unsigned char* factors, const float* S0, float* o, float* S_final,
                        hipStream_t stream);

@@ -4,32 +4,33 @@
 // prediction for the key, beta-weighted write, read-out after the update; the
 // "Raon-1 nano" teardown, section "The other 1.5B: a hybrid built to forget")
 // is evaluated in chunks of C = 64 tokens.  With S the state entering a chunk
-// (rows = value channels), g_i the in-chunk running sum of log a and
-// gamma_i = exp(g_i):
+// (rows = value channels), g_i the in-chunk running sum of log a,
+// gamma_i = exp(g_i), Gamma = diag(gamma) and Gamma_ij = exp(g_i - g_j):
 //
-//   L     = strict-lower( diag(b) K K^T * Gamma ),  Gamma_ij = exp(g_i - g_j)
-//   T     = (I + L)^-1
-//   W     = T diag(b gamma) K ,   U' = T diag(b) V
-//   A     = lower( Q K^T * Gamma )
-//   Q'    = diag(gamma) Q - A W ,  O' = A U'
-//   U     = U' - W S^T                      (the errors each token writes)
-//   O     = O' + Q' S^T
+//   L     = strict-lower( diag(b) K K^T . Gamma_ij ),   T = (I + L)^-1
+//   T_b   = T diag(b)
+//   A     = lower( Q K^T . Gamma_ij )
+//   U     = T_b V - T_b Gamma (K S^T)             (the errors each token writes)
+//   O     = Gamma (Q S^T) + A U                   (outputs of the chunk's tokens)
 //   S_out = gamma_C S + U^T diag(gamma_C / gamma) K
 //
-// which reproduces the token-by-token recurrence exactly in real arithmetic.
-// Everything not involving S is independent per chunk: the PREP kernel
-// computes it for all (chunk, head) pairs in parallel and stores W, Q', U',
-// O', K and the decay factors in MFMA-ready packed layouts.  The WALK kernel
-// then runs the S-dependent part, chunk after chunk, with the state held in
-// MFMA accumulator registers: each workgroup owns 16 value channels of one
-// (sequence, head) (rows of S evolve independently, so the 8 slices need no
-// communication).  Per chunk a walk workgroup does two dependent MFMA GEMMs:
-//   X  = [W ; Q'] S_slice^T   (128 x 16, K = 128)
-//   S_slice^T = gamma_C S_slice^T + K^T (diag(gamma_C / gamma) U)   (K = 64)
+// This is the WY / UT-transform form of the gated delta rule (W = T_b Gamma K
+// and U' = T_b V are never formed: the walk multiplies through T_b instead),
+// and it reproduces the token-by-token recurrence exactly in real arithmetic.
+//
+// PREP (parallel over chunk x head): gates, Gram tiles K K^T and Q K^T on
+// MFMA, the unit-lower-triangular solve for T in fp32, then T_b and A packed
+// as bf16 hi/lo MFMA operands (33 KiB per chunk-head in the workspace).
+// WALK (sequential over the chunks of a sequence): one workgroup per
+// (sequence, head, 16-channel value slice); the fp32 state slice lives in
+// MFMA accumulators, and each chunk costs three dependent MFMA stages
+// (Y = K S^T, X = T_b Gamma Y, S update) over the raw bf16 q, k, v tiles and
+// the two packed 64 x 64 factors.  Rows of S evolve independently, so the 8
+// slices of a head need no communication.
 //
 // Precision: q, k, v enter MFMA as exact bf16 (fp32 inputs as bf16 hi + lo).
-// Every computed fp32 operand (T, A, W, Q', S, U) is fed as a bf16 hi + lo
-// pair, and products take hi*hi + hi*lo + lo*hi, i.e. ~2^-16 relative
+// Every computed fp32 operand (T_b, A, S, Gamma Y, U) is fed as a bf16 hi +
+// lo pair, and products take hi*hi + hi*lo + lo*hi, i.e. ~2^-16 relative
 // accuracy with fp32 accumulation.  The triangular solve and all gate
 // arithmetic run in fp32; decay factors are formed only as exp of
 // differences g_i - g_j <= 0, so nothing overflows.
@@ -58,20 +59,22 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u16x8 x) { return __builtin_bit_cast(bf16x8, x); }
 
-// Split 8 fp32 values into bf16 hi and lo vectors.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Split 8 fp32 values into bf16 hi and lo vectors (paired conversions).
 __device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
-    u16x8 h, l;
+    u32x4 h, l;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        uint16_t a, b;
-        split_bf16(x[j], a, b);
-        h[j] = a;
-        l[j] = b;
+    for (int p = 0; p < 4; ++p) {
+        uint32_t a, b;
+        split_pk(x[2 * p], x[2 * p + 1], a, b);
+        h[p] = a;
+        l[p] = b;
     }
-    hi = as_bf16x8(h);
-    lo = as_bf16x8(l);
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
@@ -81,24 +84,19 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 // ---------------------------------------------------------------------------
 constexpr int kTS = 136;   // bf16 tile row stride (elements): 272 B, spreads LDS banks
 constexpr int kFS = 68;    // fp32 64x64 matrix row stride
-constexpr int kXS = 132;   // fp32 64x128 staging row stride
 constexpr int kTileB = kC * kTS * 2;   // 17408 B
 constexpr int kMatB = kC * kFS * 4;    // 17408 B
 
-// LDS layout (bytes).  Ks and Ls are adjacent so the fp32 64 x 128 staging
-// buffer Xs can reuse both once K and L are dead.
 constexpr int kSmK = 0;
-constexpr int kSmL = kSmK + kTileB;
-constexpr int kSmQ = kSmL + kMatB;
-constexpr int kSmV = kSmQ + kTileB;
-constexpr int kSmA = kSmV + kTileB;
+constexpr int kSmQ = kSmK + kTileB;
+constexpr int kSmL = kSmQ + kTileB;
+constexpr int kSmA = kSmL + kMatB;
 constexpr int kSmT = kSmA + kMatB;
-constexpr int kSmG = kSmT + kMatB;           // la, bb, gg, gam, bgam: 5 x 64 floats
-constexpr int kSmR = kSmG + 5 * 64 * 4;      // 3 x 16x16 fp32 solve scratch
-constexpr int kSmLo = kSmR + 3 * 256 * 4;    // lo planes of K, Q, V (fp32 inputs only)
+constexpr int kSmG = kSmT + kMatB;           // la, bb, gg, gam: 4 x 64 floats
+constexpr int kSmR = kSmG + 4 * 64 * 4;      // 3 x 16x16 fp32 solve scratch
+constexpr int kSmLo = kSmR + 3 * 256 * 4;    // lo planes of K, Q (fp32 inputs only)
 constexpr int kPrepSmemBf16 = kSmLo;
-constexpr int kPrepSmemSplit = kSmLo + 3 * kTileB;
-static_assert(kC * kXS * 4 <= kTileB + kMatB, "staging buffer must fit over K and L");
+constexpr int kPrepSmemSplit = kSmLo + 2 * kTileB;
 
 template <bool kSplit>
 struct PrepIn;
@@ -145,30 +143,41 @@ __device__ __forceinline__ void stage_tile(const typename PrepIn<kSplit>::T* __r
     }
 }
 
-// 8 bf16 of column `col` for rows r0 .. r0+7 of a row-major bf16 tile.
-__device__ __forceinline__ bf16x8 column8(const uint16_t* tile, int r0, int col) {
-    u16x8 x;
+// Pack rows of a 64 x 64 fp32 matrix (columns scaled by `colscale` when
+// given) as bf16 hi/lo A operands for the walk: slot (row tile w, token
+// block m, lane) holds row 16w + (lane % 16), columns {32m + 4g + i,
+// 32m + 16 + 4g + i} with g = lane / 16; hi at [(w*2+m)*2][lane], lo after it.
+__device__ __forceinline__ void pack_rows(const float* M, const float* colscale, bf16x8* dst,
+                                          int tid) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = tile[(r0 + j) * kTS + col];
-    return as_bf16x8(x);
-}
-
-// Column `col`, rows {r0 + i, r0 + 16 + i : i < 4} (the permuted token order).
-__device__ __forceinline__ bf16x8 column8_perm(const uint16_t* tile, int r0, int col) {
-    u16x8 x;
+    for (int qq = 0; qq < 2; ++qq) {
+        const int slot = tid + 256 * qq;
+        const int lp = slot & 63, m = (slot >> 6) & 1, wp = slot >> 7;
+        const int r = 16 * wp + (lp & 15), c0 = 32 * m + 4 * (lp >> 4);
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(M + r * kFS + c0);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(M + r * kFS + c0 + 16);
+        float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        if (colscale) {
+            const f32x4 s0 = *reinterpret_cast<const f32x4*>(colscale + c0);
+            const f32x4 s1 = *reinterpret_cast<const f32x4*>(colscale + c0 + 16);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        x[i] = tile[(r0 + i) * kTS + col];
-        x[4 + i] = tile[(r0 + 16 + i) * kTS + col];
+            for (int j = 0; j < 4; ++j) {
+                x[j] *= s0[j];
+                x[4 + j] *= s1[j];
+            }
+        }
+        bf16x8 hi, lo;
+        split8(x, hi, lo);
+        const int base = ((wp * 2 + m) * 2) * 64 + lp;
+        dst[base] = hi;
+        dst[base + 64] = lo;
     }
-    return as_bf16x8(x);
 }
 
 template <bool kSplit>
 __global__ __launch_bounds__(256) void prep_kernel(
     const typename PrepIn<kSplit>::T* __restrict__ q, const typename PrepIn<kSplit>::T* __restrict__ k,
-    const typename PrepIn<kSplit>::T* __restrict__ v, const float* __restrict__ a,
-    const float* __restrict__ b, int H, const int32_t* __restrict__ rec,
+    const float* __restrict__ a, const float* __restrict__ b, int H, const int32_t* __restrict__ rec,
     const int32_t* __restrict__ num_chunks, unsigned char* __restrict__ factors) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[kSplit ? kPrepSmemSplit : kPrepSmemBf16];
     const int chunk = blockIdx.x / H;
@@ -182,62 +191,56 @@ __global__ __launch_bounds__(256) void prep_kernel(
 
     uint16_t* Ks = reinterpret_cast<uint16_t*>(smem + kSmK);
     uint16_t* Qs = reinterpret_cast<uint16_t*>(smem + kSmQ);
-    uint16_t* Vs = reinterpret_cast<uint16_t*>(smem + kSmV);
     uint16_t* Kl = reinterpret_cast<uint16_t*>(smem + kSmLo);
     uint16_t* Ql = Kl + kC * kTS;
-    uint16_t* Vl = Ql + kC * kTS;
     float* Ls = reinterpret_cast<float*>(smem + kSmL);
     float* As = reinterpret_cast<float*>(smem + kSmA);
     float* Ts = reinterpret_cast<float*>(smem + kSmT);
-    float* Xs = reinterpret_cast<float*>(smem + kSmK);   // aliases Ks + Ls
     float* la = reinterpret_cast<float*>(smem + kSmG);
     float* bb = la + 64;
     float* gg = bb + 64;
     float* gam = gg + 64;
-    float* bgam = gam + 64;
     float* Rs = reinterpret_cast<float*>(smem + kSmR);
 
     unsigned char* F = factors + (size_t(chunk) * H + h) * kChunkHeadBytes;
 
-    // ---- stage inputs; zero T and the upper blocks of A -------------------
+    // ---- stage inputs; zero T and A (their upper triangles stay zero) ------
     stage_tile<kSplit>(k, t0, len, H, h, Ks, Kl, tid);
     stage_tile<kSplit>(q, t0, len, H, h, Qs, Ql, tid);
-    stage_tile<kSplit>(v, t0, len, H, h, Vs, Vl, tid);
     for (int e = tid; e < kC * kFS; e += 256) {
         Ts[e] = 0.f;
         As[e] = 0.f;
     }
     if (w == 0) {
-        // gates: log a (clamped far below any fp32-visible decay), prefix sum
+        // gates: log a (clamped far below any fp32-visible decay), prefix sum;
+        // rows past the chunk's end act as a = 1, b = 0 (inert)
         float lav = 0.f, bv = 0.f;
         if (l < len) {
             const size_t th = size_t(t0 + l) * H + h;
             lav = fmaxf(logf(a[th]), -100.f);
             bv = b[th];
         }
-        float s = lav;
+        float sum = lav;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-            const float o = __shfl_up(s, off, 64);
-            if (l >= off) s += o;
+            const float o = __shfl_up(sum, off, 64);
+            if (l >= off) sum += o;
         }
         la[l] = lav;
         bb[l] = bv;
-        gg[l] = s;
-        const float gm = expf(s);
-        gam[l] = gm;
-        bgam[l] = bv * gm;
+        gg[l] = sum;
+        gam[l] = expf(sum);
     }
     __syncthreads();
 
     // ---- Gram tiles: L = strict-lower(diag(b) K K^T . Gamma), A = lower(Q K^T . Gamma)
     {
-        const int8_t tri[10][2] = {{0, 0}, {1, 0}, {1, 1}, {2, 0}, {2, 1},
-                                   {2, 2}, {3, 0}, {3, 1}, {3, 2}, {3, 3}};
         for (int task = w; task < 20; task += 4) {
+            // lower-triangular tile (ti, tj), ti >= tj, enumerated row by row
             const bool isq = task >= 10;
-            const int ti = tri[isq ? task - 10 : task][0];
-            const int tj = tri[isq ? task - 10 : task][1];
+            const int idx = isq ? task - 10 : task;
+            const int ti = (idx >= 1) + (idx >= 3) + (idx >= 6);
+            const int tj = idx - ti * (ti + 1) / 2;
             const uint16_t* X = isq ? Qs : Ks;
             const uint16_t* Xl = isq ? Ql : Kl;
             f32x4 acc = zero4();
@@ -324,276 +327,447 @@ __global__ __launch_bounds__(256) void prep_kernel(
         __syncthreads();
     }
 
-    // ---- W = T diag(b gamma) K  (wave w: key tiles 2w, 2w+1; all token tiles)
-    f32x4 accW[4][2];
-#pragma unroll
-    for (int ti = 0; ti < 4; ++ti) accW[ti][0] = accW[ti][1] = zero4();
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        const int r0 = 32 * m + 8 * g;
-        bf16x8 bkh[2], bkl[2];
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            bkh[jj] = column8(Ks, r0, 16 * (2 * w + jj) + c);
-            if constexpr (kSplit) bkl[jj] = column8(Kl, r0, 16 * (2 * w + jj) + c);
-        }
-        const f32x4 s0 = *reinterpret_cast<const f32x4*>(bgam + r0);
-        const f32x4 s1 = *reinterpret_cast<const f32x4*>(bgam + r0 + 4);
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-            const f32x4 t0v = *reinterpret_cast<const f32x4*>(Ts + (16 * ti + c) * kFS + r0);
-            const f32x4 t1v = *reinterpret_cast<const f32x4*>(Ts + (16 * ti + c) * kFS + r0 + 4);
-            float x[8];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                x[j] = t0v[j] * s0[j];
-                x[4 + j] = t1v[j] * s1[j];
-            }
-            bf16x8 ah, al;
-            split8(x, ah, al);
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                accW[ti][jj] = mfma_bf16(ah, bkh[jj], accW[ti][jj]);
-                accW[ti][jj] = mfma_bf16(al, bkh[jj], accW[ti][jj]);
-                if constexpr (kSplit) accW[ti][jj] = mfma_bf16(ah, bkl[jj], accW[ti][jj]);
-            }
-        }
-    }
-
-    // ---- K^T packed for the walk's state update (reads Ks before it is reused)
-    {
-        uint16_t* Kt = reinterpret_cast<uint16_t*>(F + kOffK);
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-            const int slot = tid + 256 * qq;
-            const int lp = slot & 63, mp = (slot >> 6) & 1, kt = slot >> 7;
-            const int col = 16 * kt + (lp & 15), r0 = 32 * mp + 4 * (lp >> 4);
-            *reinterpret_cast<bf16x8*>(Kt + slot * 8) = column8_perm(Ks, r0, col);
-            if constexpr (kSplit)
-                *reinterpret_cast<bf16x8*>(Kt + kC * kD + slot * 8) = column8_perm(Kl, r0, col);
-        }
-    }
-
-    // ---- Q' = diag(gamma) Q - A W -------------------------------------------
-    f32x4 accQ[4][2];
-    {
-        bf16x8 bwh[2][2], bwl[2][2];
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                float x[8];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    x[i] = accW[2 * m][jj][i];
-                    x[4 + i] = accW[2 * m + 1][jj][i];
-                }
-                split8(x, bwh[m][jj], bwl[m][jj]);
-            }
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-            accQ[ti][0] = accQ[ti][1] = zero4();
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const float* arow = As + (16 * ti + c) * kFS + 32 * m + 4 * g;
-                const f32x4 a0 = *reinterpret_cast<const f32x4*>(arow);
-                const f32x4 a1 = *reinterpret_cast<const f32x4*>(arow + 16);
-                float x[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-                bf16x8 ah, al;
-                split8(x, ah, al);
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    accQ[ti][jj] = mfma_bf16(ah, bwh[m][jj], accQ[ti][jj]);
-                    accQ[ti][jj] = mfma_bf16(ah, bwl[m][jj], accQ[ti][jj]);
-                    accQ[ti][jj] = mfma_bf16(al, bwh[m][jj], accQ[ti][jj]);
-                }
-            }
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * ti + 4 * g + i, kc = 16 * (2 * w + jj) + c;
-                    float qv = bf16_bits_to_f32(Qs[r * kTS + kc]);
-                    if constexpr (kSplit) qv += bf16_bits_to_f32(Ql[r * kTS + kc]);
-                    accQ[ti][jj][i] = gam[r] * qv - accQ[ti][jj][i];
-                }
-        }
-    }
-    __syncthreads();   // every wavefront is done with Ks and Ls
-
-    // ---- pack W and Q' for the walk through the fp32 staging buffer ----------
-#pragma unroll
-    for (int which = 0; which < 2; ++which) {
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    Xs[(16 * ti + 4 * g + i) * kXS + 16 * (2 * w + jj) + c] =
-                        which == 0 ? accW[ti][jj][i] : accQ[ti][jj][i];
-        __syncthreads();
-        uint16_t* P = reinterpret_cast<uint16_t*>(F + (which == 0 ? kOffW : kOffQ));
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-            const int slot = tid + 256 * qq;   // (w', m, lane)
-            const int lp = slot & 63, m = (slot >> 6) & 3, wp = slot >> 8;
-            const float* row = Xs + (16 * wp + (lp & 15)) * kXS + 32 * m + 4 * (lp >> 4);
-            const f32x4 x0 = *reinterpret_cast<const f32x4*>(row);
-            const f32x4 x1 = *reinterpret_cast<const f32x4*>(row + 16);
-            float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-            bf16x8 hi, lo;
-            split8(x, hi, lo);
-            const int base = ((wp * 4 + m) * 2) * 64 + lp;
-            *reinterpret_cast<bf16x8*>(P + base * 8) = hi;
-            *reinterpret_cast<bf16x8*>(P + (base + 64) * 8) = lo;
-        }
-        __syncthreads();
-    }
-
-    // ---- U' = T diag(b) V and O' = A U'  (wave w: value tiles 2w, 2w+1) -------
-    {
-        f32x4 accU[4][2];
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) accU[ti][0] = accU[ti][1] = zero4();
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int r0 = 32 * m + 8 * g;
-            bf16x8 bvh[2], bvl[2];
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                bvh[jj] = column8(Vs, r0, 16 * (2 * w + jj) + c);
-                if constexpr (kSplit) bvl[jj] = column8(Vl, r0, 16 * (2 * w + jj) + c);
-            }
-            const f32x4 s0 = *reinterpret_cast<const f32x4*>(bb + r0);
-            const f32x4 s1 = *reinterpret_cast<const f32x4*>(bb + r0 + 4);
-#pragma unroll
-            for (int ti = 0; ti < 4; ++ti) {
-                const f32x4 t0v = *reinterpret_cast<const f32x4*>(Ts + (16 * ti + c) * kFS + r0);
-                const f32x4 t1v = *reinterpret_cast<const f32x4*>(Ts + (16 * ti + c) * kFS + r0 + 4);
-                float x[8];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    x[j] = t0v[j] * s0[j];
-                    x[4 + j] = t1v[j] * s1[j];
-                }
-                bf16x8 ah, al;
-                split8(x, ah, al);
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    accU[ti][jj] = mfma_bf16(ah, bvh[jj], accU[ti][jj]);
-                    accU[ti][jj] = mfma_bf16(al, bvh[jj], accU[ti][jj]);
-                    if constexpr (kSplit) accU[ti][jj] = mfma_bf16(ah, bvl[jj], accU[ti][jj]);
-                }
-            }
-        }
-        f32x4* Up = reinterpret_cast<f32x4*>(F + kOffU);
-        f32x4* Op = reinterpret_cast<f32x4*>(F + kOffO);
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) Up[((2 * w + jj) * 4 + ti) * 64 + l] = accU[ti][jj];
-
-        bf16x8 buh[2][2], bul[2][2];
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                float x[8];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    x[i] = accU[2 * m][jj][i];
-                    x[4 + i] = accU[2 * m + 1][jj][i];
-                }
-                split8(x, buh[m][jj], bul[m][jj]);
-            }
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-            f32x4 accO[2] = {zero4(), zero4()};
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const float* arow = As + (16 * ti + c) * kFS + 32 * m + 4 * g;
-                const f32x4 a0 = *reinterpret_cast<const f32x4*>(arow);
-                const f32x4 a1 = *reinterpret_cast<const f32x4*>(arow + 16);
-                float x[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-                bf16x8 ah, al;
-                split8(x, ah, al);
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    accO[jj] = mfma_bf16(ah, buh[m][jj], accO[jj]);
-                    accO[jj] = mfma_bf16(ah, bul[m][jj], accO[jj]);
-                    accO[jj] = mfma_bf16(al, buh[m][jj], accO[jj]);
-                }
-            }
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) Op[((2 * w + jj) * 4 + ti) * 64 + l] = accO[jj];
-        }
-    }
-
-    // ---- decay factors gamma_C / gamma_i = exp(g_C - g_i), and gamma_C --------
+    // ---- outputs: T_b = T diag(b) and A as packed hi/lo operands; gates ----
+    pack_rows(Ts, bb, reinterpret_cast<bf16x8*>(F + kOffTb), tid);
+    pack_rows(As, nullptr, reinterpret_cast<bf16x8*>(F + kOffA), tid);
     if (tid < 64) {
-        float* gs = reinterpret_cast<float*>(F + kOffG);
-        gs[tid] = expf(gg[63] - gg[tid]);
-        if (tid == 0) gs[64] = gam[63];
+        float* G = reinterpret_cast<float*>(F + kOffG);
+        G[kGGam + tid] = gam[tid];
+        G[kGScale + tid] = expf(gg[63] - gg[tid]);
+        if (tid == 0) G[kGC] = gam[63];
     }
 }
 
 // ---------------------------------------------------------------------------
-// WALK: one 256-thread workgroup per (sequence, head, 16-channel value slice).
+// WALK: one workgroup per (sequence, head, 16-channel value slice), 8 waves.
+//
+// Wave w owns the 16 x 16 tile of S^T with keys 16w .. 16w+15 (an MFMA
+// accumulator).  Waves 0..3 ("state waves") carry the state-critical chain,
+// waves 4..7 ("output waves") the outputs; token tile tt = w % 4.  Per chunk:
+//   P1  every wave publishes its state tile (bf16 hi/lo) to LDS; state waves
+//       store their 16 rows of the K tile and V slice, output waves their 16
+//       rows of the Q tile (all loaded a chunk ahead with coalesced loads).
+//   P2  state waves: Y = K S^T for token tile tt, Gamma Y (hi/lo) to LDS, and
+//       U' = T_b V;  output waves: Z = Q S^T.  Every wave also fetches its K^T
+//       operand for P4 with transposing LDS reads.
+//   P3  state waves: X = T_b (Gamma Y), U = U' - X, and U and
+//       U~ = diag(gamma_C / gamma) U (hi/lo) to LDS.
+//   P4  every wave: S^T = gamma_C S^T + K^T U~ for its key tile;
+//       output waves: O = Gamma Z + A U, stored.
+// Three barriers per chunk.  Global operands of the chunk after next are
+// loaded as soon as the current chunk has consumed them (two operand sets,
+// ping-pong), with unconditional, clamped, in-bounds addresses so the
+// compiler's load counters stay exact.
 // ---------------------------------------------------------------------------
+constexpr int kWalkWaves = 8;
+constexpr int kWalkThreads = kWalkWaves * 64;
+constexpr int kKS = 136;   // LDS K / Q tile row stride (bf16 elements)
+constexpr int kVS = 20;    // LDS V slice row stride (bf16 elements)
+
+template <typename TIn>
+struct WalkIn;
+template <>
+struct WalkIn<uint16_t> { static constexpr bool kSplit = false; };
+template <>
+struct WalkIn<float> { static constexpr bool kSplit = true; };
+
+// Global operands of one chunk for one wave (state-independent).
+template <bool kSplit>
 struct WalkOps {
-    bf16x8 wh[4], wl[4], qh[4], ql[4];   // A operands of [W ; Q'], k-blocks 0..3
-    f32x4 up, op;                        // U', O' for this lane's 4 tokens
-    bf16x8 kt[2][2];                     // K^T A operands: key tile 2w+j, token block m
-    bf16x8 ktl[2][2];                    // lo planes (fp32 inputs only)
-    f32x4 gs;                            // gamma_C / gamma for this lane's 4 tokens
-    float gC;
-    int t0, len;
+    // raw rows 16tt + 4i + l/16 (i < 4), elements 8(l%16) .. +7 of the K
+    // tile (state waves) or Q tile (output waves): 8 bf16, or 8 floats for
+    // fp32 inputs.  Masking and conversion happen at staging time so that the
+    // loads are never waited on where they are issued.
+    u32x4 rows[4][kSplit ? 2 : 1];
+    u32x4 vrow;                   // V slice: row 16tt + l/4, channels 4(l%4) .. +3 (state waves)
+    bf16x8 ah[2], al[2];          // T_b (state waves) or A (output waves), token blocks 0, 1
+    f32x4 gam;                    // gamma of this lane's 4 tokens (16tt + 4g + i)
+    f32x4 gs;                     // gamma_C / gamma of the same tokens (state waves)
+    float gC;                     // gamma_C
+    int t0, len;                  // first token and valid length of the chunk
 };
 
-template <bool kSplit>
-__device__ __forceinline__ void walk_load(WalkOps& o, const unsigned char* __restrict__ factors,
-                                          const int32_t* __restrict__ rec, int chunk, int H, int h,
-                                          int s, int w, int l) {
-    const unsigned char* F = factors + (size_t(chunk) * H + h) * kChunkHeadBytes;
-    const bf16x8* Wp = reinterpret_cast<const bf16x8*>(F + kOffW);
-    const bf16x8* Qp = reinterpret_cast<const bf16x8*>(F + kOffQ);
+template <typename TIn>
+struct WalkCtx {
+    const TIn* q;
+    const TIn* k;
+    const TIn* v;
+    const unsigned char* factors;
+    const int32_t* rec;
+    int H, h, s, w, l;
+};
+
+template <typename TIn>
+__device__ __forceinline__ const unsigned char* chunk_factors(const WalkCtx<TIn>& x, int chunk) {
+    return x.factors + (size_t(chunk) * x.H + x.h) * kChunkHeadBytes;
+}
+
+// Coalesced rows of the K (state waves) or Q (output waves) tile: instruction
+// i covers rows 16tt + 4i .. +3 (256 contiguous bytes each for bf16).  Rows
+// past the chunk's end read a valid row; stage_rows zeroes them.
+template <typename TIn>
+__device__ __forceinline__ void load_rows(WalkOps<WalkIn<TIn>::kSplit>& o, const WalkCtx<TIn>& x,
+                                          int chunk) {
+    const int t0 = x.rec[4 * chunk + 1], len = x.rec[4 * chunk + 2];
+    const TIn* src = x.w < 4 ? x.k : x.q;
+    const int tt = x.w & 3;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int base = ((w * 4 + m) * 2) * 64 + l;
-        o.wh[m] = Wp[base];
-        o.wl[m] = Wp[base + 64];
-        o.qh[m] = Qp[base];
-        o.ql[m] = Qp[base + 64];
+    for (int i = 0; i < 4; ++i) {
+        const int r = 16 * tt + 4 * i + (x.l >> 4);
+        const TIn* p = src + ((size_t(t0) + (r < len ? r : len - 1)) * x.H + x.h) * kD + 8 * (x.l & 15);
+        o.rows[i][0] = *reinterpret_cast<const u32x4*>(p);
+        if constexpr (WalkIn<TIn>::kSplit) o.rows[i][1] = *reinterpret_cast<const u32x4*>(p + 4);
     }
-    o.up = reinterpret_cast<const f32x4*>(F + kOffU)[(s * 4 + w) * 64 + l];
-    o.op = reinterpret_cast<const f32x4*>(F + kOffO)[(s * 4 + w) * 64 + l];
-    const bf16x8* Kt = reinterpret_cast<const bf16x8*>(F + kOffK);
+}
+
+// V slice rows (state waves); stage_rows zeroes rows past the chunk's end
+template <typename TIn>
+__device__ __forceinline__ void load_v(WalkOps<WalkIn<TIn>::kSplit>& o, const WalkCtx<TIn>& x,
+                                       int chunk) {
+    const int t0 = x.rec[4 * chunk + 1], len = x.rec[4 * chunk + 2];
+    const int r = 16 * (x.w & 3) + (x.l >> 2);
+    const TIn* p = x.v + ((size_t(t0) + (r < len ? r : len - 1)) * x.H + x.h) * kD + 16 * x.s +
+                   4 * (x.l & 3);
+    if constexpr (!WalkIn<TIn>::kSplit) {
+        const u32x2 d = *reinterpret_cast<const u32x2*>(p);
+        o.vrow = u32x4{d[0], d[1], 0u, 0u};
+    } else {
+        o.vrow = *reinterpret_cast<const u32x4*>(p);
+    }
+}
+
+// T_b (state waves) or A (output waves) rows of the token tile, and gates
+template <typename TIn>
+__device__ __forceinline__ void load_f(WalkOps<WalkIn<TIn>::kSplit>& o, const WalkCtx<TIn>& x,
+                                       int chunk) {
+    const unsigned char* F = chunk_factors(x, chunk);
+    const int tt = x.w & 3;
+    const bf16x8* P = reinterpret_cast<const bf16x8*>(F + (x.w < 4 ? kOffTb : kOffA));
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            o.kt[j][m] = Kt[((2 * w + j) * 2 + m) * 64 + l];
-            if constexpr (kSplit) o.ktl[j][m] = Kt[1024 + ((2 * w + j) * 2 + m) * 64 + l];
-        }
-    const float* gs = reinterpret_cast<const float*>(F + kOffG);
-    o.gs = *reinterpret_cast<const f32x4*>(gs + 16 * w + 4 * (l >> 4));
-    o.gC = gs[64];
-    o.t0 = rec[4 * chunk + 1];
-    o.len = rec[4 * chunk + 2];
+    for (int m = 0; m < 2; ++m) {
+        const int base = ((tt * 2 + m) * 2) * 64 + x.l;
+        o.ah[m] = P[base];
+        o.al[m] = P[base + 64];
+    }
+    const float* G = reinterpret_cast<const float*>(F + kOffG);
+    o.gam = *reinterpret_cast<const f32x4*>(G + kGGam + 16 * tt + 4 * (x.l >> 4));
+    o.gs = *reinterpret_cast<const f32x4*>(G + kGScale + 16 * tt + 4 * (x.l >> 4));
+    o.gC = G[kGC];
+}
+
+template <typename TIn>
+__device__ __forceinline__ void load_rec(WalkOps<WalkIn<TIn>::kSplit>& o, const WalkCtx<TIn>& x,
+                                         int chunk) {
+    o.t0 = x.rec[4 * chunk + 1];
+    o.len = x.rec[4 * chunk + 2];
+}
+
+template <typename TIn>
+__device__ __forceinline__ void load_all(WalkOps<WalkIn<TIn>::kSplit>& o, const WalkCtx<TIn>& x,
+                                         int chunk) {
+    load_rec(o, x, chunk);
+    load_rows(o, x, chunk);
+    if (x.w < 4) load_v(o, x, chunk);
+    load_f(o, x, chunk);
+}
+
+// LDS exchange buffers hold ready 16-byte B operands: entry [blk][hl][lane]
+// is key (or token) block blk, whose low 8 bytes come from tile 2 blk and
+// high 8 bytes from tile 2 blk + 1, each written by the wave owning it.
+__device__ __forceinline__ void put_half(u32x4 (*X)[2][64], int tile, int l, u32x2 hi, u32x2 lo) {
+    u32x2* hp = reinterpret_cast<u32x2*>(&X[tile >> 1][0][l]) + (tile & 1);
+    u32x2* lp = reinterpret_cast<u32x2*>(&X[tile >> 1][1][l]) + (tile & 1);
+    *hp = hi;
+    *lp = lo;
+}
+
+__device__ __forceinline__ void publish4(u32x4 (*X)[2][64], int tile, int l, f32x4 v) {
+    uint32_t h01, l01, h23, l23;
+    split_pk(v[0], v[1], h01, l01);
+    split_pk(v[2], v[3], h23, l23);
+    put_half(X, tile, l, u32x2{h01, h23}, u32x2{l01, l23});
+}
+
+__device__ __forceinline__ bf16x8 ldsop(u32x4 (*X)[2][64], int blk, int hl, int l) {
+    return __builtin_bit_cast(bf16x8, X[blk][hl][l]);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposed operand from a row-major bf16 LDS tile (row stride `stride`):
+// lane (g = l/16, c = l%16) receives column col0 + c of rows
+// {r0 + i, r0 + 16 + i : i < 4} with r0 = 32m + 4g (the permuted token order).
+// ds_read_b64_tr_b16: within a 16-lane group, output lane i, element e is
+// element i%4 of the 8 bytes addressed by source lane 4e + i/4, so source
+// lane j points at row r0 + j/4, columns col0 + 4(j%4) .. +3.
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int stride, int r0, int col0,
+                                             int l) {
+    const int j = l & 15;
+    const uint16_t* p0 = tile + (r0 + (j >> 2)) * stride + col0 + 4 * (j & 3);
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 16 * stride));
+    return __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(u32x2, a)[0],
+                                             __builtin_bit_cast(u32x2, a)[1],
+                                             __builtin_bit_cast(u32x2, b)[0],
+                                             __builtin_bit_cast(u32x2, b)[1]});
+}
+
+// A operand from a row-major bf16 LDS tile: row r, keys {32m + 4g + i,
+// 32m + 16 + 4g + i : i < 4} (the permuted key order of the state operand).
+__device__ __forceinline__ bf16x8 row_operand(const uint16_t* tile, int r, int m, int g) {
+    const uint16_t* p = tile + r * kKS + 32 * m + 4 * g;
+    const u32x2 a = *reinterpret_cast<const u32x2*>(p);
+    const u32x2 b = *reinterpret_cast<const u32x2*>(p + 16);
+    return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
 }
 
 template <bool kSplit>
-__global__ __launch_bounds__(256) void walk_kernel(int N, int H, const int32_t* __restrict__ rec,
-                                                   const int32_t* __restrict__ seq_off,
-                                                   const int32_t* __restrict__ num_chunks,
-                                                   const unsigned char* __restrict__ factors,
-                                                   const float* __restrict__ S0,
-                                                   float* __restrict__ o,
-                                                   float* __restrict__ S_final) {
+struct WalkLds {
+    u32x4 Sx[4][2][64];   // state tiles (hi/lo) as B operands, key blocks 0..3
+    u32x4 Yx[2][2][64];   // Gamma Y (hi/lo), token blocks 0, 1
+    u32x4 Ux[2][2][64];   // U (hi/lo)
+    u32x4 Uy[2][2][64];   // U~ (hi/lo)
+    uint16_t K[2][kSplit ? 2 : 1][kC][kKS];   // K tile by chunk parity (hi, lo planes)
+    uint16_t Q[kSplit ? 2 : 1][kC][kKS];      // Q tile
+    uint16_t V[kSplit ? 2 : 1][kC][kVS];      // V slice
+};
+
+// P1 staging of this wave's tile rows into LDS (bf16 hi, and lo for fp32
+// inputs); rows at or past `len` are stored as zeros.
+template <bool kSplit>
+__device__ __forceinline__ void stage_rows(const WalkOps<kSplit>& cur, uint16_t (*T)[kC][kKS],
+                                           int tt, int l, int len) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 16 * tt + 4 * i + (l >> 4);
+        const bool valid = r < len;
+        if constexpr (!kSplit) {
+            *reinterpret_cast<u32x4*>(&T[0][r][8 * (l & 15)]) =
+                valid ? cur.rows[i][0] : u32x4{0u, 0u, 0u, 0u};
+        } else {
+            const f32x4 d0 = __builtin_bit_cast(f32x4, cur.rows[i][0]);
+            const f32x4 d1 = __builtin_bit_cast(f32x4, cur.rows[i][1]);
+            float v8[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+            if (!valid)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v8[j] = 0.f;
+            bf16x8 hi, lo;
+            split8(v8, hi, lo);
+            *reinterpret_cast<bf16x8*>(&T[0][r][8 * (l & 15)]) = hi;
+            *reinterpret_cast<bf16x8*>(&T[1][r][8 * (l & 15)]) = lo;
+        }
+    }
+}
+
+template <bool kSplit>
+__device__ __forceinline__ void stage_v(const WalkOps<kSplit>& cur, uint16_t (*V)[kC][kVS], int tt,
+                                        int l, int len) {
+    const int vr = 16 * tt + (l >> 2), vc = 4 * (l & 3);
+    const bool valid = vr < len;
+    if constexpr (!kSplit) {
+        *reinterpret_cast<u32x2*>(&V[0][vr][vc]) =
+            valid ? u32x2{cur.vrow[0], cur.vrow[1]} : u32x2{0u, 0u};
+    } else {
+        const f32x4 d = __builtin_bit_cast(f32x4, cur.vrow);
+        uint32_t h01, l01, h23, l23;
+        split_pk(valid ? d[0] : 0.f, valid ? d[1] : 0.f, h01, l01);
+        split_pk(valid ? d[2] : 0.f, valid ? d[3] : 0.f, h23, l23);
+        *reinterpret_cast<u32x2*>(&V[0][vr][vc]) = u32x2{h01, h23};
+        *reinterpret_cast<u32x2*>(&V[1][vr][vc]) = u32x2{l01, l23};
+    }
+}
+
+template <typename TIn, int kPar>
+__device__ __forceinline__ void state_step(WalkOps<WalkIn<TIn>::kSplit>& cur, f32x4& acc,
+                                           const WalkCtx<TIn>& x, int next,
+                                           WalkLds<WalkIn<TIn>::kSplit>& S) {
+    constexpr bool kSplit = WalkIn<TIn>::kSplit;
+    const int w = x.w, l = x.l, g = l >> 4, c = l & 15, tt = w & 3;
+    // P1
+    publish4(S.Sx, w, l, acc);
+    stage_rows<kSplit>(cur, S.K[kPar], tt, l, cur.len);
+    stage_v<kSplit>(cur, S.V, tt, l, cur.len);
+    __syncthreads();
+    // P2: operands from LDS first, then Y = K S^T
+    bf16x8 kt[2][kSplit ? 2 : 1], vb[2][kSplit ? 2 : 1], ka[4][kSplit ? 2 : 1];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int pl = 0; pl < (kSplit ? 2 : 1); ++pl) {
+            kt[m][pl] = tr_operand(&S.K[kPar][pl][0][0], kKS, 32 * m + 4 * g, 16 * w, l);
+            vb[m][pl] = tr_operand(&S.V[pl][0][0], kVS, 32 * m + 4 * g, 0, l);
+        }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int pl = 0; pl < (kSplit ? 2 : 1); ++pl)
+            ka[m][pl] = row_operand(&S.K[kPar][pl][0][0], 16 * tt + c, m, g);
+    f32x4 y;
+    {
+        f32x4 p0 = zero4(), p1 = zero4(), p2 = zero4();
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const bf16x8 bh = ldsop(S.Sx, m, 0, l), bl = ldsop(S.Sx, m, 1, l);
+            p0 = mfma_bf16(ka[m][0], bh, p0);
+            p1 = mfma_bf16(ka[m][0], bl, p1);
+            if constexpr (kSplit) p2 = mfma_bf16(ka[m][kSplit ? 1 : 0], bh, p2);
+        }
+        y = p0 + p1 + p2;
+    }
+    publish4(S.Yx, tt, l, y * cur.gam);
+    f32x4 up;
+    {
+        f32x4 p0 = zero4(), p1 = zero4(), p2 = zero4();
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            p0 = mfma_bf16(cur.ah[m], vb[m][0], p0);
+            p1 = mfma_bf16(cur.al[m], vb[m][0], p1);
+            if constexpr (kSplit) p2 = mfma_bf16(cur.ah[m], vb[m][kSplit ? 1 : 0], p2);
+        }
+        up = p0 + p1 + p2;
+    }
+    load_rows(cur, x, next);
+    load_v(cur, x, next);
+    __builtin_amdgcn_sched_barrier(0);   // keep the prefetch here: never sink it to its use
+    __syncthreads();
+    // P3: X = T_b (Gamma Y), U = U' - X, publish U and U~
+    {
+        f32x4 p0 = zero4(), p1 = zero4(), p2 = zero4();
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const bf16x8 bh = ldsop(S.Yx, m, 0, l), bl = ldsop(S.Yx, m, 1, l);
+            p0 = mfma_bf16(cur.ah[m], bh, p0);
+            p1 = mfma_bf16(cur.ah[m], bl, p1);
+            p2 = mfma_bf16(cur.al[m], bh, p2);
+        }
+        const f32x4 u = up - (p0 + p1 + p2);
+        publish4(S.Ux, tt, l, u);
+        publish4(S.Uy, tt, l, u * cur.gs);
+    }
+    const float gC = cur.gC;
+    load_f(cur, x, next);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    // P4: S^T = gamma_C S^T + K^T U~
+    {
+        acc *= gC;
+        f32x4 lo = zero4();
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const bf16x8 ubh = ldsop(S.Uy, m, 0, l), ubl = ldsop(S.Uy, m, 1, l);
+            acc = mfma_bf16(kt[m][0], ubh, acc);
+            lo = mfma_bf16(kt[m][0], ubl, lo);
+            if constexpr (kSplit) lo = mfma_bf16(kt[m][kSplit ? 1 : 0], ubh, lo);
+        }
+        acc += lo;
+    }
+    load_rec(cur, x, next);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <typename TIn, int kPar>
+__device__ __forceinline__ void output_step(WalkOps<WalkIn<TIn>::kSplit>& cur, f32x4& acc,
+                                            const WalkCtx<TIn>& x, int next,
+                                            WalkLds<WalkIn<TIn>::kSplit>& S,
+                                            float* __restrict__ o) {
+    constexpr bool kSplit = WalkIn<TIn>::kSplit;
+    const int w = x.w, l = x.l, g = l >> 4, c = l & 15, tt = w & 3;
+    // P1
+    publish4(S.Sx, w, l, acc);
+    stage_rows<kSplit>(cur, S.Q, tt, l, cur.len);
+    __syncthreads();
+    // P2: Z = Q S^T; K^T operand for P4
+    bf16x8 kt[2][kSplit ? 2 : 1], qa[4][kSplit ? 2 : 1];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int pl = 0; pl < (kSplit ? 2 : 1); ++pl)
+            kt[m][pl] = tr_operand(&S.K[kPar][pl][0][0], kKS, 32 * m + 4 * g, 16 * w, l);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int pl = 0; pl < (kSplit ? 2 : 1); ++pl)
+            qa[m][pl] = row_operand(&S.Q[pl][0][0], 16 * tt + c, m, g);
+    f32x4 z;
+    {
+        f32x4 p0 = zero4(), p1 = zero4(), p2 = zero4();
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const bf16x8 bh = ldsop(S.Sx, m, 0, l), bl = ldsop(S.Sx, m, 1, l);
+            p0 = mfma_bf16(qa[m][0], bh, p0);
+            p1 = mfma_bf16(qa[m][0], bl, p1);
+            if constexpr (kSplit) p2 = mfma_bf16(qa[m][kSplit ? 1 : 0], bh, p2);
+        }
+        z = p0 + p1 + p2;
+    }
+    load_rows(cur, x, next);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    // P3: nothing for output waves
+    __syncthreads();
+    // P4: state update for key tile w, then O = Gamma Z + A U
+    {
+        const float gC = cur.gC;
+        acc *= gC;
+        f32x4 lo = zero4();
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const bf16x8 ubh = ldsop(S.Uy, m, 0, l), ubl = ldsop(S.Uy, m, 1, l);
+            acc = mfma_bf16(kt[m][0], ubh, acc);
+            lo = mfma_bf16(kt[m][0], ubl, lo);
+            if constexpr (kSplit) lo = mfma_bf16(kt[m][kSplit ? 1 : 0], ubh, lo);
+        }
+        acc += lo;
+    }
+    {
+        f32x4 p0 = zero4(), p1 = zero4(), p2 = zero4();
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const bf16x8 bh = ldsop(S.Ux, m, 0, l), bl = ldsop(S.Ux, m, 1, l);
+            p0 = mfma_bf16(cur.ah[m], bh, p0);
+            p1 = mfma_bf16(cur.ah[m], bl, p1);
+            p2 = mfma_bf16(cur.al[m], bh, p2);
+        }
+        const f32x4 ov = z * cur.gam + (p0 + p1 + p2);
+        const int t0 = cur.t0, len = cur.len;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tok = 16 * tt + 4 * g + i;
+            if (tok < len) o[((size_t(t0) + tok) * x.H + x.h) * kD + 16 * x.s + c] = ov[i];
+        }
+    }
+    load_f(cur, x, next);
+    load_rec(cur, x, next);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <typename TIn, bool kState>
+__device__ __forceinline__ void walk_loop(f32x4& acc, const WalkCtx<TIn>& x, int c_begin,
+                                          int c_end, WalkLds<WalkIn<TIn>::kSplit>& S,
+                                          float* __restrict__ o) {
+    WalkOps<WalkIn<TIn>::kSplit> A, B;
+    const int last = c_end - 1;
+    load_all(A, x, c_begin);
+    load_all(B, x, c_begin + 1 < c_end ? c_begin + 1 : last);
+    for (int ch = c_begin; ch < c_end; ch += 2) {
+        if constexpr (kState) state_step<TIn, 0>(A, acc, x, ch + 2 < c_end ? ch + 2 : last, S);
+        else output_step<TIn, 0>(A, acc, x, ch + 2 < c_end ? ch + 2 : last, S, o);
+        if (ch + 1 >= c_end) break;
+        if constexpr (kState) state_step<TIn, 1>(B, acc, x, ch + 3 < c_end ? ch + 3 : last, S);
+        else output_step<TIn, 1>(B, acc, x, ch + 3 < c_end ? ch + 3 : last, S, o);
+    }
+}
+
+template <typename TIn>
+__global__ __launch_bounds__(kWalkThreads) void walk_kernel(
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v, int N, int H,
+    const int32_t* __restrict__ rec, const int32_t* __restrict__ seq_off,
+    const int32_t* __restrict__ num_chunks, const unsigned char* __restrict__ factors,
+    const float* __restrict__ S0, float* __restrict__ o, float* __restrict__ S_final) {
     // XCD-aware mapping: the 8 value slices of one (sequence, head) share the
-    // same blockIdx.x % 8, hence the same XCD and L2, which holds the chunk
-    // factors all 8 of them read.
+    // same blockIdx.x % 8, hence the same XCD and L2, which holds the chunk's
+    // K, Q and factors that all 8 of them read.
     const int id = blockIdx.x;
     const int xcd = id & 7, rest = id >> 3;
     const int s = rest & 7, pg = rest >> 3;
@@ -604,122 +778,59 @@ __global__ __launch_bounds__(256) void walk_kernel(int N, int H, const int32_t* 
     const int tid = threadIdx.x;
     const int w = tid >> 6, l = tid & 63, g = l >> 4, c = l & 15;
 
-    __shared__ __attribute__((aligned(16))) bf16x8 Sx[4][2][64];   // state B operands
-    __shared__ __attribute__((aligned(16))) u16x4 Ux[4][2][64];    // scaled U (hi, lo)
-
-    // state: lane holds S^T[k = 32w + 16j + 4g + i][v = 16s + c], i.e.
-    // S[v][k .. k+3], a 16-byte run of one state row
-    const size_t srow = ((size_t(n) * H + h) * kD + 16 * s + c) * kD;
-    f32x4 acc[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-        acc[j] = S0 ? *reinterpret_cast<const f32x4*>(S0 + srow + 32 * w + 16 * j + 4 * g) : zero4();
+    __shared__ __attribute__((aligned(16))) WalkLds<WalkIn<TIn>::kSplit> lds;
 
     const int nch = num_chunks[0];
-    int c_begin = seq_off[n], c_end = seq_off[n + 1];
-    if (c_end > nch) c_end = nch;
+    const int c_begin = seq_off[n];
+    const int c_end = seq_off[n + 1] < nch ? seq_off[n + 1] : nch;
+    const WalkCtx<TIn> x{q, k, v, factors, rec, H, h, s, w, l};
 
-    WalkOps cur, nxt;
-    if (c_begin < c_end) walk_load<kSplit>(nxt, factors, rec, c_begin, H, h, s, w, l);
-    for (int ch = c_begin; ch < c_end; ++ch) {
-        cur = nxt;
-        if (ch + 1 < c_end) walk_load<kSplit>(nxt, factors, rec, ch + 1, H, h, s, w, l);
-
-        // 1. this wave's state k-block -> hi/lo B operand in LDS
-        {
-            float x[8] = {acc[0][0], acc[0][1], acc[0][2], acc[0][3],
-                          acc[1][0], acc[1][1], acc[1][2], acc[1][3]};
-            bf16x8 hi, lo;
-            split8(x, hi, lo);
-            Sx[w][0][l] = hi;
-            Sx[w][1][l] = lo;
-        }
-        __syncthreads();
-
-        // 2. X = [W ; Q'] S^T for this wave's token tile
-        f32x4 xw = zero4(), xq = zero4();
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const bf16x8 bh = Sx[m][0][l], bl = Sx[m][1][l];
-            xw = mfma_bf16(cur.wh[m], bh, xw);
-            xq = mfma_bf16(cur.qh[m], bh, xq);
-            xw = mfma_bf16(cur.wh[m], bl, xw);
-            xq = mfma_bf16(cur.qh[m], bl, xq);
-            xw = mfma_bf16(cur.wl[m], bh, xw);
-            xq = mfma_bf16(cur.ql[m], bh, xq);
-        }
-
-        // 3. outputs and the scaled errors
-        u16x4 uh, ul;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tok = 16 * w + 4 * g + i;
-            const float u = cur.up[i] - xw[i];
-            const float ov = cur.op[i] + xq[i];
-            if (tok < cur.len) o[((size_t(cur.t0) + tok) * H + h) * kD + 16 * s + c] = ov;
-            uint16_t hb, lb;
-            split_bf16(u * cur.gs[i], hb, lb);
-            uh[i] = hb;
-            ul[i] = lb;
-        }
-        Ux[w][0][l] = uh;
-        Ux[w][1][l] = ul;
-        __syncthreads();
-
-        // 4. S^T = gamma_C S^T + K^T U~  (this wave's two key tiles)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            acc[j] *= cur.gC;
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const u16x4 h0 = Ux[2 * m][0][l], h1 = Ux[2 * m + 1][0][l];
-                const u16x4 l0 = Ux[2 * m][1][l], l1 = Ux[2 * m + 1][1][l];
-                const bf16x8 bh = as_bf16x8(u16x8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]});
-                const bf16x8 bl = as_bf16x8(u16x8{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]});
-                acc[j] = mfma_bf16(cur.kt[j][m], bh, acc[j]);
-                acc[j] = mfma_bf16(cur.kt[j][m], bl, acc[j]);
-                if constexpr (kSplit) acc[j] = mfma_bf16(cur.ktl[j][m], bh, acc[j]);
-            }
-        }
+    // state: lane holds S^T[k = 16w + 4g + i][v = 16s + c] = S[v][k .. k+3]
+    const size_t srow = ((size_t(n) * H + h) * kD + 16 * s + c) * kD + 16 * w + 4 * g;
+    f32x4 acc = S0 ? *reinterpret_cast<const f32x4*>(S0 + srow) : zero4();
+    if (c_begin < c_end) {
+        if (w < 4) walk_loop<TIn, true>(acc, x, c_begin, c_end, lds, o);
+        else walk_loop<TIn, false>(acc, x, c_begin, c_end, lds, o);
     }
-    if (S_final) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            *reinterpret_cast<f32x4*>(S_final + srow + 32 * w + 16 * j + 4 * g) = acc[j];
-    }
+    if (S_final) *reinterpret_cast<f32x4*>(S_final + srow) = acc;
 }
 
 }  // namespace
 
-hipError_t launch_prep(const void* q, const void* k, const void* v, rda_dtype dt, const float* a,
+hipError_t launch_prep(const void* q, const void* k, rda_dtype dt, const float* a,
                        const float* b, int32_t heads, int32_t max_chunks, const int32_t* rec,
                        const int32_t* num_chunks, unsigned char* factors, hipStream_t stream) {
     const unsigned grid = unsigned(int64_t(max_chunks) * heads);
     if (grid == 0) return hipSuccess;
     if (dt == RDA_BF16) {
         hipLaunchKernelGGL(prep_kernel<false>, dim3(grid), dim3(256), 0, stream,
-                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                           static_cast<const uint16_t*>(v), a, b, heads, rec, num_chunks, factors);
+                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), a, b,
+                           heads, rec, num_chunks, factors);
     } else {
         hipLaunchKernelGGL(prep_kernel<true>, dim3(grid), dim3(256), 0, stream,
-                           static_cast<const float*>(q), static_cast<const float*>(k),
-                           static_cast<const float*>(v), a, b, heads, rec, num_chunks, factors);
+                           static_cast<const float*>(q), static_cast<const float*>(k), a, b,
+                           heads, rec, num_chunks, factors);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_walk(rda_dtype dt, int32_t num_seqs, int32_t heads, const int32_t* rec,
+hipError_t launch_walk(const void* q, const void* k, const void* v, rda_dtype dt,
+                       int32_t num_seqs, int32_t heads, const int32_t* rec,
                        const int32_t* seq_off, const int32_t* num_chunks,
                        const unsigned char* factors, const float* S0, float* o, float* S_final,
                        hipStream_t stream) {
     const int64_t pairs = int64_t(num_seqs) * heads;
     const unsigned grid = unsigned(64 * ((pairs + 7) / 8));
     if (dt == RDA_BF16) {
-        hipLaunchKernelGGL(walk_kernel<false>, dim3(grid), dim3(256), 0, stream, num_seqs, heads,
-                           rec, seq_off, num_chunks, factors, S0, o, S_final);
+        hipLaunchKernelGGL(walk_kernel<uint16_t>, dim3(grid), dim3(kWalkThreads), 0, stream,
+                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                           static_cast<const uint16_t*>(v), num_seqs, heads, rec, seq_off,
+                           num_chunks, factors, S0, o, S_final);
     } else {
-        hipLaunchKernelGGL(walk_kernel<true>, dim3(grid), dim3(256), 0, stream, num_seqs, heads,
-                           rec, seq_off, num_chunks, factors, S0, o, S_final);
+        hipLaunchKernelGGL(walk_kernel<float>, dim3(grid), dim3(kWalkThreads), 0, stream,
+                           static_cast<const float*>(q), static_cast<const float*>(k),
+                           static_cast<const float*>(v), num_seqs, heads, rec, seq_off,
+                           num_chunks, factors, S0, o, S_final);
     }
     return hipGetLastError();
 }

@@ -83,7 +83,10 @@ EXACT = dict(gram="f64", solve="f64", wu="f64", qo="f64", walk_x="f64", walk_s="
 # Plan used by the HIP kernels: exact-bf16 inputs need no split; every
 # computed fp32 operand is fed to MFMA as a bf16 hi + lo pair.
 KERNEL_PLAN = dict(gram="x1", solve="f32", wu="xa", qo="x3", walk_x="x3", walk_s="xa",
-                   state="f32")
+                   state="f32", form="B", walk_y="xb")
+# The same algebra with W, Q', U', O' formed per chunk (the WY form written out).
+WY_PLAN = dict(gram="x1", solve="f32", wu="xa", qo="x3", walk_x="x3", walk_s="xa",
+               state="f32")
 
 
 def chunk_prefill(q, k, v, a, b, cu_seqlens=None, S0=None, C=64, plan=None):
@@ -132,8 +135,21 @@ def chunk_prefill(q, k, v, a, b, cu_seqlens=None, S0=None, C=64, plan=None):
                 Qp = _f32(gam[:, None] * Qc - _mm(Am, W, plan["qo"])) \
                     if plan["qo"] != "f64" else gam[:, None] * Qc - Am @ W
                 Op = _mm(Am, Up, plan["qo"])
-                X_w = _mm(W, S.T, plan["walk_x"])
-                X_q = _mm(Qp, S.T, plan["walk_x"])
+                if plan.get("form") == "B":
+                    # walk on the raw inputs and the small factors T_b, A:
+                    # X_W = T_b (Gamma (K S^T)), U' = T_b V, O = Gamma (Q S^T) + A U
+                    Tb = Tm * bc[None, :]
+                    Y = gam[:, None] * _mm(Kc, S.T, plan["walk_y"])
+                    X_w = _mm(Tb, Y, plan["walk_x"])
+                    Up = _mm(Tb, Vc, plan["wu"])
+                    U = Up - X_w
+                    Oc = gam[:, None] * _mm(Qc, S.T, plan["walk_y"]) + _mm(Am, U, plan["qo"])
+                    o[c0:c0 + L_, h] = Oc[:L_]
+                    scale = gam[-1] / gam
+                    S = rnd_state(gam[-1] * S + _mm((U * scale[:, None]).T, Kc, plan["walk_s"]))
+                    continue
+                X_w = _mm(W, S.T, plan.get("walk_w", plan["walk_x"]))
+                X_q = _mm(Qp, S.T, plan.get("walk_q", plan["walk_x"]))
                 U = Up - X_w
                 Oc = Op + X_q
                 o[c0:c0 + L_, h] = Oc[:L_]
