@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const TIn* __restrict_
                                                           float* __restrict__ o) {
     const int64_t bh = blockIdx.x;
     const int t = threadIdx.x;
-    const int w = t >> 6;         // wavefront 0..3 -> rows 32w .. 32w+31
+    const int w = wave_id();      // wavefront 0..3 -> rows 32w .. 32w+31
     const int g = (t >> 4) & 3;   // 16-lane group within the wavefront
     const int c = t & 15;         // lane within the group -> columns 4c.., 64+4c..
     float* __restrict__ Sb = S + bh * (kD * kD);

@@ -60,6 +60,45 @@ __device__ __forceinline__ float dpp_sum16(float x) {
     return x;
 }
 
+// Index of this lane's wavefront in the workgroup, as a wave-uniform scalar.
+// Branches on it then compile to scalar branches: an MFMA placed under a
+// per-lane EXEC mask would still execute for every lane (MFMA ignores EXEC),
+// so wave-role conditions around matrix code must never be lane-divergent.
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// D += A * B on v_mfma_f32_16x16x32_bf16 (lane l, g = l / 16, c = l % 16:
+// A lane holds row c, k = 8g .. 8g+7; B lane holds column c, the same k;
+// D lane holds rows 4g .. 4g+3 of column c).
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// D += A * B on v_mfma_f32_16x16x4_f32 (A lane: row c, k = g; B: column c, k = g).
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Split 8 fp32 values into bf16 hi and lo vectors (paired conversions).
+__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+    u32x4 h, l;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        uint32_t a, b;
+        split_pk(x[2 * p], x[2 * p + 1], a, b);
+        h[p] = a;
+        l[p] = b;
+    }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+}
+
 // Load 4 consecutive input elements as fp32 (bf16 bits or fp32).
 __device__ __forceinline__ void load4_bf16(const uint16_t* p, float out[4]) {
     u16x4 h = *reinterpret_cast<const u16x4*>(p);

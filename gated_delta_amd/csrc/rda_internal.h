@@ -24,7 +24,10 @@ constexpr int kD = RDA_HEAD_DIM;   // dk = dv
 //                 Tb   bf16 hi/lo of T diag(b), T = (I + L)^-1, packed as the
 //                      walk's MFMA A operand (rows = tokens, K dim = tokens)
 //                 Am   bf16 hi/lo of A = lower(Q K^T . Gamma), same packing
-//                 G    fp32 gamma_i (64), gamma_C / gamma_i (64), gamma_C
+//                      (written for fp32 inputs only; the bf16 walk forms A
+//                      itself from the Q and K tiles it already holds)
+//                 G    fp32 gamma_i (64), gamma_C / gamma_i (64), gamma_C,
+//                      g_i = running sum of log a (64, at float 192)
 // ---------------------------------------------------------------------------
 constexpr size_t kPackBytes = size_t(kC) * kC * 2 * 2;   // hi + lo bf16, 64 x 64
 constexpr size_t kGBytes = 1024;
@@ -35,6 +38,7 @@ constexpr size_t kChunkHeadBytes = kOffG + kGBytes;
 constexpr int kGGam = 0;     // float offsets inside G
 constexpr int kGScale = 64;
 constexpr int kGC = 128;
+constexpr int kGLog = 192;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -72,5 +76,12 @@ hipError_t launch_walk(const void* q, const void* k, const void* v, rda_dtype dt
                        const int32_t* seq_off, const int32_t* num_chunks,
                        const unsigned char* factors, const float* S0, float* o, float* S_final,
                        hipStream_t stream);
+
+// bf16 walk (operands streamed into LDS by a loader wave)
+hipError_t launch_walk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            int32_t num_seqs, int32_t heads, const int32_t* rec,
+                            const int32_t* seq_off, const int32_t* num_chunks,
+                            const unsigned char* factors, const float* S0, float* o,
+                            float* S_final, hipStream_t stream);
 
 }  // namespace rda

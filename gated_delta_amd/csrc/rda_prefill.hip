@@ -51,34 +51,6 @@ namespace rda {
 
 namespace {
 
-__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-// Split 8 fp32 values into bf16 hi and lo vectors (paired conversions).
-__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
-    u32x4 h, l;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        uint32_t a, b;
-        split_pk(x[2 * p], x[2 * p + 1], a, b);
-        h[p] = a;
-        l[p] = b;
-    }
-    hi = __builtin_bit_cast(bf16x8, h);
-    lo = __builtin_bit_cast(bf16x8, l);
-}
-
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-
 // ---------------------------------------------------------------------------
 // PREP: one 256-thread workgroup per (chunk, head).
 // ---------------------------------------------------------------------------
@@ -187,7 +159,7 @@ __global__ __launch_bounds__(256) void prep_kernel(
     const int len = rec[4 * chunk + 2];
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6, l = tid & 63, g = l >> 4, c = l & 15;
+    const int w = wave_id(), l = tid & 63, g = l >> 4, c = l & 15;
 
     uint16_t* Ks = reinterpret_cast<uint16_t*>(smem + kSmK);
     uint16_t* Qs = reinterpret_cast<uint16_t*>(smem + kSmQ);
@@ -334,6 +306,7 @@ __global__ __launch_bounds__(256) void prep_kernel(
         float* G = reinterpret_cast<float*>(F + kOffG);
         G[kGGam + tid] = gam[tid];
         G[kGScale + tid] = expf(gg[63] - gg[tid]);
+        G[kGLog + tid] = gg[tid];
         if (tid == 0) G[kGC] = gam[63];
     }
 }
@@ -776,7 +749,7 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(
     const int n = p / H, h = p - n * H;
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6, l = tid & 63, g = l >> 4, c = l & 15;
+    const int w = wave_id(), l = tid & 63, g = l >> 4, c = l & 15;
 
     __shared__ __attribute__((aligned(16))) WalkLds<WalkIn<TIn>::kSplit> lds;
 
@@ -822,10 +795,9 @@ hipError_t launch_walk(const void* q, const void* k, const void* v, rda_dtype dt
     const int64_t pairs = int64_t(num_seqs) * heads;
     const unsigned grid = unsigned(64 * ((pairs + 7) / 8));
     if (dt == RDA_BF16) {
-        hipLaunchKernelGGL(walk_kernel<uint16_t>, dim3(grid), dim3(kWalkThreads), 0, stream,
-                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                           static_cast<const uint16_t*>(v), num_seqs, heads, rec, seq_off,
-                           num_chunks, factors, S0, o, S_final);
+        return launch_walk_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                static_cast<const uint16_t*>(v), num_seqs, heads, rec, seq_off,
+                                num_chunks, factors, S0, o, S_final, stream);
     } else {
         hipLaunchKernelGGL(walk_kernel<float>, dim3(grid), dim3(kWalkThreads), 0, stream,
                            static_cast<const float*>(q), static_cast<const float*>(k),

@@ -1,0 +1,500 @@
+// rda_walk.hip -- the sequential chunk walk of the chunked RDA prefill for
+// bf16 inputs on gfx950 (the chunk algebra and the operand conventions are
+// those stated at the top of rda_prefill.hip; T_b, A and the gates come from
+// its prep kernel).
+//
+// One workgroup per (sequence, head, 16-channel value slice): 4 compute waves
+// (one per SIMD) and 8 loader waves.  The loaders stream each chunk's operands
+// -- the K and Q tiles, the packed T_b and A factors, the gates and this
+// slice's V columns -- straight into a two-stage LDS ring with LDS-DMA loads
+// (global_load_lds_dwordx4), and touch the lines of chunks further ahead so
+// that they sit in L2 when the DMA asks for them.  The compute waves issue no
+// global loads at all.
+//
+// Compute wave w owns the state S^T for key block w (key tiles 2w, 2w+1, as
+// MFMA accumulators) and token tile w of every chunk-local product.  Per
+// chunk (three barriers):
+//   P1  publish its S^T block (bf16 hi/lo) as ready B operands, key order
+//       natural so that K and Q rows are single 16-byte LDS reads
+//   P2  Y = K S^T and Z = Q S^T for token tile w, U' = T_b V; publish Gamma Y
+//   P3  X = T_b (Gamma Y), U = U' - X; publish U and U~ = diag(gamma_C/gamma) U
+//   P4  S^T = gamma_C S^T + K^T U~ for its key block; O = Gamma Z + A U, stored
+// Stage reads end at the third barrier of a chunk; that stage is refilled
+// with the chunk two ahead during the next chunk (stage of chunk c:
+// (c - first) % 2), and each loader waits for all its loads before the
+// first barrier of a chunk.
+//
+// LDS reads are issued in fenced groups (scheduling barriers) of at most 15:
+// the compiler clamps its lgkmcnt waits to 14 when more are outstanding,
+// which only holds while the 4-bit counter cannot overflow.
+//
+// Past the end of a chunk (len < 64) the loaders duplicate the last valid
+// token row instead of zeroing: T_b has zero rows and columns there (b = 0),
+// so U and U~ vanish on those rows and no duplicate reaches S or a stored
+// output; they only need to be finite, which copies of real rows are.
+#include "rda_device.h"
+#include "rda_internal.h"
+
+namespace rda {
+
+namespace {
+
+constexpr int kCompute = 4;                        // compute waves, one per SIMD
+constexpr int kLoaders = 8;                        // loader waves
+constexpr int kThreads = (kCompute + kLoaders) * 64;
+constexpr int kPfAhead = 4;                        // L2 touch distance past the DMA (chunks)
+
+// One chunk's operands in LDS (68608 bytes, every part whole 1 KiB DMA blocks).
+struct Stage {
+    uint16_t K[kC * kD];   // 64 token rows x 256 B; 16-byte granules swizzled per row
+    uint16_t Q[kC * kD];
+    u32x4 Tb[16][64];      // T_b packed: [(tile * 2 + block) * 2 + hi/lo][lane]
+    u32x4 Am[16][64];      // A, same packing
+    uint16_t V[kC * 16];   // this slice's 16 value channels, 32 B per token row
+    float G[256];          // gamma, gamma_C / gamma, gamma_C, running log gate
+};
+
+struct Lds {
+    Stage st[2];
+    u32x4 Sx[4][2][64];    // S^T key block m hi/lo; lane (g, c): keys 32m + 8g .. +7, column c
+    u32x4 Yx[2][2][64];    // Gamma Y token block (tiles 2m, 2m+1) hi/lo
+    u32x4 Ux[2][2][64];    // U
+    u32x4 Uy[2][2][64];    // U~
+    float sink[64];        // landing words of the L2 touches
+};
+
+static_assert(sizeof(Stage) == 67 * 1024, "stage is whole 1 KiB DMA blocks");
+static_assert(sizeof(Lds) <= 160 * 1024, "LDS budget of one workgroup");
+
+// Row r of a K or Q tile keeps 16-byte granule j at position j ^ swz(r).
+// Sixteen consecutive rows read at one granule (row operands) and eight
+// consecutive rows read at two adjacent granules (transposing reads) both
+// land on distinct granules, i.e. on distinct LDS banks.
+__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, void* lds_dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 4, 0, 0);
+}
+
+struct Ctx {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const unsigned char* factors;
+    const int32_t* rec;
+    int H, h, s, l;
+};
+
+__device__ __forceinline__ const unsigned char* chunk_factors(const Ctx& x, int chunk) {
+    return x.factors + (size_t(chunk) * x.H + x.h) * kChunkHeadBytes;
+}
+
+__device__ __forceinline__ const uint16_t* token_row(const uint16_t* base, const Ctx& x,
+                                                     int t0, int r) {
+    return base + (size_t(t0 + r) * x.H + x.h) * kD;
+}
+
+// ---- loader waves -------------------------------------------------------------
+// The chunk's operands are 67 DMA blocks of 1 KiB: K 0..15, Q 16..31, T_b
+// 32..47, A 48..63, V 64..65, G 66.  Loader i owns the blocks i, i + 8, ...
+// (9 or 8 of them); loaders 0 and 1 also touch one line set each for L2.
+// A chunk's blocks are issued in three parts, one in each barrier window of
+// the chunk before it, so that no window carries a long DMA burst (which
+// would hold back the compute waves' output stores and the next barrier).
+
+__device__ __forceinline__ void issue_block(const Ctx& x, int t0, int len,
+                                            const unsigned char* F, int blk, Stage& st) {
+    const int L = x.l;
+    if (blk < 32) {   // K or Q tile block: rows 4n .. 4n+3
+        const int n = blk & 15;
+        const int r = 4 * n + (L >> 4);
+        const int rr = r < len ? r : len - 1;
+        const int j = (L & 15) ^ swz(r);
+        const uint16_t* src = blk < 16 ? x.k : x.q;
+        uint16_t* dst = blk < 16 ? st.K : st.Q;
+        dma16(token_row(src, x, t0, rr) + 8 * j, reinterpret_cast<char*>(dst) + 1024 * n);
+    } else if (blk < 64) {   // T_b then A: contiguous 32 KiB in the factors
+        dma16(F + kOffTb + 1024 * (blk - 32) + 16 * L,
+              reinterpret_cast<char*>(st.Tb) + 1024 * (blk - 32));
+    } else if (blk < 66) {   // V slice rows 32n .. 32n+31
+        const int n = blk - 64;
+        const int r = 32 * n + (L >> 1);
+        const int rr = r < len ? r : len - 1;
+        dma16(token_row(x.v, x, t0, rr) + 16 * x.s + 8 * (L & 1),
+              reinterpret_cast<char*>(st.V) + 1024 * n);
+    } else {
+        dma16(F + kOffG + 16 * L, st.G);
+    }
+}
+
+// Touch this slice's share of a chunk's 128-byte lines, one line per lane.
+// Half kHalf of the shared lines (K, Q, T_b, A: 512 lines, every eighth
+// one for this slice), plus (half 1) a quarter of the V lines that this
+// slice shares with the three other slices of its 64-channel group.
+template <int kHalf>
+__device__ __forceinline__ void touch_chunk(const Ctx& x, int chunk, float* sink) {
+    const int t0 = x.rec[4 * chunk + 1], len = x.rec[4 * chunk + 2];
+    const int L = x.l;
+    const unsigned char* F = chunk_factors(x, chunk);
+    const void* a;
+    const int u = 32 * kHalf + (L & 31);   // this slice's shared line index, 0..63
+    const int i = x.s + 8 * u;             // shared line, 0..511
+    if (kHalf == 1 && L >= 32) {
+        const int r = 4 * (L & 15) + (x.s & 3);
+        const int rr = r < len ? r : len - 1;
+        a = token_row(x.v, x, t0, rr) + 64 * (x.s >> 2);
+    } else if (i < 256) {
+        const int r = (i & 127) >> 1;
+        const int rr = r < len ? r : len - 1;
+        a = token_row(i < 128 ? x.k : x.q, x, t0, rr) + 64 * (i & 1);
+    } else {
+        a = F + kOffTb + 128 * (i - 256);   // T_b then A: contiguous 32 KiB
+    }
+    dma4(a, sink);
+}
+
+// Part kPart (0..2) of loader kI's blocks of `chunk`.
+template <int kI, int kPart>
+__device__ __forceinline__ void issue_part(const Ctx& x, int chunk, Stage& st) {
+    const int t0 = x.rec[4 * chunk + 1], len = x.rec[4 * chunk + 2];
+    const unsigned char* F = chunk_factors(x, chunk);
+#pragma unroll
+    for (int q = 3 * kPart; q < 3 * kPart + 3; ++q) {
+        const int blk = kI + 8 * q;
+        if (blk < 67) issue_block(x, t0, len, F, blk, st);
+    }
+}
+
+template <int kN>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(kN >= 0 && kN < 64, "vmcnt field");
+    // vmcnt = kN (split field), expcnt and lgkmcnt at their maxima: no wait
+    __builtin_amdgcn_s_waitcnt((kN & 15) | ((kN >> 4) << 14) | 0x0F70);
+}
+
+// Loaders 0 and 1 end every chunk's issue with one L2 touch, the only load
+// they leave pending at a barrier (loads complete in issue order).
+template <int kI>
+__device__ void loader(const Ctx& x, int c0, int c_end, Lds& S) {
+    constexpr int kPending = kI < 2 ? 1 : 0;
+    const int last = c_end - 1;
+    auto cl = [last](int c) { return c < last ? c : last; };
+    // touches for the first chunks, the first chunk whole, one more touch
+    if constexpr (kI < 2) {
+#pragma unroll
+        for (int d = 1; d < kPfAhead; ++d) touch_chunk<kI>(x, cl(c0 + d), S.sink);
+    }
+    issue_part<kI, 0>(x, c0, S.st[0]);
+    issue_part<kI, 1>(x, c0, S.st[0]);
+    issue_part<kI, 2>(x, c0, S.st[0]);
+    if constexpr (kI < 2) touch_chunk<kI>(x, cl(c0 + kPfAhead), S.sink);
+    for (int c = c0; c < c_end; ++c) {
+        // chunk c + 1 goes to the stage chunk c - 1 used (free since its
+        // third barrier); all loads issued before now, but the last touch,
+        // belong to chunk c
+        Stage& nxt = S.st[(c + 1 - c0) & 1];
+        const int cn = cl(c + 1);
+        wait_vm<kPending>();
+        __builtin_amdgcn_s_barrier();   // A
+        issue_part<kI, 0>(x, cn, nxt);
+        __builtin_amdgcn_s_barrier();   // B
+        issue_part<kI, 1>(x, cn, nxt);
+        __builtin_amdgcn_s_barrier();   // C
+        issue_part<kI, 2>(x, cn, nxt);
+        if constexpr (kI < 2) touch_chunk<kI>(x, cl(c + 1 + kPfAhead), S.sink);
+    }
+    wait_vm<0>();   // nothing may land in LDS after the workgroup ends
+}
+
+// ---- compute waves ---------------------------------------------------------------
+
+// Row r of a swizzled 64 x 128 tile, natural k order: lane (g, c) gets
+// elements 32m + 8g .. +7 (one 16-byte granule).
+__device__ __forceinline__ bf16x8 row_op(const uint16_t* T, int r, int m, int g) {
+    const unsigned char* row = reinterpret_cast<const unsigned char*>(T) + r * 256;
+    return __builtin_bit_cast(bf16x8,
+                              *reinterpret_cast<const u32x4*>(row + 16 * ((4 * m + g) ^ swz(r))));
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ u32x2 tr_read(const void* p) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
+}
+
+// Transposed operand of a swizzled tile: lane (g, c) receives column
+// 16 kt + c of rows {32m + 4g + i, 32m + 16 + 4g + i : i < 4} (the permuted
+// token order of the packed factors and of the exchanged U~).
+// ds_read_b64_tr_b16 gives output lane i of a 16-lane group element i % 4 of
+// the 8 bytes that source lane 4e + i / 4 addresses, so source lane j points
+// at row r0 + j / 4, columns 16 kt + 4 (j % 4) .. +3.
+__device__ __forceinline__ bf16x8 tr_op(const uint16_t* T, int m, int kt, int l) {
+    const int g = l >> 4, j = l & 15;
+    const int r = 32 * m + 4 * g + (j >> 2);
+    const int gran = 2 * kt + ((j >> 1) & 1), hb = 8 * (j & 1);
+    const unsigned char* base = reinterpret_cast<const unsigned char*>(T);
+    const u32x2 a = tr_read(base + r * 256 + 16 * (gran ^ swz(r)) + hb);
+    const u32x2 b = tr_read(base + (r + 16) * 256 + 16 * (gran ^ swz(r + 16)) + hb);
+    return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+}
+
+// Transposed operand of the V slice (32-byte rows): channel c, tokens of block m.
+__device__ __forceinline__ bf16x8 tr_v(const uint16_t* V, int m, int l) {
+    const int g = l >> 4, j = l & 15;
+    const unsigned char* p =
+        reinterpret_cast<const unsigned char*>(V) + (32 * m + 4 * g + (j >> 2)) * 32 + 8 * (j & 3);
+    const u32x2 a = tr_read(p);
+    const u32x2 b = tr_read(p + 16 * 32);
+    return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+}
+
+__device__ __forceinline__ bf16x8 xop(const u32x4 (*X)[2][64], int blk, int hl, int l) {
+    return __builtin_bit_cast(bf16x8, X[blk][hl][l]);
+}
+
+__device__ __forceinline__ bf16x8 packed(const u32x4 (*P)[64], int tile, int m, int hl, int l) {
+    return __builtin_bit_cast(bf16x8, P[(tile * 2 + m) * 2 + hl][l]);
+}
+
+// Write a D-layout tile's 4 values (hi/lo) into its half of block tile / 2.
+__device__ __forceinline__ void put_half(u32x4 (*X)[2][64], int tile, int l, f32x4 v) {
+    uint32_t h01, l01, h23, l23;
+    split_pk(v[0], v[1], h01, l01);
+    split_pk(v[2], v[3], h23, l23);
+    reinterpret_cast<u32x2*>(&X[tile >> 1][0][l])[tile & 1] = u32x2{h01, h23};
+    reinterpret_cast<u32x2*>(&X[tile >> 1][1][l])[tile & 1] = u32x2{l01, l23};
+}
+
+// Products of a hi/lo A operand with a hi/lo B operand: hi*hi + hi*lo + lo*hi.
+__device__ __forceinline__ void mma3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, f32x4& p0,
+                                     f32x4& p1, f32x4& p2) {
+    p0 = mfma_bf16(ah, bh, p0);
+    p1 = mfma_bf16(ah, bl, p1);
+    p2 = mfma_bf16(al, bh, p2);
+}
+
+__device__ void compute_wave(const Ctx& x, int w, int c0, int c_end, Lds& S, f32x4& s0,
+                             f32x4& s1, float* __restrict__ o) {
+    const int l = x.l, g = l >> 4, c = l & 15;
+    // this lane's slots of S^T block w in natural key order: tile 2w (keys
+    // 32w + 4g + i) -> lane c + 16 (g / 2), tile 2w + 1 -> lane c + 16 (2 + g / 2),
+    // both in 8-byte half g % 2
+    const int lane0 = c + 16 * (g >> 1), lane1 = lane0 + 32, half = g & 1;
+    const int nb = (w >> 1) + 1;   // token blocks at or below token tile w
+    for (int ch = c0; ch < c_end; ++ch) {
+        const Stage& st = S.st[(ch - c0) & 1];
+        // P1: publish S^T block w
+        {
+            uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+            split_pk(s0[0], s0[1], h0, l0);
+            split_pk(s0[2], s0[3], h1, l1);
+            split_pk(s1[0], s1[1], h2, l2);
+            split_pk(s1[2], s1[3], h3, l3);
+            reinterpret_cast<u32x2*>(&S.Sx[w][0][lane0])[half] = u32x2{h0, h1};
+            reinterpret_cast<u32x2*>(&S.Sx[w][1][lane0])[half] = u32x2{l0, l1};
+            reinterpret_cast<u32x2*>(&S.Sx[w][0][lane1])[half] = u32x2{h2, h3};
+            reinterpret_cast<u32x2*>(&S.Sx[w][1][lane1])[half] = u32x2{l2, l3};
+        }
+        __syncthreads();   // A
+        // P2: Y = K S^T, Z = Q S^T (token tile w); U' = T_b V; publish Gamma Y
+        f32x4 z, up, gam, gs;
+        float gC;
+        bf16x8 tbh[2], tbl[2];
+        {
+            // group 1 (15 LDS reads): gates, S^T blocks, K rows -> Y
+            bf16x8 sh[4], sl[4], ka[4];
+            gam = *reinterpret_cast<const f32x4*>(st.G + kGGam + 16 * w + 4 * g);
+            gs = *reinterpret_cast<const f32x4*>(st.G + kGScale + 16 * w + 4 * g);
+            gC = st.G[kGC];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                sh[m] = xop(S.Sx, m, 0, l);
+                sl[m] = xop(S.Sx, m, 1, l);
+                ka[m] = row_op(st.K, 16 * w + c, m, g);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4 y0 = zero4(), y1 = zero4();
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                y0 = mfma_bf16(ka[m], sh[m], y0);
+                y1 = mfma_bf16(ka[m], sl[m], y1);
+            }
+            put_half(S.Yx, w, l, (y0 + y1) * gam);
+            __builtin_amdgcn_sched_barrier(0);
+            // group 2 (at most 12 LDS reads): Q rows, T_b, V -> Z, U'
+            bf16x8 qa[4], vb[2];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) qa[m] = row_op(st.Q, 16 * w + c, m, g);
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                if (m >= nb) break;   // T_b is lower triangular
+                tbh[m] = packed(st.Tb, w, m, 0, l);
+                tbl[m] = packed(st.Tb, w, m, 1, l);
+                vb[m] = tr_v(st.V, m, l);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4 z0 = zero4(), z1 = zero4();
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                z0 = mfma_bf16(qa[m], sh[m], z0);
+                z1 = mfma_bf16(qa[m], sl[m], z1);
+            }
+            z = z0 + z1;
+            f32x4 q0 = zero4(), q1 = zero4();
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                if (m >= nb) break;
+                q0 = mfma_bf16(tbh[m], vb[m], q0);
+                q1 = mfma_bf16(tbl[m], vb[m], q1);
+            }
+            up = q0 + q1;
+        }
+        __syncthreads();   // B
+        // P3: X = T_b (Gamma Y), U = U' - X; K^T and A operands for P4
+        bf16x8 kt[2][2], ah[2], al[2];
+        {
+            // group 1 (at most 8 LDS reads): Gamma Y blocks and A -> X, U
+            bf16x8 yh[2], yl[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                if (m >= nb) break;
+                yh[m] = xop(S.Yx, m, 0, l);
+                yl[m] = xop(S.Yx, m, 1, l);
+                ah[m] = packed(st.Am, w, m, 0, l);
+                al[m] = packed(st.Am, w, m, 1, l);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4 p0 = zero4(), p1 = zero4(), p2 = zero4();
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                if (m >= nb) break;
+                mma3(tbh[m], tbl[m], yh[m], yl[m], p0, p1, p2);
+            }
+            const f32x4 u = up - (p0 + p1 + p2);
+            put_half(S.Ux, w, l, u);
+            put_half(S.Uy, w, l, u * gs);
+            __builtin_amdgcn_sched_barrier(0);
+            // group 2 (8 transposing reads): K^T operands for P4
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int m = 0; m < 2; ++m) kt[j][m] = tr_op(st.K, m, 2 * w + j, l);
+        }
+        const int t0 = x.rec[4 * ch + 1], len = x.rec[4 * ch + 2];
+        __syncthreads();   // C
+        // P4: S^T = gamma_C S^T + K^T U~;  O = Gamma Z + A U
+        f32x4 p0 = zero4(), p1 = zero4(), p2 = zero4();
+        {
+            bf16x8 uh[2], ul[2], xh[2], xl[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                uh[m] = xop(S.Uy, m, 0, l);
+                ul[m] = xop(S.Uy, m, 1, l);
+            }
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                if (m >= nb) break;
+                xh[m] = xop(S.Ux, m, 0, l);
+                xl[m] = xop(S.Ux, m, 1, l);
+            }
+            f32x4 a0 = s0 * gC, a1 = s1 * gC, b0 = zero4(), b1 = zero4();
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                a0 = mfma_bf16(kt[0][m], uh[m], a0);
+                b0 = mfma_bf16(kt[0][m], ul[m], b0);
+                a1 = mfma_bf16(kt[1][m], uh[m], a1);
+                b1 = mfma_bf16(kt[1][m], ul[m], b1);
+            }
+            s0 = a0 + b0;
+            s1 = a1 + b1;
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                if (m >= nb) break;
+                mma3(ah[m], al[m], xh[m], xl[m], p0, p1, p2);
+            }
+        }
+        {
+            const f32x4 ov = z * gam + (p0 + p1 + p2);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int tok = 16 * w + 4 * g + e;
+                if (tok < len) o[(size_t(t0 + tok) * x.H + x.h) * kD + 16 * x.s + c] = ov[e];
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void walk_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, int N, int H, const int32_t* __restrict__ rec,
+    const int32_t* __restrict__ seq_off, const int32_t* __restrict__ num_chunks,
+    const unsigned char* __restrict__ factors, const float* __restrict__ S0,
+    float* __restrict__ o, float* __restrict__ S_final) {
+    // XCD-aware mapping: the 8 value slices of one (sequence, head) share
+    // blockIdx.x % 8, hence one XCD and its L2, which then holds the chunk's
+    // K, Q and factors once for all of them.
+    const int id = blockIdx.x;
+    const int xcd = id & 7, rest = id >> 3;
+    const int s = rest & 7, pg = rest >> 3;
+    const int p = pg * 8 + xcd;
+    if (p >= N * H) return;
+    const int n = p / H, h = p - n * H;
+
+    __shared__ __attribute__((aligned(16))) Lds lds;
+
+    const int w = wave_id(), l = threadIdx.x & 63, g = l >> 4, c = l & 15;
+    const int nch = num_chunks[0];
+    const int c0 = seq_off[n];
+    const int c_end = seq_off[n + 1] < nch ? seq_off[n + 1] : nch;
+    const Ctx x{q, k, v, factors, rec, H, h, s, l};
+
+    if (w >= kCompute) {
+        if (c0 < c_end) {
+            switch (w - kCompute) {
+                case 0: loader<0>(x, c0, c_end, lds); break;
+                case 1: loader<1>(x, c0, c_end, lds); break;
+                case 2: loader<2>(x, c0, c_end, lds); break;
+                case 3: loader<3>(x, c0, c_end, lds); break;
+                case 4: loader<4>(x, c0, c_end, lds); break;
+                case 5: loader<5>(x, c0, c_end, lds); break;
+                case 6: loader<6>(x, c0, c_end, lds); break;
+                default: loader<7>(x, c0, c_end, lds); break;
+            }
+        }
+        return;
+    }
+    // lane holds S^T[k = 16 kt + 4g + e][v = 16s + c] = S[v][k] for kt = 2w, 2w+1
+    const size_t srow = ((size_t(n) * H + h) * kD + 16 * s + c) * kD + 32 * w + 4 * g;
+    f32x4 s0 = zero4(), s1 = zero4();
+    if (S0) {
+        s0 = *reinterpret_cast<const f32x4*>(S0 + srow);
+        s1 = *reinterpret_cast<const f32x4*>(S0 + srow + 16);
+    }
+    if (c0 < c_end) compute_wave(x, w, c0, c_end, lds, s0, s1, o);
+    if (S_final) {
+        *reinterpret_cast<f32x4*>(S_final + srow) = s0;
+        *reinterpret_cast<f32x4*>(S_final + srow + 16) = s1;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_walk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            int32_t num_seqs, int32_t heads, const int32_t* rec,
+                            const int32_t* seq_off, const int32_t* num_chunks,
+                            const unsigned char* factors, const float* S0, float* o,
+                            float* S_final, hipStream_t stream) {
+    const int64_t pairs = int64_t(num_seqs) * heads;
+    const unsigned grid = unsigned(64 * ((pairs + 7) / 8));
+    hipLaunchKernelGGL(walk_bf16_kernel, dim3(grid), dim3(kThreads), 0, stream, q, k, v, num_seqs,
+                       heads, rec, seq_off, num_chunks, factors, S0, o, S_final);
+    return hipGetLastError();
+}
+
+}  // namespace rda
