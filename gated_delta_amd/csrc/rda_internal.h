@@ -24,8 +24,6 @@ constexpr int kD = RDA_HEAD_DIM;   // dk = dv
 //                 Tb   bf16 hi/lo of T diag(b), T = (I + L)^-1, packed as the
 //                      walk's MFMA A operand (rows = tokens, K dim = tokens)
 //                 Am   bf16 hi/lo of A = lower(Q K^T . Gamma), same packing
-//                      (written for fp32 inputs only; the bf16 walk forms A
-//                      itself from the Q and K tiles it already holds)
 //                 G    fp32 gamma_i (64), gamma_C / gamma_i (64), gamma_C,
 //                      g_i = running sum of log a (64, at float 192)
 // ---------------------------------------------------------------------------
@@ -77,7 +75,12 @@ hipError_t launch_walk(const void* q, const void* k, const void* v, rda_dtype dt
                        const unsigned char* factors, const float* S0, float* o, float* S_final,
                        hipStream_t stream);
 
-// bf16 walk (operands streamed into LDS by a loader wave)
+// bf16 prep (factors from LDS-DMA'd tiles, four workgroups per CU)
+hipError_t launch_prep_bf16(const uint16_t* q, const uint16_t* k, const float* a, const float* b,
+                            int32_t heads, int32_t max_chunks, const int32_t* rec,
+                            const int32_t* num_chunks, unsigned char* factors, hipStream_t stream);
+
+// bf16 walk (operands streamed into LDS by loader waves)
 hipError_t launch_walk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             int32_t num_seqs, int32_t heads, const int32_t* rec,
                             const int32_t* seq_off, const int32_t* num_chunks,
