@@ -7,7 +7,7 @@
 #include <cstddef>
 #include <cstdint>
 
-#include "../../include/rda.h"
+#include "rda.h"
 
 namespace rda {
 

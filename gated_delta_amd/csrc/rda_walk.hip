@@ -1,32 +1,29 @@
 // rda_walk.hip -- the sequential chunk walk of the chunked RDA prefill for
 // bf16 inputs on gfx950 (the chunk algebra and the operand conventions are
 // those stated at the top of rda_prefill.hip; T_b, A and the gates come from
-// its prep kernel).
+// the prep kernel).
 //
-// One workgroup per (sequence, head, 16-channel value slice): 4 compute waves
-// (one per SIMD) and 8 loader waves.  The loaders stream each chunk's operands
-// -- the K and Q tiles, the packed T_b and A factors, the gates and this
-// slice's V columns -- straight into a two-stage LDS ring with LDS-DMA loads
-// (global_load_lds_dwordx4), and touch the lines of chunks further ahead so
-// that they sit in L2 when the DMA asks for them.  The compute waves issue no
-// global loads at all.
-//
-// Compute wave w owns the state S^T for key block w (key tiles 2w, 2w+1, as
-// MFMA accumulators) and token tile w of every chunk-local product.  Per
-// chunk (three barriers):
-//   P1  publish its S^T block (bf16 hi/lo) as ready B operands, key order
-//       natural so that K and Q rows are single 16-byte LDS reads
-//   P2  Y = K S^T and Z = Q S^T for token tile w, U' = T_b V; publish Gamma Y
-//   P3  X = T_b (Gamma Y), U = U' - X; publish U and U~ = diag(gamma_C/gamma) U
-//   P4  S^T = gamma_C S^T + K^T U~ for its key block; O = Gamma Z + A U, stored
-// Stage reads end at the third barrier of a chunk; that stage is refilled
-// with the chunk two ahead during the next chunk (stage of chunk c:
-// (c - first) % 2), and each loader waits for all its loads before the
-// first barrier of a chunk.
-//
-// LDS reads are issued in fenced groups (scheduling barriers) of at most 15:
-// the compiler clamps its lgkmcnt waits to 14 when more are outstanding,
-// which only holds while the 4-bit counter cannot overflow.
+// One workgroup per (sequence, head, 16-channel value slice), three roles:
+//   state waves 0..3   carry the recurrence.  Wave w owns S^T for key block
+//                      w (key tiles 2w, 2w+1, MFMA accumulators) and token
+//                      tile w of the chunk-local products.  Per chunk:
+//     P1  publish its S^T block (bf16 hi/lo) as ready B operands, keys in
+//         natural order so that K and Q rows are single 16-byte reads
+//     P2  Y = K S^T, publish Gamma Y; U' = T_b V
+//     P3  X = T_b (Gamma Y), U = U' - X; publish U and U~ = diag(gamma_C/gamma) U
+//     P4  S^T = gamma_C S^T + K^T U~
+//   output waves 4..7  produce the outputs of token tile tt = w - 4:
+//     P2  Z = Q S^T;  P4  O = Gamma Z + A U, stored
+//   loader waves 8..15 stream each chunk's operands -- the K and Q tiles, the
+//                      packed T_b and A factors, the gates and this slice's V
+//                      columns -- into a two-stage LDS ring with LDS-DMA
+//                      (global_load_lds_dwordx4), and touch the lines of
+//                      chunks further ahead so that they sit in L2 when the
+//                      DMA asks for them.
+// The compute waves issue no global loads at all (a wave stalls when it
+// issues a memory instruction into a full queue, and any such stall would
+// land on the recurrence), and the output work runs beside the recurrence on
+// the other wave slots instead of lengthening it.
 //
 // Past the end of a chunk (len < 64) the loaders duplicate the last valid
 // token row instead of zeroing: T_b has zero rows and columns there (b = 0),
@@ -39,10 +36,12 @@ namespace rda {
 
 namespace {
 
-constexpr int kCompute = 4;                        // compute waves, one per SIMD
-constexpr int kLoaders = 8;                        // loader waves
-constexpr int kThreads = (kCompute + kLoaders) * 64;
-constexpr int kPfAhead = 4;                        // L2 touch distance past the DMA (chunks)
+constexpr int kStateWaves = 4;
+constexpr int kOutWaves = 4;
+constexpr int kLoaders = 8;
+constexpr int kLoader0 = kStateWaves + kOutWaves;   // wave index of the first loader
+constexpr int kThreads = (kStateWaves + kOutWaves + kLoaders) * 64;
+constexpr int kPfAhead = 4;                          // L2 touch distance (chunks)
 
 // One chunk's operands in LDS (68608 bytes, every part whole 1 KiB DMA blocks).
 struct Stage {
@@ -103,9 +102,9 @@ __device__ __forceinline__ const uint16_t* token_row(const uint16_t* base, const
 // The chunk's operands are 67 DMA blocks of 1 KiB: K 0..15, Q 16..31, T_b
 // 32..47, A 48..63, V 64..65, G 66.  Loader i owns the blocks i, i + 8, ...
 // (9 or 8 of them); loaders 0 and 1 also touch one line set each for L2.
-// A chunk's blocks are issued in three parts, one in each barrier window of
-// the chunk before it, so that no window carries a long DMA burst (which
-// would hold back the compute waves' output stores and the next barrier).
+// Spreading a chunk's blocks over three barrier windows keeps any one window
+// free of a long DMA burst, which would hold back the output waves' stores
+// and the next barrier.
 
 __device__ __forceinline__ void issue_block(const Ctx& x, int t0, int len,
                                             const unsigned char* F, int blk, Stage& st) {
@@ -177,14 +176,17 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((kN & 15) | ((kN >> 4) << 14) | 0x0F70);
 }
 
-// Loaders 0 and 1 end every chunk's issue with one L2 touch, the only load
-// they leave pending at a barrier (loads complete in issue order).
+// A chunk's blocks go out in three parts: part 0 right after the third
+// barrier of the chunk two before it (its stage is free from then on),
+// parts 1 and 2 after the first two barriers of the chunk before it.
+// Loaders 0 and 1 end part 0 with one L2 touch.  Before a chunk's first
+// barrier each loader waits until only the part 0 of the chunk after it
+// (and that touch) may still be in flight: loads complete in issue order.
 template <int kI>
 __device__ void loader(const Ctx& x, int c0, int c_end, Lds& S) {
-    constexpr int kPending = kI < 2 ? 1 : 0;
+    constexpr int kPending = 3 + (kI < 2 ? 1 : 0);
     const int last = c_end - 1;
     auto cl = [last](int c) { return c < last ? c : last; };
-    // touches for the first chunks, the first chunk whole, one more touch
     if constexpr (kI < 2) {
 #pragma unroll
         for (int d = 1; d < kPfAhead; ++d) touch_chunk<kI>(x, cl(c0 + d), S.sink);
@@ -192,29 +194,28 @@ __device__ void loader(const Ctx& x, int c0, int c_end, Lds& S) {
     issue_part<kI, 0>(x, c0, S.st[0]);
     issue_part<kI, 1>(x, c0, S.st[0]);
     issue_part<kI, 2>(x, c0, S.st[0]);
+    issue_part<kI, 0>(x, cl(c0 + 1), S.st[1]);
     if constexpr (kI < 2) touch_chunk<kI>(x, cl(c0 + kPfAhead), S.sink);
     for (int c = c0; c < c_end; ++c) {
-        // chunk c + 1 goes to the stage chunk c - 1 used (free since its
-        // third barrier); all loads issued before now, but the last touch,
-        // belong to chunk c
         Stage& nxt = S.st[(c + 1 - c0) & 1];
+        Stage& cur = S.st[(c - c0) & 1];
         const int cn = cl(c + 1);
         wait_vm<kPending>();
         __builtin_amdgcn_s_barrier();   // A
-        issue_part<kI, 0>(x, cn, nxt);
-        __builtin_amdgcn_s_barrier();   // B
         issue_part<kI, 1>(x, cn, nxt);
-        __builtin_amdgcn_s_barrier();   // C
+        __builtin_amdgcn_s_barrier();   // B
         issue_part<kI, 2>(x, cn, nxt);
-        if constexpr (kI < 2) touch_chunk<kI>(x, cl(c + 1 + kPfAhead), S.sink);
+        __builtin_amdgcn_s_barrier();   // C: chunk c's stage is free
+        issue_part<kI, 0>(x, cl(c + 2), cur);
+        if constexpr (kI < 2) touch_chunk<kI>(x, cl(c + 2 + kPfAhead), S.sink);
     }
     wait_vm<0>();   // nothing may land in LDS after the workgroup ends
 }
 
-// ---- compute waves ---------------------------------------------------------------
+// ---- LDS operand helpers -----------------------------------------------------------
 
-// Row r of a swizzled 64 x 128 tile, natural k order: lane (g, c) gets
-// elements 32m + 8g .. +7 (one 16-byte granule).
+// Row r of a swizzled K or Q tile, natural k order: lane (g, c) gets elements
+// 32m + 8g .. +7 (one 16-byte granule).
 __device__ __forceinline__ bf16x8 row_op(const uint16_t* T, int r, int m, int g) {
     const unsigned char* row = reinterpret_cast<const unsigned char*>(T) + r * 256;
     return __builtin_bit_cast(bf16x8,
@@ -228,7 +229,7 @@ __device__ __forceinline__ u32x2 tr_read(const void* p) {
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
 }
 
-// Transposed operand of a swizzled tile: lane (g, c) receives column
+// Transposed operand of the swizzled K tile: lane (g, c) receives column
 // 16 kt + c of rows {32m + 4g + i, 32m + 16 + 4g + i : i < 4} (the permuted
 // token order of the packed factors and of the exchanged U~).
 // ds_read_b64_tr_b16 gives output lane i of a 16-lane group element i % 4 of
@@ -258,10 +259,6 @@ __device__ __forceinline__ bf16x8 xop(const u32x4 (*X)[2][64], int blk, int hl, 
     return __builtin_bit_cast(bf16x8, X[blk][hl][l]);
 }
 
-__device__ __forceinline__ bf16x8 packed(const u32x4 (*P)[64], int tile, int m, int hl, int l) {
-    return __builtin_bit_cast(bf16x8, P[(tile * 2 + m) * 2 + hl][l]);
-}
-
 // Write a D-layout tile's 4 values (hi/lo) into its half of block tile / 2.
 __device__ __forceinline__ void put_half(u32x4 (*X)[2][64], int tile, int l, f32x4 v) {
     uint32_t h01, l01, h23, l23;
@@ -279,154 +276,169 @@ __device__ __forceinline__ void mma3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl,
     p2 = mfma_bf16(al, bh, p2);
 }
 
-__device__ void compute_wave(const Ctx& x, int w, int c0, int c_end, Lds& S, f32x4& s0,
-                             f32x4& s1, float* __restrict__ o) {
+__device__ __forceinline__ bf16x8 packed(const u32x4 (*P)[64], int tile, int m, int hl, int l) {
+    return __builtin_bit_cast(bf16x8, P[(tile * 2 + m) * 2 + hl][l]);
+}
+
+// ---- state waves -------------------------------------------------------------------
+
+__device__ __forceinline__ void state_step(const Ctx& x, int w, const Stage& st, Lds& S,
+                                           f32x4& s0, f32x4& s1) {
     const int l = x.l, g = l >> 4, c = l & 15;
-    // this lane's slots of S^T block w in natural key order: tile 2w (keys
-    // 32w + 4g + i) -> lane c + 16 (g / 2), tile 2w + 1 -> lane c + 16 (2 + g / 2),
-    // both in 8-byte half g % 2
-    const int lane0 = c + 16 * (g >> 1), lane1 = lane0 + 32, half = g & 1;
     const int nb = (w >> 1) + 1;   // token blocks at or below token tile w
-    for (int ch = c0; ch < c_end; ++ch) {
-        const Stage& st = S.st[(ch - c0) & 1];
-        // P1: publish S^T block w
-        {
-            uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
-            split_pk(s0[0], s0[1], h0, l0);
-            split_pk(s0[2], s0[3], h1, l1);
-            split_pk(s1[0], s1[1], h2, l2);
-            split_pk(s1[2], s1[3], h3, l3);
-            reinterpret_cast<u32x2*>(&S.Sx[w][0][lane0])[half] = u32x2{h0, h1};
-            reinterpret_cast<u32x2*>(&S.Sx[w][1][lane0])[half] = u32x2{l0, l1};
-            reinterpret_cast<u32x2*>(&S.Sx[w][0][lane1])[half] = u32x2{h2, h3};
-            reinterpret_cast<u32x2*>(&S.Sx[w][1][lane1])[half] = u32x2{l2, l3};
+    // P1: publish S^T block w in natural key order: tile 2w (keys 32w + 4g + e)
+    // -> lane c + 16 (g / 2), tile 2w + 1 -> lane c + 16 (2 + g / 2), 8-byte half g % 2
+    {
+        const int lane0 = c + 16 * (g >> 1), lane1 = lane0 + 32, half = g & 1;
+        uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+        split_pk(s0[0], s0[1], h0, l0);
+        split_pk(s0[2], s0[3], h1, l1);
+        split_pk(s1[0], s1[1], h2, l2);
+        split_pk(s1[2], s1[3], h3, l3);
+        reinterpret_cast<u32x2*>(&S.Sx[w][0][lane0])[half] = u32x2{h0, h1};
+        reinterpret_cast<u32x2*>(&S.Sx[w][1][lane0])[half] = u32x2{l0, l1};
+        reinterpret_cast<u32x2*>(&S.Sx[w][0][lane1])[half] = u32x2{h2, h3};
+        reinterpret_cast<u32x2*>(&S.Sx[w][1][lane1])[half] = u32x2{l2, l3};
+    }
+    __syncthreads();   // A
+    // P2: Y = K S^T (token tile w), publish Gamma Y; U' = T_b V
+    f32x4 up, gs;
+    float gC;
+    bf16x8 th[2], tl[2];
+    {
+        bf16x8 sh[4], sl[4], ka[4];
+        const f32x4 gam = *reinterpret_cast<const f32x4*>(st.G + kGGam + 16 * w + 4 * g);
+        gs = *reinterpret_cast<const f32x4*>(st.G + kGScale + 16 * w + 4 * g);
+        gC = st.G[kGC];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            sh[m] = xop(S.Sx, m, 0, l);
+            sl[m] = xop(S.Sx, m, 1, l);
+            ka[m] = row_op(st.K, 16 * w + c, m, g);
         }
-        __syncthreads();   // A
-        // P2: Y = K S^T, Z = Q S^T (token tile w); U' = T_b V; publish Gamma Y
-        f32x4 z, up, gam, gs;
-        float gC;
-        bf16x8 tbh[2], tbl[2];
-        {
-            // group 1 (15 LDS reads): gates, S^T blocks, K rows -> Y
-            bf16x8 sh[4], sl[4], ka[4];
-            gam = *reinterpret_cast<const f32x4*>(st.G + kGGam + 16 * w + 4 * g);
-            gs = *reinterpret_cast<const f32x4*>(st.G + kGScale + 16 * w + 4 * g);
-            gC = st.G[kGC];
+        f32x4 y0 = zero4(), y1 = zero4();
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                sh[m] = xop(S.Sx, m, 0, l);
-                sl[m] = xop(S.Sx, m, 1, l);
-                ka[m] = row_op(st.K, 16 * w + c, m, g);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            f32x4 y0 = zero4(), y1 = zero4();
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                y0 = mfma_bf16(ka[m], sh[m], y0);
-                y1 = mfma_bf16(ka[m], sl[m], y1);
-            }
-            put_half(S.Yx, w, l, (y0 + y1) * gam);
-            __builtin_amdgcn_sched_barrier(0);
-            // group 2 (at most 12 LDS reads): Q rows, T_b, V -> Z, U'
-            bf16x8 qa[4], vb[2];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) qa[m] = row_op(st.Q, 16 * w + c, m, g);
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                if (m >= nb) break;   // T_b is lower triangular
-                tbh[m] = packed(st.Tb, w, m, 0, l);
-                tbl[m] = packed(st.Tb, w, m, 1, l);
-                vb[m] = tr_v(st.V, m, l);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            f32x4 z0 = zero4(), z1 = zero4();
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                z0 = mfma_bf16(qa[m], sh[m], z0);
-                z1 = mfma_bf16(qa[m], sl[m], z1);
-            }
-            z = z0 + z1;
-            f32x4 q0 = zero4(), q1 = zero4();
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                if (m >= nb) break;
-                q0 = mfma_bf16(tbh[m], vb[m], q0);
-                q1 = mfma_bf16(tbl[m], vb[m], q1);
-            }
-            up = q0 + q1;
+        for (int m = 0; m < 4; ++m) {
+            y0 = mfma_bf16(ka[m], sh[m], y0);
+            y1 = mfma_bf16(ka[m], sl[m], y1);
         }
-        __syncthreads();   // B
-        // P3: X = T_b (Gamma Y), U = U' - X; K^T and A operands for P4
-        bf16x8 kt[2][2], ah[2], al[2];
-        {
-            // group 1 (at most 8 LDS reads): Gamma Y blocks and A -> X, U
-            bf16x8 yh[2], yl[2];
+        put_half(S.Yx, w, l, (y0 + y1) * gam);
+        f32x4 q0 = zero4(), q1 = zero4();
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                if (m >= nb) break;
-                yh[m] = xop(S.Yx, m, 0, l);
-                yl[m] = xop(S.Yx, m, 1, l);
-                ah[m] = packed(st.Am, w, m, 0, l);
-                al[m] = packed(st.Am, w, m, 1, l);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            f32x4 p0 = zero4(), p1 = zero4(), p2 = zero4();
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                if (m >= nb) break;
-                mma3(tbh[m], tbl[m], yh[m], yl[m], p0, p1, p2);
-            }
-            const f32x4 u = up - (p0 + p1 + p2);
-            put_half(S.Ux, w, l, u);
-            put_half(S.Uy, w, l, u * gs);
-            __builtin_amdgcn_sched_barrier(0);
-            // group 2 (8 transposing reads): K^T operands for P4
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int m = 0; m < 2; ++m) kt[j][m] = tr_op(st.K, m, 2 * w + j, l);
+        for (int m = 0; m < 2; ++m) {
+            if (m >= nb) break;   // T_b is lower triangular
+            th[m] = packed(st.Tb, w, m, 0, l);
+            tl[m] = packed(st.Tb, w, m, 1, l);
+            const bf16x8 vb = tr_v(st.V, m, l);
+            q0 = mfma_bf16(th[m], vb, q0);
+            q1 = mfma_bf16(tl[m], vb, q1);
         }
-        const int t0 = x.rec[4 * ch + 1], len = x.rec[4 * ch + 2];
-        __syncthreads();   // C
-        // P4: S^T = gamma_C S^T + K^T U~;  O = Gamma Z + A U
+        up = q0 + q1;
+    }
+    __syncthreads();   // B
+    // P3: X = T_b (Gamma Y), U = U' - X; K^T operands for P4
+    bf16x8 kt[2][2];
+    {
+        bf16x8 yh[2], yl[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            if (m >= nb) break;
+            yh[m] = xop(S.Yx, m, 0, l);
+            yl[m] = xop(S.Yx, m, 1, l);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int m = 0; m < 2; ++m) kt[j][m] = tr_op(st.K, m, 2 * w + j, l);
         f32x4 p0 = zero4(), p1 = zero4(), p2 = zero4();
-        {
-            bf16x8 uh[2], ul[2], xh[2], xl[2];
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                uh[m] = xop(S.Uy, m, 0, l);
-                ul[m] = xop(S.Uy, m, 1, l);
-            }
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                if (m >= nb) break;
-                xh[m] = xop(S.Ux, m, 0, l);
-                xl[m] = xop(S.Ux, m, 1, l);
-            }
-            f32x4 a0 = s0 * gC, a1 = s1 * gC, b0 = zero4(), b1 = zero4();
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                a0 = mfma_bf16(kt[0][m], uh[m], a0);
-                b0 = mfma_bf16(kt[0][m], ul[m], b0);
-                a1 = mfma_bf16(kt[1][m], uh[m], a1);
-                b1 = mfma_bf16(kt[1][m], ul[m], b1);
-            }
-            s0 = a0 + b0;
-            s1 = a1 + b1;
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                if (m >= nb) break;
-                mma3(ah[m], al[m], xh[m], xl[m], p0, p1, p2);
-            }
+        for (int m = 0; m < 2; ++m) {
+            if (m >= nb) break;
+            mma3(th[m], tl[m], yh[m], yl[m], p0, p1, p2);
         }
-        {
-            const f32x4 ov = z * gam + (p0 + p1 + p2);
+        const f32x4 u = up - (p0 + p1 + p2);
+        put_half(S.Ux, w, l, u);
+        put_half(S.Uy, w, l, u * gs);
+    }
+    __syncthreads();   // C
+    // P4: S^T = gamma_C S^T + K^T U~
+    {
+        bf16x8 uh[2], ul[2];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int tok = 16 * w + 4 * g + e;
-                if (tok < len) o[(size_t(t0 + tok) * x.H + x.h) * kD + 16 * x.s + c] = ov[e];
-            }
+        for (int m = 0; m < 2; ++m) {
+            uh[m] = xop(S.Uy, m, 0, l);
+            ul[m] = xop(S.Uy, m, 1, l);
         }
+        f32x4 a0 = s0 * gC, a1 = s1 * gC, b0 = zero4(), b1 = zero4();
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            a0 = mfma_bf16(kt[0][m], uh[m], a0);
+            b0 = mfma_bf16(kt[0][m], ul[m], b0);
+            a1 = mfma_bf16(kt[1][m], uh[m], a1);
+            b1 = mfma_bf16(kt[1][m], ul[m], b1);
+        }
+        s0 = a0 + b0;
+        s1 = a1 + b1;
+    }
+}
+
+// ---- output waves ------------------------------------------------------------------
+
+__device__ __forceinline__ void output_step(const Ctx& x, int tt, int ch, const Stage& st, Lds& S,
+                                            float* __restrict__ o) {
+    const int l = x.l, g = l >> 4, c = l & 15;
+    const int nb = (tt >> 1) + 1;
+    const int t0 = x.rec[4 * ch + 1], len = x.rec[4 * ch + 2];
+    __syncthreads();   // A
+    // P2: Z = Q S^T; A rows for P4
+    f32x4 z;
+    bf16x8 ah[2], al[2];
+    {
+        bf16x8 sh[4], sl[4], qa[4];
+        const f32x4 gam = *reinterpret_cast<const f32x4*>(st.G + kGGam + 16 * tt + 4 * g);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            sh[m] = xop(S.Sx, m, 0, l);
+            sl[m] = xop(S.Sx, m, 1, l);
+            qa[m] = row_op(st.Q, 16 * tt + c, m, g);
+        }
+        f32x4 z0 = zero4(), z1 = zero4();
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            z0 = mfma_bf16(qa[m], sh[m], z0);
+            z1 = mfma_bf16(qa[m], sl[m], z1);
+        }
+        z = (z0 + z1) * gam;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            if (m >= nb) break;
+            ah[m] = packed(st.Am, tt, m, 0, l);
+            al[m] = packed(st.Am, tt, m, 1, l);
+        }
+    }
+    __syncthreads();   // B
+    __syncthreads();   // C
+    // P4: O = Gamma Z + A U
+    {
+        bf16x8 xh[2], xl[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            if (m >= nb) break;
+            xh[m] = xop(S.Ux, m, 0, l);
+            xl[m] = xop(S.Ux, m, 1, l);
+        }
+        f32x4 p0 = zero4(), p1 = zero4(), p2 = zero4();
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            if (m >= nb) break;
+            mma3(ah[m], al[m], xh[m], xl[m], p0, p1, p2);
+        }
+        const f32x4 ov = z + (p0 + p1 + p2);
+        float* orow = o + (size_t(t0 + 16 * tt + 4 * g) * x.H + x.h) * kD + 16 * x.s + c;
+        const size_t tstride = size_t(x.H) * kD;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (16 * tt + 4 * g + e < len) orow[e * tstride] = ov[e];
     }
 }
 
@@ -454,9 +466,9 @@ __global__ __launch_bounds__(kThreads) void walk_bf16_kernel(
     const int c_end = seq_off[n + 1] < nch ? seq_off[n + 1] : nch;
     const Ctx x{q, k, v, factors, rec, H, h, s, l};
 
-    if (w >= kCompute) {
+    if (w >= kLoader0) {
         if (c0 < c_end) {
-            switch (w - kCompute) {
+            switch (w - kLoader0) {
                 case 0: loader<0>(x, c0, c_end, lds); break;
                 case 1: loader<1>(x, c0, c_end, lds); break;
                 case 2: loader<2>(x, c0, c_end, lds); break;
@@ -469,6 +481,11 @@ __global__ __launch_bounds__(kThreads) void walk_bf16_kernel(
         }
         return;
     }
+    if (w >= kStateWaves) {
+        for (int ch = c0; ch < c_end; ++ch)
+            output_step(x, w - kStateWaves, ch, lds.st[(ch - c0) & 1], lds, o);
+        return;
+    }
     // lane holds S^T[k = 16 kt + 4g + e][v = 16s + c] = S[v][k] for kt = 2w, 2w+1
     const size_t srow = ((size_t(n) * H + h) * kD + 16 * s + c) * kD + 32 * w + 4 * g;
     f32x4 s0 = zero4(), s1 = zero4();
@@ -476,7 +493,7 @@ __global__ __launch_bounds__(kThreads) void walk_bf16_kernel(
         s0 = *reinterpret_cast<const f32x4*>(S0 + srow);
         s1 = *reinterpret_cast<const f32x4*>(S0 + srow + 16);
     }
-    if (c0 < c_end) compute_wave(x, w, c0, c_end, lds, s0, s1, o);
+    for (int ch = c0; ch < c_end; ++ch) state_step(x, w, lds.st[(ch - c0) & 1], lds, s0, s1);
     if (S_final) {
         *reinterpret_cast<f32x4*>(S_final + srow) = s0;
         *reinterpret_cast<f32x4*>(S_final + srow + 16) = s1;
