@@ -1,0 +1,25 @@
+#!/bin/bash
+# Collects the rocprofv3 kernel summary and the HBM counter passes behind
+# profiles/: kernel trace + stats of the default bench command, then one
+# FETCH_SIZE and one WRITE_SIZE pass over the prefill alone and over a plain
+# device copy of known size (the counter calibration).
+#   usage: gated_delta_amd/profile_run.sh OUTDIR
+# Raw rocprofv3 output lands in OUTDIR/prof_*; then
+#   python gated_delta_amd/profile_summary.py OUTDIR
+# condenses it into profiles/.
+set -o pipefail
+R="$(cd "$(dirname "$0")/.." && pwd)"
+OUT="$(mkdir -p "${1:?output directory}" && cd "$1" && pwd)"
+cd /tmp && export TMPDIR=/tmp
+echo "== kernel trace + stats: python bench.py --steps 20 --warmup 3 --no-cpu"
+timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d "$OUT/prof_trace" -o trace \
+    -- python -u "$R/bench.py" --steps 20 --warmup 3 --no-cpu > "$OUT/prof_trace.log" 2>&1 || exit $?
+for ctr in FETCH_SIZE WRITE_SIZE; do
+  for mode in prefill copy; do
+    echo "== pmc $ctr: python bench.py --mode $mode --steps 2 --warmup 1 --no-cpu"
+    timeout -s KILL 120 rocprofv3 --pmc $ctr --output-format csv -d "$OUT/prof_${ctr}_$mode" -o pmc \
+        -- python -u "$R/bench.py" --mode $mode --steps 2 --warmup 1 --no-cpu \
+        > "$OUT/prof_${ctr}_$mode.log" 2>&1 || exit $?
+  done
+done
+echo "== done"

@@ -1,0 +1,121 @@
+"""Condense the rocprofv3 output of profile_run.sh into profiles/.
+
+usage: python gated_delta_amd/profile_summary.py OUTDIR
+
+Writes
+  profiles/kernels_rda_prefill_T16384_H16_decode_B256_H16.txt
+      per-kernel call count and average / total duration of the default
+      bench command (kernel trace + stats);
+  profiles/hbm_traffic.txt
+      FETCH_SIZE and WRITE_SIZE per dispatch of every prefill kernel, each
+      scaled by what the same counter reads for a device copy of known size,
+      as bytes per launch (read by bench.py for its roofline entry), with the
+      hash of the kernel sources they were taken on.
+"""
+import csv
+import glob
+import hashlib
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "gated_delta_amd", "csrc", "*"))):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+# HIP kernel -> the stage name bench.py reports it under
+STAGE = {"chunk_table_kernel": "rda_chunk_table", "prep_bf16_kernel": "rda_prep",
+         "walk_bf16_kernel": "rda_walk", "decode_step_kernel": "rda_decode_step"}
+
+
+def short(name: str) -> str:
+    n = name.replace("rda::(anonymous namespace)::", "").replace("void ", "")
+    return n.split("(")[0].split("<")[0].strip()
+
+
+def find(d, pattern):
+    hits = glob.glob(os.path.join(d, "**", pattern), recursive=True)
+    if not hits:
+        sys.exit(f"no {pattern} under {d}")
+    return hits[0]
+
+
+def counter(d, name):
+    """Average per-dispatch value of counter `name` by kernel (first launch of
+    each kernel skipped when it ran more than once)."""
+    rows = list(csv.DictReader(open(find(d, "*counter_collection.csv"))))
+    by = {}
+    for r in rows:
+        if r["Counter_Name"] != name:
+            continue
+        by.setdefault(short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return {k: statistics.mean(v[1:] if len(v) > 1 else v) for k, v in by.items()}
+
+
+def main():
+    out = sys.argv[1]
+    prof = os.path.join(ROOT, "profiles")
+    os.makedirs(prof, exist_ok=True)
+
+    # ---- kernel trace summary ------------------------------------------------
+    rows = list(csv.DictReader(open(find(os.path.join(out, "prof_trace"), "*kernel_stats.csv"))))
+    lines = ["# rocprofv3 kernel trace, default bench step: RDA prefill T=16384 H=16 d=128 (bf16",
+             "# q/k/v, fp32 state) + one RDA decode step B=256 H=16, 20 timed + 3 warmup steps",
+             "# command: gated_delta_amd/profile_run.sh OUTDIR, whose first pass is",
+             "#   rocprofv3 --kernel-trace --stats --output-format csv -d OUTDIR/prof_trace -o trace \\",
+             "#     -- python bench.py --steps 20 --warmup 3 --no-cpu",
+             "# then python gated_delta_amd/profile_summary.py OUTDIR",
+             f"# kernel sources: {source_hash()}",
+             f"{'kernel':40s} {'calls':>6s} {'avg_us':>10s} {'total_us':>12s} {'pct':>6s}"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"{short(r['Name'])[:40]:40s} {int(r['Calls']):6d} "
+                     f"{float(r['AverageNs']) / 1e3:10.2f} {float(r['TotalDurationNs']) / 1e3:12.1f} "
+                     f"{float(r['Percentage']):6.2f}")
+    path = os.path.join(prof, "kernels_rda_prefill_T16384_H16_decode_B256_H16.txt")
+    open(path, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+    # ---- HBM traffic -------------------------------------------------------------
+    n = 1 << 30   # bytes the calibration copy reads and writes per launch
+    f_copy = counter(os.path.join(out, "prof_FETCH_SIZE_copy"), "FETCH_SIZE")
+    w_copy = counter(os.path.join(out, "prof_WRITE_SIZE_copy"), "WRITE_SIZE")
+    fk = max(f_copy, key=f_copy.get)
+    wk = max(w_copy, key=w_copy.get)
+    f_scale = n / (f_copy[fk] * 1024.0)
+    w_scale = n / (w_copy[wk] * 1024.0)
+    fetch = counter(os.path.join(out, "prof_FETCH_SIZE_prefill"), "FETCH_SIZE")
+    write = counter(os.path.join(out, "prof_WRITE_SIZE_prefill"), "WRITE_SIZE")
+    lines = ["# HBM bytes per launch of the prefill kernels, RDA prefill T=16384 H=16 d=128",
+             "# (bf16 q/k/v).  FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from one",
+             "# rocprofv3 --pmc pass each, scaled by what the same counter reads for a plain",
+             "# device copy of 1 GiB (bench.py --mode copy):",
+             f"#   copy FETCH_SIZE = {f_copy[fk]:.0f} KiB -> scale {f_scale:.3f};"
+             f" copy WRITE_SIZE = {w_copy[wk]:.0f} KiB -> scale {w_scale:.3f}",
+             "# command: gated_delta_amd/profile_run.sh OUTDIR (passes",
+             "#   rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE --output-format csv -d OUTDIR/prof_<ctr>_<mode> -o pmc \\",
+             "#     -- python bench.py --mode prefill|copy --steps 2 --warmup 1 --no-cpu)",
+             "# then python gated_delta_amd/profile_summary.py OUTDIR",
+             f"source_hash = {source_hash()}",
+             f"fetch_scale = {f_scale:.4f}",
+             f"write_scale = {w_scale:.4f}"]
+    for k in sorted(set(fetch) | set(write)):
+        fb = fetch.get(k, 0.0) * 1024.0 * f_scale
+        wb = write.get(k, 0.0) * 1024.0 * w_scale
+        name = STAGE.get(k, k)
+        lines.append(f"{name}.kernel = {k}")
+        lines.append(f"{name}.fetch_bytes = {fb:.0f}")
+        lines.append(f"{name}.write_bytes = {wb:.0f}")
+        lines.append(f"{name}.bytes_per_launch = {fb + wb:.0f}")
+    path = os.path.join(prof, "hbm_traffic.txt")
+    open(path, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    main()
