@@ -42,6 +42,95 @@ rda_status record(hipEvent_t const* ev, int idx, hipStream_t stream) {
     return RDA_OK;
 }
 
+// Everything a prefill launch sequence needs, validated.
+struct Prefill {
+    const void *q, *k, *v;
+    rda_dtype dt;
+    const float *a, *b;
+    const int32_t* cu;
+    int32_t N, T, H, mc;
+    const float* S0;
+    float *o, *S_final;
+    int32_t *rec, *seq_off, *nch;
+    unsigned char* factors;
+};
+
+rda_status check_prefill(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
+                         const float* a, const float* b, const int32_t* cu_seqlens,
+                         int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t dk,
+                         int32_t dv, const float* S0, float* o, float* S_final, void* workspace,
+                         size_t workspace_bytes, Prefill& P) {
+    if (qkv_dtype != RDA_BF16 && qkv_dtype != RDA_FP32) return RDA_ERR_DTYPE;
+    if (total_tokens < 0 || num_seqs < 1) return RDA_ERR_SHAPE;
+    if (!cu_seqlens && num_seqs != 1) return RDA_ERR_SHAPE;
+    rda_status st = check_dims(num_heads, dk, dv);
+    if (st != RDA_OK) return st;
+    const int32_t mc = rda_max_chunks(num_seqs, total_tokens);
+    if (mc < 0) return RDA_ERR_SHAPE;
+    if (int64_t(mc) * num_heads > INT32_MAX || int64_t(num_seqs) * num_heads * kWalkSlices > INT32_MAX)
+        return RDA_ERR_SHAPE;
+    if (total_tokens > 0 && (!q || !k || !v || !a || !b || !o)) return RDA_ERR_NULL;
+    if (!workspace) return RDA_ERR_WORKSPACE;
+    const size_t need = rda_prefill_workspace_bytes(num_seqs, total_tokens, num_heads, dk, dv);
+    if (workspace_bytes < need) return RDA_ERR_WORKSPACE;
+    for (const void* p : {q, k, v, static_cast<const void*>(a), static_cast<const void*>(b),
+                          static_cast<const void*>(S0), static_cast<const void*>(o),
+                          static_cast<const void*>(S_final), static_cast<const void*>(workspace)})
+        if (p && !aligned16(p)) return RDA_ERR_ALIGN;
+    if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return RDA_ERR_ALIGN;
+
+    const size_t esz = qkv_dtype == RDA_BF16 ? 2 : 4;
+    const size_t th = size_t(total_tokens) * num_heads;
+    const size_t sbytes = size_t(num_seqs) * num_heads * kD * kD * sizeof(float);
+    const Range rq = rng(q, th * kD * esz), rk = rng(k, th * kD * esz), rv = rng(v, th * kD * esz);
+    const Range ra = rng(a, th * 4), rb = rng(b, th * 4);
+    const Range ro = rng(o, th * kD * 4), rs0 = rng(S0, S0 ? sbytes : 0);
+    const Range rsf = rng(S_final, S_final ? sbytes : 0), rws = rng(workspace, need);
+    const Range rcu = rng(cu_seqlens, cu_seqlens ? size_t(num_seqs + 1) * 4 : 0);
+    for (Range in : {rq, rk, rv, ra, rb, rs0, rcu, rsf, rws})
+        if (overlap(ro, in)) return RDA_ERR_ALIAS;
+    for (Range in : {rq, rk, rv, ra, rb, rcu, rws})
+        if (overlap(rsf, in)) return RDA_ERR_ALIAS;
+    if (S0 && S_final && S0 != S_final && overlap(rs0, rsf)) return RDA_ERR_ALIAS;
+    for (Range in : {rq, rk, rv, ra, rb, rs0, rcu})
+        if (overlap(rws, in)) return RDA_ERR_ALIAS;
+
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    const TableLayout tl = table_layout(mc, num_seqs);
+    P = Prefill{q, k, v, qkv_dtype, a, b, cu_seqlens, num_seqs, total_tokens, num_heads, mc,
+                S0, o, S_final,
+                reinterpret_cast<int32_t*>(ws + tl.rec_off),
+                reinterpret_cast<int32_t*>(ws + tl.seq_off_off),
+                reinterpret_cast<int32_t*>(ws + tl.num_off), ws + align256(tl.bytes)};
+    return RDA_OK;
+}
+
+// Table, prep and walk one after another on `stream`, each stage bracketed
+// by its event pair when `ev` is given.  (Running the prep of later chunks
+// beside the walk of earlier ones on a second stream was measured: the
+// walk's chunk steps slow down under the prep's memory traffic by about as
+// much as the overlap hides, so the stages stay in sequence.)
+rda_status prefill_sequential(const Prefill& P, hipStream_t stream, hipEvent_t const* ev) {
+    rda_status st;
+    if ((st = record(ev, 2 * RDA_STAGE_TABLE, stream)) != RDA_OK) return st;
+    if (launch_chunk_table(P.cu, P.N, P.T, P.mc, P.rec, P.seq_off, P.nch, stream) != hipSuccess)
+        return RDA_ERR_HIP;
+    if ((st = record(ev, 2 * RDA_STAGE_TABLE + 1, stream)) != RDA_OK) return st;
+    if ((st = record(ev, 2 * RDA_STAGE_PREP, stream)) != RDA_OK) return st;
+    if (P.mc > 0 && P.T > 0) {
+        if (launch_prep(P.q, P.k, P.dt, P.a, P.b, P.H, P.mc, P.rec, P.nch, P.factors, stream) !=
+            hipSuccess)
+            return RDA_ERR_HIP;
+    }
+    if ((st = record(ev, 2 * RDA_STAGE_PREP + 1, stream)) != RDA_OK) return st;
+    if ((st = record(ev, 2 * RDA_STAGE_WALK, stream)) != RDA_OK) return st;
+    if (launch_walk(P.q, P.k, P.v, P.dt, P.N, P.H, P.rec, P.seq_off, P.nch, P.factors, P.S0, P.o,
+                    P.S_final, stream) != hipSuccess)
+        return RDA_ERR_HIP;
+    if ((st = record(ev, 2 * RDA_STAGE_WALK + 1, stream)) != RDA_OK) return st;
+    return RDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -85,68 +174,12 @@ rda_status rda_prefill_profiled(const void* q, const void* k, const void* v, rda
                                 int32_t dk, int32_t dv, const float* S0, float* o, float* S_final,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream,
                                 hipEvent_t const* stage_events) {
-    if (qkv_dtype != RDA_BF16 && qkv_dtype != RDA_FP32) return RDA_ERR_DTYPE;
-    if (total_tokens < 0 || num_seqs < 1) return RDA_ERR_SHAPE;
-    if (!cu_seqlens && num_seqs != 1) return RDA_ERR_SHAPE;
-    rda_status st = check_dims(num_heads, dk, dv);
+    Prefill P;
+    const rda_status st = check_prefill(q, k, v, qkv_dtype, a, b, cu_seqlens, num_seqs,
+                                        total_tokens, num_heads, dk, dv, S0, o, S_final,
+                                        workspace, workspace_bytes, P);
     if (st != RDA_OK) return st;
-    const int32_t mc = rda_max_chunks(num_seqs, total_tokens);
-    if (mc < 0) return RDA_ERR_SHAPE;
-    if (int64_t(mc) * num_heads > INT32_MAX || int64_t(num_seqs) * num_heads * kWalkSlices > INT32_MAX)
-        return RDA_ERR_SHAPE;
-    if (total_tokens > 0 && (!q || !k || !v || !a || !b || !o)) return RDA_ERR_NULL;
-    if (!workspace) return RDA_ERR_WORKSPACE;
-    const size_t need = rda_prefill_workspace_bytes(num_seqs, total_tokens, num_heads, dk, dv);
-    if (workspace_bytes < need) return RDA_ERR_WORKSPACE;
-    for (const void* p : {q, k, v, static_cast<const void*>(a), static_cast<const void*>(b),
-                          static_cast<const void*>(S0), static_cast<const void*>(o),
-                          static_cast<const void*>(S_final), static_cast<const void*>(workspace)})
-        if (p && !aligned16(p)) return RDA_ERR_ALIGN;
-    if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return RDA_ERR_ALIGN;
-
-    const size_t esz = qkv_dtype == RDA_BF16 ? 2 : 4;
-    const size_t th = size_t(total_tokens) * num_heads;
-    const size_t sbytes = size_t(num_seqs) * num_heads * kD * kD * sizeof(float);
-    const Range rq = rng(q, th * kD * esz), rk = rng(k, th * kD * esz), rv = rng(v, th * kD * esz);
-    const Range ra = rng(a, th * 4), rb = rng(b, th * 4);
-    const Range ro = rng(o, th * kD * 4), rs0 = rng(S0, S0 ? sbytes : 0);
-    const Range rsf = rng(S_final, S_final ? sbytes : 0), rws = rng(workspace, need);
-    const Range rcu = rng(cu_seqlens, cu_seqlens ? size_t(num_seqs + 1) * 4 : 0);
-    for (Range in : {rq, rk, rv, ra, rb, rs0, rcu, rsf, rws})
-        if (overlap(ro, in)) return RDA_ERR_ALIAS;
-    for (Range in : {rq, rk, rv, ra, rb, rcu, rws})
-        if (overlap(rsf, in)) return RDA_ERR_ALIAS;
-    if (S0 && S_final && S0 != S_final && overlap(rs0, rsf)) return RDA_ERR_ALIAS;
-    for (Range in : {rq, rk, rv, ra, rb, rs0, rcu})
-        if (overlap(rws, in)) return RDA_ERR_ALIAS;
-
-    unsigned char* ws = static_cast<unsigned char*>(workspace);
-    const TableLayout tl = table_layout(mc, num_seqs);
-    int32_t* rec = reinterpret_cast<int32_t*>(ws + tl.rec_off);
-    int32_t* seq_off = reinterpret_cast<int32_t*>(ws + tl.seq_off_off);
-    int32_t* nch = reinterpret_cast<int32_t*>(ws + tl.num_off);
-    unsigned char* factors = ws + align256(tl.bytes);
-
-    if ((st = record(stage_events, 2 * RDA_STAGE_TABLE, stream)) != RDA_OK) return st;
-    if (launch_chunk_table(cu_seqlens, num_seqs, total_tokens, mc, rec, seq_off, nch, stream) !=
-        hipSuccess)
-        return RDA_ERR_HIP;
-    if ((st = record(stage_events, 2 * RDA_STAGE_TABLE + 1, stream)) != RDA_OK) return st;
-
-    if ((st = record(stage_events, 2 * RDA_STAGE_PREP, stream)) != RDA_OK) return st;
-    if (mc > 0 && total_tokens > 0) {
-        if (launch_prep(q, k, qkv_dtype, a, b, num_heads, mc, rec, nch, factors, stream) !=
-            hipSuccess)
-            return RDA_ERR_HIP;
-    }
-    if ((st = record(stage_events, 2 * RDA_STAGE_PREP + 1, stream)) != RDA_OK) return st;
-
-    if ((st = record(stage_events, 2 * RDA_STAGE_WALK, stream)) != RDA_OK) return st;
-    if (launch_walk(q, k, v, qkv_dtype, num_seqs, num_heads, rec, seq_off, nch, factors, S0, o,
-                    S_final, stream) != hipSuccess)
-        return RDA_ERR_HIP;
-    if ((st = record(stage_events, 2 * RDA_STAGE_WALK + 1, stream)) != RDA_OK) return st;
-    return RDA_OK;
+    return prefill_sequential(P, stream, stage_events);
 }
 
 rda_status rda_prefill(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
@@ -154,9 +187,12 @@ rda_status rda_prefill(const void* q, const void* k, const void* v, rda_dtype qk
                        int32_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
                        const float* S0, float* o, float* S_final, void* workspace,
                        size_t workspace_bytes, hipStream_t stream) {
-    return rda_prefill_profiled(q, k, v, qkv_dtype, a, b, cu_seqlens, num_seqs, total_tokens,
-                                num_heads, dk, dv, S0, o, S_final, workspace, workspace_bytes,
-                                stream, nullptr);
+    Prefill P;
+    const rda_status st = check_prefill(q, k, v, qkv_dtype, a, b, cu_seqlens, num_seqs,
+                                        total_tokens, num_heads, dk, dv, S0, o, S_final,
+                                        workspace, workspace_bytes, P);
+    if (st != RDA_OK) return st;
+    return prefill_sequential(P, stream, nullptr);
 }
 
 rda_status rda_decode_step(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,

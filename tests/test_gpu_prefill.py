@@ -178,3 +178,21 @@ def test_random_unnormalised_inputs(dev):
     q *= rng.uniform(0.2, 3.0, (150, 3, 1)).astype(np.float32)
     p = synth.PrefillInputs(q, k, v, a, b, None, S0.astype(np.float32), False)
     check_against_oracle("unnormalised fp32", p, dev)
+
+
+@pytest.mark.parametrize("T,H", [(513, 16), (7000, 16)])
+def test_profiled_entry_point_matches(dev, T, H):
+    """rda_prefill_profiled (stage events) and rda_prefill agree bit for bit."""
+    p = synth.make_prefill(T, H, bf16=True, s0_std=0.02, key=(110, T, H))
+    say(f"[prefill] profiled vs plain entry point T={T} H={H}")
+    q, k, v = (dev_tokens(getattr(p, n), True, dev) for n in "qkv")
+    a, b = dev_f32(p.a, dev), dev_f32(p.b, dev)
+    S0 = dev_f32(p.S0, dev)
+    o1, S1 = rda.rda_prefill(q, k, v, a, b, S0=S0)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * rda.RDA_NUM_STAGES)]
+    o2, S2 = rda.rda_prefill(q, k, v, a, b, S0=S0, stage_events=ev)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    ro, rS = run_oracle(p)
+    assert_parity("plain o", to_host(o1), ro)
+    assert_parity("plain S_final", to_host(S1), rS)
