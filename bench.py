@@ -8,13 +8,14 @@ pre-drawn bf16 tokens).  Inputs are resident in HBM before the timed region.
 
 Prints ONE JSON line:
   value      prefill tokens/s on the long-prompt workload: T / the mean time of
-             one rda_prefill call between HIP events on its stream (its prep
-             overlaps its walk; the decode step between calls streams 512 MiB,
-             so no prefill starts with its inputs in the Infinity Cache)
+             one rda_prefill call between HIP events on its stream (prep,
+             then walk; the decode step between calls streams 512 MiB, so no
+             prefill starts with its inputs in the Infinity Cache)
   decode     decode state bandwidth (algorithmic bytes / kernel time)
   roofline   the kernel with the largest time per step, against its bound
   kernels    every kernel's average duration (HIP events on its stream), from
-             calls of rda_prefill_profiled, which runs the stages in sequence
+             calls of rda_prefill_profiled; for one sequence without offsets
+             the prep kernel writes the chunk table, so no table kernel runs
   cpu_baseline  the fp64 oracle on the same prefill inputs, host cores
   parity     rel-L2 / max-abs of this run's prefill output vs the oracle
 
@@ -231,6 +232,8 @@ def main():
         kb = {0: 0.0, 1: PREFILL_IN_BYTES * units,
               2: PREFILL_OUT_BYTES * units + 2 * H * STATE_BYTES}
         for s in range(rda.RDA_NUM_STAGES):
+            if s == rda.RDA_STAGE_TABLE:
+                continue    # no cu_seqlens: the table is written by the prep kernel
             ms = float(np.mean(st[:, s]))
             kernels[names[s]] = {"avg_us": ms * 1e3, "alg_bytes": kb[s]}
     if do_decode:

@@ -75,10 +75,17 @@ hipError_t launch_walk(const void* q, const void* k, const void* v, rda_dtype dt
                        const unsigned char* factors, const float* S0, float* o, float* S_final,
                        hipStream_t stream);
 
-// bf16 prep (factors from LDS-DMA'd tiles, four workgroups per CU)
+// bf16 prep (factors from LDS-DMA'd tiles, four workgroups per CU).  With
+// single_T >= 0 the input is one sequence of single_T tokens without offsets:
+// rec / num_chunks are not read, the grid covers ceil(single_T / 64) chunks,
+// and the kernel writes the chunk table to rec_out / seq_off_out / num_out.
+// With single_T < 0 the table in rec / num_chunks is read and the *_out
+// pointers are unused.
 hipError_t launch_prep_bf16(const uint16_t* q, const uint16_t* k, const float* a, const float* b,
                             int32_t heads, int32_t max_chunks, const int32_t* rec,
-                            const int32_t* num_chunks, unsigned char* factors, hipStream_t stream);
+                            const int32_t* num_chunks, unsigned char* factors, int32_t single_T,
+                            int32_t* rec_out, int32_t* seq_off_out, int32_t* num_out,
+                            hipStream_t stream);
 
 // bf16 walk (operands streamed into LDS by loader waves)
 hipError_t launch_walk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -777,7 +777,8 @@ hipError_t launch_prep(const void* q, const void* k, rda_dtype dt, const float* 
     if (grid == 0) return hipSuccess;
     if (dt == RDA_BF16) {
         return launch_prep_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), a,
-                                b, heads, max_chunks, rec, num_chunks, factors, stream);
+                                b, heads, max_chunks, rec, num_chunks, factors, -1, nullptr,
+                                nullptr, nullptr, stream);
     } else {
         hipLaunchKernelGGL(prep_kernel<true>, dim3(grid), dim3(256), 0, stream,
                            static_cast<const float*>(q), static_cast<const float*>(k), a, b,

@@ -57,13 +57,35 @@ __device__ __forceinline__ bf16x8 row_op(const uint16_t* T, int r, int m, int g)
 __global__ __launch_bounds__(256) void prep_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ a,
     const float* __restrict__ b, int H, const int32_t* __restrict__ rec,
-    const int32_t* __restrict__ num_chunks, unsigned char* __restrict__ factors) {
+    const int32_t* __restrict__ num_chunks, unsigned char* __restrict__ factors,
+    int32_t single_T, int32_t* __restrict__ rec_out, int32_t* __restrict__ seq_off_out,
+    int32_t* __restrict__ num_out) {
     __shared__ __attribute__((aligned(16))) PrepLds S;
     const int chunk = blockIdx.x / H;
     const int h = blockIdx.x - chunk * H;
-    if (chunk >= num_chunks[0]) return;
-    const int t0 = rec[4 * chunk + 1];
-    const int len = rec[4 * chunk + 2];
+    int t0, len;
+    if (single_T >= 0) {
+        // one sequence of single_T tokens and no offsets: every chunk record
+        // is plain arithmetic (the grid holds exactly ceil(single_T / 64)
+        // chunks), and the head-0 workgroups also write the chunk table the
+        // walk reads, so that no table kernel runs for this case
+        t0 = kC * chunk;
+        len = single_T - t0 < kC ? single_T - t0 : kC;
+        if (h == 0 && threadIdx.x < 4) {
+            const int32_t field[4] = {0, t0, len, chunk};
+            rec_out[4 * chunk + threadIdx.x] = field[threadIdx.x];
+            if (chunk == 0) {
+                const int32_t nch = int32_t(gridDim.x / H);
+                if (threadIdx.x == 0) seq_off_out[0] = 0;
+                if (threadIdx.x == 1) seq_off_out[1] = nch;
+                if (threadIdx.x == 2) num_out[0] = nch;
+            }
+        }
+    } else {
+        if (chunk >= num_chunks[0]) return;
+        t0 = rec[4 * chunk + 1];
+        len = rec[4 * chunk + 2];
+    }
     const int tid = threadIdx.x;
     const int w = wave_id(), l = tid & 63, g = l >> 4, c = l & 15;
     unsigned char* F = factors + (size_t(chunk) * H + h) * kChunkHeadBytes;
@@ -261,11 +283,14 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(
 
 hipError_t launch_prep_bf16(const uint16_t* q, const uint16_t* k, const float* a, const float* b,
                             int32_t heads, int32_t max_chunks, const int32_t* rec,
-                            const int32_t* num_chunks, unsigned char* factors, hipStream_t stream) {
+                            const int32_t* num_chunks, unsigned char* factors, int32_t single_T,
+                            int32_t* rec_out, int32_t* seq_off_out, int32_t* num_out,
+                            hipStream_t stream) {
+    if (single_T >= 0) max_chunks = (single_T + kC - 1) / kC;
     const unsigned grid = unsigned(int64_t(max_chunks) * heads);
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL(prep_bf16_kernel, dim3(grid), dim3(256), 0, stream, q, k, a, b, heads, rec,
-                       num_chunks, factors);
+                       num_chunks, factors, single_T, rec_out, seq_off_out, num_out);
     return hipGetLastError();
 }
 

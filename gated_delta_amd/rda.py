@@ -23,6 +23,7 @@ RDA_BF16 = 0
 RDA_FP32 = 1
 RDA_CHUNK = 64
 RDA_HEAD_DIM = 128
+RDA_STAGE_TABLE, RDA_STAGE_PREP, RDA_STAGE_WALK = 0, 1, 2
 RDA_NUM_STAGES = 3
 STAGES = ("table", "prep", "walk")
 

@@ -70,7 +70,8 @@ typedef enum { RDA_BF16 = 0, RDA_FP32 = 1 } rda_dtype;
 
 /* Stages of one rda_prefill call, in launch order (for rda_prefill_profiled). */
 typedef enum {
-    RDA_STAGE_TABLE = 0, /* chunk table from cu_seqlens */
+    RDA_STAGE_TABLE = 0, /* chunk table from cu_seqlens (empty for one bf16 sequence
+                            with cu_seqlens NULL: the prep kernel writes the table) */
     RDA_STAGE_PREP = 1,  /* per-chunk intra-chunk solve and WY products (parallel) */
     RDA_STAGE_WALK = 2,  /* inter-chunk state passing and outputs (sequential per sequence) */
     RDA_NUM_STAGES = 3

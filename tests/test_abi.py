@@ -40,6 +40,16 @@ def test_header_declares_the_entry_points():
         assert n in names
 
 
+def test_binding_constants_match_header():
+    text = open(HEADER).read()
+    vals = {m[0]: int(m[1]) for m in re.findall(r"\b(RDA_[A-Z0-9_]+)\s*=\s*(\d+)", text)}
+    vals.update({m[0]: int(m[1]) for m in
+                 re.findall(r"#define\s+(RDA_[A-Z0-9_]+)\s+(\d+)", text)})
+    for name in ("RDA_BF16", "RDA_FP32", "RDA_CHUNK", "RDA_HEAD_DIM", "RDA_STAGE_TABLE",
+                 "RDA_STAGE_PREP", "RDA_STAGE_WALK", "RDA_NUM_STAGES"):
+        assert getattr(rda, name) == vals[name], name
+
+
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), f"librda.so does not export {name}"

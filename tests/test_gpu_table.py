@@ -58,3 +58,35 @@ def test_malformed_offsets_stay_in_bounds(dev):
     assert 0 <= n <= table_ref.max_chunks(N, T)
     for r in rec[:n]:
         assert 0 <= r[0] < N and 0 <= r[1] and 1 <= r[2] <= 64 and r[1] + r[2] <= T
+
+
+def _align256(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 1000, 16384])
+def test_prep_written_table_single_sequence(dev, T):
+    """One bf16 sequence without offsets: the prep kernel writes the chunk
+    table itself (no table kernel runs).  Read it back from the workspace
+    (library-internal layout: records at 0, then sequence offsets and the
+    chunk count at the next 256-byte boundaries) and compare with the integer
+    reference; the workspace starts filled with a byte pattern so that a
+    missing write shows."""
+    H = 2
+    say(f"[table] prep-written T={T}")
+    p = synth.make_prefill(T, H, bf16=True, key=(900, T))
+    q, k, v = (torch.from_numpy(getattr(p, n)).to(dev).to(torch.bfloat16) for n in "qkv")
+    a, b = (torch.from_numpy(x).to(dev) for x in (p.a, p.b))
+    mc = table_ref.max_chunks(1, T)
+    ws = torch.full((rda.rda_prefill_workspace_bytes(1, T, H),), 0x5A, dtype=torch.uint8,
+                    device=dev)
+    rda.rda_prefill(q, k, v, a, b, workspace=ws)
+    torch.cuda.synchronize()
+    w = to_host(ws)
+    so = _align256(mc * 16)
+    no = so + _align256(2 * 4)
+    rec = w[:mc * 16].view(np.int32).reshape(mc, 4)
+    off = w[so:so + 8].view(np.int32)
+    n = int(w[no:no + 4].view(np.int32)[0])
+    rrec, roff, rn = table_ref.chunk_table(None, 1, T)
+    assert n == rn and np.array_equal(off, roff) and np.array_equal(rec, rrec)
