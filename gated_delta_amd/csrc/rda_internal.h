@@ -24,6 +24,9 @@ constexpr int kD = RDA_HEAD_DIM;   // dk = dv
 //                 Tb   bf16 hi/lo of T diag(b), T = (I + L)^-1, packed as the
 //                      walk's MFMA A operand (rows = tokens, K dim = tokens)
 //                 Am   bf16 hi/lo of A = lower(Q K^T . Gamma), same packing
+//                      (for both: the slots of token tiles 0 and 1 against
+//                      key block 1 are zero; the bf16 kernels neither write
+//                      nor read them)
 //                 G    fp32 gamma_i (64), gamma_C / gamma_i (64), gamma_C,
 //                      g_i = running sum of log a (64, at float 192)
 // ---------------------------------------------------------------------------

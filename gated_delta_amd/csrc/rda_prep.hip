@@ -174,10 +174,12 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(
                 at[t] = zero4();
             }
         }
-        // A slots (w, m): row 16w + c, tokens {32m + 4g + e, 32m + 16 + 4g + e}
+        // A slots (w, m): row 16w + c, tokens {32m + 4g + e, 32m + 16 + 4g + e};
+        // slots (w < 2, m = 1) are zero and never read, so they are not written
         bf16x8* P = reinterpret_cast<bf16x8*>(F + kOffA);
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
+            if (m > (w >> 1)) break;
             const float x8[8] = {at[2 * m][0],     at[2 * m][1],     at[2 * m][2],
                                  at[2 * m][3],     at[2 * m + 1][0], at[2 * m + 1][1],
                                  at[2 * m + 1][2], at[2 * m + 1][3]};
@@ -253,6 +255,7 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(
         bf16x8* P = reinterpret_cast<bf16x8*>(F + kOffTb);
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
+            if (m > (w >> 1)) break;   // zero slot, never read
             const int r = 16 * w + c, c0 = 32 * m + 4 * g;
             const f32x4 x0 = *reinterpret_cast<const f32x4*>(Ts + r * kFS + c0);
             const f32x4 x1 = *reinterpret_cast<const f32x4*>(Ts + r * kFS + c0 + 16);

@@ -157,7 +157,17 @@ __device__ __forceinline__ void touch_chunk(const Ctx& x, int chunk, float* sink
     dma4(a, sink);
 }
 
-// Part kPart (0..2) of loader kI's blocks of `chunk`.
+// Blocks of the packed factors that no wave reads: slots (tile, block 1) of
+// token tiles 0 and 1, whose operands are zero (both factors are lower
+// triangular).  They are neither written by the prep kernel nor streamed.
+constexpr bool unread_block(int blk) {
+    const int slot = (blk - 32) & 15;   // (tile * 2 + block) * 2 + hi/lo
+    return blk >= 32 && blk < 64 && ((slot >> 1) & 1) == 1 && (slot >> 2) < 2;
+}
+
+// Part kPart (0..2) of loader kI's blocks of `chunk`.  The skipped blocks all
+// fall in parts 1 and 2, so the count of part 0 that the waits rely on is
+// the same for every loader.
 template <int kI, int kPart>
 __device__ __forceinline__ void issue_part(const Ctx& x, int chunk, Stage& st) {
     const int t0 = x.rec[4 * chunk + 1], len = x.rec[4 * chunk + 2];
@@ -165,7 +175,8 @@ __device__ __forceinline__ void issue_part(const Ctx& x, int chunk, Stage& st) {
 #pragma unroll
     for (int q = 3 * kPart; q < 3 * kPart + 3; ++q) {
         const int blk = kI + 8 * q;
-        if (blk < 67) issue_block(x, t0, len, F, blk, st);
+        static_assert(kPart > 0 || kI + 8 * 2 < 32, "part 0 holds no factor block");
+        if (blk < 67 && !unread_block(blk)) issue_block(x, t0, len, F, blk, st);
     }
 }
 
