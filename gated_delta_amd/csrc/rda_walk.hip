@@ -9,8 +9,9 @@
 //                      tile w of the chunk-local products.  Per chunk:
 //     P1  publish its S^T block (bf16 hi/lo) as ready B operands, keys in
 //         natural order so that K and Q rows are single 16-byte reads
-//     P2  Y = K S^T, publish Gamma Y; U' = T_b V
-//     P3  X = T_b (Gamma Y), U = U' - X; publish U and U~ = diag(gamma_C/gamma) U
+//     P2  Y = K S^T, publish E = V - Gamma Y (the chunk's errors before the
+//         solve)
+//     P3  U = T_b E; publish U and U~ = diag(gamma_C/gamma) U
 //     P4  S^T = gamma_C S^T + K^T U~
 //   output waves 4..7  produce the outputs of token tile tt = w - 4:
 //     P2  Z = Q S^T;  P4  O = Gamma Z + A U, stored
@@ -56,7 +57,7 @@ struct Stage {
 struct Lds {
     Stage st[2];
     u32x4 Sx[4][2][64];    // S^T key block m hi/lo; lane (g, c): keys 32m + 8g .. +7, column c
-    u32x4 Yx[2][2][64];    // Gamma Y token block (tiles 2m, 2m+1) hi/lo
+    u32x4 Ex[2][2][64];    // E token block (tiles 2m, 2m+1) hi/lo
     u32x4 Ux[2][2][64];    // U
     u32x4 Uy[2][2][64];    // U~
     float sink[64];        // landing words of the L2 touches
@@ -256,14 +257,12 @@ __device__ __forceinline__ bf16x8 tr_op(const uint16_t* T, int m, int kt, int l)
     return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
 }
 
-// Transposed operand of the V slice (32-byte rows): channel c, tokens of block m.
-__device__ __forceinline__ bf16x8 tr_v(const uint16_t* V, int m, int l) {
+// This slice's V in accumulator layout for token tile t: lane (g, c) gets
+// channel c of tokens 16t + 4g + i, i < 4 (one transposing read).
+__device__ __forceinline__ u32x2 tr_vd(const uint16_t* V, int t, int l) {
     const int g = l >> 4, j = l & 15;
-    const unsigned char* p =
-        reinterpret_cast<const unsigned char*>(V) + (32 * m + 4 * g + (j >> 2)) * 32 + 8 * (j & 3);
-    const u32x2 a = tr_read(p);
-    const u32x2 b = tr_read(p + 16 * 32);
-    return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+    return tr_read(reinterpret_cast<const unsigned char*>(V) + (16 * t + 4 * g + (j >> 2)) * 32 +
+                   8 * (j & 3));
 }
 
 __device__ __forceinline__ bf16x8 xop(const u32x4 (*X)[2][64], int blk, int hl, int l) {
@@ -312,15 +311,15 @@ __device__ __forceinline__ void state_step(const Ctx& x, int w, const Stage& st,
         reinterpret_cast<u32x2*>(&S.Sx[w][1][lane1])[half] = u32x2{l2, l3};
     }
     __syncthreads();   // A
-    // P2: Y = K S^T (token tile w), publish Gamma Y; U' = T_b V
-    f32x4 up, gs;
+    // P2: Y = K S^T (token tile w), publish E = V - Gamma Y
+    f32x4 gs;
     float gC;
-    bf16x8 th[2], tl[2];
     {
         bf16x8 sh[4], sl[4], ka[4];
         const f32x4 gam = *reinterpret_cast<const f32x4*>(st.G + kGGam + 16 * w + 4 * g);
         gs = *reinterpret_cast<const f32x4*>(st.G + kGScale + 16 * w + 4 * g);
         gC = st.G[kGC];
+        const u32x2 vv = tr_vd(st.V, w, l);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             sh[m] = xop(S.Sx, m, 0, l);
@@ -333,29 +332,23 @@ __device__ __forceinline__ void state_step(const Ctx& x, int w, const Stage& st,
             y0 = mfma_bf16(ka[m], sh[m], y0);
             y1 = mfma_bf16(ka[m], sl[m], y1);
         }
-        put_half(S.Yx, w, l, (y0 + y1) * gam);
-        f32x4 q0 = zero4(), q1 = zero4();
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            if (m >= nb) break;   // T_b is lower triangular
-            th[m] = packed(st.Tb, w, m, 0, l);
-            tl[m] = packed(st.Tb, w, m, 1, l);
-            const bf16x8 vb = tr_v(st.V, m, l);
-            q0 = mfma_bf16(th[m], vb, q0);
-            q1 = mfma_bf16(tl[m], vb, q1);
-        }
-        up = q0 + q1;
+        const f32x4 vf = {__uint_as_float(vv[0] << 16), __uint_as_float(vv[0] & 0xffff0000u),
+                          __uint_as_float(vv[1] << 16), __uint_as_float(vv[1] & 0xffff0000u)};
+        put_half(S.Ex, w, l, vf - (y0 + y1) * gam);
     }
     __syncthreads();   // B
-    // P3: X = T_b (Gamma Y), U = U' - X; K^T operands for P4
+    // P3: U = T_b E (T_b is lower triangular: blocks m <= w / 2); K^T
+    // operands for P4
     bf16x8 kt[2][2];
     {
-        bf16x8 yh[2], yl[2];
+        bf16x8 eh[2], el[2], th[2], tl[2];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             if (m >= nb) break;
-            yh[m] = xop(S.Yx, m, 0, l);
-            yl[m] = xop(S.Yx, m, 1, l);
+            eh[m] = xop(S.Ex, m, 0, l);
+            el[m] = xop(S.Ex, m, 1, l);
+            th[m] = packed(st.Tb, w, m, 0, l);
+            tl[m] = packed(st.Tb, w, m, 1, l);
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j)
@@ -365,9 +358,9 @@ __device__ __forceinline__ void state_step(const Ctx& x, int w, const Stage& st,
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             if (m >= nb) break;
-            mma3(th[m], tl[m], yh[m], yl[m], p0, p1, p2);
+            mma3(th[m], tl[m], eh[m], el[m], p0, p1, p2);
         }
-        const f32x4 u = up - (p0 + p1 + p2);
+        const f32x4 u = p0 + p1 + p2;
         put_half(S.Ux, w, l, u);
         put_half(S.Uy, w, l, u * gs);
     }
@@ -401,33 +394,36 @@ __device__ __forceinline__ void output_step(const Ctx& x, int tt, int ch, const 
     const int nb = (tt >> 1) + 1;
     const int t0 = x.rec[4 * ch + 1], len = x.rec[4 * ch + 2];
     __syncthreads();   // A
-    // P2: Z = Q S^T; A rows for P4
-    f32x4 z;
+    // Z = Q S^T, key blocks 0 and 1 before barrier B and blocks 2 and 3 (and
+    // the A operands) after it, which spreads the output waves' LDS reads
+    // over both windows in which the published S and this stage are valid
+    f32x4 z0 = zero4(), z1 = zero4();
     bf16x8 ah[2], al[2];
-    {
-        bf16x8 sh[4], sl[4], qa[4];
-        const f32x4 gam = *reinterpret_cast<const f32x4*>(st.G + kGGam + 16 * tt + 4 * g);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            sh[m] = xop(S.Sx, m, 0, l);
-            sl[m] = xop(S.Sx, m, 1, l);
-            qa[m] = row_op(st.Q, 16 * tt + c, m, g);
+    for (int half = 0; half < 2; ++half) {
+        if (half == 1) __syncthreads();   // B
+        bf16x8 sh[2], sl[2], qa[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int m = 2 * half + i;
+            sh[i] = xop(S.Sx, m, 0, l);
+            sl[i] = xop(S.Sx, m, 1, l);
+            qa[i] = row_op(st.Q, 16 * tt + c, m, g);
         }
-        f32x4 z0 = zero4(), z1 = zero4();
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            z0 = mfma_bf16(qa[m], sh[m], z0);
-            z1 = mfma_bf16(qa[m], sl[m], z1);
-        }
-        z = (z0 + z1) * gam;
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            if (m >= nb) break;
-            ah[m] = packed(st.Am, tt, m, 0, l);
-            al[m] = packed(st.Am, tt, m, 1, l);
+        for (int i = 0; i < 2; ++i) {
+            z0 = mfma_bf16(qa[i], sh[i], z0);
+            z1 = mfma_bf16(qa[i], sl[i], z1);
         }
     }
-    __syncthreads();   // B
+    const f32x4 gam = *reinterpret_cast<const f32x4*>(st.G + kGGam + 16 * tt + 4 * g);
+    const f32x4 z = (z0 + z1) * gam;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        if (m >= nb) break;
+        ah[m] = packed(st.Am, tt, m, 0, l);
+        al[m] = packed(st.Am, tt, m, 1, l);
+    }
     __syncthreads();   // C
     // P4: O = Gamma Z + A U
     {
