@@ -102,10 +102,8 @@ __device__ __forceinline__ const uint16_t* token_row(const uint16_t* base, const
 // ---- loader waves -------------------------------------------------------------
 // The chunk's operands are 67 DMA blocks of 1 KiB: K 0..15, Q 16..31, T_b
 // 32..47, A 48..63, V 64..65, G 66.  Loader i owns the blocks i, i + 8, ...
-// (9 or 8 of them); loaders 0 and 1 also touch one line set each for L2.
-// Spreading a chunk's blocks over three barrier windows keeps any one window
-// free of a long DMA burst, which would hold back the output waves' stores
-// and the next barrier.
+// (9 or 8 of them, fewer the unread factor blocks); loaders 0 and 1 also
+// touch one line set each for L2.
 
 __device__ __forceinline__ void issue_block(const Ctx& x, int t0, int len,
                                             const unsigned char* F, int blk, Stage& st) {
@@ -166,19 +164,33 @@ constexpr bool unread_block(int blk) {
     return blk >= 32 && blk < 64 && ((slot >> 1) & 1) == 1 && (slot >> 2) < 2;
 }
 
-// Part kPart (0..2) of loader kI's blocks of `chunk`.  The skipped blocks all
-// fall in parts 1 and 2, so the count of part 0 that the waits rely on is
-// the same for every loader.
-template <int kI, int kPart>
-__device__ __forceinline__ void issue_part(const Ctx& x, int chunk, Stage& st) {
+// Number of blocks loader kI issues per chunk.
+template <int kI>
+constexpr int loader_blocks() {
+    int n = 0;
+    for (int blk = kI; blk < 67; blk += 8) n += unread_block(blk) ? 0 : 1;
+    return n;
+}
+
+// Loader kI's blocks of `chunk`, in three groups of ascending block number
+// (the compiler keeps the order inside each group; left free to interleave
+// all of them, it produced an order measured slower).
+template <int kI, int kGroup>
+__device__ __forceinline__ void issue_group(const Ctx& x, int chunk, Stage& st) {
     const int t0 = x.rec[4 * chunk + 1], len = x.rec[4 * chunk + 2];
     const unsigned char* F = chunk_factors(x, chunk);
 #pragma unroll
-    for (int q = 3 * kPart; q < 3 * kPart + 3; ++q) {
+    for (int q = 3 * kGroup; q < 3 * kGroup + 3; ++q) {
         const int blk = kI + 8 * q;
-        static_assert(kPart > 0 || kI + 8 * 2 < 32, "part 0 holds no factor block");
         if (blk < 67 && !unread_block(blk)) issue_block(x, t0, len, F, blk, st);
     }
+}
+
+template <int kI>
+__device__ __forceinline__ void issue_chunk(const Ctx& x, int chunk, Stage& st) {
+    issue_group<kI, 0>(x, chunk, st);
+    issue_group<kI, 1>(x, chunk, st);
+    issue_group<kI, 2>(x, chunk, st);
 }
 
 template <int kN>
@@ -188,37 +200,30 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((kN & 15) | ((kN >> 4) << 14) | 0x0F70);
 }
 
-// A chunk's blocks go out in three parts: part 0 right after the third
-// barrier of the chunk two before it (its stage is free from then on),
-// parts 1 and 2 after the first two barriers of the chunk before it.
-// Loaders 0 and 1 end part 0 with one L2 touch.  Before a chunk's first
-// barrier each loader waits until only the part 0 of the chunk after it
-// (and that touch) may still be in flight: loads complete in issue order.
+// A chunk's blocks go out at once, right after the third barrier of the
+// chunk two before it (its stage is free from then on), followed by one L2
+// touch from loaders 0 and 1.  Before a chunk's first barrier each loader
+// waits until only the blocks of the chunk after it (and that touch) may
+// still be in flight: loads complete in issue order.  (Spreading the blocks
+// over the three barrier windows instead was measured slightly slower.)
 template <int kI>
 __device__ void loader(const Ctx& x, int c0, int c_end, Lds& S) {
-    constexpr int kPending = 3 + (kI < 2 ? 1 : 0);
+    constexpr int kPending = loader_blocks<kI>() + (kI < 2 ? 1 : 0);
     const int last = c_end - 1;
     auto cl = [last](int c) { return c < last ? c : last; };
     if constexpr (kI < 2) {
 #pragma unroll
         for (int d = 1; d < kPfAhead; ++d) touch_chunk<kI>(x, cl(c0 + d), S.sink);
     }
-    issue_part<kI, 0>(x, c0, S.st[0]);
-    issue_part<kI, 1>(x, c0, S.st[0]);
-    issue_part<kI, 2>(x, c0, S.st[0]);
-    issue_part<kI, 0>(x, cl(c0 + 1), S.st[1]);
+    issue_chunk<kI>(x, c0, S.st[0]);
+    issue_chunk<kI>(x, cl(c0 + 1), S.st[1]);
     if constexpr (kI < 2) touch_chunk<kI>(x, cl(c0 + kPfAhead), S.sink);
     for (int c = c0; c < c_end; ++c) {
-        Stage& nxt = S.st[(c + 1 - c0) & 1];
-        Stage& cur = S.st[(c - c0) & 1];
-        const int cn = cl(c + 1);
         wait_vm<kPending>();
         __builtin_amdgcn_s_barrier();   // A
-        issue_part<kI, 1>(x, cn, nxt);
         __builtin_amdgcn_s_barrier();   // B
-        issue_part<kI, 2>(x, cn, nxt);
         __builtin_amdgcn_s_barrier();   // C: chunk c's stage is free
-        issue_part<kI, 0>(x, cl(c + 2), cur);
+        issue_chunk<kI>(x, cl(c + 2), S.st[(c - c0) & 1]);
         if constexpr (kI < 2) touch_chunk<kI>(x, cl(c + 2 + kPfAhead), S.sink);
     }
     wait_vm<0>();   // nothing may land in LDS after the workgroup ends
