@@ -211,7 +211,8 @@ rda_status rda_decode_step(const void* q, const void* k, const void* v, rda_dtyp
     if (batch < 0) return RDA_ERR_SHAPE;
     rda_status st = check_dims(num_heads, dk, dv);
     if (st != RDA_OK) return st;
-    if (int64_t(batch) * num_heads > INT32_MAX) return RDA_ERR_SHAPE;
+    // two workgroups per (batch, head): the grid must stay within int32
+    if (int64_t(batch) * num_heads > INT32_MAX / 2) return RDA_ERR_SHAPE;
     if (batch == 0) return RDA_OK;
     if (!q || !k || !v || !a || !b || !S || !o) return RDA_ERR_NULL;
     for (const void* p : {q, k, v, static_cast<const void*>(a), static_cast<const void*>(b),

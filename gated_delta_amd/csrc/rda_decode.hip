@@ -14,11 +14,14 @@
 //     o_i    = S'_i . q = a (Sq)_i + b e_i kappa
 //
 // Decode is bound by HBM: 128 KiB of state traffic per (batch, head) against
-// ~0.9 flop per byte.  Mapping: one 256-thread workgroup per (batch, head);
-// 16 lanes own one row (each lane 8 columns: 4 in each 64-column half, so
-// every load instruction of a wavefront reads four 256-byte runs), a lane
-// holds 8 rows, i.e. all 64 KiB of the state is in flight at once per
-// workgroup.  Row dot products are 16-lane DPP reductions.
+// ~0.9 flop per byte.  Mapping: two 256-thread workgroups per (batch, head),
+// each owning 64 rows of the state; 16 lanes own one row (each lane 8
+// columns: 4 in each 64-column half, so every load instruction of a
+// wavefront reads four 256-byte runs), a lane holds 4 rows, i.e. the
+// workgroup's 32 KiB of state is in flight at once.  (One workgroup per
+// (batch, head) holding all 64 KiB was measured 11 % slower: fewer, larger
+// workgroups leave a ragged last round; quarters were in between.)  Row dot
+// products are 16-lane DPP reductions.
 #include "rda_device.h"
 #include "rda_internal.h"
 
@@ -32,18 +35,19 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const TIn* __restrict_
                                                           const float* __restrict__ b,
                                                           float* __restrict__ S,
                                                           float* __restrict__ o) {
-    const int64_t bh = blockIdx.x;
+    const int64_t bh = blockIdx.x >> 1;
+    const int half = blockIdx.x & 1;
     const int t = threadIdx.x;
-    const int w = wave_id();      // wavefront 0..3 -> rows 32w .. 32w+31
+    const int w = wave_id();      // wavefront 0..3 -> rows 64 half + 16w .. +15
     const int g = (t >> 4) & 3;   // 16-lane group within the wavefront
     const int c = t & 15;         // lane within the group -> columns 4c.., 64+4c..
     float* __restrict__ Sb = S + bh * (kD * kD);
 
     // all state loads first: 8 rows x 2 float4 per lane
-    f32x4 s[8][2];
+    f32x4 s[4][2];
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        const int row = 32 * w + 4 * p + g;
+    for (int p = 0; p < 4; ++p) {
+        const int row = 64 * half + 16 * w + 4 * p + g;
         s[p][0] = *reinterpret_cast<const f32x4*>(Sb + row * kD + 4 * c);
         s[p][1] = *reinterpret_cast<const f32x4*>(Sb + row * kD + 64 + 4 * c);
     }
@@ -54,9 +58,9 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const TIn* __restrict_
     load4<TIn>(q + bh * kD + 64 + 4 * c, qx + 4);
     const float av = a[bh];
     const float bv = b[bh];
-    float vr[8];
+    float vr[4];
 #pragma unroll
-    for (int p = 0; p < 8; ++p) vr[p] = load1<TIn>(v + bh * kD + 32 * w + 4 * p + g);
+    for (int p = 0; p < 4; ++p) vr[p] = load1<TIn>(v + bh * kD + 64 * half + 16 * w + 4 * p + g);
 
     float kap = 0.f;
 #pragma unroll
@@ -65,7 +69,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const TIn* __restrict_
 
     float o_mine = 0.f;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
+    for (int p = 0; p < 4; ++p) {
         float sk = 0.f, sq = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -84,17 +88,17 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const TIn* __restrict_
             n0[j] = av * s[p][0][j] + be * kx[j];
             n1[j] = av * s[p][1][j] + be * kx[4 + j];
         }
-        const int row = 32 * w + 4 * p + g;
+        const int row = 64 * half + 16 * w + 4 * p + g;
         *reinterpret_cast<f32x4*>(Sb + row * kD + 4 * c) = n0;
         *reinterpret_cast<f32x4*>(Sb + row * kD + 64 + 4 * c) = n1;
     }
-    if (c < 8) o[bh * kD + 32 * w + 4 * c + g] = o_mine;
+    if (c < 4) o[bh * kD + 64 * half + 16 * w + 4 * c + g] = o_mine;
 }
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, rda_dtype dt,
                          const float* a, const float* b, int32_t batch, int32_t heads,
                          float* S, float* o, hipStream_t stream) {
-    const unsigned grid = unsigned(int64_t(batch) * heads);
+    const unsigned grid = unsigned(2 * int64_t(batch) * heads);
     if (grid == 0) return hipSuccess;
     if (dt == RDA_BF16) {
         hipLaunchKernelGGL(decode_step_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream,

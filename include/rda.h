@@ -141,7 +141,8 @@ rda_status rda_prefill_profiled(const void* q, const void* k, const void* v, rda
  *   q, k [batch, H, dk], v [batch, H, dv] (qkv_dtype); a, b [batch, H] fp32
  *   S    [batch, H, dv, dk] fp32, read and overwritten with the new state
  *   o    [batch, H, dv] fp32 output (o = S_new q)
- * batch = 0 is allowed (nothing is launched).
+ * batch = 0 is allowed (nothing is launched); batch x H above 2^30 - 1 is
+ * rejected with RDA_ERR_SHAPE.
  */
 rda_status rda_decode_step(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
                            const float* a, const float* b,

@@ -115,6 +115,7 @@ def test_decode_rejects_bad_arguments(lib):
     assert dec(S=None) == NULL
     assert dec(dt=3) == DTYPE
     assert dec(B=-1) == SHAPE
+    assert dec(B=1 << 26, H=16) == SHAPE       # 2 workgroups per (b, h) must fit the grid
     assert dec(dk=96) == UNSUP
     assert dec(o=P + 4) == ALIGN
     assert dec(o=P + 5 * GiB + 512) == ALIAS      # o inside S
