@@ -54,6 +54,20 @@ __device__ __forceinline__ bf16x8 row_op(const uint16_t* T, int r, int m, int g)
                               *reinterpret_cast<const u32x4*>(row + 16 * ((4 * m + g) ^ swz(r))));
 }
 
+// Step m of the column-oriented substitution in a 16 x 16 diagonal block:
+// x_r -= L_rm x_m on every lane, with x_m taken from lane m of the same
+// 16-lane row (DPP row_newbcast:m), then steps m + 1 .. 14.
+template <int kM>
+__device__ __forceinline__ void substitute_step(float (&x)[4], const float (&Lrow)[16]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float xm = __int_as_float(
+            __builtin_amdgcn_update_dpp(0, __float_as_int(x[j]), 0x150 + kM, 0xF, 0xF, false));
+        x[j] -= Lrow[kM] * xm;
+    }
+    if constexpr (kM < 14) substitute_step<kM + 1>(x, Lrow);
+}
+
 __global__ __launch_bounds__(256) void prep_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ a,
     const float* __restrict__ b, int H, const int32_t* __restrict__ rec,
@@ -204,21 +218,26 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(
     __syncthreads();
 
     // ---- T = (I + L)^-1 -------------------------------------------------------
-    // (a) diagonal block w: lane c (of the first 16) solves column c,
-    //     x_r = [r == c] - sum_{m < r} L_rm x_m, with the row of L broadcast.
-    if (l < 16) {
-        const int base = 16 * w;
-        float x[16];
+    // (a) diagonal block w, all 64 lanes: lane (g, r = c) holds row r of
+    //     columns 4g .. 4g+3, starting from the identity.  Column-oriented
+    //     forward substitution: once x_m is final, every row r > m takes
+    //     x_r -= L_rm x_m, with x_m broadcast inside each 16-lane row by DPP
+    //     (row_newbcast).  L is zero on and above the diagonal, so rows
+    //     r <= m are left unchanged without a branch.
+    {
+        const int base = 16 * w, r = c;
+        float Lrow[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = r == c ? 1.f : 0.f;
-            const float* Lr = Ls + (base + r) * kFS + base;
+        for (int m4 = 0; m4 < 4; ++m4) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(Ls + (base + r) * kFS + base + 4 * m4);
 #pragma unroll
-            for (int m = 0; m < r; ++m) acc -= Lr[m] * x[m];
-            x[r] = acc;
+            for (int e = 0; e < 4; ++e) Lrow[4 * m4 + e] = v[e];
         }
+        float x[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) Ts[(base + r) * kFS + base + c] = x[r];
+        for (int j = 0; j < 4; ++j) x[j] = r == 4 * g + j ? 1.f : 0.f;
+        substitute_step<0>(x, Lrow);
+        *reinterpret_cast<f32x4*>(Ts + (base + r) * kFS + base + 4 * g) = f32x4{x[0], x[1], x[2], x[3]};
     }
     __syncthreads();
     // (b) off-diagonal blocks, block row by block row, on fp32 MFMA:
