@@ -180,6 +180,37 @@ def test_random_unnormalised_inputs(dev):
     check_against_oracle("unnormalised fp32", p, dev)
 
 
+def test_random_unnormalised_inputs_bf16(dev):
+    """The same key and query scaling on the bf16 path (its own prep and
+    walk kernels), rounded to bf16 before both sides see them."""
+    rng = np.random.default_rng(110)
+    q, k, v, a, b, S0 = pins.random_case(rng, 300, 3, 128, 128, unit_keys=True)
+    k *= rng.uniform(0.5, 1.3, (300, 3, 1)).astype(np.float32)
+    q *= rng.uniform(0.2, 3.0, (300, 3, 1)).astype(np.float32)
+    q, k, v = (synth.round_bf16(x.astype(np.float32)) for x in (q, k, v))
+    p = synth.PrefillInputs(q, k, v, a, b, None, S0.astype(np.float32), True)
+    check_against_oracle("unnormalised bf16", p, dev)
+
+
+def test_correlated_keys_bf16(dev):
+    """Keys clustered around one direction per head make the Gram entries
+    b_i k_i.k_j close to b_i, the hardest case for the triangular solve:
+    T = (I + L)^-1 then has large alternating entries."""
+    rng = np.random.default_rng(111)
+    T, H = 260, 2
+    u = rng.standard_normal((1, H, 128))
+    k = u + 0.1 * rng.standard_normal((T, H, 128))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    q = rng.standard_normal((T, H, 128))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, H, 128))
+    q, k, v = (synth.round_bf16(x.astype(np.float32)) for x in (q, k, v))
+    a = rng.uniform(0.9, 1.0, (T, H)).astype(np.float32)
+    b = rng.uniform(0.0, 1.0, (T, H)).astype(np.float32)
+    p = synth.PrefillInputs(q, k, v, a, b, None, None, True)
+    check_against_oracle("correlated keys bf16", p, dev)
+
+
 @pytest.mark.parametrize("T,H", [(513, 16), (7000, 16)])
 def test_profiled_entry_point_matches(dev, T, H):
     """rda_prefill_profiled (stage events) and rda_prefill agree bit for bit."""
