@@ -15,17 +15,20 @@
 //   S_out = gamma_C S + U^T diag(gamma_C / gamma) K
 //
 // This is the WY / UT-transform form of the gated delta rule (W = T_b Gamma K
-// and U' = T_b V are never formed: the walk multiplies through T_b instead),
-// and it reproduces the token-by-token recurrence exactly in real arithmetic.
+// is never formed: the walk multiplies through T_b instead; the bf16 walk
+// applies T_b once, to E = V - Gamma (K S^T), while the fp32 walk below forms
+// T_b V and T_b Gamma Y separately), and it reproduces the token-by-token
+// recurrence exactly in real arithmetic.
 //
 // PREP (parallel over chunk x head): gates, Gram tiles K K^T and Q K^T on
 // MFMA, the unit-lower-triangular solve for T in fp32, then T_b and A packed
-// as bf16 hi/lo MFMA operands (33 KiB per chunk-head in the workspace).
+// as bf16 hi/lo MFMA operands (33 KiB per chunk-head in the workspace; the
+// bf16 kernels skip the slots that are zero, 25 KiB in use).
 // WALK (sequential over the chunks of a sequence): one workgroup per
 // (sequence, head, 16-channel value slice); the fp32 state slice lives in
 // MFMA accumulators, and each chunk costs three dependent MFMA stages
-// (Y = K S^T, X = T_b Gamma Y, S update) over the raw bf16 q, k, v tiles and
-// the two packed 64 x 64 factors.  Rows of S evolve independently, so the 8
+// (Y = K S^T, the T_b product, the S update) over the raw bf16 q, k, v tiles
+// and the two packed 64 x 64 factors.  Rows of S evolve independently, so the 8
 // slices of a head need no communication.
 //
 // Precision: q, k, v enter MFMA as exact bf16 (fp32 inputs as bf16 hi + lo).

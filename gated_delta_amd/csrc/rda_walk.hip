@@ -14,13 +14,18 @@
 //     P3  U = T_b E; publish U and U~ = diag(gamma_C/gamma) U
 //     P4  S^T = gamma_C S^T + K^T U~
 //   output waves 4..7  produce the outputs of token tile tt = w - 4:
-//     P2  Z = Q S^T;  P4  O = Gamma Z + A U, stored
+//     P2, P3  Z = Q S^T (key blocks 0-1 before the second barrier, 2-3 after
+//             it, which spreads their LDS reads over two windows)
+//     P4      O = Gamma Z + A U, stored
 //   loader waves 8..15 stream each chunk's operands -- the K and Q tiles, the
 //                      packed T_b and A factors, the gates and this slice's V
 //                      columns -- into a two-stage LDS ring with LDS-DMA
 //                      (global_load_lds_dwordx4), and touch the lines of
 //                      chunks further ahead so that they sit in L2 when the
 //                      DMA asks for them.
+// A chunk's DMA goes out in one burst as soon as its stage is free (after
+// the third barrier of the chunk two before it); the factor slots that are
+// zero are not streamed.
 // The compute waves issue no global loads at all (a wave stalls when it
 // issues a memory instruction into a full queue, and any such stall would
 // land on the recurrence), and the output work runs beside the recurrence on
