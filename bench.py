@@ -24,8 +24,6 @@ Usage: python bench.py [--gpus 1] [--steps 128] [--warmup 5] [--no-cpu]
 from __future__ import annotations
 
 import argparse
-import glob
-import hashlib
 import json
 import os
 import sys
@@ -61,13 +59,7 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    # the device code only: the kernels and the headers they include
-    for f in sorted(glob.glob(os.path.join(ROOT, "gated_delta_amd", "csrc", "*"))):
-        if os.path.basename(f) != "rda_api.hip":
-            h.update(open(f, "rb").read())
-    return h.hexdigest()[:16]
+from gated_delta_amd.srchash import kernel_source_hash  # noqa: E402
 
 
 def read_traffic(kernel: str):

@@ -14,7 +14,6 @@ Writes
 """
 import csv
 import glob
-import hashlib
 import os
 import statistics
 import sys
@@ -22,13 +21,8 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def source_hash() -> str:
-    h = hashlib.sha256()
-    # the device code only: the kernels and the headers they include
-    for f in sorted(glob.glob(os.path.join(ROOT, "gated_delta_amd", "csrc", "*"))):
-        if os.path.basename(f) != "rda_api.hip":
-            h.update(open(f, "rb").read())
-    return h.hexdigest()[:16]
+sys.path.insert(0, ROOT)
+from gated_delta_amd.srchash import kernel_source_hash as source_hash  # noqa: E402
 
 
 # HIP kernel -> the stage name bench.py reports it under
