@@ -18,6 +18,13 @@ Prints ONE JSON line:
              the prep kernel writes the chunk table, so no table kernel runs
   cpu_baseline  the fp64 oracle on the same prefill inputs, host cores
   parity     rel-L2 / max-abs of this run's prefill output vs the oracle
+  also       the prefill back to back without the flush (ms_per_call_unflushed),
+             the practical HBM rate of an in-place read-modify-write of 256 MiB
+             (hbm_practical, and decode.frac_of_practical), and the three other
+             prefill workloads -- one fp32 head of 64 tokens, T = 2048 x 16
+             heads, 8 packed sequences of 32768 tokens x 16 heads -- each with
+             time, algorithmic MFMA / HBM fractions and parity against the oracle
+             (other_prefill_workloads)
 
 Usage: python bench.py [--gpus 1] [--steps 128] [--warmup 5] [--no-cpu]
 """
@@ -249,6 +256,10 @@ def main():
     out["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS,
                        "unit": "GB/s", "frac": ach / PEAK_HBM_GBPS, "traffic": tr}
 
+    if args.mode == "bench":
+        extra_measurements(args, out, torch, np, rda, synth, dev, stream, q, k, v, a, b, S0,
+                           o, Sf, ws, T, H)
+
     if do_prefill:
         o_h = o.cpu().numpy().astype(np.float64)
         S_h = Sf.cpu().numpy().astype(np.float64)
@@ -268,6 +279,88 @@ def main():
                          "o_max_abs": float(np.max(np.abs(o_h - ro))),
                          "S_rel_l2": float(np.linalg.norm(S_h - rS) / np.linalg.norm(rS))}
     print(json.dumps(out), flush=True)
+
+
+def extra_measurements(args, out, torch, np, rda, synth, dev, stream, q, k, v, a, b, S0, o, Sf,
+                       ws, T, H):
+    """The other figures the measurement plan asks for beside the headline:
+    the prefill without the cache flush between calls, the practical HBM
+    rate of an in-place read-modify-write of the decode's size, and the three
+    other prefill workloads (time, algorithmic fractions, parity)."""
+    def timed(fn, reps, flush=None):
+        ts = []
+        for _ in range(reps):
+            if flush is not None:
+                flush()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.median([e0.elapsed_time(e1) for e0, e1 in ts])) * 1e-3   # s
+
+    # prefill back to back, inputs left in the Infinity Cache by the call before
+    warm = timed(lambda: rda.rda_prefill(q, k, v, a, b, S0=S0, o=o, S_final=Sf, workspace=ws), 10)
+    out["prefill"]["ms_per_call_unflushed"] = warm * 1e3
+    out["prefill"]["tokens_per_s_unflushed"] = T / warm
+
+    # practical HBM ceiling: in-place scaling of 256 MiB of fp32 (read + write)
+    scratch = torch.ones((64 << 20,), dtype=torch.float32, device=dev)
+    hs = timed(lambda: scratch.mul_(1.0), 10)
+    hbm_gbps = 2 * scratch.numel() * 4 / hs / 1e9
+    out["hbm_practical"] = {"GBps": hbm_gbps, "frac_of_peak": hbm_gbps / PEAK_HBM_GBPS,
+                            "how": "in-place scaling of a 256 MiB fp32 buffer (read + write)"}
+    if "decode" in out:
+        out["decode"]["frac_of_practical"] = out["decode"]["value"] / hbm_gbps
+
+    flush = lambda: scratch.mul_(1.0)   # 512 MiB of traffic evicts the Infinity Cache
+    configs = {}
+    for cid, name in ((1, "single_head_fp32_T64"), (2, "nano_layer_T2048_H16"),
+                      (4, "varlen_8_seqs_T32768_H16")):
+        pc = synth.CONFIGS[cid]()
+        Tc, Hc = pc.total_tokens, pc.num_heads
+        tok = (lambda x: torch.from_numpy(x).to(torch.bfloat16).to(dev)) if pc.bf16 else \
+            (lambda x: torch.from_numpy(x).to(dev))
+        qc, kc, vc = tok(pc.q), tok(pc.k), tok(pc.v)
+        ac, bc = torch.from_numpy(pc.a).to(dev), torch.from_numpy(pc.b).to(dev)
+        S0c = torch.from_numpy(pc.S0).to(dev) if pc.S0 is not None else None
+        cuc = pc.cu_seqlens
+        oc, Sfc = rda.rda_prefill(qc, kc, vc, ac, bc, cu_seqlens=cuc, S0=S0c)
+        wsc = torch.empty(rda.rda_prefill_workspace_bytes(pc.num_seqs, Tc, Hc), dtype=torch.uint8,
+                          device=dev)
+        cu_dev = torch.from_numpy(cuc.astype(np.int32)).to(dev) if cuc is not None else None
+        # the C entry point itself: the binding's check of cu_seqlens reads it
+        # back to the host, which would put a device sync inside the timing
+        cargs = [rda._ptr(qc), rda._ptr(kc), rda._ptr(vc), 0 if pc.bf16 else 1, rda._ptr(ac),
+                 rda._ptr(bc), rda._ptr(cu_dev), pc.num_seqs, Tc, Hc, D, D, rda._ptr(S0c),
+                 rda._ptr(oc), rda._ptr(Sfc), rda._ptr(wsc), wsc.numel(), stream.cuda_stream]
+
+        def call():
+            if rda.lib().rda_prefill(*cargs) != 0:
+                raise RuntimeError("rda_prefill failed")
+        sec = timed(call, 10, flush)
+        units = Tc * Hc
+        entry = {"T": Tc, "H": Hc, "N": pc.num_seqs, "qkv": "bf16" if pc.bf16 else "fp32",
+                 "ms_per_call": sec * 1e3, "tokens_per_s": Tc / sec,
+                 "mfma_frac_algorithmic": PREFILL_FLOPS * units / sec / 1e12 / PEAK_BF16_TFLOPS,
+                 "hbm_frac_algorithmic": (PREFILL_BYTES * units +
+                                          (2 if S0c is not None else 1) * pc.num_seqs * Hc *
+                                          STATE_BYTES) / sec / 1e9 / PEAK_HBM_GBPS}
+        if not args.no_cpu:
+            import oracle
+            ro, rS = oracle.prefill(pc.q, pc.k, pc.v, pc.a, pc.b, cu_seqlens=cuc, S0=pc.S0,
+                                    threads=args.cpu_threads)
+            oh = oc.cpu().numpy().astype(np.float64)
+            Sh = Sfc.cpu().numpy().astype(np.float64)
+            entry["parity"] = {"o_rel_l2": float(np.linalg.norm(oh - ro) / np.linalg.norm(ro)),
+                               "o_max_abs": float(np.max(np.abs(oh - ro))),
+                               "S_rel_l2": float(np.linalg.norm(Sh - rS) / np.linalg.norm(rS))}
+        configs[name] = entry
+        if cid == 4:
+            entry["lengths"] = [int(x) for x in np.diff(cuc)]
+    out["other_prefill_workloads"] = configs
+    del scratch
 
 
 if __name__ == "__main__":
