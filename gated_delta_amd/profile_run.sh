@@ -1,8 +1,9 @@
 #!/bin/bash
-# Collects the rocprofv3 kernel summary and the HBM counter passes behind
+# Collects the rocprofv3 kernel summary and the counter passes behind
 # profiles/: kernel trace + stats of the default bench command, then one
 # FETCH_SIZE and one WRITE_SIZE pass over the prefill alone and over a plain
-# device copy of known size (the counter calibration).
+# device copy of known size (the counter calibration), then one pass of the
+# MFMA counters over the prefill.
 #   usage: gated_delta_amd/profile_run.sh OUTDIR
 # Raw rocprofv3 output lands in OUTDIR/prof_*; then
 #   python gated_delta_amd/profile_summary.py OUTDIR
@@ -22,4 +23,9 @@ for ctr in FETCH_SIZE WRITE_SIZE; do
         > "$OUT/prof_${ctr}_$mode.log" 2>&1 || exit $?
   done
 done
+MFMA="SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_INSTS_VALU_MFMA_BF16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES"
+echo "== pmc MFMA counters: python bench.py --mode prefill --steps 2 --warmup 1 --no-cpu"
+timeout -s KILL 120 rocprofv3 --pmc $MFMA --output-format csv -d "$OUT/prof_MFMA_prefill" -o pmc \
+    -- python -u "$R/bench.py" --mode prefill --steps 2 --warmup 1 --no-cpu \
+    > "$OUT/prof_MFMA_prefill.log" 2>&1 || exit $?
 echo "== done"

@@ -112,6 +112,49 @@ def main():
     open(path, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
+    # ---- MFMA counters -------------------------------------------------------------
+    mdir = os.path.join(out, "prof_MFMA_prefill")
+    if not os.path.isdir(mdir):
+        return
+    avg_us = {short(r["Name"]): float(r["AverageNs"]) / 1e3 for r in rows}
+    mops16 = counter(mdir, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    mops32 = counter(mdir, "SQ_INSTS_VALU_MFMA_MOPS_F32")
+    inst16 = counter(mdir, "SQ_INSTS_VALU_MFMA_BF16")
+    busy = counter(mdir, "SQ_VALU_MFMA_BUSY_CYCLES")
+    cu = counter(mdir, "SQ_BUSY_CU_CYCLES")
+    lines = ["# MFMA work executed per launch of the prefill kernels, RDA prefill T=16384",
+             "# H=16 d=128 (bf16 q/k/v), from one rocprofv3 --pmc pass:",
+             "#   rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 \\",
+             "#     SQ_INSTS_VALU_MFMA_BF16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES \\",
+             "#     --output-format csv -d OUTDIR/prof_MFMA_prefill -o pmc \\",
+             "#     -- python bench.py --mode prefill --steps 2 --warmup 1 --no-cpu",
+             "# (part of gated_delta_amd/profile_run.sh OUTDIR; then",
+             "# python gated_delta_amd/profile_summary.py OUTDIR).  MOPS count 512 flops each;",
+             "# the executed work includes the hi/lo split products.  The rate divides by",
+             "# the kernel's average duration in the kernel trace summary; the fraction is",
+             "# of the 2.5 PFLOP/s dense bf16 peak.  mfma_busy_per_simd = MFMA busy cycles",
+             "# (summed over a CU's four SIMDs) / (4 x CU busy cycles).",
+             f"source_hash = {source_hash()}"]
+    for k in sorted(mops16):
+        name = STAGE.get(k, k)
+        f16 = mops16[k] * 512.0
+        f32 = mops32.get(k, 0.0) * 512.0
+        lines.append(f"{name}.kernel = {k}")
+        lines.append(f"{name}.mfma_bf16_instructions = {inst16.get(k, 0.0):.0f}")
+        lines.append(f"{name}.mfma_bf16_flops = {f16:.0f}")
+        lines.append(f"{name}.mfma_f32_flops = {f32:.0f}")
+        if k in avg_us and avg_us[k] > 0:
+            rate = (f16 + f32) / (avg_us[k] * 1e-6) / 1e12
+            lines.append(f"{name}.mfma_tflops = {rate:.2f}")
+            lines.append(f"{name}.mfma_frac_of_bf16_peak = {rate / 2500.0:.4f}")
+        if cu.get(k):
+            # the busy count sums a CU's four SIMDs (16 cycles per 16x16x32
+            # instruction), the CU count one per CU: per-SIMD utilisation
+            lines.append(f"{name}.mfma_busy_per_simd = {busy.get(k, 0.0) / (4 * cu[k]):.4f}")
+    path = os.path.join(prof, "mfma_rda_prefill_T16384_H16.txt")
+    open(path, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
 
 if __name__ == "__main__":
     main()
