@@ -69,10 +69,10 @@ def parse():
 from gated_delta_amd.srchash import kernel_source_hash  # noqa: E402
 
 
-def read_traffic(kernel: str):
-    """HBM bytes per launch from the committed counter summary, or None when
+def read_profile(fname: str, key: str):
+    """A value from a committed counter summary under profiles/, or None when
     the summary is missing or the kernels changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    path = os.path.join(ROOT, "profiles", fname)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -83,8 +83,13 @@ def read_traffic(kernel: str):
             kv[k.strip()] = v.strip()
     if kv.get("source_hash") != kernel_source_hash():
         return None
-    val = kv.get(f"{kernel}.bytes_per_launch")
+    val = kv.get(key)
     return float(val) if val else None
+
+
+def read_traffic(kernel: str):
+    """HBM bytes per launch of one kernel (FETCH_SIZE + WRITE_SIZE, calibrated)."""
+    return read_profile("hbm_traffic.txt", f"{kernel}.bytes_per_launch")
 
 
 def main():
@@ -227,6 +232,14 @@ def main():
                           / PEAK_BF16_TFLOPS,
                           "hbm_frac_algorithmic": (PREFILL_BYTES * units + 2 * H * STATE_BYTES)
                           / call_s / 1e9 / PEAK_HBM_GBPS}
+        # MFMA work rocprofv3 counted per launch (hi/lo split products
+        # included), over this run's call time
+        mf = [read_profile("mfma_rda_prefill_T16384_H16.txt", f"{n}.mfma_{t}_flops")
+              for n in ("rda_prep", "rda_walk") for t in ("bf16", "f32")]
+        if all(x is not None for x in mf):
+            out["prefill"]["mfma_frac_executed_rocprof"] = sum(mf) / call_s / 1e12 / PEAK_BF16_TFLOPS
+        else:
+            out["prefill"]["mfma_frac_executed_rocprof"] = None
         names = {0: "rda_chunk_table", 1: "rda_prep", 2: "rda_walk"}
         kb = {0: 0.0, 1: PREFILL_IN_BYTES * units,
               2: PREFILL_OUT_BYTES * units + 2 * H * STATE_BYTES}
