@@ -18,13 +18,20 @@ Prints ONE JSON line:
              the prep kernel writes the chunk table, so no table kernel runs
   cpu_baseline  the fp64 oracle on the same prefill inputs, host cores
   parity     rel-L2 / max-abs of this run's prefill output vs the oracle
-  also       the prefill back to back without the flush (ms_per_call_unflushed),
+The oracle runs only in this CPU leg (skipped with --no-cpu): the baseline
+timing, and the parity figures of this run's outputs (parity, and the parity
+entries of other_prefill_workloads and decode_tokens below).
+  also       the prefill back to back without the flush (ms_per_call_unflushed)
+             and after a read-only 512 MiB flush (ms_per_call_read_flushed),
              the practical HBM rate of an in-place read-modify-write of 256 MiB
              (hbm_practical, and decode.frac_of_practical), and the three other
              prefill workloads -- one fp32 head of 64 tokens, T = 2048 x 16
              heads, 8 packed sequences of 32768 tokens x 16 heads -- each with
              time, algorithmic MFMA / HBM fractions and parity against the oracle
-             (other_prefill_workloads)
+             (other_prefill_workloads); rda_decode_tokens on the decode batch
+             with one token plus two drafts per sequence: one-pass verify +
+             commit, read-only verify and commit-only, each with its state
+             bandwidth (decode_tokens)
 
 Usage: python bench.py [--gpus 1] [--steps 128] [--warmup 5] [--no-cpu]
 """
@@ -60,9 +67,15 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0 = all)")
-    ap.add_argument("--mode", choices=["bench", "prefill", "decode", "copy"], default="bench",
-                    help="prefill/decode: run only that part (for profiling); copy: a plain "
-                         "device copy of known size (counter calibration)")
+    ap.add_argument("--mode", choices=["bench", "prefill", "decode", "decode_tokens", "copy"],
+                    default="bench",
+                    help="prefill/decode: run only that part (for profiling); decode_tokens: "
+                         "only the one-pass multi-token decode, --steps calls after a cache "
+                         "flush each; copy: a plain device copy of known size (counter "
+                         "calibration)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the timed steps and the per-stage calls (the kernel trace "
+                         "of exactly what the kernels entry reports)")
     return ap.parse_args()
 
 
@@ -122,6 +135,15 @@ def main():
 
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    if args.mode == "decode_tokens":
+        timed = make_timer(torch, np, stream)
+        flush_buf = torch.ones((128 << 20,), dtype=torch.float32, device=dev)
+        res = decode_tokens_measurements(args, {}, torch, np, rda, synth, dev, stream, timed,
+                                         lambda: flush_buf.sum(), reps=args.steps,
+                                         modes=("verify_commit_in_place",))
+        print(json.dumps({"mode": "decode_tokens", **res}), flush=True)
+        return
 
     # ---- inputs (host draw, then resident on the device) --------------------
     t = time.time()
@@ -269,7 +291,7 @@ def main():
     out["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS,
                        "unit": "GB/s", "frac": ach / PEAK_HBM_GBPS, "traffic": tr}
 
-    if args.mode == "bench":
+    if args.mode == "bench" and not args.no_extras:
         extra_measurements(args, out, torch, np, rda, synth, dev, stream, q, k, v, a, b, S0,
                            o, Sf, ws, T, H)
 
@@ -294,12 +316,9 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def extra_measurements(args, out, torch, np, rda, synth, dev, stream, q, k, v, a, b, S0, o, Sf,
-                       ws, T, H):
-    """The other figures the measurement plan asks for beside the headline:
-    the prefill without the cache flush between calls, the practical HBM
-    rate of an in-place read-modify-write of the decode's size, and the three
-    other prefill workloads (time, algorithmic fractions, parity)."""
+def make_timer(torch, np, stream):
+    """timed(fn, reps, flush=None): median seconds of `fn` between HIP events
+    on `stream`, each call preceded by `flush()` when given."""
     def timed(fn, reps, flush=None):
         ts = []
         for _ in range(reps):
@@ -312,6 +331,16 @@ def extra_measurements(args, out, torch, np, rda, synth, dev, stream, q, k, v, a
             ts.append((e0, e1))
         torch.cuda.synchronize()
         return float(np.median([e0.elapsed_time(e1) for e0, e1 in ts])) * 1e-3   # s
+    return timed
+
+
+def extra_measurements(args, out, torch, np, rda, synth, dev, stream, q, k, v, a, b, S0, o, Sf,
+                       ws, T, H):
+    """The other figures the measurement plan asks for beside the headline:
+    the prefill without the cache flush between calls, the practical HBM
+    rate of an in-place read-modify-write of the decode's size, and the three
+    other prefill workloads (time, algorithmic fractions, parity)."""
+    timed = make_timer(torch, np, stream)
 
     # prefill back to back, inputs left in the Infinity Cache by the call before
     warm = timed(lambda: rda.rda_prefill(q, k, v, a, b, S0=S0, o=o, S_final=Sf, workspace=ws), 10)
@@ -327,7 +356,17 @@ def extra_measurements(args, out, torch, np, rda, synth, dev, stream, q, k, v, a
     if "decode" in out:
         out["decode"]["frac_of_practical"] = out["decode"]["value"] / hbm_gbps
 
-    flush = lambda: scratch.mul_(1.0)   # 512 MiB of traffic evicts the Infinity Cache
+    # evicts the Infinity Cache by reading 512 MiB: a read-only flush, so the
+    # timed call does not pay for writing back the flush's own dirty lines
+    flush_buf = torch.ones((128 << 20,), dtype=torch.float32, device=dev)
+    flush = lambda: flush_buf.sum()
+    # the headline prefill again, each call after the read-only flush (no
+    # input in the cache and no dirty lines of other work left to write back)
+    clean = timed(lambda: rda.rda_prefill(q, k, v, a, b, S0=S0, o=o, S_final=Sf, workspace=ws),
+                  10, flush)
+    out["prefill"]["ms_per_call_read_flushed"] = clean * 1e3
+    out["prefill"]["tokens_per_s_read_flushed"] = T / clean
+
     configs = {}
     for cid, name in ((1, "single_head_fp32_T64"), (2, "nano_layer_T2048_H16"),
                       (4, "varlen_8_seqs_T32768_H16")):
@@ -373,7 +412,70 @@ def extra_measurements(args, out, torch, np, rda, synth, dev, stream, q, k, v, a
         if cid == 4:
             entry["lengths"] = [int(x) for x in np.diff(cuc)]
     out["other_prefill_workloads"] = configs
-    del scratch
+    out["decode_tokens"] = decode_tokens_measurements(args, out, torch, np, rda, synth, dev,
+                                                      stream, timed, flush)
+    del scratch, flush_buf
+
+
+def decode_tokens_measurements(args, out, torch, np, rda, synth, dev, stream, timed, flush,
+                               reps=10, modes=None):
+    """rda_decode_tokens on the decode batch with one token plus two drafts
+    (B = 256 sequences x 16 heads, T = 3, per-sequence accept counts): the
+    one-pass verify + commit in place, a read-only verify, and a commit-only
+    call, each timed after a cache flush, with algorithmic state bandwidth."""
+    B, T, H = 256, 3, 16
+    x = synth.decode_tokens_inputs(B, T, H)
+    S0 = synth.decode_state(B, H)
+    qd, kd, vd = (torch.from_numpy(getattr(x, n)).to(torch.bfloat16).to(dev) for n in "qkv")
+    ad, bd = torch.from_numpy(x.a).to(dev), torch.from_numpy(x.b).to(dev)
+    acc = torch.from_numpy(x.accept).to(dev)
+    S = torch.from_numpy(S0).to(dev)
+    od = torch.empty((B, T, H, D), dtype=torch.float32, device=dev)
+    n_acc = float(np.mean(x.accept))
+    tok_in = 3 * D * 2 + 2 * 4                  # bf16 q, k, v + fp32 a, b per token-head
+    st_bytes = B * H * STATE_BYTES
+    table = {
+        # name: (S_out, accept, o, algorithmic bytes)
+        "verify_commit_in_place": (S, acc, od, 2 * st_bytes + B * H * T * (tok_in + D * 4)),
+        "verify_only": (None, None, od, st_bytes + B * H * T * (tok_in + D * 4)),
+        "commit_only": (S, acc, None, 2 * st_bytes + B * H * n_acc * (tok_in - D * 2)),
+    }
+    res = {"B": B, "T": T, "H": H, "mean_accept": n_acc}
+    S_copy = S.clone()
+    for name, (So, ac, o_, nbytes) in table.items():
+        if modes is not None and name not in modes:
+            continue
+        cargs = [rda._ptr(qd) if o_ is not None else None, rda._ptr(kd), rda._ptr(vd), 0,
+                 rda._ptr(ad), rda._ptr(bd), B, T, H, D, D, rda._ptr(S), rda._ptr(So),
+                 rda._ptr(ac), rda._ptr(o_), stream.cuda_stream]
+
+        def call():
+            if rda.lib().rda_decode_tokens(*cargs) != 0:
+                raise RuntimeError("rda_decode_tokens failed")
+        sec = timed(call, reps, flush)
+        S.copy_(S_copy)         # in-place modes advanced the states: restore them
+        res[name] = {"us_per_call": sec * 1e6, "GBps": nbytes / sec / 1e9,
+                     "frac_of_peak": nbytes / sec / 1e9 / PEAK_HBM_GBPS}
+    if "decode" in out:
+        res["three_decode_steps_us"] = 3 * out["decode"]["us_per_step"]
+    # parity of the one-pass call on 32 sampled (sequence, head) states
+    if not args.no_cpu:
+        import oracle
+        torch.cuda.synchronize()
+        rda.rda_decode_tokens(qd, kd, vd, ad, bd, S, S_out=S, accept=acc, o=od, stream=stream)
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(9)
+        pick = rng.choice(B * H, size=32, replace=False)
+        sb, sh = pick // H, pick % H
+        sel = lambda arr: np.ascontiguousarray(arr[sb, :, sh][:, :, None])
+        ro, rS = oracle.decode_tokens(sel(x.q), sel(x.k), sel(x.v), sel(x.a), sel(x.b),
+                                      S0[sb, sh][:, None], x.accept[sb])
+        og = od.cpu().numpy()[sb, :, sh].astype(np.float64)
+        Sg = S.cpu().numpy()[sb, sh].astype(np.float64)
+        res["parity_sampled"] = {
+            "o_rel_l2": float(np.linalg.norm(og - ro[:, :, 0]) / np.linalg.norm(ro)),
+            "S_rel_l2": float(np.linalg.norm(Sg - rS[:, 0]) / np.linalg.norm(rS))}
+    return res
 
 
 if __name__ == "__main__":

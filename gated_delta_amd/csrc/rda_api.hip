@@ -232,6 +232,43 @@ rda_status rda_decode_step(const void* q, const void* k, const void* v, rda_dtyp
     return RDA_OK;
 }
 
+rda_status rda_decode_tokens(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
+                             const float* a, const float* b, int32_t batch, int32_t tokens,
+                             int32_t num_heads, int32_t dk, int32_t dv, const float* S_in,
+                             float* S_out, const int32_t* accept, float* o, hipStream_t stream) {
+    if (qkv_dtype != RDA_BF16 && qkv_dtype != RDA_FP32) return RDA_ERR_DTYPE;
+    if (batch < 0 || tokens < 0 || tokens > RDA_DECODE_MAX_TOKENS) return RDA_ERR_SHAPE;
+    rda_status st = check_dims(num_heads, dk, dv);
+    if (st != RDA_OK) return st;
+    if (int64_t(batch) * num_heads > INT32_MAX / 2) return RDA_ERR_SHAPE;
+    if (batch == 0) return RDA_OK;
+    if (!S_in || (!S_out && !o)) return RDA_ERR_NULL;
+    if (tokens > 0 && (!k || !v || !a || !b || (o && !q))) return RDA_ERR_NULL;
+    for (const void* p : {q, k, v, static_cast<const void*>(a), static_cast<const void*>(b),
+                          static_cast<const void*>(S_in), static_cast<const void*>(S_out),
+                          static_cast<const void*>(o)})
+        if (p && !aligned16(p)) return RDA_ERR_ALIGN;
+    if (accept && (reinterpret_cast<uintptr_t>(accept) & 3u)) return RDA_ERR_ALIGN;
+    const size_t esz = qkv_dtype == RDA_BF16 ? 2 : 4;
+    const size_t bh = size_t(batch) * num_heads;
+    const size_t th = bh * size_t(tokens);
+    const Range rq = rng(o ? q : nullptr, th * kD * esz), rk = rng(k, th * kD * esz);
+    const Range rv = rng(v, th * kD * esz), ra = rng(a, th * 4), rb = rng(b, th * 4);
+    const Range rsi = rng(S_in, bh * kD * kD * 4), rso = rng(S_out, bh * kD * kD * 4);
+    const Range racc = rng(accept, accept ? size_t(batch) * 4 : 0), ro = rng(o, th * kD * 4);
+    for (Range in : {rq, rk, rv, ra, rb, rsi, rso, racc})
+        if (overlap(ro, in)) return RDA_ERR_ALIAS;
+    for (Range in : {rq, rk, rv, ra, rb, racc})
+        if (overlap(rso, in)) return RDA_ERR_ALIAS;
+    if (S_out && S_out != S_in && overlap(rso, rsi)) return RDA_ERR_ALIAS;
+    // zero tokens: the only work is copying S_in to a distinct S_out
+    if (tokens == 0 && (!S_out || S_out == S_in)) return RDA_OK;
+    if (launch_decode_tokens(q, k, v, qkv_dtype, a, b, batch, tokens, num_heads, S_in, S_out,
+                             accept, o, stream) != hipSuccess)
+        return RDA_ERR_HIP;
+    return RDA_OK;
+}
+
 rda_status rda_chunk_table(const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
                            int32_t* out, int32_t* out_seq_offsets, int32_t* out_num_chunks,
                            hipStream_t stream) {

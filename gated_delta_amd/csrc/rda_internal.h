@@ -67,6 +67,13 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, rda_dtype 
                          const float* a, const float* b, int32_t batch, int32_t heads,
                          float* S, float* o, hipStream_t stream);
 
+// Several tokens per (batch, head); o == nullptr selects the commit-only
+// kernel (no outputs, stops after the accepted tokens).
+hipError_t launch_decode_tokens(const void* q, const void* k, const void* v, rda_dtype dt,
+                                const float* a, const float* b, int32_t batch, int32_t tokens,
+                                int32_t heads, const float* S_in, float* S_out,
+                                const int32_t* accept, float* o, hipStream_t stream);
+
 hipError_t launch_prep(const void* q, const void* k, rda_dtype dt,
                        const float* a, const float* b, int32_t heads, int32_t max_chunks,
                        const int32_t* rec, const int32_t* num_chunks, unsigned char* factors,

@@ -1,6 +1,7 @@
 #!/bin/bash
-# Collects the rocprofv3 kernel summary and the counter passes behind
-# profiles/: kernel trace + stats of the default bench command, then one
+# Collects the rocprofv3 kernel summaries and the counter passes behind
+# profiles/: kernel trace + stats of the bench's timed steps (and, in a pass
+# of its own, of the one-pass multi-token decode), then one
 # FETCH_SIZE and one WRITE_SIZE pass over the prefill alone and over a plain
 # device copy of known size (the counter calibration), then one pass of the
 # MFMA counters over the prefill.
@@ -12,9 +13,14 @@ set -o pipefail
 R="$(cd "$(dirname "$0")/.." && pwd)"
 OUT="$(mkdir -p "${1:?output directory}" && cd "$1" && pwd)"
 cd /tmp && export TMPDIR=/tmp
-echo "== kernel trace + stats: python bench.py --steps 20 --warmup 3 --no-cpu"
+echo "== kernel trace + stats: python bench.py --steps 20 --warmup 3 --no-cpu --no-extras"
 timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d "$OUT/prof_trace" -o trace \
-    -- python -u "$R/bench.py" --steps 20 --warmup 3 --no-cpu > "$OUT/prof_trace.log" 2>&1 || exit $?
+    -- python -u "$R/bench.py" --steps 20 --warmup 3 --no-cpu --no-extras \
+    > "$OUT/prof_trace.log" 2>&1 || exit $?
+echo "== kernel trace + stats: python bench.py --mode decode_tokens --steps 20 --no-cpu"
+timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d "$OUT/prof_trace_dt" -o trace \
+    -- python -u "$R/bench.py" --mode decode_tokens --steps 20 --no-cpu \
+    > "$OUT/prof_trace_dt.log" 2>&1 || exit $?
 for ctr in FETCH_SIZE WRITE_SIZE; do
   for mode in prefill copy; do
     echo "== pmc $ctr: python bench.py --mode $mode --steps 2 --warmup 1 --no-cpu"

@@ -4,8 +4,10 @@ usage: python gated_delta_amd/profile_summary.py OUTDIR
 
 Writes
   profiles/kernels_rda_prefill_T16384_H16_decode_B256_H16.txt
-      per-kernel call count and average / total duration of the default
-      bench command (kernel trace + stats);
+      per-kernel call count and average / total duration of the bench's
+      timed steps (kernel trace + stats);
+  profiles/kernels_rda_decode_tokens_B256_T3_H16.txt
+      the same for the one-pass multi-token decode (bench --mode decode_tokens);
   profiles/hbm_traffic.txt
       FETCH_SIZE and WRITE_SIZE per dispatch of every prefill kernel, each
       scaled by what the same counter reads for a device copy of known size,
@@ -27,7 +29,8 @@ from gated_delta_amd.srchash import kernel_source_hash as source_hash  # noqa: E
 
 # HIP kernel -> the stage name bench.py reports it under
 STAGE = {"chunk_table_kernel": "rda_chunk_table", "prep_bf16_kernel": "rda_prep",
-         "walk_bf16_kernel": "rda_walk", "decode_step_kernel": "rda_decode_step"}
+         "walk_bf16_kernel": "rda_walk", "decode_step_kernel": "rda_decode_step",
+         "decode_tokens_kernel": "rda_decode_tokens"}
 
 
 def short(name: str) -> str:
@@ -54,28 +57,49 @@ def counter(d, name):
     return {k: statistics.mean(v[1:] if len(v) > 1 else v) for k, v in by.items()}
 
 
+def kernel_table(trace_dir, path, header):
+    """Write the per-kernel call count / average / total of one kernel-trace
+    pass to `path` under `header`; returns the stats rows."""
+    rows = list(csv.DictReader(open(find(trace_dir, "*kernel_stats.csv"))))
+    lines = header + [f"# kernel sources: {source_hash()}",
+                      f"{'kernel':40s} {'calls':>6s} {'avg_us':>10s} {'total_us':>12s} {'pct':>6s}"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"{short(r['Name'])[:40]:40s} {int(r['Calls']):6d} "
+                     f"{float(r['AverageNs']) / 1e3:10.2f} {float(r['TotalDurationNs']) / 1e3:12.1f} "
+                     f"{float(r['Percentage']):6.2f}")
+    open(path, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return rows
+
+
 def main():
     out = sys.argv[1]
     prof = os.path.join(ROOT, "profiles")
     os.makedirs(prof, exist_ok=True)
 
     # ---- kernel trace summary ------------------------------------------------
-    rows = list(csv.DictReader(open(find(os.path.join(out, "prof_trace"), "*kernel_stats.csv"))))
-    lines = ["# rocprofv3 kernel trace, default bench step: RDA prefill T=16384 H=16 d=128 (bf16",
-             "# q/k/v, fp32 state) + one RDA decode step B=256 H=16, 20 timed + 3 warmup steps",
-             "# command: gated_delta_amd/profile_run.sh OUTDIR, whose first pass is",
-             "#   rocprofv3 --kernel-trace --stats --output-format csv -d OUTDIR/prof_trace -o trace \\",
-             "#     -- python bench.py --steps 20 --warmup 3 --no-cpu",
-             "# then python gated_delta_amd/profile_summary.py OUTDIR",
-             f"# kernel sources: {source_hash()}",
-             f"{'kernel':40s} {'calls':>6s} {'avg_us':>10s} {'total_us':>12s} {'pct':>6s}"]
-    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
-        lines.append(f"{short(r['Name'])[:40]:40s} {int(r['Calls']):6d} "
-                     f"{float(r['AverageNs']) / 1e3:10.2f} {float(r['TotalDurationNs']) / 1e3:12.1f} "
-                     f"{float(r['Percentage']):6.2f}")
-    path = os.path.join(prof, "kernels_rda_prefill_T16384_H16_decode_B256_H16.txt")
-    open(path, "w").write("\n".join(lines) + "\n")
-    print("\n".join(lines))
+    rows = kernel_table(
+        os.path.join(out, "prof_trace"),
+        os.path.join(prof, "kernels_rda_prefill_T16384_H16_decode_B256_H16.txt"),
+        ["# rocprofv3 kernel trace, the bench's timed steps: RDA prefill T=16384 H=16",
+         "# d=128 (bf16 q/k/v, fp32 state) + one RDA decode step B=256 H=16; 3 warmup + 20",
+         "# timed steps, then 20 per-stage prefill calls (each followed by a decode step)",
+         "# command: gated_delta_amd/profile_run.sh OUTDIR, whose first pass is",
+         "#   rocprofv3 --kernel-trace --stats --output-format csv -d OUTDIR/prof_trace -o trace \\",
+         "#     -- python bench.py --steps 20 --warmup 3 --no-cpu --no-extras",
+         "# then python gated_delta_amd/profile_summary.py OUTDIR"])
+    if os.path.isdir(os.path.join(out, "prof_trace_dt")):
+        kernel_table(
+            os.path.join(out, "prof_trace_dt"),
+            os.path.join(prof, "kernels_rda_decode_tokens_B256_T3_H16.txt"),
+            ["# rocprofv3 kernel trace, the one-pass multi-token decode: rda_decode_tokens on",
+             "# B=256 sequences x H=16 heads, T=3 tokens (one token plus two drafts), bf16",
+             "# q/k/v, per-sequence accept counts, fp32 states in place; 20 calls, each after a",
+             "# 512 MiB read (reduce_kernel: the cache flush) and followed by a state restore",
+             "# command: gated_delta_amd/profile_run.sh OUTDIR, whose second pass is",
+             "#   rocprofv3 --kernel-trace --stats --output-format csv -d OUTDIR/prof_trace_dt -o trace \\",
+             "#     -- python bench.py --mode decode_tokens --steps 20 --no-cpu",
+             "# then python gated_delta_amd/profile_summary.py OUTDIR"])
 
     # ---- HBM traffic -------------------------------------------------------------
     n = 1 << 30   # bytes the calibration copy reads and writes per launch

@@ -23,6 +23,7 @@ RDA_BF16 = 0
 RDA_FP32 = 1
 RDA_CHUNK = 64
 RDA_HEAD_DIM = 128
+RDA_DECODE_MAX_TOKENS = 64
 RDA_STAGE_TABLE, RDA_STAGE_PREP, RDA_STAGE_WALK = 0, 1, 2
 RDA_NUM_STAGES = 3
 STAGES = ("table", "prep", "walk")
@@ -62,6 +63,9 @@ def _load():
         lib.rda_prefill_profiled.restype = ctypes.c_int
         lib.rda_decode_step.argtypes = [p, p, p, ctypes.c_int, p, p, i32, i32, i32, i32, p, p, p]
         lib.rda_decode_step.restype = ctypes.c_int
+        lib.rda_decode_tokens.argtypes = [p, p, p, ctypes.c_int, p, p, i32, i32, i32, i32, i32,
+                                          p, p, p, p, p]
+        lib.rda_decode_tokens.restype = ctypes.c_int
         lib.rda_chunk_table.argtypes = [p, i32, i32, p, p, p, p]
         lib.rda_chunk_table.restype = ctypes.c_int
         _lib = lib
@@ -243,6 +247,58 @@ def rda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, a: torch.
                               _ptr(S), _ptr(o), _stream_handle(stream))
     if st != 0:
         raise RdaError(st, "rda_decode_step")
+    return o
+
+
+_NO_OUTPUT = object()
+
+
+def rda_decode_tokens(q: Optional[torch.Tensor], k: torch.Tensor, v: torch.Tensor,
+                      a: torch.Tensor, b: torch.Tensor, S_in: torch.Tensor, *,
+                      S_out: Optional[torch.Tensor] = None,
+                      accept: Optional[torch.Tensor] = None, o=None,
+                      stream=None) -> Optional[torch.Tensor]:
+    """Several tokens per sequence in one pass (C entry point ``rda_decode_tokens``).
+
+    q, k, v [B, T, H, 128] (bf16 or fp32), a, b [B, T, H] fp32, S_in
+    [B, H, 128, 128] fp32.  S_out (same shape, may be S_in itself) receives
+    the state after the first accept[n] tokens of each sequence (accept
+    int32 [B] on the device, None = all T); S_out=None leaves every state
+    unchanged.  Returns o [B, T, H, 128] fp32 for every token, or None when
+    called with o=False (commit only: q is then not read and may be None).
+    """
+    lib_ = _load()
+    dev = k.device
+    if k.dim() != 4:
+        raise ValueError(f"k must be [B, T, H, d], got shape {tuple(k.shape)}")
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    dt = _qkv_dtype(k)
+    want_o = o is not False
+    if want_o:
+        if q is None:
+            raise ValueError("q is required when outputs are produced")
+        _need(q, "q", k.dtype, (B, T, H, dk), dev)
+    _need(k, "k", k.dtype, (B, T, H, dk), dev)
+    _need(v, "v", k.dtype, (B, T, H, dv), dev)
+    _need(a, "a", torch.float32, (B, T, H), dev)
+    _need(b, "b", torch.float32, (B, T, H), dev)
+    _need(S_in, "S_in", torch.float32, (B, H, dv, dk), dev)
+    if S_out is not None:
+        _need(S_out, "S_out", torch.float32, (B, H, dv, dk), dev)
+    if accept is not None:
+        _need(accept, "accept", torch.int32, (B,), dev)
+    if want_o:
+        if o is None:
+            o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+        _need(o, "o", torch.float32, (B, T, H, dv), dev)
+    else:
+        o = None
+    st = lib_.rda_decode_tokens(_ptr(q) if want_o else None, _ptr(k), _ptr(v), dt, _ptr(a),
+                                _ptr(b), B, T, H, dk, dv, _ptr(S_in), _ptr(S_out),
+                                _ptr(accept), _ptr(o), _stream_handle(stream))
+    if st != 0:
+        raise RdaError(st, "rda_decode_tokens")
     return o
 
 

@@ -234,4 +234,29 @@ def decode_step_inputs(step: int, B: int = 256, H: int = 16, dk: int = 128,
     return DecodeStepInputs(q, k, v, a, b)
 
 
+@dataclass
+class DecodeTokensInputs:
+    q: np.ndarray   # [B, T, H, dk] float32 (exact bf16 values)
+    k: np.ndarray
+    v: np.ndarray   # [B, T, H, dv]
+    a: np.ndarray   # [B, T, H]
+    b: np.ndarray
+    accept: np.ndarray  # int32 [B], uniform in [0, T]
+
+
+def decode_tokens_inputs(B: int = 256, T: int = 3, H: int = 16, dk: int = 128,
+                         dv: int = 128, bf16: bool = True, key=(6,)) -> DecodeTokensInputs:
+    """T tokens per (batch, head) for a verify of drafted tokens (one token
+    plus T - 1 drafts), with a per-sequence accepted count."""
+    rq, rk, rv, ra, rb, rc = _children(*key, n=6)
+    q = unit_rows(rq, (B, T, H, dk)).astype(np.float32)
+    k = unit_rows(rk, (B, T, H, dk)).astype(np.float32)
+    v = rv.standard_normal((B, T, H, dv)).astype(np.float32)
+    if bf16:
+        q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
+    a, b = gates(ra, rb, (B, T, H))
+    accept = rc.integers(0, T + 1, size=B).astype(np.int32)
+    return DecodeTokensInputs(q, k, v, a, b, accept)
+
+
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4}

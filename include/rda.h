@@ -19,7 +19,8 @@
  * (read-out after the update; no query scale; q and k are used as given --
  * callers L2-normalise them).  rda_prefill evaluates it for whole prompts in
  * chunks of 64 tokens (WY / UT-transform form on bf16 MFMA); rda_decode_step
- * applies one token in place.
+ * applies one token in place; rda_decode_tokens applies a few (a verify of
+ * drafted tokens) in one pass over the state.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -53,6 +54,7 @@ extern "C" {
 #define RDA_ABI_VERSION 1
 #define RDA_CHUNK 64      /* tokens per prefill chunk */
 #define RDA_HEAD_DIM 128  /* the only supported dk = dv */
+#define RDA_DECODE_MAX_TOKENS 64  /* tokens per rda_decode_tokens call (one chunk) */
 
 typedef enum {
     RDA_OK = 0,
@@ -148,6 +150,41 @@ rda_status rda_decode_step(const void* q, const void* k, const void* v, rda_dtyp
                            const float* a, const float* b,
                            int32_t batch, int32_t num_heads, int32_t dk, int32_t dv,
                            float* S, float* o, hipStream_t stream);
+
+/*
+ * Several tokens per sequence in one pass over the state: the decode step
+ * for a verify of drafted tokens.  The "Raon-1-nano-gguf" model card's
+ * llama.cpp section runs the model with multi-token prediction proposing
+ * two drafts per step, and the Raon-1-mini vLLM support article discusses
+ * the speculative-decoding draft model; verifying such a step feeds the
+ * current token plus its drafts (tokens = 1 + drafts) through the mixer
+ * and keeps the state only up to the last accepted token.  The recurrence
+ * is the one above, applied token after token; each state is read once and
+ * written at most once.
+ *
+ *   q, k [batch, tokens, H, dk], v [batch, tokens, H, dv] (qkv_dtype);
+ *   a, b [batch, tokens, H] fp32 -- the packed layout of `batch` sequences
+ *        of `tokens` tokens each
+ *   S_in   [batch, H, dv, dk] fp32 state before the first token (read)
+ *   accept device int32 [batch] or NULL: tokens to commit per sequence,
+ *          clamped to [0, tokens]; NULL commits all `tokens`
+ *   S_out  [batch, H, dv, dk] fp32 or NULL: receives the state after the
+ *          first accept[n] tokens of sequence n.  S_out == S_in updates in
+ *          place; NULL leaves every state untouched (read-only verify)
+ *   o      [batch, tokens, H, dv] fp32 or NULL: o_t = S_t q_t for every
+ *          token, accepted or not.  NULL skips the outputs (q is then not
+ *          read and may be NULL): a commit after a read-only verify
+ * A verify whose accept counts are only known from its outputs runs as two
+ * calls: S_out = NULL with o, then accept with S_out and o = NULL.
+ * tokens in [0, RDA_DECODE_MAX_TOKENS] (longer runs belong to rda_prefill);
+ * tokens = 1 with S_out == S_in and accept = NULL is rda_decode_step.
+ * S_in may be NULL only when batch = 0; S_out and o may not both be NULL.
+ * S_out and S_in must be the same pointer or disjoint (RDA_ERR_ALIAS).
+ */
+rda_status rda_decode_tokens(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
+                             const float* a, const float* b, int32_t batch, int32_t tokens,
+                             int32_t num_heads, int32_t dk, int32_t dv, const float* S_in,
+                             float* S_out, const int32_t* accept, float* o, hipStream_t stream);
 
 /*
  * Test hook: the chunk table rda_prefill builds from cu_seqlens.

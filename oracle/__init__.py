@@ -66,6 +66,9 @@ class Oracle:
     def decode_step(self, q, k, v, a, b, S, threads: int = 0):
         return _decode_step(self.lib, q, k, v, a, b, S, threads)
 
+    def decode_tokens(self, q, k, v, a, b, S_in, accept=None, threads: int = 0):
+        return _decode_tokens(self.lib, q, k, v, a, b, S_in, accept, threads)
+
 
 def default() -> Oracle:
     global _default
@@ -98,6 +101,11 @@ def prefill(q, k, v, a, b, cu_seqlens=None, S0=None, threads: int = 0):
 def decode_step(q, k, v, a, b, S, threads: int = 0):
     """One in-place fp64 decode step with the default build (see _decode_step)."""
     return default().decode_step(q, k, v, a, b, S, threads)
+
+
+def decode_tokens(q, k, v, a, b, S_in, accept=None, threads: int = 0):
+    """Several tokens per sequence with the default build (see _decode_tokens)."""
+    return default().decode_tokens(q, k, v, a, b, S_in, accept, threads)
 
 
 def _prefill(lib, q, k, v, a, b, cu_seqlens=None, S0=None, threads: int = 0):
@@ -147,3 +155,39 @@ def _decode_step(lib, q, k, v, a, b, S, threads: int = 0):
     if rc != 0:
         raise ValueError(f"oracle_rda_decode_step failed with code {rc}")
     return o
+
+
+def _decode_tokens(lib, q, k, v, a, b, S_in, accept=None, threads: int = 0):
+    """Several tokens per sequence: the verify of drafted tokens.
+
+    The "Raon-1-nano-gguf" model card runs the model with multi-token
+    prediction proposing two drafts per step; verifying them feeds the
+    current token and its drafts through the recurrence in order and keeps
+    the state only up to the last accepted token.  So: the T tokens of
+    sequence n run through the recurrence from S_in[n]; o holds every
+    token's output and S the state after the first accept[n] tokens.
+
+    q, k: [B, T, H, dk]; v: [B, T, H, dv]; a, b: [B, T, H]; S_in: [B, H, dv, dk];
+    accept: ints [B] in [0, T], or None for T.
+    Returns (o [B, T, H, dv] float64, S [B, H, dv, dk] float64).
+    """
+    q, k, v, a, b = (_f32(x) for x in (q, k, v, a, b))
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    S_in = _f64(S_in)
+    assert S_in.shape == (B, H, dv, dk)
+    acc = np.full(B, T, dtype=np.int64) if accept is None else np.asarray(accept, np.int64)
+    assert acc.shape == (B,) and np.all((acc >= 0) & (acc <= T))
+
+    def packed(x, rows):
+        return np.ascontiguousarray(x.reshape((B * T,) + x.shape[2:])[rows])
+
+    every = np.arange(B * T)
+    cu = (T * np.arange(B + 1)).astype(np.int32)
+    o, _ = _prefill(lib, *(packed(x, every) for x in (q, k, v, a, b)), cu_seqlens=cu,
+                    S0=S_in, threads=threads)
+    kept = np.concatenate([n * T + np.arange(acc[n]) for n in range(B)] + [np.zeros(0, int)])
+    cu_kept = np.concatenate([[0], np.cumsum(acc)]).astype(np.int32)
+    _, S = _prefill(lib, *(packed(x, kept) for x in (q, k, v, a, b)), cu_seqlens=cu_kept,
+                    S0=S_in, threads=threads)
+    return o.reshape(B, T, H, dv), S

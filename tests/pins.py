@@ -313,7 +313,32 @@ def pin_decode_equals_prefill(orc):
     _close(S, s, 1e-13, "decode final state")
 
 
+def pin_decode_tokens(orc):
+    """Several tokens per sequence equal that many single-token decode steps
+    per sequence; the committed state is the one after the accepted tokens
+    (0 keeps S_in, T is the state after every token)."""
+    rng = _rng(21)
+    B, T, H, dk, dv = 4, 3, 2, 6, 5
+    q, k, v, a, b, _ = random_case(rng, B * T, H, dk, dv)
+    q, k, v = (x.reshape(B, T, H, -1) for x in (q, k, v))
+    a, b = (x.reshape(B, T, H) for x in (a, b))
+    S_in = rng.standard_normal((B, H, dv, dk))
+    accept = np.array([0, 3, 1, 2])
+    o, S = orc.decode_tokens(q, k, v, a, b, S_in, accept)
+    o_all, S_all = orc.decode_tokens(q, k, v, a, b, S_in)
+    Sd = np.ascontiguousarray(S_in.copy())
+    for t in range(T):
+        ot = orc.decode_step(q[:, t], k[:, t], v[:, t], a[:, t], b[:, t], Sd)
+        _close(o[:, t], ot, 1e-13, f"decode_tokens o token {t}")
+        for n in range(B):
+            if accept[n] == t + 1:
+                _close(S[n], Sd[n], 1e-13, f"decode_tokens state seq {n}")
+    assert np.array_equal(S[0], S_in[0])
+    _close(S_all, Sd, 1e-13, "decode_tokens state, all accepted")
+    _close(o_all, o, 0, "outputs do not depend on accept")
+
+
 ALL_PINS = [pin_bruteforce, pin_exact_dyadic, pin_hand_example, pin_identity_gates,
             pin_readback, pin_pure_decay, pin_single_step, pin_linearity, pin_rotation,
             pin_permutation, pin_norm_bound, pin_resume, pin_varlen,
-            pin_decode_equals_prefill]
+            pin_decode_equals_prefill, pin_decode_tokens]

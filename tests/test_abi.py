@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("rda_prefill", "rda_decode_step", "rda_prefill_workspace_bytes",
+    for n in ("rda_prefill", "rda_decode_step", "rda_decode_tokens", "rda_prefill_workspace_bytes",
               "rda_chunk_table", "rda_abi_version", "rda_status_string"):
         assert n in names
 
@@ -45,7 +45,8 @@ def test_binding_constants_match_header():
     vals = {m[0]: int(m[1]) for m in re.findall(r"\b(RDA_[A-Z0-9_]+)\s*=\s*(\d+)", text)}
     vals.update({m[0]: int(m[1]) for m in
                  re.findall(r"#define\s+(RDA_[A-Z0-9_]+)\s+(\d+)", text)})
-    for name in ("RDA_BF16", "RDA_FP32", "RDA_CHUNK", "RDA_HEAD_DIM", "RDA_STAGE_TABLE",
+    for name in ("RDA_BF16", "RDA_FP32", "RDA_CHUNK", "RDA_HEAD_DIM", "RDA_DECODE_MAX_TOKENS",
+                 "RDA_STAGE_TABLE",
                  "RDA_STAGE_PREP", "RDA_STAGE_WALK", "RDA_NUM_STAGES"):
         assert getattr(rda, name) == vals[name], name
 
@@ -120,6 +121,32 @@ def test_decode_rejects_bad_arguments(lib):
     assert dec(o=P + 4) == ALIGN
     assert dec(o=P + 5 * GiB + 512) == ALIAS      # o inside S
     assert dec(S=P + 2 * GiB) == ALIAS            # S over v
+
+
+def test_decode_tokens_rejects_bad_arguments(lib):
+    def dec(q=P, k=P + GiB, v=P + 2 * GiB, dt=0, a=P + 3 * GiB, b=P + 4 * GiB, B=4, T=3, H=2,
+            dk=128, dv=128, Si=P + 5 * GiB, So=P + 5 * GiB, acc=None, o=P + 6 * GiB):
+        return lib.rda_decode_tokens(q, k, v, dt, a, b, B, T, H, dk, dv, Si, So, acc, o, None)
+    assert dec(B=0) == OK                        # nothing to do: no launch
+    assert dec(T=0) == OK                        # in place, no tokens: no launch
+    assert dec(T=0, So=None) == OK
+    assert dec(Si=None) == NULL
+    assert dec(So=None, o=None) == NULL          # nothing would be produced
+    assert dec(q=None) == NULL                   # q is read when o is produced
+    assert dec(k=None) == NULL
+    assert dec(dt=2) == DTYPE
+    assert dec(B=-1) == SHAPE
+    assert dec(T=-1) == SHAPE
+    assert dec(T=65) == SHAPE                    # beyond one chunk: rda_prefill's job
+    assert dec(B=1 << 26, H=16) == SHAPE
+    assert dec(dv=64) == UNSUP
+    assert dec(o=P + 8) == ALIGN
+    assert dec(acc=P + 7 * GiB + 2) == ALIGN
+    assert dec(o=P + 5 * GiB + 4096) == ALIAS    # o inside the state
+    assert dec(So=P + 2 * GiB) == ALIAS          # S_out over v
+    assert dec(So=P + 5 * GiB + 1024) == ALIAS   # S_out partly over S_in
+    assert dec(acc=P + 6 * GiB + 16) == ALIAS    # accept inside o
+    assert dec(So=P + 7 * GiB, acc=P + 7 * GiB + 4096) == ALIAS  # accept inside S_out
 
 
 def test_chunk_table_rejects_bad_arguments(lib):
