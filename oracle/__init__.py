@@ -32,7 +32,7 @@ def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
     if force or not os.path.exists(out):
         tmp = out + ".tmp"
         cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared",
-               "-Wall", "-Wextra", "-o", tmp, src]
+               "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, out)
     return out
@@ -53,6 +53,9 @@ class Oracle:
         lib.oracle_rda_decode_step.argtypes = [p, p, p, p, p, i32, i32, i32, i32,
                                                p, p, i32]
         lib.oracle_rda_decode_step.restype = ctypes.c_int
+        lib.oracle_output_norm_gate.argtypes = [p, p, p, ctypes.c_double, i32,
+                                                ctypes.c_int64, i32, p]
+        lib.oracle_output_norm_gate.restype = ctypes.c_int
         lib.oracle_threads.argtypes = [i32]
         lib.oracle_threads.restype = ctypes.c_int
         self.lib = lib
@@ -68,6 +71,9 @@ class Oracle:
 
     def decode_tokens(self, q, k, v, a, b, S_in, accept=None, threads: int = 0):
         return _decode_tokens(self.lib, q, k, v, a, b, S_in, accept, threads)
+
+    def output_norm_gate(self, o, g, w, eps: float = 1e-5, act: str = "sigmoid"):
+        return _output_norm_gate(self.lib, o, g, w, eps, act)
 
 
 def default() -> Oracle:
@@ -106,6 +112,38 @@ def decode_step(q, k, v, a, b, S, threads: int = 0):
 def decode_tokens(q, k, v, a, b, S_in, accept=None, threads: int = 0):
     """Several tokens per sequence with the default build (see _decode_tokens)."""
     return default().decode_tokens(q, k, v, a, b, S_in, accept, threads)
+
+
+def output_norm_gate(o, g, w, eps: float = 1e-5, act: str = "sigmoid"):
+    """Output epilogue with the default build (see _output_norm_gate)."""
+    return default().output_norm_gate(o, g, w, eps, act)
+
+
+GATE_ACTS = {"sigmoid": 0, "silu": 1, "none": 2}
+
+
+def _output_norm_gate(lib, o, g, w, eps=1e-5, act="sigmoid"):
+    """Per row of the last axis: RMS norm with eps and weight w, times act(g).
+
+    o, g: [..., dv] (values exactly representable in fp32); w: [dv] or None;
+    act: "sigmoid", "silu" or "none" (g may then be None).
+    Returns float64 of o's shape.
+    """
+    o = _f32(o)
+    dv = o.shape[-1]
+    rows = o.size // dv if dv else 0
+    g = None if g is None else _f32(g)
+    if g is not None:
+        assert g.shape == o.shape
+    w = None if w is None else _f32(w)
+    if w is not None:
+        assert w.shape == (dv,)
+    out = np.zeros(o.shape, dtype=np.float64)
+    rc = lib.oracle_output_norm_gate(_ptr(o), _ptr(g), _ptr(w), float(eps), GATE_ACTS[act],
+                                     rows, dv, _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_output_norm_gate failed with code {rc}")
+    return out
 
 
 def _prefill(lib, q, k, v, a, b, cu_seqlens=None, S0=None, threads: int = 0):

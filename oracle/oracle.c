@@ -35,6 +35,7 @@
  * Every input is widened exactly to double before use; all arithmetic is
  * double.
  */
+#include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -186,6 +187,41 @@ int oracle_rda_decode_step(const float* q, const float* k, const float* v,
         free(e);
     }
     return err;
+}
+
+/*
+ * Output epilogue of the mixer: per output row of one head (dv channels),
+ * an RMS normalisation with epsilon and a per-channel weight, times an
+ * activation of the output gate.  The tiny-random/raon-1-mini model card,
+ * section "Printing the model", lists the RDA block's o_norm as an RMS norm
+ * over the head dimension with eps 1e-5 and a g_proj projection producing
+ * the gate; the gate's activation is not printed, so `act` selects it:
+ * 0 = sigmoid, 1 = SiLU (x sigmoid(x)), 2 = none.  w may be NULL (unit
+ * weight); g may be NULL only with act = 2.
+ *
+ *     y_c = o_c / sqrt(mean_c'(o_c'^2) + eps) * w_c * act(g_c)
+ */
+int oracle_output_norm_gate(const float* o, const float* g, const float* w, double eps,
+                            int32_t act, int64_t rows, int32_t dv, double* out) {
+    if (rows < 0 || dv <= 0 || !out || (rows > 0 && !o)) return ORACLE_ERR_ARG;
+    if (act < 0 || act > 2 || (act != 2 && rows > 0 && !g)) return ORACLE_ERR_ARG;
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* orow = o + (size_t)r * dv;
+        double ms = 0.0;
+        for (int32_t c = 0; c < dv; ++c) ms += (double)orow[c] * (double)orow[c];
+        ms /= dv;
+        const double inv = 1.0 / sqrt(ms + eps);
+        for (int32_t c = 0; c < dv; ++c) {
+            double gate = 1.0;
+            if (act != 2) {
+                const double x = (double)g[(size_t)r * dv + c];
+                const double sig = 1.0 / (1.0 + exp(-x));
+                gate = act == 0 ? sig : x * sig;
+            }
+            out[(size_t)r * dv + c] = (double)orow[c] * inv * (w ? (double)w[c] : 1.0) * gate;
+        }
+    }
+    return 0;
 }
 
 /* Number of OpenMP threads a call with `threads` would use. */

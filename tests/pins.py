@@ -338,7 +338,50 @@ def pin_decode_tokens(orc):
     _close(o_all, o, 0, "outputs do not depend on accept")
 
 
+def pin_norm_gate_library(orc):
+    """The output epilogue equals torch's RMS norm (a library routine, in
+    float64) times torch's sigmoid / SiLU of the gate."""
+    import torch
+    rng = _rng(22)
+    o = _f32(rng.standard_normal((7, 3, 16)) * 2.0)
+    g = _f32(rng.standard_normal((7, 3, 16)))
+    w = _f32(rng.uniform(0.5, 1.5, 16))
+    ot, gt, wt = (torch.from_numpy(x.astype(np.float64)) for x in (o, g, w))
+    for eps in (1e-5, 0.3):
+        base = torch.nn.functional.rms_norm(ot, (16,), wt, eps)
+        _close(orc.output_norm_gate(o, g, w, eps, "sigmoid"), (base * torch.sigmoid(gt)).numpy(),
+               1e-13, f"norm gate sigmoid eps {eps}")
+        _close(orc.output_norm_gate(o, g, w, eps, "silu"),
+               (base * torch.nn.functional.silu(gt)).numpy(), 1e-13, f"norm gate silu eps {eps}")
+        _close(orc.output_norm_gate(o, None, None, eps, "none"),
+               torch.nn.functional.rms_norm(ot, (16,), None, eps).numpy(), 1e-13,
+               f"norm, no gate, eps {eps}")
+
+
+def pin_norm_gate_closed_forms(orc):
+    """A constant row c gives c / sqrt(c^2 + eps) per channel; the gate at 0
+    is 1/2 (sigmoid); scaling o by s and eps by s^2 changes nothing; the
+    result's mean square is ms / (ms + eps) without weight and gate."""
+    dv = 8
+    for c, eps in ((3.0, 1e-5), (-0.5, 0.25), (2.0, 4.0)):
+        o = np.full((1, dv), c, dtype=np.float32)
+        y = orc.output_norm_gate(o, np.zeros((1, dv), np.float32), None, eps, "sigmoid")
+        _close(y, np.full((1, dv), 0.5 * c / np.sqrt(c * c + eps)), 1e-14, f"constant row {c}")
+    rng = _rng(23)
+    o = _f32(rng.standard_normal((5, dv)))
+    g = _f32(rng.standard_normal((5, dv)))
+    w = _f32(rng.uniform(-1, 1, dv))
+    s = 4.0   # a power of two keeps the scaled inputs exact
+    _close(orc.output_norm_gate(s * o, g, w, 1e-3 * s * s, "sigmoid"),
+           orc.output_norm_gate(o, g, w, 1e-3, "sigmoid"), 1e-13, "scale invariance")
+    eps = 0.7
+    y = orc.output_norm_gate(o, None, None, eps, "none")
+    ms = np.mean(_d(o) ** 2, axis=1)
+    _close(np.mean(y ** 2, axis=1), ms / (ms + eps), 1e-13, "mean square after the norm")
+
+
 ALL_PINS = [pin_bruteforce, pin_exact_dyadic, pin_hand_example, pin_identity_gates,
             pin_readback, pin_pure_decay, pin_single_step, pin_linearity, pin_rotation,
             pin_permutation, pin_norm_bound, pin_resume, pin_varlen,
-            pin_decode_equals_prefill, pin_decode_tokens]
+            pin_decode_equals_prefill, pin_decode_tokens, pin_norm_gate_library,
+            pin_norm_gate_closed_forms]

@@ -1,6 +1,7 @@
 """Plant plausible mistakes in copies of the oracle source (CPU only) and
 check that every one of them fails at least one pin.  This shows the pins
-constrain each term, sign, index and operand of the recurrence."""
+constrain each term, sign, index and operand of the recurrence and of the
+output epilogue."""
 import os
 import shutil
 import subprocess
@@ -41,6 +42,17 @@ MUTANTS = [
      "const size_t th = (size_t)t * H + (H - 1 - h);"),
     ("decode_state_of_head0", "oracle_token(S + (size_t)u * dd, e,",
      "oracle_token(S + (size_t)(u - u % H) * dd, e,"),
+    ("norm_sum_not_mean", "ms /= dv;", "(void)0;"),
+    ("norm_without_eps", "const double inv = 1.0 / sqrt(ms + eps);",
+     "const double inv = 1.0 / sqrt(ms);"),
+    ("norm_rms_not_inverse", "const double inv = 1.0 / sqrt(ms + eps);",
+     "const double inv = sqrt(ms + eps);"),
+    ("gate_sign", "const double sig = 1.0 / (1.0 + exp(-x));",
+     "const double sig = 1.0 / (1.0 + exp(x));"),
+    ("silu_is_sigmoid", "gate = act == 0 ? sig : x * sig;", "gate = sig;"),
+    ("weight_ignored", "* (w ? (double)w[c] : 1.0) * gate;", "* gate;"),
+    ("gate_of_first_channel", "const double x = (double)g[(size_t)r * dv + c];",
+     "const double x = (double)g[(size_t)r * dv];"),
 ]
 
 
