@@ -20,7 +20,7 @@ Prints ONE JSON line:
   parity     rel-L2 / max-abs of this run's prefill output vs the oracle
 The oracle runs only in this CPU leg (skipped with --no-cpu): the baseline
 timing, and the parity figures of this run's outputs (parity, and the parity
-entries of other_prefill_workloads and decode_tokens below).
+entries of other_prefill_workloads, output_norm_gate and decode_tokens).
   also       the prefill back to back without the flush (ms_per_call_unflushed)
              and after a read-only 512 MiB flush (ms_per_call_read_flushed),
              the practical HBM rate of an in-place read-modify-write of 256 MiB
@@ -31,7 +31,8 @@ entries of other_prefill_workloads and decode_tokens below).
              (other_prefill_workloads); rda_decode_tokens on the decode batch
              with one token plus two drafts per sequence: one-pass verify +
              commit, read-only verify and commit-only, each with its state
-             bandwidth (decode_tokens)
+             bandwidth (decode_tokens); the output norm and gate on the long
+             prompt's 262144 output rows (output_norm_gate)
 
 Usage: python bench.py [--gpus 1] [--steps 128] [--warmup 5] [--no-cpu]
 """
@@ -67,12 +68,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0 = all)")
-    ap.add_argument("--mode", choices=["bench", "prefill", "decode", "decode_tokens", "copy"],
+    ap.add_argument("--mode", choices=["bench", "prefill", "decode", "decode_tokens",
+                                       "output_norm_gate", "copy"],
                     default="bench",
-                    help="prefill/decode: run only that part (for profiling); decode_tokens: "
-                         "only the one-pass multi-token decode, --steps calls after a cache "
-                         "flush each; copy: a plain device copy of known size (counter "
-                         "calibration)")
+                    help="prefill/decode: run only that part (for profiling); decode_tokens / "
+                         "output_norm_gate: only the one-pass multi-token decode / the output "
+                         "norm and gate, --steps calls after a cache flush each; copy: a plain "
+                         "device copy of known size (counter calibration)")
     ap.add_argument("--no-extras", action="store_true",
                     help="only the timed steps and the per-stage calls (the kernel trace "
                          "of exactly what the kernels entry reports)")
@@ -136,13 +138,18 @@ def main():
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
-    if args.mode == "decode_tokens":
+    if args.mode in ("decode_tokens", "output_norm_gate"):
         timed = make_timer(torch, np, stream)
         flush_buf = torch.ones((128 << 20,), dtype=torch.float32, device=dev)
-        res = decode_tokens_measurements(args, {}, torch, np, rda, synth, dev, stream, timed,
-                                         lambda: flush_buf.sum(), reps=args.steps,
-                                         modes=("verify_commit_in_place",))
-        print(json.dumps({"mode": "decode_tokens", **res}), flush=True)
+        flush = lambda: flush_buf.sum()
+        if args.mode == "decode_tokens":
+            res = decode_tokens_measurements(args, {}, torch, np, rda, synth, dev, stream, timed,
+                                             flush, reps=args.steps,
+                                             modes=("verify_commit_in_place",))
+        else:
+            res = epilogue_measurements(args, {}, torch, np, rda, synth, dev, timed, flush,
+                                        16384, 16, reps=args.steps)
+        print(json.dumps({"mode": args.mode, **res}), flush=True)
         return
 
     # ---- inputs (host draw, then resident on the device) --------------------
@@ -412,9 +419,43 @@ def extra_measurements(args, out, torch, np, rda, synth, dev, stream, q, k, v, a
         if cid == 4:
             entry["lengths"] = [int(x) for x in np.diff(cuc)]
     out["other_prefill_workloads"] = configs
+    out["output_norm_gate"] = epilogue_measurements(args, out, torch, np, rda, synth, dev, timed,
+                                                    flush, T, H)
     out["decode_tokens"] = decode_tokens_measurements(args, out, torch, np, rda, synth, dev,
                                                       stream, timed, flush)
     del scratch, flush_buf
+
+
+def epilogue_measurements(args, out, torch, np, rda, synth, dev, timed, flush, T, H, reps=10):
+    """rda_output_norm_gate on the long prompt's output rows (T x H rows of
+    128: fp32 o, bf16 gate, bf16 out, sigmoid gate), timed after a cache
+    flush, with its algorithmic bandwidth, and the prefill plus the
+    epilogue as tokens/s."""
+    rows = T * H
+    x = synth.epilogue_inputs(rows)
+    o = torch.from_numpy(x.o).to(dev)
+    g = torch.from_numpy(x.g).to(torch.bfloat16).to(dev)
+    w = torch.from_numpy(x.weight).to(dev)
+    y = torch.empty((rows, D), dtype=torch.bfloat16, device=dev)
+    sec = timed(lambda: rda.rda_output_norm_gate(o, g, weight=w, out=y), reps, flush)
+    nbytes = rows * (D * 4 + D * 2 + D * 2)
+    res = {"rows": rows, "us_per_call": sec * 1e6, "GBps": nbytes / sec / 1e9,
+           "frac_of_peak": nbytes / sec / 1e9 / PEAK_HBM_GBPS, "bytes_per_call": nbytes,
+           "traffic": read_traffic("rda_output_norm_gate")}
+    if "hbm_practical" in out:
+        res["frac_of_practical"] = res["GBps"] / out["hbm_practical"]["GBps"]
+    if "prefill" in out:
+        tot = out["prefill"]["ms_per_call"] * 1e-3 + sec
+        res["prefill_plus_epilogue_tokens_per_s"] = T / tot
+    if not args.no_cpu:
+        import oracle
+        pick = np.random.default_rng(11).choice(rows, size=2048, replace=False)
+        ref = oracle.output_norm_gate(x.o[pick], x.g[pick], x.weight, 1e-5, "sigmoid")
+        got = y.float().cpu().numpy()[pick].astype(np.float64)
+        res["parity_sampled"] = {"rel_l2": float(np.linalg.norm(got - ref) / np.linalg.norm(ref)),
+                                 "max_rel": float(np.max(np.abs(got - ref) /
+                                                         np.maximum(np.abs(ref), 1e-30)))}
+    return res
 
 
 def decode_tokens_measurements(args, out, torch, np, rda, synth, dev, stream, timed, flush,
@@ -455,7 +496,10 @@ def decode_tokens_measurements(args, out, torch, np, rda, synth, dev, stream, ti
         sec = timed(call, reps, flush)
         S.copy_(S_copy)         # in-place modes advanced the states: restore them
         res[name] = {"us_per_call": sec * 1e6, "GBps": nbytes / sec / 1e9,
-                     "frac_of_peak": nbytes / sec / 1e9 / PEAK_HBM_GBPS}
+                     "frac_of_peak": nbytes / sec / 1e9 / PEAK_HBM_GBPS, "bytes": nbytes}
+    if "verify_commit_in_place" in res:
+        # counted HBM bytes of the one-pass call (profiles/hbm_traffic.txt)
+        res["verify_commit_in_place"]["traffic"] = read_traffic("rda_decode_tokens")
     if "decode" in out:
         res["three_decode_steps_us"] = 3 * out["decode"]["us_per_step"]
     # parity of the one-pass call on 32 sampled (sequence, head) states

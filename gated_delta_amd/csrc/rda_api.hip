@@ -3,6 +3,7 @@
 // is pure host code and runs before anything is enqueued, so every error
 // path returns a status without touching the device.
 #include <climits>
+#include <cmath>
 #include <cstdint>
 
 #include "rda_internal.h"
@@ -157,6 +158,7 @@ const char* rda_status_string(int status) {
         case RDA_ERR_ALIGN: return "pointer not 16-byte aligned";
         case RDA_ERR_HIP: return "HIP launch error";
         case RDA_ERR_ALIAS: return "output buffers overlap other arguments";
+        case RDA_ERR_VALUE: return "scalar argument out of range";
         default: return "unknown status";
     }
 }
@@ -265,6 +267,37 @@ rda_status rda_decode_tokens(const void* q, const void* k, const void* v, rda_dt
     if (tokens == 0 && (!S_out || S_out == S_in)) return RDA_OK;
     if (launch_decode_tokens(q, k, v, qkv_dtype, a, b, batch, tokens, num_heads, S_in, S_out,
                              accept, o, stream) != hipSuccess)
+        return RDA_ERR_HIP;
+    return RDA_OK;
+}
+
+rda_status rda_output_norm_gate(const float* o, const void* g, rda_dtype g_dtype,
+                                const float* weight, float eps, int32_t act, int64_t rows,
+                                int32_t dv, void* out, rda_dtype out_dtype, hipStream_t stream) {
+    if (out_dtype != RDA_BF16 && out_dtype != RDA_FP32) return RDA_ERR_DTYPE;
+    if (act != RDA_GATE_SIGMOID && act != RDA_GATE_SILU && act != RDA_GATE_NONE)
+        return RDA_ERR_VALUE;
+    if (act == RDA_GATE_NONE) g_dtype = RDA_BF16;   // g is not read
+    if (g_dtype != RDA_BF16 && g_dtype != RDA_FP32) return RDA_ERR_DTYPE;
+    if (!(eps >= 0.f) || eps == INFINITY) return RDA_ERR_VALUE;
+    if (rows < 0 || dv <= 0) return RDA_ERR_SHAPE;
+    if (dv != kD) return RDA_ERR_UNSUPPORTED;
+    if (norm_gate_blocks(rows) > INT32_MAX) return RDA_ERR_SHAPE;
+    if (rows == 0) return RDA_OK;
+    if (!o || !out || (act != RDA_GATE_NONE && !g)) return RDA_ERR_NULL;
+    if (act == RDA_GATE_NONE) g = nullptr;
+    for (const void* p : {static_cast<const void*>(o), g, static_cast<const void*>(weight),
+                          static_cast<const void*>(out)})
+        if (p && !aligned16(p)) return RDA_ERR_ALIGN;
+    const size_t n = size_t(rows) * kD;
+    const Range ro = rng(o, n * 4), rg = rng(g, n * (g_dtype == RDA_BF16 ? 2 : 4));
+    const Range rw = rng(weight, weight ? kD * 4 : 0);
+    const Range rout = rng(out, n * (out_dtype == RDA_BF16 ? 2 : 4));
+    const bool in_place = out_dtype == RDA_FP32 && out == static_cast<const void*>(o);
+    if ((!in_place && overlap(rout, ro)) || overlap(rout, rg) || overlap(rout, rw))
+        return RDA_ERR_ALIAS;
+    if (launch_norm_gate(o, g, g_dtype, weight, eps, act, rows, out, out_dtype, stream) !=
+        hipSuccess)
         return RDA_ERR_HIP;
     return RDA_OK;
 }

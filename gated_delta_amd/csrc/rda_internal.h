@@ -74,6 +74,12 @@ hipError_t launch_decode_tokens(const void* q, const void* k, const void* v, rda
                                 int32_t heads, const float* S_in, float* S_out,
                                 const int32_t* accept, float* o, hipStream_t stream);
 
+// Output norm and gate over `rows` rows of 128 channels.
+int64_t norm_gate_blocks(int64_t rows);
+hipError_t launch_norm_gate(const float* o, const void* g, rda_dtype g_dtype, const float* w,
+                            float eps, int32_t act, int64_t rows, void* out, rda_dtype out_dtype,
+                            hipStream_t stream);
+
 hipError_t launch_prep(const void* q, const void* k, rda_dtype dt,
                        const float* a, const float* b, int32_t heads, int32_t max_chunks,
                        const int32_t* rec, const int32_t* num_chunks, unsigned char* factors,

@@ -8,6 +8,8 @@ Writes
       timed steps (kernel trace + stats);
   profiles/kernels_rda_decode_tokens_B256_T3_H16.txt
       the same for the one-pass multi-token decode (bench --mode decode_tokens);
+  profiles/kernels_rda_output_norm_gate_rows262144.txt
+      the same for the output norm and gate (bench --mode output_norm_gate);
   profiles/hbm_traffic.txt
       FETCH_SIZE and WRITE_SIZE per dispatch of every prefill kernel, each
       scaled by what the same counter reads for a device copy of known size,
@@ -30,11 +32,12 @@ from gated_delta_amd.srchash import kernel_source_hash as source_hash  # noqa: E
 # HIP kernel -> the stage name bench.py reports it under
 STAGE = {"chunk_table_kernel": "rda_chunk_table", "prep_bf16_kernel": "rda_prep",
          "walk_bf16_kernel": "rda_walk", "decode_step_kernel": "rda_decode_step",
-         "decode_tokens_kernel": "rda_decode_tokens"}
+         "decode_tokens_kernel": "rda_decode_tokens", "norm_gate_kernel": "rda_output_norm_gate"}
 
 
 def short(name: str) -> str:
     n = name.replace("rda::(anonymous namespace)::", "").replace("void ", "")
+    n = n.replace("rda::", "")
     return n.split("(")[0].split("<")[0].strip()
 
 
@@ -101,6 +104,19 @@ def main():
              "#     -- python bench.py --mode decode_tokens --steps 20 --no-cpu",
              "# then python gated_delta_amd/profile_summary.py OUTDIR"])
 
+    if os.path.isdir(os.path.join(out, "prof_trace_ep")):
+        kernel_table(
+            os.path.join(out, "prof_trace_ep"),
+            os.path.join(prof, "kernels_rda_output_norm_gate_rows262144.txt"),
+            ["# rocprofv3 kernel trace, the output norm and gate: rda_output_norm_gate on the",
+             "# long prompt's 16384 x 16 = 262144 output rows of 128 (fp32 o, bf16 gate, bf16",
+             "# out, sigmoid gate, weight); 20 calls, each after a 512 MiB read (reduce_kernel:",
+             "# the cache flush)",
+             "# command: gated_delta_amd/profile_run.sh OUTDIR, whose third pass is",
+             "#   rocprofv3 --kernel-trace --stats --output-format csv -d OUTDIR/prof_trace_ep -o trace \\",
+             "#     -- python bench.py --mode output_norm_gate --steps 20 --no-cpu",
+             "# then python gated_delta_amd/profile_summary.py OUTDIR"])
+
     # ---- HBM traffic -------------------------------------------------------------
     n = 1 << 30   # bytes the calibration copy reads and writes per launch
     f_copy = counter(os.path.join(out, "prof_FETCH_SIZE_copy"), "FETCH_SIZE")
@@ -111,15 +127,27 @@ def main():
     w_scale = n / (w_copy[wk] * 1024.0)
     fetch = counter(os.path.join(out, "prof_FETCH_SIZE_prefill"), "FETCH_SIZE")
     write = counter(os.path.join(out, "prof_WRITE_SIZE_prefill"), "WRITE_SIZE")
+    # the multi-token decode and the output norm and gate, from passes of
+    # their own (only their own kernel: the flush and restores are not theirs)
+    for mode, kern in (("decode_tokens", "decode_tokens_kernel"),
+                       ("output_norm_gate", "norm_gate_kernel")):
+        fd = os.path.join(out, f"prof_FETCH_SIZE_{mode}")
+        wd = os.path.join(out, f"prof_WRITE_SIZE_{mode}")
+        if os.path.isdir(fd) and os.path.isdir(wd):
+            fm, wm = counter(fd, "FETCH_SIZE"), counter(wd, "WRITE_SIZE")
+            if kern in fm and kern in wm:
+                fetch[kern], write[kern] = fm[kern], wm[kern]
     lines = ["# HBM bytes per launch of the prefill kernels, RDA prefill T=16384 H=16 d=128",
-             "# (bf16 q/k/v).  FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from one",
-             "# rocprofv3 --pmc pass each, scaled by what the same counter reads for a plain",
-             "# device copy of 1 GiB (bench.py --mode copy):",
+             "# (bf16 q/k/v), of the one-pass multi-token decode (B=256 T=3 H=16) and of the",
+             "# output norm and gate (262144 rows).  FETCH_SIZE and WRITE_SIZE (KiB per",
+             "# dispatch) from one rocprofv3 --pmc pass each, scaled by what the same counter",
+             "# reads for a plain device copy of 1 GiB (bench.py --mode copy):",
              f"#   copy FETCH_SIZE = {f_copy[fk]:.0f} KiB -> scale {f_scale:.3f};"
              f" copy WRITE_SIZE = {w_copy[wk]:.0f} KiB -> scale {w_scale:.3f}",
              "# command: gated_delta_amd/profile_run.sh OUTDIR (passes",
              "#   rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE --output-format csv -d OUTDIR/prof_<ctr>_<mode> -o pmc \\",
-             "#     -- python bench.py --mode prefill|copy --steps 2 --warmup 1 --no-cpu)",
+             "#     -- python bench.py --mode prefill|copy|decode_tokens|output_norm_gate \\",
+             "#        --steps 2 --warmup 1 --no-cpu)",
              "# then python gated_delta_amd/profile_summary.py OUTDIR",
              f"source_hash = {source_hash()}",
              f"fetch_scale = {f_scale:.4f}",

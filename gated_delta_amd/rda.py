@@ -24,6 +24,8 @@ RDA_FP32 = 1
 RDA_CHUNK = 64
 RDA_HEAD_DIM = 128
 RDA_DECODE_MAX_TOKENS = 64
+RDA_GATE_SIGMOID, RDA_GATE_SILU, RDA_GATE_NONE = 0, 1, 2
+_GATE_ACTS = {"sigmoid": RDA_GATE_SIGMOID, "silu": RDA_GATE_SILU, "none": RDA_GATE_NONE}
 RDA_STAGE_TABLE, RDA_STAGE_PREP, RDA_STAGE_WALK = 0, 1, 2
 RDA_NUM_STAGES = 3
 STAGES = ("table", "prep", "walk")
@@ -66,6 +68,9 @@ def _load():
         lib.rda_decode_tokens.argtypes = [p, p, p, ctypes.c_int, p, p, i32, i32, i32, i32, i32,
                                           p, p, p, p, p]
         lib.rda_decode_tokens.restype = ctypes.c_int
+        lib.rda_output_norm_gate.argtypes = [p, p, ctypes.c_int, p, ctypes.c_float, i32,
+                                             ctypes.c_int64, i32, p, ctypes.c_int, p]
+        lib.rda_output_norm_gate.restype = ctypes.c_int
         lib.rda_chunk_table.argtypes = [p, i32, i32, p, p, p, p]
         lib.rda_chunk_table.restype = ctypes.c_int
         _lib = lib
@@ -322,3 +327,48 @@ def rda_chunk_table(cu_seqlens, num_seqs: int, total_tokens: int, device="cuda",
     if st != 0:
         raise RdaError(st, "rda_chunk_table")
     return rec[:mc], seq_off, nch
+
+
+def rda_output_norm_gate(o: torch.Tensor, g: Optional[torch.Tensor], *,
+                         weight: Optional[torch.Tensor] = None, eps: float = 1e-5,
+                         act: str = "sigmoid", out: Optional[torch.Tensor] = None,
+                         out_dtype=torch.bfloat16, stream=None) -> torch.Tensor:
+    """Output norm and gate (C entry point ``rda_output_norm_gate``).
+
+    o [..., 128] fp32 (rda_prefill's or a decode entry point's output); g the
+    gate, same shape, bf16 or fp32 (None with act="none"); weight [128] fp32
+    or None; act "sigmoid", "silu" or "none".  Returns out, same shape, in
+    out_dtype (bf16 or fp32; an fp32 out may be o itself).
+    """
+    lib_ = _load()
+    dev = o.device
+    if o.dtype != torch.float32 or o.dim() < 1:
+        raise TypeError("o must be a float32 tensor [..., dv]")
+    shape = tuple(o.shape)
+    dv = shape[-1]
+    rows = o.numel() // dv if dv else 0
+    _need(o, "o", torch.float32, shape, dev)
+    if act not in _GATE_ACTS:
+        raise ValueError(f"act must be one of {sorted(_GATE_ACTS)}")
+    g_dt = RDA_BF16
+    if act != "none":
+        if g is None:
+            raise ValueError("g is required unless act='none'")
+        g_dt = _qkv_dtype(g)
+        _need(g, "g", g.dtype, shape, dev)
+    else:
+        g = None
+    if weight is not None:
+        _need(weight, "weight", torch.float32, (dv,), dev)
+    o_dt = {torch.bfloat16: RDA_BF16, torch.float32: RDA_FP32}.get(out_dtype)
+    if o_dt is None:
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+    if out is None:
+        out = torch.empty(shape, dtype=out_dtype, device=dev)
+    _need(out, "out", out_dtype, shape, dev)
+    st = lib_.rda_output_norm_gate(_ptr(o), _ptr(g), g_dt, _ptr(weight), float(eps),
+                                   _GATE_ACTS[act], rows, dv, _ptr(out), o_dt,
+                                   _stream_handle(stream))
+    if st != 0:
+        raise RdaError(st, "rda_output_norm_gate")
+    return out

@@ -259,4 +259,24 @@ def decode_tokens_inputs(B: int = 256, T: int = 3, H: int = 16, dk: int = 128,
     return DecodeTokensInputs(q, k, v, a, b, accept)
 
 
+@dataclass
+class EpilogueInputs:
+    o: np.ndarray       # [rows, dv] float32, row scales spread over 1e-3 .. 1e2
+    g: np.ndarray       # [rows, dv] float32 (exact bf16 values when bf16)
+    weight: np.ndarray  # [dv] float32, uniform in [0.5, 1.5]
+
+
+def epilogue_inputs(rows: int, dv: int = 128, bf16: bool = True, key=(7,)) -> EpilogueInputs:
+    """Mixer outputs and gates for the output norm and gate: N(0, 1) rows
+    scaled by a log-uniform factor, gate N(0, 2), weight U(0.5, 1.5)."""
+    ro, rs, rg, rw = _children(*key, n=4)
+    scale = np.exp(rs.uniform(np.log(1e-3), np.log(1e2), size=(rows, 1)))
+    o = (ro.standard_normal((rows, dv)) * scale).astype(np.float32)
+    g = (rg.standard_normal((rows, dv)) * 2.0).astype(np.float32)
+    if bf16:
+        g = round_bf16(g)
+    w = rw.uniform(0.5, 1.5, size=dv).astype(np.float32)
+    return EpilogueInputs(o, g, w)
+
+
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4}

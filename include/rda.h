@@ -20,7 +20,8 @@
  * callers L2-normalise them).  rda_prefill evaluates it for whole prompts in
  * chunks of 64 tokens (WY / UT-transform form on bf16 MFMA); rda_decode_step
  * applies one token in place; rda_decode_tokens applies a few (a verify of
- * drafted tokens) in one pass over the state.
+ * drafted tokens) in one pass over the state; rda_output_norm_gate is the
+ * block's output norm and gate on the mixer's output.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -65,7 +66,8 @@ typedef enum {
     RDA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than rda_prefill_workspace_bytes */
     RDA_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned */
     RDA_ERR_HIP = 7,         /* a HIP launch reported an error */
-    RDA_ERR_ALIAS = 8        /* outputs overlap inputs (other than S_final == S0) */
+    RDA_ERR_ALIAS = 8,       /* outputs overlap inputs (other than S_final == S0) */
+    RDA_ERR_VALUE = 9        /* a scalar argument out of range (eps, gate activation) */
 } rda_status;
 
 typedef enum { RDA_BF16 = 0, RDA_FP32 = 1 } rda_dtype;
@@ -185,6 +187,39 @@ rda_status rda_decode_tokens(const void* q, const void* k, const void* v, rda_dt
                              const float* a, const float* b, int32_t batch, int32_t tokens,
                              int32_t num_heads, int32_t dk, int32_t dv, const float* S_in,
                              float* S_out, const int32_t* accept, float* o, hipStream_t stream);
+
+/* Activation of the output gate in rda_output_norm_gate. */
+typedef enum {
+    RDA_GATE_SIGMOID = 0,  /* sigmoid(g) */
+    RDA_GATE_SILU = 1,     /* g * sigmoid(g) */
+    RDA_GATE_NONE = 2      /* no gate: the RMS norm alone */
+} rda_gate_act;
+
+/*
+ * The output epilogue of the RDA block, applied to the mixer's output rows:
+ * per row of one head (dv channels) an RMS normalisation with epsilon and a
+ * per-channel weight, times an activation of the output gate.  The
+ * tiny-random/raon-1-mini model card, section "Printing the model", lists
+ * the block's o_norm (an RMS norm over the head dimension, eps 1e-5, with a
+ * weight of the head dimension's size) and the g_proj projection producing
+ * the gate; the card does not print the gate's activation, hence `act`.
+ *
+ *     out_c = o_c / sqrt(mean_c'(o_c'^2) + eps) * weight_c * act(g_c)
+ *
+ *   o       [rows, dv] fp32: the mixer's output, rows = tokens x heads
+ *           (rda_prefill's o) or batch x heads (the decode entry points')
+ *   g       [rows, dv] in g_dtype (bf16 or fp32); may be NULL with
+ *           RDA_GATE_NONE (then g_dtype is ignored)
+ *   weight  [dv] fp32, shared by the heads; NULL means 1
+ *   eps     finite and >= 0 (RDA_ERR_VALUE otherwise); act an rda_gate_act
+ *   out     [rows, dv] in out_dtype (bf16, rounded to nearest even, or fp32).
+ *           An fp32 out may be o itself (in place); any other overlap with
+ *           an input is RDA_ERR_ALIAS.
+ * rows = 0 is allowed (nothing is launched); dv must be 128.
+ */
+rda_status rda_output_norm_gate(const float* o, const void* g, rda_dtype g_dtype,
+                                const float* weight, float eps, int32_t act, int64_t rows,
+                                int32_t dv, void* out, rda_dtype out_dtype, hipStream_t stream);
 
 /*
  * Test hook: the chunk table rda_prefill builds from cu_seqlens.

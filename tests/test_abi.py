@@ -14,7 +14,7 @@ from gated_delta_amd import rda
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rda.h")
 
-OK, NULL, SHAPE, UNSUP, DTYPE, WS, ALIGN, HIPERR, ALIAS = range(9)
+OK, NULL, SHAPE, UNSUP, DTYPE, WS, ALIGN, HIPERR, ALIAS, VALUE = range(10)
 P = 1 << 40          # fake, well-aligned device addresses: never dereferenced
 GiB = 1 << 30
 
@@ -46,6 +46,7 @@ def test_binding_constants_match_header():
     vals.update({m[0]: int(m[1]) for m in
                  re.findall(r"#define\s+(RDA_[A-Z0-9_]+)\s+(\d+)", text)})
     for name in ("RDA_BF16", "RDA_FP32", "RDA_CHUNK", "RDA_HEAD_DIM", "RDA_DECODE_MAX_TOKENS",
+                 "RDA_GATE_SIGMOID", "RDA_GATE_SILU", "RDA_GATE_NONE",
                  "RDA_STAGE_TABLE",
                  "RDA_STAGE_PREP", "RDA_STAGE_WALK", "RDA_NUM_STAGES"):
         assert getattr(rda, name) == vals[name], name
@@ -58,7 +59,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert rda.rda_abi_version() == 1
-    for s in range(9):
+    for s in range(10):
         assert rda.rda_status_string(s) and rda.rda_status_string(s) != "unknown status"
     assert rda.rda_status_string(99) == "unknown status"
 
@@ -147,6 +148,34 @@ def test_decode_tokens_rejects_bad_arguments(lib):
     assert dec(So=P + 5 * GiB + 1024) == ALIAS   # S_out partly over S_in
     assert dec(acc=P + 6 * GiB + 16) == ALIAS    # accept inside o
     assert dec(So=P + 7 * GiB, acc=P + 7 * GiB + 4096) == ALIAS  # accept inside S_out
+
+
+def test_output_norm_gate_rejects_bad_arguments(lib):
+    import ctypes
+    lib.rda_output_norm_gate.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                         ctypes.c_void_p, ctypes.c_float, ctypes.c_int32,
+                                         ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_int, ctypes.c_void_p]
+
+    def ng(o=P, g=P + GiB, gdt=0, w=P + 2 * GiB, eps=1e-5, act=0, rows=1000, dv=128,
+           out=P + 3 * GiB, odt=0):
+        return lib.rda_output_norm_gate(o, g, gdt, w, eps, act, rows, dv, out, odt, None)
+    assert ng(rows=0) == OK                       # nothing to do
+    assert ng(o=None) == NULL
+    assert ng(g=None) == NULL                     # the gate is read
+    assert ng(odt=5) == DTYPE
+    assert ng(gdt=7) == DTYPE
+    assert ng(act=3) == VALUE
+    assert ng(eps=-1.0) == VALUE
+    assert ng(eps=float("nan")) == VALUE
+    assert ng(eps=float("inf")) == VALUE
+    assert ng(rows=-1) == SHAPE
+    assert ng(dv=64) == UNSUP
+    assert ng(out=P + 3 * GiB + 8) == ALIGN
+    assert ng(out=P + GiB + 4096) == ALIAS        # out inside g
+    assert ng(out=P + 2 * GiB) == ALIAS           # out over the weight
+    assert ng(out=P, odt=0) == ALIAS              # bf16 out over fp32 o
+    assert ng(rows=1 << 40) == SHAPE              # grid beyond int32 blocks
 
 
 def test_chunk_table_rejects_bad_arguments(lib):
