@@ -56,6 +56,10 @@ class Oracle:
         lib.oracle_output_norm_gate.argtypes = [p, p, p, ctypes.c_double, i32,
                                                 ctypes.c_int64, i32, p]
         lib.oracle_output_norm_gate.restype = ctypes.c_int
+        lib.oracle_prologue.argtypes = [p, p, p, p, i32, i32, p, p, p, p, ctypes.c_double,
+                                        ctypes.c_double, p, i32, ctypes.c_int64, i32, i32,
+                                        p, p, p, p, p, p]
+        lib.oracle_prologue.restype = ctypes.c_int
         lib.oracle_threads.argtypes = [i32]
         lib.oracle_threads.restype = ctypes.c_int
         self.lib = lib
@@ -74,6 +78,11 @@ class Oracle:
 
     def output_norm_gate(self, o, g, w, eps: float = 1e-5, act: str = "sigmoid"):
         return _output_norm_gate(self.lib, o, g, w, eps, act)
+
+    def prologue(self, xq, xk, xv, w, beta_raw, delta, g_log, hist_in=None, cu_seqlens=None,
+                 act: str = "silu", floor: float = -5.0, l2_eps: float = 1e-6):
+        return _prologue(self.lib, xq, xk, xv, w, beta_raw, delta, g_log, hist_in, cu_seqlens,
+                         act, floor, l2_eps)
 
 
 def default() -> Oracle:
@@ -120,6 +129,53 @@ def output_norm_gate(o, g, w, eps: float = 1e-5, act: str = "sigmoid"):
 
 
 GATE_ACTS = {"sigmoid": 0, "silu": 1, "none": 2}
+CONV_ACTS = {"none": 0, "silu": 1}
+
+
+def prologue(xq, xk, xv, w, beta_raw, delta, g_log, hist_in=None, cu_seqlens=None,
+             act: str = "silu", floor: float = -5.0, l2_eps: float = 1e-6):
+    """Prologue with the default build (see _prologue)."""
+    return default().prologue(xq, xk, xv, w, beta_raw, delta, g_log, hist_in, cu_seqlens,
+                              act, floor, l2_eps)
+
+
+def _prologue(lib, xq, xk, xv, w, beta_raw, delta, g_log, hist_in=None, cu_seqlens=None,
+              act="silu", floor=-5.0, l2_eps=1e-6):
+    """The steps between the projections and the recurrence (oracle.c,
+    oracle_prologue): causal short convolution with history, activation,
+    q / k L2 norm, the write gate on v, b = sigmoid(beta_raw) and the
+    floored decay.
+
+    xq, xk, xv: raw [T, H, d]; w: [3, H, d, K] (q, k, v; tap K-1 multiplies
+    the current token); beta_raw, g_log: [T, H]; delta: [T, H] or None;
+    hist_in: [N, 3, K-1, H, d] or None (zeros); cu_seqlens: [N+1] or None.
+    Returns (q, k, v [T, H, d], a, b [T, H], hist_out [N, 3, K-1, H, d]),
+    all float64.
+    """
+    xq, xk, xv, beta_raw, g_log = (_f32(x) for x in (xq, xk, xv, beta_raw, g_log))
+    T, H, d = xq.shape
+    w = _f32(w)
+    K = w.shape[-1]
+    assert w.shape == (3, H, d, K)
+    delta = None if delta is None else _f32(delta)
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        N = cu.shape[0] - 1
+    else:
+        cu, N = None, 1
+    if hist_in is not None:
+        hist_in = _f32(hist_in)
+        assert hist_in.shape == (N, 3, K - 1, H, d)
+    q, k, v = (np.zeros((T, H, d)) for _ in range(3))
+    a, b = np.zeros((T, H)), np.zeros((T, H))
+    hist_out = np.zeros((N, 3, K - 1, H, d))
+    rc = lib.oracle_prologue(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(w), K, CONV_ACTS[act],
+                             _ptr(hist_in), _ptr(beta_raw), _ptr(delta), _ptr(g_log),
+                             float(floor), float(l2_eps), _ptr(cu), N, T, H, d, _ptr(q),
+                             _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(hist_out))
+    if rc != 0:
+        raise ValueError(f"oracle_prologue failed with code {rc}")
+    return q, k, v, a, b, hist_out
 
 
 def _output_norm_gate(lib, o, g, w, eps=1e-5, act="sigmoid"):

@@ -224,6 +224,100 @@ int oracle_output_norm_gate(const float* o, const float* g, const float* w, doub
     return 0;
 }
 
+/*
+ * Prologue of the mixer: the steps between the projections and the
+ * recurrence, for packed sequences (cu: int32 [N+1], or NULL for one
+ * sequence of T tokens).  The Raon-1 nano teardown (section "The cache is
+ * small if the runtime keeps it small") keeps a short convolution window per
+ * layer beside the recurrent state; its section "The other 1.5B" gives the
+ * decoupled gates -- erase with beta = sigmoid(beta_raw), a separate write
+ * gate sigmoid(beta_raw + delta) / sigmoid(beta_raw) scaling the value -- and
+ * the decay bounded below by -5 in log space; the Raon-1 mini vLLM article
+ * applies the write gate after the convolution, so the raw history is kept.
+ * Per token t of sequence n and tensor x in (q, k, v), channel c of head h:
+ *
+ *   y = sum_{i<K} w[x][h][c][i] * raw_x(t - (K-1) + i)      (causal conv,
+ *       raw_x of positions before the sequence from the history hist_in)
+ *   y = silu(y) when act = 1 (act = 0: no activation)
+ *   q, k: y / sqrt(sum_c y^2 + l2_eps)     v: y * sig(beta_raw + delta) / sig(beta_raw)
+ *   b = sig(beta_raw),   a = exp(max(g_log, floor))
+ *
+ * Layouts: raw q, k, v [T, H, d] (values exact in fp32); w [3][H][d][K]
+ * (q, k, v; tap K-1 multiplies the current token); hist [N][3][K-1][H][d]
+ * with slot m holding the token m - (K-1) positions before the sequence's
+ * first token (NULL: zeros); beta_raw, delta, g_log [T, H] (delta NULL: 0).
+ * Outputs q, k, v as doubles [T, H, d], a, b [T, H] and hist_out (the raw
+ * tokens at the last K-1 positions of each sequence, from hist_in where the
+ * sequence is shorter), all double.
+ */
+int oracle_prologue(const float* xq, const float* xk, const float* xv, const float* w,
+                    int32_t K, int32_t act, const float* hist_in, const float* beta_raw,
+                    const float* delta, const float* g_log, double floor_log, double l2_eps,
+                    const int32_t* cu, int32_t N, int64_t T, int32_t H, int32_t d,
+                    double* q, double* k, double* v, double* a, double* b, double* hist_out) {
+    if (K < 1 || K > 8 || (act != 0 && act != 1) || N < 1 || T < 0 || H <= 0 || d <= 0)
+        return ORACLE_ERR_ARG;
+    if (!cu && N != 1) return ORACLE_ERR_ARG;
+    const float* raw[3] = {xq, xk, xv};
+    double* out[3] = {q, k, v};
+    const size_t hd = (size_t)H * d;
+    double* y = (double*)malloc((size_t)d * sizeof(double));
+    if (!y) return ORACLE_ERR_NOMEM;
+    for (int32_t n = 0; n < N; ++n) {
+        const int64_t t0 = cu ? cu[n] : 0, t1 = cu ? cu[n + 1] : T;
+        if (t0 < 0 || t1 < t0 || t1 > T) { free(y); return ORACLE_ERR_ARG; }
+        for (int64_t t = t0; t < t1; ++t) {
+            for (int32_t h = 0; h < H; ++h) {
+                const size_t tkh = (size_t)t * H + h;
+                const double br = beta_raw[tkh];
+                const double sig_b = 1.0 / (1.0 + exp(-br));
+                const double dl = delta ? (double)delta[tkh] : 0.0;
+                const double wgate = (1.0 / (1.0 + exp(-(br + dl)))) / sig_b;
+                b[tkh] = sig_b;
+                a[tkh] = exp(fmax((double)g_log[tkh], floor_log));
+                for (int x = 0; x < 3; ++x) {
+                    double ss = 0.0;
+                    for (int32_t c = 0; c < d; ++c) {
+                        double acc = 0.0;
+                        for (int32_t i = 0; i < K; ++i) {
+                            const int64_t pos = t - (K - 1) + i;   /* raw position */
+                            double xr = 0.0;
+                            if (pos >= t0) {
+                                xr = raw[x][(size_t)pos * hd + (size_t)h * d + c];
+                            } else if (hist_in) {
+                                const int64_t m = pos - t0 + (K - 1);   /* history slot */
+                                xr = hist_in[(((size_t)n * 3 + x) * (K - 1) + m) * hd +
+                                             (size_t)h * d + c];
+                            }
+                            acc += (double)w[(((size_t)x * H + h) * d + c) * K + i] * xr;
+                        }
+                        if (act == 1) acc = acc / (1.0 + exp(-acc));
+                        y[c] = acc;
+                        ss += acc * acc;
+                    }
+                    const double scale = x < 2 ? 1.0 / sqrt(ss + l2_eps) : wgate;
+                    for (int32_t c = 0; c < d; ++c) out[x][tkh * d + c] = y[c] * scale;
+                }
+            }
+        }
+        /* the history after the sequence: its last K-1 raw tokens */
+        const int64_t len = t1 - t0;
+        for (int x = 0; x < 3; ++x)
+            for (int32_t m = 0; m < K - 1; ++m)
+                for (size_t e = 0; e < hd; ++e) {
+                    const int64_t pos = t1 - (K - 1) + m;
+                    double val = 0.0;
+                    if (pos >= t0)
+                        val = raw[x][(size_t)pos * hd + e];
+                    else if (hist_in)
+                        val = hist_in[(((size_t)n * 3 + x) * (K - 1) + (m + len)) * hd + e];
+                    hist_out[(((size_t)n * 3 + x) * (K - 1) + m) * hd + e] = val;
+                }
+    }
+    free(y);
+    return 0;
+}
+
 /* Number of OpenMP threads a call with `threads` would use. */
 int oracle_threads(int32_t threads) {
 #ifdef _OPENMP

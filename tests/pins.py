@@ -380,8 +380,100 @@ def pin_norm_gate_closed_forms(orc):
     _close(np.mean(y ** 2, axis=1), ms / (ms + eps), 1e-13, "mean square after the norm")
 
 
+def _prologue_case(rng, T, H, d, K):
+    x = [_f32(rng.standard_normal((T, H, d))) for _ in range(3)]
+    w = _f32(rng.standard_normal((3, H, d, K)) * 0.5)
+    beta = _f32(rng.standard_normal((T, H)))
+    delta = _f32(rng.standard_normal((T, H)))
+    g = _f32(-rng.exponential(2.0, (T, H)))
+    return x, w, beta, delta, g
+
+
+def pin_prologue_library(orc):
+    """With no history the convolution is torch's depthwise conv1d with K-1
+    zeros of left padding; q and k are then torch's L2 normalisation (eps 0),
+    v the convolution itself when the write gate is 1 (delta = 0); SiLU is
+    torch's."""
+    import torch
+    import torch.nn.functional as F
+    T, H, d, K = 9, 2, 6, 4
+    x, w, beta, _, g = _prologue_case(_rng(24), T, H, d, K)
+    for act in ("none", "silu"):
+        q, k, v, _, _, _ = orc.prologue(*x, w, beta, None, g, act=act, l2_eps=0.0)
+        for i, got in enumerate((q, k, v)):
+            xt = torch.from_numpy(x[i].astype(np.float64)).reshape(T, H * d).T[None]   # [1, C, T]
+            wt = torch.from_numpy(w[i].astype(np.float64)).reshape(H * d, 1, K)
+            y = F.conv1d(F.pad(xt, (K - 1, 0)), wt, groups=H * d)[0].T.reshape(T, H, d)
+            if act == "silu":
+                y = F.silu(y)
+            if i < 2:
+                y = F.normalize(y, dim=-1)
+            _close(got, y.numpy(), 1e-13, f"prologue tensor {i} act {act}")
+
+
+def pin_prologue_gates(orc):
+    """b = expit(beta_raw) (scipy); a = exp(max(g_log, floor)); with a
+    one-tap unit convolution and no activation v is scaled by the write gate,
+    which at beta_raw = 0 is 2 sigmoid(delta)."""
+    from scipy.special import expit
+    T, H, d = 6, 3, 4
+    rng = _rng(25)
+    x = [_f32(rng.standard_normal((T, H, d))) for _ in range(3)]
+    w = np.ones((3, H, d, 1), np.float32)
+    beta = _f32(rng.standard_normal((T, H)))
+    beta[0] = 0.0
+    delta = _f32(rng.standard_normal((T, H)))
+    g = _f32(np.array([-10.0, -5.0, -1.0, -0.25, 0.0, -7.5])[:, None].repeat(H, 1))
+    q, k, v, a, b, _ = orc.prologue(*x, w, beta, delta, g, act="none", floor=-5.0)
+    _close(b, expit(_d(beta)), 1e-15, "b = sigmoid(beta_raw)")
+    _close(a, np.exp(np.maximum(_d(g), -5.0)), 1e-15, "floored decay")
+    _close(v[0], _d(x[2][0]) * 2.0 * expit(_d(delta[0]))[:, None], 1e-14, "write gate at beta 0")
+    _close(v, _d(x[2]) * (expit(_d(beta) + _d(delta)) / expit(_d(beta)))[:, :, None], 1e-14,
+           "write gate")
+    _close(q, _d(x[0]) / np.sqrt(np.sum(_d(x[0]) ** 2, axis=-1, keepdims=True) + 1e-6), 1e-14,
+           "q norm")
+    _, _, v0, _, _, _ = orc.prologue(*x, w, beta, None, g, act="none")
+    _close(v0, _d(x[2]), 0, "no delta: v unchanged")
+
+
+def pin_prologue_history(orc):
+    """A sequence run in two calls, the history of the first passed to the
+    second, equals one call; the history out holds the last K-1 raw tokens
+    (from the history in where the sequence is shorter); a packed batch equals
+    separate calls."""
+    T, H, d, K = 11, 2, 5, 4
+    rng = _rng(26)
+    x, w, beta, delta, g = _prologue_case(rng, T, H, d, K)
+    h0 = _f32(rng.standard_normal((1, 3, K - 1, H, d)))
+    full = orc.prologue(*x, w, beta, delta, g, hist_in=h0)
+    for cut in (1, 2, 7):
+        p1 = orc.prologue(*(y[:cut] for y in x), w, beta[:cut], delta[:cut], g[:cut], hist_in=h0)
+        p2 = orc.prologue(*(y[cut:] for y in x), w, beta[cut:], delta[cut:], g[cut:],
+                          hist_in=_f32(p1[5]))
+        for i in range(5):
+            _close(np.concatenate([p1[i], p2[i]]), full[i], 1e-14, f"split at {cut}, output {i}")
+        _close(p2[5], full[5], 0, f"split at {cut}, history")
+    for i in range(3):
+        _close(full[5][0, i], _d(x[i][T - (K - 1):]), 0, f"history of tensor {i}")
+    lens = [4, 1, 0, 6]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    hs = _f32(rng.standard_normal((len(lens), 3, K - 1, H, d)))
+    packed = orc.prologue(*(y[:cu[-1]] for y in x), w, beta[:cu[-1]], delta[:cu[-1]],
+                          g[:cu[-1]], hist_in=hs, cu_seqlens=cu)
+    for n, L in enumerate(lens):
+        t0, t1 = cu[n], cu[n + 1]
+        one = orc.prologue(*(y[t0:t1] for y in x), w, beta[t0:t1], delta[t0:t1], g[t0:t1],
+                           hist_in=hs[n:n + 1])
+        for i in range(5):
+            _close(packed[i][t0:t1], one[i], 0, f"packed seq {n} output {i}")
+        _close(packed[5][n], one[5][0], 0, f"packed seq {n} history")
+    _close(packed[5][2], hs[2], 0, "empty sequence keeps its history")
+    _close(packed[5][1, :, :K - 2], hs[1, :, 1:], 0, "one-token sequence shifts its history")
+
+
 ALL_PINS = [pin_bruteforce, pin_exact_dyadic, pin_hand_example, pin_identity_gates,
             pin_readback, pin_pure_decay, pin_single_step, pin_linearity, pin_rotation,
             pin_permutation, pin_norm_bound, pin_resume, pin_varlen,
             pin_decode_equals_prefill, pin_decode_tokens, pin_norm_gate_library,
-            pin_norm_gate_closed_forms]
+            pin_norm_gate_closed_forms, pin_prologue_library, pin_prologue_gates,
+            pin_prologue_history]

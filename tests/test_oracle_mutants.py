@@ -1,7 +1,7 @@
 """Plant plausible mistakes in copies of the oracle source (CPU only) and
 check that every one of them fails at least one pin.  This shows the pins
-constrain each term, sign, index and operand of the recurrence and of the
-output epilogue."""
+constrain each term, sign, index and operand of the recurrence, of the
+prologue and of the output epilogue."""
 import os
 import shutil
 import subprocess
@@ -53,6 +53,22 @@ MUTANTS = [
     ("weight_ignored", "* (w ? (double)w[c] : 1.0) * gate;", "* gate;"),
     ("gate_of_first_channel", "const double x = (double)g[(size_t)r * dv + c];",
      "const double x = (double)g[(size_t)r * dv];"),
+    ("conv_taps_reversed", "acc += (double)w[(((size_t)x * H + h) * d + c) * K + i] * xr;",
+     "acc += (double)w[(((size_t)x * H + h) * d + c) * K + (K - 1 - i)] * xr;"),
+    ("conv_history_ignored", "} else if (hist_in) {", "} else if (0) {"),
+    ("history_out_not_shifted", "val = hist_in[(((size_t)n * 3 + x) * (K - 1) + (m + len)) * hd + e];",
+     "val = hist_in[(((size_t)n * 3 + x) * (K - 1) + m) * hd + e];"),
+    ("write_gate_inverted", "const double wgate = (1.0 / (1.0 + exp(-(br + dl)))) / sig_b;",
+     "const double wgate = sig_b / (1.0 / (1.0 + exp(-(br + dl))));"),
+    ("decay_floor_missing", "a[tkh] = exp(fmax((double)g_log[tkh], floor_log));",
+     "a[tkh] = exp((double)g_log[tkh]);"),
+    ("beta_without_sigmoid", "b[tkh] = sig_b;", "b[tkh] = br;"),
+    ("l2_norm_without_sqrt", "const double scale = x < 2 ? 1.0 / sqrt(ss + l2_eps) : wgate;",
+     "const double scale = x < 2 ? 1.0 / (ss + l2_eps) : wgate;"),
+    ("value_normalised_too", "const double scale = x < 2 ? 1.0 / sqrt(ss + l2_eps) : wgate;",
+     "const double scale = x < 3 ? 1.0 / sqrt(ss + l2_eps) : wgate;"),
+    ("silu_sign", "if (act == 1) acc = acc / (1.0 + exp(-acc));",
+     "if (act == 1) acc = acc / (1.0 + exp(acc));"),
 ]
 
 
