@@ -20,7 +20,8 @@ Prints ONE JSON line:
   parity     rel-L2 / max-abs of this run's prefill output vs the oracle
 The oracle runs only in this CPU leg (skipped with --no-cpu): the baseline
 timing, and the parity figures of this run's outputs (parity, and the parity
-entries of other_prefill_workloads, output_norm_gate and decode_tokens).
+entries of other_prefill_workloads, prologue, output_norm_gate and
+decode_tokens).
   also       the prefill back to back without the flush (ms_per_call_unflushed)
              and after a read-only 512 MiB flush (ms_per_call_read_flushed),
              the practical HBM rate of an in-place read-modify-write of 256 MiB
@@ -32,7 +33,10 @@ entries of other_prefill_workloads, output_norm_gate and decode_tokens).
              with one token plus two drafts per sequence: one-pass verify +
              commit, read-only verify and commit-only, each with its state
              bandwidth (decode_tokens); the output norm and gate on the long
-             prompt's 262144 output rows (output_norm_gate)
+             prompt's 262144 output rows (output_norm_gate); the prologue on
+             the long prompt and on the decode batch (prologue), and the
+             whole block -- prologue, prefill, output norm and gate -- as
+             tokens/s (output_norm_gate.block_tokens_per_s)
 
 Usage: python bench.py [--gpus 1] [--steps 128] [--warmup 5] [--no-cpu]
 """
@@ -69,12 +73,13 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0 = all)")
     ap.add_argument("--mode", choices=["bench", "prefill", "decode", "decode_tokens",
-                                       "output_norm_gate", "copy"],
+                                       "output_norm_gate", "prologue", "copy"],
                     default="bench",
                     help="prefill/decode: run only that part (for profiling); decode_tokens / "
-                         "output_norm_gate: only the one-pass multi-token decode / the output "
-                         "norm and gate, --steps calls after a cache flush each; copy: a plain "
-                         "device copy of known size (counter calibration)")
+                         "output_norm_gate / prologue: only the one-pass multi-token decode / "
+                         "the output norm and gate / the long prompt's prologue, --steps calls "
+                         "after a cache flush each; copy: a plain device copy of known size "
+                         "(counter calibration)")
     ap.add_argument("--no-extras", action="store_true",
                     help="only the timed steps and the per-stage calls (the kernel trace "
                          "of exactly what the kernels entry reports)")
@@ -138,7 +143,7 @@ def main():
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
-    if args.mode in ("decode_tokens", "output_norm_gate"):
+    if args.mode in ("decode_tokens", "output_norm_gate", "prologue"):
         timed = make_timer(torch, np, stream)
         flush_buf = torch.ones((128 << 20,), dtype=torch.float32, device=dev)
         flush = lambda: flush_buf.sum()
@@ -146,9 +151,12 @@ def main():
             res = decode_tokens_measurements(args, {}, torch, np, rda, synth, dev, stream, timed,
                                              flush, reps=args.steps,
                                              modes=("verify_commit_in_place",))
-        else:
+        elif args.mode == "output_norm_gate":
             res = epilogue_measurements(args, {}, torch, np, rda, synth, dev, timed, flush,
                                         16384, 16, reps=args.steps)
+        else:
+            res = prologue_measurements(args, {}, torch, np, rda, synth, dev, timed, flush,
+                                        16384, 16, reps=args.steps, decode=False)
         print(json.dumps({"mode": args.mode, **res}), flush=True)
         return
 
@@ -419,11 +427,65 @@ def extra_measurements(args, out, torch, np, rda, synth, dev, stream, q, k, v, a
         if cid == 4:
             entry["lengths"] = [int(x) for x in np.diff(cuc)]
     out["other_prefill_workloads"] = configs
+    out["prologue"] = prologue_measurements(args, out, torch, np, rda, synth, dev, timed, flush,
+                                            T, H)
     out["output_norm_gate"] = epilogue_measurements(args, out, torch, np, rda, synth, dev, timed,
                                                     flush, T, H)
     out["decode_tokens"] = decode_tokens_measurements(args, out, torch, np, rda, synth, dev,
                                                       stream, timed, flush)
     del scratch, flush_buf
+
+
+PROLOGUE_K = 4   # conv width: three cached raw tokens per tensor
+
+
+def prologue_measurements(args, out, torch, np, rda, synth, dev, timed, flush, T, H, reps=10,
+                          decode=True):
+    """rda_prologue on the long prompt (T x H token-heads, conv width 4, SiLU,
+    bf16 raw q, k, v in and q, k, v out, fp32 gates) and, with `decode`, on
+    the decode batch (256 sequences x 16 heads, one token, history updated
+    in place), each timed after a cache flush with its algorithmic
+    bandwidth; with the other stages measured, the whole block on the long
+    prompt (prologue, prefill, output norm and gate) as tokens/s."""
+    K = PROLOGUE_K
+    x = synth.prologue_inputs(T, H, K)
+    dv = lambda a: torch.from_numpy(a).to(dev)
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)
+    args_dev = (bf(x.xq), bf(x.xk), bf(x.xv), dv(x.conv_w), dv(x.beta_raw), dv(x.g_log))
+    delta, hin = dv(x.delta), bf(x.hist)
+    hout = torch.empty_like(hin)
+    res_out = []
+
+    def call():
+        res_out[:] = rda.rda_prologue(*args_dev, delta=delta, hist_in=hin, hist_out=hout)
+    sec = timed(call, reps, flush)
+    tok_bytes = 3 * D * 2 * 2 + 3 * 4 + 2 * 4     # raw in + bf16 out, 3 gates in, a and b out
+    hist_bytes = 2 * 3 * (K - 1) * H * D * 2      # one sequence's history in and out
+    nbytes = T * H * tok_bytes + hist_bytes
+    res = {"T": T, "H": H, "conv_width": K, "conv_act": "silu", "us_per_call": sec * 1e6,
+           "GBps": nbytes / sec / 1e9, "frac_of_peak": nbytes / sec / 1e9 / PEAK_HBM_GBPS,
+           "bytes_per_call": nbytes, "traffic": read_traffic("rda_prologue")}
+    if not args.no_cpu:
+        import oracle
+        rows = np.arange(0, T, max(T // 512, 1))    # every 32nd token's full row
+        ref = oracle.prologue(x.xq, x.xk, x.xv, x.conv_w, x.beta_raw, x.delta, x.g_log,
+                              hist_in=x.hist)
+        got = [t.float().cpu().numpy()[rows].astype(np.float64) for t in res_out[:3]]
+        rel = [float(np.linalg.norm(g - r[rows]) / np.linalg.norm(r[rows]))
+               for g, r in zip(got, ref[:3])]
+        res["parity_sampled"] = {"q_rel_l2": rel[0], "k_rel_l2": rel[1], "v_rel_l2": rel[2]}
+    if decode:
+        B = 256
+        xd = synth.prologue_inputs(B, H, K, N=B, key=(9,))
+        dargs = tuple(f(a) for f, a in ((bf, xd.xq), (bf, xd.xk), (bf, xd.xv), (dv, xd.conv_w),
+                                        (dv, xd.beta_raw), (dv, xd.g_log)))
+        ddelta, dh = dv(xd.delta), bf(xd.hist)
+        dsec = timed(lambda: rda.rda_prologue(*dargs, delta=ddelta, hist_in=dh, hist_out=dh,
+                                              num_seqs=B), reps, flush)
+        dbytes = B * H * tok_bytes + B * hist_bytes
+        res["decode"] = {"B": B, "us_per_call": dsec * 1e6, "GBps": dbytes / dsec / 1e9,
+                         "bytes_per_call": dbytes}
+    return res
 
 
 def epilogue_measurements(args, out, torch, np, rda, synth, dev, timed, flush, T, H, reps=10):
@@ -447,6 +509,9 @@ def epilogue_measurements(args, out, torch, np, rda, synth, dev, timed, flush, T
     if "prefill" in out:
         tot = out["prefill"]["ms_per_call"] * 1e-3 + sec
         res["prefill_plus_epilogue_tokens_per_s"] = T / tot
+        if "prologue" in out:
+            tot += out["prologue"]["us_per_call"] * 1e-6
+            res["block_tokens_per_s"] = T / tot     # prologue + prefill + norm and gate
     if not args.no_cpu:
         import oracle
         pick = np.random.default_rng(11).choice(rows, size=2048, replace=False)

@@ -271,6 +271,88 @@ rda_status rda_decode_tokens(const void* q, const void* k, const void* v, rda_dt
     return RDA_OK;
 }
 
+rda_status rda_prologue(const void* x_q, const void* x_k, const void* x_v, rda_dtype x_dtype,
+                        const float* conv_w, int32_t conv_width, int32_t conv_act,
+                        const void* hist_in, void* hist_out, const float* beta_raw,
+                        const float* delta, const float* g_log, float decay_floor, float l2_eps,
+                        const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                        int32_t num_heads, int32_t d, void* q, void* k, void* v, float* a,
+                        float* b, hipStream_t stream) {
+    if (x_dtype != RDA_BF16 && x_dtype != RDA_FP32) return RDA_ERR_DTYPE;
+    if (x_dtype != RDA_BF16) return RDA_ERR_UNSUPPORTED;
+    if (conv_width < 1 || conv_width > RDA_CONV_MAX_WIDTH) return RDA_ERR_VALUE;
+    if (conv_act != RDA_CONV_ACT_NONE && conv_act != RDA_CONV_ACT_SILU) return RDA_ERR_VALUE;
+    if (std::isnan(decay_floor) || decay_floor == INFINITY) return RDA_ERR_VALUE;
+    if (!(l2_eps >= 0.f) || l2_eps == INFINITY) return RDA_ERR_VALUE;
+    if (total_tokens < 0 || num_seqs < 1) return RDA_ERR_SHAPE;
+    rda_status st = check_dims(num_heads, d, d);
+    if (st != RDA_OK) return st;
+    if ((num_heads + 15) / 16 > 65535) return RDA_ERR_SHAPE;   // grid y: 16 heads per block
+    if (!cu_seqlens && total_tokens % num_seqs != 0) return RDA_ERR_SHAPE;
+    const int32_t K = conv_width;
+    const size_t hd = size_t(num_heads) * kD;
+    const size_t th = size_t(total_tokens) * num_heads;
+    const size_t hist_bytes = size_t(num_seqs) * 3 * (K - 1) * hd * 2;
+    const bool need_hist_out = hist_out && K > 1;
+    if (total_tokens == 0 && !need_hist_out) return RDA_OK;
+    if (total_tokens > 0 &&
+        (!x_q || !x_k || !x_v || !conv_w || !beta_raw || !g_log || !q || !k || !v || !a || !b))
+        return RDA_ERR_NULL;
+    for (const void* p : {x_q, x_k, x_v, static_cast<const void*>(conv_w), hist_in,
+                          static_cast<const void*>(hist_out),
+                          static_cast<const void*>(beta_raw), static_cast<const void*>(delta),
+                          static_cast<const void*>(g_log), static_cast<const void*>(q),
+                          static_cast<const void*>(k), static_cast<const void*>(v),
+                          static_cast<const void*>(a), static_cast<const void*>(b)})
+        if (p && !aligned16(p)) return RDA_ERR_ALIGN;
+    if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return RDA_ERR_ALIGN;
+    const Range rxq = rng(x_q, th * kD * 2), rxk = rng(x_k, th * kD * 2), rxv = rng(x_v, th * kD * 2);
+    const Range rw = rng(conv_w, size_t(3) * hd * K * 4);
+    const Range rhi = rng(hist_in, hist_in ? hist_bytes : 0);
+    const Range rho = rng(need_hist_out ? hist_out : nullptr, hist_bytes);
+    const Range rbr = rng(beta_raw, th * 4), rdl = rng(delta, delta ? th * 4 : 0);
+    const Range rg = rng(g_log, th * 4);
+    const Range rcu = rng(cu_seqlens, cu_seqlens ? size_t(num_seqs + 1) * 4 : 0);
+    const Range rq = rng(q, th * kD * 2), rk = rng(k, th * kD * 2), rv = rng(v, th * kD * 2);
+    const Range ra = rng(a, th * 4), rb = rng(b, th * 4);
+    const Range ins[] = {rxq, rxk, rxv, rw, rhi, rbr, rdl, rg, rcu};
+    const Range outs[] = {rq, rk, rv, ra, rb, rho};
+    for (int i = 0; i < 6; ++i) {
+        for (Range in : ins) {
+            // the history may be updated in place when every sequence has one token
+            const bool hist_pair = i == 5 && in.lo == rhi.lo && in.hi == rhi.hi && rhi.lo != 0;
+            if (hist_pair && !cu_seqlens && total_tokens == num_seqs) continue;
+            if (overlap(outs[i], in)) return RDA_ERR_ALIAS;
+        }
+        for (int j = 0; j < i; ++j)
+            if (overlap(outs[i], outs[j])) return RDA_ERR_ALIAS;
+    }
+    PrologueArgs P;
+    P.x[0] = static_cast<const uint16_t*>(x_q);
+    P.x[1] = static_cast<const uint16_t*>(x_k);
+    P.x[2] = static_cast<const uint16_t*>(x_v);
+    P.w = conv_w;
+    P.hin = static_cast<const uint16_t*>(hist_in);
+    P.hout = need_hist_out ? static_cast<uint16_t*>(hist_out) : nullptr;
+    P.beta = beta_raw;
+    P.delta = delta;
+    P.glog = g_log;
+    P.floor_log = decay_floor;
+    P.l2eps = l2_eps;
+    P.cu = cu_seqlens;
+    P.N = num_seqs;
+    P.T = total_tokens;
+    P.H = num_heads;
+    P.L = cu_seqlens ? 0 : total_tokens / num_seqs;
+    P.out[0] = static_cast<uint16_t*>(q);
+    P.out[1] = static_cast<uint16_t*>(k);
+    P.out[2] = static_cast<uint16_t*>(v);
+    P.a = a;
+    P.b = b;
+    if (launch_prologue(P, K, conv_act, stream) != hipSuccess) return RDA_ERR_HIP;
+    return RDA_OK;
+}
+
 rda_status rda_output_norm_gate(const float* o, const void* g, rda_dtype g_dtype,
                                 const float* weight, float eps, int32_t act, int64_t rows,
                                 int32_t dv, void* out, rda_dtype out_dtype, hipStream_t stream) {

@@ -63,7 +63,8 @@ __device__ __forceinline__ void store_out<float>(float* p, const float y[4]) {
 template <int kAct>
 __device__ __forceinline__ float gate_act(float x) {
     if (kAct == RDA_GATE_NONE) return 1.f;
-    const float sig = __builtin_amdgcn_rcpf(1.f + __expf(-x));
+    // sigmoid on the hardware's exp2 (one instruction, about 1 ulp)
+    const float sig = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x * -1.44269504088896341f));
     return kAct == RDA_GATE_SIGMOID ? sig : x * sig;
 }
 

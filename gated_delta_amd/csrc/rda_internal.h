@@ -74,6 +74,26 @@ hipError_t launch_decode_tokens(const void* q, const void* k, const void* v, rda
                                 int32_t heads, const float* S_in, float* S_out,
                                 const int32_t* accept, float* o, hipStream_t stream);
 
+// Prologue: raw q, k, v (bf16) -> conv, activation, q/k norm, write gate;
+// a, b from the gates; the conv history.  cu == nullptr: N sequences of L
+// tokens each.
+struct PrologueArgs {
+    const uint16_t* x[3];      // raw q, k, v [T, H, 128]
+    const float* w;            // [3][H][128][K]
+    const uint16_t* hin;       // [N][3][K-1][H][128] or nullptr (zeros)
+    uint16_t* hout;            // same shape or nullptr
+    const float* beta;         // [T, H]
+    const float* delta;        // [T, H] or nullptr
+    const float* glog;         // [T, H]
+    float floor_log, l2eps;
+    const int32_t* cu;         // [N+1] or nullptr
+    int32_t N, T, H, L;
+    uint16_t* out[3];          // q, k, v [T, H, 128] bf16
+    float* a;                  // [T, H]
+    float* b;
+};
+hipError_t launch_prologue(const PrologueArgs& P, int32_t K, int32_t act, hipStream_t stream);
+
 // Output norm and gate over `rows` rows of 128 channels.
 int64_t norm_gate_blocks(int64_t rows);
 hipError_t launch_norm_gate(const float* o, const void* g, rda_dtype g_dtype, const float* w,

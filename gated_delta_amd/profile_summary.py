@@ -10,6 +10,8 @@ Writes
       the same for the one-pass multi-token decode (bench --mode decode_tokens);
   profiles/kernels_rda_output_norm_gate_rows262144.txt
       the same for the output norm and gate (bench --mode output_norm_gate);
+  profiles/kernels_rda_prologue_T16384_H16.txt
+      the same for the prologue (bench --mode prologue);
   profiles/hbm_traffic.txt
       FETCH_SIZE and WRITE_SIZE per dispatch of every prefill kernel, each
       scaled by what the same counter reads for a device copy of known size,
@@ -32,7 +34,8 @@ from gated_delta_amd.srchash import kernel_source_hash as source_hash  # noqa: E
 # HIP kernel -> the stage name bench.py reports it under
 STAGE = {"chunk_table_kernel": "rda_chunk_table", "prep_bf16_kernel": "rda_prep",
          "walk_bf16_kernel": "rda_walk", "decode_step_kernel": "rda_decode_step",
-         "decode_tokens_kernel": "rda_decode_tokens", "norm_gate_kernel": "rda_output_norm_gate"}
+         "decode_tokens_kernel": "rda_decode_tokens", "norm_gate_kernel": "rda_output_norm_gate",
+         "prologue_kernel": "rda_prologue"}
 
 
 def short(name: str) -> str:
@@ -117,6 +120,19 @@ def main():
              "#     -- python bench.py --mode output_norm_gate --steps 20 --no-cpu",
              "# then python gated_delta_amd/profile_summary.py OUTDIR"])
 
+    if os.path.isdir(os.path.join(out, "prof_trace_pro")):
+        kernel_table(
+            os.path.join(out, "prof_trace_pro"),
+            os.path.join(prof, "kernels_rda_prologue_T16384_H16.txt"),
+            ["# rocprofv3 kernel trace, the prologue: rda_prologue on the long prompt, 16384",
+             "# tokens x 16 heads (bf16 raw q, k, v; conv width 4 with a history; SiLU; q/k",
+             "# norm; write gate; b and the floored decay); 20 calls, each after a 512 MiB",
+             "# read (reduce_kernel: the cache flush)",
+             "# command: gated_delta_amd/profile_run.sh OUTDIR, whose fourth pass is",
+             "#   rocprofv3 --kernel-trace --stats --output-format csv -d OUTDIR/prof_trace_pro -o trace \\",
+             "#     -- python bench.py --mode prologue --steps 20 --no-cpu",
+             "# then python gated_delta_amd/profile_summary.py OUTDIR"])
+
     # ---- HBM traffic -------------------------------------------------------------
     n = 1 << 30   # bytes the calibration copy reads and writes per launch
     f_copy = counter(os.path.join(out, "prof_FETCH_SIZE_copy"), "FETCH_SIZE")
@@ -130,7 +146,7 @@ def main():
     # the multi-token decode and the output norm and gate, from passes of
     # their own (only their own kernel: the flush and restores are not theirs)
     for mode, kern in (("decode_tokens", "decode_tokens_kernel"),
-                       ("output_norm_gate", "norm_gate_kernel")):
+                       ("output_norm_gate", "norm_gate_kernel"), ("prologue", "prologue_kernel")):
         fd = os.path.join(out, f"prof_FETCH_SIZE_{mode}")
         wd = os.path.join(out, f"prof_WRITE_SIZE_{mode}")
         if os.path.isdir(fd) and os.path.isdir(wd):
@@ -138,15 +154,16 @@ def main():
             if kern in fm and kern in wm:
                 fetch[kern], write[kern] = fm[kern], wm[kern]
     lines = ["# HBM bytes per launch of the prefill kernels, RDA prefill T=16384 H=16 d=128",
-             "# (bf16 q/k/v), of the one-pass multi-token decode (B=256 T=3 H=16) and of the",
-             "# output norm and gate (262144 rows).  FETCH_SIZE and WRITE_SIZE (KiB per",
+             "# (bf16 q/k/v), of the one-pass multi-token decode (B=256 T=3 H=16), of the",
+             "# output norm and gate (262144 rows) and of the prologue (T=16384 H=16, conv",
+             "# width 4).  FETCH_SIZE and WRITE_SIZE (KiB per",
              "# dispatch) from one rocprofv3 --pmc pass each, scaled by what the same counter",
              "# reads for a plain device copy of 1 GiB (bench.py --mode copy):",
              f"#   copy FETCH_SIZE = {f_copy[fk]:.0f} KiB -> scale {f_scale:.3f};"
              f" copy WRITE_SIZE = {w_copy[wk]:.0f} KiB -> scale {w_scale:.3f}",
              "# command: gated_delta_amd/profile_run.sh OUTDIR (passes",
              "#   rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE --output-format csv -d OUTDIR/prof_<ctr>_<mode> -o pmc \\",
-             "#     -- python bench.py --mode prefill|copy|decode_tokens|output_norm_gate \\",
+             "#     -- python bench.py --mode prefill|copy|decode_tokens|output_norm_gate|prologue \\",
              "#        --steps 2 --warmup 1 --no-cpu)",
              "# then python gated_delta_amd/profile_summary.py OUTDIR",
              f"source_hash = {source_hash()}",

@@ -25,6 +25,9 @@ RDA_CHUNK = 64
 RDA_HEAD_DIM = 128
 RDA_DECODE_MAX_TOKENS = 64
 RDA_GATE_SIGMOID, RDA_GATE_SILU, RDA_GATE_NONE = 0, 1, 2
+RDA_CONV_MAX_WIDTH = 4
+RDA_CONV_ACT_NONE, RDA_CONV_ACT_SILU = 0, 1
+_CONV_ACTS = {"none": RDA_CONV_ACT_NONE, "silu": RDA_CONV_ACT_SILU}
 _GATE_ACTS = {"sigmoid": RDA_GATE_SIGMOID, "silu": RDA_GATE_SILU, "none": RDA_GATE_NONE}
 RDA_STAGE_TABLE, RDA_STAGE_PREP, RDA_STAGE_WALK = 0, 1, 2
 RDA_NUM_STAGES = 3
@@ -71,6 +74,10 @@ def _load():
         lib.rda_output_norm_gate.argtypes = [p, p, ctypes.c_int, p, ctypes.c_float, i32,
                                              ctypes.c_int64, i32, p, ctypes.c_int, p]
         lib.rda_output_norm_gate.restype = ctypes.c_int
+        lib.rda_prologue.argtypes = [p, p, p, ctypes.c_int, p, i32, i32, p, p, p, p, p,
+                                     ctypes.c_float, ctypes.c_float, p, i32, i32, i32, i32,
+                                     p, p, p, p, p, p]
+        lib.rda_prologue.restype = ctypes.c_int
         lib.rda_chunk_table.argtypes = [p, i32, i32, p, p, p, p]
         lib.rda_chunk_table.restype = ctypes.c_int
         _lib = lib
@@ -372,3 +379,62 @@ def rda_output_norm_gate(o: torch.Tensor, g: Optional[torch.Tensor], *,
     if st != 0:
         raise RdaError(st, "rda_output_norm_gate")
     return out
+
+
+def rda_prologue(x_q: torch.Tensor, x_k: torch.Tensor, x_v: torch.Tensor,
+                 conv_w: torch.Tensor, beta_raw: torch.Tensor, g_log: torch.Tensor, *,
+                 delta: Optional[torch.Tensor] = None, hist_in: Optional[torch.Tensor] = None,
+                 hist_out: Optional[torch.Tensor] = None, cu_seqlens=None, num_seqs: int = 1,
+                 conv_act: str = "silu", decay_floor: float = -5.0, l2_eps: float = 1e-6,
+                 stream=None):
+    """The block's prologue (C entry point ``rda_prologue``).
+
+    x_q, x_k, x_v [..., H, 128] bf16 raw projections (the leading axes are
+    the tokens: [T], or [B] / [B, T] for the decode layouts); conv_w
+    [3, H, 128, K] fp32; beta_raw, g_log (and delta) [..., H] fp32; hist_in /
+    hist_out [N, 3, K-1, H, 128] bf16 (hist_out may be hist_in when every
+    sequence has one token).  cu_seqlens: offsets (host array or tensor,
+    checked on the host), or None for num_seqs equal-length sequences.
+    Returns q, k, v (bf16, shaped like x_q) and a, b (fp32, shaped like
+    beta_raw).
+    """
+    lib_ = _load()
+    dev = x_q.device
+    if x_q.dtype != torch.bfloat16:
+        raise TypeError("x_q, x_k, x_v must be bfloat16")
+    shape = tuple(x_q.shape)
+    if len(shape) < 2:
+        raise ValueError("x_q must be [..., H, d]")
+    H, d = shape[-2], shape[-1]
+    lead = shape[:-2]
+    T = int(np.prod(lead)) if lead else 1
+    for name, t in (("x_q", x_q), ("x_k", x_k), ("x_v", x_v)):
+        _need(t, name, torch.bfloat16, shape, dev)
+    if conv_w.dim() != 4:
+        raise ValueError("conv_w must be [3, H, d, K]")
+    K = conv_w.shape[-1]
+    _need(conv_w, "conv_w", torch.float32, (3, H, d, K), dev)
+    for name, t in (("beta_raw", beta_raw), ("g_log", g_log), ("delta", delta)):
+        if t is not None:
+            _need(t, name, torch.float32, lead + (H,), dev)
+    cu_dev = None
+    if cu_seqlens is not None:
+        cu_np = check_cu_seqlens(cu_seqlens, T)
+        num_seqs = len(cu_np) - 1
+        cu_dev = torch.from_numpy(cu_np).to(dev)
+    hshape = (num_seqs, 3, max(K - 1, 0), H, d)
+    for name, t in (("hist_in", hist_in), ("hist_out", hist_out)):
+        if t is not None:
+            _need(t, name, torch.bfloat16, hshape, dev)
+    if conv_act not in _CONV_ACTS:
+        raise ValueError(f"conv_act must be one of {sorted(_CONV_ACTS)}")
+    q, k, v = (torch.empty(shape, dtype=torch.bfloat16, device=dev) for _ in range(3))
+    a, b = (torch.empty(lead + (H,), dtype=torch.float32, device=dev) for _ in range(2))
+    st = lib_.rda_prologue(_ptr(x_q), _ptr(x_k), _ptr(x_v), RDA_BF16, _ptr(conv_w), K,
+                           _CONV_ACTS[conv_act], _ptr(hist_in), _ptr(hist_out), _ptr(beta_raw),
+                           _ptr(delta), _ptr(g_log), float(decay_floor), float(l2_eps),
+                           _ptr(cu_dev), int(num_seqs), T, H, d, _ptr(q), _ptr(k), _ptr(v),
+                           _ptr(a), _ptr(b), _stream_handle(stream))
+    if st != 0:
+        raise RdaError(st, "rda_prologue")
+    return q, k, v, a, b

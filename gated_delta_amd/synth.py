@@ -279,4 +279,31 @@ def epilogue_inputs(rows: int, dv: int = 128, bf16: bool = True, key=(7,)) -> Ep
     return EpilogueInputs(o, g, w)
 
 
+@dataclass
+class PrologueInputs:
+    xq: np.ndarray        # raw projections [T, H, d] float32 (exact bf16 values)
+    xk: np.ndarray
+    xv: np.ndarray
+    conv_w: np.ndarray    # [3, H, d, K] float32
+    beta_raw: np.ndarray  # [T, H]
+    delta: np.ndarray     # [T, H]
+    g_log: np.ndarray     # [T, H], some below the -5 floor
+    hist: np.ndarray      # [N, 3, K-1, H, d] float32 (exact bf16 values)
+
+
+def prologue_inputs(T: int, H: int = 16, K: int = 4, N: int = 1, d: int = 128,
+                    key=(8,)) -> PrologueInputs:
+    """Raw projections and gates for the prologue: q, k, v N(0, 1) in bf16,
+    conv weights N(0, 0.5^2), beta_raw and delta N(0, 1), log decay
+    -Exp(mean 1.5) (about 4 % below -5), a bf16 N(0, 1) history."""
+    r = _children(*key, n=8)
+    xq, xk, xv = (round_bf16(r[i].standard_normal((T, H, d)).astype(np.float32)) for i in range(3))
+    conv_w = (r[3].standard_normal((3, H, d, K)) * 0.5).astype(np.float32)
+    beta_raw = r[4].standard_normal((T, H)).astype(np.float32)
+    delta = r[5].standard_normal((T, H)).astype(np.float32)
+    g_log = (-r[6].exponential(1.5, (T, H))).astype(np.float32)
+    hist = round_bf16(r[7].standard_normal((N, 3, max(K - 1, 0), H, d)).astype(np.float32))
+    return PrologueInputs(xq, xk, xv, conv_w, beta_raw, delta, g_log, hist)
+
+
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4}

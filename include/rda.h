@@ -20,8 +20,10 @@
  * callers L2-normalise them).  rda_prefill evaluates it for whole prompts in
  * chunks of 64 tokens (WY / UT-transform form on bf16 MFMA); rda_decode_step
  * applies one token in place; rda_decode_tokens applies a few (a verify of
- * drafted tokens) in one pass over the state; rda_output_norm_gate is the
- * block's output norm and gate on the mixer's output.
+ * drafted tokens) in one pass over the state; rda_prologue produces their
+ * inputs from the raw projections (short convolution, q/k norm, gates), and
+ * rda_output_norm_gate is the block's output norm and gate on the mixer's
+ * output.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -56,6 +58,7 @@ extern "C" {
 #define RDA_CHUNK 64      /* tokens per prefill chunk */
 #define RDA_HEAD_DIM 128  /* the only supported dk = dv */
 #define RDA_DECODE_MAX_TOKENS 64  /* tokens per rda_decode_tokens call (one chunk) */
+#define RDA_CONV_MAX_WIDTH 4      /* taps of the prologue's short convolution */
 
 typedef enum {
     RDA_OK = 0,
@@ -187,6 +190,66 @@ rda_status rda_decode_tokens(const void* q, const void* k, const void* v, rda_dt
                              const float* a, const float* b, int32_t batch, int32_t tokens,
                              int32_t num_heads, int32_t dk, int32_t dv, const float* S_in,
                              float* S_out, const int32_t* accept, float* o, hipStream_t stream);
+
+/* Activation after the prologue's short convolution. */
+typedef enum {
+    RDA_CONV_ACT_NONE = 0,
+    RDA_CONV_ACT_SILU = 1  /* y * sigmoid(y) */
+} rda_conv_act;
+
+/*
+ * The prologue of the RDA block: the steps between its projections and the
+ * recurrence, producing the inputs of rda_prefill / the decode entry points.
+ * The Raon-1 nano teardown keeps a short convolution window per layer beside
+ * the recurrent state (section "The cache is small if the runtime keeps it
+ * small") and gives the decoupled gates -- erase strength b =
+ * sigmoid(beta_raw), a write gate sigmoid(beta_raw + delta) / sigmoid(beta_raw)
+ * scaling the value -- and the decay bounded below by -5 in log space
+ * (section "The other 1.5B: a hybrid built to forget"); the Raon-1 mini vLLM
+ * article applies the write gate after the convolution, so the history holds
+ * raw tokens, and keeps that history in bf16.  Per token t of sequence n,
+ * tensor x in (q, k, v), head h, channel c:
+ *
+ *   y   = sum_{i<K} w[x][h][c][i] * raw_x[t - (K-1) + i]   (raw tokens before
+ *         the sequence's first token come from its history)
+ *   y   = silu(y) with RDA_CONV_ACT_SILU
+ *   q,k = y / sqrt(sum_c y^2 + l2_eps);   v = y * sig(beta_raw + delta) / sig(beta_raw)
+ *   b   = sig(beta_raw);   a = exp(max(g_log, decay_floor))
+ *
+ *   x_q, x_k, x_v  raw projections [total_tokens, H, d] bf16 (x_dtype must be
+ *                  RDA_BF16)
+ *   conv_w         [3, H, d, K] fp32: the q, k and v depthwise weights, tap
+ *                  K-1 multiplying the current token; K = conv_width in
+ *                  1..RDA_CONV_MAX_WIDTH
+ *   hist_in        [num_seqs, 3, K-1, H, d] bf16: the K-1 raw tokens before
+ *                  each sequence, oldest first (q, k, v), or NULL for zeros
+ *   hist_out       same shape, or NULL to skip: the raw tokens at each
+ *                  sequence's last K-1 positions (the newest of hist_in where
+ *                  a sequence is shorter; hist_in itself for an empty one).
+ *                  It may be hist_in itself only when every sequence has one
+ *                  token (cu_seqlens NULL and total_tokens = num_seqs);
+ *                  otherwise any overlap is RDA_ERR_ALIAS
+ *   beta_raw, g_log  [total_tokens, H] fp32; delta [total_tokens, H] fp32 or
+ *                  NULL (write gate 1)
+ *   decay_floor    log-space floor of the decay (-5 per the teardown; -INF
+ *                  for none; NaN is RDA_ERR_VALUE); l2_eps >= 0 and finite
+ *   cu_seqlens     device int32 [num_seqs + 1] offsets (trusted as in
+ *                  rda_prefill, never read or used out of bounds), or NULL
+ *                  for num_seqs sequences of total_tokens / num_seqs tokens
+ *                  each (the layouts of rda_decode_step, one token, and
+ *                  rda_decode_tokens); total_tokens must then divide evenly
+ *   q, k, v        outputs [total_tokens, H, d] bf16 (round to nearest even),
+ *                  the inputs of rda_prefill / rda_decode_*; a, b outputs
+ *                  [total_tokens, H] fp32
+ * d must be 128.  total_tokens = 0 is allowed (only hist_out is written).
+ */
+rda_status rda_prologue(const void* x_q, const void* x_k, const void* x_v, rda_dtype x_dtype,
+                        const float* conv_w, int32_t conv_width, int32_t conv_act,
+                        const void* hist_in, void* hist_out, const float* beta_raw,
+                        const float* delta, const float* g_log, float decay_floor, float l2_eps,
+                        const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                        int32_t num_heads, int32_t d, void* q, void* k, void* v, float* a,
+                        float* b, hipStream_t stream);
 
 /* Activation of the output gate in rda_output_norm_gate. */
 typedef enum {

@@ -46,7 +46,8 @@ def test_binding_constants_match_header():
     vals.update({m[0]: int(m[1]) for m in
                  re.findall(r"#define\s+(RDA_[A-Z0-9_]+)\s+(\d+)", text)})
     for name in ("RDA_BF16", "RDA_FP32", "RDA_CHUNK", "RDA_HEAD_DIM", "RDA_DECODE_MAX_TOKENS",
-                 "RDA_GATE_SIGMOID", "RDA_GATE_SILU", "RDA_GATE_NONE",
+                 "RDA_GATE_SIGMOID", "RDA_GATE_SILU", "RDA_GATE_NONE", "RDA_CONV_MAX_WIDTH",
+                 "RDA_CONV_ACT_NONE", "RDA_CONV_ACT_SILU",
                  "RDA_STAGE_TABLE",
                  "RDA_STAGE_PREP", "RDA_STAGE_WALK", "RDA_NUM_STAGES"):
         assert getattr(rda, name) == vals[name], name
@@ -176,6 +177,44 @@ def test_output_norm_gate_rejects_bad_arguments(lib):
     assert ng(out=P + 2 * GiB) == ALIAS           # out over the weight
     assert ng(out=P, odt=0) == ALIAS              # bf16 out over fp32 o
     assert ng(rows=1 << 40) == SHAPE              # grid beyond int32 blocks
+
+
+def test_prologue_rejects_bad_arguments(lib):
+    rda.lib()     # the binding sets the argument types
+    T, H = 100, 2
+    tok = T * H * 128 * 2          # bytes of one bf16 token tensor
+
+    def pro(xq=P, xk=P + GiB, xv=P + 2 * GiB, xdt=0, w=P + 3 * GiB, K=4, act=1,
+            hin=P + 4 * GiB, hout=P + 5 * GiB, beta=P + 6 * GiB, delta=P + 7 * GiB,
+            g=P + 8 * GiB, floor=-5.0, eps=1e-6, cu=None, N=4, T=T, H=H, d=128,
+            q=P + 9 * GiB, k=P + 10 * GiB, v=P + 11 * GiB, a=P + 12 * GiB, b=P + 13 * GiB):
+        return lib.rda_prologue(xq, xk, xv, xdt, w, K, act, hin, hout, beta, delta, g, floor,
+                                eps, cu, N, T, H, d, q, k, v, a, b, None)
+    assert pro(T=0, hout=None) == OK             # nothing to write
+    assert pro(xdt=1) == UNSUP                   # raw projections in bf16 only
+    assert pro(xdt=4) == DTYPE
+    assert pro(K=0) == VALUE
+    assert pro(K=5) == VALUE
+    assert pro(act=2) == VALUE
+    assert pro(floor=float("nan")) == VALUE
+    assert pro(floor=float("inf")) == VALUE
+    assert pro(eps=-1.0) == VALUE
+    assert pro(N=0) == SHAPE
+    assert pro(T=-1) == SHAPE
+    assert pro(N=3) == SHAPE                     # 100 tokens do not split into 3 equal runs
+    assert pro(H=16 * 65536) == SHAPE
+    assert pro(d=64) == UNSUP
+    assert pro(xq=None) == NULL
+    assert pro(g=None) == NULL
+    assert pro(a=None) == NULL
+    assert pro(q=P + 9 * GiB + 4) == ALIGN
+    assert pro(cu=P + 14 * GiB + 2) == ALIGN
+    assert pro(q=P + 16) == ALIAS                # q over the raw q
+    assert pro(v=P + 9 * GiB + tok // 2) == ALIAS   # v over q
+    assert pro(hout=P + 4 * GiB) == ALIAS        # history in place with 25 tokens per sequence
+    assert pro(hout=P + 4 * GiB + 64) == ALIAS   # partial overlap
+    assert pro(a=P + 6 * GiB) == ALIAS           # a over beta_raw
+    assert pro(b=P + 12 * GiB + 16) == ALIAS     # b over a
 
 
 def test_chunk_table_rejects_bad_arguments(lib):
