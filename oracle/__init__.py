@@ -60,6 +60,11 @@ class Oracle:
                                         ctypes.c_double, p, i32, ctypes.c_int64, i32, i32,
                                         p, p, p, p, p, p]
         lib.oracle_prologue.restype = ctypes.c_int
+        lib.oracle_rda_prefill_diag.argtypes = [p, p, p, p, p, p, i32, ctypes.c_int64,
+                                                i32, i32, i32, p, p, p, i32]
+        lib.oracle_rda_prefill_diag.restype = ctypes.c_int
+        lib.oracle_rda_decode_step_diag.argtypes = [p, p, p, p, p, i32, i32, i32, i32, p, p]
+        lib.oracle_rda_decode_step_diag.restype = ctypes.c_int
         lib.oracle_threads.argtypes = [i32]
         lib.oracle_threads.restype = ctypes.c_int
         self.lib = lib
@@ -75,6 +80,12 @@ class Oracle:
 
     def decode_tokens(self, q, k, v, a, b, S_in, accept=None, threads: int = 0):
         return _decode_tokens(self.lib, q, k, v, a, b, S_in, accept, threads)
+
+    def prefill_diag(self, q, k, v, alpha, b, cu_seqlens=None, S0=None, threads: int = 0):
+        return _prefill_diag(self.lib, q, k, v, alpha, b, cu_seqlens, S0, threads)
+
+    def decode_step_diag(self, q, k, v, alpha, b, S):
+        return _decode_step_diag(self.lib, q, k, v, alpha, b, S)
 
     def output_norm_gate(self, o, g, w, eps: float = 1e-5, act: str = "sigmoid"):
         return _output_norm_gate(self.lib, o, g, w, eps, act)
@@ -121,6 +132,58 @@ def decode_step(q, k, v, a, b, S, threads: int = 0):
 def decode_tokens(q, k, v, a, b, S_in, accept=None, threads: int = 0):
     """Several tokens per sequence with the default build (see _decode_tokens)."""
     return default().decode_tokens(q, k, v, a, b, S_in, accept, threads)
+
+
+def prefill_diag(q, k, v, alpha, b, cu_seqlens=None, S0=None, threads: int = 0):
+    """Per-channel-decay prefill with the default build (see _prefill_diag)."""
+    return default().prefill_diag(q, k, v, alpha, b, cu_seqlens, S0, threads)
+
+
+def decode_step_diag(q, k, v, alpha, b, S):
+    """Per-channel-decay decode step with the default build."""
+    return default().decode_step_diag(q, k, v, alpha, b, S)
+
+
+def _prefill_diag(lib, q, k, v, alpha, b, cu_seqlens=None, S0=None, threads: int = 0):
+    """Sequential fp64 prefill with a per-key-channel decay (oracle.c,
+    oracle_rda_prefill_diag): alpha [T, H, dk] in (0, 1]; the rest as in
+    _prefill.  Returns (o [T, H, dv], S_final [N, H, dv, dk]) float64."""
+    q, k, v, alpha, b = (_f32(x) for x in (q, k, v, alpha, b))
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    assert alpha.shape == (T, H, dk) and b.shape == (T, H)
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        N = cu.shape[0] - 1
+    else:
+        cu, N = None, 1
+    if S0 is not None:
+        S0 = _f64(S0)
+        assert S0.shape == (N, H, dv, dk)
+    o = np.zeros((T, H, dv))
+    S_final = np.zeros((N, H, dv, dk))
+    rc = lib.oracle_rda_prefill_diag(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(cu),
+                                     N, T, H, dk, dv, _ptr(S0), _ptr(o), _ptr(S_final),
+                                     int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_rda_prefill_diag failed with code {rc}")
+    return o, S_final
+
+
+def _decode_step_diag(lib, q, k, v, alpha, b, S):
+    """One in-place fp64 decode step with a per-key-channel decay on S
+    [B, H, dv, dk] (float64, modified); alpha [B, H, dk].  Returns o."""
+    q, k, v, alpha, b = (_f32(x) for x in (q, k, v, alpha, b))
+    B, H, dk = q.shape
+    dv = v.shape[2]
+    assert isinstance(S, np.ndarray) and S.dtype == np.float64 and S.flags.c_contiguous
+    assert S.shape == (B, H, dv, dk) and alpha.shape == (B, H, dk)
+    o = np.zeros((B, H, dv))
+    rc = lib.oracle_rda_decode_step_diag(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), B, H,
+                                         dk, dv, _ptr(S), _ptr(o))
+    if rc != 0:
+        raise ValueError(f"oracle_rda_decode_step_diag failed with code {rc}")
+    return o
 
 
 def output_norm_gate(o, g, w, eps: float = 1e-5, act: str = "sigmoid"):

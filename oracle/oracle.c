@@ -190,6 +190,113 @@ int oracle_rda_decode_step(const float* q, const float* k, const float* v,
 }
 
 /*
+ * Per-channel (diagonal) decay: the variant where the decay is a vector over
+ * the key channels instead of one scalar per token and head.  The vLLM
+ * article on Raon-1 mini calls RDA a modification of Kimi Delta Attention,
+ * whose decay is per channel, and the tiny-model card prints a low-rank
+ * decay projection (f_a_proj, f_b_proj) whose output has the width of the
+ * heads' key channels.  With alpha_t in (0,1]^dk the step, in the teardown's
+ * order (decay, error against the decayed state, write, read-out), is
+ *
+ *     S'  = S_{t-1} diag(alpha_t)      (column j of S scaled by alpha_tj)
+ *     e   = v_t - S' k_t
+ *     S_t = S' + b_t e k_t^T
+ *     o_t = S_t q_t
+ *
+ * alpha: [total_tokens, H, dk] fp32; everything else as in
+ * oracle_rda_prefill / oracle_rda_decode_step.
+ */
+static void oracle_token_diag(double* Sd, double* err, int dk, int dv, const float* qv,
+                              const float* kv, const float* vv, const float* alpha,
+                              double beta, double* out) {
+    for (int r = 0; r < dv; ++r) {
+        double* row = Sd + (size_t)r * dk;
+        double pr = 0.0;
+        for (int c = 0; c < dk; ++c) {
+            row[c] = row[c] * (double)alpha[c];
+            pr += row[c] * (double)kv[c];
+        }
+        err[r] = (double)vv[r] - pr;
+    }
+    for (int r = 0; r < dv; ++r) {
+        double* row = Sd + (size_t)r * dk;
+        const double be = beta * err[r];
+        for (int c = 0; c < dk; ++c) row[c] += be * (double)kv[c];
+        if (out) {
+            double acc = 0.0;
+            for (int c = 0; c < dk; ++c) acc += row[c] * (double)qv[c];
+            out[r] = acc;
+        }
+    }
+}
+
+int oracle_rda_prefill_diag(const float* q, const float* k, const float* v,
+                            const float* alpha, const float* b, const int32_t* cu,
+                            int32_t n_seq, int64_t total_tokens, int32_t H, int32_t dk,
+                            int32_t dv, const double* S0, double* o, double* S_final,
+                            int32_t threads) {
+    if (!q || !k || !v || !alpha || !b || !o) return ORACLE_ERR_ARG;
+    if (H <= 0 || dk <= 0 || dv <= 0 || total_tokens < 0 || n_seq <= 0) return ORACLE_ERR_ARG;
+    if (!cu && n_seq != 1) return ORACLE_ERR_ARG;
+    if (cu) {
+        if (cu[0] != 0 || cu[n_seq] != total_tokens) return ORACLE_ERR_ARG;
+        for (int32_t n = 0; n < n_seq; ++n)
+            if (cu[n + 1] < cu[n]) return ORACLE_ERR_ARG;
+    }
+    const size_t dd = (size_t)dv * dk;
+    const int64_t units = (int64_t)n_seq * H;
+    int rc = ORACLE_OK;
+#ifdef _OPENMP
+    int nt = threads > 0 ? threads : omp_get_max_threads();
+#pragma omp parallel num_threads(nt)
+#endif
+    {
+        double* Sd = (double*)malloc(dd * sizeof(double));
+        double* err = (double*)malloc((size_t)dv * sizeof(double));
+        if (!Sd || !err) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            rc = ORACLE_ERR_NOMEM;
+        } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+            for (int64_t u = 0; u < units; ++u) {
+                const int32_t n = (int32_t)(u / H), h = (int32_t)(u % H);
+                const int64_t first = cu ? cu[n] : 0, last = cu ? cu[n + 1] : total_tokens;
+                if (S0) memcpy(Sd, S0 + (size_t)u * dd, dd * sizeof(double));
+                else memset(Sd, 0, dd * sizeof(double));
+                for (int64_t t = first; t < last; ++t) {
+                    const size_t row = (size_t)t * H + h;
+                    oracle_token_diag(Sd, err, dk, dv, q + row * dk, k + row * dk, v + row * dv,
+                                      alpha + row * dk, (double)b[row], o + row * dv);
+                }
+                if (S_final) memcpy(S_final + (size_t)u * dd, Sd, dd * sizeof(double));
+            }
+        }
+        free(Sd);
+        free(err);
+    }
+    return rc;
+}
+
+int oracle_rda_decode_step_diag(const float* q, const float* k, const float* v,
+                                const float* alpha, const float* b, int32_t B, int32_t H,
+                                int32_t dk, int32_t dv, double* S, double* o) {
+    if (!q || !k || !v || !alpha || !b || !S || !o) return ORACLE_ERR_ARG;
+    if (B < 0 || H <= 0 || dk <= 0 || dv <= 0) return ORACLE_ERR_ARG;
+    double* err = (double*)malloc((size_t)dv * sizeof(double));
+    if (!err) return ORACLE_ERR_NOMEM;
+    for (int64_t u = 0; u < (int64_t)B * H; ++u)
+        oracle_token_diag(S + (size_t)u * dv * dk, err, dk, dv, q + (size_t)u * dk,
+                          k + (size_t)u * dk, v + (size_t)u * dv, alpha + (size_t)u * dk,
+                          (double)b[u], o + (size_t)u * dv);
+    free(err);
+    return 0;
+}
+
+/*
  * Output epilogue of the mixer: per output row of one head (dv channels),
  * an RMS normalisation with epsilon and a per-channel weight, times an
  * activation of the output gate.  The tiny-random/raon-1-mini model card,

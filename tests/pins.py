@@ -471,9 +471,85 @@ def pin_prologue_history(orc):
     _close(packed[5][1, :, :K - 2], hs[1, :, 1:], 0, "one-token sequence shifts its history")
 
 
+def _diag_case(rng, T, H, dk, dv):
+    q, k, v, a, b, S0 = random_case(rng, T, H, dk, dv)
+    alpha = _f32(rng.uniform(0.2, 1.0, (T, H, dk)))
+    return q, k, v, alpha, b, S0
+
+
+def pin_diag_scalar_special_case(orc):
+    """A decay equal on every key channel is the scalar rule (the scalar
+    oracle is pinned on its own)."""
+    rng = _rng(27)
+    q, k, v, a, b, S0 = random_case(rng, 13, 3, 6, 5)
+    alpha = _f32(np.repeat(a[:, :, None], 6, axis=2))
+    o1, s1 = orc.prefill_diag(q, k, v, alpha, b, S0=S0)
+    o2, s2 = orc.prefill(q, k, v, a, b, S0=S0)
+    _close(o1, o2, 1e-13, "diag = scalar, o")
+    _close(s1, s2, 1e-13, "diag = scalar, S")
+
+
+def pin_diag_product_form(orc):
+    """Brute force with matrices: S_t = S_{t-1} diag(alpha_t) (I - b k k^T)
+    + b v k^T, o_t = S_t q_t, per head (T = 4, two heads)."""
+    rng = _rng(28)
+    T, H, dk, dv = 4, 2, 5, 3
+    q, k, v, alpha, b, S0 = _diag_case(rng, T, H, dk, dv)
+    o, S = orc.prefill_diag(q, k, v, alpha, b, S0=S0)
+    for h in range(H):
+        St = _d(S0[0, h])
+        for t in range(T):
+            kt = _d(k[t, h])
+            St = St @ np.diag(_d(alpha[t, h])) @ (np.eye(dk) - b[t, h] * np.outer(kt, kt)) \
+                + b[t, h] * np.outer(_d(v[t, h]), kt)
+            _close(o[t, h], St @ _d(q[t, h]), 1e-13, f"diag product form o t={t} h={h}")
+        _close(S[0, h], St, 1e-13, f"diag product form S h={h}")
+
+
+def pin_diag_channel_separation(orc):
+    """Keys and queries on channels 0..2 only: the state's other columns
+    just decay, S[:, j] = S0[:, j] prod_t alpha_tj, and never reach o."""
+    rng = _rng(29)
+    T, H, dk, dv = 9, 2, 7, 4
+    q, k, v, alpha, b, S0 = _diag_case(rng, T, H, dk, dv)
+    q[:, :, 3:] = 0.0
+    k[:, :, 3:] = 0.0
+    o, S = orc.prefill_diag(q, k, v, alpha, b, S0=S0)
+    prod = np.prod(_d(alpha[:, :, 3:]), axis=0)            # [H, 4]
+    _close(S[0, :, :, 3:], _d(S0[0, :, :, 3:]) * prod[:, None, :], 1e-14, "untouched columns")
+    S0b = S0.copy()
+    S0b[..., 3:] = 0.0
+    o2, _ = orc.prefill_diag(q, k, v, alpha, b, S0=S0b)
+    _close(o, o2, 1e-14, "untouched columns never reach o")
+
+
+def pin_diag_decode_and_varlen(orc):
+    """Decode steps equal the prefill; a packed batch equals separate calls."""
+    rng = _rng(30)
+    q, k, v, alpha, b, S0 = _diag_case(rng, 10, 3, 6, 5)
+    o, s = orc.prefill_diag(q, k, v, alpha, b, S0=S0)
+    S = np.ascontiguousarray(_d(S0))
+    for t in range(10):
+        ot = orc.decode_step_diag(q[t:t + 1], k[t:t + 1], v[t:t + 1], alpha[t:t + 1],
+                                  b[t:t + 1], S)
+        _close(ot[0], o[t], 1e-13, f"diag decode step {t}")
+    _close(S, s, 1e-13, "diag decode final state")
+    lens = [4, 0, 6]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    S0s = rng.standard_normal((3, 3, 5, 6))
+    o, s = orc.prefill_diag(q, k, v, alpha, b, cu_seqlens=cu, S0=S0s)
+    for n, L in enumerate(lens):
+        t0, t1 = cu[n], cu[n + 1]
+        on, sn = orc.prefill_diag(q[t0:t1], k[t0:t1], v[t0:t1], alpha[t0:t1], b[t0:t1],
+                                  S0=S0s[n:n + 1])
+        _close(o[t0:t1], on, 1e-14, f"diag varlen seq {n}")
+        _close(s[n], sn[0], 1e-14, f"diag varlen S seq {n}")
+
+
 ALL_PINS = [pin_bruteforce, pin_exact_dyadic, pin_hand_example, pin_identity_gates,
             pin_readback, pin_pure_decay, pin_single_step, pin_linearity, pin_rotation,
             pin_permutation, pin_norm_bound, pin_resume, pin_varlen,
             pin_decode_equals_prefill, pin_decode_tokens, pin_norm_gate_library,
             pin_norm_gate_closed_forms, pin_prologue_library, pin_prologue_gates,
-            pin_prologue_history]
+            pin_prologue_history, pin_diag_scalar_special_case, pin_diag_product_form,
+            pin_diag_channel_separation, pin_diag_decode_and_varlen]

@@ -1,7 +1,7 @@
 """Plant plausible mistakes in copies of the oracle source (CPU only) and
 check that every one of them fails at least one pin.  This shows the pins
-constrain each term, sign, index and operand of the recurrence, of the
-prologue and of the output epilogue."""
+constrain each term, sign, index and operand of the recurrence (scalar and
+per-channel decay), of the prologue and of the output epilogue."""
 import os
 import shutil
 import subprocess
@@ -69,6 +69,16 @@ MUTANTS = [
      "const double scale = x < 3 ? 1.0 / sqrt(ss + l2_eps) : wgate;"),
     ("silu_sign", "if (act == 1) acc = acc / (1.0 + exp(-acc));",
      "if (act == 1) acc = acc / (1.0 + exp(acc));"),
+    ("diag_decay_of_wrong_channel", "row[c] = row[c] * (double)alpha[c];",
+     "row[c] = row[c] * (double)alpha[dk - 1 - c];"),
+    ("diag_decay_on_value_channel", "row[c] = row[c] * (double)alpha[c];",
+     "row[c] = row[c] * (double)alpha[r % dk];"),
+    ("diag_error_before_decay",
+     "row[c] = row[c] * (double)alpha[c];\n            pr += row[c] * (double)kv[c];",
+     "pr += row[c] * (double)kv[c];\n            row[c] = row[c] * (double)alpha[c];"),
+    ("diag_decay_of_head0", "alpha + row * dk, (double)b[row], o + row * dv);",
+     "alpha + ((size_t)t * H) * dk, (double)b[row], o + row * dv);"),
+    ("diag_write_without_beta", "const double be = beta * err[r];", "const double be = err[r];"),
 ]
 
 
