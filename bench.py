@@ -20,8 +20,8 @@ Prints ONE JSON line:
   parity     rel-L2 / max-abs of this run's prefill output vs the oracle
 The oracle runs only in this CPU leg (skipped with --no-cpu): the baseline
 timing, and the parity figures of this run's outputs (parity, and the parity
-entries of other_prefill_workloads, prologue, output_norm_gate and
-decode_tokens).
+entries of other_prefill_workloads, prefill_diag, prologue,
+output_norm_gate and decode_tokens).
   also       the prefill back to back without the flush (ms_per_call_unflushed)
              and after a read-only 512 MiB flush (ms_per_call_read_flushed),
              the practical HBM rate of an in-place read-modify-write of 256 MiB
@@ -36,7 +36,9 @@ decode_tokens).
              prompt's 262144 output rows (output_norm_gate); the prologue on
              the long prompt and on the decode batch (prologue), and the
              whole block -- prologue, prefill, output norm and gate -- as
-             tokens/s (output_norm_gate.block_tokens_per_s)
+             tokens/s (output_norm_gate.block_tokens_per_s); the long prompt
+             with a per-channel decay and the per-channel decode step
+             (prefill_diag)
 
 Usage: python bench.py [--gpus 1] [--steps 128] [--warmup 5] [--no-cpu]
 """
@@ -73,13 +75,14 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0 = all)")
     ap.add_argument("--mode", choices=["bench", "prefill", "decode", "decode_tokens",
-                                       "output_norm_gate", "prologue", "copy"],
+                                       "output_norm_gate", "prologue", "prefill_diag", "copy"],
                     default="bench",
                     help="prefill/decode: run only that part (for profiling); decode_tokens / "
-                         "output_norm_gate / prologue: only the one-pass multi-token decode / "
-                         "the output norm and gate / the long prompt's prologue, --steps calls "
-                         "after a cache flush each; copy: a plain device copy of known size "
-                         "(counter calibration)")
+                         "output_norm_gate / prologue / prefill_diag: only the one-pass "
+                         "multi-token decode / the output norm and gate / the long prompt's "
+                         "prologue / its per-channel-decay prefill, --steps calls after a cache "
+                         "flush each; copy: a plain device copy of known size (counter "
+                         "calibration)")
     ap.add_argument("--no-extras", action="store_true",
                     help="only the timed steps and the per-stage calls (the kernel trace "
                          "of exactly what the kernels entry reports)")
@@ -143,7 +146,7 @@ def main():
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
-    if args.mode in ("decode_tokens", "output_norm_gate", "prologue"):
+    if args.mode in ("decode_tokens", "output_norm_gate", "prologue", "prefill_diag"):
         timed = make_timer(torch, np, stream)
         flush_buf = torch.ones((128 << 20,), dtype=torch.float32, device=dev)
         flush = lambda: flush_buf.sum()
@@ -154,9 +157,12 @@ def main():
         elif args.mode == "output_norm_gate":
             res = epilogue_measurements(args, {}, torch, np, rda, synth, dev, timed, flush,
                                         16384, 16, reps=args.steps)
-        else:
+        elif args.mode == "prologue":
             res = prologue_measurements(args, {}, torch, np, rda, synth, dev, timed, flush,
                                         16384, 16, reps=args.steps, decode=False)
+        else:
+            res = diag_measurements(args, {}, torch, np, rda, synth, dev, timed, flush,
+                                    reps=args.steps, decode=False)
         print(json.dumps({"mode": args.mode, **res}), flush=True)
         return
 
@@ -427,6 +433,7 @@ def extra_measurements(args, out, torch, np, rda, synth, dev, stream, q, k, v, a
         if cid == 4:
             entry["lengths"] = [int(x) for x in np.diff(cuc)]
     out["other_prefill_workloads"] = configs
+    out["prefill_diag"] = diag_measurements(args, out, torch, np, rda, synth, dev, timed, flush)
     out["prologue"] = prologue_measurements(args, out, torch, np, rda, synth, dev, timed, flush,
                                             T, H)
     out["output_norm_gate"] = epilogue_measurements(args, out, torch, np, rda, synth, dev, timed,
@@ -434,6 +441,51 @@ def extra_measurements(args, out, torch, np, rda, synth, dev, stream, q, k, v, a
     out["decode_tokens"] = decode_tokens_measurements(args, out, torch, np, rda, synth, dev,
                                                       stream, timed, flush)
     del scratch, flush_buf
+
+
+def diag_measurements(args, out, torch, np, rda, synth, dev, timed, flush, reps=10,
+                      decode=True):
+    """The per-channel-decay prefill on the long prompt (T = 16384, H = 16,
+    bf16 q/k/v, per-channel decay, S0 ~ N(0, 0.02)) as tokens/s after a cache
+    flush, with parity against the oracle; with `decode`, the per-channel
+    decode step on the decode batch (256 x 16 states) as state GB/s."""
+    T, H = 16384, 16
+    p = synth.config3()
+    alpha = synth.diag_alpha(T, H)
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)
+    dv = lambda a: torch.from_numpy(a).to(dev)
+    q, k, v = bf(p.q), bf(p.k), bf(p.v)
+    al, b, S0 = dv(alpha), dv(p.b), dv(p.S0)
+    o = torch.empty((T, H, D), dtype=torch.float32, device=dev)
+    Sf = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(rda.rda_prefill_diag_workspace_bytes(1, T, H), dtype=torch.uint8, device=dev)
+    sec = timed(lambda: rda.rda_prefill_diag(q, k, v, al, b, S0=S0, o=o, S_final=Sf,
+                                             workspace=ws), reps, flush)
+    res = {"T": T, "H": H, "ms_per_call": sec * 1e3, "tokens_per_s": T / sec,
+           "workspace_bytes": ws.numel()}
+    if "prefill" in out:
+        res["vs_scalar_decay"] = out["prefill"]["ms_per_call"] / (sec * 1e3)
+    if not args.no_cpu:
+        import oracle
+        ro, rS = oracle.prefill_diag(p.q, p.k, p.v, alpha, p.b, S0=p.S0,
+                                     threads=args.cpu_threads)
+        oh, Sh = o.cpu().numpy().astype(np.float64), Sf.cpu().numpy().astype(np.float64)
+        res["parity"] = {"o_rel_l2": float(np.linalg.norm(oh - ro) / np.linalg.norm(ro)),
+                         "o_max_abs": float(np.max(np.abs(oh - ro))),
+                         "S_rel_l2": float(np.linalg.norm(Sh - rS) / np.linalg.norm(rS))}
+    if decode:
+        B = 256
+        S_dec = dv(synth.decode_state(B, H))
+        x = synth.decode_step_inputs(0, B, H)
+        xq, xk, xv = (torch.from_numpy(getattr(x, n)).to(torch.bfloat16).to(dev) for n in "qkv")
+        ad, bd = dv(synth.diag_alpha(B, H, key=(11,))), dv(x.b)
+        od = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+        dsec = timed(lambda: rda.rda_decode_step_diag(xq, xk, xv, ad, bd, S_dec, o=od), reps,
+                     flush)
+        dbytes = B * H * (2 * STATE_BYTES + PREFILL_IN_BYTES + PREFILL_OUT_BYTES + D * 4)
+        res["decode"] = {"B": B, "us_per_step": dsec * 1e6, "GBps": dbytes / dsec / 1e9,
+                         "frac_of_peak": dbytes / dsec / 1e9 / PEAK_HBM_GBPS}
+    return res
 
 
 PROLOGUE_K = 4   # conv width: three cached raw tokens per tensor

@@ -271,6 +271,100 @@ rda_status rda_decode_tokens(const void* q, const void* k, const void* v, rda_dt
     return RDA_OK;
 }
 
+size_t rda_prefill_diag_workspace_bytes(int32_t num_seqs, int32_t total_tokens,
+                                        int32_t num_heads, int32_t dk, int32_t dv) {
+    if (check_dims(num_heads, dk, dv) != RDA_OK) return 0;
+    const int32_t mc = rda_max_chunks(num_seqs, total_tokens);
+    if (mc < 0) return 0;
+    const TableLayout tl = table_layout(mc, num_seqs);
+    return align256(tl.bytes) + size_t(mc) * size_t(num_heads) * kDiagChunkHeadBytes;
+}
+
+rda_status rda_prefill_diag(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
+                            const float* alpha, const float* b, const int32_t* cu_seqlens,
+                            int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                            int32_t dk, int32_t dv, const float* S0, float* o, float* S_final,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (qkv_dtype != RDA_BF16 && qkv_dtype != RDA_FP32) return RDA_ERR_DTYPE;
+    if (total_tokens < 0 || num_seqs < 1) return RDA_ERR_SHAPE;
+    if (!cu_seqlens && num_seqs != 1) return RDA_ERR_SHAPE;
+    rda_status st = check_dims(num_heads, dk, dv);
+    if (st != RDA_OK) return st;
+    if (qkv_dtype != RDA_BF16) return RDA_ERR_UNSUPPORTED;
+    const int32_t mc = rda_max_chunks(num_seqs, total_tokens);
+    if (mc < 0) return RDA_ERR_SHAPE;
+    if (int64_t(mc) * num_heads > INT32_MAX || int64_t(num_seqs) * num_heads * kWalkSlices > INT32_MAX)
+        return RDA_ERR_SHAPE;
+    if (total_tokens > 0 && (!q || !k || !v || !alpha || !b || !o)) return RDA_ERR_NULL;
+    if (!workspace) return RDA_ERR_WORKSPACE;
+    const size_t need =
+        rda_prefill_diag_workspace_bytes(num_seqs, total_tokens, num_heads, dk, dv);
+    if (workspace_bytes < need) return RDA_ERR_WORKSPACE;
+    for (const void* p : {q, k, v, static_cast<const void*>(alpha), static_cast<const void*>(b),
+                          static_cast<const void*>(S0), static_cast<const void*>(o),
+                          static_cast<const void*>(S_final), static_cast<const void*>(workspace)})
+        if (p && !aligned16(p)) return RDA_ERR_ALIGN;
+    if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return RDA_ERR_ALIGN;
+    const size_t th = size_t(total_tokens) * num_heads;
+    const size_t sbytes = size_t(num_seqs) * num_heads * kD * kD * sizeof(float);
+    const Range rq = rng(q, th * kD * 2), rk = rng(k, th * kD * 2), rv = rng(v, th * kD * 2);
+    const Range ral = rng(alpha, th * kD * 4), rb = rng(b, th * 4);
+    const Range ro = rng(o, th * kD * 4), rs0 = rng(S0, S0 ? sbytes : 0);
+    const Range rsf = rng(S_final, S_final ? sbytes : 0), rws = rng(workspace, need);
+    const Range rcu = rng(cu_seqlens, cu_seqlens ? size_t(num_seqs + 1) * 4 : 0);
+    for (Range in : {rq, rk, rv, ral, rb, rs0, rcu, rsf, rws})
+        if (overlap(ro, in)) return RDA_ERR_ALIAS;
+    for (Range in : {rq, rk, rv, ral, rb, rcu, rws})
+        if (overlap(rsf, in)) return RDA_ERR_ALIAS;
+    if (S0 && S_final && S0 != S_final && overlap(rs0, rsf)) return RDA_ERR_ALIAS;
+    for (Range in : {rq, rk, rv, ral, rb, rs0, rcu})
+        if (overlap(rws, in)) return RDA_ERR_ALIAS;
+
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    const TableLayout tl = table_layout(mc, num_seqs);
+    int32_t* rec = reinterpret_cast<int32_t*>(ws + tl.rec_off);
+    int32_t* seq_off = reinterpret_cast<int32_t*>(ws + tl.seq_off_off);
+    int32_t* nch = reinterpret_cast<int32_t*>(ws + tl.num_off);
+    if (launch_chunk_table(cu_seqlens, num_seqs, total_tokens, mc, rec, seq_off, nch, stream) !=
+        hipSuccess)
+        return RDA_ERR_HIP;
+    if (launch_prefill_diag(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                            static_cast<const uint16_t*>(v), alpha, b, num_seqs, num_heads,
+                            total_tokens > 0 ? mc : 0, rec, seq_off, nch, ws + align256(tl.bytes),
+                            S0, o, S_final, stream) != hipSuccess)
+        return RDA_ERR_HIP;
+    return RDA_OK;
+}
+
+rda_status rda_decode_step_diag(const void* q, const void* k, const void* v,
+                                rda_dtype qkv_dtype, const float* alpha, const float* b,
+                                int32_t batch, int32_t num_heads, int32_t dk, int32_t dv,
+                                float* S, float* o, hipStream_t stream) {
+    if (qkv_dtype != RDA_BF16 && qkv_dtype != RDA_FP32) return RDA_ERR_DTYPE;
+    if (batch < 0) return RDA_ERR_SHAPE;
+    rda_status st = check_dims(num_heads, dk, dv);
+    if (st != RDA_OK) return st;
+    if (int64_t(batch) * num_heads > INT32_MAX / 2) return RDA_ERR_SHAPE;
+    if (batch == 0) return RDA_OK;
+    if (!q || !k || !v || !alpha || !b || !S || !o) return RDA_ERR_NULL;
+    for (const void* p : {q, k, v, static_cast<const void*>(alpha), static_cast<const void*>(b),
+                          static_cast<const void*>(S), static_cast<const void*>(o)})
+        if (!aligned16(p)) return RDA_ERR_ALIGN;
+    const size_t esz = qkv_dtype == RDA_BF16 ? 2 : 4;
+    const size_t bh = size_t(batch) * num_heads;
+    const Range rq = rng(q, bh * kD * esz), rk = rng(k, bh * kD * esz), rv = rng(v, bh * kD * esz);
+    const Range ral = rng(alpha, bh * kD * 4), rb = rng(b, bh * 4);
+    const Range rS = rng(S, bh * kD * kD * 4), ro = rng(o, bh * kD * 4);
+    for (Range in : {rq, rk, rv, ral, rb, rS})
+        if (overlap(ro, in)) return RDA_ERR_ALIAS;
+    for (Range in : {rq, rk, rv, ral, rb})
+        if (overlap(rS, in)) return RDA_ERR_ALIAS;
+    if (launch_decode_diag(q, k, v, qkv_dtype, alpha, b, batch, num_heads, S, o, stream) !=
+        hipSuccess)
+        return RDA_ERR_HIP;
+    return RDA_OK;
+}
+
 rda_status rda_prologue(const void* x_q, const void* x_k, const void* x_v, rda_dtype x_dtype,
                         const float* conv_w, int32_t conv_width, int32_t conv_act,
                         const void* hist_in, void* hist_out, const float* beta_raw,

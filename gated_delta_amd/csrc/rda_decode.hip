@@ -256,6 +256,97 @@ __global__ __launch_bounds__(256) void decode_tokens_kernel(
     }
 }
 
+// One decode step with a per-key-channel decay alpha [batch, H, 128]: the
+// same layout and single pass as decode_step_kernel, with column j of the
+// state scaled by alpha_j: for row i,
+//     (S'k)_i = sum_j S_ij alpha_j k_j,   (S'q)_i = sum_j S_ij alpha_j q_j
+//     e_i = v_i - (S'k)_i,   S_ij <- alpha_j S_ij + b e_i k_j
+//     o_i = (S'q)_i + b e_i (k . q)
+template <typename TIn>
+__global__ __launch_bounds__(256) void decode_diag_kernel(const TIn* __restrict__ q,
+                                                          const TIn* __restrict__ k,
+                                                          const TIn* __restrict__ v,
+                                                          const float* __restrict__ alpha,
+                                                          const float* __restrict__ b,
+                                                          float* __restrict__ S,
+                                                          float* __restrict__ o) {
+    const int64_t bh = blockIdx.x >> 1;
+    const int half = blockIdx.x & 1;
+    const int t = threadIdx.x;
+    const int w = wave_id();
+    const int g = (t >> 4) & 3;
+    const int c = t & 15;
+    float* __restrict__ Sb = S + bh * (kD * kD);
+    f32x4 s[4][2];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int row = 64 * half + 16 * w + 4 * p + g;
+        s[p][0] = *reinterpret_cast<const f32x4*>(Sb + row * kD + 4 * c);
+        s[p][1] = *reinterpret_cast<const f32x4*>(Sb + row * kD + 64 + 4 * c);
+    }
+    float kx[8], qx[8];
+    load4<TIn>(k + bh * kD + 4 * c, kx);
+    load4<TIn>(k + bh * kD + 64 + 4 * c, kx + 4);
+    load4<TIn>(q + bh * kD + 4 * c, qx);
+    load4<TIn>(q + bh * kD + 64 + 4 * c, qx + 4);
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(alpha + bh * kD + 4 * c);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(alpha + bh * kD + 64 + 4 * c);
+    const float ax[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    const float bv = b[bh];
+    float vr[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) vr[p] = load1<TIn>(v + bh * kD + 64 * half + 16 * w + 4 * p + g);
+    float ak[8], aq[8], kap = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        ak[j] = ax[j] * kx[j];
+        aq[j] = ax[j] * qx[j];
+        kap += kx[j] * qx[j];
+    }
+    kap = dpp_sum16(kap);
+    float o_mine = 0.f;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            sk = fmaf(s[p][0][j], ak[j], fmaf(s[p][1][j], ak[4 + j], sk));
+            sq = fmaf(s[p][0][j], aq[j], fmaf(s[p][1][j], aq[4 + j], sq));
+        }
+        sk = dpp_sum16(sk);
+        sq = dpp_sum16(sq);
+        const float be = bv * (vr[p] - sk);
+        const float orow = sq + be * kap;
+        if (c == p) o_mine = orow;
+        f32x4 n0, n1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            n0[j] = fmaf(ax[j], s[p][0][j], be * kx[j]);
+            n1[j] = fmaf(ax[4 + j], s[p][1][j], be * kx[4 + j]);
+        }
+        const int row = 64 * half + 16 * w + 4 * p + g;
+        *reinterpret_cast<f32x4*>(Sb + row * kD + 4 * c) = n0;
+        *reinterpret_cast<f32x4*>(Sb + row * kD + 64 + 4 * c) = n1;
+    }
+    if (c < 4) o[bh * kD + 64 * half + 16 * w + 4 * c + g] = o_mine;
+}
+
+hipError_t launch_decode_diag(const void* q, const void* k, const void* v, rda_dtype dt,
+                              const float* alpha, const float* b, int32_t batch, int32_t heads,
+                              float* S, float* o, hipStream_t stream) {
+    const unsigned grid = unsigned(2 * int64_t(batch) * heads);
+    if (grid == 0) return hipSuccess;
+    if (dt == RDA_BF16)
+        hipLaunchKernelGGL(decode_diag_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                           static_cast<const uint16_t*>(v), alpha, b, S, o);
+    else
+        hipLaunchKernelGGL(decode_diag_kernel<float>, dim3(grid), dim3(256), 0, stream,
+                           static_cast<const float*>(q), static_cast<const float*>(k),
+                           static_cast<const float*>(v), alpha, b, S, o);
+    return hipGetLastError();
+}
+
 hipError_t launch_decode(const void* q, const void* k, const void* v, rda_dtype dt,
                          const float* a, const float* b, int32_t batch, int32_t heads,
                          float* S, float* o, hipStream_t stream) {

@@ -41,6 +41,22 @@ constexpr int kGScale = 64;
 constexpr int kGC = 128;
 constexpr int kGLog = 192;
 
+// Per-(chunk, head) factors of the per-channel-decay prefill (same table in
+// front), each packed as the walk's bf16 hi/lo MFMA operands:
+//   Tb  T diag(b)                       rows tokens, K dim tokens   16 KiB
+//   Am  A                               rows tokens, K dim tokens   16 KiB
+//   Kt  K . e^G                         rows tokens, K dim keys     32 KiB
+//   Qt  Q . e^G                         rows tokens, K dim keys     32 KiB
+//   Kh  (K . e^{G_C - G})^T             rows keys, K dim tokens     32 KiB
+//   GC  e^{G_C} per key channel, fp32                               512 B
+constexpr size_t kDOffTb = 0;
+constexpr size_t kDOffA = kDOffTb + kPackBytes;
+constexpr size_t kDOffKt = kDOffA + kPackBytes;
+constexpr size_t kDOffQt = kDOffKt + 2 * kPackBytes;
+constexpr size_t kDOffKh = kDOffQt + 2 * kPackBytes;
+constexpr size_t kDOffGC = kDOffKh + 2 * kPackBytes;
+constexpr size_t kDiagChunkHeadBytes = kDOffGC + 512;
+
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct TableLayout {
@@ -93,6 +109,17 @@ struct PrologueArgs {
     float* b;
 };
 hipError_t launch_prologue(const PrologueArgs& P, int32_t K, int32_t act, hipStream_t stream);
+
+// Per-channel decay: prep + walk after the chunk table (bf16 q, k, v).
+hipError_t launch_prefill_diag(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               const float* alpha, const float* b, int32_t num_seqs,
+                               int32_t heads, int32_t max_chunks, const int32_t* rec,
+                               const int32_t* seq_off, const int32_t* num_chunks,
+                               unsigned char* factors, const float* S0, float* o,
+                               float* S_final, hipStream_t stream);
+hipError_t launch_decode_diag(const void* q, const void* k, const void* v, rda_dtype dt,
+                              const float* alpha, const float* b, int32_t batch, int32_t heads,
+                              float* S, float* o, hipStream_t stream);
 
 // Output norm and gate over `rows` rows of 128 channels.
 int64_t norm_gate_blocks(int64_t rows);

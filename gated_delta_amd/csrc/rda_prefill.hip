@@ -49,6 +49,7 @@
 // accumulator tile pair is then a ready B operand with no data movement.
 #include "rda_device.h"
 #include "rda_internal.h"
+#include "rda_solve.h"
 
 namespace rda {
 
@@ -58,7 +59,6 @@ namespace {
 // PREP: one 256-thread workgroup per (chunk, head).
 // ---------------------------------------------------------------------------
 constexpr int kTS = 136;   // bf16 tile row stride (elements): 272 B, spreads LDS banks
-constexpr int kFS = 68;    // fp32 64x64 matrix row stride
 constexpr int kTileB = kC * kTS * 2;   // 17408 B
 constexpr int kMatB = kC * kFS * 4;    // 17408 B
 
@@ -115,37 +115,6 @@ __device__ __forceinline__ void stage_tile(const typename PrepIn<kSplit>::T* __r
             *reinterpret_cast<u16x4*>(hi + r * kTS + c4) = xh;
             *reinterpret_cast<u16x4*>(lo + r * kTS + c4) = xl;
         }
-    }
-}
-
-// Pack rows of a 64 x 64 fp32 matrix (columns scaled by `colscale` when
-// given) as bf16 hi/lo A operands for the walk: slot (row tile w, token
-// block m, lane) holds row 16w + (lane % 16), columns {32m + 4g + i,
-// 32m + 16 + 4g + i} with g = lane / 16; hi at [(w*2+m)*2][lane], lo after it.
-__device__ __forceinline__ void pack_rows(const float* M, const float* colscale, bf16x8* dst,
-                                          int tid) {
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-        const int slot = tid + 256 * qq;
-        const int lp = slot & 63, m = (slot >> 6) & 1, wp = slot >> 7;
-        const int r = 16 * wp + (lp & 15), c0 = 32 * m + 4 * (lp >> 4);
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(M + r * kFS + c0);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(M + r * kFS + c0 + 16);
-        float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        if (colscale) {
-            const f32x4 s0 = *reinterpret_cast<const f32x4*>(colscale + c0);
-            const f32x4 s1 = *reinterpret_cast<const f32x4*>(colscale + c0 + 16);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                x[j] *= s0[j];
-                x[4 + j] *= s1[j];
-            }
-        }
-        bf16x8 hi, lo;
-        split8(x, hi, lo);
-        const int base = ((wp * 2 + m) * 2) * 64 + lp;
-        dst[base] = hi;
-        dst[base + 64] = lo;
     }
 }
 
@@ -247,60 +216,7 @@ __global__ __launch_bounds__(256) void prep_kernel(
     __syncthreads();
 
     // ---- T = (I + L)^-1 ------------------------------------------------------
-    // (a) diagonal 16x16 blocks by forward substitution, one wavefront per block:
-    //     lane (column c, part g) keeps x[m] for m = g (mod 4); each row step
-    //     sums its part of L[r][m] x[m] and reduces across the four parts.
-    {
-        const int base = 16 * w;
-        float xs[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float part = 0.f;
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const int m = 4 * qq + g;
-                if (m < r) part += Ls[(base + r) * kFS + base + m] * xs[qq];
-            }
-            part += __shfl_xor(part, 16, 64);
-            part += __shfl_xor(part, 32, 64);
-            const float x = (r == c ? 1.f : 0.f) - part;
-            if ((r & 3) == g) {
-                xs[r >> 2] = x;
-                Ts[(base + r) * kFS + base + c] = x;
-            }
-        }
-    }
-    __syncthreads();
-    // (b) off-diagonal blocks, block row by block row, on fp32 MFMA:
-    //     T_ij = -T_ii * sum_{m=j}^{i-1} L_im T_mj.
-    for (int bi = 1; bi < 4; ++bi) {
-        if (w < bi) {
-            const int bj = w;
-            f32x4 acc = zero4();
-            for (int m = bj; m < bi; ++m) {
-#pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) {
-                    const float av = Ls[(16 * bi + c) * kFS + 16 * m + 4 * s4 + g];
-                    const float bv = Ts[(16 * m + 4 * s4 + g) * kFS + 16 * bj + c];
-                    acc = mfma_f32(av, bv, acc);
-                }
-            }
-            float* R = Rs + 256 * w;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) R[(4 * g + i) * 16 + c] = acc[i];
-            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): R visible to this wavefront
-            f32x4 acc2 = zero4();
-#pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
-                const float av = Ts[(16 * bi + c) * kFS + 16 * bi + 4 * s4 + g];
-                const float bv = R[(4 * s4 + g) * 16 + c];
-                acc2 = mfma_f32(av, bv, acc2);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Ts[(16 * bi + 4 * g + i) * kFS + 16 * bj + c] = -acc2[i];
-        }
-        __syncthreads();
-    }
+    solve_unit_lower(Ls, Ts, Rs, w, g, c);
 
     // ---- outputs: T_b = T diag(b) and A as packed hi/lo operands; gates ----
     pack_rows(Ts, bb, reinterpret_cast<bf16x8*>(F + kOffTb), tid);

@@ -1,11 +1,11 @@
 #!/bin/bash
 # Collects the rocprofv3 kernel summaries and the counter passes behind
 # profiles/: kernel trace + stats of the bench's timed steps (and, in passes
-# of their own, of the one-pass multi-token decode, the output norm and gate
-# and the prologue), then one FETCH_SIZE and one WRITE_SIZE pass over the
-# prefill alone, the multi-token decode, the output norm and gate, the
-# prologue, and a plain device copy of known size (the counter calibration),
-# then one pass of the MFMA counters over the prefill.
+# of their own, of the one-pass multi-token decode, the output norm and gate,
+# the prologue and the per-channel-decay prefill), then one FETCH_SIZE and one
+# WRITE_SIZE pass over the prefill alone, each of those, and a plain device
+# copy of known size (the counter calibration), then one pass of the MFMA
+# counters over the prefill.
 #   usage: gated_delta_amd/profile_run.sh OUTDIR
 # Raw rocprofv3 output lands in OUTDIR/prof_*; then
 #   python gated_delta_amd/profile_summary.py OUTDIR
@@ -30,8 +30,12 @@ echo "== kernel trace + stats: python bench.py --mode prologue --steps 20 --no-c
 timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d "$OUT/prof_trace_pro" -o trace \
     -- python -u "$R/bench.py" --mode prologue --steps 20 --no-cpu \
     > "$OUT/prof_trace_pro.log" 2>&1 || exit $?
+echo "== kernel trace + stats: python bench.py --mode prefill_diag --steps 10 --no-cpu"
+timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d "$OUT/prof_trace_diag" -o trace \
+    -- python -u "$R/bench.py" --mode prefill_diag --steps 10 --no-cpu \
+    > "$OUT/prof_trace_diag.log" 2>&1 || exit $?
 for ctr in FETCH_SIZE WRITE_SIZE; do
-  for mode in prefill copy decode_tokens output_norm_gate prologue; do
+  for mode in prefill copy decode_tokens output_norm_gate prologue prefill_diag; do
     echo "== pmc $ctr: python bench.py --mode $mode --steps 2 --warmup 1 --no-cpu"
     timeout -s KILL 120 rocprofv3 --pmc $ctr --output-format csv -d "$OUT/prof_${ctr}_$mode" -o pmc \
         -- python -u "$R/bench.py" --mode $mode --steps 2 --warmup 1 --no-cpu \

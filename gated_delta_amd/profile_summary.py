@@ -12,6 +12,8 @@ Writes
       the same for the output norm and gate (bench --mode output_norm_gate);
   profiles/kernels_rda_prologue_T16384_H16.txt
       the same for the prologue (bench --mode prologue);
+  profiles/kernels_rda_prefill_diag_T16384_H16.txt
+      the same for the per-channel-decay prefill (bench --mode prefill_diag);
   profiles/hbm_traffic.txt
       FETCH_SIZE and WRITE_SIZE per dispatch of every prefill kernel, each
       scaled by what the same counter reads for a device copy of known size,
@@ -35,7 +37,8 @@ from gated_delta_amd.srchash import kernel_source_hash as source_hash  # noqa: E
 STAGE = {"chunk_table_kernel": "rda_chunk_table", "prep_bf16_kernel": "rda_prep",
          "walk_bf16_kernel": "rda_walk", "decode_step_kernel": "rda_decode_step",
          "decode_tokens_kernel": "rda_decode_tokens", "norm_gate_kernel": "rda_output_norm_gate",
-         "prologue_kernel": "rda_prologue"}
+         "prologue_kernel": "rda_prologue", "prep_diag_kernel": "rda_prep_diag",
+         "walk_diag_kernel": "rda_walk_diag"}
 
 
 def short(name: str) -> str:
@@ -133,6 +136,19 @@ def main():
              "#     -- python bench.py --mode prologue --steps 20 --no-cpu",
              "# then python gated_delta_amd/profile_summary.py OUTDIR"])
 
+    if os.path.isdir(os.path.join(out, "prof_trace_diag")):
+        kernel_table(
+            os.path.join(out, "prof_trace_diag"),
+            os.path.join(prof, "kernels_rda_prefill_diag_T16384_H16.txt"),
+            ["# rocprofv3 kernel trace, the per-channel-decay prefill: rda_prefill_diag on the",
+             "# long prompt, 16384 tokens x 16 heads (bf16 q/k/v, a decay per key channel,",
+             "# S0 ~ N(0, 0.02)): chunk table, prep_diag, walk_diag; 10 calls, each after a",
+             "# 512 MiB read (reduce_kernel: the cache flush)",
+             "# command: gated_delta_amd/profile_run.sh OUTDIR, whose fifth pass is",
+             "#   rocprofv3 --kernel-trace --stats --output-format csv -d OUTDIR/prof_trace_diag -o trace \\",
+             "#     -- python bench.py --mode prefill_diag --steps 10 --no-cpu",
+             "# then python gated_delta_amd/profile_summary.py OUTDIR"])
+
     # ---- HBM traffic -------------------------------------------------------------
     n = 1 << 30   # bytes the calibration copy reads and writes per launch
     f_copy = counter(os.path.join(out, "prof_FETCH_SIZE_copy"), "FETCH_SIZE")
@@ -146,7 +162,8 @@ def main():
     # the multi-token decode and the output norm and gate, from passes of
     # their own (only their own kernel: the flush and restores are not theirs)
     for mode, kern in (("decode_tokens", "decode_tokens_kernel"),
-                       ("output_norm_gate", "norm_gate_kernel"), ("prologue", "prologue_kernel")):
+                       ("output_norm_gate", "norm_gate_kernel"), ("prologue", "prologue_kernel"),
+                       ("prefill_diag", "prep_diag_kernel"), ("prefill_diag", "walk_diag_kernel")):
         fd = os.path.join(out, f"prof_FETCH_SIZE_{mode}")
         wd = os.path.join(out, f"prof_WRITE_SIZE_{mode}")
         if os.path.isdir(fd) and os.path.isdir(wd):
@@ -155,15 +172,16 @@ def main():
                 fetch[kern], write[kern] = fm[kern], wm[kern]
     lines = ["# HBM bytes per launch of the prefill kernels, RDA prefill T=16384 H=16 d=128",
              "# (bf16 q/k/v), of the one-pass multi-token decode (B=256 T=3 H=16), of the",
-             "# output norm and gate (262144 rows) and of the prologue (T=16384 H=16, conv",
-             "# width 4).  FETCH_SIZE and WRITE_SIZE (KiB per",
+             "# output norm and gate (262144 rows), of the prologue (T=16384 H=16, conv",
+             "# width 4) and of the per-channel-decay prefill's two kernels (T=16384 H=16).",
+             "# FETCH_SIZE and WRITE_SIZE (KiB per",
              "# dispatch) from one rocprofv3 --pmc pass each, scaled by what the same counter",
              "# reads for a plain device copy of 1 GiB (bench.py --mode copy):",
              f"#   copy FETCH_SIZE = {f_copy[fk]:.0f} KiB -> scale {f_scale:.3f};"
              f" copy WRITE_SIZE = {w_copy[wk]:.0f} KiB -> scale {w_scale:.3f}",
              "# command: gated_delta_amd/profile_run.sh OUTDIR (passes",
              "#   rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE --output-format csv -d OUTDIR/prof_<ctr>_<mode> -o pmc \\",
-             "#     -- python bench.py --mode prefill|copy|decode_tokens|output_norm_gate|prologue \\",
+             "#     -- python bench.py --mode prefill|copy|decode_tokens|output_norm_gate|prologue|prefill_diag \\",
              "#        --steps 2 --warmup 1 --no-cpu)",
              "# then python gated_delta_amd/profile_summary.py OUTDIR",
              f"source_hash = {source_hash()}",

@@ -78,6 +78,13 @@ def _load():
                                      ctypes.c_float, ctypes.c_float, p, i32, i32, i32, i32,
                                      p, p, p, p, p, p]
         lib.rda_prologue.restype = ctypes.c_int
+        lib.rda_prefill_diag_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        lib.rda_prefill_diag_workspace_bytes.restype = ctypes.c_size_t
+        lib.rda_prefill_diag.argtypes = pre[:18]
+        lib.rda_prefill_diag.restype = ctypes.c_int
+        lib.rda_decode_step_diag.argtypes = [p, p, p, ctypes.c_int, p, p, i32, i32, i32, i32,
+                                             p, p, p]
+        lib.rda_decode_step_diag.restype = ctypes.c_int
         lib.rda_chunk_table.argtypes = [p, i32, i32, p, p, p, p]
         lib.rda_chunk_table.restype = ctypes.c_int
         _lib = lib
@@ -438,3 +445,80 @@ def rda_prologue(x_q: torch.Tensor, x_k: torch.Tensor, x_v: torch.Tensor,
     if st != 0:
         raise RdaError(st, "rda_prologue")
     return q, k, v, a, b
+
+
+def rda_prefill_diag_workspace_bytes(num_seqs: int, total_tokens: int, num_heads: int,
+                                     dk: int = RDA_HEAD_DIM, dv: int = RDA_HEAD_DIM) -> int:
+    return int(_load().rda_prefill_diag_workspace_bytes(int(num_seqs), int(total_tokens),
+                                                        int(num_heads), int(dk), int(dv)))
+
+
+def rda_prefill_diag(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+                     b: torch.Tensor, *, cu_seqlens=None, S0: Optional[torch.Tensor] = None,
+                     o: Optional[torch.Tensor] = None, S_final: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None):
+    """Prefill with a per-key-channel decay (C entry point ``rda_prefill_diag``).
+
+    q, k, v [T, H, 128] bf16; alpha [T, H, 128] fp32 in (0, 1]; b [T, H]
+    fp32; the rest as in rda_prefill.  Returns (o, S_final).
+    """
+    lib_ = _load()
+    dev = q.device
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    if q.dtype != torch.bfloat16:
+        raise TypeError("rda_prefill_diag takes bfloat16 q, k, v")
+    for name, t in (("q", q), ("k", k)):
+        _need(t, name, torch.bfloat16, (T, H, dk), dev)
+    _need(v, "v", torch.bfloat16, (T, H, dv), dev)
+    _need(alpha, "alpha", torch.float32, (T, H, dk), dev)
+    _need(b, "b", torch.float32, (T, H), dev)
+    cu_dev, N = None, 1
+    if cu_seqlens is not None:
+        cu_np = check_cu_seqlens(cu_seqlens, T)
+        N = len(cu_np) - 1
+        cu_dev = torch.from_numpy(cu_np).to(dev)
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (N, H, dv, dk), dev)
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=torch.float32, device=dev)
+    _need(o, "o", torch.float32, (T, H, dv), dev)
+    if S_final is None:
+        S_final = torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev)
+    _need(S_final, "S_final", torch.float32, (N, H, dv, dk), dev)
+    need = rda_prefill_diag_workspace_bytes(N, T, H, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib_.rda_prefill_diag(_ptr(q), _ptr(k), _ptr(v), RDA_BF16, _ptr(alpha), _ptr(b),
+                               _ptr(cu_dev), N, T, H, dk, dv, _ptr(S0), _ptr(o), _ptr(S_final),
+                               _ptr(workspace), workspace.numel(), _stream_handle(stream))
+    if st != 0:
+        raise RdaError(st, "rda_prefill_diag")
+    return o, S_final
+
+
+def rda_decode_step_diag(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+                         b: torch.Tensor, S: torch.Tensor, *, o: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+    """One in-place decode step with a per-key-channel decay (C entry point
+    ``rda_decode_step_diag``): alpha [B, H, 128] fp32; the rest as in
+    rda_decode_step.  Returns o [B, H, 128] fp32."""
+    lib_ = _load()
+    dev = q.device
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _qkv_dtype(q)
+    _need(q, "q", q.dtype, (B, H, dk), dev)
+    _need(k, "k", q.dtype, (B, H, dk), dev)
+    _need(v, "v", q.dtype, (B, H, dv), dev)
+    _need(alpha, "alpha", torch.float32, (B, H, dk), dev)
+    _need(b, "b", torch.float32, (B, H), dev)
+    _need(S, "S", torch.float32, (B, H, dv, dk), dev)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=torch.float32, device=dev)
+    _need(o, "o", torch.float32, (B, H, dv), dev)
+    st = lib_.rda_decode_step_diag(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(alpha), _ptr(b), B, H,
+                                   dk, dv, _ptr(S), _ptr(o), _stream_handle(stream))
+    if st != 0:
+        raise RdaError(st, "rda_decode_step_diag")
+    return o

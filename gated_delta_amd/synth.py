@@ -259,6 +259,13 @@ def decode_tokens_inputs(B: int = 256, T: int = 3, H: int = 16, dk: int = 128,
     return DecodeTokensInputs(q, k, v, a, b, accept)
 
 
+def diag_alpha(T: int, H: int = 16, dk: int = 128, key=(10,)) -> np.ndarray:
+    """Per-channel decays [T, H, dk]: alpha = exp(-softplus(x)), x ~ N(-1,
+    1.5^2) per element (median about 0.73, a long tail of fast channels)."""
+    x = _rng(*key).standard_normal((T, H, dk)) * 1.5 - 1.0
+    return np.exp(-np.logaddexp(0.0, x)).astype(np.float32)
+
+
 @dataclass
 class EpilogueInputs:
     o: np.ndarray       # [rows, dv] float32, row scales spread over 1e-3 .. 1e2

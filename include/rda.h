@@ -19,7 +19,8 @@
  * (read-out after the update; no query scale; q and k are used as given --
  * callers L2-normalise them).  rda_prefill evaluates it for whole prompts in
  * chunks of 64 tokens (WY / UT-transform form on bf16 MFMA); rda_decode_step
- * applies one token in place; rda_decode_tokens applies a few (a verify of
+ * applies one token in place (both also with a per-channel decay:
+ * rda_prefill_diag, rda_decode_step_diag); rda_decode_tokens applies a few (a verify of
  * drafted tokens) in one pass over the state; rda_prologue produces their
  * inputs from the raw projections (short convolution, q/k norm, gates), and
  * rda_output_norm_gate is the block's output norm and gate on the mixer's
@@ -190,6 +191,37 @@ rda_status rda_decode_tokens(const void* q, const void* k, const void* v, rda_dt
                              const float* a, const float* b, int32_t batch, int32_t tokens,
                              int32_t num_heads, int32_t dk, int32_t dv, const float* S_in,
                              float* S_out, const int32_t* accept, float* o, hipStream_t stream);
+
+/*
+ * Per-channel (diagonal) decay: the variants of rda_prefill and
+ * rda_decode_step whose decay is a vector over the key channels,
+ * alpha_t in (0, 1]^dk, instead of one scalar per token and head.  The
+ * Raon-1 mini vLLM article calls RDA a modification of Kimi Delta Attention,
+ * whose decay is per channel, and the tiny-model card prints a low-rank
+ * decay projection whose output has the heads' key width.  The step, in the
+ * teardown's order:
+ *
+ *     S' = S_{t-1} diag(alpha_t),  e = v_t - S' k_t,  S_t = S' + b_t e k_t^T,
+ *     o_t = S_t q_t
+ *
+ * Arguments as in rda_prefill / rda_decode_step, with alpha [total_tokens, H,
+ * dk] (prefill) or [batch, H, dk] (decode) fp32 in place of a; the prefill
+ * takes bf16 q, k, v only (RDA_ERR_UNSUPPORTED for fp32) and its own
+ * workspace size.  Any alpha in (0, 1] is safe: the chunked prefill never
+ * forms a decay factor above e^60 (it falls back to exact per-element
+ * factors where a 16-token block decays by more than that).
+ */
+size_t rda_prefill_diag_workspace_bytes(int32_t num_seqs, int32_t total_tokens,
+                                        int32_t num_heads, int32_t dk, int32_t dv);
+rda_status rda_prefill_diag(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
+                            const float* alpha, const float* b, const int32_t* cu_seqlens,
+                            int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                            int32_t dk, int32_t dv, const float* S0, float* o, float* S_final,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+rda_status rda_decode_step_diag(const void* q, const void* k, const void* v,
+                                rda_dtype qkv_dtype, const float* alpha, const float* b,
+                                int32_t batch, int32_t num_heads, int32_t dk, int32_t dv,
+                                float* S, float* o, hipStream_t stream);
 
 /* Activation after the prologue's short convolution. */
 typedef enum {

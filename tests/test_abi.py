@@ -35,7 +35,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("rda_prefill", "rda_decode_step", "rda_decode_tokens", "rda_prefill_workspace_bytes",
+    for n in ("rda_prefill", "rda_decode_step", "rda_decode_tokens", "rda_prefill_diag",
+              "rda_decode_step_diag", "rda_prologue", "rda_output_norm_gate",
+              "rda_prefill_workspace_bytes",
               "rda_chunk_table", "rda_abi_version", "rda_status_string"):
         assert n in names
 
@@ -215,6 +217,46 @@ def test_prologue_rejects_bad_arguments(lib):
     assert pro(hout=P + 4 * GiB + 64) == ALIAS   # partial overlap
     assert pro(a=P + 6 * GiB) == ALIAS           # a over beta_raw
     assert pro(b=P + 12 * GiB + 16) == ALIAS     # b over a
+
+
+def test_prefill_diag_rejects_bad_arguments(lib):
+    rda.lib()
+
+    def pre(q=P, k=P + GiB, v=P + 2 * GiB, dt=0, al=P + 3 * GiB, b=P + 4 * GiB, cu=None, N=1,
+            T=100, H=2, dk=128, dv=128, S0=None, o=P + 5 * GiB, Sf=P + 6 * GiB,
+            ws=P + 7 * GiB, wsb=1 << 30):
+        return lib.rda_prefill_diag(q, k, v, dt, al, b, cu, N, T, H, dk, dv, S0, o, Sf, ws,
+                                    wsb, None)
+    assert pre(dt=1) == UNSUP                    # bf16 q, k, v only
+    assert pre(dt=3) == DTYPE
+    assert pre(T=-1) == SHAPE
+    assert pre(N=2) == SHAPE                     # several sequences need offsets
+    assert pre(dk=64) == UNSUP
+    assert pre(al=None) == NULL
+    assert pre(ws=None) == WS
+    assert pre(wsb=1024) == WS
+    assert pre(o=P + 5 * GiB + 4) == ALIGN
+    assert pre(o=P + 3 * GiB + 4096) == ALIAS    # o inside alpha
+    assert pre(Sf=P + 7 * GiB) == ALIAS          # S_final over the workspace
+    need = lib.rda_prefill_diag_workspace_bytes(1, 100, 2, 128, 128)
+    assert need > lib.rda_prefill_workspace_bytes(1, 100, 2, 128, 128)
+    assert lib.rda_prefill_diag_workspace_bytes(1, 100, 2, 64, 128) == 0
+
+
+def test_decode_diag_rejects_bad_arguments(lib):
+    rda.lib()
+
+    def dec(q=P, k=P + GiB, v=P + 2 * GiB, dt=0, al=P + 3 * GiB, b=P + 4 * GiB, B=4, H=2,
+            dk=128, dv=128, S=P + 5 * GiB, o=P + 6 * GiB):
+        return lib.rda_decode_step_diag(q, k, v, dt, al, b, B, H, dk, dv, S, o, None)
+    assert dec(B=0) == OK
+    assert dec(al=None) == NULL
+    assert dec(dt=3) == DTYPE
+    assert dec(B=1 << 26, H=16) == SHAPE
+    assert dec(dv=96) == UNSUP
+    assert dec(al=P + 3 * GiB + 8) == ALIGN
+    assert dec(S=P + 3 * GiB) == ALIAS          # S over alpha
+    assert dec(o=P + 5 * GiB + 512) == ALIAS    # o inside S
 
 
 def test_chunk_table_rejects_bad_arguments(lib):
