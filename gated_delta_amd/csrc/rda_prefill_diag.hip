@@ -20,7 +20,7 @@
 // chunk algebra when alpha is equal on every channel, and reproduces the
 // token-by-token recurrence in real arithmetic.
 //
-// PREP (parallel over chunk x head, 8 waves): G, the three decayed operands
+// PREP (parallel over chunk x head, 16 waves): G, the three decayed operands
 // K e^G, Q e^G and (K e^{G_C - G})^T packed as bf16 hi/lo MFMA operands,
 // L and A, the solve, T_b and A packed.  L and A are built from 16 x 16
 // sub-blocks on MFMA, each factored through a reference token r so that no
@@ -89,7 +89,7 @@ __device__ __forceinline__ void scaled_keys(const PrepDiagLds& S, const uint16_t
     split8(v, hi, lo);
 }
 
-constexpr int kPrepThreads = 512;
+constexpr int kPrepThreads = 1024;
 
 __global__ __launch_bounds__(kPrepThreads) void prep_diag_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ alpha,
@@ -105,50 +105,49 @@ __global__ __launch_bounds__(kPrepThreads) void prep_diag_kernel(
     const int w = wave_id(), l = tid & 63, g = l >> 4, c = l & 15;
     unsigned char* F = factors + (size_t(chunk) * H + h) * kDiagChunkHeadBytes;
 
-    // ---- stage K, Q (rows past the chunk's end are zero), b, zero T and A --
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-        const int p = tid + kPrepThreads * qq;
-        const int r = p >> 4, c8 = (p & 15) * 8;
-        u16x8 xk = {0, 0, 0, 0, 0, 0, 0, 0}, xq = xk;
-        if (r < len) {
-            xk = *reinterpret_cast<const u16x8*>(k + ((t0 + r) * H + h) * kD + c8);
-            xq = *reinterpret_cast<const u16x8*>(q + ((t0 + r) * H + h) * kD + c8);
-        }
-        *reinterpret_cast<u16x8*>(&S.K[r][c8]) = xk;
-        *reinterpret_cast<u16x8*>(&S.Q[r][c8]) = xq;
+    // ---- every global load of the workgroup first (one memory latency):
+    //      K, Q rows, b, and alpha for (channel, eighth of 8 tokens) ---------
+    u16x8 xk = {0, 0, 0, 0, 0, 0, 0, 0}, xq = xk;
+    const int sr = tid >> 4, sc8 = (tid & 15) * 8;
+    if (sr < len) {
+        xk = *reinterpret_cast<const u16x8*>(k + ((t0 + sr) * H + h) * kD + sc8);
+        xq = *reinterpret_cast<const u16x8*>(q + ((t0 + sr) * H + h) * kD + sc8);
     }
-    if (tid < kC) S.bb[tid] = tid < len ? b[(t0 + tid) * H + h] : 0.f;
+    const float bv = tid < len ? b[(t0 + tid) * H + h] : 0.f;
+    const int ch = tid & 127, qt = tid >> 7;
+    float al[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const int row = 8 * qt + r;
+        al[r] = row < len ? alpha[((t0 + row) * H + h) * kD + ch] : 1.f;
+    }
+    // ---- stage K, Q (rows past the chunk's end are zero), b; zero T and A;
+    //      G = running sum of log2(alpha) per channel, each eighth of the
+    //      chunk first on its own, then offset by the eighths before it
+    *reinterpret_cast<u16x8*>(&S.K[sr][sc8]) = xk;
+    *reinterpret_cast<u16x8*>(&S.Q[sr][sc8]) = xq;
+    if (tid < kC) S.bb[tid] = bv;
     for (int e = tid; e < kC * kFS; e += kPrepThreads) {
         S.T[e] = 0.f;
         S.A[e] = 0.f;
     }
-    // ---- G: running sum of log2(alpha) per channel; thread = (channel,
-    //      quarter of 16 tokens), then each quarter adds the ones before it
     {
-        const int ch = tid & 127, qt = tid >> 7;
-        float la[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = 16 * qt + r;
-            la[r] = row < len ? __builtin_amdgcn_logf(alpha[((t0 + row) * H + h) * kD + ch]) : 0.f;
-        }
         float run = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            run += fmaxf(la[r], -1000.f);   // beyond any fp32-visible decay; keeps G finite
-            S.G[16 * qt + r][ch] = run;
+        for (int r = 0; r < 8; ++r) {
+            // beyond any fp32-visible decay; keeps G finite
+            run += fmaxf(__builtin_amdgcn_logf(al[r]), -1000.f);
+            S.G[8 * qt + r][ch] = run;
         }
     }
     __syncthreads();
     {
-        const int ch = tid & 127, qt = tid >> 7;
         float base = 0.f;
-        for (int p = 0; p < qt; ++p) base += S.G[16 * p + 15][ch];
+        for (int p = 0; p < qt; ++p) base += S.G[8 * p + 7][ch];
         __syncthreads();
         if (qt > 0)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) S.G[16 * qt + r][ch] += base;
+            for (int r = 0; r < 8; ++r) S.G[8 * qt + r][ch] += base;
     }
     __syncthreads();
     // diagonal block w: is the decay across it within e^60 on every channel?
@@ -164,10 +163,9 @@ __global__ __launch_bounds__(kPrepThreads) void prep_diag_kernel(
     bf16x8* Kt = reinterpret_cast<bf16x8*>(F + kDOffKt);
     bf16x8* Qt = reinterpret_cast<bf16x8*>(F + kDOffQt);
     bf16x8* Kh = reinterpret_cast<bf16x8*>(F + kDOffKh);
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
+    {
         // (K e^G), (Q e^G): slot (token tile tt, key block m): row 16tt + lane % 16
-        const int idx = tid + kPrepThreads * qq;
+        const int idx = tid;
         const int lp = idx & 63, m = (idx >> 6) & 3, tt = idx >> 8, gp = lp >> 4;
         const int row = 16 * tt + (lp & 15);
         float vk[8], vq[8];
@@ -189,10 +187,9 @@ __global__ __launch_bounds__(kPrepThreads) void prep_diag_kernel(
         Qt[base] = hq;
         Qt[base + 64] = lq;
     }
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
+    {
         // (K e^{G_C - G})^T: slot (key tile kt, token block m): key 16kt + lane % 16
-        const int idx = tid + kPrepThreads * qq;
+        const int idx = tid;
         const int lp = idx & 63, m = (idx >> 6) & 1, kt = idx >> 7, gp = lp >> 4;
         const int key = 16 * kt + (lp & 15);
         const float gc = S.G[kC - 1][key];
@@ -260,7 +257,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_diag_kernel(
     // ---- T = (I + L)^-1, then T_b and A packed -------------------------------
     solve_unit_lower(S.L, S.T, S.R, w, g, c);
     if (tid < 256) pack_rows(S.T, S.bb, reinterpret_cast<bf16x8*>(F + kDOffTb), tid);
-    else pack_rows(S.A, nullptr, reinterpret_cast<bf16x8*>(F + kDOffA), tid - 256);
+    else if (tid < 512) pack_rows(S.A, nullptr, reinterpret_cast<bf16x8*>(F + kDOffA), tid - 256);
 }
 
 // ---------------------------------------------------------------------------
