@@ -592,24 +592,33 @@ def decode_tokens_measurements(args, out, torch, np, rda, synth, dev, stream, ti
     n_acc = float(np.mean(x.accept))
     tok_in = 3 * D * 2 + 2 * 4                  # bf16 q, k, v + fp32 a, b per token-head
     st_bytes = B * H * STATE_BYTES
+    # the per-channel decay variant: alpha [B, T, H, 128] fp32 in place of a
+    alpha = synth.diag_alpha(B * T, H, key=(11,)).reshape(B, T, H, D)
+    ald = torch.from_numpy(alpha).to(dev)
+    tok_in_diag = tok_in + (D - 1) * 4
     table = {
-        # name: (S_out, accept, o, algorithmic bytes)
-        "verify_commit_in_place": (S, acc, od, 2 * st_bytes + B * H * T * (tok_in + D * 4)),
-        "verify_only": (None, None, od, st_bytes + B * H * T * (tok_in + D * 4)),
-        "commit_only": (S, acc, None, 2 * st_bytes + B * H * n_acc * (tok_in - D * 2)),
+        # name: (entry point, decay, S_out, accept, o, algorithmic bytes)
+        "verify_commit_in_place": ("rda_decode_tokens", ad, S, acc, od,
+                                   2 * st_bytes + B * H * T * (tok_in + D * 4)),
+        "verify_only": ("rda_decode_tokens", ad, None, None, od,
+                        st_bytes + B * H * T * (tok_in + D * 4)),
+        "commit_only": ("rda_decode_tokens", ad, S, acc, None,
+                        2 * st_bytes + B * H * n_acc * (tok_in - D * 2)),
+        "diag_verify_commit_in_place": ("rda_decode_tokens_diag", ald, S, acc, od,
+                                        2 * st_bytes + B * H * T * (tok_in_diag + D * 4)),
     }
     res = {"B": B, "T": T, "H": H, "mean_accept": n_acc}
     S_copy = S.clone()
-    for name, (So, ac, o_, nbytes) in table.items():
+    for name, (fn, dec, So, ac, o_, nbytes) in table.items():
         if modes is not None and name not in modes:
             continue
         cargs = [rda._ptr(qd) if o_ is not None else None, rda._ptr(kd), rda._ptr(vd), 0,
-                 rda._ptr(ad), rda._ptr(bd), B, T, H, D, D, rda._ptr(S), rda._ptr(So),
+                 rda._ptr(dec), rda._ptr(bd), B, T, H, D, D, rda._ptr(S), rda._ptr(So),
                  rda._ptr(ac), rda._ptr(o_), stream.cuda_stream]
 
-        def call():
-            if rda.lib().rda_decode_tokens(*cargs) != 0:
-                raise RuntimeError("rda_decode_tokens failed")
+        def call(fn=fn, cargs=cargs):
+            if getattr(rda.lib(), fn)(*cargs) != 0:
+                raise RuntimeError(f"{fn} failed")
         sec = timed(call, reps, flush)
         S.copy_(S_copy)         # in-place modes advanced the states: restore them
         res[name] = {"us_per_call": sec * 1e6, "GBps": nbytes / sec / 1e9,
@@ -636,6 +645,18 @@ def decode_tokens_measurements(args, out, torch, np, rda, synth, dev, stream, ti
         res["parity_sampled"] = {
             "o_rel_l2": float(np.linalg.norm(og - ro[:, :, 0]) / np.linalg.norm(ro)),
             "S_rel_l2": float(np.linalg.norm(Sg - rS[:, 0]) / np.linalg.norm(rS))}
+        if "diag_verify_commit_in_place" in res:
+            S.copy_(S_copy)
+            rda.rda_decode_tokens_diag(qd, kd, vd, ald, bd, S, S_out=S, accept=acc, o=od,
+                                       stream=stream)
+            torch.cuda.synchronize()
+            ro, rS = oracle.decode_tokens_diag(sel(x.q), sel(x.k), sel(x.v), sel(alpha),
+                                               sel(x.b), S0[sb, sh][:, None], x.accept[sb])
+            og = od.cpu().numpy()[sb, :, sh].astype(np.float64)
+            Sg = S.cpu().numpy()[sb, sh].astype(np.float64)
+            res["diag_verify_commit_in_place"]["parity_sampled"] = {
+                "o_rel_l2": float(np.linalg.norm(og - ro[:, :, 0]) / np.linalg.norm(ro)),
+                "S_rel_l2": float(np.linalg.norm(Sg - rS[:, 0]) / np.linalg.norm(rS))}
     return res
 
 

@@ -234,10 +234,12 @@ rda_status rda_decode_step(const void* q, const void* k, const void* v, rda_dtyp
     return RDA_OK;
 }
 
-rda_status rda_decode_tokens(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
-                             const float* a, const float* b, int32_t batch, int32_t tokens,
-                             int32_t num_heads, int32_t dk, int32_t dv, const float* S_in,
-                             float* S_out, const int32_t* accept, float* o, hipStream_t stream) {
+static rda_status decode_tokens_any(const void* q, const void* k, const void* v,
+                                    rda_dtype qkv_dtype, const float* a, const float* b,
+                                    int32_t batch, int32_t tokens, int32_t num_heads, int32_t dk,
+                                    int32_t dv, const float* S_in, float* S_out,
+                                    const int32_t* accept, float* o, bool diag,
+                                    hipStream_t stream) {
     if (qkv_dtype != RDA_BF16 && qkv_dtype != RDA_FP32) return RDA_ERR_DTYPE;
     if (batch < 0 || tokens < 0 || tokens > RDA_DECODE_MAX_TOKENS) return RDA_ERR_SHAPE;
     rda_status st = check_dims(num_heads, dk, dv);
@@ -255,7 +257,8 @@ rda_status rda_decode_tokens(const void* q, const void* k, const void* v, rda_dt
     const size_t bh = size_t(batch) * num_heads;
     const size_t th = bh * size_t(tokens);
     const Range rq = rng(o ? q : nullptr, th * kD * esz), rk = rng(k, th * kD * esz);
-    const Range rv = rng(v, th * kD * esz), ra = rng(a, th * 4), rb = rng(b, th * 4);
+    const Range rv = rng(v, th * kD * esz), ra = rng(a, th * (diag ? kD : 1) * 4);
+    const Range rb = rng(b, th * 4);
     const Range rsi = rng(S_in, bh * kD * kD * 4), rso = rng(S_out, bh * kD * kD * 4);
     const Range racc = rng(accept, accept ? size_t(batch) * 4 : 0), ro = rng(o, th * kD * 4);
     for (Range in : {rq, rk, rv, ra, rb, rsi, rso, racc})
@@ -266,7 +269,7 @@ rda_status rda_decode_tokens(const void* q, const void* k, const void* v, rda_dt
     // zero tokens: the only work is copying S_in to a distinct S_out
     if (tokens == 0 && (!S_out || S_out == S_in)) return RDA_OK;
     if (launch_decode_tokens(q, k, v, qkv_dtype, a, b, batch, tokens, num_heads, S_in, S_out,
-                             accept, o, stream) != hipSuccess)
+                             accept, o, diag, stream) != hipSuccess)
         return RDA_ERR_HIP;
     return RDA_OK;
 }
@@ -476,6 +479,23 @@ rda_status rda_output_norm_gate(const float* o, const void* g, rda_dtype g_dtype
         hipSuccess)
         return RDA_ERR_HIP;
     return RDA_OK;
+}
+
+rda_status rda_decode_tokens(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
+                             const float* a, const float* b, int32_t batch, int32_t tokens,
+                             int32_t num_heads, int32_t dk, int32_t dv, const float* S_in,
+                             float* S_out, const int32_t* accept, float* o, hipStream_t stream) {
+    return decode_tokens_any(q, k, v, qkv_dtype, a, b, batch, tokens, num_heads, dk, dv, S_in,
+                             S_out, accept, o, false, stream);
+}
+
+rda_status rda_decode_tokens_diag(const void* q, const void* k, const void* v,
+                                  rda_dtype qkv_dtype, const float* alpha, const float* b,
+                                  int32_t batch, int32_t tokens, int32_t num_heads, int32_t dk,
+                                  int32_t dv, const float* S_in, float* S_out,
+                                  const int32_t* accept, float* o, hipStream_t stream) {
+    return decode_tokens_any(q, k, v, qkv_dtype, alpha, b, batch, tokens, num_heads, dk, dv,
+                             S_in, S_out, accept, o, true, stream);
 }
 
 rda_status rda_chunk_table(const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,

@@ -142,7 +142,7 @@ struct Raw4<float> {
     }
 };
 
-template <typename TIn, bool kOut>
+template <typename TIn, bool kOut, bool kDiag>
 __global__ __launch_bounds__(256) void decode_tokens_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const float* __restrict__ a, const float* __restrict__ b, int32_t tokens, int32_t heads,
@@ -181,6 +181,7 @@ __global__ __launch_bounds__(256) void decode_tokens_kernel(
     struct Tok {
         Raw4<TIn> k[2], q[kOut ? 2 : 1];
         float vr[4], av, bv;
+        f32x4 al[kDiag ? 2 : 1];   // per-channel decay of this lane's 8 columns
     };
     auto load_tok = [&](int tok, Tok& x) {
         const int64_t r = (seq * tokens + tok) * heads + h;
@@ -192,7 +193,13 @@ __global__ __launch_bounds__(256) void decode_tokens_kernel(
         }
 #pragma unroll
         for (int p = 0; p < 4; ++p) x.vr[p] = load1<TIn>(v + r * kD + rbase + 4 * p);
-        x.av = a[r];
+        if constexpr (kDiag) {
+            x.al[0] = *reinterpret_cast<const f32x4*>(a + r * kD + 4 * c);
+            x.al[1] = *reinterpret_cast<const f32x4*>(a + r * kD + 64 + 4 * c);
+            x.av = 1.f;
+        } else {
+            x.av = a[r];
+        }
         x.bv = b[r];
     };
     auto step = [&](int tok, const Tok& x) {
@@ -202,6 +209,15 @@ __global__ __launch_bounds__(256) void decode_tokens_kernel(
         if (kOut) {
             x.q[0].widen(qx);
             x.q[1].widen(qx + 4);
+        }
+        // the decayed state's products: per-channel decay folds into k and q
+        // (S diag(alpha) k = S (alpha . k)); the scalar one scales the sums
+        float ak[8], aq[8], dj[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            dj[j] = kDiag ? x.al[j >> 2][j & 3] : x.av;
+            ak[j] = kDiag ? dj[j] * kx[j] : kx[j];
+            aq[j] = kDiag && kOut ? dj[j] * qx[j] : qx[j];
         }
         float kap = 0.f;
         if (kOut) {
@@ -219,24 +235,25 @@ __global__ __launch_bounds__(256) void decode_tokens_kernel(
             float sk0 = 0.f, sk1 = 0.f, sq0 = 0.f, sq1 = 0.f;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                sk0 = fmaf(s[p][0][j], kx[j], sk0);
-                sk1 = fmaf(s[p][1][j], kx[4 + j], sk1);
+                sk0 = fmaf(s[p][0][j], ak[j], sk0);
+                sk1 = fmaf(s[p][1][j], ak[4 + j], sk1);
                 if (kOut) {
-                    sq0 = fmaf(s[p][0][j], qx[j], sq0);
-                    sq1 = fmaf(s[p][1][j], qx[4 + j], sq1);
+                    sq0 = fmaf(s[p][0][j], aq[j], sq0);
+                    sq1 = fmaf(s[p][1][j], aq[4 + j], sq1);
                 }
             }
             const float sk = dpp_sum16(sk0 + sk1);
-            const float e = x.vr[p] - x.av * sk;
+            const float e = x.vr[p] - (kDiag ? sk : x.av * sk);
             const float be = x.bv * e;
             if (kOut) {
-                const float orow = x.av * dpp_sum16(sq0 + sq1) + be * kap;
+                const float sq = dpp_sum16(sq0 + sq1);
+                const float orow = (kDiag ? sq : x.av * sq) + be * kap;
                 if (c == p) o_mine = orow;
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                s[p][0][j] = fmaf(x.av, s[p][0][j], be * kx[j]);
-                s[p][1][j] = fmaf(x.av, s[p][1][j], be * kx[4 + j]);
+                s[p][0][j] = fmaf(dj[j], s[p][0][j], be * kx[j]);
+                s[p][1][j] = fmaf(dj[4 + j], s[p][1][j], be * kx[4 + j]);
             }
         }
         if (kOut && c < 4) o[((seq * tokens + tok) * heads + h) * kD + rbase + 4 * c] = o_mine;
@@ -364,32 +381,34 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, rda_dtype 
     return hipGetLastError();
 }
 
+template <typename TIn, bool kDiag>
+void launch_tokens_t(const void* q, const void* k, const void* v, const float* a,
+                     const float* b, int32_t tokens, int32_t heads, const float* S_in,
+                     float* S_out, const int32_t* accept, float* o, unsigned grid,
+                     hipStream_t stream) {
+    const TIn* qt = static_cast<const TIn*>(q);
+    const TIn* kt = static_cast<const TIn*>(k);
+    const TIn* vt = static_cast<const TIn*>(v);
+    if (o)
+        hipLaunchKernelGGL((decode_tokens_kernel<TIn, true, kDiag>), dim3(grid), dim3(256), 0,
+                           stream, qt, kt, vt, a, b, tokens, heads, S_in, S_out, accept, o);
+    else
+        hipLaunchKernelGGL((decode_tokens_kernel<TIn, false, kDiag>), dim3(grid), dim3(256), 0,
+                           stream, qt, kt, vt, a, b, tokens, heads, S_in, S_out, accept, o);
+}
+
 hipError_t launch_decode_tokens(const void* q, const void* k, const void* v, rda_dtype dt,
                                 const float* a, const float* b, int32_t batch, int32_t tokens,
                                 int32_t heads, const float* S_in, float* S_out,
-                                const int32_t* accept, float* o, hipStream_t stream) {
+                                const int32_t* accept, float* o, bool diag, hipStream_t stream) {
     const unsigned grid = unsigned(2 * int64_t(batch) * heads);
     if (grid == 0) return hipSuccess;
     if (dt == RDA_BF16) {
-        const auto* q16 = static_cast<const uint16_t*>(q);
-        const auto* k16 = static_cast<const uint16_t*>(k);
-        const auto* v16 = static_cast<const uint16_t*>(v);
-        if (o)
-            hipLaunchKernelGGL((decode_tokens_kernel<uint16_t, true>), dim3(grid), dim3(256), 0,
-                               stream, q16, k16, v16, a, b, tokens, heads, S_in, S_out, accept, o);
-        else
-            hipLaunchKernelGGL((decode_tokens_kernel<uint16_t, false>), dim3(grid), dim3(256), 0,
-                               stream, q16, k16, v16, a, b, tokens, heads, S_in, S_out, accept, o);
+        if (diag) launch_tokens_t<uint16_t, true>(q, k, v, a, b, tokens, heads, S_in, S_out, accept, o, grid, stream);
+        else launch_tokens_t<uint16_t, false>(q, k, v, a, b, tokens, heads, S_in, S_out, accept, o, grid, stream);
     } else {
-        const auto* q32 = static_cast<const float*>(q);
-        const auto* k32 = static_cast<const float*>(k);
-        const auto* v32 = static_cast<const float*>(v);
-        if (o)
-            hipLaunchKernelGGL((decode_tokens_kernel<float, true>), dim3(grid), dim3(256), 0,
-                               stream, q32, k32, v32, a, b, tokens, heads, S_in, S_out, accept, o);
-        else
-            hipLaunchKernelGGL((decode_tokens_kernel<float, false>), dim3(grid), dim3(256), 0,
-                               stream, q32, k32, v32, a, b, tokens, heads, S_in, S_out, accept, o);
+        if (diag) launch_tokens_t<float, true>(q, k, v, a, b, tokens, heads, S_in, S_out, accept, o, grid, stream);
+        else launch_tokens_t<float, false>(q, k, v, a, b, tokens, heads, S_in, S_out, accept, o, grid, stream);
     }
     return hipGetLastError();
 }

@@ -85,10 +85,12 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, rda_dtype 
 
 // Several tokens per (batch, head); o == nullptr selects the commit-only
 // kernel (no outputs, stops after the accepted tokens).
+// diag: a is a per-key-channel decay [batch, tokens, H, 128] instead of a
+// scalar [batch, tokens, H].
 hipError_t launch_decode_tokens(const void* q, const void* k, const void* v, rda_dtype dt,
                                 const float* a, const float* b, int32_t batch, int32_t tokens,
                                 int32_t heads, const float* S_in, float* S_out,
-                                const int32_t* accept, float* o, hipStream_t stream);
+                                const int32_t* accept, float* o, bool diag, hipStream_t stream);
 
 // Prologue: raw q, k, v (bf16) -> conv, activation, q/k norm, write gate;
 // a, b from the gates; the conv history.  cu == nullptr: N sequences of L

@@ -71,6 +71,8 @@ def _load():
         lib.rda_decode_tokens.argtypes = [p, p, p, ctypes.c_int, p, p, i32, i32, i32, i32, i32,
                                           p, p, p, p, p]
         lib.rda_decode_tokens.restype = ctypes.c_int
+        lib.rda_decode_tokens_diag.argtypes = lib.rda_decode_tokens.argtypes
+        lib.rda_decode_tokens_diag.restype = ctypes.c_int
         lib.rda_output_norm_gate.argtypes = [p, p, ctypes.c_int, p, ctypes.c_float, i32,
                                              ctypes.c_int64, i32, p, ctypes.c_int, p]
         lib.rda_output_norm_gate.restype = ctypes.c_int
@@ -272,20 +274,7 @@ def rda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, a: torch.
 _NO_OUTPUT = object()
 
 
-def rda_decode_tokens(q: Optional[torch.Tensor], k: torch.Tensor, v: torch.Tensor,
-                      a: torch.Tensor, b: torch.Tensor, S_in: torch.Tensor, *,
-                      S_out: Optional[torch.Tensor] = None,
-                      accept: Optional[torch.Tensor] = None, o=None,
-                      stream=None) -> Optional[torch.Tensor]:
-    """Several tokens per sequence in one pass (C entry point ``rda_decode_tokens``).
-
-    q, k, v [B, T, H, 128] (bf16 or fp32), a, b [B, T, H] fp32, S_in
-    [B, H, 128, 128] fp32.  S_out (same shape, may be S_in itself) receives
-    the state after the first accept[n] tokens of each sequence (accept
-    int32 [B] on the device, None = all T); S_out=None leaves every state
-    unchanged.  Returns o [B, T, H, 128] fp32 for every token, or None when
-    called with o=False (commit only: q is then not read and may be None).
-    """
+def _decode_tokens(name, q, k, v, a, b, S_in, S_out, accept, o, stream, diag):
     lib_ = _load()
     dev = k.device
     if k.dim() != 4:
@@ -300,7 +289,10 @@ def rda_decode_tokens(q: Optional[torch.Tensor], k: torch.Tensor, v: torch.Tenso
         _need(q, "q", k.dtype, (B, T, H, dk), dev)
     _need(k, "k", k.dtype, (B, T, H, dk), dev)
     _need(v, "v", k.dtype, (B, T, H, dv), dev)
-    _need(a, "a", torch.float32, (B, T, H), dev)
+    if diag:
+        _need(a, "alpha", torch.float32, (B, T, H, dk), dev)
+    else:
+        _need(a, "a", torch.float32, (B, T, H), dev)
     _need(b, "b", torch.float32, (B, T, H), dev)
     _need(S_in, "S_in", torch.float32, (B, H, dv, dk), dev)
     if S_out is not None:
@@ -313,12 +305,42 @@ def rda_decode_tokens(q: Optional[torch.Tensor], k: torch.Tensor, v: torch.Tenso
         _need(o, "o", torch.float32, (B, T, H, dv), dev)
     else:
         o = None
-    st = lib_.rda_decode_tokens(_ptr(q) if want_o else None, _ptr(k), _ptr(v), dt, _ptr(a),
-                                _ptr(b), B, T, H, dk, dv, _ptr(S_in), _ptr(S_out),
-                                _ptr(accept), _ptr(o), _stream_handle(stream))
+    st = getattr(lib_, name)(_ptr(q) if want_o else None, _ptr(k), _ptr(v), dt, _ptr(a),
+                             _ptr(b), B, T, H, dk, dv, _ptr(S_in), _ptr(S_out),
+                             _ptr(accept), _ptr(o), _stream_handle(stream))
     if st != 0:
-        raise RdaError(st, "rda_decode_tokens")
+        raise RdaError(st, name)
     return o
+
+
+def rda_decode_tokens(q: Optional[torch.Tensor], k: torch.Tensor, v: torch.Tensor,
+                      a: torch.Tensor, b: torch.Tensor, S_in: torch.Tensor, *,
+                      S_out: Optional[torch.Tensor] = None,
+                      accept: Optional[torch.Tensor] = None, o=None,
+                      stream=None) -> Optional[torch.Tensor]:
+    """Several tokens per sequence in one pass (C entry point ``rda_decode_tokens``).
+
+    q, k, v [B, T, H, 128] (bf16 or fp32), a, b [B, T, H] fp32, S_in
+    [B, H, 128, 128] fp32.  S_out (same shape, may be S_in itself) receives
+    the state after the first accept[n] tokens of each sequence (accept
+    int32 [B] on the device, None = all T); S_out=None leaves every state
+    unchanged.  Returns o [B, T, H, 128] fp32 for every token, or None when
+    called with o=False (commit only: q is then not read and may be None).
+    """
+    return _decode_tokens("rda_decode_tokens", q, k, v, a, b, S_in, S_out, accept, o, stream,
+                          False)
+
+
+def rda_decode_tokens_diag(q: Optional[torch.Tensor], k: torch.Tensor, v: torch.Tensor,
+                           alpha: torch.Tensor, b: torch.Tensor, S_in: torch.Tensor, *,
+                           S_out: Optional[torch.Tensor] = None,
+                           accept: Optional[torch.Tensor] = None, o=None,
+                           stream=None) -> Optional[torch.Tensor]:
+    """rda_decode_tokens with a per-key-channel decay (C entry point
+    ``rda_decode_tokens_diag``): alpha [B, T, H, 128] fp32 in place of a;
+    everything else as in rda_decode_tokens."""
+    return _decode_tokens("rda_decode_tokens_diag", q, k, v, alpha, b, S_in, S_out, accept, o,
+                          stream, True)
 
 
 def rda_chunk_table(cu_seqlens, num_seqs: int, total_tokens: int, device="cuda",

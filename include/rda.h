@@ -21,7 +21,8 @@
  * chunks of 64 tokens (WY / UT-transform form on bf16 MFMA); rda_decode_step
  * applies one token in place (both also with a per-channel decay:
  * rda_prefill_diag, rda_decode_step_diag); rda_decode_tokens applies a few (a verify of
- * drafted tokens) in one pass over the state; rda_prologue produces their
+ * drafted tokens) in one pass over the state (rda_decode_tokens_diag with the
+ * per-channel decay); rda_prologue produces their
  * inputs from the raw projections (short convolution, q/k norm, gates), and
  * rda_output_norm_gate is the block's output norm and gate on the mixer's
  * output.
@@ -222,6 +223,18 @@ rda_status rda_decode_step_diag(const void* q, const void* k, const void* v,
                                 rda_dtype qkv_dtype, const float* alpha, const float* b,
                                 int32_t batch, int32_t num_heads, int32_t dk, int32_t dv,
                                 float* S, float* o, hipStream_t stream);
+/*
+ * rda_decode_tokens with the per-channel decay: alpha [batch, tokens, H, dk]
+ * fp32 in place of a (token t of sequence n, head h at row
+ * (n * tokens + t) * H + h), every other argument, layout, accept rule and
+ * error as in rda_decode_tokens.  Its result equals rda_prefill_diag over the
+ * same tokens taken as batch sequences of `tokens` tokens each.
+ */
+rda_status rda_decode_tokens_diag(const void* q, const void* k, const void* v,
+                                  rda_dtype qkv_dtype, const float* alpha, const float* b,
+                                  int32_t batch, int32_t tokens, int32_t num_heads, int32_t dk,
+                                  int32_t dv, const float* S_in, float* S_out,
+                                  const int32_t* accept, float* o, hipStream_t stream);
 
 /* Activation after the prologue's short convolution. */
 typedef enum {

@@ -81,6 +81,10 @@ class Oracle:
     def decode_tokens(self, q, k, v, a, b, S_in, accept=None, threads: int = 0):
         return _decode_tokens(self.lib, q, k, v, a, b, S_in, accept, threads)
 
+    def decode_tokens_diag(self, q, k, v, alpha, b, S_in, accept=None, threads: int = 0):
+        return _decode_tokens(self.lib, q, k, v, alpha, b, S_in, accept, threads,
+                              prefill=_prefill_diag)
+
     def prefill_diag(self, q, k, v, alpha, b, cu_seqlens=None, S0=None, threads: int = 0):
         return _prefill_diag(self.lib, q, k, v, alpha, b, cu_seqlens, S0, threads)
 
@@ -132,6 +136,12 @@ def decode_step(q, k, v, a, b, S, threads: int = 0):
 def decode_tokens(q, k, v, a, b, S_in, accept=None, threads: int = 0):
     """Several tokens per sequence with the default build (see _decode_tokens)."""
     return default().decode_tokens(q, k, v, a, b, S_in, accept, threads)
+
+
+def decode_tokens_diag(q, k, v, alpha, b, S_in, accept=None, threads: int = 0):
+    """Several tokens per sequence with a per-key-channel decay alpha
+    [B, T, H, dk] (see _decode_tokens and _prefill_diag)."""
+    return default().decode_tokens_diag(q, k, v, alpha, b, S_in, accept, threads)
 
 
 def prefill_diag(q, k, v, alpha, b, cu_seqlens=None, S0=None, threads: int = 0):
@@ -314,7 +324,7 @@ def _decode_step(lib, q, k, v, a, b, S, threads: int = 0):
     return o
 
 
-def _decode_tokens(lib, q, k, v, a, b, S_in, accept=None, threads: int = 0):
+def _decode_tokens(lib, q, k, v, a, b, S_in, accept=None, threads: int = 0, prefill=None):
     """Several tokens per sequence: the verify of drafted tokens.
 
     The "Raon-1-nano-gguf" model card runs the model with multi-token
@@ -325,9 +335,11 @@ def _decode_tokens(lib, q, k, v, a, b, S_in, accept=None, threads: int = 0):
     token's output and S the state after the first accept[n] tokens.
 
     q, k: [B, T, H, dk]; v: [B, T, H, dv]; a, b: [B, T, H]; S_in: [B, H, dv, dk];
-    accept: ints [B] in [0, T], or None for T.
+    accept: ints [B] in [0, T], or None for T.  `prefill` is the recurrence
+    the tokens run through (_prefill, or _prefill_diag with a [B, T, H, dk]).
     Returns (o [B, T, H, dv] float64, S [B, H, dv, dk] float64).
     """
+    prefill = _prefill if prefill is None else prefill
     q, k, v, a, b = (_f32(x) for x in (q, k, v, a, b))
     B, T, H, dk = q.shape
     dv = v.shape[3]
@@ -341,10 +353,10 @@ def _decode_tokens(lib, q, k, v, a, b, S_in, accept=None, threads: int = 0):
 
     every = np.arange(B * T)
     cu = (T * np.arange(B + 1)).astype(np.int32)
-    o, _ = _prefill(lib, *(packed(x, every) for x in (q, k, v, a, b)), cu_seqlens=cu,
+    o, _ = prefill(lib, *(packed(x, every) for x in (q, k, v, a, b)), cu_seqlens=cu,
                     S0=S_in, threads=threads)
     kept = np.concatenate([n * T + np.arange(acc[n]) for n in range(B)] + [np.zeros(0, int)])
     cu_kept = np.concatenate([[0], np.cumsum(acc)]).astype(np.int32)
-    _, S = _prefill(lib, *(packed(x, kept) for x in (q, k, v, a, b)), cu_seqlens=cu_kept,
+    _, S = prefill(lib, *(packed(x, kept) for x in (q, k, v, a, b)), cu_seqlens=cu_kept,
                     S0=S_in, threads=threads)
     return o.reshape(B, T, H, dv), S

@@ -546,10 +546,38 @@ def pin_diag_decode_and_varlen(orc):
         _close(s[n], sn[0], 1e-14, f"diag varlen S seq {n}")
 
 
+def pin_diag_decode_tokens(orc):
+    """Several tokens per sequence with a per-channel decay equal that many
+    per-channel decode steps, the committed state the one after the accepted
+    tokens; a decay equal on every channel gives the scalar decode_tokens."""
+    rng = _rng(31)
+    B, T, H, dk, dv = 4, 3, 2, 6, 5
+    q, k, v, alpha, b, _ = _diag_case(rng, B * T, H, dk, dv)
+    q, k, v, alpha = (x.reshape(B, T, H, -1) for x in (q, k, v, alpha))
+    b = b.reshape(B, T, H)
+    S_in = rng.standard_normal((B, H, dv, dk))
+    accept = np.array([2, 0, 3, 1])
+    o, S = orc.decode_tokens_diag(q, k, v, alpha, b, S_in, accept)
+    Sd = np.ascontiguousarray(S_in.copy())
+    for t in range(T):
+        ot = orc.decode_step_diag(q[:, t], k[:, t], v[:, t], alpha[:, t], b[:, t], Sd)
+        _close(o[:, t], ot, 1e-13, f"decode_tokens_diag o token {t}")
+        for n in range(B):
+            if accept[n] == t + 1:
+                _close(S[n], Sd[n], 1e-13, f"decode_tokens_diag state seq {n}")
+    assert np.array_equal(S[1], S_in[1])
+    a = alpha[..., 0].copy()
+    flat = _f32(np.repeat(a[..., None], dk, axis=3))
+    o1, S1 = orc.decode_tokens_diag(q, k, v, flat, b, S_in, accept)
+    o2, S2 = orc.decode_tokens(q, k, v, a, b, S_in, accept)
+    _close(o1, o2, 1e-13, "decode_tokens_diag, channel-constant decay: o")
+    _close(S1, S2, 1e-13, "decode_tokens_diag, channel-constant decay: S")
+
+
 ALL_PINS = [pin_bruteforce, pin_exact_dyadic, pin_hand_example, pin_identity_gates,
             pin_readback, pin_pure_decay, pin_single_step, pin_linearity, pin_rotation,
             pin_permutation, pin_norm_bound, pin_resume, pin_varlen,
             pin_decode_equals_prefill, pin_decode_tokens, pin_norm_gate_library,
             pin_norm_gate_closed_forms, pin_prologue_library, pin_prologue_gates,
             pin_prologue_history, pin_diag_scalar_special_case, pin_diag_product_form,
-            pin_diag_channel_separation, pin_diag_decode_and_varlen]
+            pin_diag_channel_separation, pin_diag_decode_and_varlen, pin_diag_decode_tokens]

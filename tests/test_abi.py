@@ -36,7 +36,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("rda_prefill", "rda_decode_step", "rda_decode_tokens", "rda_prefill_diag",
-              "rda_decode_step_diag", "rda_prologue", "rda_output_norm_gate",
+              "rda_decode_step_diag", "rda_decode_tokens_diag", "rda_prologue", "rda_output_norm_gate",
               "rda_prefill_workspace_bytes",
               "rda_chunk_table", "rda_abi_version", "rda_status_string"):
         assert n in names
@@ -151,6 +151,23 @@ def test_decode_tokens_rejects_bad_arguments(lib):
     assert dec(So=P + 5 * GiB + 1024) == ALIAS   # S_out partly over S_in
     assert dec(acc=P + 6 * GiB + 16) == ALIAS    # accept inside o
     assert dec(So=P + 7 * GiB, acc=P + 7 * GiB + 4096) == ALIAS  # accept inside S_out
+
+
+def test_decode_tokens_diag_rejects_bad_arguments(lib):
+    def dec(q=P, k=P + GiB, v=P + 2 * GiB, dt=0, al=P + 3 * GiB, b=P + 4 * GiB, B=4, T=3, H=2,
+            dk=128, dv=128, Si=P + 5 * GiB, So=P + 5 * GiB, acc=None, o=P + 6 * GiB):
+        return lib.rda_decode_tokens_diag(q, k, v, dt, al, b, B, T, H, dk, dv, Si, So, acc, o,
+                                          None)
+    assert dec(B=0) == OK
+    assert dec(al=None) == NULL
+    assert dec(Si=None) == NULL
+    assert dec(dt=3) == DTYPE
+    assert dec(T=65) == SHAPE
+    assert dec(dk=64) == UNSUP
+    assert dec(al=P + 3 * GiB + 4) == ALIGN
+    # alpha holds B * T * H * dk floats (12 KiB here), not B * T * H as a does
+    assert dec(o=P + 3 * GiB + 8192) == ALIAS
+    assert dec(So=P + 3 * GiB + 8192) == ALIAS
 
 
 def test_output_norm_gate_rejects_bad_arguments(lib):
