@@ -20,8 +20,8 @@ Prints ONE JSON line:
   parity     rel-L2 / max-abs of this run's prefill output vs the oracle
 The oracle runs only in this CPU leg (skipped with --no-cpu): the baseline
 timing, and the parity figures of this run's outputs (parity, and the parity
-entries of other_prefill_workloads, prefill_diag, prologue,
-output_norm_gate and decode_tokens).
+entries of other_prefill_workloads, prefill_segmented, prefill_diag,
+prologue, output_norm_gate and decode_tokens).
   also       the prefill back to back without the flush (ms_per_call_unflushed)
              and after a read-only 512 MiB flush (ms_per_call_read_flushed),
              the practical HBM rate of an in-place read-modify-write of 256 MiB
@@ -38,7 +38,9 @@ output_norm_gate and decode_tokens).
              whole block -- prologue, prefill, output norm and gate -- as
              tokens/s (output_norm_gate.block_tokens_per_s); the long prompt
              with a per-channel decay and the per-channel decode step
-             (prefill_diag)
+             (prefill_diag); the long prompt with 1, 2 and 4 of its heads
+             (one GPU's share under head sharding), segmented state pass
+             against the one-pass walk (prefill_segmented)
 
 Usage: python bench.py [--gpus 1] [--steps 128] [--warmup 5] [--no-cpu]
 """
@@ -75,14 +77,16 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0 = all)")
     ap.add_argument("--mode", choices=["bench", "prefill", "decode", "decode_tokens",
-                                       "output_norm_gate", "prologue", "prefill_diag", "copy"],
+                                       "output_norm_gate", "prologue", "prefill_diag",
+                                       "segments", "copy"],
                     default="bench",
                     help="prefill/decode: run only that part (for profiling); decode_tokens / "
-                         "output_norm_gate / prologue / prefill_diag: only the one-pass "
-                         "multi-token decode / the output norm and gate / the long prompt's "
-                         "prologue / its per-channel-decay prefill, --steps calls after a cache "
-                         "flush each; copy: a plain device copy of known size (counter "
-                         "calibration)")
+                         "output_norm_gate / prologue / prefill_diag / segments: only the "
+                         "one-pass multi-token decode / the output norm and gate / the long "
+                         "prompt's prologue / its per-channel-decay prefill / its first two "
+                         "heads through the segmented and the one-pass state pass, --steps "
+                         "calls after a cache flush each; copy: a plain device copy of known "
+                         "size (counter calibration)")
     ap.add_argument("--no-extras", action="store_true",
                     help="only the timed steps and the per-stage calls (the kernel trace "
                          "of exactly what the kernels entry reports)")
@@ -146,7 +150,8 @@ def main():
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
-    if args.mode in ("decode_tokens", "output_norm_gate", "prologue", "prefill_diag"):
+    if args.mode in ("decode_tokens", "output_norm_gate", "prologue", "prefill_diag",
+                     "segments"):
         timed = make_timer(torch, np, stream)
         flush_buf = torch.ones((128 << 20,), dtype=torch.float32, device=dev)
         flush = lambda: flush_buf.sum()
@@ -157,6 +162,9 @@ def main():
         elif args.mode == "output_norm_gate":
             res = epilogue_measurements(args, {}, torch, np, rda, synth, dev, timed, flush,
                                         16384, 16, reps=args.steps)
+        elif args.mode == "segments":
+            res = segment_measurements(args, torch, np, rda, synth, dev, stream, timed, flush,
+                                       reps=args.steps, heads=(2,))
         elif args.mode == "prologue":
             res = prologue_measurements(args, {}, torch, np, rda, synth, dev, timed, flush,
                                         16384, 16, reps=args.steps, decode=False)
@@ -433,6 +441,8 @@ def extra_measurements(args, out, torch, np, rda, synth, dev, stream, q, k, v, a
         if cid == 4:
             entry["lengths"] = [int(x) for x in np.diff(cuc)]
     out["other_prefill_workloads"] = configs
+    out["prefill_segmented"] = segment_measurements(args, torch, np, rda, synth, dev, stream,
+                                                    timed, flush)
     out["prefill_diag"] = diag_measurements(args, out, torch, np, rda, synth, dev, timed, flush)
     out["prologue"] = prologue_measurements(args, out, torch, np, rda, synth, dev, timed, flush,
                                             T, H)
@@ -572,6 +582,55 @@ def epilogue_measurements(args, out, torch, np, rda, synth, dev, timed, flush, T
         res["parity_sampled"] = {"rel_l2": float(np.linalg.norm(got - ref) / np.linalg.norm(ref)),
                                  "max_rel": float(np.max(np.abs(got - ref) /
                                                          np.maximum(np.abs(ref), 1e-30)))}
+    return res
+
+
+def segment_measurements(args, torch, np, rda, synth, dev, stream, timed, flush, reps=10,
+                         heads=(1, 2, 4)):
+    """The long prompt (T = 16384) with few heads -- one GPU's share of its 16
+    heads at 16-, 8- and 4-way head sharding -- where rda_prefill takes the
+    segmented state pass (one sequence, no offsets).  Timed beside the
+    one-pass walk on the same inputs (cu_seqlens = [0, T] selects it), each
+    call after the read-only flush; parity of the segmented call against the
+    oracle."""
+    p = synth.config3()
+    T = p.total_tokens
+    res = {"T": T}
+    cu_one = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    for H in heads:
+        sl = lambda x: np.ascontiguousarray(x[:, :H])
+        qh, kh, vh = (torch.from_numpy(sl(getattr(p, n))).to(torch.bfloat16).to(dev) for n in "qkv")
+        ah, bh = torch.from_numpy(sl(p.a)).to(dev), torch.from_numpy(sl(p.b)).to(dev)
+        S0h = torch.from_numpy(np.ascontiguousarray(p.S0[:, :H])).to(dev)
+        oh = torch.empty((T, H, D), dtype=torch.float32, device=dev)
+        Sfh = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
+        ws = torch.empty(rda.rda_prefill_workspace_bytes(1, T, H), dtype=torch.uint8, device=dev)
+        entry = {}
+        for name, cu in (("segmented", None), ("one_pass", cu_one)):
+            cargs = [rda._ptr(qh), rda._ptr(kh), rda._ptr(vh), 0, rda._ptr(ah), rda._ptr(bh),
+                     rda._ptr(cu), 1, T, H, D, D, rda._ptr(S0h), rda._ptr(oh), rda._ptr(Sfh),
+                     rda._ptr(ws), ws.numel(), stream.cuda_stream]
+
+            def call(cargs=cargs):
+                if rda.lib().rda_prefill(*cargs) != 0:
+                    raise RuntimeError("rda_prefill failed")
+            call()
+            sec = timed(call, reps, flush)
+            entry[name] = {"ms_per_call": sec * 1e3, "tokens_per_s": T / sec}
+        entry["speedup"] = entry["one_pass"]["ms_per_call"] / entry["segmented"]["ms_per_call"]
+        if not args.no_cpu and H == 2:
+            import oracle
+            torch.cuda.synchronize()
+            rda.rda_prefill(qh, kh, vh, ah, bh, S0=S0h, o=oh, S_final=Sfh, workspace=ws,
+                            stream=stream)
+            torch.cuda.synchronize()
+            ro, rS = oracle.prefill(sl(p.q), sl(p.k), sl(p.v), sl(p.a), sl(p.b),
+                                    S0=np.ascontiguousarray(p.S0[:, :H]), threads=args.cpu_threads)
+            og = oh.cpu().numpy().astype(np.float64)
+            Sg = Sfh.cpu().numpy().astype(np.float64)
+            entry["parity"] = {"o_rel_l2": float(np.linalg.norm(og - ro) / np.linalg.norm(ro)),
+                               "S_rel_l2": float(np.linalg.norm(Sg - rS) / np.linalg.norm(rS))}
+        res[f"H{H}"] = entry
     return res
 
 

@@ -30,6 +30,42 @@ bool overlap(Range x, Range y) {
 
 constexpr int kWalkSlices = kD / 16;  // value-channel slices per (sequence, head)
 
+// The segmented state pass for one long sequence with few heads.  The walk
+// is sequential over chunks and gives each (sequence, head) 8 workgroups, so
+// a few heads leave most of the 256 CUs idle whatever the length.  Cut into
+// P segments, the sequence is walked three times as long in total but P
+// times shorter in sequence: (1) every segment from zero (its end state E_p)
+// and from the identity with zero values (its transition M_p) in one launch
+// (2 x 8 x P x H workgroups, no outputs), (2) the combine chains the
+// segments, S_in[p + 1] = S_in[p] M_p + E_p, (3) every segment again from its
+// true starting state, with outputs.  Worth it when P >= 4; P fills the
+// chip in the first pass and keeps segments at >= 16 chunks.
+constexpr int kSegCUs = 256;
+constexpr int kSegMinChunks = 16;
+constexpr int kSegMax = 16;
+
+struct SegPlan {
+    int P = 0;     // segments (0: no segmented pass)
+    int cps = 0;   // chunks per segment (the last may be shorter)
+};
+
+SegPlan seg_plan(int32_t num_seqs, int32_t total_tokens, int32_t heads) {
+    SegPlan sp;
+    if (num_seqs != 1 || total_tokens <= 0 || heads <= 0) return sp;
+    const int64_t nch = (int64_t(total_tokens) + kC - 1) / kC;
+    int64_t P = kSegCUs / (2 * kWalkSlices * int64_t(heads));
+    P = P < nch / kSegMinChunks ? P : nch / kSegMinChunks;
+    P = P < kSegMax ? P : kSegMax;
+    if (P < 4) return sp;
+    sp.cps = int((nch + P - 1) / P);
+    sp.P = int((nch + sp.cps - 1) / sp.cps);
+    return sp;
+}
+
+size_t seg_state_bytes(const SegPlan& sp, int32_t heads) {
+    return size_t(sp.P) * heads * kD * kD * sizeof(float);
+}
+
 rda_status check_dims(int32_t heads, int32_t dk, int32_t dv) {
     if (heads <= 0 || dk <= 0 || dv <= 0) return RDA_ERR_SHAPE;
     if (dk != kD || dv != kD) return RDA_ERR_UNSUPPORTED;
@@ -54,6 +90,8 @@ struct Prefill {
     float *o, *S_final;
     int32_t *rec, *seq_off, *nch;
     unsigned char* factors;
+    SegPlan seg;          // used when the input is one bf16 sequence without offsets
+    float *E, *F, *S_in;  // segmented pass: end states from zero, transitions, starts
 };
 
 rda_status check_prefill(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
@@ -102,7 +140,17 @@ rda_status check_prefill(const void* q, const void* k, const void* v, rda_dtype 
                 S0, o, S_final,
                 reinterpret_cast<int32_t*>(ws + tl.rec_off),
                 reinterpret_cast<int32_t*>(ws + tl.seq_off_off),
-                reinterpret_cast<int32_t*>(ws + tl.num_off), ws + align256(tl.bytes)};
+                reinterpret_cast<int32_t*>(ws + tl.num_off), ws + align256(tl.bytes),
+                SegPlan{}, nullptr, nullptr, nullptr};
+    const SegPlan sp = seg_plan(num_seqs, total_tokens, num_heads);
+    if (sp.P > 0 && cu_seqlens == nullptr && qkv_dtype == RDA_BF16) {
+        unsigned char* seg = P.factors + size_t(mc) * num_heads * kChunkHeadBytes;
+        const size_t sb = seg_state_bytes(sp, num_heads);
+        P.seg = sp;
+        P.E = reinterpret_cast<float*>(seg);
+        P.F = reinterpret_cast<float*>(seg + sb);
+        P.S_in = reinterpret_cast<float*>(seg + 2 * sb);
+    }
     return RDA_OK;
 }
 
@@ -134,9 +182,24 @@ rda_status prefill_sequential(const Prefill& P, hipStream_t stream, hipEvent_t c
     }
     if ((st = record(ev, 2 * RDA_STAGE_PREP + 1, stream)) != RDA_OK) return st;
     if ((st = record(ev, 2 * RDA_STAGE_WALK, stream)) != RDA_OK) return st;
-    if (launch_walk(P.q, P.k, P.v, P.dt, P.N, P.H, P.rec, P.seq_off, P.nch, P.factors, P.S0, P.o,
-                    P.S_final, stream) != hipSuccess)
+    if (P.seg.P > 0) {
+        // the segmented pass: both first-pass jobs, the combine, the output pass
+        const auto* q16 = static_cast<const uint16_t*>(P.q);
+        const auto* k16 = static_cast<const uint16_t*>(P.k);
+        const auto* v16 = static_cast<const uint16_t*>(P.v);
+        const WalkJob first[2] = {{nullptr, P.E, 0, 0}, {nullptr, P.F, 1, 1}};
+        const WalkJob last{P.S_in, nullptr, 0, 0};
+        if (launch_walk_bf16(q16, k16, v16, P.seg.P, P.H, P.rec, P.seq_off, P.nch, P.factors,
+                             nullptr, first, 2, P.seg.cps, false, stream) != hipSuccess ||
+            launch_segment_combine(P.S0, P.E, P.F, P.S_in, P.S_final, P.seg.P, P.H, stream) !=
+                hipSuccess ||
+            launch_walk_bf16(q16, k16, v16, P.seg.P, P.H, P.rec, P.seq_off, P.nch, P.factors,
+                             P.o, &last, 1, P.seg.cps, true, stream) != hipSuccess)
+            return RDA_ERR_HIP;
+    } else if (launch_walk(P.q, P.k, P.v, P.dt, P.N, P.H, P.rec, P.seq_off, P.nch, P.factors,
+                           P.S0, P.o, P.S_final, stream) != hipSuccess) {
         return RDA_ERR_HIP;
+    }
     if ((st = record(ev, 2 * RDA_STAGE_WALK + 1, stream)) != RDA_OK) return st;
     return RDA_OK;
 }
@@ -176,7 +239,9 @@ size_t rda_prefill_workspace_bytes(int32_t num_seqs, int32_t total_tokens, int32
     const int32_t mc = rda_max_chunks(num_seqs, total_tokens);
     if (mc < 0) return 0;
     const TableLayout tl = table_layout(mc, num_seqs);
-    return align256(tl.bytes) + size_t(mc) * size_t(num_heads) * kChunkHeadBytes;
+    // one sequence: room for the segmented pass's three state arrays
+    return align256(tl.bytes) + size_t(mc) * size_t(num_heads) * kChunkHeadBytes +
+           3 * seg_state_bytes(seg_plan(num_seqs, total_tokens, num_heads), num_heads);
 }
 
 rda_status rda_prefill_profiled(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,

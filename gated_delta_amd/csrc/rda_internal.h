@@ -153,10 +153,37 @@ hipError_t launch_prep_bf16(const uint16_t* q, const uint16_t* k, const float* a
                             hipStream_t stream);
 
 // bf16 walk (operands streamed into LDS by loader waves)
+// One walk job: where the state starts (identity, S0, or zero when S0 is
+// null), whether v counts (zero_v: every value taken as 0, so the walk
+// applies the chunks' transition alone) and where the final state goes
+// (skipped when null).
+struct WalkJob {
+    const float* S0;
+    float* S_final;
+    int identity;
+    int zero_v;
+};
+
+// bf16 walk.  num_jobs (1 or 2) walks over the same chunks in one launch,
+// differing only in their WalkJob.  seg_chunks > 0: sequence n is the n-th
+// run of seg_chunks chunks of the table (segments of one sequence) instead of
+// seq_off[n] .. seq_off[n + 1].  outputs = false: no o is written, and Q and
+// A are not streamed.
 hipError_t launch_walk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             int32_t num_seqs, int32_t heads, const int32_t* rec,
                             const int32_t* seq_off, const int32_t* num_chunks,
-                            const unsigned char* factors, const float* S0, float* o,
-                            float* S_final, hipStream_t stream);
+                            const unsigned char* factors, float* o, const WalkJob* jobs,
+                            int32_t num_jobs, int32_t seg_chunks, bool outputs,
+                            hipStream_t stream);
+
+// The segment combine of the segmented state pass, per head and value row:
+// S_in[0] = S0 (zero when null); for p < P: with E_p = segment p's final
+// state from zero and M_p = its transition (the final state from the
+// identity with zero values),
+//   S_in[p + 1] = S_in[p] M_p + E_p,
+// written to S_in[p + 1] for p + 1 < P and to S_final (when not null) for
+// p + 1 = P.  E, M, S_in are [P, H, 128, 128] fp32.
+hipError_t launch_segment_combine(const float* S0, const float* E, const float* M, float* S_in,
+                                  float* S_final, int32_t P, int32_t heads, hipStream_t stream);
 
 }  // namespace rda

@@ -714,9 +714,10 @@ hipError_t launch_walk(const void* q, const void* k, const void* v, rda_dtype dt
     const int64_t pairs = int64_t(num_seqs) * heads;
     const unsigned grid = unsigned(64 * ((pairs + 7) / 8));
     if (dt == RDA_BF16) {
+        const WalkJob job{S0, S_final, 0, 0};
         return launch_walk_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                 static_cast<const uint16_t*>(v), num_seqs, heads, rec, seq_off,
-                                num_chunks, factors, S0, o, S_final, stream);
+                                num_chunks, factors, o, &job, 1, 0, true, stream);
     } else {
         hipLaunchKernelGGL(walk_kernel<float>, dim3(grid), dim3(kWalkThreads), 0, stream,
                            static_cast<const float*>(q), static_cast<const float*>(k),

@@ -31,6 +31,15 @@
 // land on the recurrence), and the output work runs beside the recurrence on
 // the other wave slots instead of lengthening it.
 //
+// The same kernel serves the segmented form of the state pass: a launch may
+// carry two jobs over the same chunks that differ only in the starting state
+// (taken from S0, zero, or the identity), in whether the values count (a job
+// with zero values walks the state's own transition), and in where the final
+// state goes;
+// the sequences may be equal runs of chunks of one sequence (segments); and
+// the instantiation without outputs streams neither Q nor A and leaves its
+// output waves idle at the barriers.
+//
 // Past the end of a chunk (len < 64) the loaders duplicate the last valid
 // token row instead of zeroing: T_b has zero rows and columns there (b = 0),
 // so U and U~ vanish on those rows and no duplicate reaches S or a stored
@@ -164,38 +173,42 @@ __device__ __forceinline__ void touch_chunk(const Ctx& x, int chunk, float* sink
 // Blocks of the packed factors that no wave reads: slots (tile, block 1) of
 // token tiles 0 and 1, whose operands are zero (both factors are lower
 // triangular).  They are neither written by the prep kernel nor streamed.
+// Without outputs the Q tile (blocks 16..31) and A (48..63) are not read
+// either.
+template <bool kOut>
 constexpr bool unread_block(int blk) {
     const int slot = (blk - 32) & 15;   // (tile * 2 + block) * 2 + hi/lo
+    if (!kOut && ((blk >= 16 && blk < 32) || (blk >= 48 && blk < 64))) return true;
     return blk >= 32 && blk < 64 && ((slot >> 1) & 1) == 1 && (slot >> 2) < 2;
 }
 
 // Number of blocks loader kI issues per chunk.
-template <int kI>
+template <int kI, bool kOut>
 constexpr int loader_blocks() {
     int n = 0;
-    for (int blk = kI; blk < 67; blk += 8) n += unread_block(blk) ? 0 : 1;
+    for (int blk = kI; blk < 67; blk += 8) n += unread_block<kOut>(blk) ? 0 : 1;
     return n;
 }
 
 // Loader kI's blocks of `chunk`, in three groups of ascending block number
 // (the compiler keeps the order inside each group; left free to interleave
 // all of them, it produced an order measured slower).
-template <int kI, int kGroup>
+template <int kI, int kGroup, bool kOut>
 __device__ __forceinline__ void issue_group(const Ctx& x, int chunk, Stage& st) {
     const int t0 = x.rec[4 * chunk + 1], len = x.rec[4 * chunk + 2];
     const unsigned char* F = chunk_factors(x, chunk);
 #pragma unroll
     for (int q = 3 * kGroup; q < 3 * kGroup + 3; ++q) {
         const int blk = kI + 8 * q;
-        if (blk < 67 && !unread_block(blk)) issue_block(x, t0, len, F, blk, st);
+        if (blk < 67 && !unread_block<kOut>(blk)) issue_block(x, t0, len, F, blk, st);
     }
 }
 
-template <int kI>
+template <int kI, bool kOut>
 __device__ __forceinline__ void issue_chunk(const Ctx& x, int chunk, Stage& st) {
-    issue_group<kI, 0>(x, chunk, st);
-    issue_group<kI, 1>(x, chunk, st);
-    issue_group<kI, 2>(x, chunk, st);
+    issue_group<kI, 0, kOut>(x, chunk, st);
+    issue_group<kI, 1, kOut>(x, chunk, st);
+    issue_group<kI, 2, kOut>(x, chunk, st);
 }
 
 template <int kN>
@@ -211,24 +224,24 @@ __device__ __forceinline__ void wait_vm() {
 // waits until only the blocks of the chunk after it (and that touch) may
 // still be in flight: loads complete in issue order.  (Spreading the blocks
 // over the three barrier windows instead was measured slightly slower.)
-template <int kI>
+template <int kI, bool kOut>
 __device__ void loader(const Ctx& x, int c0, int c_end, Lds& S) {
-    constexpr int kPending = loader_blocks<kI>() + (kI < 2 ? 1 : 0);
+    constexpr int kPending = loader_blocks<kI, kOut>() + (kI < 2 ? 1 : 0);
     const int last = c_end - 1;
     auto cl = [last](int c) { return c < last ? c : last; };
     if constexpr (kI < 2) {
 #pragma unroll
         for (int d = 1; d < kPfAhead; ++d) touch_chunk<kI>(x, cl(c0 + d), S.sink);
     }
-    issue_chunk<kI>(x, c0, S.st[0]);
-    issue_chunk<kI>(x, cl(c0 + 1), S.st[1]);
+    issue_chunk<kI, kOut>(x, c0, S.st[0]);
+    issue_chunk<kI, kOut>(x, cl(c0 + 1), S.st[1]);
     if constexpr (kI < 2) touch_chunk<kI>(x, cl(c0 + kPfAhead), S.sink);
     for (int c = c0; c < c_end; ++c) {
         wait_vm<kPending>();
         __builtin_amdgcn_s_barrier();   // A
         __builtin_amdgcn_s_barrier();   // B
         __builtin_amdgcn_s_barrier();   // C: chunk c's stage is free
-        issue_chunk<kI>(x, cl(c + 2), S.st[(c - c0) & 1]);
+        issue_chunk<kI, kOut>(x, cl(c + 2), S.st[(c - c0) & 1]);
         if constexpr (kI < 2) touch_chunk<kI>(x, cl(c + 2 + kPfAhead), S.sink);
     }
     wait_vm<0>();   // nothing may land in LDS after the workgroup ends
@@ -303,7 +316,7 @@ __device__ __forceinline__ bf16x8 packed(const u32x4 (*P)[64], int tile, int m, 
 // ---- state waves -------------------------------------------------------------------
 
 __device__ __forceinline__ void state_step(const Ctx& x, int w, const Stage& st, Lds& S,
-                                           f32x4& s0, f32x4& s1) {
+                                           f32x4& s0, f32x4& s1, bool zero_v) {
     const int l = x.l, g = l >> 4, c = l & 15;
     const int nb = (w >> 1) + 1;   // token blocks at or below token tile w
     // P1: publish S^T block w in natural key order: tile 2w (keys 32w + 4g + e)
@@ -342,8 +355,11 @@ __device__ __forceinline__ void state_step(const Ctx& x, int w, const Stage& st,
             y0 = mfma_bf16(ka[m], sh[m], y0);
             y1 = mfma_bf16(ka[m], sl[m], y1);
         }
-        const f32x4 vf = {__uint_as_float(vv[0] << 16), __uint_as_float(vv[0] & 0xffff0000u),
-                          __uint_as_float(vv[1] << 16), __uint_as_float(vv[1] & 0xffff0000u)};
+        const f32x4 vf = zero_v ? zero4()
+                                : f32x4{__uint_as_float(vv[0] << 16),
+                                        __uint_as_float(vv[0] & 0xffff0000u),
+                                        __uint_as_float(vv[1] << 16),
+                                        __uint_as_float(vv[1] & 0xffff0000u)};
         put_half(S.Ex, w, l, vf - (y0 + y1) * gam);
     }
     __syncthreads();   // B
@@ -459,16 +475,21 @@ __device__ __forceinline__ void output_step(const Ctx& x, int tt, int ch, const 
     }
 }
 
+template <bool kOut>
 __global__ __launch_bounds__(kThreads) void walk_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int N, int H, const int32_t* __restrict__ rec,
     const int32_t* __restrict__ seq_off, const int32_t* __restrict__ num_chunks,
-    const unsigned char* __restrict__ factors, const float* __restrict__ S0,
-    float* __restrict__ o, float* __restrict__ S_final) {
-    // XCD-aware mapping: the 8 value slices of one (sequence, head) share
-    // blockIdx.x % 8, hence one XCD and its L2, which then holds the chunk's
-    // K, Q and factors once for all of them.
-    const int id = blockIdx.x;
+    const unsigned char* __restrict__ factors, float* __restrict__ o, WalkJob j0, WalkJob j1,
+    int seg_chunks) {
+    // Jobs split the grid in halves.  Within a job the mapping is XCD-aware:
+    // the 8 value slices of one (sequence, head) share blockIdx.x % 8, hence
+    // one XCD and its L2, which then holds the chunk's K, Q and factors once
+    // for all of them.
+    const int per_job = 64 * ((N * H + 7) / 8);
+    const int job = blockIdx.x >= per_job ? 1 : 0;
+    const WalkJob J = job ? j1 : j0;
+    const int id = blockIdx.x - job * per_job;
     const int xcd = id & 7, rest = id >> 3;
     const int s = rest & 7, pg = rest >> 3;
     const int p = pg * 8 + xcd;
@@ -479,41 +500,64 @@ __global__ __launch_bounds__(kThreads) void walk_bf16_kernel(
 
     const int w = wave_id(), l = threadIdx.x & 63, g = l >> 4, c = l & 15;
     const int nch = num_chunks[0];
-    const int c0 = seq_off[n];
-    const int c_end = seq_off[n + 1] < nch ? seq_off[n + 1] : nch;
+    // sequence n's chunks: from the table, or the n-th run of seg_chunks
+    int c0, c_end;
+    if (seg_chunks > 0) {
+        c0 = n * seg_chunks < nch ? n * seg_chunks : nch;
+        c_end = c0 + seg_chunks < nch ? c0 + seg_chunks : nch;
+    } else {
+        c0 = seq_off[n];
+        c_end = seq_off[n + 1] < nch ? seq_off[n + 1] : nch;
+    }
     const Ctx x{q, k, v, factors, rec, H, h, s, l};
 
     if (w >= kLoader0) {
         if (c0 < c_end) {
             switch (w - kLoader0) {
-                case 0: loader<0>(x, c0, c_end, lds); break;
-                case 1: loader<1>(x, c0, c_end, lds); break;
-                case 2: loader<2>(x, c0, c_end, lds); break;
-                case 3: loader<3>(x, c0, c_end, lds); break;
-                case 4: loader<4>(x, c0, c_end, lds); break;
-                case 5: loader<5>(x, c0, c_end, lds); break;
-                case 6: loader<6>(x, c0, c_end, lds); break;
-                default: loader<7>(x, c0, c_end, lds); break;
+                case 0: loader<0, kOut>(x, c0, c_end, lds); break;
+                case 1: loader<1, kOut>(x, c0, c_end, lds); break;
+                case 2: loader<2, kOut>(x, c0, c_end, lds); break;
+                case 3: loader<3, kOut>(x, c0, c_end, lds); break;
+                case 4: loader<4, kOut>(x, c0, c_end, lds); break;
+                case 5: loader<5, kOut>(x, c0, c_end, lds); break;
+                case 6: loader<6, kOut>(x, c0, c_end, lds); break;
+                default: loader<7, kOut>(x, c0, c_end, lds); break;
             }
         }
         return;
     }
     if (w >= kStateWaves) {
-        for (int ch = c0; ch < c_end; ++ch)
-            output_step(x, w - kStateWaves, ch, lds.st[(ch - c0) & 1], lds, o);
+        for (int ch = c0; ch < c_end; ++ch) {
+            if constexpr (kOut) {
+                output_step(x, w - kStateWaves, ch, lds.st[(ch - c0) & 1], lds, o);
+            } else {
+                __syncthreads();   // A
+                __syncthreads();   // B
+                __syncthreads();   // C
+            }
+        }
         return;
     }
     // lane holds S^T[k = 16 kt + 4g + e][v = 16s + c] = S[v][k] for kt = 2w, 2w+1
     const size_t srow = ((size_t(n) * H + h) * kD + 16 * s + c) * kD + 32 * w + 4 * g;
     f32x4 s0 = zero4(), s1 = zero4();
-    if (S0) {
-        s0 = *reinterpret_cast<const f32x4*>(S0 + srow);
-        s1 = *reinterpret_cast<const f32x4*>(S0 + srow + 16);
+    if (J.identity) {
+        const int vrow = 16 * s + c, key = 32 * w + 4 * g;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            s0[e] = key + e == vrow ? 1.f : 0.f;
+            s1[e] = key + 16 + e == vrow ? 1.f : 0.f;
+        }
+    } else if (J.S0) {
+        s0 = *reinterpret_cast<const f32x4*>(J.S0 + srow);
+        s1 = *reinterpret_cast<const f32x4*>(J.S0 + srow + 16);
     }
-    for (int ch = c0; ch < c_end; ++ch) state_step(x, w, lds.st[(ch - c0) & 1], lds, s0, s1);
-    if (S_final) {
-        *reinterpret_cast<f32x4*>(S_final + srow) = s0;
-        *reinterpret_cast<f32x4*>(S_final + srow + 16) = s1;
+    const bool zero_v = J.zero_v != 0;
+    for (int ch = c0; ch < c_end; ++ch)
+        state_step(x, w, lds.st[(ch - c0) & 1], lds, s0, s1, zero_v);
+    if (J.S_final) {
+        *reinterpret_cast<f32x4*>(J.S_final + srow) = s0;
+        *reinterpret_cast<f32x4*>(J.S_final + srow + 16) = s1;
     }
 }
 
@@ -522,12 +566,21 @@ __global__ __launch_bounds__(kThreads) void walk_bf16_kernel(
 hipError_t launch_walk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             int32_t num_seqs, int32_t heads, const int32_t* rec,
                             const int32_t* seq_off, const int32_t* num_chunks,
-                            const unsigned char* factors, const float* S0, float* o,
-                            float* S_final, hipStream_t stream) {
+                            const unsigned char* factors, float* o, const WalkJob* jobs,
+                            int32_t num_jobs, int32_t seg_chunks, bool outputs,
+                            hipStream_t stream) {
     const int64_t pairs = int64_t(num_seqs) * heads;
-    const unsigned grid = unsigned(64 * ((pairs + 7) / 8));
-    hipLaunchKernelGGL(walk_bf16_kernel, dim3(grid), dim3(kThreads), 0, stream, q, k, v, num_seqs,
-                       heads, rec, seq_off, num_chunks, factors, S0, o, S_final);
+    const unsigned grid = unsigned(num_jobs * 64 * ((pairs + 7) / 8));
+    const WalkJob none{nullptr, nullptr, 0, 0};
+    const WalkJob j1 = num_jobs > 1 ? jobs[1] : none;
+    if (outputs)
+        hipLaunchKernelGGL(walk_bf16_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, q, k, v,
+                           num_seqs, heads, rec, seq_off, num_chunks, factors, o, jobs[0], j1,
+                           seg_chunks);
+    else
+        hipLaunchKernelGGL(walk_bf16_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, q, k,
+                           v, num_seqs, heads, rec, seq_off, num_chunks, factors, o, jobs[0], j1,
+                           seg_chunks);
     return hipGetLastError();
 }
 

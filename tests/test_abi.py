@@ -73,6 +73,17 @@ def test_max_chunks_matches_reference(lib):
     assert rda.rda_max_chunks(0, 5) == -1 and rda.rda_max_chunks(1, -1) == -1
 
 
+def test_workspace_covers_the_segmented_pass(lib):
+    """One sequence with few heads gets room for three [P, H, 128, 128]
+    state arrays; with 16 heads, or two sequences, it does not."""
+    seg = rda.rda_prefill_workspace_bytes(1, 16384, 2)
+    two = rda.rda_prefill_workspace_bytes(2, 16384, 2)
+    assert seg - two >= 3 * 8 * 2 * 128 * 128 * 4 - 2 * 2 * 131584
+    assert rda.rda_prefill_workspace_bytes(1, 16384, 16) < rda.rda_prefill_workspace_bytes(2, 16384, 16)
+    # short sequences keep the one-pass walk
+    assert rda.rda_prefill_workspace_bytes(1, 2048, 2) < rda.rda_prefill_workspace_bytes(2, 2048, 2)
+
+
 def test_workspace_bytes(lib):
     w1 = rda.rda_prefill_workspace_bytes(1, 16384, 16)
     w2 = rda.rda_prefill_workspace_bytes(1, 16384, 8)
