@@ -27,7 +27,6 @@ namespace {
 // the 64 lanes of one B read (rows 4 ks + g, 16 consecutive columns) then
 // hit 64 distinct banks.
 constexpr int kRows = 16;
-constexpr int kBlocksPerHead = kD / kRows;
 constexpr int kSx = kD + 4;   // row stride (floats) of the staged rows: spreads banks
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -57,11 +56,13 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((kN & 15) | ((kN >> 4) << 14) | 0x0F70);
 }
 
-// All of M_p into LDS: wave w moves the 1 KiB blocks w, w + 4, ... (rows
-// 2 blk, 2 blk + 1), each lane fetching the granule that lands at its slot.
+// Half kHalf of M_p into LDS: wave w moves the 1 KiB blocks w + 4 i (rows
+// 2 blk, 2 blk + 1) for i in that half, each lane fetching the granule that
+// lands at its slot.
+template <int kHalf>
 __device__ __forceinline__ void dma_matrix(const float* src, float* dst, int w, int l) {
 #pragma unroll
-    for (int i = 0; i < kD * kD * 4 / 1024 / 4; ++i) {
+    for (int i = 8 * kHalf; i < 8 * kHalf + 8; ++i) {
         const int blk = w + 4 * i;
         const int r = 2 * blk + (l >> 5), pq = l & 31;
         __builtin_amdgcn_global_load_lds(src + r * kD + 4 * (pq ^ mswz(r)),
@@ -80,15 +81,22 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(const float* S0,
                                                               float* __restrict__ S_in,
                                                               float* S_final, int P, int H) {
     __shared__ __attribute__((aligned(16))) CombineLds L;
-    const int h = blockIdx.x / kBlocksPerHead;
-    const int rb = blockIdx.x - h * kBlocksPerHead;
+    // the 8 row blocks of a head share blockIdx.x % 8, hence one XCD and its
+    // L2, which then fetches each M_p once for all of them (the grid holds 8
+    // heads per 64 workgroups; those past the last head exit)
+    const int h = (blockIdx.x >> 6) * 8 + (blockIdx.x & 7);
+    const int rb = (blockIdx.x >> 3) & 7;
+    if (h >= H) return;
     const int w = wave_id(), l = threadIdx.x & 63, g = l >> 4, c = l & 15;
     const size_t head = size_t(h) * kD * kD;
     const size_t seg = size_t(H) * kD * kD;
     const size_t rows = head + size_t(rb) * kRows * kD;   // this block's first row
     const int steps = S_final ? P : P - 1;   // the last step only feeds S_final
 
-    if (steps > 0) dma_matrix(Mt + head, L.M[0], w, l);
+    if (steps > 0) {
+        dma_matrix<0>(Mt + head, L.M[0], w, l);
+        dma_matrix<1>(Mt + head, L.M[0], w, l);
+    }
     // S_in[0] = S0 (or zero): the operand registers, and (wave w's columns)
     // the copy in S_in
     float aS[kD / 4];
@@ -113,16 +121,20 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(const float* S0,
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 ev[u][e] = Ep[rows + size_t(4 * g + e) * kD + 32 * w + 16 * u + c];
-        // the next step's matrix, one step ahead (the last step fetches its own
-        // again, unread: a fixed count of loads keeps the waits exact)
+        // the next step's matrix, one step ahead, in two halves issued before
+        // the two halves of the products (the last step fetches its own again,
+        // unread: a fixed count of loads keeps the waits exact)
         const int pn = p + 1 < steps ? p + 1 : p;
-        dma_matrix(Mt + pn * seg + head, L.M[(p + 1) & 1], w, l);
+        const float* Mnext = Mt + pn * seg + head;
+        float* Mbuf = L.M[(p + 1) & 1];
         const float* M = L.M[p & 1];
         f32x4 acc0 = zero4(), acc1 = zero4();
         // half of the B operands read at once, then their products (read
         // one at a time, every product waits out the LDS latency)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
+            if (half == 0) dma_matrix<0>(Mnext, Mbuf, w, l);
+            else dma_matrix<1>(Mnext, Mbuf, w, l);
             float b0[16], b1[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -158,7 +170,7 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(const float* S0,
 
 hipError_t launch_segment_combine(const float* S0, const float* E, const float* M, float* S_in,
                                   float* S_final, int32_t P, int32_t heads, hipStream_t stream) {
-    const unsigned grid = unsigned(heads * kBlocksPerHead);
+    const unsigned grid = unsigned(64 * ((heads + 7) / 8));
     if (grid == 0 || P <= 0) return hipSuccess;
     hipLaunchKernelGGL(segment_combine_kernel, dim3(grid), dim3(256), 0, stream, S0, E, M, S_in,
                        S_final, P, heads);

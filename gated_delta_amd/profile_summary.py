@@ -14,6 +14,9 @@ Writes
       the same for the prologue (bench --mode prologue);
   profiles/kernels_rda_prefill_diag_T16384_H16.txt
       the same for the per-channel-decay prefill (bench --mode prefill_diag);
+  profiles/kernels_rda_prefill_segmented_T16384_H2.txt
+      the same for the segmented state pass beside the one-pass walk on the
+      long prompt's first two heads (bench --mode segments);
   profiles/hbm_traffic.txt
       FETCH_SIZE and WRITE_SIZE per dispatch of every prefill kernel, each
       scaled by what the same counter reads for a device copy of known size,
@@ -38,7 +41,7 @@ STAGE = {"chunk_table_kernel": "rda_chunk_table", "prep_bf16_kernel": "rda_prep"
          "walk_bf16_kernel": "rda_walk", "decode_step_kernel": "rda_decode_step",
          "decode_tokens_kernel": "rda_decode_tokens", "norm_gate_kernel": "rda_output_norm_gate",
          "prologue_kernel": "rda_prologue", "prep_diag_kernel": "rda_prep_diag",
-         "walk_diag_kernel": "rda_walk_diag"}
+         "walk_diag_kernel": "rda_walk_diag", "segment_combine_kernel": "rda_segment_combine"}
 
 
 def short(name: str) -> str:
@@ -66,14 +69,20 @@ def counter(d, name):
     return {k: statistics.mean(v[1:] if len(v) > 1 else v) for k, v in by.items()}
 
 
-def kernel_table(trace_dir, path, header):
+def kernel_table(trace_dir, path, header, templates=False):
     """Write the per-kernel call count / average / total of one kernel-trace
-    pass to `path` under `header`; returns the stats rows."""
+    pass to `path` under `header`; returns the stats rows.  templates: keep
+    the template arguments in the names (instantiations listed apart)."""
     rows = list(csv.DictReader(open(find(trace_dir, "*kernel_stats.csv"))))
+    name = short
+    if templates:
+        def name(n):
+            n = n.replace("rda::(anonymous namespace)::", "").replace("void ", "")
+            return n.replace("rda::", "").split("(")[0].strip()
     lines = header + [f"# kernel sources: {source_hash()}",
                       f"{'kernel':40s} {'calls':>6s} {'avg_us':>10s} {'total_us':>12s} {'pct':>6s}"]
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
-        lines.append(f"{short(r['Name'])[:40]:40s} {int(r['Calls']):6d} "
+        lines.append(f"{name(r['Name'])[:40]:40s} {int(r['Calls']):6d} "
                      f"{float(r['AverageNs']) / 1e3:10.2f} {float(r['TotalDurationNs']) / 1e3:12.1f} "
                      f"{float(r['Percentage']):6.2f}")
     open(path, "w").write("\n".join(lines) + "\n")
@@ -148,6 +157,23 @@ def main():
              "#   rocprofv3 --kernel-trace --stats --output-format csv -d OUTDIR/prof_trace_diag -o trace \\",
              "#     -- python bench.py --mode prefill_diag --steps 10 --no-cpu",
              "# then python gated_delta_amd/profile_summary.py OUTDIR"])
+
+    if os.path.isdir(os.path.join(out, "prof_trace_seg")):
+        kernel_table(
+            os.path.join(out, "prof_trace_seg"),
+            os.path.join(prof, "kernels_rda_prefill_segmented_T16384_H2.txt"),
+            ["# rocprofv3 kernel trace, the segmented state pass: rda_prefill on the long",
+             "# prompt's first 2 heads (16384 tokens x 2 heads, bf16 q/k/v, S0 ~ N(0, 0.02)),",
+             "# P = 8 segments: prep, walk_bf16_kernel<false> (every segment from zero and",
+             "# from the identity), segment_combine_kernel, walk_bf16_kernel<true> (outputs);",
+             "# then the same inputs through the one-pass walk (cu_seqlens = {0, T}: chunk",
+             "# table, prep, walk_bf16_kernel<true>); 11 calls of each, each after a 512 MiB",
+             "# read (reduce_kernel: the cache flush).  walk_bf16_kernel<true> averages the",
+             "# output pass and the one-pass walk.",
+             "# command: gated_delta_amd/profile_run.sh OUTDIR, whose sixth pass is",
+             "#   rocprofv3 --kernel-trace --stats --output-format csv -d OUTDIR/prof_trace_seg -o trace \\",
+             "#     -- python bench.py --mode segments --steps 10 --no-cpu",
+             "# then python gated_delta_amd/profile_summary.py OUTDIR"], templates=True)
 
     # ---- HBM traffic -------------------------------------------------------------
     n = 1 << 30   # bytes the calibration copy reads and writes per launch

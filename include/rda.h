@@ -121,6 +121,18 @@ size_t rda_prefill_workspace_bytes(int32_t num_seqs, int32_t total_tokens,
  *               same pointer as S0 (in-place resume), no other overlap allowed
  *   workspace   device scratch of at least rda_prefill_workspace_bytes(...)
  * total_tokens = 0 is allowed (only S_final is written).
+ *
+ * The state passing between chunks is sequential per (sequence, head) and
+ * gives each pair 8 workgroups.  One bf16 sequence without offsets with few
+ * heads (H <= 4 with at least 16 chunks per segment; the plan is fixed by
+ * total_tokens and H) is instead cut into P = 4..16 segments. Each segment is
+ * walked from zero and, with its values taken as zero, from the identity;
+ * the segments' affine maps are chained, and each segment is walked again from
+ * its true starting state for the outputs. This is the segment-summary form
+ * in the state-passing row of the chunked method (one long prompt's share of
+ * heads on one GPU). It gives the same result up to rounding, and
+ * rda_prefill_workspace_bytes(1, T, H) includes its three [P, H, dv, dk]
+ * state arrays.  Passing cu_seqlens = {0, T} keeps the one-pass walk.
  */
 rda_status rda_prefill(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
                        const float* a, const float* b,
