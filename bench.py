@@ -40,7 +40,8 @@ prologue, output_norm_gate and decode_tokens).
              with a per-channel decay and the per-channel decode step
              (prefill_diag); the long prompt with 1, 2 and 4 of its heads
              (one GPU's share under head sharding), segmented state pass
-             against the one-pass walk (prefill_segmented)
+             against the one-pass walk, and the same for the per-channel
+             decay on 2 heads (prefill_segmented)
 
 Usage: python bench.py [--gpus 1] [--steps 128] [--warmup 5] [--no-cpu]
 """
@@ -631,6 +632,43 @@ def segment_measurements(args, torch, np, rda, synth, dev, stream, timed, flush,
             entry["parity"] = {"o_rel_l2": float(np.linalg.norm(og - ro) / np.linalg.norm(ro)),
                                "S_rel_l2": float(np.linalg.norm(Sg - rS) / np.linalg.norm(rS))}
         res[f"H{H}"] = entry
+    # the per-channel decay on the long prompt's first 2 heads, the same way
+    H = 2
+    sl = lambda x: np.ascontiguousarray(x[:, :H])
+    alpha = synth.diag_alpha(T, H, key=(10,))
+    qh, kh, vh = (torch.from_numpy(sl(getattr(p, n))).to(torch.bfloat16).to(dev) for n in "qkv")
+    alh, bh = torch.from_numpy(alpha).to(dev), torch.from_numpy(sl(p.b)).to(dev)
+    S0h = torch.from_numpy(np.ascontiguousarray(p.S0[:, :H])).to(dev)
+    oh = torch.empty((T, H, D), dtype=torch.float32, device=dev)
+    Sfh = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(rda.rda_prefill_diag_workspace_bytes(1, T, H), dtype=torch.uint8, device=dev)
+    entry = {}
+    for name, cu in (("segmented", None), ("one_pass", cu_one)):
+        cargs = [rda._ptr(qh), rda._ptr(kh), rda._ptr(vh), 0, rda._ptr(alh), rda._ptr(bh),
+                 rda._ptr(cu), 1, T, H, D, D, rda._ptr(S0h), rda._ptr(oh), rda._ptr(Sfh),
+                 rda._ptr(ws), ws.numel(), stream.cuda_stream]
+
+        def call(cargs=cargs):
+            if rda.lib().rda_prefill_diag(*cargs) != 0:
+                raise RuntimeError("rda_prefill_diag failed")
+        call()
+        sec = timed(call, reps, flush)
+        entry[name] = {"ms_per_call": sec * 1e3, "tokens_per_s": T / sec}
+    entry["speedup"] = entry["one_pass"]["ms_per_call"] / entry["segmented"]["ms_per_call"]
+    if not args.no_cpu:
+        import oracle
+        torch.cuda.synchronize()
+        rda.rda_prefill_diag(qh, kh, vh, alh, bh, S0=S0h, o=oh, S_final=Sfh, workspace=ws,
+                             stream=stream)
+        torch.cuda.synchronize()
+        ro, rS = oracle.prefill_diag(sl(p.q), sl(p.k), sl(p.v), alpha, sl(p.b),
+                                     S0=np.ascontiguousarray(p.S0[:, :H]),
+                                     threads=args.cpu_threads)
+        og = oh.cpu().numpy().astype(np.float64)
+        Sg = Sfh.cpu().numpy().astype(np.float64)
+        entry["parity"] = {"o_rel_l2": float(np.linalg.norm(og - ro) / np.linalg.norm(ro)),
+                           "S_rel_l2": float(np.linalg.norm(Sg - rS) / np.linalg.norm(rS))}
+    res["per_channel_H2"] = entry
     return res
 
 

@@ -345,7 +345,9 @@ size_t rda_prefill_diag_workspace_bytes(int32_t num_seqs, int32_t total_tokens,
     const int32_t mc = rda_max_chunks(num_seqs, total_tokens);
     if (mc < 0) return 0;
     const TableLayout tl = table_layout(mc, num_seqs);
-    return align256(tl.bytes) + size_t(mc) * size_t(num_heads) * kDiagChunkHeadBytes;
+    // one sequence: room for the segmented pass's three state arrays
+    return align256(tl.bytes) + size_t(mc) * size_t(num_heads) * kDiagChunkHeadBytes +
+           3 * seg_state_bytes(seg_plan(num_seqs, total_tokens, num_heads), num_heads);
 }
 
 rda_status rda_prefill_diag(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
@@ -396,10 +398,34 @@ rda_status rda_prefill_diag(const void* q, const void* k, const void* v, rda_dty
     if (launch_chunk_table(cu_seqlens, num_seqs, total_tokens, mc, rec, seq_off, nch, stream) !=
         hipSuccess)
         return RDA_ERR_HIP;
-    if (launch_prefill_diag(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                            static_cast<const uint16_t*>(v), alpha, b, num_seqs, num_heads,
-                            total_tokens > 0 ? mc : 0, rec, seq_off, nch, ws + align256(tl.bytes),
-                            S0, o, S_final, stream) != hipSuccess)
+    const auto* q16 = static_cast<const uint16_t*>(q);
+    const auto* k16 = static_cast<const uint16_t*>(k);
+    const auto* v16 = static_cast<const uint16_t*>(v);
+    unsigned char* factors = ws + align256(tl.bytes);
+    const SegPlan sp = seg_plan(num_seqs, total_tokens, num_heads);
+    if (sp.P > 0 && cu_seqlens == nullptr) {
+        // the segmented state pass, as for rda_prefill
+        unsigned char* seg = factors + size_t(mc) * num_heads * kDiagChunkHeadBytes;
+        const size_t sb = seg_state_bytes(sp, num_heads);
+        float* E = reinterpret_cast<float*>(seg);
+        float* M = reinterpret_cast<float*>(seg + sb);
+        float* S_in = reinterpret_cast<float*>(seg + 2 * sb);
+        const WalkJob first[2] = {{nullptr, E, 0, 0}, {nullptr, M, 1, 1}};
+        const WalkJob last{S_in, nullptr, 0, 0};
+        if (launch_prep_diag(q16, k16, alpha, b, num_heads, mc, rec, nch, factors, stream) !=
+                hipSuccess ||
+            launch_walk_diag(v16, sp.P, num_heads, rec, seq_off, nch, factors, nullptr, first, 2,
+                             sp.cps, false, stream) != hipSuccess ||
+            launch_segment_combine(S0, E, M, S_in, S_final, sp.P, num_heads, stream) !=
+                hipSuccess ||
+            launch_walk_diag(v16, sp.P, num_heads, rec, seq_off, nch, factors, o, &last, 1,
+                             sp.cps, true, stream) != hipSuccess)
+            return RDA_ERR_HIP;
+        return RDA_OK;
+    }
+    if (launch_prefill_diag(q16, k16, v16, alpha, b, num_seqs, num_heads,
+                            total_tokens > 0 ? mc : 0, rec, seq_off, nch, factors, S0, o, S_final,
+                            stream) != hipSuccess)
         return RDA_ERR_HIP;
     return RDA_OK;
 }

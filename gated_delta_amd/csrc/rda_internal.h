@@ -112,6 +112,17 @@ struct PrologueArgs {
 };
 hipError_t launch_prologue(const PrologueArgs& P, int32_t K, int32_t act, hipStream_t stream);
 
+// One walk job: where the state starts (identity, S0, or zero when S0 is
+// null), whether v counts (zero_v: every value taken as 0, so the walk
+// applies the chunks' transition alone) and where the final state goes
+// (skipped when null).
+struct WalkJob {
+    const float* S0;
+    float* S_final;
+    int identity;
+    int zero_v;
+};
+
 // Per-channel decay: prep + walk after the chunk table (bf16 q, k, v).
 hipError_t launch_prefill_diag(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                const float* alpha, const float* b, int32_t num_seqs,
@@ -119,6 +130,18 @@ hipError_t launch_prefill_diag(const uint16_t* q, const uint16_t* k, const uint1
                                const int32_t* seq_off, const int32_t* num_chunks,
                                unsigned char* factors, const float* S0, float* o,
                                float* S_final, hipStream_t stream);
+// Its two stages apart (the segmented state pass runs the walk three times
+// over one prep): the prep, and the walk with jobs, segment runs and the
+// instantiation without outputs as for launch_walk_bf16.
+hipError_t launch_prep_diag(const uint16_t* q, const uint16_t* k, const float* alpha,
+                            const float* b, int32_t heads, int32_t max_chunks, const int32_t* rec,
+                            const int32_t* num_chunks, unsigned char* factors,
+                            hipStream_t stream);
+hipError_t launch_walk_diag(const uint16_t* v, int32_t num_seqs, int32_t heads,
+                            const int32_t* rec, const int32_t* seq_off,
+                            const int32_t* num_chunks, const unsigned char* factors, float* o,
+                            const WalkJob* jobs, int32_t num_jobs, int32_t seg_chunks,
+                            bool outputs, hipStream_t stream);
 hipError_t launch_decode_diag(const void* q, const void* k, const void* v, rda_dtype dt,
                               const float* alpha, const float* b, int32_t batch, int32_t heads,
                               float* S, float* o, hipStream_t stream);
@@ -153,16 +176,6 @@ hipError_t launch_prep_bf16(const uint16_t* q, const uint16_t* k, const float* a
                             hipStream_t stream);
 
 // bf16 walk (operands streamed into LDS by loader waves)
-// One walk job: where the state starts (identity, S0, or zero when S0 is
-// null), whether v counts (zero_v: every value taken as 0, so the walk
-// applies the chunks' transition alone) and where the final state goes
-// (skipped when null).
-struct WalkJob {
-    const float* S0;
-    float* S_final;
-    int identity;
-    int zero_v;
-};
 
 // bf16 walk.  num_jobs (1 or 2) walks over the same chunks in one launch,
 // differing only in their WalkJob.  seg_chunks > 0: sequence n is the n-th

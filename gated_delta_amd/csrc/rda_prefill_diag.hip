@@ -389,19 +389,25 @@ __device__ __forceinline__ f32x4 prod3(const bf16x8 (*a)[2], u32x4 (*B)[2][64], 
 }
 
 // One chunk; `cur` holds its operands and is refilled with chunk `next`
-// as each part is consumed.
+// as each part is consumed.  Without outputs (kOut false) the output waves
+// only carry their state tiles; zero_v takes every value as zero (the walk
+// then applies the chunks' transition alone).
+template <bool kOut>
 __device__ __forceinline__ void diag_step(DiagOps& cur, f32x4& acc, const DiagCtx& x, int next,
-                                          DiagLds& S, float* __restrict__ o) {
+                                          DiagLds& S, float* __restrict__ o, bool zero_v) {
     const int w = x.w, l = x.l, g = l >> 4, c = l & 15, tt = w & 3;
     const bool state = w < 4;
     // P1
     publish4(S.Sx, w, l, acc);
     __syncthreads();
     // P2
-    const f32x4 yz = prod3<4>(cur.xa, S.Sx, l);
+    f32x4 yz = zero4();
+    if (kOut || state) yz = prod3<4>(cur.xa, S.Sx, l);
     if (state) {
-        const f32x4 vv = {bf16_bits_to_f32(cur.vraw[0]), bf16_bits_to_f32(cur.vraw[1]),
-                          bf16_bits_to_f32(cur.vraw[2]), bf16_bits_to_f32(cur.vraw[3])};
+        const f32x4 vv = zero_v ? zero4()
+                                : f32x4{bf16_bits_to_f32(cur.vraw[0]), bf16_bits_to_f32(cur.vraw[1]),
+                                        bf16_bits_to_f32(cur.vraw[2]),
+                                        bf16_bits_to_f32(cur.vraw[3])};
         publish4(S.Ex, tt, l, vv - yz);
     }
     load_xa(cur, x, next);
@@ -413,7 +419,7 @@ __device__ __forceinline__ void diag_step(DiagOps& cur, f32x4& acc, const DiagCt
     // P4
     const f32x4 upd = prod3<2>(cur.kh, S.Ux, l);
     acc = acc * cur.gc + upd;
-    if (!state) {
+    if (kOut && !state) {
         const f32x4 ov = yz + prod3<2>(cur.fa, S.Ux, l);
         const int t0 = cur.t0, len = cur.len;
 #pragma unroll
@@ -428,15 +434,20 @@ __device__ __forceinline__ void diag_step(DiagOps& cur, f32x4& acc, const DiagCt
     __builtin_amdgcn_sched_barrier(0);
 }
 
+template <bool kOut>
 __global__ __launch_bounds__(kDWaves * 64) void walk_diag_kernel(
     const uint16_t* __restrict__ v, int N, int H, const int32_t* __restrict__ rec,
     const int32_t* __restrict__ seq_off, const int32_t* __restrict__ num_chunks,
-    const unsigned char* __restrict__ factors, const float* __restrict__ S0,
-    float* __restrict__ o, float* __restrict__ S_final) {
-    // XCD-aware mapping: the 8 value slices of one (sequence, head) share the
-    // same blockIdx.x % 8, hence one XCD and its L2, which holds the chunk
+    const unsigned char* __restrict__ factors, float* __restrict__ o, WalkJob j0, WalkJob j1,
+    int seg_chunks) {
+    // Jobs split the grid in halves.  Within a job the mapping is XCD-aware:
+    // the 8 value slices of one (sequence, head) share the same
+    // blockIdx.x % 8, hence one XCD and its L2, which holds the chunk
     // operands all 8 of them read.
-    const int id = blockIdx.x;
+    const int per_job = 64 * ((N * H + 7) / 8);
+    const int job = blockIdx.x >= per_job ? 1 : 0;
+    const WalkJob J = job ? j1 : j0;
+    const int id = blockIdx.x - job * per_job;
     const int xcd = id & 7, rest = id >> 3;
     const int s = rest & 7, pg = rest >> 3;
     const int p = pg * 8 + xcd;
@@ -446,9 +457,16 @@ __global__ __launch_bounds__(kDWaves * 64) void walk_diag_kernel(
     const int w = wave_id(), l = tid & 63, g = l >> 4, c = l & 15;
     __shared__ __attribute__((aligned(16))) DiagLds lds;
 
+    // sequence n's chunks: from the table, or the n-th run of seg_chunks
     const int nch = num_chunks[0];
-    const int c_begin = seq_off[n];
-    const int c_end = seq_off[n + 1] < nch ? seq_off[n + 1] : nch;
+    int c_begin, c_end;
+    if (seg_chunks > 0) {
+        c_begin = n * seg_chunks < nch ? n * seg_chunks : nch;
+        c_end = c_begin + seg_chunks < nch ? c_begin + seg_chunks : nch;
+    } else {
+        c_begin = seq_off[n];
+        c_end = seq_off[n + 1] < nch ? seq_off[n + 1] : nch;
+    }
     int t_begin = 0, t_end = 0;
     if (c_begin < c_end) {
         t_begin = rec[4 * c_begin + 1];
@@ -458,7 +476,14 @@ __global__ __launch_bounds__(kDWaves * 64) void walk_diag_kernel(
 
     // state: lane holds S^T[key 16w + 4g + i][value 16s + c] = S[value][key .. key+3]
     const size_t srow = ((size_t(n) * H + h) * kD + 16 * s + c) * kD + 16 * w + 4 * g;
-    f32x4 acc = S0 ? *reinterpret_cast<const f32x4*>(S0 + srow) : zero4();
+    f32x4 acc = zero4();
+    if (J.identity) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = 16 * w + 4 * g + i == 16 * s + c ? 1.f : 0.f;
+    } else if (J.S0) {
+        acc = *reinterpret_cast<const f32x4*>(J.S0 + srow);
+    }
+    const bool zero_v = J.zero_v != 0;
     if (c_begin < c_end) {
         // two operand sets in turn, a pair of chunks per iteration (no exit
         // between the two steps, so the loads pending at the loop head are
@@ -470,15 +495,46 @@ __global__ __launch_bounds__(kDWaves * 64) void walk_diag_kernel(
         load_all(B, x, c_begin + 1 < c_end ? c_begin + 1 : last);
         int ch = c_begin;
         for (; ch + 1 < c_end; ch += 2) {
-            diag_step(A, acc, x, ch + 2 < c_end ? ch + 2 : last, lds, o);
-            diag_step(B, acc, x, ch + 3 < c_end ? ch + 3 : last, lds, o);
+            diag_step<kOut>(A, acc, x, ch + 2 < c_end ? ch + 2 : last, lds, o, zero_v);
+            diag_step<kOut>(B, acc, x, ch + 3 < c_end ? ch + 3 : last, lds, o, zero_v);
         }
-        if (ch < c_end) diag_step(A, acc, x, last, lds, o);
+        if (ch < c_end) diag_step<kOut>(A, acc, x, last, lds, o, zero_v);
     }
-    if (S_final) *reinterpret_cast<f32x4*>(S_final + srow) = acc;
+    if (J.S_final) *reinterpret_cast<f32x4*>(J.S_final + srow) = acc;
 }
 
 }  // namespace
+
+hipError_t launch_prep_diag(const uint16_t* q, const uint16_t* k, const float* alpha,
+                            const float* b, int32_t heads, int32_t max_chunks, const int32_t* rec,
+                            const int32_t* num_chunks, unsigned char* factors,
+                            hipStream_t stream) {
+    const unsigned pgrid = unsigned(int64_t(max_chunks) * heads);
+    if (pgrid == 0) return hipSuccess;
+    hipLaunchKernelGGL(prep_diag_kernel, dim3(pgrid), dim3(kPrepThreads), 0, stream, q, k, alpha,
+                       b, heads, rec, num_chunks, factors);
+    return hipGetLastError();
+}
+
+hipError_t launch_walk_diag(const uint16_t* v, int32_t num_seqs, int32_t heads,
+                            const int32_t* rec, const int32_t* seq_off,
+                            const int32_t* num_chunks, const unsigned char* factors, float* o,
+                            const WalkJob* jobs, int32_t num_jobs, int32_t seg_chunks,
+                            bool outputs, hipStream_t stream) {
+    const int64_t pairs = int64_t(num_seqs) * heads;
+    const unsigned wgrid = unsigned(num_jobs * 64 * ((pairs + 7) / 8));
+    const WalkJob none{nullptr, nullptr, 0, 0};
+    const WalkJob j1 = num_jobs > 1 ? jobs[1] : none;
+    if (outputs)
+        hipLaunchKernelGGL(walk_diag_kernel<true>, dim3(wgrid), dim3(kDWaves * 64), 0, stream, v,
+                           num_seqs, heads, rec, seq_off, num_chunks, factors, o, jobs[0], j1,
+                           seg_chunks);
+    else
+        hipLaunchKernelGGL(walk_diag_kernel<false>, dim3(wgrid), dim3(kDWaves * 64), 0, stream,
+                           v, num_seqs, heads, rec, seq_off, num_chunks, factors, o, jobs[0], j1,
+                           seg_chunks);
+    return hipGetLastError();
+}
 
 hipError_t launch_prefill_diag(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                const float* alpha, const float* b, int32_t num_seqs,
@@ -486,18 +542,12 @@ hipError_t launch_prefill_diag(const uint16_t* q, const uint16_t* k, const uint1
                                const int32_t* seq_off, const int32_t* num_chunks,
                                unsigned char* factors, const float* S0, float* o,
                                float* S_final, hipStream_t stream) {
-    const unsigned pgrid = unsigned(int64_t(max_chunks) * heads);
-    if (pgrid > 0) {
-        hipLaunchKernelGGL(prep_diag_kernel, dim3(pgrid), dim3(kPrepThreads), 0, stream, q, k,
-                           alpha, b, heads, rec, num_chunks, factors);
-        const hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
-    }
-    const int64_t pairs = int64_t(num_seqs) * heads;
-    const unsigned wgrid = unsigned(64 * ((pairs + 7) / 8));
-    hipLaunchKernelGGL(walk_diag_kernel, dim3(wgrid), dim3(kDWaves * 64), 0, stream, v, num_seqs,
-                       heads, rec, seq_off, num_chunks, factors, S0, o, S_final);
-    return hipGetLastError();
+    const hipError_t err =
+        launch_prep_diag(q, k, alpha, b, heads, max_chunks, rec, num_chunks, factors, stream);
+    if (err != hipSuccess) return err;
+    const WalkJob job{S0, S_final, 0, 0};
+    return launch_walk_diag(v, num_seqs, heads, rec, seq_off, num_chunks, factors, o, &job, 1, 0,
+                            true, stream);
 }
 
 }  // namespace rda

@@ -222,7 +222,9 @@ rda_status rda_decode_tokens(const void* q, const void* k, const void* v, rda_dt
  * takes bf16 q, k, v only (RDA_ERR_UNSUPPORTED for fp32) and its own
  * workspace size.  Any alpha in (0, 1] is safe: the chunked prefill never
  * forms a decay factor above e^60 (it falls back to exact per-element
- * factors where a 16-token block decays by more than that).
+ * factors where a 16-token block decays by more than that).  One sequence
+ * without offsets with few heads takes the segmented state pass described
+ * at rda_prefill (same plan; its workspace size includes the state arrays).
  */
 size_t rda_prefill_diag_workspace_bytes(int32_t num_seqs, int32_t total_tokens,
                                         int32_t num_heads, int32_t dk, int32_t dv);

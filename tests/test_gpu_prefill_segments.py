@@ -149,3 +149,51 @@ def test_bitwise_deterministic(dev):
     a1, b1 = run(p, dev, S0=S0)
     a2, b2 = run(p, dev, S0=S0)
     assert np.array_equal(a1, a2) and np.array_equal(b1, b2)
+
+
+# ---- the per-channel decay (rda_prefill_diag) takes the same segmented pass ----
+
+def diag_run(p, alpha, dev, one_pass=False, S0=None, S_final=None):
+    q, k, v = (dev_tokens(getattr(p, n), True, dev) for n in "qkv")
+    cu = np.array([0, p.total_tokens], dtype=np.int32) if one_pass else None
+    o, Sf = rda.rda_prefill_diag(q, k, v, dev_f32(alpha, dev), dev_f32(p.b, dev), cu_seqlens=cu,
+                                 S0=S0, S_final=S_final)
+    torch.cuda.synchronize()
+    return to_host(o), (to_host(Sf) if Sf is not None else None)
+
+
+@pytest.mark.parametrize("gates", ["long", "default"])
+@pytest.mark.parametrize("T,H", [(4096, 4), (8192 + 37, 2), (16384, 1)])
+def test_diag_against_oracle_and_one_pass(dev, T, H, gates):
+    P = segments(T, H)
+    p = synth.make_prefill(T, H, s0_std=0.02, key=(710, T, H))
+    if gates == "long":
+        rng = np.random.default_rng((710, T, H))
+        alpha = np.exp(-rng.uniform(0.0, 4e-3, (T, H, 128))).astype(np.float32)
+    else:
+        alpha = synth.diag_alpha(T, H, key=(710, T, H))
+    say(f"[segments, per-channel] T={T} H={H} P={P} gates={gates}")
+    S0 = dev_f32(p.S0, dev)
+    o, Sf = diag_run(p, alpha, dev, S0=S0)
+    ro, rS = oracle.prefill_diag(p.q, p.k, p.v, alpha, p.b, S0=p.S0)
+    assert_parity("o", o, ro)
+    assert_parity("S_final", Sf, rS)
+    o1, S1 = diag_run(p, alpha, dev, one_pass=True, S0=S0)
+    for name, x, y in (("o", o, o1), ("S_final", Sf, S1)):
+        rel = float(np.linalg.norm(x - y) / np.linalg.norm(y))
+        say(f"  segmented vs one pass {name}: rel-L2 {rel:.2e}")
+        assert rel < 1e-4
+    if gates == "long":
+        assert not np.array_equal(o, o1)
+
+
+def test_diag_resume_in_place(dev):
+    T, H = 8192, 2
+    p = synth.make_prefill(T, H, s0_std=0.02, key=(711,))
+    alpha = np.exp(-np.random.default_rng(711).uniform(0.0, 4e-3, (T, H, 128))).astype(np.float32)
+    S = dev_f32(p.S0, dev)
+    say("[segments, per-channel] S_final = S0 in place")
+    o, _ = diag_run(p, alpha, dev, S0=S, S_final=S)
+    ro, rS = oracle.prefill_diag(p.q, p.k, p.v, alpha, p.b, S0=p.S0)
+    assert_parity("o", o, ro)
+    assert_parity("S_final in place", to_host(S), rS)
