@@ -167,9 +167,11 @@ def main():
              "# P = 8 segments: prep, walk_bf16_kernel<false> (every segment from zero and",
              "# from the identity), segment_combine_kernel, walk_bf16_kernel<true> (outputs);",
              "# then the same inputs through the one-pass walk (cu_seqlens = {0, T}: chunk",
-             "# table, prep, walk_bf16_kernel<true>); 11 calls of each, each after a 512 MiB",
-             "# read (reduce_kernel: the cache flush).  walk_bf16_kernel<true> averages the",
-             "# output pass and the one-pass walk.",
+             "# table, prep, walk_bf16_kernel<true>); then the same two ways with a",
+             "# per-channel decay (prep_diag_kernel, walk_diag_kernel<false>, the combine,",
+             "# walk_diag_kernel<true>); 11 calls of each, each after a 512 MiB read",
+             "# (reduce_kernel: the cache flush).  The <true> walks average the output pass",
+             "# and the one-pass walk; the combine averages the two decays.",
              "# command: gated_delta_amd/profile_run.sh OUTDIR, whose sixth pass is",
              "#   rocprofv3 --kernel-trace --stats --output-format csv -d OUTDIR/prof_trace_seg -o trace \\",
              "#     -- python bench.py --mode segments --steps 10 --no-cpu",

@@ -53,7 +53,7 @@ def run(p, dev, one_pass=False, S0=None, S_final=None, want_state=True):
 
 
 @pytest.mark.parametrize("gates", ["long", "default"])
-@pytest.mark.parametrize("T,H", [(4096, 4), (8192 + 37, 2), (16384, 1), (16384, 2)])
+@pytest.mark.parametrize("T,H", [(4096, 4), (8192 + 37, 2), (16384, 1), (16384, 2), (16384, 3)])
 def test_against_oracle_and_one_pass(dev, T, H, gates):
     P = segments(T, H)
     assert P >= 4
