@@ -422,6 +422,23 @@ def extra_measurements(args, out, torch, np, rda, synth, dev, stream, q, k, v, a
             if rda.lib().rda_prefill(*cargs) != 0:
                 raise RuntimeError("rda_prefill failed")
         sec = timed(call, 10, flush)
+        graph_ms = None
+        if cid == 1:
+            # launch-bound: the same call captured once in a HIP graph, replayed
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                call()
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                gcargs = list(cargs)
+                gcargs[-1] = torch.cuda.current_stream().cuda_stream
+                if rda.lib().rda_prefill(*gcargs) != 0:
+                    raise RuntimeError("rda_prefill failed")
+            torch.cuda.synchronize()
+            graph_ms = timed(graph.replay, 10, flush) * 1e3
         units = Tc * Hc
         entry = {"T": Tc, "H": Hc, "N": pc.num_seqs, "qkv": "bf16" if pc.bf16 else "fp32",
                  "ms_per_call": sec * 1e3, "tokens_per_s": Tc / sec,
@@ -429,6 +446,8 @@ def extra_measurements(args, out, torch, np, rda, synth, dev, stream, q, k, v, a
                  "hbm_frac_algorithmic": (PREFILL_BYTES * units +
                                           (2 if S0c is not None else 1) * pc.num_seqs * Hc *
                                           STATE_BYTES) / sec / 1e9 / PEAK_HBM_GBPS}
+        if graph_ms is not None:
+            entry["ms_per_call_graph_replay"] = graph_ms
         if not args.no_cpu:
             import oracle
             ro, rS = oracle.prefill(pc.q, pc.k, pc.v, pc.a, pc.b, cu_seqlens=cuc, S0=pc.S0,

@@ -37,7 +37,9 @@
  *   j = key channel (column); outputs o [T, H, dv] fp32.
  * - Only dk = dv = 128 is supported (RDA_ERR_UNSUPPORTED otherwise).
  * - Work is enqueued asynchronously on `stream` (0 = the null stream); no
- *   entry point synchronises the host.  Argument checks run on the host
+ *   entry point synchronises the host.  Entry points only launch kernels (no
+ *   allocation, memset or copy), so a caller may capture them in a HIP
+ *   graph and replay it.  Argument checks run on the host
  *   before anything is enqueued; on an error nothing is launched.  Launch
  *   failures return RDA_ERR_HIP.  Nothing aborts, throws or prints.
  * - Gates must satisfy a in (0, 1] and b in [0, 1]; other values are not
