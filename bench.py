@@ -11,7 +11,9 @@ Prints ONE JSON line:
              one rda_prefill call between HIP events on its stream (prep,
              then walk; the decode step between calls streams 512 MiB, so no
              prefill starts with its inputs in the Infinity Cache)
-  decode     decode state bandwidth (algorithmic bytes / kernel time)
+  decode     decode state bandwidth (algorithmic bytes / kernel time) of the
+             steps between prefill calls, and of 128 steps back to back
+             (back_to_back_128)
   roofline   the kernel with the largest time per step, against its bound
   kernels    every kernel's average duration (HIP events on its stream), from
              calls of rda_prefill_profiled; for one sequence without offsets
@@ -311,6 +313,22 @@ def main():
         kernels["rda_decode_step"] = {"avg_us": dsec * 1e6, "alg_bytes": dbytes}
         if "value" not in out:
             out["value"], out["unit"] = gbps, "GB/s"
+        if not args.no_extras:
+            # 128 decode steps back to back (the serving loop), one event pair
+            # around all of them
+            torch.cuda.synchronize()
+            e0, e1 = make_events(2)
+            e0.record(stream)
+            for i in range(NTOK):
+                qt, kt, vt, at, bt = toks[i]
+                rda.rda_decode_step(qt, kt, vt, at, bt, S_dec, o=o_dec)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            bsec = e0.elapsed_time(e1) * 1e-3 / NTOK
+            out["decode"]["back_to_back_128"] = {"us_per_step": bsec * 1e6,
+                                                 "GBps": dbytes / bsec / 1e9,
+                                                 "frac_of_peak": dbytes / bsec / 1e9
+                                                 / PEAK_HBM_GBPS}
     out["kernels"] = kernels
 
     # roofline of the kernel with the largest time per step

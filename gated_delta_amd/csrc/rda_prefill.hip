@@ -256,10 +256,10 @@ constexpr int kWalkThreads = kWalkWaves * 64;
 constexpr int kKS = 136;   // LDS K / Q tile row stride (bf16 elements)
 constexpr int kVS = 20;    // LDS V slice row stride (bf16 elements)
 
+// (bf16 inputs take the walk in rda_walk.hip; this one serves fp32 inputs,
+// fed to MFMA as bf16 hi + lo planes)
 template <typename TIn>
 struct WalkIn;
-template <>
-struct WalkIn<uint16_t> { static constexpr bool kSplit = false; };
 template <>
 struct WalkIn<float> { static constexpr bool kSplit = true; };
 
