@@ -109,18 +109,27 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(const float* S0,
             const size_t idx = rows + size_t(4 * g + e) * kD + 32 * w + 16 * u + c;
             S_in[idx] = S0 ? S0[idx] : 0.f;
         }
-    for (int p = 0; p < steps; ++p) {
-        // this wave's part of M_p has landed once at most the 8 row stores
-        // issued after it are in flight; after the barrier, all of M_p has
-        wait_vm<8>();
-        lds_barrier();
-        f32x4 ev[2];
+    // E_p's values at this lane's outputs, loaded one step ahead like M_p
+    auto load_e = [&](int p, f32x4 (&ev)[2]) {
         const float* Ep = E + p * seg;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 ev[u][e] = Ep[rows + size_t(4 * g + e) * kD + 32 * w + 16 * u + c];
+    };
+    f32x4 ev_next[2];
+    if (steps > 0) load_e(0, ev_next);
+    for (int p = 0; p < steps; ++p) {
+        // this wave's part of M_p and its E_p values (issued before M_p) have
+        // landed once at most the 8 row stores issued after them are in
+        // flight; after the barrier, all of M_p has
+        wait_vm<8>();
+        lds_barrier();
+        const f32x4 ev[2] = {ev_next[0], ev_next[1]};
+        if (p + 1 < steps) load_e(p + 1, ev_next);
+        else load_e(p, ev_next);   // a fixed count of loads keeps the waits exact
+        __builtin_amdgcn_sched_barrier(0);   // issue them here, not after the products
         // the next step's matrix, one step ahead, in two halves issued before
         // the two halves of the products (the last step fetches its own again,
         // unread: a fixed count of loads keeps the waits exact)
@@ -148,7 +157,6 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(const float* S0,
                 acc1 = mfma_f32(aS[16 * half + i], b1[i], acc1);
             }
         }
-        wait_vm<16>();   // the E values, loaded before the 16 prefetches
         const f32x4 n0 = acc0 + ev[0], n1 = acc1 + ev[1];
         float* dst = p + 1 < P ? S_in + (p + 1) * seg : S_final;
 #pragma unroll
