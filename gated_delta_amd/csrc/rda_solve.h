@@ -41,34 +41,46 @@ __device__ __forceinline__ void pack_rows(const float* M, const float* colscale,
     }
 }
 
+// Step m of the column-oriented substitution in a 16 x 16 diagonal block:
+// x_r -= L_rm x_m on every lane, with x_m taken from lane m of the same
+// 16-lane row (DPP row_newbcast:m), then steps m + 1 .. 14.
+template <int kM>
+__device__ __forceinline__ void substitute_col_step(float (&x)[4], const float (&Lrow)[16]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float xm = __int_as_float(
+            __builtin_amdgcn_update_dpp(0, __float_as_int(x[j]), 0x150 + kM, 0xF, 0xF, false));
+        x[j] -= Lrow[kM] * xm;
+    }
+    if constexpr (kM < 14) substitute_col_step<kM + 1>(x, Lrow);
+}
+
 // T = (I + L)^-1 for the strictly lower L in Ls (row stride kFS; Ts must
 // hold zeros above the diagonal); one call by every wavefront of the
 // workgroup (w = wave, g = lane / 16, c = lane % 16), of which waves 0-3 do
 // the work; Rs is 3 x 256 floats of scratch.  Ends with a workgroup barrier.
 __device__ __forceinline__ void solve_unit_lower(const float* Ls, float* Ts, float* Rs, int w,
                                                  int g, int c) {
-    // (a) diagonal 16x16 blocks by forward substitution, one wavefront per block:
-    //     lane (column c, part g) keeps x[m] for m = g (mod 4); each row step
-    //     sums its part of L[r][m] x[m] and reduces across the four parts.
+    // (a) diagonal 16x16 blocks, one wavefront per block: lane (g, r = c)
+    //     holds row r of columns 4g .. 4g+3, starting from the identity.
+    //     Column-oriented forward substitution: once x_m is final, every row
+    //     r > m takes x_r -= L_rm x_m, x_m broadcast inside each 16-lane row
+    //     by DPP; L is zero on and above the diagonal, so rows r <= m are
+    //     left unchanged without a branch.
     if (w < 4) {
-        const int base = 16 * w;
-        float xs[4] = {0.f, 0.f, 0.f, 0.f};
+        const int base = 16 * w, r = c;
+        float Lrow[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float part = 0.f;
+        for (int m4 = 0; m4 < 4; ++m4) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(Ls + (base + r) * kFS + base + 4 * m4);
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const int m = 4 * qq + g;
-                if (m < r) part += Ls[(base + r) * kFS + base + m] * xs[qq];
-            }
-            part += __shfl_xor(part, 16, 64);
-            part += __shfl_xor(part, 32, 64);
-            const float x = (r == c ? 1.f : 0.f) - part;
-            if ((r & 3) == g) {
-                xs[r >> 2] = x;
-                Ts[(base + r) * kFS + base + c] = x;
-            }
+            for (int e = 0; e < 4; ++e) Lrow[4 * m4 + e] = v[e];
         }
+        float x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = r == 4 * g + j ? 1.f : 0.f;
+        substitute_col_step<0>(x, Lrow);
+        *reinterpret_cast<f32x4*>(Ts + (base + r) * kFS + base + 4 * g) = f32x4{x[0], x[1], x[2], x[3]};
     }
     __syncthreads();
     // (b) off-diagonal blocks, block row by block row, on fp32 MFMA:
