@@ -90,37 +90,58 @@ __device__ __forceinline__ void scaled_keys(const PrepDiagLds& S, const uint16_t
 }
 
 constexpr int kPrepThreads = 1024;
+constexpr int64_t kPrepDiagGrid = 256;
 
 __global__ __launch_bounds__(kPrepThreads) void prep_diag_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ alpha,
     const float* __restrict__ b, int H, const int32_t* __restrict__ rec,
     const int32_t* __restrict__ num_chunks, unsigned char* __restrict__ factors) {
     __shared__ __attribute__((aligned(16))) PrepDiagLds S;
-    const int chunk = blockIdx.x / H;
-    const int h = blockIdx.x - chunk * H;
-    if (chunk >= num_chunks[0]) return;
-    const int64_t t0 = rec[4 * chunk + 1];
-    const int len = rec[4 * chunk + 2];
-    const int tid = threadIdx.x;
-    const int w = wave_id(), l = tid & 63, g = l >> 4, c = l & 15;
-    unsigned char* F = factors + (size_t(chunk) * H + h) * kDiagChunkHeadBytes;
+    // Persistent: the workgroup takes items (chunk, head) blockIdx.x,
+    // blockIdx.x + gridDim.x, ... and loads the next item's inputs into
+    // registers while it works on the current one (one workgroup fills a CU,
+    // so nothing else would hide that load's latency).
+    const int total = num_chunks[0] * H;
+    int item = blockIdx.x;
+    if (item >= total) return;
 
-    // ---- every global load of the workgroup first (one memory latency):
-    //      K, Q rows, b, and alpha for (channel, eighth of 8 tokens) ---------
-    u16x8 xk = {0, 0, 0, 0, 0, 0, 0, 0}, xq = xk;
-    const int sr = tid >> 4, sc8 = (tid & 15) * 8;
-    if (sr < len) {
-        xk = *reinterpret_cast<const u16x8*>(k + ((t0 + sr) * H + h) * kD + sc8);
-        xq = *reinterpret_cast<const u16x8*>(q + ((t0 + sr) * H + h) * kD + sc8);
-    }
-    const float bv = tid < len ? b[(t0 + tid) * H + h] : 0.f;
-    const int ch = tid & 127, qt = tid >> 7;
-    float al[8];
+    // K, Q rows, b, and alpha for (channel, eighth of 8 tokens) of one item;
+    // rows past the chunk's end read as zero keys, b = 0 and alpha = 1
+    u16x8 xk, xq;
+    float bv, al[8];
+    auto load_item = [&](int it) {
+        const int tid = threadIdx.x;
+        const int sr = tid >> 4, sc8 = (tid & 15) * 8;
+        const int ch = tid & 127, qt = tid >> 7;
+        const int ck = it / H, hh = it - ck * H;
+        const int64_t s0 = rec[4 * ck + 1];
+        const int n = rec[4 * ck + 2];
+        xk = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        xq = xk;
+        if (sr < n) {
+            xk = *reinterpret_cast<const u16x8*>(k + ((s0 + sr) * H + hh) * kD + sc8);
+            xq = *reinterpret_cast<const u16x8*>(q + ((s0 + sr) * H + hh) * kD + sc8);
+        }
+        bv = tid < n ? b[(s0 + tid) * H + hh] : 0.f;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const int row = 8 * qt + r;
-        al[r] = row < len ? alpha[((t0 + row) * H + h) * kD + ch] : 1.f;
-    }
+        for (int r = 0; r < 8; ++r) {
+            const int row = 8 * qt + r;
+            al[r] = row < n ? alpha[((s0 + row) * H + hh) * kD + ch] : 1.f;
+        }
+    };
+    load_item(item);
+    for (;;) {
+    // the lane's indices, opaque to the compiler on every item, so that
+    // nothing derived from them is kept live across items
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int w = wave_id(), l = tid & 63, g = l >> 4, c = l & 15;
+    const int sr = tid >> 4, sc8 = (tid & 15) * 8;
+    const int ch = tid & 127, qt = tid >> 7;
+    const int chunk = item / H;
+    const int h = item - chunk * H;
+    unsigned char* F = factors + (size_t(chunk) * H + h) * kDiagChunkHeadBytes;
+    const int next = item + int(gridDim.x);
     // ---- stage K, Q (rows past the chunk's end are zero), b; zero T and A;
     //      G = running sum of log2(alpha) per channel, each eighth of the
     //      chunk first on its own, then offset by the eighths before it
@@ -140,6 +161,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_diag_kernel(
             S.G[8 * qt + r][ch] = run;
         }
     }
+    // this item's registers are in LDS: the next item's loads go out now
+    if (next < total) load_item(next);
     __syncthreads();
     {
         float base = 0.f;
@@ -258,6 +281,10 @@ __global__ __launch_bounds__(kPrepThreads) void prep_diag_kernel(
     solve_unit_lower(S.L, S.T, S.R, w, g, c);
     if (tid < 256) pack_rows(S.T, S.bb, reinterpret_cast<bf16x8*>(F + kDOffTb), tid);
     else if (tid < 512) pack_rows(S.A, nullptr, reinterpret_cast<bf16x8*>(F + kDOffA), tid - 256);
+    if (next >= total) break;
+    item = next;
+    __syncthreads();   // T, A and the staged rows are rewritten next
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -509,7 +536,9 @@ hipError_t launch_prep_diag(const uint16_t* q, const uint16_t* k, const float* a
                             const float* b, int32_t heads, int32_t max_chunks, const int32_t* rec,
                             const int32_t* num_chunks, unsigned char* factors,
                             hipStream_t stream) {
-    const unsigned pgrid = unsigned(int64_t(max_chunks) * heads);
+    // one persistent workgroup per CU at most (each holds a CU's LDS)
+    const int64_t items = int64_t(max_chunks) * heads;
+    const unsigned pgrid = unsigned(items < kPrepDiagGrid ? items : kPrepDiagGrid);
     if (pgrid == 0) return hipSuccess;
     hipLaunchKernelGGL(prep_diag_kernel, dim3(pgrid), dim3(kPrepThreads), 0, stream, q, k, alpha,
                        b, heads, rec, num_chunks, factors);
