@@ -67,6 +67,20 @@ def test_packed_sequences(dev):
     assert np.array_equal(to_host(S)[1], p.S0[1])          # empty sequence: S0 unchanged
 
 
+def test_packed_sequences_many_items(dev):
+    """More (chunk, head) items than prep workgroups: each workgroup takes
+    several items, its prefetch crossing sequence ends and partial chunks."""
+    lens = [1000, 37, 2050, 0, 513, 64]
+    p, alpha = case(0, 16, (607,), lengths=lens)
+    say(f"[prefill_diag] packed {lens}")
+    o, S = run_gpu(p, alpha, dev)
+    torch.cuda.synchronize()
+    ro, rS = oracle.prefill_diag(p.q, p.k, p.v, alpha, p.b, cu_seqlens=p.cu_seqlens, S0=p.S0)
+    assert_parity("o", to_host(o), ro)
+    assert_parity("S_final", to_host(S), rS)
+    assert np.array_equal(to_host(S)[3], p.S0[3])          # empty sequence: S0 unchanged
+
+
 @pytest.mark.parametrize("kind", ["fast_channels", "near_one", "mixed_blocks"])
 def test_decay_regimes(dev, kind):
     """Decays small enough that a 16-token block decays beyond e^60 on some
