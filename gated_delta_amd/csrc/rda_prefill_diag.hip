@@ -233,46 +233,54 @@ __global__ __launch_bounds__(kPrepThreads) void prep_diag_kernel(
     if (tid < kD) reinterpret_cast<float*>(F + kDOffGC)[tid] = exp2_hw(S.G[kC - 1][tid]);
     __syncthreads();
 
-    // ---- L and A from 16 x 16 sub-blocks: 10 blocks (I >= J) x {L, A} -------
-    for (int task = w; task < 20; task += kPrepThreads / 64) {
-        const bool isq = task >= 10;
-        const int idx = isq ? task - 10 : task;
-        const int I = (idx >= 1) + (idx >= 3) + (idx >= 6);
-        const int J = idx - I * (I + 1) / 2;
-        const uint16_t(*X)[kKS] = isq ? S.Q : S.K;
-        f32x4 acc = zero4();
+    // ---- L and A from 16 x 16 sub-blocks: one task per block (I >= J) forms
+    //      both, sharing the scaled key rows of block J --------------------
+    if (w < 10) {
+        const int I = (w >= 1) + (w >= 3) + (w >= 6);
+        const int J = w - I * (I + 1) / 2;
+        f32x4 accL = zero4(), accA = zero4();
         if (I > J || !S.exact[J]) {
             const int ref = I > J ? 16 * J + 15 : 16 * J;
-            f32x4 p0 = zero4(), p1 = zero4(), p2 = zero4();
-#pragma unroll
+            f32x4 l0 = zero4(), l1 = zero4(), l2 = zero4();
+            f32x4 a0 = zero4(), a1 = zero4(), a2 = zero4();
+#pragma unroll 2
             for (int m = 0; m < 4; ++m) {
-                bf16x8 ah, al, bh, bl;
-                scaled_keys(S, X, 16 * I + c, ref, m, g, false, ah, al);
+                bf16x8 bh, bl, xh, xl;
                 scaled_keys(S, S.K, 16 * J + c, ref, m, g, true, bh, bl);
-                p0 = mfma_bf16(ah, bh, p0);
-                p1 = mfma_bf16(ah, bl, p1);
-                p2 = mfma_bf16(al, bh, p2);
+                scaled_keys(S, S.K, 16 * I + c, ref, m, g, false, xh, xl);
+                l0 = mfma_bf16(xh, bh, l0);
+                l1 = mfma_bf16(xh, bl, l1);
+                l2 = mfma_bf16(xl, bh, l2);
+                scaled_keys(S, S.Q, 16 * I + c, ref, m, g, false, xh, xl);
+                a0 = mfma_bf16(xh, bh, a0);
+                a1 = mfma_bf16(xh, bl, a1);
+                a2 = mfma_bf16(xl, bh, a2);
             }
-            acc = p0 + p1 + p2;
+            accL = l0 + l1 + l2;
+            accA = a0 + a1 + a2;
         } else {
             // exact: every factor e^{G_i - G_j} <= 1 formed on its own
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int ri = 16 * I + 4 * g + i, sj = 16 * J + c;
-                float s = 0.f;
+                float sl = 0.f, sa = 0.f;
                 if (ri >= sj)
-                    for (int key = 0; key < kD; ++key)
-                        s = fmaf(bf16_bits_to_f32(X[ri][key]) * bf16_bits_to_f32(S.K[sj][key]),
-                                 exp2_hw(S.G[ri][key] - S.G[sj][key]), s);
-                acc[i] = s;
+                    for (int key = 0; key < kD; ++key) {
+                        const float kj = bf16_bits_to_f32(S.K[sj][key]) *
+                                         exp2_hw(S.G[ri][key] - S.G[sj][key]);
+                        sl = fmaf(bf16_bits_to_f32(S.K[ri][key]), kj, sl);
+                        sa = fmaf(bf16_bits_to_f32(S.Q[ri][key]), kj, sa);
+                    }
+                accL[i] = sl;
+                accA[i] = sa;
             }
         }
         const int sj = 16 * J + c;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int ri = 16 * I + 4 * g + i;
-            if (isq) S.A[ri * kFS + sj] = ri >= sj ? acc[i] : 0.f;
-            else S.L[ri * kFS + sj] = ri > sj ? S.bb[ri] * acc[i] : 0.f;
+            S.A[ri * kFS + sj] = ri >= sj ? accA[i] : 0.f;
+            S.L[ri * kFS + sj] = ri > sj ? S.bb[ri] * accL[i] : 0.f;
         }
     }
     __syncthreads();
