@@ -182,55 +182,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_diag_kernel(
         if (l == 0) S.exact[w] = span > kSpanMax ? 1 : 0;
     }
 
-    // ---- decayed operands, packed for the walk ----------------------------
-    bf16x8* Kt = reinterpret_cast<bf16x8*>(F + kDOffKt);
-    bf16x8* Qt = reinterpret_cast<bf16x8*>(F + kDOffQt);
-    bf16x8* Kh = reinterpret_cast<bf16x8*>(F + kDOffKh);
-    {
-        // (K e^G), (Q e^G): slot (token tile tt, key block m): row 16tt + lane % 16
-        const int idx = tid;
-        const int lp = idx & 63, m = (idx >> 6) & 3, tt = idx >> 8, gp = lp >> 4;
-        const int row = 16 * tt + (lp & 15);
-        float vk[8], vq[8];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = 32 * m + 16 * hh + 4 * gp + i;
-                const float e = exp2_hw(S.G[row][key]);
-                vk[4 * hh + i] = bf16_bits_to_f32(S.K[row][key]) * e;
-                vq[4 * hh + i] = bf16_bits_to_f32(S.Q[row][key]) * e;
-            }
-        bf16x8 hk, lk, hq, lq;
-        split8(vk, hk, lk);
-        split8(vq, hq, lq);
-        const int base = ((tt * 4 + m) * 2) * 64 + lp;
-        Kt[base] = hk;
-        Kt[base + 64] = lk;
-        Qt[base] = hq;
-        Qt[base + 64] = lq;
-    }
-    {
-        // (K e^{G_C - G})^T: slot (key tile kt, token block m): key 16kt + lane % 16
-        const int idx = tid;
-        const int lp = idx & 63, m = (idx >> 6) & 1, kt = idx >> 7, gp = lp >> 4;
-        const int key = 16 * kt + (lp & 15);
-        const float gc = S.G[kC - 1][key];
-        float v[8];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tok = 32 * m + 16 * hh + 4 * gp + i;
-                v[4 * hh + i] = bf16_bits_to_f32(S.K[tok][key]) * exp2_hw(gc - S.G[tok][key]);
-            }
-        bf16x8 hi, lo;
-        split8(v, hi, lo);
-        const int base = ((kt * 2 + m) * 2) * 64 + lp;
-        Kh[base] = hi;
-        Kh[base + 64] = lo;
-    }
-    if (tid < kD) reinterpret_cast<float*>(F + kDOffGC)[tid] = exp2_hw(S.G[kC - 1][tid]);
+    // the exact-path flags are read by every Gram task
     __syncthreads();
 
     // ---- L and A from 16 x 16 sub-blocks: one task per block (I >= J) forms
@@ -282,6 +234,56 @@ __global__ __launch_bounds__(kPrepThreads) void prep_diag_kernel(
             S.A[ri * kFS + sj] = ri >= sj ? accA[i] : 0.f;
             S.L[ri * kFS + sj] = ri > sj ? S.bb[ri] * accL[i] : 0.f;
         }
+    } else {
+        // ---- the other 6 waves meanwhile: decayed operands, packed for the
+        //      walk (global stores only, so no barrier between the two) ----
+        bf16x8* Kt = reinterpret_cast<bf16x8*>(F + kDOffKt);
+        bf16x8* Qt = reinterpret_cast<bf16x8*>(F + kDOffQt);
+        bf16x8* Kh = reinterpret_cast<bf16x8*>(F + kDOffKh);
+        for (int idx = tid - 640; idx < 1024; idx += 384) {
+            // (K e^G), (Q e^G): slot (token tile tt, key block m): row 16tt + lane % 16
+            const int lp = idx & 63, m = (idx >> 6) & 3, tt = idx >> 8, gp = lp >> 4;
+            const int row = 16 * tt + (lp & 15);
+            float vk[8], vq[8];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = 32 * m + 16 * hh + 4 * gp + i;
+                    const float e = exp2_hw(S.G[row][key]);
+                    vk[4 * hh + i] = bf16_bits_to_f32(S.K[row][key]) * e;
+                    vq[4 * hh + i] = bf16_bits_to_f32(S.Q[row][key]) * e;
+                }
+            bf16x8 hk, lk, hq, lq;
+            split8(vk, hk, lk);
+            split8(vq, hq, lq);
+            const int base = ((tt * 4 + m) * 2) * 64 + lp;
+            Kt[base] = hk;
+            Kt[base + 64] = lk;
+            Qt[base] = hq;
+            Qt[base + 64] = lq;
+        }
+        for (int idx = tid - 640; idx < 1024; idx += 384) {
+            // (K e^{G_C - G})^T: slot (key tile kt, token block m): key 16kt + lane % 16
+            const int lp = idx & 63, m = (idx >> 6) & 1, kt = idx >> 7, gp = lp >> 4;
+            const int key = 16 * kt + (lp & 15);
+            const float gc = S.G[kC - 1][key];
+            float v[8];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tok = 32 * m + 16 * hh + 4 * gp + i;
+                    v[4 * hh + i] = bf16_bits_to_f32(S.K[tok][key]) * exp2_hw(gc - S.G[tok][key]);
+                }
+            bf16x8 hi, lo;
+            split8(v, hi, lo);
+            const int base = ((kt * 2 + m) * 2) * 64 + lp;
+            Kh[base] = hi;
+            Kh[base + 64] = lo;
+        }
+        for (int e = tid - 640; e < kD; e += 384)
+            reinterpret_cast<float*>(F + kDOffGC)[e] = exp2_hw(S.G[kC - 1][e]);
     }
     __syncthreads();
 
