@@ -63,6 +63,7 @@ struct PrepDiagLds {
     uint16_t K[kC][kKS];
     uint16_t Q[kC][kKS];
     float G[kC][kGS];        // running sum of log2(alpha) per key channel
+    float Gtot[8][kD];       // each eighth of the chunk's own sum per channel
     float L[kC * kFS];
     float A[kC * kFS];
     float T[kC * kFS];
@@ -153,24 +154,22 @@ __global__ __launch_bounds__(kPrepThreads) void prep_diag_kernel(
         S.A[e] = 0.f;
     }
     {
-        float run = 0.f;
+        float run[8];
+        float acc = 0.f;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             // beyond any fp32-visible decay; keeps G finite
-            run += fmaxf(__builtin_amdgcn_logf(al[r]), -1000.f);
-            S.G[8 * qt + r][ch] = run;
+            acc += fmaxf(__builtin_amdgcn_logf(al[r]), -1000.f);
+            run[r] = acc;
         }
-    }
-    // this item's registers are in LDS: the next item's loads go out now
-    if (next < total) load_item(next);
-    __syncthreads();
-    {
-        float base = 0.f;
-        for (int p = 0; p < qt; ++p) base += S.G[8 * p + 7][ch];
+        S.Gtot[qt][ch] = acc;
+        // this item's inputs are in LDS or registers: the next item's loads go out now
+        if (next < total) load_item(next);
         __syncthreads();
-        if (qt > 0)
+        float base = 0.f;
+        for (int p = 0; p < qt; ++p) base += S.Gtot[p][ch];
 #pragma unroll
-            for (int r = 0; r < 8; ++r) S.G[8 * qt + r][ch] += base;
+        for (int r = 0; r < 8; ++r) S.G[8 * qt + r][ch] = qt > 0 ? run[r] + base : run[r];
     }
     __syncthreads();
     // diagonal block w: is the decay across it within e^60 on every channel?
