@@ -2,8 +2,8 @@
 //
 // Per (batch, head) the state S [128 x 128] fp32 (row i = value channel,
 // column j = key channel) is read once and written once.  The recurrent
-// step -- decay, error of the value against the decayed state's prediction
-// for the key, beta-weighted write, read-out with the updated state -- is
+// step -- decay, the residual e = v - S'k of the decayed state at the key,
+// the rank-one write b e k^T, read-out with the updated state -- is
 // the one the "Raon-1 nano" teardown (section "The other 1.5B: a hybrid
 // built to forget") describes.  Because each row of S is updated
 // independently, one pass suffices: for row i,

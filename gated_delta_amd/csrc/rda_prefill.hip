@@ -1,7 +1,7 @@
 // rda_prefill.hip -- chunked prefill of the RDA gated delta rule on gfx950.
 //
-// The recurrence (decay, error of the value against the decayed state's
-// prediction for the key, beta-weighted write, read-out after the update; the
+// The recurrence (decay, the residual e = v - S'k of the decayed state at
+// the key, the rank-one write b e k^T, read-out after the update; the
 // "Raon-1 nano" teardown, section "The other 1.5B: a hybrid built to forget")
 // is evaluated in chunks of C = 64 tokens.  With S the state entering a chunk
 // (rows = value channels), g_i the in-chunk running sum of log a,
@@ -49,6 +49,7 @@
 // accumulator tile pair is then a ready B operand with no data movement.
 #include "rda_device.h"
 #include "rda_internal.h"
+#include "rda_lds.h"
 #include "rda_solve.h"
 
 namespace rda {
@@ -366,27 +367,6 @@ __device__ __forceinline__ void load_all(WalkOps<WalkIn<TIn>::kSplit>& o, const 
 // LDS exchange buffers hold ready 16-byte B operands: entry [blk][hl][lane]
 // is key (or token) block blk, whose low 8 bytes come from tile 2 blk and
 // high 8 bytes from tile 2 blk + 1, each written by the wave owning it.
-__device__ __forceinline__ void put_half(u32x4 (*X)[2][64], int tile, int l, u32x2 hi, u32x2 lo) {
-    u32x2* hp = reinterpret_cast<u32x2*>(&X[tile >> 1][0][l]) + (tile & 1);
-    u32x2* lp = reinterpret_cast<u32x2*>(&X[tile >> 1][1][l]) + (tile & 1);
-    *hp = hi;
-    *lp = lo;
-}
-
-__device__ __forceinline__ void publish4(u32x4 (*X)[2][64], int tile, int l, f32x4 v) {
-    uint32_t h01, l01, h23, l23;
-    split_pk(v[0], v[1], h01, l01);
-    split_pk(v[2], v[3], h23, l23);
-    put_half(X, tile, l, u32x2{h01, h23}, u32x2{l01, l23});
-}
-
-__device__ __forceinline__ bf16x8 ldsop(u32x4 (*X)[2][64], int blk, int hl, int l) {
-    return __builtin_bit_cast(bf16x8, X[blk][hl][l]);
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
 // Transposed operand from a row-major bf16 LDS tile (row stride `stride`):
 // lane (g = l/16, c = l%16) receives column col0 + c of rows
 // {r0 + i, r0 + 16 + i : i < 4} with r0 = 32m + 4g (the permuted token order).

@@ -47,6 +47,7 @@
 // hi*lo + lo*hi (about 2^-16 relative) with fp32 accumulation.
 #include "rda_device.h"
 #include "rda_internal.h"
+#include "rda_lds.h"
 #include "rda_solve.h"
 
 namespace rda {
@@ -391,24 +392,6 @@ struct DiagLds {
     u32x4 Ex[2][2][64];   // E (hi/lo), token blocks 0, 1
     u32x4 Ux[2][2][64];   // U (hi/lo)
 };
-
-__device__ __forceinline__ void put_half(u32x4 (*X)[2][64], int tile, int l, u32x2 hi, u32x2 lo) {
-    u32x2* hp = reinterpret_cast<u32x2*>(&X[tile >> 1][0][l]) + (tile & 1);
-    u32x2* lp = reinterpret_cast<u32x2*>(&X[tile >> 1][1][l]) + (tile & 1);
-    *hp = hi;
-    *lp = lo;
-}
-
-__device__ __forceinline__ void publish4(u32x4 (*X)[2][64], int tile, int l, f32x4 v) {
-    uint32_t h01, l01, h23, l23;
-    split_pk(v[0], v[1], h01, l01);
-    split_pk(v[2], v[3], h23, l23);
-    put_half(X, tile, l, u32x2{h01, h23}, u32x2{l01, l23});
-}
-
-__device__ __forceinline__ bf16x8 ldsop(u32x4 (*X)[2][64], int blk, int hl, int l) {
-    return __builtin_bit_cast(bf16x8, X[blk][hl][l]);
-}
 
 // hi*hi + hi*lo + lo*hi over `nb` k blocks: A from registers, B from LDS
 template <int nb>

@@ -16,14 +16,13 @@
 // diagonal blocks by forward substitution with one lane per column (no
 // cross-lane reductions), the off-diagonal blocks by block substitution on
 // fp32 MFMA.
-#include "rda_device.h"
 #include "rda_internal.h"
+#include "rda_lds.h"
+#include "rda_solve.h"
 
 namespace rda {
 
 namespace {
-
-constexpr int kFS = 68;   // fp32 64 x 64 matrix row stride (floats): spreads LDS banks
 
 struct PrepLds {
     union {
@@ -41,32 +40,6 @@ struct PrepLds {
 };
 
 static_assert(sizeof(PrepLds) <= 40 * 1024, "four workgroups per CU");
-
-__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Row r of a swizzled tile, natural k order: lane (g, c) gets elements
-// 32m + 8g .. +7 (one 16-byte granule).
-__device__ __forceinline__ bf16x8 row_op(const uint16_t* T, int r, int m, int g) {
-    const unsigned char* row = reinterpret_cast<const unsigned char*>(T) + r * 256;
-    return __builtin_bit_cast(bf16x8,
-                              *reinterpret_cast<const u32x4*>(row + 16 * ((4 * m + g) ^ swz(r))));
-}
-
-// Step m of the column-oriented substitution in a 16 x 16 diagonal block:
-// x_r -= L_rm x_m on every lane, with x_m taken from lane m of the same
-// 16-lane row (DPP row_newbcast:m), then steps m + 1 .. 14.
-template <int kM>
-__device__ __forceinline__ void substitute_step(float (&x)[4], const float (&Lrow)[16]) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float xm = __int_as_float(
-            __builtin_amdgcn_update_dpp(0, __float_as_int(x[j]), 0x150 + kM, 0xF, 0xF, false));
-        x[j] -= Lrow[kM] * xm;
-    }
-    if constexpr (kM < 14) substitute_step<kM + 1>(x, Lrow);
-}
 
 __global__ __launch_bounds__(256) void prep_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ a,
@@ -113,10 +86,8 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(
         const int rr = r < len ? r : len - 1;
         const int j = (l & 15) ^ swz(r);
         const size_t off = (size_t(t0 + rr) * H + h) * kD + 8 * j;
-        __builtin_amdgcn_global_load_lds(k + off, (lds_void*)(reinterpret_cast<char*>(S.u.in.K) + 1024 * n),
-                                         16, 0, 0);
-        __builtin_amdgcn_global_load_lds(q + off, (lds_void*)(reinterpret_cast<char*>(S.u.in.Q) + 1024 * n),
-                                         16, 0, 0);
+        dma16(k + off, reinterpret_cast<char*>(S.u.in.K) + 1024 * n);
+        dma16(q + off, reinterpret_cast<char*>(S.u.in.Q) + 1024 * n);
     }
     if (w == 0) {
         // gates: log a (clamped far below any fp32-visible decay), prefix sum;
@@ -217,59 +188,10 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(
     }
     __syncthreads();
 
-    // ---- T = (I + L)^-1 -------------------------------------------------------
-    // (a) diagonal block w, all 64 lanes: lane (g, r = c) holds row r of
-    //     columns 4g .. 4g+3, starting from the identity.  Column-oriented
-    //     forward substitution: once x_m is final, every row r > m takes
-    //     x_r -= L_rm x_m, with x_m broadcast inside each 16-lane row by DPP
-    //     (row_newbcast).  L is zero on and above the diagonal, so rows
-    //     r <= m are left unchanged without a branch.
-    {
-        const int base = 16 * w, r = c;
-        float Lrow[16];
-#pragma unroll
-        for (int m4 = 0; m4 < 4; ++m4) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(Ls + (base + r) * kFS + base + 4 * m4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Lrow[4 * m4 + e] = v[e];
-        }
-        float x[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = r == 4 * g + j ? 1.f : 0.f;
-        substitute_step<0>(x, Lrow);
-        *reinterpret_cast<f32x4*>(Ts + (base + r) * kFS + base + 4 * g) = f32x4{x[0], x[1], x[2], x[3]};
-    }
-    __syncthreads();
-    // (b) off-diagonal blocks, block row by block row, on fp32 MFMA:
-    //     T_ij = -T_ii * sum_{m=j}^{i-1} L_im T_mj.
-    for (int bi = 1; bi < 4; ++bi) {
-        if (w < bi) {
-            const int bj = w;
-            f32x4 acc = zero4();
-            for (int m = bj; m < bi; ++m) {
-#pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) {
-                    const float av = Ls[(16 * bi + c) * kFS + 16 * m + 4 * s4 + g];
-                    const float bv = Ts[(16 * m + 4 * s4 + g) * kFS + 16 * bj + c];
-                    acc = mfma_f32(av, bv, acc);
-                }
-            }
-            float* R = S.R[w];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) R[(4 * g + i) * 16 + c] = acc[i];
-            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): R visible to this wavefront
-            f32x4 acc2 = zero4();
-#pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
-                const float av = Ts[(16 * bi + c) * kFS + 16 * bi + 4 * s4 + g];
-                const float bv = R[(4 * s4 + g) * 16 + c];
-                acc2 = mfma_f32(av, bv, acc2);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Ts[(16 * bi + 4 * g + i) * kFS + 16 * bj + c] = -acc2[i];
-        }
-        __syncthreads();
-    }
+    // ---- T = (I + L)^-1: the four 16 x 16 diagonal blocks by column-oriented
+    // forward substitution (one wave per block), the off-diagonal blocks by
+    // block substitution on fp32 MFMA (ends with a workgroup barrier) ---------
+    solve_unit_lower(Ls, Ts, &S.R[0][0], w, g, c);
 
     // ---- T_b = T diag(b) packed (slot (w, m): row 16w + lane % 16, tokens
     // {32m + 4g + e, 32m + 16 + 4g + e}); T is zero above the diagonal

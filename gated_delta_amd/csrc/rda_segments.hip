@@ -14,6 +14,7 @@
 // MFMA (full fp32 arithmetic).
 #include "rda_device.h"
 #include "rda_internal.h"
+#include "rda_lds.h"
 
 namespace rda {
 
@@ -28,8 +29,6 @@ namespace {
 // hit 64 distinct banks.
 constexpr int kRows = 16;
 constexpr int kSx = kD + 4;   // row stride (floats) of the staged rows: spreads banks
-
-typedef __attribute__((address_space(3))) void lds_void;
 
 struct CombineLds {
     float M[2][kD * kD];    // M_p, double-buffered, granules swizzled per row
@@ -46,14 +45,6 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// Wait until at most kN vector memory operations of this wave are in flight
-// (they complete in issue order).
-template <int kN>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(kN >= 0 && kN < 64, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt((kN & 15) | ((kN >> 4) << 14) | 0x0F70);
 }
 
 // Half kHalf of M_p into LDS: wave w moves the 1 KiB blocks w + 4 i (rows

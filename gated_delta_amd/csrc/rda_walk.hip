@@ -44,8 +44,8 @@
 // token row instead of zeroing: T_b has zero rows and columns there (b = 0),
 // so U and U~ vanish on those rows and no duplicate reaches S or a stored
 // output; they only need to be finite, which copies of real rows are.
-#include "rda_device.h"
 #include "rda_internal.h"
+#include "rda_lds.h"
 
 namespace rda {
 
@@ -79,21 +79,6 @@ struct Lds {
 
 static_assert(sizeof(Stage) == 67 * 1024, "stage is whole 1 KiB DMA blocks");
 static_assert(sizeof(Lds) <= 160 * 1024, "LDS budget of one workgroup");
-
-// Row r of a K or Q tile keeps 16-byte granule j at position j ^ swz(r).
-// Sixteen consecutive rows read at one granule (row operands) and eight
-// consecutive rows read at two adjacent granules (transposing reads) both
-// land on distinct granules, i.e. on distinct LDS banks.
-__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* src, void* lds_dst) {
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 4, 0, 0);
-}
 
 struct Ctx {
     const uint16_t* q;
@@ -211,13 +196,6 @@ __device__ __forceinline__ void issue_chunk(const Ctx& x, int chunk, Stage& st) 
     issue_group<kI, 2, kOut>(x, chunk, st);
 }
 
-template <int kN>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(kN >= 0 && kN < 64, "vmcnt field");
-    // vmcnt = kN (split field), expcnt and lgkmcnt at their maxima: no wait
-    __builtin_amdgcn_s_waitcnt((kN & 15) | ((kN >> 4) << 14) | 0x0F70);
-}
-
 // A chunk's blocks go out at once, right after the third barrier of the
 // chunk two before it (its stage is free from then on), followed by one L2
 // touch from loaders 0 and 1.  Before a chunk's first barrier each loader
@@ -249,21 +227,6 @@ __device__ void loader(const Ctx& x, int c0, int c_end, Lds& S) {
 
 // ---- LDS operand helpers -----------------------------------------------------------
 
-// Row r of a swizzled K or Q tile, natural k order: lane (g, c) gets elements
-// 32m + 8g .. +7 (one 16-byte granule).
-__device__ __forceinline__ bf16x8 row_op(const uint16_t* T, int r, int m, int g) {
-    const unsigned char* row = reinterpret_cast<const unsigned char*>(T) + r * 256;
-    return __builtin_bit_cast(bf16x8,
-                              *reinterpret_cast<const u32x4*>(row + 16 * ((4 * m + g) ^ swz(r))));
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-__device__ __forceinline__ u32x2 tr_read(const void* p) {
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
-}
-
 // Transposed operand of the swizzled K tile: lane (g, c) receives column
 // 16 kt + c of rows {32m + 4g + i, 32m + 16 + 4g + i : i < 4} (the permuted
 // token order of the packed factors and of the exchanged U~).
@@ -286,27 +249,6 @@ __device__ __forceinline__ u32x2 tr_vd(const uint16_t* V, int t, int l) {
     const int g = l >> 4, j = l & 15;
     return tr_read(reinterpret_cast<const unsigned char*>(V) + (16 * t + 4 * g + (j >> 2)) * 32 +
                    8 * (j & 3));
-}
-
-__device__ __forceinline__ bf16x8 xop(const u32x4 (*X)[2][64], int blk, int hl, int l) {
-    return __builtin_bit_cast(bf16x8, X[blk][hl][l]);
-}
-
-// Write a D-layout tile's 4 values (hi/lo) into its half of block tile / 2.
-__device__ __forceinline__ void put_half(u32x4 (*X)[2][64], int tile, int l, f32x4 v) {
-    uint32_t h01, l01, h23, l23;
-    split_pk(v[0], v[1], h01, l01);
-    split_pk(v[2], v[3], h23, l23);
-    reinterpret_cast<u32x2*>(&X[tile >> 1][0][l])[tile & 1] = u32x2{h01, h23};
-    reinterpret_cast<u32x2*>(&X[tile >> 1][1][l])[tile & 1] = u32x2{l01, l23};
-}
-
-// Products of a hi/lo A operand with a hi/lo B operand: hi*hi + hi*lo + lo*hi.
-__device__ __forceinline__ void mma3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, f32x4& p0,
-                                     f32x4& p1, f32x4& p2) {
-    p0 = mfma_bf16(ah, bh, p0);
-    p1 = mfma_bf16(ah, bl, p1);
-    p2 = mfma_bf16(al, bh, p2);
 }
 
 __device__ __forceinline__ bf16x8 packed(const u32x4 (*P)[64], int tile, int m, int hl, int l) {
@@ -345,8 +287,8 @@ __device__ __forceinline__ void state_step(const Ctx& x, int w, const Stage& st,
         const u32x2 vv = tr_vd(st.V, w, l);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            sh[m] = xop(S.Sx, m, 0, l);
-            sl[m] = xop(S.Sx, m, 1, l);
+            sh[m] = ldsop(S.Sx, m, 0, l);
+            sl[m] = ldsop(S.Sx, m, 1, l);
             ka[m] = row_op(st.K, 16 * w + c, m, g);
         }
         f32x4 y0 = zero4(), y1 = zero4();
@@ -360,7 +302,7 @@ __device__ __forceinline__ void state_step(const Ctx& x, int w, const Stage& st,
                                         __uint_as_float(vv[0] & 0xffff0000u),
                                         __uint_as_float(vv[1] << 16),
                                         __uint_as_float(vv[1] & 0xffff0000u)};
-        put_half(S.Ex, w, l, vf - (y0 + y1) * gam);
+        publish4(S.Ex, w, l, vf - (y0 + y1) * gam);
     }
     __syncthreads();   // B
     // P3: U = T_b E (T_b is lower triangular: blocks m <= w / 2); K^T
@@ -371,8 +313,8 @@ __device__ __forceinline__ void state_step(const Ctx& x, int w, const Stage& st,
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             if (m >= nb) break;
-            eh[m] = xop(S.Ex, m, 0, l);
-            el[m] = xop(S.Ex, m, 1, l);
+            eh[m] = ldsop(S.Ex, m, 0, l);
+            el[m] = ldsop(S.Ex, m, 1, l);
             th[m] = packed(st.Tb, w, m, 0, l);
             tl[m] = packed(st.Tb, w, m, 1, l);
         }
@@ -387,8 +329,8 @@ __device__ __forceinline__ void state_step(const Ctx& x, int w, const Stage& st,
             mma3(th[m], tl[m], eh[m], el[m], p0, p1, p2);
         }
         const f32x4 u = p0 + p1 + p2;
-        put_half(S.Ux, w, l, u);
-        put_half(S.Uy, w, l, u * gs);
+        publish4(S.Ux, w, l, u);
+        publish4(S.Uy, w, l, u * gs);
     }
     __syncthreads();   // C
     // P4: S^T = gamma_C S^T + K^T U~
@@ -396,8 +338,8 @@ __device__ __forceinline__ void state_step(const Ctx& x, int w, const Stage& st,
         bf16x8 uh[2], ul[2];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            uh[m] = xop(S.Uy, m, 0, l);
-            ul[m] = xop(S.Uy, m, 1, l);
+            uh[m] = ldsop(S.Uy, m, 0, l);
+            ul[m] = ldsop(S.Uy, m, 1, l);
         }
         f32x4 a0 = s0 * gC, a1 = s1 * gC, b0 = zero4(), b1 = zero4();
 #pragma unroll
@@ -432,8 +374,8 @@ __device__ __forceinline__ void output_step(const Ctx& x, int tt, int ch, const 
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int m = 2 * half + i;
-            sh[i] = xop(S.Sx, m, 0, l);
-            sl[i] = xop(S.Sx, m, 1, l);
+            sh[i] = ldsop(S.Sx, m, 0, l);
+            sl[i] = ldsop(S.Sx, m, 1, l);
             qa[i] = row_op(st.Q, 16 * tt + c, m, g);
         }
 #pragma unroll
@@ -457,8 +399,8 @@ __device__ __forceinline__ void output_step(const Ctx& x, int tt, int ch, const 
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             if (m >= nb) break;
-            xh[m] = xop(S.Ux, m, 0, l);
-            xl[m] = xop(S.Ux, m, 1, l);
+            xh[m] = ldsop(S.Ux, m, 0, l);
+            xl[m] = ldsop(S.Ux, m, 1, l);
         }
         f32x4 p0 = zero4(), p1 = zero4(), p2 = zero4();
 #pragma unroll

@@ -15,9 +15,9 @@ set -o pipefail
 R="$(cd "$(dirname "$0")/.." && pwd)"
 OUT="$(mkdir -p "${1:?output directory}" && cd "$1" && pwd)"
 cd /tmp && export TMPDIR=/tmp
-echo "== kernel trace + stats: python bench.py --steps 20 --warmup 3 --no-cpu --no-extras"
+echo "== kernel trace + stats: python bench.py --steps 20 --warmup 3 --no-cpu --no-extras --processes 1"
 timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d "$OUT/prof_trace" -o trace \
-    -- python -u "$R/bench.py" --steps 20 --warmup 3 --no-cpu --no-extras \
+    -- python -u "$R/bench.py" --steps 20 --warmup 3 --no-cpu --no-extras --processes 1 \
     > "$OUT/prof_trace.log" 2>&1 || exit $?
 echo "== kernel trace + stats: python bench.py --mode decode_tokens --steps 20 --no-cpu"
 timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d "$OUT/prof_trace_dt" -o trace \
@@ -52,4 +52,14 @@ echo "== pmc MFMA counters: python bench.py --mode prefill --steps 2 --warmup 1 
 timeout -s KILL 120 rocprofv3 --pmc $MFMA --output-format csv -d "$OUT/prof_MFMA_prefill" -o pmc \
     -- python -u "$R/bench.py" --mode prefill --steps 2 --warmup 1 --no-cpu \
     > "$OUT/prof_MFMA_prefill.log" 2>&1 || exit $?
+for cfg in 1 2 4; do
+  echo "== kernel trace + stats: python bench.py --mode prefill_config --config $cfg --steps 10 --warmup 2 --no-cpu"
+  timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d "$OUT/prof_trace_c$cfg" -o trace \
+      -- python -u "$R/bench.py" --mode prefill_config --config $cfg --steps 10 --warmup 2 --no-cpu \
+      > "$OUT/prof_trace_c$cfg.log" 2>&1 || exit $?
+  echo "== pmc MFMA counters: python bench.py --mode prefill_config --config $cfg --steps 2 --warmup 1 --no-cpu"
+  timeout -s KILL 120 rocprofv3 --pmc $MFMA --output-format csv -d "$OUT/prof_MFMA_c$cfg" -o pmc \
+      -- python -u "$R/bench.py" --mode prefill_config --config $cfg --steps 2 --warmup 1 --no-cpu \
+      > "$OUT/prof_MFMA_c$cfg.log" 2>&1 || exit $?
+done
 echo "== done"

@@ -41,7 +41,14 @@ STAGE = {"chunk_table_kernel": "rda_chunk_table", "prep_bf16_kernel": "rda_prep"
          "walk_bf16_kernel": "rda_walk", "decode_step_kernel": "rda_decode_step",
          "decode_tokens_kernel": "rda_decode_tokens", "norm_gate_kernel": "rda_output_norm_gate",
          "prologue_kernel": "rda_prologue", "prep_diag_kernel": "rda_prep_diag",
-         "walk_diag_kernel": "rda_walk_diag", "segment_combine_kernel": "rda_segment_combine"}
+         "walk_diag_kernel": "rda_walk_diag", "segment_combine_kernel": "rda_segment_combine",
+         "prep_kernel": "rda_prep", "walk_kernel": "rda_walk"}
+
+# the other prefill workloads: bench --mode prefill_config --config N
+CONFIGS = {1: ("T64_H1_fp32", "one fp32 head of 64 tokens (S0 = 0)"),
+           2: ("T2048_H16", "T=2048 x H=16, bf16 q/k/v, S0 = 0"),
+           4: ("varlen8_T32768_H16", "8 packed sequences, 32768 tokens x H=16 in all, bf16 "
+                                     "q/k/v, S0 per sequence")}
 
 
 def short(name: str) -> str:
@@ -104,7 +111,7 @@ def main():
          "# timed steps, then 20 per-stage prefill calls (each followed by a decode step)",
          "# command: gated_delta_amd/profile_run.sh OUTDIR, whose first pass is",
          "#   rocprofv3 --kernel-trace --stats --output-format csv -d OUTDIR/prof_trace -o trace \\",
-         "#     -- python bench.py --steps 20 --warmup 3 --no-cpu --no-extras",
+         "#     -- python bench.py --steps 20 --warmup 3 --no-cpu --no-extras --processes 1",
          "# then python gated_delta_amd/profile_summary.py OUTDIR"])
     if os.path.isdir(os.path.join(out, "prof_trace_dt")):
         kernel_table(
@@ -229,20 +236,45 @@ def main():
 
     # ---- MFMA counters -------------------------------------------------------------
     mdir = os.path.join(out, "prof_MFMA_prefill")
-    if not os.path.isdir(mdir):
-        return
+    if os.path.isdir(mdir):
+        mfma_summary(mdir, rows, os.path.join(prof, "mfma_rda_prefill_T16384_H16.txt"),
+                     "RDA prefill T=16384", "H=16 d=128 (bf16 q/k/v)",
+                     "--mode prefill --steps 2 --warmup 1 --no-cpu",
+                     "prof_MFMA_prefill")
+    for cid, (tag, what) in CONFIGS.items():
+        tdir = os.path.join(out, f"prof_trace_c{cid}")
+        mdir = os.path.join(out, f"prof_MFMA_c{cid}")
+        if not (os.path.isdir(tdir) and os.path.isdir(mdir)):
+            continue
+        crows = kernel_table(
+            tdir, os.path.join(prof, f"kernels_rda_prefill_{tag}.txt"),
+            [f"# rocprofv3 kernel trace, the prefill workload {what}; 12 calls",
+             f"# command: gated_delta_amd/profile_run.sh OUTDIR, whose pass for this workload is",
+             f"#   rocprofv3 --kernel-trace --stats --output-format csv -d OUTDIR/prof_trace_c{cid} -o trace \\",
+             f"#     -- python bench.py --mode prefill_config --config {cid} --steps 10 --warmup 2 --no-cpu",
+             "# then python gated_delta_amd/profile_summary.py OUTDIR"])
+        mfma_summary(mdir, crows, os.path.join(prof, f"mfma_rda_prefill_{tag}.txt"),
+                     "the prefill workload", what,
+                     f"--mode prefill_config --config {cid} --steps 2 --warmup 1 --no-cpu",
+                     f"prof_MFMA_c{cid}")
+
+
+def mfma_summary(mdir, rows, path, what1, what2, bench_args, dname):
+    """Executed MFMA work per launch of each kernel from one counter pass,
+    with its rate over the kernel's average duration in `rows` (the kernel
+    trace of the same workload)."""
     avg_us = {short(r["Name"]): float(r["AverageNs"]) / 1e3 for r in rows}
     mops16 = counter(mdir, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
     mops32 = counter(mdir, "SQ_INSTS_VALU_MFMA_MOPS_F32")
     inst16 = counter(mdir, "SQ_INSTS_VALU_MFMA_BF16")
     busy = counter(mdir, "SQ_VALU_MFMA_BUSY_CYCLES")
     cu = counter(mdir, "SQ_BUSY_CU_CYCLES")
-    lines = ["# MFMA work executed per launch of the prefill kernels, RDA prefill T=16384",
-             "# H=16 d=128 (bf16 q/k/v), from one rocprofv3 --pmc pass:",
+    lines = [f"# MFMA work executed per launch of the prefill kernels, {what1}",
+             f"# {what2}, from one rocprofv3 --pmc pass:",
              "#   rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 \\",
              "#     SQ_INSTS_VALU_MFMA_BF16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES \\",
-             "#     --output-format csv -d OUTDIR/prof_MFMA_prefill -o pmc \\",
-             "#     -- python bench.py --mode prefill --steps 2 --warmup 1 --no-cpu",
+             f"#     --output-format csv -d OUTDIR/{dname} -o pmc \\",
+             f"#     -- python bench.py {bench_args}",
              "# (part of gated_delta_amd/profile_run.sh OUTDIR; then",
              "# python gated_delta_amd/profile_summary.py OUTDIR).  MOPS count 512 flops each;",
              "# the executed work includes the hi/lo split products.  The rate divides by",
@@ -266,7 +298,6 @@ def main():
             # the busy count sums a CU's four SIMDs (16 cycles per 16x16x32
             # instruction), the CU count one per CU: per-SIMD utilisation
             lines.append(f"{name}.mfma_busy_per_simd = {busy.get(k, 0.0) / (4 * cu[k]):.4f}")
-    path = os.path.join(prof, "mfma_rda_prefill_T16384_H16.txt")
     open(path, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 

@@ -3,10 +3,10 @@
  *
  * RDA ("Raon Delta Attention") is the linear-attention token mixer of the
  * Raon-1 models.  The "Raon-1 nano" teardown page (ai.satyajit.si), section
- * "The other 1.5B: a hybrid built to forget", describes its recurrent step:
- * decay the matrix state, form the error between the value and what the
- * decayed state predicts for the key, and write that error back with
- * strength beta.  Section "The cache is small if the runtime keeps it small"
+ * "The other 1.5B: a hybrid built to forget", orders its recurrent step:
+ * scale the matrix state by the decay, take the residual e = v - S'k of the
+ * scaled state S' at the key, and add the rank-one update b e k^T (b is the
+ * page's beta).  Section "The cache is small if the runtime keeps it small"
  * of the same page fixes the state as 16 heads x 128 x 128 fp32 per layer,
  * carried across calls; the "Raon-1-nano-gguf" page's spec table gives the
  * 16 heads of dimension 128, and its Transformers section notes that the
@@ -107,6 +107,14 @@ size_t rda_prefill_workspace_bytes(int32_t num_seqs, int32_t total_tokens,
 /*
  * Chunked prefill over a packed batch of variable-length sequences.
  *
+ * The "Raon-1-nano-gguf" model card (Transformers section) notes that the
+ * plain PyTorch path processes a prompt one token at a time, which makes
+ * long prompts slow; this entry point computes the same recurrence (the
+ * step ordered as in the teardown's section "The other 1.5B: a hybrid built
+ * to forget") for every token of a prompt in one call, with the chunks of 64
+ * tokens handled in parallel where the algebra allows and only the state
+ * passed from chunk to chunk in sequence.
+ *
  *   q, k        [total_tokens, H, dk], v [total_tokens, H, dv], dtype qkv_dtype
  *               (RDA_BF16 or RDA_FP32; fp32 values are fed to MFMA as exact
  *               bf16 hi + lo pairs)
@@ -159,7 +167,11 @@ rda_status rda_prefill_profiled(const void* q, const void* k, const void* v, rda
 
 /*
  * One decode step: the recurrence for a single token per (batch, head),
- * updating the state in place in one read-modify-write pass over it.
+ * updating the state in place in one read-modify-write pass over it.  The
+ * teardown's section "The cache is small if the runtime keeps it small"
+ * describes the generation-time cost this serves: per RDA layer the runtime
+ * carries the 16 x 128 x 128 fp32 state from token to token (1 MiB per
+ * sequence), so each generated token reads and rewrites it once.
  *
  *   q, k [batch, H, dk], v [batch, H, dv] (qkv_dtype); a, b [batch, H] fp32
  *   S    [batch, H, dv, dk] fp32, read and overwritten with the new state

@@ -7,10 +7,9 @@ package imports nothing from the product path.
 
 The arithmetic lives in ``oracle.c`` (plain C, double precision): the gated
 delta rule as the page "Raon-1 nano" (ai.satyajit.si), section "The other
-1.5B: a hybrid built to forget", describes its recurrent step -- decay the
-state, form the error between the value and the decayed state's prediction
-for the key, write it back with strength beta -- and read-out o_t = S_t q_t
-after the update.  This module only marshals NumPy arrays into that library.
+1.5B: a hybrid built to forget", orders its recurrent step -- scale the
+state by the decay, take the residual e = v - S'k of the scaled state at the
+key, add b e k^T -- and read-out o_t = S_t q_t after the update.  This module only marshals NumPy arrays into that library.
 """
 from __future__ import annotations
 
@@ -101,9 +100,12 @@ class Oracle:
 
 
 def default() -> Oracle:
+    """The oracle build the module-level functions use: liboracle.so beside
+    oracle.c, or the build that RDA_ORACLE_LIB names (the tests use this to
+    run the pins on a sanitizer build)."""
     global _default
     if _default is None:
-        _default = Oracle()
+        _default = Oracle(os.environ.get("RDA_ORACLE_LIB", _LIB))
     return _default
 
 

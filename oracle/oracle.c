@@ -8,10 +8,10 @@
  *
  * What it computes.  RDA ("Raon Delta Attention") is described on the page
  * "Raon-1 nano" (ai.satyajit.si), section "The other 1.5B: a hybrid built to
- * forget", as a gated delta-rule linear attention whose recurrent step first
- * decays the matrix state, then forms the error between the value and what
- * the decayed state predicts for the key, and writes that error back with
- * strength beta.  The same page, section "The cache is small if the runtime
+ * forget", as a gated delta-rule linear attention.  Its recurrent step, in
+ * the order that section gives: scale the matrix state S by the decay a,
+ * take the residual e = v - S'k of the scaled state S' at the key, and add
+ * the rank-one update b e k^T (b the write strength, beta on the page).  The same page, section "The cache is small if the runtime
  * keeps it small", fixes the state as one 128 x 128 fp32 matrix per head.
  * With a scalar decay a_t in (0,1] and write strength b_t in [0,1] per token
  * and head, that step is the gated delta rule

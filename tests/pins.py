@@ -13,9 +13,9 @@ handle disagrees with a result fixed independently of the oracle's code:
   decode steps = prefill).
 
 The recurrence, per the "Raon-1 nano" teardown (section "The other 1.5B: a
-hybrid built to forget"): decay the state, take the error of the value
-against the decayed state's prediction for the key, write it with strength
-beta; read out o_t = S_t q_t.  As a product: S_t = S_{t-1} A_t + b_t v_t k_t^T
+hybrid built to forget"): scale the state by the decay, take the residual
+e = v - S'k of the scaled state at the key, add b e k^T; read out
+o_t = S_t q_t.  As a product: S_t = S_{t-1} A_t + b_t v_t k_t^T
 with A_t = a_t (I - b_t k_t k_t^T).  The module is shared by
 ``test_oracle_pins.py`` (real oracle) and ``test_oracle_mutants.py``
 (builds of the oracle with a planted mistake, which must fail some pin).

@@ -176,27 +176,20 @@ def test_max_tokens_equals_prefill(dev):
     assert_parity("S", to_host(S), rS)
 
 
-def test_full_workload_sampled(dev):
+def test_full_workload(dev):
     """256 sequences x 16 heads, one token plus two drafts, per-sequence
     accept counts, in place (the launch the bench times); the oracle checks
-    48 sampled (sequence, head) states."""
+    every one of the 4096 states: o of every token and the committed S."""
     B, T, H = 256, 3, 16
     x = synth.decode_tokens_inputs(B, T, H)
     S0 = synth.decode_state(B, H)
     S = dev_f32(S0, dev)
-    say(f"[decode_tokens] full workload B={B} T={T} H={H}")
+    say(f"[decode_tokens] full workload B={B} T={T} H={H}, every state")
     o = rda.rda_decode_tokens(*tok_dev(x, dev), S, S_out=S, accept=accept_dev(x.accept, dev))
     torch.cuda.synchronize()
-    rng = np.random.default_rng(309)
-    sample = rng.choice(B * H, size=48, replace=False)
-    sb, sh = sample // H, sample % H
-    og, Sg = to_host(o), to_host(S)
-    assert np.all(np.isfinite(og)) and np.all(np.isfinite(Sg))
-    sel = lambda arr: np.ascontiguousarray(arr[sb, :, sh][:, :, None])   # [48, T, 1, ...]
-    ro, rS = oracle.decode_tokens(sel(x.q), sel(x.k), sel(x.v), sel(x.a), sel(x.b),
-                                  S0[sb, sh][:, None], x.accept[sb])
-    assert_parity("sampled o", og[sb, :, sh], ro[:, :, 0])
-    assert_parity("sampled S", Sg[sb, sh], rS[:, 0])
+    ro, rS = oracle.decode_tokens(x.q, x.k, x.v, x.a, x.b, S0, x.accept)
+    assert_parity("o, all states", to_host(o), ro)
+    assert_parity("S, all states", to_host(S), rS)
 
 
 def test_bitwise_deterministic(dev):

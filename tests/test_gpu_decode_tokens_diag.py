@@ -145,27 +145,21 @@ def test_max_tokens_equals_prefill_diag(dev):
     assert_parity("S", to_host(S), rS)
 
 
-def test_full_workload_sampled(dev):
+def test_full_workload(dev):
     """256 sequences x 16 heads, three tokens, per-sequence accept counts,
-    in place (the launch the bench times); 48 sampled states checked."""
+    in place (the launch the bench times); every one of the 4096 states is
+    checked against the oracle."""
     B, T, H = 256, 3, 16
     x, alpha = case(B, T, H, (327,))
     S0 = synth.decode_state(B, H)
     S = dev_f32(S0, dev)
-    say(f"[decode_tokens_diag] full workload B={B} T={T} H={H}")
+    say(f"[decode_tokens_diag] full workload B={B} T={T} H={H}, every state")
     o = rda.rda_decode_tokens_diag(*args_dev(x, alpha, dev), S, S_out=S,
                                    accept=accept_dev(x.accept, dev))
     torch.cuda.synchronize()
-    rng = np.random.default_rng(328)
-    sample = rng.choice(B * H, size=48, replace=False)
-    sb, sh = sample // H, sample % H
-    og, Sg = to_host(o), to_host(S)
-    assert np.all(np.isfinite(og)) and np.all(np.isfinite(Sg))
-    sel = lambda arr: np.ascontiguousarray(arr[sb, :, sh][:, :, None])
-    ro, rS = oracle.decode_tokens_diag(sel(x.q), sel(x.k), sel(x.v), sel(alpha), sel(x.b),
-                                       S0[sb, sh][:, None], x.accept[sb])
-    assert_parity("sampled o", og[sb, :, sh], ro[:, :, 0])
-    assert_parity("sampled S", Sg[sb, sh], rS[:, 0])
+    ro, rS = oracle.decode_tokens_diag(x.q, x.k, x.v, alpha, x.b, S0, x.accept)
+    assert_parity("o, all states", to_host(o), ro)
+    assert_parity("S, all states", to_host(S), rS)
 
 
 def test_bitwise_deterministic(dev):

@@ -11,7 +11,7 @@ import torch
 import oracle
 import pins
 from gated_delta_amd import rda, synth
-from gpu_util import (assert_parity, dev_f32, dev_tokens, need_gpu, say, to_host)
+from gpu_util import (assert_parity, dev_f32, dev_tokens, guarded, need_gpu, say, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -22,13 +22,21 @@ def dev():
 
 
 def run_gpu(p: synth.PrefillInputs, dev, S0=None, want_state=True):
+    """The HIP path with o and S_final inside guard bands (checked after
+    the call: no store may land outside the outputs)."""
     S0 = p.S0 if S0 is None else S0
     q, k, v = (dev_tokens(getattr(p, n), p.bf16, dev) for n in "qkv")
     a, b = dev_f32(p.a, dev), dev_f32(p.b, dev)
     S0d = dev_f32(S0, dev)
-    o, Sf = rda.rda_prefill(q, k, v, a, b, cu_seqlens=p.cu_seqlens, S0=S0d,
-                            want_state=want_state)
+    T, H = p.total_tokens, p.num_heads
+    go = guarded((T, H, 128), torch.float32, dev)
+    gs = guarded((p.num_seqs, H, 128, 128), torch.float32, dev) if want_state else None
+    o, Sf = rda.rda_prefill(q, k, v, a, b, cu_seqlens=p.cu_seqlens, S0=S0d, o=go.t,
+                            S_final=gs.t if gs else None, want_state=want_state)
     torch.cuda.synchronize()
+    go.check("o")
+    if gs:
+        gs.check("S_final")
     return to_host(o), to_host(Sf)
 
 

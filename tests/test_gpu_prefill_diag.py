@@ -6,7 +6,7 @@ import torch
 
 import oracle
 from gated_delta_amd import rda, synth
-from gpu_util import assert_parity, dev_f32, dev_tokens, need_gpu, say, to_host
+from gpu_util import assert_parity, dev_f32, dev_tokens, guarded, need_gpu, say, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -23,9 +23,17 @@ def case(T, H, key, s0=0.02, lengths=None):
 
 
 def run_gpu(p, alpha, dev):
+    """o and S_final inside guard bands, checked after the call."""
     q, k, v = (dev_tokens(getattr(p, n), True, dev) for n in "qkv")
-    return rda.rda_prefill_diag(q, k, v, dev_f32(alpha, dev), dev_f32(p.b, dev),
-                                cu_seqlens=p.cu_seqlens, S0=dev_f32(p.S0, dev))
+    go = guarded((p.total_tokens, p.num_heads, 128), torch.float32, dev)
+    gs = guarded((p.num_seqs, p.num_heads, 128, 128), torch.float32, dev)
+    o, S = rda.rda_prefill_diag(q, k, v, dev_f32(alpha, dev), dev_f32(p.b, dev),
+                                cu_seqlens=p.cu_seqlens, S0=dev_f32(p.S0, dev), o=go.t,
+                                S_final=gs.t)
+    torch.cuda.synchronize()
+    go.check("o")
+    gs.check("S_final")
+    return o, S
 
 
 @pytest.mark.parametrize("T", [1, 15, 16, 17, 63, 64, 65, 130, 300])

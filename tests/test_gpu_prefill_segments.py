@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from gated_delta_amd import rda, synth
-from gpu_util import assert_parity, dev_f32, dev_tokens, need_gpu, say, to_host
+from gpu_util import assert_parity, dev_f32, dev_tokens, guarded, need_gpu, say, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -43,12 +43,22 @@ def long_memory(p, key):
 
 
 def run(p, dev, one_pass=False, S0=None, S_final=None, want_state=True):
+    """o (and S_final unless given) inside guard bands, checked after the
+    call."""
     q, k, v = (dev_tokens(getattr(p, n), True, dev) for n in "qkv")
     a, b = dev_f32(p.a, dev), dev_f32(p.b, dev)
     cu = np.array([0, p.total_tokens], dtype=np.int32) if one_pass else None
-    o, Sf = rda.rda_prefill(q, k, v, a, b, cu_seqlens=cu, S0=S0, S_final=S_final,
+    go = guarded((p.total_tokens, p.num_heads, 128), torch.float32, dev)
+    gs = None
+    if S_final is None and want_state:
+        gs = guarded((1, p.num_heads, 128, 128), torch.float32, dev)
+        S_final = gs.t
+    o, Sf = rda.rda_prefill(q, k, v, a, b, cu_seqlens=cu, S0=S0, o=go.t, S_final=S_final,
                             want_state=want_state)
     torch.cuda.synchronize()
+    go.check("o")
+    if gs is not None:
+        gs.check("S_final")
     return to_host(o), (to_host(Sf) if Sf is not None else None)
 
 
@@ -154,11 +164,21 @@ def test_bitwise_deterministic(dev):
 # ---- the per-channel decay (rda_prefill_diag) takes the same segmented pass ----
 
 def diag_run(p, alpha, dev, one_pass=False, S0=None, S_final=None):
+    """o (and S_final unless given) inside guard bands, checked after the
+    call."""
     q, k, v = (dev_tokens(getattr(p, n), True, dev) for n in "qkv")
     cu = np.array([0, p.total_tokens], dtype=np.int32) if one_pass else None
+    go = guarded((p.total_tokens, p.num_heads, 128), torch.float32, dev)
+    gs = None
+    if S_final is None:
+        gs = guarded((1, p.num_heads, 128, 128), torch.float32, dev)
+        S_final = gs.t
     o, Sf = rda.rda_prefill_diag(q, k, v, dev_f32(alpha, dev), dev_f32(p.b, dev), cu_seqlens=cu,
-                                 S0=S0, S_final=S_final)
+                                 S0=S0, o=go.t, S_final=S_final)
     torch.cuda.synchronize()
+    go.check("o")
+    if gs is not None:
+        gs.check("S_final")
     return to_host(o), (to_host(Sf) if Sf is not None else None)
 
 
