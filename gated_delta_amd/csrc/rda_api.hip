@@ -2,9 +2,11 @@
 // workspace sizing and the launch sequence of each entry point.  Validation
 // is pure host code and runs before anything is enqueued, so every error
 // path returns a status without touching the device.
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "rda_internal.h"
 
@@ -204,6 +206,35 @@ rda_status prefill_sequential(const Prefill& P, hipStream_t stream, hipEvent_t c
     return RDA_OK;
 }
 
+// ---- the fixed scratch of rda_prefill_noalloc ------------------------------
+// One array per GPU in the library's code object.  In host code `scratch`
+// names a host-side stand-in, not device memory: only the address that
+// hipGetSymbolAddress returns for the current device may reach a kernel.
+constexpr size_t kScratchBytes = RDA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_addr[kMaxDevices];
+std::mutex scratch_mu;
+
+// The current device's copy of `scratch`, looked up once per device.
+rda_status device_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return RDA_ERR_HIP;
+    void* p = scratch_addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(scratch_mu);
+        p = scratch_addr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+                return RDA_ERR_HIP;
+            scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return RDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -222,6 +253,7 @@ const char* rda_status_string(int status) {
         case RDA_ERR_HIP: return "HIP launch error";
         case RDA_ERR_ALIAS: return "output buffers overlap other arguments";
         case RDA_ERR_VALUE: return "scalar argument out of range";
+        case RDA_ERR_TOO_LARGE: return "sizes exceed the fixed scratch of rda_prefill_noalloc";
         default: return "unknown status";
     }
 }
@@ -267,6 +299,31 @@ rda_status rda_prefill(const void* q, const void* k, const void* v, rda_dtype qk
     const rda_status st = check_prefill(q, k, v, qkv_dtype, a, b, cu_seqlens, num_seqs,
                                         total_tokens, num_heads, dk, dv, S0, o, S_final,
                                         workspace, workspace_bytes, P);
+    if (st != RDA_OK) return st;
+    return prefill_sequential(P, stream, nullptr);
+}
+
+rda_status rda_prefill_noalloc(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
+                               const float* a, const float* b, const int32_t* cu_seqlens,
+                               int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                               int32_t dk, int32_t dv, const float* S0, float* o,
+                               float* S_final, hipStream_t stream) {
+    // every check that needs no device first, the size against the scratch
+    // included, so that an error launches nothing and touches no device
+    if (qkv_dtype != RDA_BF16 && qkv_dtype != RDA_FP32) return RDA_ERR_DTYPE;
+    if (total_tokens < 0 || num_seqs < 1) return RDA_ERR_SHAPE;
+    if (!cu_seqlens && num_seqs != 1) return RDA_ERR_SHAPE;
+    rda_status st = check_dims(num_heads, dk, dv);
+    if (st != RDA_OK) return st;
+    if (rda_max_chunks(num_seqs, total_tokens) < 0) return RDA_ERR_SHAPE;
+    const size_t need = rda_prefill_workspace_bytes(num_seqs, total_tokens, num_heads, dk, dv);
+    if (need == 0) return RDA_ERR_SHAPE;
+    if (need > kScratchBytes) return RDA_ERR_TOO_LARGE;
+    void* ws = nullptr;
+    if ((st = device_scratch(&ws)) != RDA_OK) return st;
+    Prefill P;
+    st = check_prefill(q, k, v, qkv_dtype, a, b, cu_seqlens, num_seqs, total_tokens, num_heads,
+                       dk, dv, S0, o, S_final, ws, kScratchBytes, P);
     if (st != RDA_OK) return st;
     return prefill_sequential(P, stream, nullptr);
 }

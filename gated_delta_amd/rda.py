@@ -66,6 +66,8 @@ def _load():
         lib.rda_prefill.restype = ctypes.c_int
         lib.rda_prefill_profiled.argtypes = pre + [p]
         lib.rda_prefill_profiled.restype = ctypes.c_int
+        lib.rda_prefill_noalloc.argtypes = pre[:15] + [p]
+        lib.rda_prefill_noalloc.restype = ctypes.c_int
         lib.rda_decode_step.argtypes = [p, p, p, ctypes.c_int, p, p, i32, i32, i32, i32, p, p, p]
         lib.rda_decode_step.restype = ctypes.c_int
         lib.rda_decode_tokens.argtypes = [p, p, p, ctypes.c_int, p, p, i32, i32, i32, i32, i32,
@@ -239,6 +241,48 @@ def rda_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, a: torch.Tens
         st = lib_.rda_prefill(*args)
     if st != 0:
         raise RdaError(st, "rda_prefill")
+    return o, S_final
+
+
+RDA_NOALLOC_SCRATCH_BYTES = 64 << 20
+RDA_ERR_TOO_LARGE = 10
+
+
+def rda_prefill_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, a: torch.Tensor,
+                        b: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
+                        S0: Optional[torch.Tensor] = None, *, o: torch.Tensor,
+                        S_final: Optional[torch.Tensor] = None, stream=None):
+    """rda_prefill without a workspace (C entry point ``rda_prefill_noalloc``):
+    the library's fixed per-GPU scratch holds the chunk table and factors, so
+    the call allocates nothing.  The caller passes every output (o, and
+    S_final or None), and cu_seqlens, when given, as a device int32 tensor
+    (no host copy is made).  Raises RdaError with RDA_ERR_TOO_LARGE when the
+    sizes need more than RDA_NOALLOC_SCRATCH_BYTES."""
+    lib_ = _load()
+    dev = q.device
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _qkv_dtype(q)
+    for name, t, shape in (("q", q, (T, H, dk)), ("k", k, (T, H, dk)), ("v", v, (T, H, dv))):
+        _need(t, name, q.dtype, shape, dev)
+    _need(a, "a", torch.float32, (T, H), dev)
+    _need(b, "b", torch.float32, (T, H), dev)
+    N = 1
+    if cu_seqlens is not None:
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be 1-D with at least 2 entries")
+        N = cu_seqlens.numel() - 1
+        _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (N, H, dv, dk), dev)
+    _need(o, "o", torch.float32, (T, H, dv), dev)
+    if S_final is not None:
+        _need(S_final, "S_final", torch.float32, (N, H, dv, dk), dev)
+    st = lib_.rda_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(a), _ptr(b),
+                                  _ptr(cu_seqlens), N, T, H, dk, dv, _ptr(S0), _ptr(o),
+                                  _ptr(S_final), _stream_handle(stream))
+    if st != 0:
+        raise RdaError(st, "rda_prefill_noalloc")
     return o, S_final
 
 

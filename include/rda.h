@@ -74,7 +74,8 @@ typedef enum {
     RDA_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned */
     RDA_ERR_HIP = 7,         /* a HIP launch reported an error */
     RDA_ERR_ALIAS = 8,       /* outputs overlap inputs (other than S_final == S0) */
-    RDA_ERR_VALUE = 9        /* a scalar argument out of range (eps, gate activation) */
+    RDA_ERR_VALUE = 9,       /* a scalar argument out of range (eps, gate activation) */
+    RDA_ERR_TOO_LARGE = 10   /* sizes need more than rda_prefill_noalloc's fixed scratch */
 } rda_status;
 
 typedef enum { RDA_BF16 = 0, RDA_FP32 = 1 } rda_dtype;
@@ -164,6 +165,33 @@ rda_status rda_prefill_profiled(const void* q, const void* k, const void* v, rda
                                 const float* S0, float* o, float* S_final,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream,
                                 hipEvent_t const* stage_events);
+
+/*
+ * rda_prefill for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and errors as rda_prefill, without the workspace:
+ * the chunk table and the per-chunk factors go to a fixed device array of
+ * RDA_NOALLOC_SCRATCH_BYTES inside the library (one per GPU, allocated when
+ * the library's code is loaded on that GPU and held until the process
+ * ends).  The call itself allocates nothing (no hipMalloc / hipFree, no
+ * allocating library routine).  Sizes whose rda_prefill_workspace_bytes
+ * exceed RDA_NOALLOC_SCRATCH_BYTES return RDA_ERR_TOO_LARGE before anything
+ * is enqueued (for one sequence of 16 heads that is a prompt of up to about
+ * 7900 tokens).
+ * The first call on a device looks up that device's copy of the array
+ * (hipGetSymbolAddress) and keeps its address; a failed lookup returns
+ * RDA_ERR_HIP.  Every call on one GPU uses the same array: calls that may
+ * overlap in time on one GPU (different streams, or threads without
+ * ordering) race on it and give undefined results, so serialise them on
+ * one stream.  The array needs no clearing between calls (every byte a call
+ * reads is written earlier in the same call).
+ */
+#define RDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+rda_status rda_prefill_noalloc(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
+                               const float* a, const float* b,
+                               const int32_t* cu_seqlens, int32_t num_seqs,
+                               int32_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
+                               const float* S0, float* o, float* S_final, hipStream_t stream);
 
 /*
  * One decode step: the recurrence for a single token per (batch, head),

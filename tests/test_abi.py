@@ -14,7 +14,7 @@ from gated_delta_amd import rda
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rda.h")
 
-OK, NULL, SHAPE, UNSUP, DTYPE, WS, ALIGN, HIPERR, ALIAS, VALUE = range(10)
+OK, NULL, SHAPE, UNSUP, DTYPE, WS, ALIGN, HIPERR, ALIAS, VALUE, TOO_LARGE = range(11)
 P = 1 << 40          # fake, well-aligned device addresses: never dereferenced
 GiB = 1 << 30
 
@@ -37,7 +37,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("rda_prefill", "rda_decode_step", "rda_decode_tokens", "rda_prefill_diag",
               "rda_decode_step_diag", "rda_decode_tokens_diag", "rda_prologue", "rda_output_norm_gate",
-              "rda_prefill_workspace_bytes",
+              "rda_prefill_workspace_bytes", "rda_prefill_noalloc",
               "rda_chunk_table", "rda_abi_version", "rda_status_string"):
         assert n in names
 
@@ -62,7 +62,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert rda.rda_abi_version() == 1
-    for s in range(10):
+    for s in range(11):
         assert rda.rda_status_string(s) and rda.rda_status_string(s) != "unknown status"
     assert rda.rda_status_string(99) == "unknown status"
 
@@ -121,6 +121,39 @@ def test_prefill_rejects_bad_arguments(lib):
     # S0 == S_final (in-place resume) is allowed to pass validation; a partial
     # overlap is not
     assert _prefill(lib, S0=P + 6 * GiB + 1024, Sf=P + 6 * GiB) == ALIAS
+
+
+def test_noalloc_scratch_constants_match_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+RDA_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)(\d+)\s*<<\s*(\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == rda.RDA_NOALLOC_SCRATCH_BYTES
+    assert re.search(r"RDA_ERR_TOO_LARGE\s*=\s*10", text) and rda.RDA_ERR_TOO_LARGE == 10
+
+
+def _noalloc(lib, q=P, k=P + GiB, v=P + 2 * GiB, dt=0, a=P + 3 * GiB, b=P + 4 * GiB, cu=None,
+             N=1, T=1000, H=4, dk=128, dv=128, S0=None, o=P + 5 * GiB, Sf=P + 6 * GiB):
+    return lib.rda_prefill_noalloc(q, k, v, dt, a, b, cu, N, T, H, dk, dv, S0, o, Sf, None)
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    """Checked on the host before any device call: sizes whose workspace would
+    exceed the fixed scratch, and the other size / dtype errors."""
+    cap = rda.RDA_NOALLOC_SCRATCH_BYTES
+    assert rda.rda_prefill_workspace_bytes(1, 16384, 16) > cap
+    assert _noalloc(lib, T=16384, H=16) == TOO_LARGE
+    assert _noalloc(lib, T=1 << 20, H=1) == TOO_LARGE
+    # the largest single-sequence prompt of 16 heads that fits, and one more chunk
+    T = 64
+    while rda.rda_prefill_workspace_bytes(1, T + 64, 16) <= cap:
+        T += 64
+    assert rda.rda_prefill_workspace_bytes(1, T, 16) <= cap
+    assert _noalloc(lib, T=T + 64, H=16) == TOO_LARGE
+    assert _noalloc(lib, dt=7) == DTYPE
+    assert _noalloc(lib, T=-1) == SHAPE
+    assert _noalloc(lib, N=0) == SHAPE
+    assert _noalloc(lib, N=2) == SHAPE
+    assert _noalloc(lib, H=0) == SHAPE
+    assert _noalloc(lib, dk=64) == UNSUP
 
 
 def test_decode_rejects_bad_arguments(lib):
