@@ -82,7 +82,8 @@ def parse():
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0 = all)")
     ap.add_argument("--mode", choices=["bench", "prefill", "decode", "decode_tokens",
                                        "output_norm_gate", "prologue", "prefill_diag",
-                                       "segments", "copy", "prefill_config"],
+                                       "segments", "copy", "prefill_config",
+                                       "decode_prologue"],
                     default="bench",
                     help="prefill/decode: run only that part (for profiling); decode_tokens / "
                          "output_norm_gate / prologue / prefill_diag / segments: only the "
@@ -205,11 +206,14 @@ def main():
         return
 
     if args.mode in ("decode_tokens", "output_norm_gate", "prologue", "prefill_diag",
-                     "segments"):
+                     "segments", "decode_prologue"):
         timed = make_timer(torch, np, stream)
         flush_buf = torch.ones((128 << 20,), dtype=torch.float32, device=dev)
         flush = lambda: flush_buf.sum()
-        if args.mode == "decode_tokens":
+        if args.mode == "decode_prologue":
+            res = decode_prologue_measurement(args, {}, torch, np, rda, synth, dev, timed, flush,
+                                              reps=args.steps)
+        elif args.mode == "decode_tokens":
             res = decode_tokens_measurements(args, {}, torch, np, rda, synth, dev, stream, timed,
                                              flush, reps=args.steps,
                                              modes=("verify_commit_in_place",))
@@ -704,7 +708,44 @@ def prologue_measurements(args, out, torch, np, rda, synth, dev, timed, flush, T
         dbytes = B * H * tok_bytes + B * hist_bytes
         res["decode"] = {"B": B, "us_per_call": dsec * 1e6, "GBps": dbytes / dsec / 1e9,
                          "bytes_per_call": dbytes, "roofline": hbm_roofline(dbytes, dsec)}
+        res["decode_fused"] = decode_prologue_measurement(args, out, torch, np, rda, synth, dev,
+                                                          timed, flush, reps)
+        if "decode" in out:
+            res["decode_fused"]["prologue_plus_decode_step_us"] = (
+                dsec * 1e6 + out["decode"]["us_per_step"])
     return res
+
+
+def decode_prologue_measurement(args, out, torch, np, rda, synth, dev, timed, flush, reps=10,
+                                B=256, H=16):
+    """rda_decode_step_prologue on the decode batch (B sequences x H heads,
+    conv width 4, SiLU, the history updated in place, fp32 states in place),
+    timed after a cache flush, with its algorithmic bandwidth: the state read
+    and written, the raw token and the gates' inputs read, the history read
+    and written, o written."""
+    K = PROLOGUE_K
+    x = synth.prologue_inputs(B, H, K, N=B, key=(9,))
+    dv = lambda a: torch.from_numpy(a).to(dev)
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)
+    xq, xk, xv, w, br, gl = (bf(x.xq), bf(x.xk), bf(x.xv), dv(x.conv_w), dv(x.beta_raw),
+                             dv(x.g_log))
+    dl, hist = dv(x.delta), bf(x.hist)
+    S = dv(synth.decode_state(B, H))
+    o = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    sec = timed(lambda: rda.rda_decode_step_prologue(xq, xk, xv, w, br, gl, S, delta=dl,
+                                                     hist_in=hist, hist_out=hist, o=o),
+                reps, flush)
+    nbytes = B * H * (2 * STATE_BYTES + 3 * D * 2 + 3 * 4 + D * 4) + \
+        B * 2 * 3 * (K - 1) * H * D * 2
+    # the plain decode step on the same states, timed the same way
+    xd = synth.decode_step_inputs(0, B, H)
+    q, k, v = (bf(getattr(xd, nm)) for nm in "qkv")
+    a, b = dv(xd.a), dv(xd.b)
+    psec = timed(lambda: rda.rda_decode_step(q, k, v, a, b, S, o=o), reps, flush)
+    return {"B": B, "H": H, "conv_width": K, "us_per_step": sec * 1e6,
+            "GBps": nbytes / sec / 1e9, "bytes_per_step": nbytes,
+            "roofline": hbm_roofline(nbytes, sec, read_traffic("rda_decode_step_prologue")),
+            "plain_decode_step_us_same_timing": psec * 1e6}
 
 
 def epilogue_measurements(args, out, torch, np, rda, synth, dev, timed, flush, T, H, reps=10):

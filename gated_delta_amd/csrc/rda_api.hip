@@ -598,6 +598,70 @@ rda_status rda_prologue(const void* x_q, const void* x_k, const void* x_v, rda_d
     return RDA_OK;
 }
 
+rda_status rda_decode_step_prologue(const void* x_q, const void* x_k, const void* x_v,
+                                   rda_dtype x_dtype, const float* conv_w, int32_t conv_width,
+                                   int32_t conv_act, const void* hist_in, void* hist_out,
+                                   const float* beta_raw, const float* delta, const float* g_log,
+                                   float decay_floor, float l2_eps, int32_t batch,
+                                   int32_t num_heads, int32_t dk, int32_t dv, float* S, float* o,
+                                   hipStream_t stream) {
+    if (x_dtype != RDA_BF16 && x_dtype != RDA_FP32) return RDA_ERR_DTYPE;
+    if (x_dtype != RDA_BF16) return RDA_ERR_UNSUPPORTED;
+    if (conv_width < 1 || conv_width > RDA_CONV_MAX_WIDTH) return RDA_ERR_VALUE;
+    if (conv_act != RDA_CONV_ACT_NONE && conv_act != RDA_CONV_ACT_SILU) return RDA_ERR_VALUE;
+    if (std::isnan(decay_floor) || decay_floor == INFINITY) return RDA_ERR_VALUE;
+    if (!(l2_eps >= 0.f) || l2_eps == INFINITY) return RDA_ERR_VALUE;
+    if (batch < 0) return RDA_ERR_SHAPE;
+    rda_status st = check_dims(num_heads, dk, dv);
+    if (st != RDA_OK) return st;
+    if (int64_t(batch) * num_heads > INT32_MAX) return RDA_ERR_SHAPE;
+    if (batch == 0) return RDA_OK;
+    if (!x_q || !x_k || !x_v || !conv_w || !beta_raw || !g_log || !S || !o) return RDA_ERR_NULL;
+    for (const void* p : {x_q, x_k, x_v, static_cast<const void*>(conv_w), hist_in,
+                          static_cast<const void*>(hist_out), static_cast<const void*>(beta_raw),
+                          static_cast<const void*>(delta), static_cast<const void*>(g_log),
+                          static_cast<const void*>(S), static_cast<const void*>(o)})
+        if (p && !aligned16(p)) return RDA_ERR_ALIGN;
+    const int32_t K = conv_width;
+    const size_t bh = size_t(batch) * num_heads;
+    const size_t hist_bytes = size_t(batch) * 3 * (K - 1) * num_heads * kD * 2;
+    const bool keep_hist = hist_out && K > 1;
+    const Range rxq = rng(x_q, bh * kD * 2), rxk = rng(x_k, bh * kD * 2), rxv = rng(x_v, bh * kD * 2);
+    const Range rw = rng(conv_w, size_t(3) * num_heads * kD * K * 4);
+    const Range rhi = rng(hist_in, hist_in ? hist_bytes : 0);
+    const Range rho = rng(keep_hist ? hist_out : nullptr, hist_bytes);
+    const Range rbr = rng(beta_raw, bh * 4), rdl = rng(delta, delta ? bh * 4 : 0);
+    const Range rg = rng(g_log, bh * 4);
+    const Range rS = rng(S, bh * kD * kD * 4), ro = rng(o, bh * kD * 4);
+    // the history may be updated in place (hist_out == hist_in exactly)
+    const bool hist_same = keep_hist && hist_in == hist_out;
+    for (Range out : {rS, ro, rho}) {
+        for (Range in : {rxq, rxk, rxv, rw, rbr, rdl, rg})
+            if (overlap(out, in)) return RDA_ERR_ALIAS;
+    }
+    if (!hist_same && overlap(rho, rhi)) return RDA_ERR_ALIAS;
+    if (overlap(rS, rhi) || overlap(ro, rhi) || overlap(rS, ro) || overlap(rS, rho) ||
+        overlap(ro, rho))
+        return RDA_ERR_ALIAS;
+    DecodePrologueArgs P;
+    P.x[0] = static_cast<const uint16_t*>(x_q);
+    P.x[1] = static_cast<const uint16_t*>(x_k);
+    P.x[2] = static_cast<const uint16_t*>(x_v);
+    P.w = conv_w;
+    P.hin = static_cast<const uint16_t*>(hist_in);
+    P.hout = keep_hist ? static_cast<uint16_t*>(hist_out) : nullptr;
+    P.beta = beta_raw;
+    P.delta = delta;
+    P.glog = g_log;
+    P.floor_log = decay_floor;
+    P.l2eps = l2_eps;
+    P.H = num_heads;
+    P.S = S;
+    P.o = o;
+    if (launch_decode_prologue(P, batch, K, conv_act, stream) != hipSuccess) return RDA_ERR_HIP;
+    return RDA_OK;
+}
+
 rda_status rda_output_norm_gate(const float* o, const void* g, rda_dtype g_dtype,
                                 const float* weight, float eps, int32_t act, int64_t rows,
                                 int32_t dv, void* out, rda_dtype out_dtype, hipStream_t stream) {

@@ -24,8 +24,55 @@
 // products are 16-lane DPP reductions.
 #include "rda_device.h"
 #include "rda_internal.h"
+#include "rda_lds.h"
+#include "rda_prologue_math.h"
 
 namespace rda {
+
+// The single-pass update of one lane's 4 state rows (rows rbase + 4p, p < 4,
+// columns 4c.. and 64+4c..) for one token: the dot products, the error, the
+// in-place state write and this row set's outputs (lane c < 4 returns the
+// output of row rbase + 4c).  Shared by the decode step kernels so that they
+// give the same bits.
+// Every multiply-add is an explicit fmaf and the compiler may fuse nothing
+// else, so each kernel that inlines this runs the same IEEE operations.
+__device__ __forceinline__ float decode_rows(const f32x4 (&s)[4][2], const float (&kx)[8],
+                                             const float (&qx)[8], float av, float bv,
+                                             const float (&vr)[4], int c, float* __restrict__ Sb,
+                                             int rbase) {
+#pragma clang fp contract(off)
+    float kap = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kap = fmaf(kx[j], qx[j], kap);
+    kap = dpp_sum16(kap);
+
+    float o_mine = 0.f;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            sk = fmaf(s[p][1][j], kx[4 + j], fmaf(s[p][0][j], kx[j], sk));
+            sq = fmaf(s[p][1][j], qx[4 + j], fmaf(s[p][0][j], qx[j], sq));
+        }
+        sk = dpp_sum16(sk);
+        sq = dpp_sum16(sq);
+        const float e = fmaf(-av, sk, vr[p]);
+        const float be = bv * e;
+        const float orow = fmaf(av, sq, be * kap);
+        if (c == p) o_mine = orow;
+        f32x4 n0, n1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            n0[j] = fmaf(av, s[p][0][j], be * kx[j]);
+            n1[j] = fmaf(av, s[p][1][j], be * kx[4 + j]);
+        }
+        const int row = rbase + 4 * p;
+        *reinterpret_cast<f32x4*>(Sb + row * kD + 4 * c) = n0;
+        *reinterpret_cast<f32x4*>(Sb + row * kD + 64 + 4 * c) = n1;
+    }
+    return o_mine;
+}
 
 template <typename TIn>
 __global__ __launch_bounds__(256) void decode_step_kernel(const TIn* __restrict__ q,
@@ -62,36 +109,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const TIn* __restrict_
 #pragma unroll
     for (int p = 0; p < 4; ++p) vr[p] = load1<TIn>(v + bh * kD + 64 * half + 16 * w + 4 * p + g);
 
-    float kap = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) kap += kx[j] * qx[j];
-    kap = dpp_sum16(kap);
-
-    float o_mine = 0.f;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        float sk = 0.f, sq = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            sk += s[p][0][j] * kx[j] + s[p][1][j] * kx[4 + j];
-            sq += s[p][0][j] * qx[j] + s[p][1][j] * qx[4 + j];
-        }
-        sk = dpp_sum16(sk);
-        sq = dpp_sum16(sq);
-        const float e = vr[p] - av * sk;
-        const float be = bv * e;
-        const float orow = av * sq + be * kap;
-        if (c == p) o_mine = orow;
-        f32x4 n0, n1;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            n0[j] = av * s[p][0][j] + be * kx[j];
-            n1[j] = av * s[p][1][j] + be * kx[4 + j];
-        }
-        const int row = 64 * half + 16 * w + 4 * p + g;
-        *reinterpret_cast<f32x4*>(Sb + row * kD + 4 * c) = n0;
-        *reinterpret_cast<f32x4*>(Sb + row * kD + 64 + 4 * c) = n1;
-    }
+    const float o_mine = decode_rows(s, kx, qx, av, bv, vr, c, Sb, 64 * half + 16 * w + g);
     if (c < 4) o[bh * kD + 64 * half + 16 * w + 4 * c + g] = o_mine;
 }
 
@@ -346,6 +364,157 @@ __global__ __launch_bounds__(256) void decode_diag_kernel(const TIn* __restrict_
         *reinterpret_cast<f32x4*>(Sb + row * kD + 64 + 4 * c) = n1;
     }
     if (c < 4) o[bh * kD + 64 * half + 16 * w + 4 * c + g] = o_mine;
+}
+
+// ---------------------------------------------------------------------------
+// One decode step with the block's prologue in front, one 512-thread
+// workgroup per (batch, head).  Lane groups 0, 1, 2 of wave 0 run the
+// prologue for q, k and v in the prologue kernel's own lane layout (a lane
+// 8 channels, 4c.. and 64+4c..) and per-channel arithmetic
+// (rda_prologue_math.h): the short convolution over the history and the
+// raw token, the activation, the q / k L2 norm or the write gate on v, the
+// rounding to bf16.  They put q, k, v (768 bytes) in LDS and move the
+// history on by one token; every wave then reads its operands after one
+// barrier and runs the decode step's single pass over its 16 state rows
+// (decode_rows, wave w rows 16w + 4p + g).  The result is that of
+// rda_prologue (one-token layout) followed by rda_decode_step, bit for bit,
+// and q, k, v, a, b never reach memory.  A lane reads its history slots
+// before it writes the shifted ones, and no other lane touches them, so the
+// history may be updated in place.
+//
+// That the history may be updated in place is what fixes one workgroup per
+// (batch, head): both halves of the state need every q and k channel, hence
+// the whole q / k history.  On 256 x 16 states this step takes about 93 us,
+// as long as rda_prologue followed by rda_decode_step (about 13 + 80.5 us);
+// the plain decode step keeps twice the bytes in flight per CU with two
+// 32 KiB workgroups per (batch, head).  Measured and not kept: every lane
+// group running the whole prologue for itself (173 us: 157 registers and
+// all the conv weights loaded by every group), eight waves per SIMD (2
+// registers spilled: 99 us), a
+// ninth wave for the prologue (94 us), and persistent workgroups with the
+// prologue one item ahead in a second LDS buffer (88 registers: 100 us).
+template <int K, int kAct>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6)))
+void decode_prologue_kernel(const DecodePrologueArgs P) {
+    __shared__ __attribute__((aligned(16))) uint16_t qkv[3][kD];
+    const int64_t bh = blockIdx.x;
+    const int64_t n = bh / P.H;
+    const int h = int(bh - n * P.H);
+    const int t = threadIdx.x;
+    const int w = wave_id();      // 0..7
+    const int g = (t >> 4) & 3;
+    const int c = t & 15;
+    const int rbase = 16 * w + g;
+    float* __restrict__ Sb = P.S + bh * (kD * kD);
+
+    const int ch0 = 4 * c, ch1 = 64 + 4 * c;
+    const float br = P.beta[bh];
+    f32x4 s[4][2];
+    auto load_state = [&]() {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int row = rbase + 4 * p;
+            s[p][0] = *reinterpret_cast<const f32x4*>(Sb + row * kD + 4 * c);
+            s[p][1] = *reinterpret_cast<const f32x4*>(Sb + row * kD + 64 + 4 * c);
+        }
+    };
+    // the state loads go out first everywhere except in the prologue's lanes,
+    // which load theirs once the convolution is done (their registers then
+    // hold either the convolution's operands or the state, never both, which
+    // keeps the kernel at 6 waves per SIMD without spills)
+    if (!(w == 0 && g < 3)) load_state();
+    if (w == 0 && g < 3) {
+        const int x = g;   // 0 = q, 1 = k, 2 = v
+        const size_t hd = size_t(P.H) * kD;
+        // history slot m of tensor x for this (sequence, head): [N][3][K-1][H][128]
+        auto slot = [&](int m) { return ((size_t(n) * 3 + x) * (K - 1) + m) * hd + size_t(h) * kD; };
+        float wt[K][8];
+        const float* wb = P.w + (size_t(x) * P.H + h) * kD * K;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < K; ++i) {
+                wt[i][j] = wb[(ch0 + j) * K + i];
+                wt[i][4 + j] = wb[(ch1 + j) * K + i];
+            }
+        u32x2 win[K][2];   // taps 0 .. K-2 from the history, tap K-1 the current token
+#pragma unroll
+        for (int i = 0; i < K - 1; ++i) {
+            win[i][0] = u32x2{0u, 0u};
+            win[i][1] = u32x2{0u, 0u};
+            if (P.hin) {
+                win[i][0] = *reinterpret_cast<const u32x2*>(P.hin + slot(i) + ch0);
+                win[i][1] = *reinterpret_cast<const u32x2*>(P.hin + slot(i) + ch1);
+            }
+        }
+        const uint16_t* xp = P.x[x] + bh * kD;
+        win[K - 1][0] = *reinterpret_cast<const u32x2*>(xp + ch0);
+        win[K - 1][1] = *reinterpret_cast<const u32x2*>(xp + ch1);
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+            float xv[8];
+            widen8(win[i], xv);
+            conv_tap(acc, wt[i], xv);
+        }
+        conv_activation<kAct>(acc);
+        const float scale =
+            x < 2 ? l2_scale(acc, P.l2eps) : write_gate(br, P.delta ? P.delta[bh] : 0.f);
+        *reinterpret_cast<u32x2*>(&qkv[x][ch0]) =
+            u32x2{pack_bf16(acc[0] * scale, acc[1] * scale), pack_bf16(acc[2] * scale, acc[3] * scale)};
+        *reinterpret_cast<u32x2*>(&qkv[x][ch1]) =
+            u32x2{pack_bf16(acc[4] * scale, acc[5] * scale), pack_bf16(acc[6] * scale, acc[7] * scale)};
+        // the history moves on by one token: slot m takes the old slot m + 1,
+        // the newest slot the current raw token (read above by this lane)
+        if (P.hout) {
+#pragma unroll
+            for (int m = 0; m < K - 1; ++m) {
+                *reinterpret_cast<u32x2*>(P.hout + slot(m) + ch0) = win[m + 1][0];
+                *reinterpret_cast<u32x2*>(P.hout + slot(m) + ch1) = win[m + 1][1];
+            }
+        }
+        load_state();
+    }
+    const float av = floored_decay(P.glog[bh], P.floor_log);
+    const float bv = erase_gate(br);
+    __syncthreads();
+
+    float kx[8], qx[8], vr[4];
+    {
+        const u32x2 kr[2] = {*reinterpret_cast<const u32x2*>(&qkv[1][ch0]),
+                             *reinterpret_cast<const u32x2*>(&qkv[1][ch1])};
+        const u32x2 qr[2] = {*reinterpret_cast<const u32x2*>(&qkv[0][ch0]),
+                             *reinterpret_cast<const u32x2*>(&qkv[0][ch1])};
+        widen8(kr, kx);
+        widen8(qr, qx);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) vr[p] = bf16_bits_to_f32(qkv[2][rbase + 4 * p]);
+    }
+    const float o_mine = decode_rows(s, kx, qx, av, bv, vr, c, Sb, rbase);
+    if (c < 4) P.o[bh * kD + rbase + 4 * c] = o_mine;
+}
+
+hipError_t launch_decode_prologue(const DecodePrologueArgs& P, int32_t batch, int32_t K,
+                                  int32_t act, hipStream_t stream) {
+    const unsigned grid = unsigned(int64_t(batch) * P.H);
+    if (grid == 0) return hipSuccess;
+#define RDA_DP_LAUNCH(KW)                                                                         \
+    if (act == RDA_CONV_ACT_SILU)                                                                 \
+        hipLaunchKernelGGL((decode_prologue_kernel<KW, RDA_CONV_ACT_SILU>), dim3(grid), dim3(512), \
+                           0, stream, P);                                                         \
+    else                                                                                          \
+        hipLaunchKernelGGL((decode_prologue_kernel<KW, RDA_CONV_ACT_NONE>), dim3(grid), dim3(512), \
+                           0, stream, P);
+    switch (K) {
+        case 1: RDA_DP_LAUNCH(1) break;
+        case 2: RDA_DP_LAUNCH(2) break;
+        case 3: RDA_DP_LAUNCH(3) break;
+        default: RDA_DP_LAUNCH(4) break;
+    }
+#undef RDA_DP_LAUNCH
+    return hipGetLastError();
 }
 
 hipError_t launch_decode_diag(const void* q, const void* k, const void* v, rda_dtype dt,

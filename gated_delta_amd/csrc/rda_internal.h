@@ -112,6 +112,25 @@ struct PrologueArgs {
 };
 hipError_t launch_prologue(const PrologueArgs& P, int32_t K, int32_t act, hipStream_t stream);
 
+// One decode step with the prologue in front (one token per sequence):
+// raw projections, conv weights and history, gates' inputs -> the state
+// update and the outputs, the history moved on (hout may be hin).
+struct DecodePrologueArgs {
+    const uint16_t* x[3];      // raw q, k, v [B, H, 128] bf16
+    const float* w;            // [3][H][128][K]
+    const uint16_t* hin;       // [B][3][K-1][H][128] or nullptr (zeros)
+    uint16_t* hout;            // same shape or nullptr (no history kept)
+    const float* beta;         // [B, H]
+    const float* delta;        // [B, H] or nullptr
+    const float* glog;         // [B, H]
+    float floor_log, l2eps;
+    int32_t H;
+    float* S;                  // [B, H, 128, 128] in/out
+    float* o;                  // [B, H, 128]
+};
+hipError_t launch_decode_prologue(const DecodePrologueArgs& P, int32_t batch, int32_t K,
+                                  int32_t act, hipStream_t stream);
+
 // One walk job: where the state starts (identity, S0, or zero when S0 is
 // null), whether v counts (zero_v: every value taken as 0, so the walk
 // applies the chunks' transition alone) and where the final state goes

@@ -34,38 +34,10 @@
 
 #include "rda_device.h"
 #include "rda_internal.h"
+#include "rda_prologue_math.h"
 
 namespace rda {
 namespace {
-
-
-__device__ __forceinline__ void widen8(const u32x2 r[2], float out[8]) {
-    for (int h = 0; h < 2; ++h) {
-        out[4 * h + 0] = __uint_as_float(r[h][0] << 16);
-        out[4 * h + 1] = __uint_as_float(r[h][0] & 0xffff0000u);
-        out[4 * h + 2] = __uint_as_float(r[h][1] << 16);
-        out[4 * h + 3] = __uint_as_float(r[h][1] & 0xffff0000u);
-    }
-}
-
-__device__ __forceinline__ uint32_t pack_bf16(float x0, float x1) {
-    const f32x2 v = {x0, x1};   // round to nearest even (v_cvt_pk_bf16_f32)
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-
-// e^x and ln(x) on the hardware's exp2 / log2 (one instruction each, about
-// 1 ulp; the results here end in bf16 or feed gates)
-__device__ __forceinline__ float hw_exp(float x) {
-    return __builtin_amdgcn_exp2f(x * 1.44269504088896341f);
-}
-__device__ __forceinline__ float hw_log(float x) {
-    return __builtin_amdgcn_logf(x) * 0.693147180559945309f;
-}
-
-// softplus(y) = ln(1 + e^y), without overflow for large |y|
-__device__ __forceinline__ float softplus(float y) {
-    return fmaxf(y, 0.f) + hw_log(1.f + hw_exp(-fabsf(y)));
-}
 
 // Sequence of token t: index n, first token s, end e (all clamped, so
 // malformed offsets stay in bounds).
@@ -185,26 +157,17 @@ __global__ __launch_bounds__(256) void prologue_kernel(const PrologueArgs P) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) xv[e] = 0.f;
             }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = fmaf(wt[i][e], xv[e], acc[e]);
+            conv_tap(acc, wt[i], xv);
         }
-        if (kAct == RDA_CONV_ACT_SILU) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                acc[e] = acc[e] * __builtin_amdgcn_rcpf(1.f + hw_exp(-acc[e]));
-        }
+        conv_activation<kAct>(acc);
         const size_t th = size_t(t) * P.H + h;
         float scale;
         if (x < 2) {
-            float ss = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ss = fmaf(acc[e], acc[e], ss);
-            scale = __builtin_amdgcn_rsqf(dpp_sum16(ss) + P.l2eps);
+            scale = l2_scale(acc, P.l2eps);
         } else {
-            // sigmoid(beta + delta) / sigmoid(beta) = exp(softplus(-beta) - softplus(-beta - delta))
             const float br = P.beta[th];
             const float dl = P.delta ? P.delta[th] : 0.f;
-            scale = hw_exp(softplus(-br) - softplus(-br - dl));
+            scale = write_gate(br, dl);
         }
         uint16_t* ob = P.out[x] + th * kD;
         *reinterpret_cast<u32x2*>(ob + ch0) =
@@ -212,9 +175,8 @@ __global__ __launch_bounds__(256) void prologue_kernel(const PrologueArgs P) {
         *reinterpret_cast<u32x2*>(ob + ch1) =
             u32x2{pack_bf16(acc[4] * scale, acc[5] * scale), pack_bf16(acc[6] * scale, acc[7] * scale)};
         if (x == 0 && c == 0) {
-            const float br = P.beta[th];
-            P.b[th] = __builtin_amdgcn_rcpf(1.f + hw_exp(-br));
-            P.a[th] = hw_exp(fmaxf(P.glog[th], P.floor_log));
+            P.b[th] = erase_gate(P.beta[th]);
+            P.a[th] = floored_decay(P.glog[th], P.floor_log);
         }
         if (P.hout && K > 1 && t < sq.e) {
             // a sequence shorter than K-1 keeps the newest slots of its old

@@ -42,7 +42,8 @@ STAGE = {"chunk_table_kernel": "rda_chunk_table", "prep_bf16_kernel": "rda_prep"
          "decode_tokens_kernel": "rda_decode_tokens", "norm_gate_kernel": "rda_output_norm_gate",
          "prologue_kernel": "rda_prologue", "prep_diag_kernel": "rda_prep_diag",
          "walk_diag_kernel": "rda_walk_diag", "segment_combine_kernel": "rda_segment_combine",
-         "prep_kernel": "rda_prep", "walk_kernel": "rda_walk"}
+         "prep_kernel": "rda_prep", "walk_kernel": "rda_walk",
+         "decode_prologue_kernel": "rda_decode_step_prologue"}
 
 # the other prefill workloads: bench --mode prefill_config --config N
 CONFIGS = {1: ("T64_H1_fp32", "one fp32 head of 64 tokens (S0 = 0)"),

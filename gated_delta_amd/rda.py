@@ -82,6 +82,10 @@ def _load():
                                      ctypes.c_float, ctypes.c_float, p, i32, i32, i32, i32,
                                      p, p, p, p, p, p]
         lib.rda_prologue.restype = ctypes.c_int
+        lib.rda_decode_step_prologue.argtypes = [p, p, p, ctypes.c_int, p, i32, i32, p, p, p, p,
+                                                 p, ctypes.c_float, ctypes.c_float, i32, i32, i32,
+                                                 i32, p, p, p]
+        lib.rda_decode_step_prologue.restype = ctypes.c_int
         lib.rda_prefill_diag_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
         lib.rda_prefill_diag_workspace_bytes.restype = ctypes.c_size_t
         lib.rda_prefill_diag.argtypes = pre[:18]
@@ -511,6 +515,53 @@ def rda_prologue(x_q: torch.Tensor, x_k: torch.Tensor, x_v: torch.Tensor,
     if st != 0:
         raise RdaError(st, "rda_prologue")
     return q, k, v, a, b
+
+
+def rda_decode_step_prologue(x_q: torch.Tensor, x_k: torch.Tensor, x_v: torch.Tensor,
+                             conv_w: torch.Tensor, beta_raw: torch.Tensor, g_log: torch.Tensor,
+                             S: torch.Tensor, *, delta: Optional[torch.Tensor] = None,
+                             hist_in: Optional[torch.Tensor] = None,
+                             hist_out: Optional[torch.Tensor] = None, conv_act: str = "silu",
+                             decay_floor: float = -5.0, l2_eps: float = 1e-6,
+                             o: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One decode step with the prologue in front (C entry point
+    ``rda_decode_step_prologue``): x_q, x_k, x_v [B, H, 128] bf16 raw
+    projections, conv_w [3, H, 128, K] fp32, beta_raw, g_log (and delta)
+    [B, H] fp32, S [B, H, 128, 128] fp32 updated in place, hist_in / hist_out
+    [B, 3, K-1, H, 128] bf16 (hist_out may be hist_in).  Returns o [B, H, 128]."""
+    lib_ = _load()
+    dev = x_q.device
+    if x_q.dtype != torch.bfloat16:
+        raise TypeError("x_q, x_k, x_v must be bfloat16")
+    if x_q.dim() != 3:
+        raise ValueError("x_q must be [B, H, d]")
+    B, H, d = x_q.shape
+    for name, t in (("x_q", x_q), ("x_k", x_k), ("x_v", x_v)):
+        _need(t, name, torch.bfloat16, (B, H, d), dev)
+    if conv_w.dim() != 4:
+        raise ValueError("conv_w must be [3, H, d, K]")
+    K = conv_w.shape[-1]
+    _need(conv_w, "conv_w", torch.float32, (3, H, d, K), dev)
+    for name, t in (("beta_raw", beta_raw), ("g_log", g_log), ("delta", delta)):
+        if t is not None:
+            _need(t, name, torch.float32, (B, H), dev)
+    for name, t in (("hist_in", hist_in), ("hist_out", hist_out)):
+        if t is not None:
+            _need(t, name, torch.bfloat16, (B, 3, max(K - 1, 0), H, d), dev)
+    _need(S, "S", torch.float32, (B, H, d, d), dev)
+    if conv_act not in _CONV_ACTS:
+        raise ValueError(f"conv_act must be one of {sorted(_CONV_ACTS)}")
+    if o is None:
+        o = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    _need(o, "o", torch.float32, (B, H, d), dev)
+    st = lib_.rda_decode_step_prologue(_ptr(x_q), _ptr(x_k), _ptr(x_v), RDA_BF16, _ptr(conv_w),
+                                       K, _CONV_ACTS[conv_act], _ptr(hist_in), _ptr(hist_out),
+                                       _ptr(beta_raw), _ptr(delta), _ptr(g_log),
+                                       float(decay_floor), float(l2_eps), B, H, d, d, _ptr(S),
+                                       _ptr(o), _stream_handle(stream))
+    if st != 0:
+        raise RdaError(st, "rda_decode_step_prologue")
+    return o
 
 
 def rda_prefill_diag_workspace_bytes(num_seqs: int, total_tokens: int, num_heads: int,

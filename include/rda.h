@@ -352,6 +352,36 @@ rda_status rda_prologue(const void* x_q, const void* x_k, const void* x_v, rda_d
                         int32_t num_heads, int32_t d, void* q, void* k, void* v, float* a,
                         float* b, hipStream_t stream);
 
+/*
+ * One decode step with the prologue in front: rda_prologue for one token
+ * per sequence (the decode layout, cu_seqlens NULL, total_tokens = batch)
+ * followed by rda_decode_step, in one launch and one pass over the state,
+ * without q, k, v, a, b reaching memory.  The teardown's section "The cache
+ * is small if the runtime keeps it small" counts the short convolution
+ * windows beside the recurrent state as the per-sequence decode cache; this
+ * entry point carries both, the state S and the history, in and out.
+ *
+ *   x_q, x_k, x_v  raw projections [batch, H, d] bf16 (x_dtype must be RDA_BF16)
+ *   conv_w, conv_width, conv_act, beta_raw, delta, g_log, decay_floor, l2_eps
+ *                  as in rda_prologue ([batch, H] for the gates)
+ *   hist_in        [batch, 3, K-1, H, d] bf16 or NULL (zeros)
+ *   hist_out       same shape or NULL (not kept); may be hist_in itself (the
+ *                  history moves on by one token in place); any other overlap
+ *                  with an argument is RDA_ERR_ALIAS
+ *   S              [batch, H, d, d] fp32, updated in place
+ *   o              [batch, H, d] fp32
+ * The result equals rda_prologue followed by rda_decode_step on its outputs
+ * bit for bit (the same arithmetic, and q, k, v rounded to bf16 as the
+ * prologue writes them).  batch = 0 is allowed; d must be 128.
+ */
+rda_status rda_decode_step_prologue(const void* x_q, const void* x_k, const void* x_v,
+                                   rda_dtype x_dtype, const float* conv_w, int32_t conv_width,
+                                   int32_t conv_act, const void* hist_in, void* hist_out,
+                                   const float* beta_raw, const float* delta, const float* g_log,
+                                   float decay_floor, float l2_eps, int32_t batch,
+                                   int32_t num_heads, int32_t dk, int32_t dv, float* S, float* o,
+                                   hipStream_t stream);
+
 /* Activation of the output gate in rda_output_norm_gate. */
 typedef enum {
     RDA_GATE_SIGMOID = 0,  /* sigmoid(g) */

@@ -37,7 +37,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("rda_prefill", "rda_decode_step", "rda_decode_tokens", "rda_prefill_diag",
               "rda_decode_step_diag", "rda_decode_tokens_diag", "rda_prologue", "rda_output_norm_gate",
-              "rda_prefill_workspace_bytes", "rda_prefill_noalloc",
+              "rda_prefill_workspace_bytes", "rda_prefill_noalloc", "rda_decode_step_prologue",
               "rda_chunk_table", "rda_abi_version", "rda_status_string"):
         assert n in names
 
@@ -154,6 +154,35 @@ def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
     assert _noalloc(lib, N=2) == SHAPE
     assert _noalloc(lib, H=0) == SHAPE
     assert _noalloc(lib, dk=64) == UNSUP
+
+
+def _dprol(lib, xq=P, xk=P + GiB, xv=P + 2 * GiB, dt=0, w=P + 3 * GiB, K=4, act=1,
+           hin=P + 4 * GiB, hout=P + 4 * GiB, beta=P + 5 * GiB, delta=None, glog=P + 6 * GiB,
+           floor=-5.0, eps=1e-6, B=8, H=16, dk=128, dv=128, S=P + 7 * GiB, o=P + 8 * GiB):
+    return lib.rda_decode_step_prologue(xq, xk, xv, dt, w, K, act, hin, hout, beta, delta, glog,
+                                        floor, eps, B, H, dk, dv, S, o, None)
+
+
+def test_decode_step_prologue_rejects_bad_arguments(lib):
+    assert _dprol(lib, dt=1) == UNSUP
+    assert _dprol(lib, dt=5) == DTYPE
+    assert _dprol(lib, K=0) == VALUE
+    assert _dprol(lib, K=5) == VALUE
+    assert _dprol(lib, act=3) == VALUE
+    assert _dprol(lib, floor=float("nan")) == VALUE
+    assert _dprol(lib, eps=-1.0) == VALUE
+    assert _dprol(lib, B=-1) == SHAPE
+    assert _dprol(lib, H=0) == SHAPE
+    assert _dprol(lib, dk=64) == UNSUP
+    assert _dprol(lib, B=0, xq=None) == OK          # nothing to do, nothing read
+    assert _dprol(lib, xq=None) == NULL
+    assert _dprol(lib, S=None) == NULL
+    assert _dprol(lib, o=None) == NULL
+    assert _dprol(lib, xk=P + GiB + 8) == ALIGN
+    assert _dprol(lib, o=P + 16) == ALIAS                   # o overlaps x_q
+    assert _dprol(lib, S=P + 5 * GiB) == ALIAS              # S overlaps beta_raw
+    assert _dprol(lib, hout=P + 4 * GiB + 256) == ALIAS     # history out overlaps history in
+    assert _dprol(lib, o=P + 7 * GiB + 1024) == ALIAS       # o overlaps S
 
 
 def test_decode_rejects_bad_arguments(lib):
