@@ -417,7 +417,6 @@ rda_status rda_prefill_diag(const void* q, const void* k, const void* v, rda_dty
     if (!cu_seqlens && num_seqs != 1) return RDA_ERR_SHAPE;
     rda_status st = check_dims(num_heads, dk, dv);
     if (st != RDA_OK) return st;
-    if (qkv_dtype != RDA_BF16) return RDA_ERR_UNSUPPORTED;
     const int32_t mc = rda_max_chunks(num_seqs, total_tokens);
     if (mc < 0) return RDA_ERR_SHAPE;
     if (int64_t(mc) * num_heads > INT32_MAX || int64_t(num_seqs) * num_heads * kWalkSlices > INT32_MAX)
@@ -434,7 +433,8 @@ rda_status rda_prefill_diag(const void* q, const void* k, const void* v, rda_dty
     if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return RDA_ERR_ALIGN;
     const size_t th = size_t(total_tokens) * num_heads;
     const size_t sbytes = size_t(num_seqs) * num_heads * kD * kD * sizeof(float);
-    const Range rq = rng(q, th * kD * 2), rk = rng(k, th * kD * 2), rv = rng(v, th * kD * 2);
+    const size_t esz = qkv_dtype == RDA_BF16 ? 2 : 4;
+    const Range rq = rng(q, th * kD * esz), rk = rng(k, th * kD * esz), rv = rng(v, th * kD * esz);
     const Range ral = rng(alpha, th * kD * 4), rb = rng(b, th * 4);
     const Range ro = rng(o, th * kD * 4), rs0 = rng(S0, S0 ? sbytes : 0);
     const Range rsf = rng(S_final, S_final ? sbytes : 0), rws = rng(workspace, need);
@@ -455,9 +455,6 @@ rda_status rda_prefill_diag(const void* q, const void* k, const void* v, rda_dty
     if (launch_chunk_table(cu_seqlens, num_seqs, total_tokens, mc, rec, seq_off, nch, stream) !=
         hipSuccess)
         return RDA_ERR_HIP;
-    const auto* q16 = static_cast<const uint16_t*>(q);
-    const auto* k16 = static_cast<const uint16_t*>(k);
-    const auto* v16 = static_cast<const uint16_t*>(v);
     unsigned char* factors = ws + align256(tl.bytes);
     const SegPlan sp = seg_plan(num_seqs, total_tokens, num_heads);
     if (sp.P > 0 && cu_seqlens == nullptr) {
@@ -469,18 +466,18 @@ rda_status rda_prefill_diag(const void* q, const void* k, const void* v, rda_dty
         float* S_in = reinterpret_cast<float*>(seg + 2 * sb);
         const WalkJob first[2] = {{nullptr, E, 0, 0}, {nullptr, M, 1, 1}};
         const WalkJob last{S_in, nullptr, 0, 0};
-        if (launch_prep_diag(q16, k16, alpha, b, num_heads, mc, rec, nch, factors, stream) !=
-                hipSuccess ||
-            launch_walk_diag(v16, sp.P, num_heads, rec, seq_off, nch, factors, nullptr, first, 2,
-                             sp.cps, false, stream) != hipSuccess ||
+        if (launch_prep_diag(q, k, qkv_dtype, alpha, b, num_heads, mc, rec, nch, factors,
+                             stream) != hipSuccess ||
+            launch_walk_diag(v, qkv_dtype, sp.P, num_heads, rec, seq_off, nch, factors, nullptr,
+                             first, 2, sp.cps, false, stream) != hipSuccess ||
             launch_segment_combine(S0, E, M, S_in, S_final, sp.P, num_heads, stream) !=
                 hipSuccess ||
-            launch_walk_diag(v16, sp.P, num_heads, rec, seq_off, nch, factors, o, &last, 1,
-                             sp.cps, true, stream) != hipSuccess)
+            launch_walk_diag(v, qkv_dtype, sp.P, num_heads, rec, seq_off, nch, factors, o, &last,
+                             1, sp.cps, true, stream) != hipSuccess)
             return RDA_ERR_HIP;
         return RDA_OK;
     }
-    if (launch_prefill_diag(q16, k16, v16, alpha, b, num_seqs, num_heads,
+    if (launch_prefill_diag(q, k, v, qkv_dtype, alpha, b, num_seqs, num_heads,
                             total_tokens > 0 ? mc : 0, rec, seq_off, nch, factors, S0, o, S_final,
                             stream) != hipSuccess)
         return RDA_ERR_HIP;

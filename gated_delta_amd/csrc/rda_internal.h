@@ -142,8 +142,8 @@ struct WalkJob {
     int zero_v;
 };
 
-// Per-channel decay: prep + walk after the chunk table (bf16 q, k, v).
-hipError_t launch_prefill_diag(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+// Per-channel decay: prep + walk after the chunk table (q, k, v in dt).
+hipError_t launch_prefill_diag(const void* q, const void* k, const void* v, rda_dtype dt,
                                const float* alpha, const float* b, int32_t num_seqs,
                                int32_t heads, int32_t max_chunks, const int32_t* rec,
                                const int32_t* seq_off, const int32_t* num_chunks,
@@ -152,11 +152,11 @@ hipError_t launch_prefill_diag(const uint16_t* q, const uint16_t* k, const uint1
 // Its two stages apart (the segmented state pass runs the walk three times
 // over one prep): the prep, and the walk with jobs, segment runs and the
 // instantiation without outputs as for launch_walk_bf16.
-hipError_t launch_prep_diag(const uint16_t* q, const uint16_t* k, const float* alpha,
+hipError_t launch_prep_diag(const void* q, const void* k, rda_dtype dt, const float* alpha,
                             const float* b, int32_t heads, int32_t max_chunks, const int32_t* rec,
                             const int32_t* num_chunks, unsigned char* factors,
                             hipStream_t stream);
-hipError_t launch_walk_diag(const uint16_t* v, int32_t num_seqs, int32_t heads,
+hipError_t launch_walk_diag(const void* v, rda_dtype dt, int32_t num_seqs, int32_t heads,
                             const int32_t* rec, const int32_t* seq_off,
                             const int32_t* num_chunks, const unsigned char* factors, float* o,
                             const WalkJob* jobs, int32_t num_jobs, int32_t seg_chunks,

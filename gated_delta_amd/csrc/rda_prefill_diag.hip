@@ -53,16 +53,26 @@
 namespace rda {
 namespace {
 
-constexpr int kKS = 136;                // bf16 K / Q tile row stride in the prep
+// K / Q tile row stride in the prep (elements): 136 bf16 or 132 fp32, both
+// 4 banks apart from row to row
+template <typename TIn>
+constexpr int kKS = sizeof(TIn) == 2 ? 136 : 132;
 constexpr int kGS = 129;                // fp32 G row stride in the prep
 constexpr float kLog2e = 1.44269504088896341f;
 constexpr float kSpanMax = 60.f * kLog2e;   // largest diagonal-block span in log2 units
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// an input element as fp32 (bf16 bits, or fp32 as it is)
+__device__ __forceinline__ float in_f32(uint16_t x) { return bf16_bits_to_f32(x); }
+__device__ __forceinline__ float in_f32(float x) { return x; }
+
+// K and Q staged in their input type: bf16 (124.5 KiB in all) or fp32
+// (156.5 KiB), so that fp32 inputs enter every product at full precision
+template <typename TIn>
 struct PrepDiagLds {
-    uint16_t K[kC][kKS];
-    uint16_t Q[kC][kKS];
+    TIn K[kC][kKS<TIn>];
+    TIn Q[kC][kKS<TIn>];
     float G[kC][kGS];        // running sum of log2(alpha) per key channel
     float Gtot[8][kD];       // each eighth of the chunk's own sum per channel
     float L[kC * kFS];
@@ -75,8 +85,9 @@ struct PrepDiagLds {
 
 // 8 values of a row of X . 2^(GL[row] - GL[ref]) at the permuted keys of k
 // block m (32m + 4g + i and 32m + 16 + 4g + i), as bf16 hi / lo
-__device__ __forceinline__ void scaled_keys(const PrepDiagLds& S, const uint16_t (*X)[kKS], int row,
-                                            int ref, int m, int g, bool ref_minus_row,
+template <typename TIn>
+__device__ __forceinline__ void scaled_keys(const PrepDiagLds<TIn>& S, const TIn (*X)[kKS<TIn>],
+                                            int row, int ref, int m, int g, bool ref_minus_row,
                                             bf16x8& hi, bf16x8& lo) {
     float v[8];
 #pragma unroll
@@ -86,7 +97,7 @@ __device__ __forceinline__ void scaled_keys(const PrepDiagLds& S, const uint16_t
             const int key = 32 * m + 16 * hh + 4 * g + i;
             const float d = ref_minus_row ? S.G[ref][key] - S.G[row][key]
                                           : S.G[row][key] - S.G[ref][key];
-            v[4 * hh + i] = bf16_bits_to_f32(X[row][key]) * exp2_hw(d);
+            v[4 * hh + i] = in_f32(X[row][key]) * exp2_hw(d);
         }
     split8(v, hi, lo);
 }
@@ -94,11 +105,38 @@ __device__ __forceinline__ void scaled_keys(const PrepDiagLds& S, const uint16_t
 constexpr int kPrepThreads = 1024;
 constexpr int64_t kPrepDiagGrid = 256;
 
+static_assert(sizeof(PrepDiagLds<float>) <= 160 * 1024, "LDS budget of one workgroup");
+
+// 8 consecutive input elements of a row, as loaded (bf16 bits or fp32)
+template <typename TIn>
+struct Row8;
+template <>
+struct Row8<uint16_t> {
+    u16x8 d;
+    __device__ __forceinline__ void zero() { d = u16x8{0, 0, 0, 0, 0, 0, 0, 0}; }
+    __device__ __forceinline__ void load(const uint16_t* p) { d = *reinterpret_cast<const u16x8*>(p); }
+    __device__ __forceinline__ void store(uint16_t* p) const { *reinterpret_cast<u16x8*>(p) = d; }
+};
+template <>
+struct Row8<float> {
+    f32x4 d0, d1;
+    __device__ __forceinline__ void zero() { d0 = zero4(); d1 = zero4(); }
+    __device__ __forceinline__ void load(const float* p) {
+        d0 = *reinterpret_cast<const f32x4*>(p);
+        d1 = *reinterpret_cast<const f32x4*>(p + 4);
+    }
+    __device__ __forceinline__ void store(float* p) const {
+        *reinterpret_cast<f32x4*>(p) = d0;
+        *reinterpret_cast<f32x4*>(p + 4) = d1;
+    }
+};
+
+template <typename TIn>
 __global__ __launch_bounds__(kPrepThreads) void prep_diag_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ alpha,
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ alpha,
     const float* __restrict__ b, int H, const int32_t* __restrict__ rec,
     const int32_t* __restrict__ num_chunks, unsigned char* __restrict__ factors) {
-    __shared__ __attribute__((aligned(16))) PrepDiagLds S;
+    __shared__ __attribute__((aligned(16))) PrepDiagLds<TIn> S;
     // Persistent: the workgroup takes items (chunk, head) blockIdx.x,
     // blockIdx.x + gridDim.x, ... and loads the next item's inputs into
     // registers while it works on the current one (one workgroup fills a CU,
@@ -109,7 +147,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_diag_kernel(
 
     // K, Q rows, b, and alpha for (channel, eighth of 8 tokens) of one item;
     // rows past the chunk's end read as zero keys, b = 0 and alpha = 1
-    u16x8 xk, xq;
+    Row8<TIn> xk, xq;
     float bv, al[8];
     auto load_item = [&](int it) {
         const int tid = threadIdx.x;
@@ -118,11 +156,11 @@ __global__ __launch_bounds__(kPrepThreads) void prep_diag_kernel(
         const int ck = it / H, hh = it - ck * H;
         const int64_t s0 = rec[4 * ck + 1];
         const int n = rec[4 * ck + 2];
-        xk = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-        xq = xk;
+        xk.zero();
+        xq.zero();
         if (sr < n) {
-            xk = *reinterpret_cast<const u16x8*>(k + ((s0 + sr) * H + hh) * kD + sc8);
-            xq = *reinterpret_cast<const u16x8*>(q + ((s0 + sr) * H + hh) * kD + sc8);
+            xk.load(k + ((s0 + sr) * H + hh) * kD + sc8);
+            xq.load(q + ((s0 + sr) * H + hh) * kD + sc8);
         }
         bv = tid < n ? b[(s0 + tid) * H + hh] : 0.f;
 #pragma unroll
@@ -147,8 +185,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_diag_kernel(
     // ---- stage K, Q (rows past the chunk's end are zero), b; zero T and A;
     //      G = running sum of log2(alpha) per channel, each eighth of the
     //      chunk first on its own, then offset by the eighths before it
-    *reinterpret_cast<u16x8*>(&S.K[sr][sc8]) = xk;
-    *reinterpret_cast<u16x8*>(&S.Q[sr][sc8]) = xq;
+    xk.store(&S.K[sr][sc8]);
+    xq.store(&S.Q[sr][sc8]);
     if (tid < kC) S.bb[tid] = bv;
     for (int e = tid; e < kC * kFS; e += kPrepThreads) {
         S.T[e] = 0.f;
@@ -218,10 +256,10 @@ __global__ __launch_bounds__(kPrepThreads) void prep_diag_kernel(
                 float sl = 0.f, sa = 0.f;
                 if (ri >= sj)
                     for (int key = 0; key < kD; ++key) {
-                        const float kj = bf16_bits_to_f32(S.K[sj][key]) *
+                        const float kj = in_f32(S.K[sj][key]) *
                                          exp2_hw(S.G[ri][key] - S.G[sj][key]);
-                        sl = fmaf(bf16_bits_to_f32(S.K[ri][key]), kj, sl);
-                        sa = fmaf(bf16_bits_to_f32(S.Q[ri][key]), kj, sa);
+                        sl = fmaf(in_f32(S.K[ri][key]), kj, sl);
+                        sa = fmaf(in_f32(S.Q[ri][key]), kj, sa);
                     }
                 accL[i] = sl;
                 accA[i] = sa;
@@ -251,8 +289,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_diag_kernel(
                 for (int i = 0; i < 4; ++i) {
                     const int key = 32 * m + 16 * hh + 4 * gp + i;
                     const float e = exp2_hw(S.G[row][key]);
-                    vk[4 * hh + i] = bf16_bits_to_f32(S.K[row][key]) * e;
-                    vq[4 * hh + i] = bf16_bits_to_f32(S.Q[row][key]) * e;
+                    vk[4 * hh + i] = in_f32(S.K[row][key]) * e;
+                    vq[4 * hh + i] = in_f32(S.Q[row][key]) * e;
                 }
             bf16x8 hk, lk, hq, lq;
             split8(vk, hk, lk);
@@ -274,7 +312,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_diag_kernel(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tok = 32 * m + 16 * hh + 4 * gp + i;
-                    v[4 * hh + i] = bf16_bits_to_f32(S.K[tok][key]) * exp2_hw(gc - S.G[tok][key]);
+                    v[4 * hh + i] = in_f32(S.K[tok][key]) * exp2_hw(gc - S.G[tok][key]);
                 }
             bf16x8 hi, lo;
             split8(v, hi, lo);
@@ -303,12 +341,13 @@ __global__ __launch_bounds__(kPrepThreads) void prep_diag_kernel(
 constexpr int kDWaves = 8;
 
 // One wave's operands of one chunk.
+template <typename TIn>
 struct DiagOps {
     bf16x8 xa[4][2];   // (K e^G) (waves 0-3) or (Q e^G) (waves 4-7), token tile tt: [key block][hi/lo]
     bf16x8 fa[2][2];   // T_b (waves 0-3) or A (waves 4-7), token tile tt: [token block][hi/lo]
     bf16x8 kh[2][2];   // (K e^{G_C - G})^T, key tile w: [token block][hi/lo]
     f32x4 gc;          // e^{G_C} of keys 16w + 4g .. +3
-    uint16_t vraw[4];  // V at tokens 16tt + 4g + i, value 16s + c (waves 0-3), bf16 bits:
+    TIn vraw[4];       // V at tokens 16tt + 4g + i, value 16s + c (waves 0-3), as loaded:
                        // widened where used, so the prefetch is never waited on here
     int t0, len;
 };
@@ -316,18 +355,21 @@ struct DiagOps {
 // The chunks of one sequence are consecutive and full but for the last, so
 // a chunk's first token and length follow from the first chunk's start and
 // the sequence's end without a dependent load in the chunk loop.
+template <typename TIn>
 struct DiagCtx {
-    const uint16_t* v;
+    const TIn* v;
     const unsigned char* factors;
     int H, h, s, w, l;
     int c_begin, t_begin, t_end;
 };
 
-__device__ __forceinline__ const unsigned char* diag_factors(const DiagCtx& x, int chunk) {
+template <typename TIn>
+__device__ __forceinline__ const unsigned char* diag_factors(const DiagCtx<TIn>& x, int chunk) {
     return x.factors + (size_t(chunk) * x.H + x.h) * kDiagChunkHeadBytes;
 }
 
-__device__ __forceinline__ void load_xa(DiagOps& o, const DiagCtx& x, int chunk) {
+template <typename TIn>
+__device__ __forceinline__ void load_xa(DiagOps<TIn>& o, const DiagCtx<TIn>& x, int chunk) {
     const bf16x8* P =
         reinterpret_cast<const bf16x8*>(diag_factors(x, chunk) + (x.w < 4 ? kDOffKt : kDOffQt));
     const int tt = x.w & 3;
@@ -339,7 +381,8 @@ __device__ __forceinline__ void load_xa(DiagOps& o, const DiagCtx& x, int chunk)
     }
 }
 
-__device__ __forceinline__ void load_fa(DiagOps& o, const DiagCtx& x, int chunk) {
+template <typename TIn>
+__device__ __forceinline__ void load_fa(DiagOps<TIn>& o, const DiagCtx<TIn>& x, int chunk) {
     const bf16x8* P =
         reinterpret_cast<const bf16x8*>(diag_factors(x, chunk) + (x.w < 4 ? kDOffTb : kDOffA));
     const int tt = x.w & 3;
@@ -351,7 +394,8 @@ __device__ __forceinline__ void load_fa(DiagOps& o, const DiagCtx& x, int chunk)
     }
 }
 
-__device__ __forceinline__ void load_kh(DiagOps& o, const DiagCtx& x, int chunk) {
+template <typename TIn>
+__device__ __forceinline__ void load_kh(DiagOps<TIn>& o, const DiagCtx<TIn>& x, int chunk) {
     const unsigned char* F = diag_factors(x, chunk);
     const bf16x8* P = reinterpret_cast<const bf16x8*>(F + kDOffKh);
 #pragma unroll
@@ -364,7 +408,8 @@ __device__ __forceinline__ void load_kh(DiagOps& o, const DiagCtx& x, int chunk)
                                            16 * x.w + 4 * (x.l >> 4));
 }
 
-__device__ __forceinline__ void load_rec_v(DiagOps& o, const DiagCtx& x, int chunk) {
+template <typename TIn>
+__device__ __forceinline__ void load_rec_v(DiagOps<TIn>& o, const DiagCtx<TIn>& x, int chunk) {
     o.t0 = x.t_begin + kC * (chunk - x.c_begin);
     o.len = min(kC, x.t_end - o.t0);
     // every wave loads (output waves do not use it): the same loads in the same
@@ -380,7 +425,8 @@ __device__ __forceinline__ void load_rec_v(DiagOps& o, const DiagCtx& x, int chu
 
 // the order of the in-loop refills, so the pending loads at the loop head are
 // the same on entry and on the back edge
-__device__ __forceinline__ void load_all(DiagOps& o, const DiagCtx& x, int chunk) {
+template <typename TIn>
+__device__ __forceinline__ void load_all(DiagOps<TIn>& o, const DiagCtx<TIn>& x, int chunk) {
     load_xa(o, x, chunk);
     load_fa(o, x, chunk);
     load_kh(o, x, chunk);
@@ -411,9 +457,10 @@ __device__ __forceinline__ f32x4 prod3(const bf16x8 (*a)[2], u32x4 (*B)[2][64], 
 // as each part is consumed.  Without outputs (kOut false) the output waves
 // only carry their state tiles; zero_v takes every value as zero (the walk
 // then applies the chunks' transition alone).
-template <bool kOut>
-__device__ __forceinline__ void diag_step(DiagOps& cur, f32x4& acc, const DiagCtx& x, int next,
-                                          DiagLds& S, float* __restrict__ o, bool zero_v) {
+template <bool kOut, typename TIn>
+__device__ __forceinline__ void diag_step(DiagOps<TIn>& cur, f32x4& acc, const DiagCtx<TIn>& x,
+                                          int next, DiagLds& S, float* __restrict__ o,
+                                          bool zero_v) {
     const int w = x.w, l = x.l, g = l >> 4, c = l & 15, tt = w & 3;
     const bool state = w < 4;
     // P1
@@ -424,9 +471,8 @@ __device__ __forceinline__ void diag_step(DiagOps& cur, f32x4& acc, const DiagCt
     if (kOut || state) yz = prod3<4>(cur.xa, S.Sx, l);
     if (state) {
         const f32x4 vv = zero_v ? zero4()
-                                : f32x4{bf16_bits_to_f32(cur.vraw[0]), bf16_bits_to_f32(cur.vraw[1]),
-                                        bf16_bits_to_f32(cur.vraw[2]),
-                                        bf16_bits_to_f32(cur.vraw[3])};
+                                : f32x4{in_f32(cur.vraw[0]), in_f32(cur.vraw[1]),
+                                        in_f32(cur.vraw[2]), in_f32(cur.vraw[3])};
         publish4(S.Ex, tt, l, vv - yz);
     }
     load_xa(cur, x, next);
@@ -453,9 +499,9 @@ __device__ __forceinline__ void diag_step(DiagOps& cur, f32x4& acc, const DiagCt
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <bool kOut>
+template <bool kOut, typename TIn>
 __global__ __launch_bounds__(kDWaves * 64) void walk_diag_kernel(
-    const uint16_t* __restrict__ v, int N, int H, const int32_t* __restrict__ rec,
+    const TIn* __restrict__ v, int N, int H, const int32_t* __restrict__ rec,
     const int32_t* __restrict__ seq_off, const int32_t* __restrict__ num_chunks,
     const unsigned char* __restrict__ factors, float* __restrict__ o, WalkJob j0, WalkJob j1,
     int seg_chunks) {
@@ -491,7 +537,7 @@ __global__ __launch_bounds__(kDWaves * 64) void walk_diag_kernel(
         t_begin = rec[4 * c_begin + 1];
         t_end = rec[4 * (c_end - 1) + 1] + rec[4 * (c_end - 1) + 2];
     }
-    const DiagCtx x{v, factors, H, h, s, w, l, c_begin, t_begin, t_end};
+    const DiagCtx<TIn> x{v, factors, H, h, s, w, l, c_begin, t_begin, t_end};
 
     // state: lane holds S^T[key 16w + 4g + i][value 16s + c] = S[value][key .. key+3]
     const size_t srow = ((size_t(n) * H + h) * kD + 16 * s + c) * kD + 16 * w + 4 * g;
@@ -508,7 +554,7 @@ __global__ __launch_bounds__(kDWaves * 64) void walk_diag_kernel(
         // between the two steps, so the loads pending at the loop head are
         // the same on every path and the compiler's waits stay exact), and
         // an odd last chunk after the loop
-        DiagOps A, B;
+        DiagOps<TIn> A, B;
         const int last = c_end - 1;
         load_all(A, x, c_begin);
         load_all(B, x, c_begin + 1 < c_end ? c_begin + 1 : last);
@@ -524,7 +570,7 @@ __global__ __launch_bounds__(kDWaves * 64) void walk_diag_kernel(
 
 }  // namespace
 
-hipError_t launch_prep_diag(const uint16_t* q, const uint16_t* k, const float* alpha,
+hipError_t launch_prep_diag(const void* q, const void* k, rda_dtype dt, const float* alpha,
                             const float* b, int32_t heads, int32_t max_chunks, const int32_t* rec,
                             const int32_t* num_chunks, unsigned char* factors,
                             hipStream_t stream) {
@@ -532,12 +578,28 @@ hipError_t launch_prep_diag(const uint16_t* q, const uint16_t* k, const float* a
     const int64_t items = int64_t(max_chunks) * heads;
     const unsigned pgrid = unsigned(items < kPrepDiagGrid ? items : kPrepDiagGrid);
     if (pgrid == 0) return hipSuccess;
-    hipLaunchKernelGGL(prep_diag_kernel, dim3(pgrid), dim3(kPrepThreads), 0, stream, q, k, alpha,
-                       b, heads, rec, num_chunks, factors);
+    if (dt == RDA_BF16)
+        hipLaunchKernelGGL(prep_diag_kernel<uint16_t>, dim3(pgrid), dim3(kPrepThreads), 0, stream,
+                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), alpha,
+                           b, heads, rec, num_chunks, factors);
+    else
+        hipLaunchKernelGGL(prep_diag_kernel<float>, dim3(pgrid), dim3(kPrepThreads), 0, stream,
+                           static_cast<const float*>(q), static_cast<const float*>(k), alpha, b,
+                           heads, rec, num_chunks, factors);
     return hipGetLastError();
 }
 
-hipError_t launch_walk_diag(const uint16_t* v, int32_t num_seqs, int32_t heads,
+template <bool kOut, typename TIn>
+static void launch_walk_diag_t(const void* v, int32_t num_seqs, int32_t heads, const int32_t* rec,
+                               const int32_t* seq_off, const int32_t* num_chunks,
+                               const unsigned char* factors, float* o, WalkJob j0, WalkJob j1,
+                               int32_t seg_chunks, unsigned wgrid, hipStream_t stream) {
+    hipLaunchKernelGGL((walk_diag_kernel<kOut, TIn>), dim3(wgrid), dim3(kDWaves * 64), 0, stream,
+                       static_cast<const TIn*>(v), num_seqs, heads, rec, seq_off, num_chunks,
+                       factors, o, j0, j1, seg_chunks);
+}
+
+hipError_t launch_walk_diag(const void* v, rda_dtype dt, int32_t num_seqs, int32_t heads,
                             const int32_t* rec, const int32_t* seq_off,
                             const int32_t* num_chunks, const unsigned char* factors, float* o,
                             const WalkJob* jobs, int32_t num_jobs, int32_t seg_chunks,
@@ -546,29 +608,36 @@ hipError_t launch_walk_diag(const uint16_t* v, int32_t num_seqs, int32_t heads,
     const unsigned wgrid = unsigned(num_jobs * 64 * ((pairs + 7) / 8));
     const WalkJob none{nullptr, nullptr, 0, 0};
     const WalkJob j1 = num_jobs > 1 ? jobs[1] : none;
-    if (outputs)
-        hipLaunchKernelGGL(walk_diag_kernel<true>, dim3(wgrid), dim3(kDWaves * 64), 0, stream, v,
-                           num_seqs, heads, rec, seq_off, num_chunks, factors, o, jobs[0], j1,
-                           seg_chunks);
-    else
-        hipLaunchKernelGGL(walk_diag_kernel<false>, dim3(wgrid), dim3(kDWaves * 64), 0, stream,
-                           v, num_seqs, heads, rec, seq_off, num_chunks, factors, o, jobs[0], j1,
-                           seg_chunks);
+    if (dt == RDA_BF16) {
+        if (outputs)
+            launch_walk_diag_t<true, uint16_t>(v, num_seqs, heads, rec, seq_off, num_chunks,
+                                               factors, o, jobs[0], j1, seg_chunks, wgrid, stream);
+        else
+            launch_walk_diag_t<false, uint16_t>(v, num_seqs, heads, rec, seq_off, num_chunks,
+                                                factors, o, jobs[0], j1, seg_chunks, wgrid, stream);
+    } else {
+        if (outputs)
+            launch_walk_diag_t<true, float>(v, num_seqs, heads, rec, seq_off, num_chunks, factors,
+                                            o, jobs[0], j1, seg_chunks, wgrid, stream);
+        else
+            launch_walk_diag_t<false, float>(v, num_seqs, heads, rec, seq_off, num_chunks,
+                                             factors, o, jobs[0], j1, seg_chunks, wgrid, stream);
+    }
     return hipGetLastError();
 }
 
-hipError_t launch_prefill_diag(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+hipError_t launch_prefill_diag(const void* q, const void* k, const void* v, rda_dtype dt,
                                const float* alpha, const float* b, int32_t num_seqs,
                                int32_t heads, int32_t max_chunks, const int32_t* rec,
                                const int32_t* seq_off, const int32_t* num_chunks,
                                unsigned char* factors, const float* S0, float* o,
                                float* S_final, hipStream_t stream) {
     const hipError_t err =
-        launch_prep_diag(q, k, alpha, b, heads, max_chunks, rec, num_chunks, factors, stream);
+        launch_prep_diag(q, k, dt, alpha, b, heads, max_chunks, rec, num_chunks, factors, stream);
     if (err != hipSuccess) return err;
     const WalkJob job{S0, S_final, 0, 0};
-    return launch_walk_diag(v, num_seqs, heads, rec, seq_off, num_chunks, factors, o, &job, 1, 0,
-                            true, stream);
+    return launch_walk_diag(v, dt, num_seqs, heads, rec, seq_off, num_chunks, factors, o, &job, 1,
+                            0, true, stream);
 }
 
 }  // namespace rda

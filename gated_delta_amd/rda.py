@@ -576,18 +576,17 @@ def rda_prefill_diag(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: t
                      workspace: Optional[torch.Tensor] = None, stream=None):
     """Prefill with a per-key-channel decay (C entry point ``rda_prefill_diag``).
 
-    q, k, v [T, H, 128] bf16; alpha [T, H, 128] fp32 in (0, 1]; b [T, H]
-    fp32; the rest as in rda_prefill.  Returns (o, S_final).
+    q, k, v [T, H, 128] (bf16 or fp32, same dtype); alpha [T, H, 128] fp32
+    in (0, 1]; b [T, H] fp32; the rest as in rda_prefill.  Returns (o, S_final).
     """
     lib_ = _load()
     dev = q.device
     T, H, dk = q.shape
     dv = v.shape[-1]
-    if q.dtype != torch.bfloat16:
-        raise TypeError("rda_prefill_diag takes bfloat16 q, k, v")
+    dt = _qkv_dtype(q)
     for name, t in (("q", q), ("k", k)):
-        _need(t, name, torch.bfloat16, (T, H, dk), dev)
-    _need(v, "v", torch.bfloat16, (T, H, dv), dev)
+        _need(t, name, q.dtype, (T, H, dk), dev)
+    _need(v, "v", q.dtype, (T, H, dv), dev)
     _need(alpha, "alpha", torch.float32, (T, H, dk), dev)
     _need(b, "b", torch.float32, (T, H), dev)
     cu_dev, N = None, 1
@@ -606,7 +605,7 @@ def rda_prefill_diag(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: t
     need = rda_prefill_diag_workspace_bytes(N, T, H, dk, dv)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    st = lib_.rda_prefill_diag(_ptr(q), _ptr(k), _ptr(v), RDA_BF16, _ptr(alpha), _ptr(b),
+    st = lib_.rda_prefill_diag(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(alpha), _ptr(b),
                                _ptr(cu_dev), N, T, H, dk, dv, _ptr(S0), _ptr(o), _ptr(S_final),
                                _ptr(workspace), workspace.numel(), _stream_handle(stream))
     if st != 0:

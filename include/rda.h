@@ -260,9 +260,10 @@ rda_status rda_decode_tokens(const void* q, const void* k, const void* v, rda_dt
  *     o_t = S_t q_t
  *
  * Arguments as in rda_prefill / rda_decode_step, with alpha [total_tokens, H,
- * dk] (prefill) or [batch, H, dk] (decode) fp32 in place of a; the prefill
- * takes bf16 q, k, v only (RDA_ERR_UNSUPPORTED for fp32) and its own
- * workspace size.  Any alpha in (0, 1] is safe: the chunked prefill never
+ * dk] (prefill) or [batch, H, dk] (decode) fp32 in place of a, q, k, v in
+ * bf16 or fp32 (fp32 values keep their full precision through the chunked
+ * products), and the prefill's own workspace size.  Any alpha in (0, 1] is
+ * safe: the chunked prefill never
  * forms a decay factor above e^60 (it falls back to exact per-element
  * factors where a 16-token block decays by more than that).  One sequence
  * without offsets with few heads takes the segmented state pass described

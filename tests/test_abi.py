@@ -317,7 +317,6 @@ def test_prefill_diag_rejects_bad_arguments(lib):
             ws=P + 7 * GiB, wsb=1 << 30):
         return lib.rda_prefill_diag(q, k, v, dt, al, b, cu, N, T, H, dk, dv, S0, o, Sf, ws,
                                     wsb, None)
-    assert pre(dt=1) == UNSUP                    # bf16 q, k, v only
     assert pre(dt=3) == DTYPE
     assert pre(T=-1) == SHAPE
     assert pre(N=2) == SHAPE                     # several sequences need offsets

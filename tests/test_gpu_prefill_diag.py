@@ -24,7 +24,7 @@ def case(T, H, key, s0=0.02, lengths=None):
 
 def run_gpu(p, alpha, dev):
     """o and S_final inside guard bands, checked after the call."""
-    q, k, v = (dev_tokens(getattr(p, n), True, dev) for n in "qkv")
+    q, k, v = (dev_tokens(getattr(p, n), p.bf16, dev) for n in "qkv")
     go = guarded((p.total_tokens, p.num_heads, 128), torch.float32, dev)
     gs = guarded((p.num_seqs, p.num_heads, 128, 128), torch.float32, dev)
     o, S = rda.rda_prefill_diag(q, k, v, dev_f32(alpha, dev), dev_f32(p.b, dev),
@@ -45,6 +45,38 @@ def test_one_sequence(dev, T):
     ro, rS = oracle.prefill_diag(p.q, p.k, p.v, alpha, p.b, S0=p.S0)
     assert_parity("o", to_host(o), ro)
     assert_parity("S_final", to_host(S), rS)
+
+
+@pytest.mark.parametrize("T", [1, 64, 65, 300])
+def test_fp32_inputs(dev, T):
+    """fp32 q, k, v (the same ABI as rda_prefill): unrounded values, every
+    product at full precision, against the oracle on the same fp32 values."""
+    p = synth.make_prefill(T, 4, bf16=False, s0_std=0.05, key=(608, T))
+    alpha = synth.diag_alpha(T, 4, key=(608, T))
+    say(f"[prefill_diag] fp32 T={T} H=4")
+    o, S = run_gpu(p, alpha, dev)
+    ro, rS = oracle.prefill_diag(p.q, p.k, p.v, alpha, p.b, S0=p.S0)
+    assert_parity("o", to_host(o), ro)
+    assert_parity("S_final", to_host(S), rS)
+
+
+def test_fp32_segmented_and_packed(dev):
+    """fp32 inputs through the segmented state pass (one long sequence, 2
+    heads) and through packed sequences with an empty one."""
+    p = synth.make_prefill(4096, 2, bf16=False, s0_std=0.02, key=(609,))
+    alpha = np.exp(-np.random.default_rng(609).uniform(0.0, 4e-3, (4096, 2, 128))).astype(np.float32)
+    say("[prefill_diag] fp32 segmented 4096 x 2")
+    o, S = run_gpu(p, alpha, dev)
+    ro, rS = oracle.prefill_diag(p.q, p.k, p.v, alpha, p.b, S0=p.S0)
+    assert_parity("segmented o", to_host(o), ro)
+    assert_parity("segmented S_final", to_host(S), rS)
+    p = synth.make_prefill(H=3, lengths=[70, 0, 129, 1], bf16=False, s0_std=0.05, key=(610,))
+    alpha = synth.diag_alpha(p.total_tokens, 3, key=(610,))
+    say("[prefill_diag] fp32 packed")
+    o, S = run_gpu(p, alpha, dev)
+    ro, rS = oracle.prefill_diag(p.q, p.k, p.v, alpha, p.b, cu_seqlens=p.cu_seqlens, S0=p.S0)
+    assert_parity("packed o", to_host(o), ro)
+    assert_parity("packed S_final", to_host(S), rS)
 
 
 def test_equal_channels_is_the_scalar_prefill(dev):
