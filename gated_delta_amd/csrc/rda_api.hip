@@ -68,6 +68,42 @@ size_t seg_state_bytes(const SegPlan& sp, int32_t heads) {
     return size_t(sp.P) * heads * kD * kD * sizeof(float);
 }
 
+// The overlapped plan for one long sequence whose walk leaves many CUs idle
+// (8 workgroups per head, one per CU): (1) the prep of the first c1 chunks
+// on the whole chip, (2) one launch whose walk workgroups walk chunks
+// [0, c1) and save the state while prep workgroups on the idle CUs prep the
+// remaining chunks, (3) the walk of chunks [c1, nch) from the saved state.
+// c1 balances (2): a walk chunk step costs about as long as 3 prep items on
+// one CU, so the walk of c1 chunks and the prep of (nch - c1) H items on
+// `idle` CUs take the same time when c1 = nch 3H / (idle + 3H).
+constexpr int kOverlapMinChunks = 32;
+constexpr int kOverlapMinIdleCUs = 64;
+constexpr int kPrepItemsPerWalkStep = 3;
+
+struct OverlapPlan {
+    int c1 = 0;           // chunks walked in the middle launch (0: no overlap)
+    int prep_blocks = 0;  // prep workgroups beside them
+};
+
+OverlapPlan overlap_plan(int32_t num_seqs, int32_t total_tokens, int32_t heads) {
+    OverlapPlan op;
+    if (num_seqs != 1 || total_tokens <= 0 || heads <= 0) return op;
+    const int64_t nch = (int64_t(total_tokens) + kC - 1) / kC;
+    const int64_t idle = kSegCUs - int64_t(kWalkSlices) * heads;
+    if (nch < kOverlapMinChunks || idle < kOverlapMinIdleCUs) return op;
+    const int64_t r = int64_t(kPrepItemsPerWalkStep) * heads;
+    int64_t c1 = (nch * r + (idle + r) / 2) / (idle + r);
+    c1 = c1 < 8 ? 8 : c1;
+    c1 = c1 > nch - 8 ? nch - 8 : c1;
+    op.c1 = int(c1);
+    op.prep_blocks = int(idle);
+    return op;
+}
+
+size_t overlap_state_bytes(const OverlapPlan& op, int32_t heads) {
+    return op.c1 > 0 ? size_t(heads) * kD * kD * sizeof(float) : 0;
+}
+
 rda_status check_dims(int32_t heads, int32_t dk, int32_t dv) {
     if (heads <= 0 || dk <= 0 || dv <= 0) return RDA_ERR_SHAPE;
     if (dk != kD || dv != kD) return RDA_ERR_UNSUPPORTED;
@@ -94,6 +130,8 @@ struct Prefill {
     unsigned char* factors;
     SegPlan seg;          // used when the input is one bf16 sequence without offsets
     float *E, *F, *S_in;  // segmented pass: end states from zero, transitions, starts
+    OverlapPlan ovl;      // likewise, when no segmented pass runs
+    float* S_mid;         // overlapped plan: the state after chunk c1
 };
 
 rda_status check_prefill(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
@@ -143,25 +181,64 @@ rda_status check_prefill(const void* q, const void* k, const void* v, rda_dtype 
                 reinterpret_cast<int32_t*>(ws + tl.rec_off),
                 reinterpret_cast<int32_t*>(ws + tl.seq_off_off),
                 reinterpret_cast<int32_t*>(ws + tl.num_off), ws + align256(tl.bytes),
-                SegPlan{}, nullptr, nullptr, nullptr};
+                SegPlan{}, nullptr, nullptr, nullptr, OverlapPlan{}, nullptr};
     const SegPlan sp = seg_plan(num_seqs, total_tokens, num_heads);
-    if (sp.P > 0 && cu_seqlens == nullptr && qkv_dtype == RDA_BF16) {
-        unsigned char* seg = P.factors + size_t(mc) * num_heads * kChunkHeadBytes;
-        const size_t sb = seg_state_bytes(sp, num_heads);
-        P.seg = sp;
-        P.E = reinterpret_cast<float*>(seg);
-        P.F = reinterpret_cast<float*>(seg + sb);
-        P.S_in = reinterpret_cast<float*>(seg + 2 * sb);
+    const OverlapPlan op = overlap_plan(num_seqs, total_tokens, num_heads);
+    unsigned char* tail = P.factors + size_t(mc) * num_heads * kChunkHeadBytes;
+    if (cu_seqlens == nullptr && qkv_dtype == RDA_BF16) {
+        if (sp.P > 0) {
+            const size_t sb = seg_state_bytes(sp, num_heads);
+            P.seg = sp;
+            P.E = reinterpret_cast<float*>(tail);
+            P.F = reinterpret_cast<float*>(tail + sb);
+            P.S_in = reinterpret_cast<float*>(tail + 2 * sb);
+        } else if (op.c1 > 0) {
+            P.ovl = op;
+            P.S_mid = reinterpret_cast<float*>(tail);
+        }
     }
     return RDA_OK;
 }
 
+// The overlapped plan (see overlap_plan), all on `stream`.
+rda_status prefill_overlapped(const Prefill& P, hipStream_t stream) {
+    const auto* q16 = static_cast<const uint16_t*>(P.q);
+    const auto* k16 = static_cast<const uint16_t*>(P.k);
+    const auto* v16 = static_cast<const uint16_t*>(P.v);
+    const int nch = (P.T + kC - 1) / kC;
+    const int c1 = P.ovl.c1;
+    WalkPrep X{};
+    X.c_lo = 0;
+    X.c_hi = c1;
+    X.prep_blocks = P.ovl.prep_blocks;
+    X.item_lo = c1 * P.H;
+    X.item_hi = nch * P.H;
+    X.single_T = P.T;
+    X.nch = nch;
+    X.args = WalkPrepArgs{q16, k16, P.a, P.b, P.H, P.factors};
+    X.rec_out = P.rec;
+    X.seq_off_out = P.seq_off;
+    X.num_out = P.nch;
+    WalkPrep Y{};
+    Y.c_lo = c1;
+    Y.c_hi = nch;
+    const WalkJob first{P.S0, P.S_mid, 0, 0};
+    const WalkJob second{P.S_mid, P.S_final, 0, 0};
+    if (launch_prep_bf16(q16, k16, P.a, P.b, P.H, P.mc, nullptr, nullptr, P.factors, P.T, P.rec,
+                         P.seq_off, P.nch, stream, 0, c1) != hipSuccess ||
+        launch_walk_bf16(q16, k16, v16, 1, P.H, P.rec, P.seq_off, P.nch, P.factors, P.o, &first,
+                         1, 0, true, stream, &X) != hipSuccess ||
+        launch_walk_bf16(q16, k16, v16, 1, P.H, P.rec, P.seq_off, P.nch, P.factors, P.o, &second,
+                         1, 0, true, stream, &Y) != hipSuccess)
+        return RDA_ERR_HIP;
+    return RDA_OK;
+}
+
 // Table, prep and walk one after another on `stream`, each stage bracketed
-// by its event pair when `ev` is given.  (Running the prep of later chunks
-// beside the walk of earlier ones on a second stream was measured: the
-// walk's chunk steps slow down under the prep's memory traffic by about as
-// much as the overlap hides, so the stages stay in sequence.)
+// by its event pair when `ev` is given; without events, one bf16 sequence
+// whose walk leaves CUs idle takes the overlapped plan instead.
 rda_status prefill_sequential(const Prefill& P, hipStream_t stream, hipEvent_t const* ev) {
+    if (ev == nullptr && P.ovl.c1 > 0) return prefill_overlapped(P, stream);
     rda_status st;
     // one bf16 sequence without offsets: the prep kernel derives each chunk's
     // record itself and writes the table, which saves the table launch
@@ -271,9 +348,12 @@ size_t rda_prefill_workspace_bytes(int32_t num_seqs, int32_t total_tokens, int32
     const int32_t mc = rda_max_chunks(num_seqs, total_tokens);
     if (mc < 0) return 0;
     const TableLayout tl = table_layout(mc, num_seqs);
-    // one sequence: room for the segmented pass's three state arrays
+    // one sequence: room for the segmented pass's three state arrays or the
+    // overlapped plan's middle state
+    const size_t seg = 3 * seg_state_bytes(seg_plan(num_seqs, total_tokens, num_heads), num_heads);
+    const size_t mid = overlap_state_bytes(overlap_plan(num_seqs, total_tokens, num_heads), num_heads);
     return align256(tl.bytes) + size_t(mc) * size_t(num_heads) * kChunkHeadBytes +
-           3 * seg_state_bytes(seg_plan(num_seqs, total_tokens, num_heads), num_heads);
+           (seg > mid ? seg : mid);
 }
 
 rda_status rda_prefill_profiled(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,

@@ -188,13 +188,40 @@ hipError_t launch_walk(const void* q, const void* k, const void* v, rda_dtype dt
 // and the kernel writes the chunk table to rec_out / seq_off_out / num_out.
 // With single_T < 0 the table in rec / num_chunks is read and the *_out
 // pointers are unused.
+// chunk_begin / chunk_count (single_T >= 0 only): prep just those chunks of
+// the sequence (count < 0: to its end); the table entries they write carry
+// the sequence's full chunk count.
 hipError_t launch_prep_bf16(const uint16_t* q, const uint16_t* k, const float* a, const float* b,
                             int32_t heads, int32_t max_chunks, const int32_t* rec,
                             const int32_t* num_chunks, unsigned char* factors, int32_t single_T,
                             int32_t* rec_out, int32_t* seq_off_out, int32_t* num_out,
-                            hipStream_t stream);
+                            hipStream_t stream, int32_t chunk_begin = 0,
+                            int32_t chunk_count = -1);
 
 // bf16 walk (operands streamed into LDS by loader waves)
+
+// Extra work a walk launch may carry (rda_prep.h's args, so forward-declared
+// as plain pointers here): a chunk range for one sequence (c_hi > 0: walk
+// chunks [c_lo, c_hi) only), and prep workgroups after the walk's that run
+// the prep items [item_lo, item_hi) of one sequence of single_T tokens and
+// write their table entries (nch = the sequence's chunk count).
+struct WalkPrepArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const float* a;
+    const float* b;
+    int H;
+    unsigned char* factors;
+};
+struct WalkPrep {
+    int c_lo, c_hi;
+    int prep_blocks;        // prep workgroups (0: none)
+    int item_lo, item_hi;
+    int single_T, nch;
+    WalkPrepArgs args;
+    int32_t *rec_out, *seq_off_out, *num_out;
+    int walk_blocks;        // set by the launcher
+};
 
 // bf16 walk.  num_jobs (1 or 2) walks over the same chunks in one launch,
 // differing only in their WalkJob.  seg_chunks > 0: sequence n is the n-th
@@ -206,7 +233,7 @@ hipError_t launch_walk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t
                             const int32_t* seq_off, const int32_t* num_chunks,
                             const unsigned char* factors, float* o, const WalkJob* jobs,
                             int32_t num_jobs, int32_t seg_chunks, bool outputs,
-                            hipStream_t stream);
+                            hipStream_t stream, const WalkPrep* extra = nullptr);
 
 // The segment combine of the segmented state pass, per head and value row:
 // S_in[0] = S0 (zero when null); for p < P: with E_p = segment p's final

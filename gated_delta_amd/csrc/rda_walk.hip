@@ -40,12 +40,18 @@
 // the instantiation without outputs streams neither Q nor A and leaves its
 // output waves idle at the barriers.
 //
+// A launch may also walk only a range of one sequence's chunks (from a saved
+// state, to a saved state) and carry prep workgroups after the walk's, which
+// run the prep of later chunks (rda_prep.h) on the CUs the walk leaves free;
+// nothing in the launch waits on them.
+//
 // Past the end of a chunk (len < 64) the loaders duplicate the last valid
 // token row instead of zeroing: T_b has zero rows and columns there (b = 0),
 // so U and U~ vanish on those rows and no duplicate reaches S or a stored
 // output; they only need to be finite, which copies of real rows are.
 #include "rda_internal.h"
 #include "rda_lds.h"
+#include "rda_prep.h"
 
 namespace rda {
 
@@ -79,6 +85,15 @@ struct Lds {
 
 static_assert(sizeof(Stage) == 67 * 1024, "stage is whole 1 KiB DMA blocks");
 static_assert(sizeof(Lds) <= 160 * 1024, "LDS budget of one workgroup");
+
+// A launch may also carry prep workgroups (after the walk's), each running
+// four prep items at a time in four 256-thread groups: the walk's LDS or
+// four PrepLds.
+union WalkOrPrepLds {
+    Lds walk;
+    PrepLds prep[4];
+};
+static_assert(sizeof(WalkOrPrepLds) == sizeof(Lds), "prep groups fit in the walk's LDS");
 
 struct Ctx {
     const uint16_t* q;
@@ -417,13 +432,43 @@ __device__ __forceinline__ void output_step(const Ctx& x, int tt, int ch, const 
     }
 }
 
+// The prep workgroups of a launch: prep items [item_lo, item_hi) (item =
+// chunk * H + head) of one sequence of single_T tokens without offsets, four
+// consecutive items per round, writing their chunks' table entries too.
+__device__ void prep_role(const WalkPrep& X, PrepLds (&S)[4]) {
+    const int sub = wave_id() >> 2;          // which of the four groups
+    const int w = wave_id() & 3;             // wave within the group
+    const int tid = threadIdx.x & 255;
+    const int nprep = int(gridDim.x) - X.walk_blocks;
+    const int wg = int(blockIdx.x) - X.walk_blocks;
+    const int H = X.args.H;
+    for (int base = X.item_lo + 4 * wg; base < X.item_hi; base += 4 * nprep) {
+        const int item = base + sub;
+        const bool valid = item < X.item_hi;
+        const int chunk = valid ? item / H : 0;
+        const int h = valid ? item - chunk * H : 0;
+        const int t0 = kC * chunk;
+        const int len = valid ? min(kC, X.single_T - t0) : 1;
+        if (valid && h == 0)
+            prep_table_entry(chunk, t0, len, X.nch, tid, X.rec_out, X.seq_off_out, X.num_out);
+        prep_item(X.args, chunk, h, t0, len, valid, S[sub], tid, w);
+        __syncthreads();   // this round's LDS is rewritten by the next
+    }
+}
+
 template <bool kOut>
 __global__ __launch_bounds__(kThreads) void walk_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int N, int H, const int32_t* __restrict__ rec,
     const int32_t* __restrict__ seq_off, const int32_t* __restrict__ num_chunks,
     const unsigned char* __restrict__ factors, float* __restrict__ o, WalkJob j0, WalkJob j1,
-    int seg_chunks) {
+    int seg_chunks, WalkPrep X) {
+    __shared__ __attribute__((aligned(16))) WalkOrPrepLds shm;
+    if (int(blockIdx.x) >= X.walk_blocks) {
+        prep_role(X, shm.prep);
+        return;
+    }
+    Lds& lds = shm.walk;
     // Jobs split the grid in halves.  Within a job the mapping is XCD-aware:
     // the 8 value slices of one (sequence, head) share blockIdx.x % 8, hence
     // one XCD and its L2, which then holds the chunk's K, Q and factors once
@@ -438,8 +483,6 @@ __global__ __launch_bounds__(kThreads) void walk_bf16_kernel(
     if (p >= N * H) return;
     const int n = p / H, h = p - n * H;
 
-    __shared__ __attribute__((aligned(16))) Lds lds;
-
     const int w = wave_id(), l = threadIdx.x & 63, g = l >> 4, c = l & 15;
     const int nch = num_chunks[0];
     // sequence n's chunks: from the table, or the n-th run of seg_chunks
@@ -450,6 +493,10 @@ __global__ __launch_bounds__(kThreads) void walk_bf16_kernel(
     } else {
         c0 = seq_off[n];
         c_end = seq_off[n + 1] < nch ? seq_off[n + 1] : nch;
+    }
+    if (X.c_hi > 0) {   // one sequence walked over chunks [c_lo, c_hi) only
+        c0 = X.c_lo < nch ? X.c_lo : nch;
+        c_end = X.c_hi < nch ? X.c_hi : nch;
     }
     const Ctx x{q, k, v, factors, rec, H, h, s, l};
 
@@ -510,19 +557,23 @@ hipError_t launch_walk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t
                             const int32_t* seq_off, const int32_t* num_chunks,
                             const unsigned char* factors, float* o, const WalkJob* jobs,
                             int32_t num_jobs, int32_t seg_chunks, bool outputs,
-                            hipStream_t stream) {
+                            hipStream_t stream, const WalkPrep* extra) {
     const int64_t pairs = int64_t(num_seqs) * heads;
-    const unsigned grid = unsigned(num_jobs * 64 * ((pairs + 7) / 8));
+    const unsigned walk_grid = unsigned(num_jobs * 64 * ((pairs + 7) / 8));
+    WalkPrep X{};
+    if (extra) X = *extra;
+    X.walk_blocks = int(walk_grid);
+    const unsigned grid = walk_grid + unsigned(extra ? extra->prep_blocks : 0);
     const WalkJob none{nullptr, nullptr, 0, 0};
     const WalkJob j1 = num_jobs > 1 ? jobs[1] : none;
     if (outputs)
         hipLaunchKernelGGL(walk_bf16_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, q, k, v,
                            num_seqs, heads, rec, seq_off, num_chunks, factors, o, jobs[0], j1,
-                           seg_chunks);
+                           seg_chunks, X);
     else
         hipLaunchKernelGGL(walk_bf16_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, q, k,
                            v, num_seqs, heads, rec, seq_off, num_chunks, factors, o, jobs[0], j1,
-                           seg_chunks);
+                           seg_chunks, X);
     return hipGetLastError();
 }
 

@@ -143,7 +143,12 @@ size_t rda_prefill_workspace_bytes(int32_t num_seqs, int32_t total_tokens,
  * in the state-passing row of the chunked method (one long prompt's share of
  * heads on one GPU). It gives the same result up to rounding, and
  * rda_prefill_workspace_bytes(1, T, H) includes its three [P, H, dv, dk]
- * state arrays.  Passing cu_seqlens = {0, T} keeps the one-pass walk.
+ * state arrays.  With more heads (at least 32 chunks and at least 64 CUs
+ * left idle by the walk's 8 H workgroups) the same input instead runs the
+ * prep of the first chunks, then their walk beside the prep of the rest on
+ * the idle CUs, then the walk of the rest; the result is bitwise that of the
+ * one-pass walk, and the workspace includes one [H, dv, dk] state.  Passing
+ * cu_seqlens = {0, T} keeps the one-pass walk.
  */
 rda_status rda_prefill(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
                        const float* a, const float* b,
@@ -177,7 +182,7 @@ rda_status rda_prefill_profiled(const void* q, const void* k, const void* v, rda
  * allocating library routine).  Sizes whose rda_prefill_workspace_bytes
  * exceed RDA_NOALLOC_SCRATCH_BYTES return RDA_ERR_TOO_LARGE before anything
  * is enqueued (for one sequence of 16 heads that is a prompt of up to about
- * 7900 tokens).
+ * 7800 tokens).
  * The first call on a device looks up that device's copy of the array
  * (hipGetSymbolAddress) and keeps its address; a failed lookup returns
  * RDA_ERR_HIP.  Every call on one GPU uses the same array: calls that may

@@ -79,9 +79,25 @@ def test_workspace_covers_the_segmented_pass(lib):
     seg = rda.rda_prefill_workspace_bytes(1, 16384, 2)
     two = rda.rda_prefill_workspace_bytes(2, 16384, 2)
     assert seg - two >= 3 * 8 * 2 * 128 * 128 * 4 - 2 * 2 * 131584
-    assert rda.rda_prefill_workspace_bytes(1, 16384, 16) < rda.rda_prefill_workspace_bytes(2, 16384, 16)
-    # short sequences keep the one-pass walk
-    assert rda.rda_prefill_workspace_bytes(1, 2048, 2) < rda.rda_prefill_workspace_bytes(2, 2048, 2)
+    # short sequences keep the one-pass walk: no room for P >= 4 segments
+    short = rda.rda_prefill_workspace_bytes(1, 2048, 2) - rda.rda_prefill_workspace_bytes(2, 2048, 2)
+    assert short < 3 * 4 * 2 * 128 * 128 * 4
+
+
+def test_workspace_covers_the_overlapped_plan(lib):
+    """One sequence of 16 heads and at least 32 chunks gets room for one
+    [H, 128, 128] state (the state the overlapped plan hands from its middle
+    launch to its last); two sequences, or fewer chunks, get none."""
+    W = rda.rda_prefill_workspace_bytes
+    H, state = 16, 16 * 128 * 128 * 4
+    per_chunk = W(2, 16384 + 64, H) - W(2, 16384, H)   # factors of one chunk, all heads
+    assert per_chunk > 0
+    extra = W(1, 16384, H) - 256 * per_chunk            # table + middle state
+    assert state <= extra < state + 64 * 1024
+    extra_two = W(2, 16384 - 64, H) - 256 * per_chunk    # 256 chunks, no middle state
+    assert 0 < extra_two < 64 * 1024
+    short = W(1, 31 * 64, H) - 31 * per_chunk            # 31 chunks: no overlap
+    assert 0 < short < 64 * 1024
 
 
 def test_workspace_bytes(lib):

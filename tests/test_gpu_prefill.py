@@ -4,6 +4,8 @@ Every case draws seeded inputs on the host, runs the HIP path through the C
 ABI (via the ctypes binding), runs the oracle on the same bits, and checks
 o and S_final with rel-L2 <= 2e-3 and max-abs <= 2e-2 over whole tensors.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -217,6 +219,28 @@ def test_correlated_keys_bf16(dev):
     b = rng.uniform(0.0, 1.0, (T, H)).astype(np.float32)
     p = synth.PrefillInputs(q, k, v, a, b, None, None, True)
     check_against_oracle("correlated keys bf16", p, dev)
+
+
+@pytest.mark.parametrize("T,H", [(2048, 16), (4097, 8), (3000, 12), (2048, 24), (2500, 1),
+                                 (16384, 16)])
+def test_overlapped_plan_matches_one_pass(dev, T, H):
+    """One bf16 sequence without offsets whose walk leaves CUs idle runs
+    the overlapped plan: the prep of the first chunks, then their walk
+    beside the prep of the rest on the idle CUs, then the walk of the rest
+    from the state saved in between.  With cu_seqlens = {0, T} the same
+    sizes run table, prep and one walk; both give the same bits, and the
+    shorter prompts also meet the oracle."""
+    p = synth.make_prefill(T, H, bf16=True, s0_std=0.02, key=(112, T, H))
+    say(f"[prefill] overlapped plan vs one pass T={T} H={H}")
+    o1, S1 = run_gpu(p, dev)
+    one = dataclasses.replace(p, cu_seqlens=np.array([0, T], np.int32))
+    o2, S2 = run_gpu(one, dev)
+    assert np.array_equal(o1, o2), "o differs from the one-pass walk"
+    assert np.array_equal(S1, S2), "S_final differs from the one-pass walk"
+    if T <= 4097:
+        ro, rS = run_oracle(p)
+        assert_parity("overlapped o", o1, ro)
+        assert_parity("overlapped S_final", S1, rS)
 
 
 @pytest.mark.parametrize("T,H", [(513, 16), (7000, 16)])

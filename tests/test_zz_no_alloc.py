@@ -47,12 +47,21 @@ def run_both(p, dev, name):
     assert_parity(f"{name} S_final", S1, rS)
 
 
+def largest_fitting_prompt(H):
+    """The longest single prompt of H heads (a multiple of 64 tokens) whose
+    workspace fits the fixed scratch."""
+    T = 64
+    while rda.rda_prefill_workspace_bytes(1, T + 64, H) <= rda.RDA_NOALLOC_SCRATCH_BYTES:
+        T += 64
+    return T
+
+
 def test_two_calls_second_smaller(dev):
-    # first: a long single sequence near the scratch's capacity (7936 x 16 is
-    # the largest that fits); second: a smaller packed batch with ragged tails
-    big = synth.make_prefill(7936, 16, bf16=True, s0_std=0.02, key=(950,))
-    assert rda.rda_prefill_workspace_bytes(1, 7936, 16) <= rda.RDA_NOALLOC_SCRATCH_BYTES
-    run_both(big, dev, "first call, 7936 x 16")
+    # first: a long single sequence at the scratch's capacity, minus a ragged
+    # tail; second: a smaller packed batch with ragged tails
+    T = largest_fitting_prompt(16) - 17
+    big = synth.make_prefill(T, 16, bf16=True, s0_std=0.02, key=(950,))
+    run_both(big, dev, f"first call, {T} x 16")
     small = synth.make_prefill(H=4, lengths=[130, 0, 1, 64, 300], bf16=True, s0_std=0.05,
                                key=(951,))
     run_both(small, dev, "second call, 5 packed sequences x 4 heads")
