@@ -83,7 +83,7 @@ def parse():
     ap.add_argument("--mode", choices=["bench", "prefill", "decode", "decode_tokens",
                                        "output_norm_gate", "prologue", "prefill_diag",
                                        "segments", "copy", "prefill_config",
-                                       "decode_prologue"],
+                                       "decode_prologue", "prefill_norm_gate"],
                     default="bench",
                     help="prefill/decode: run only that part (for profiling); decode_tokens / "
                          "output_norm_gate / prologue / prefill_diag / segments: only the "
@@ -93,7 +93,9 @@ def parse():
                          "calls after a cache flush each; copy: a plain device copy of known "
                          "size (counter calibration); prefill_config: --steps calls of the "
                          "prefill workload --config (1 = one fp32 head of 64 tokens, 2 = "
-                         "2048 x 16, 4 = 8 packed sequences of 32768 x 16 in all)")
+                         "2048 x 16, 4 = 8 packed sequences of 32768 x 16 in all); "
+                         "prefill_norm_gate: the long prompt's prefill alone, followed by "
+                         "the output norm and gate, and with both fused")
     ap.add_argument("--config", type=int, choices=[1, 2, 4], default=2)
     ap.add_argument("--no-extras", action="store_true",
                     help="only the timed steps and the per-stage calls (the kernel trace "
@@ -206,11 +208,14 @@ def main():
         return
 
     if args.mode in ("decode_tokens", "output_norm_gate", "prologue", "prefill_diag",
-                     "segments", "decode_prologue"):
+                     "segments", "decode_prologue", "prefill_norm_gate"):
         timed = make_timer(torch, np, stream)
         flush_buf = torch.ones((128 << 20,), dtype=torch.float32, device=dev)
         flush = lambda: flush_buf.sum()
-        if args.mode == "decode_prologue":
+        if args.mode == "prefill_norm_gate":
+            res = fused_norm_gate_measurement(args, torch, np, rda, synth, dev, timed, flush,
+                                              reps=args.steps)
+        elif args.mode == "decode_prologue":
             res = decode_prologue_measurement(args, {}, torch, np, rda, synth, dev, timed, flush,
                                               reps=args.steps)
         elif args.mode == "decode_tokens":
@@ -603,6 +608,8 @@ def extra_measurements(args, out, torch, np, rda, synth, dev, stream, q, k, v, a
                                             T, H)
     out["output_norm_gate"] = epilogue_measurements(args, out, torch, np, rda, synth, dev, timed,
                                                     flush, T, H)
+    out["prefill_norm_gate"] = fused_norm_gate_measurement(args, torch, np, rda, synth, dev,
+                                                           timed, flush)
     out["decode_tokens"] = decode_tokens_measurements(args, out, torch, np, rda, synth, dev,
                                                       stream, timed, flush)
     del scratch, flush_buf
@@ -782,6 +789,42 @@ def epilogue_measurements(args, out, torch, np, rda, synth, dev, timed, flush, T
                                  "max_rel": float(np.max(np.abs(got - ref) /
                                                          np.maximum(np.abs(ref), 1e-30)))}
     return res
+
+
+def fused_norm_gate_measurement(args, torch, np, rda, synth, dev, timed, flush, reps=10):
+    """The long prompt (16384 x 16, bf16 q/k/v, S0 ~ N(0, 0.02)) three ways,
+    each timed after a cache flush: rda_prefill alone (fp32 o), the same
+    followed by rda_output_norm_gate (bf16 out, sigmoid gate), and
+    rda_prefill_norm_gate (the fused form: no fp32 o)."""
+    p = synth.config3()
+    T, H = p.total_tokens, p.num_heads
+    q, k, v = (torch.from_numpy(getattr(p, n)).to(torch.bfloat16).to(dev) for n in "qkv")
+    a, b, S0 = (torch.from_numpy(getattr(p, n)).to(dev) for n in ("a", "b", "S0"))
+    x = synth.epilogue_inputs(T * H, key=(12,))
+    g = torch.from_numpy(x.g.reshape(T, H, D)).to(torch.bfloat16).to(dev)
+    w = torch.from_numpy(x.weight).to(dev)
+    o = torch.empty((T, H, D), dtype=torch.float32, device=dev)
+    Sf = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
+    y = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(rda.rda_prefill_norm_gate_workspace_bytes(1, T, H), dtype=torch.uint8,
+                     device=dev)
+    pre = lambda: rda.rda_prefill(q, k, v, a, b, S0=S0, o=o, S_final=Sf, workspace=ws)
+    two = lambda: (pre(), rda.rda_output_norm_gate(o, g, weight=w, out=y))
+    fused = lambda: rda.rda_prefill_norm_gate(q, k, v, a, b, g, S0=S0, weight=w, out=y,
+                                              S_final=Sf, workspace=ws)
+    for fn in (pre, two, fused):   # warm
+        fn()
+    t_pre, t_two, t_fused = (timed(fn, reps, flush) for fn in (pre, two, fused))
+    elems = T * H * D
+    return {"T": T, "H": H, "prefill_only_ms": t_pre * 1e3,
+            "prefill_then_norm_gate_ms": t_two * 1e3, "fused_ms": t_fused * 1e3,
+            "fused_over_prefill_only": t_fused / t_pre,
+            "fused_tokens_per_s": T / t_fused,
+            # output-side HBM bytes: fp32 o written and read back plus the gate
+            # and the bf16 out, against the slice form (2.25 B per element
+            # written and read) plus the gate and the bf16 out
+            "output_bytes_two_calls": elems * (4 + 4 + 2 + 2),
+            "output_bytes_fused": elems * (2.25 + 2.25 + 2 + 2)}
 
 
 def segment_measurements(args, torch, np, rda, synth, dev, stream, timed, flush, reps=10,

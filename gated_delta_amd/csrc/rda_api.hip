@@ -104,6 +104,23 @@ size_t overlap_state_bytes(const OverlapPlan& op, int32_t heads) {
     return op.c1 > 0 ? size_t(heads) * kD * kD * sizeof(float) : 0;
 }
 
+// The 16-bit output form of the fused output norm: [T, H, 128] 16-bit values.
+size_t slice_form_bytes(int32_t total_tokens, int32_t heads) {
+    return align256(size_t(total_tokens > 0 ? total_tokens : 0) * size_t(heads > 0 ? heads : 0) *
+                    kD * sizeof(uint16_t));
+}
+
+// Checks of the output norm's own arguments that need no sizes.
+rda_status check_norm_args(rda_dtype& g_dtype, float eps, int32_t act, rda_dtype out_dtype) {
+    if (out_dtype != RDA_BF16 && out_dtype != RDA_FP32) return RDA_ERR_DTYPE;
+    if (act != RDA_GATE_SIGMOID && act != RDA_GATE_SILU && act != RDA_GATE_NONE)
+        return RDA_ERR_VALUE;
+    if (act == RDA_GATE_NONE) g_dtype = RDA_BF16;   // g is not read
+    if (g_dtype != RDA_BF16 && g_dtype != RDA_FP32) return RDA_ERR_DTYPE;
+    if (!(eps >= 0.f) || eps == INFINITY) return RDA_ERR_VALUE;
+    return RDA_OK;
+}
+
 rda_status check_dims(int32_t heads, int32_t dk, int32_t dv) {
     if (heads <= 0 || dk <= 0 || dv <= 0) return RDA_ERR_SHAPE;
     if (dk != kD || dv != kD) return RDA_ERR_UNSUPPORTED;
@@ -132,13 +149,15 @@ struct Prefill {
     float *E, *F, *S_in;  // segmented pass: end states from zero, transitions, starts
     OverlapPlan ovl;      // likewise, when no segmented pass runs
     float* S_mid;         // overlapped plan: the state after chunk c1
+    OutSink out;          // where the walk's outputs go (o, or the slice form)
 };
 
 rda_status check_prefill(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
                          const float* a, const float* b, const int32_t* cu_seqlens,
                          int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t dk,
                          int32_t dv, const float* S0, float* o, float* S_final, void* workspace,
-                         size_t workspace_bytes, Prefill& P) {
+                         size_t workspace_bytes, Prefill& P, size_t extra_ws = 0,
+                         bool fused = false) {
     if (qkv_dtype != RDA_BF16 && qkv_dtype != RDA_FP32) return RDA_ERR_DTYPE;
     if (total_tokens < 0 || num_seqs < 1) return RDA_ERR_SHAPE;
     if (!cu_seqlens && num_seqs != 1) return RDA_ERR_SHAPE;
@@ -148,9 +167,13 @@ rda_status check_prefill(const void* q, const void* k, const void* v, rda_dtype 
     if (mc < 0) return RDA_ERR_SHAPE;
     if (int64_t(mc) * num_heads > INT32_MAX || int64_t(num_seqs) * num_heads * kWalkSlices > INT32_MAX)
         return RDA_ERR_SHAPE;
-    if (total_tokens > 0 && (!q || !k || !v || !a || !b || !o)) return RDA_ERR_NULL;
+    // fused: the walk writes the slice form of the fused output norm into the
+    // workspace's last extra_ws bytes instead of o (then null)
+    if (total_tokens > 0 && (!q || !k || !v || !a || !b || (!o && !fused)))
+        return RDA_ERR_NULL;
     if (!workspace) return RDA_ERR_WORKSPACE;
-    const size_t need = rda_prefill_workspace_bytes(num_seqs, total_tokens, num_heads, dk, dv);
+    const size_t need =
+        rda_prefill_workspace_bytes(num_seqs, total_tokens, num_heads, dk, dv) + extra_ws;
     if (workspace_bytes < need) return RDA_ERR_WORKSPACE;
     for (const void* p : {q, k, v, static_cast<const void*>(a), static_cast<const void*>(b),
                           static_cast<const void*>(S0), static_cast<const void*>(o),
@@ -181,7 +204,8 @@ rda_status check_prefill(const void* q, const void* k, const void* v, rda_dtype 
                 reinterpret_cast<int32_t*>(ws + tl.rec_off),
                 reinterpret_cast<int32_t*>(ws + tl.seq_off_off),
                 reinterpret_cast<int32_t*>(ws + tl.num_off), ws + align256(tl.bytes),
-                SegPlan{}, nullptr, nullptr, nullptr, OverlapPlan{}, nullptr};
+                SegPlan{}, nullptr, nullptr, nullptr, OverlapPlan{}, nullptr,
+                OutSink{o, nullptr}};
     const SegPlan sp = seg_plan(num_seqs, total_tokens, num_heads);
     const OverlapPlan op = overlap_plan(num_seqs, total_tokens, num_heads);
     unsigned char* tail = P.factors + size_t(mc) * num_heads * kChunkHeadBytes;
@@ -226,9 +250,9 @@ rda_status prefill_overlapped(const Prefill& P, hipStream_t stream) {
     const WalkJob second{P.S_mid, P.S_final, 0, 0};
     if (launch_prep_bf16(q16, k16, P.a, P.b, P.H, P.mc, nullptr, nullptr, P.factors, P.T, P.rec,
                          P.seq_off, P.nch, stream, 0, c1) != hipSuccess ||
-        launch_walk_bf16(q16, k16, v16, 1, P.H, P.rec, P.seq_off, P.nch, P.factors, P.o, &first,
+        launch_walk_bf16(q16, k16, v16, 1, P.H, P.rec, P.seq_off, P.nch, P.factors, P.out, &first,
                          1, 0, true, stream, &X) != hipSuccess ||
-        launch_walk_bf16(q16, k16, v16, 1, P.H, P.rec, P.seq_off, P.nch, P.factors, P.o, &second,
+        launch_walk_bf16(q16, k16, v16, 1, P.H, P.rec, P.seq_off, P.nch, P.factors, P.out, &second,
                          1, 0, true, stream, &Y) != hipSuccess)
         return RDA_ERR_HIP;
     return RDA_OK;
@@ -269,14 +293,14 @@ rda_status prefill_sequential(const Prefill& P, hipStream_t stream, hipEvent_t c
         const WalkJob first[2] = {{nullptr, P.E, 0, 0}, {nullptr, P.F, 1, 1}};
         const WalkJob last{P.S_in, nullptr, 0, 0};
         if (launch_walk_bf16(q16, k16, v16, P.seg.P, P.H, P.rec, P.seq_off, P.nch, P.factors,
-                             nullptr, first, 2, P.seg.cps, false, stream) != hipSuccess ||
+                             OutSink{}, first, 2, P.seg.cps, false, stream) != hipSuccess ||
             launch_segment_combine(P.S0, P.E, P.F, P.S_in, P.S_final, P.seg.P, P.H, stream) !=
                 hipSuccess ||
             launch_walk_bf16(q16, k16, v16, P.seg.P, P.H, P.rec, P.seq_off, P.nch, P.factors,
-                             P.o, &last, 1, P.seg.cps, true, stream) != hipSuccess)
+                             P.out, &last, 1, P.seg.cps, true, stream) != hipSuccess)
             return RDA_ERR_HIP;
     } else if (launch_walk(P.q, P.k, P.v, P.dt, P.N, P.H, P.rec, P.seq_off, P.nch, P.factors,
-                           P.S0, P.o, P.S_final, stream) != hipSuccess) {
+                           P.S0, P.out, P.S_final, stream) != hipSuccess) {
         return RDA_ERR_HIP;
     }
     if ((st = record(ev, 2 * RDA_STAGE_WALK + 1, stream)) != RDA_OK) return st;
@@ -739,15 +763,67 @@ rda_status rda_decode_step_prologue(const void* x_q, const void* x_k, const void
     return RDA_OK;
 }
 
+size_t rda_prefill_norm_gate_workspace_bytes(int32_t num_seqs, int32_t total_tokens,
+                                             int32_t num_heads, int32_t dk, int32_t dv) {
+    const size_t base = rda_prefill_workspace_bytes(num_seqs, total_tokens, num_heads, dk, dv);
+    if (base == 0) return 0;
+    return align256(base) + slice_form_bytes(total_tokens, num_heads);
+}
+
+rda_status rda_prefill_norm_gate(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
+                                 const float* a, const float* b, const int32_t* cu_seqlens,
+                                 int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                                 int32_t dk, int32_t dv, const float* S0, const void* g,
+                                 rda_dtype g_dtype, const float* weight, float eps, int32_t act,
+                                 void* out, rda_dtype out_dtype, float* S_final, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+    rda_status st = check_norm_args(g_dtype, eps, act, out_dtype);
+    if (st != RDA_OK) return st;
+    const size_t base = rda_prefill_workspace_bytes(num_seqs, total_tokens, num_heads, dk, dv);
+    const size_t extra = align256(base) - base + slice_form_bytes(total_tokens, num_heads);
+    Prefill P;
+    st = check_prefill(q, k, v, qkv_dtype, a, b, cu_seqlens, num_seqs, total_tokens, num_heads,
+                       dk, dv, S0, nullptr, S_final, workspace, workspace_bytes, P, extra,
+                       true);
+    if (st != RDA_OK) return st;
+    const int64_t rows = int64_t(total_tokens) * num_heads;
+    if (norm_gate_blocks(rows) > INT32_MAX) return RDA_ERR_SHAPE;
+    if (act == RDA_GATE_NONE) g = nullptr;
+    if (rows > 0) {
+        if (!out || (act != RDA_GATE_NONE && !g)) return RDA_ERR_NULL;
+        for (const void* p : {g, static_cast<const void*>(weight), static_cast<const void*>(out)})
+            if (p && !aligned16(p)) return RDA_ERR_ALIGN;
+        const size_t n = size_t(rows) * kD;
+        const size_t esz = qkv_dtype == RDA_BF16 ? 2 : 4;
+        const size_t sbytes = size_t(num_seqs) * num_heads * kD * kD * sizeof(float);
+        const Range rout = rng(out, n * (out_dtype == RDA_BF16 ? 2 : 4));
+        const Range rg = rng(g, n * (g_dtype == RDA_BF16 ? 2 : 4));
+        const Range rw = rng(weight, weight ? kD * 4 : 0);
+        const Range rsf = rng(S_final, S_final ? sbytes : 0);
+        const Range rws = rng(workspace, align256(base) + slice_form_bytes(total_tokens, num_heads));
+        for (Range in : {rng(q, n * esz), rng(k, n * esz), rng(v, n * esz),
+                         rng(a, size_t(rows) * 4), rng(b, size_t(rows) * 4),
+                         rng(S0, S0 ? sbytes : 0),
+                         rng(cu_seqlens, cu_seqlens ? size_t(num_seqs + 1) * 4 : 0), rg, rw, rsf,
+                         rws})
+            if (overlap(rout, in)) return RDA_ERR_ALIAS;
+        for (Range in : {rg, rw})
+            if (overlap(rsf, in) || overlap(rws, in)) return RDA_ERR_ALIAS;
+    }
+    unsigned char* slices = static_cast<unsigned char*>(workspace) + align256(base);
+    P.out = OutSink{nullptr, reinterpret_cast<uint16_t*>(slices)};
+    if ((st = prefill_sequential(P, stream, nullptr)) != RDA_OK) return st;
+    if (launch_norm_gate(nullptr, g, g_dtype, weight, eps, act, rows, out, out_dtype, stream,
+                         P.out.y) != hipSuccess)
+        return RDA_ERR_HIP;
+    return RDA_OK;
+}
+
 rda_status rda_output_norm_gate(const float* o, const void* g, rda_dtype g_dtype,
                                 const float* weight, float eps, int32_t act, int64_t rows,
                                 int32_t dv, void* out, rda_dtype out_dtype, hipStream_t stream) {
-    if (out_dtype != RDA_BF16 && out_dtype != RDA_FP32) return RDA_ERR_DTYPE;
-    if (act != RDA_GATE_SIGMOID && act != RDA_GATE_SILU && act != RDA_GATE_NONE)
-        return RDA_ERR_VALUE;
-    if (act == RDA_GATE_NONE) g_dtype = RDA_BF16;   // g is not read
-    if (g_dtype != RDA_BF16 && g_dtype != RDA_FP32) return RDA_ERR_DTYPE;
-    if (!(eps >= 0.f) || eps == INFINITY) return RDA_ERR_VALUE;
+    const rda_status st = check_norm_args(g_dtype, eps, act, out_dtype);
+    if (st != RDA_OK) return st;
     if (rows < 0 || dv <= 0) return RDA_ERR_SHAPE;
     if (dv != kD) return RDA_ERR_UNSUPPORTED;
     if (norm_gate_blocks(rows) > INT32_MAX) return RDA_ERR_SHAPE;

@@ -60,6 +60,22 @@ __device__ __forceinline__ float dpp_sum16(float x) {
     return x;
 }
 
+// Largest of x over each 16-lane row (every lane of the row gets it).
+__device__ __forceinline__ uint32_t dpp_umax16(uint32_t x) {
+    x = max(x, uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0xB1, 0xF, 0xF, false)));
+    x = max(x, uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x4E, 0xF, 0xF, false)));
+    x = max(x, uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x141, 0xF, 0xF, false)));
+    x = max(x, uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x140, 0xF, 0xF, false)));
+    return x;
+}
+
+// Bitwise or of x over each group of 4 lanes.
+__device__ __forceinline__ uint32_t dpp_or4(uint32_t x) {
+    x |= uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0xB1, 0xF, 0xF, false));
+    x |= uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x4E, 0xF, 0xF, false));
+    return x;
+}
+
 // Index of this lane's wavefront in the workgroup, as a wave-uniform scalar.
 // Branches on it then compile to scalar branches: an MFMA placed under a
 // per-lane EXEC mask would still execute for every lane (MFMA ignores EXEC),

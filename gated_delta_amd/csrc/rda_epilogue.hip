@@ -60,6 +60,26 @@ __device__ __forceinline__ void store_out<float>(float* p, const float y[4]) {
     *reinterpret_cast<f32x4*>(p) = f32x4{y[0], y[1], y[2], y[3]};
 }
 
+// Four channels 4c' .. 4c' + 3 of the 16-bit form a fused prefill's walk
+// leaves (OutSink): lane c of a row's 16 holds places 4 (c % 4) .. +3 of
+// slice c / 4 (or 4 + c / 4), so the four lanes of a quad hold one slice, and
+// its first two lanes the 8 places that carry the exponent code.
+__device__ __forceinline__ void load_enc(const uint16_t* p, int c, f32x4& out) {
+    const u32x2 d = *reinterpret_cast<const u32x2*>(p);
+    const uint32_t hv[4] = {d[0] & 0xffffu, d[0] >> 16, d[1] & 0xffffu, d[1] >> 16};
+    uint32_t bits = 0;
+    if ((c & 3) < 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bits |= (hv[e] & 1u) << (4 * (c & 3) + e);
+    }
+    const int E = int(dpp_or4(bits));
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        out[e] = E ? __builtin_amdgcn_ldexpf(float(__builtin_bit_cast(_Float16, uint16_t(hv[e]))),
+                                             E - 126)
+                   : 0.f;
+}
+
 template <int kAct>
 __device__ __forceinline__ float gate_act(float x) {
     if (kAct == RDA_GATE_NONE) return 1.f;
@@ -68,8 +88,12 @@ __device__ __forceinline__ float gate_act(float x) {
     return kAct == RDA_GATE_SIGMOID ? sig : x * sig;
 }
 
-template <typename TG, typename TO, int kAct>
-__global__ __launch_bounds__(256) void norm_gate_kernel(const float* o, const TG* __restrict__ g,
+// kEnc: the rows come in the 16-bit form of a fused prefill (oe) instead of
+// fp32 (o).
+template <typename TG, typename TO, int kAct, bool kEnc>
+__global__ __launch_bounds__(256) void norm_gate_kernel(const float* o,
+                                                        const uint16_t* __restrict__ oe,
+                                                        const TG* __restrict__ g,
                                                         const float* __restrict__ w, float eps,
                                                         int64_t rows, TO* out) {
     const int t = threadIdx.x;
@@ -92,8 +116,13 @@ __global__ __launch_bounds__(256) void norm_gate_kernel(const float* o, const TG
 #pragma unroll
     for (int i = 0; i < kRowsPerGroup; ++i) {
         const int64_t r = min(r0 + i, rows - 1);   // the tail re-reads the last row, unused
-        ox[i][0] = *reinterpret_cast<const f32x4*>(o + r * kD + 4 * c);
-        ox[i][1] = *reinterpret_cast<const f32x4*>(o + r * kD + 64 + 4 * c);
+        if constexpr (kEnc) {
+            load_enc(oe + r * kD + 4 * c, c, ox[i][0]);
+            load_enc(oe + r * kD + 64 + 4 * c, c, ox[i][1]);
+        } else {
+            ox[i][0] = *reinterpret_cast<const f32x4*>(o + r * kD + 4 * c);
+            ox[i][1] = *reinterpret_cast<const f32x4*>(o + r * kD + 64 + 4 * c);
+        }
         if (kAct != RDA_GATE_NONE) {
             load_gate<TG>(g + r * kD + 4 * c, gx[i]);
             load_gate<TG>(g + r * kD + 64 + 4 * c, gx[i] + 4);
@@ -122,20 +151,35 @@ __global__ __launch_bounds__(256) void norm_gate_kernel(const float* o, const TG
     }
 }
 
-template <typename TG, typename TO>
-void launch_act(const float* o, const void* g, const float* w, float eps, int32_t act,
-                int64_t rows, void* out, unsigned grid, hipStream_t stream) {
+template <typename TG, typename TO, bool kEnc>
+void launch_act(const float* o, const uint16_t* oe, const void* g, const float* w, float eps,
+                int32_t act, int64_t rows, void* out, unsigned grid, hipStream_t stream) {
     const TG* gt = static_cast<const TG*>(g);
     TO* ot = static_cast<TO*>(out);
     if (act == RDA_GATE_SIGMOID)
-        hipLaunchKernelGGL((norm_gate_kernel<TG, TO, RDA_GATE_SIGMOID>), dim3(grid), dim3(256), 0,
-                           stream, o, gt, w, eps, rows, ot);
+        hipLaunchKernelGGL((norm_gate_kernel<TG, TO, RDA_GATE_SIGMOID, kEnc>), dim3(grid),
+                           dim3(256), 0, stream, o, oe, gt, w, eps, rows, ot);
     else if (act == RDA_GATE_SILU)
-        hipLaunchKernelGGL((norm_gate_kernel<TG, TO, RDA_GATE_SILU>), dim3(grid), dim3(256), 0,
-                           stream, o, gt, w, eps, rows, ot);
+        hipLaunchKernelGGL((norm_gate_kernel<TG, TO, RDA_GATE_SILU, kEnc>), dim3(grid),
+                           dim3(256), 0, stream, o, oe, gt, w, eps, rows, ot);
     else
-        hipLaunchKernelGGL((norm_gate_kernel<TG, TO, RDA_GATE_NONE>), dim3(grid), dim3(256), 0,
-                           stream, o, gt, w, eps, rows, ot);
+        hipLaunchKernelGGL((norm_gate_kernel<TG, TO, RDA_GATE_NONE, kEnc>), dim3(grid),
+                           dim3(256), 0, stream, o, oe, gt, w, eps, rows, ot);
+}
+
+template <bool kEnc>
+void launch_dtypes(const float* o, const uint16_t* oe, const void* g, rda_dtype g_dtype,
+                   const float* w, float eps, int32_t act, int64_t rows, void* out,
+                   rda_dtype out_dtype, unsigned grid, hipStream_t stream) {
+    const bool g16 = g_dtype == RDA_BF16, o16 = out_dtype == RDA_BF16;
+    if (g16 && o16)
+        launch_act<uint16_t, uint16_t, kEnc>(o, oe, g, w, eps, act, rows, out, grid, stream);
+    else if (g16)
+        launch_act<uint16_t, float, kEnc>(o, oe, g, w, eps, act, rows, out, grid, stream);
+    else if (o16)
+        launch_act<float, uint16_t, kEnc>(o, oe, g, w, eps, act, rows, out, grid, stream);
+    else
+        launch_act<float, float, kEnc>(o, oe, g, w, eps, act, rows, out, grid, stream);
 }
 
 }  // namespace
@@ -144,14 +188,15 @@ int64_t norm_gate_blocks(int64_t rows) { return (rows + kRowsPerBlock - 1) / kRo
 
 hipError_t launch_norm_gate(const float* o, const void* g, rda_dtype g_dtype, const float* w,
                             float eps, int32_t act, int64_t rows, void* out, rda_dtype out_dtype,
-                            hipStream_t stream) {
+                            hipStream_t stream, const uint16_t* o_enc) {
     const unsigned grid = unsigned(norm_gate_blocks(rows));
     if (grid == 0) return hipSuccess;
-    const bool g16 = g_dtype == RDA_BF16, o16 = out_dtype == RDA_BF16;
-    if (g16 && o16) launch_act<uint16_t, uint16_t>(o, g, w, eps, act, rows, out, grid, stream);
-    else if (g16) launch_act<uint16_t, float>(o, g, w, eps, act, rows, out, grid, stream);
-    else if (o16) launch_act<float, uint16_t>(o, g, w, eps, act, rows, out, grid, stream);
-    else launch_act<float, float>(o, g, w, eps, act, rows, out, grid, stream);
+    if (o_enc)
+        launch_dtypes<true>(nullptr, o_enc, g, g_dtype, w, eps, act, rows, out, out_dtype, grid,
+                            stream);
+    else
+        launch_dtypes<false>(o, nullptr, g, g_dtype, w, eps, act, rows, out, out_dtype, grid,
+                             stream);
     return hipGetLastError();
 }
 

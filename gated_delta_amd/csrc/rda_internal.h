@@ -165,11 +165,25 @@ hipError_t launch_decode_diag(const void* q, const void* k, const void* v, rda_d
                               const float* alpha, const float* b, int32_t batch, int32_t heads,
                               float* S, float* o, hipStream_t stream);
 
-// Output norm and gate over `rows` rows of 128 channels.
+// Where a prefill walk puts its outputs [T, H, 128]: fp32 rows (o), or the
+// 16-bit form the fused output norm reads (y, o null).  In y each token-head
+// row's 16-channel slice is scaled by a power of two, 2^(126 - E) with E the
+// biased fp32 exponent of the slice's largest magnitude (so every value lies
+// in (-1, 1)), and stored as fp16; in the first 8 channels of the slice the
+// lowest significand bit is replaced by bit p of E, p = the channel's place
+// in its slice.  E = 0 (a slice of zeros or fp32 subnormals) stands for a
+// slice of zeros.
+struct OutSink {
+    float* o;
+    uint16_t* y;
+};
+
+// Output norm and gate over `rows` rows of 128 channels: from fp32 o, or
+// (o_enc) from the 16-bit form of OutSink.
 int64_t norm_gate_blocks(int64_t rows);
 hipError_t launch_norm_gate(const float* o, const void* g, rda_dtype g_dtype, const float* w,
                             float eps, int32_t act, int64_t rows, void* out, rda_dtype out_dtype,
-                            hipStream_t stream);
+                            hipStream_t stream, const uint16_t* o_enc = nullptr);
 
 hipError_t launch_prep(const void* q, const void* k, rda_dtype dt,
                        const float* a, const float* b, int32_t heads, int32_t max_chunks,
@@ -179,8 +193,8 @@ hipError_t launch_prep(const void* q, const void* k, rda_dtype dt,
 hipError_t launch_walk(const void* q, const void* k, const void* v, rda_dtype dt,
                        int32_t num_seqs, int32_t heads, const int32_t* rec,
                        const int32_t* seq_off, const int32_t* num_chunks,
-                       const unsigned char* factors, const float* S0, float* o, float* S_final,
-                       hipStream_t stream);
+                       const unsigned char* factors, const float* S0, OutSink out,
+                       float* S_final, hipStream_t stream);
 
 // bf16 prep (factors from LDS-DMA'd tiles, four workgroups per CU).  With
 // single_T >= 0 the input is one sequence of single_T tokens without offsets:
@@ -226,12 +240,12 @@ struct WalkPrep {
 // bf16 walk.  num_jobs (1 or 2) walks over the same chunks in one launch,
 // differing only in their WalkJob.  seg_chunks > 0: sequence n is the n-th
 // run of seg_chunks chunks of the table (segments of one sequence) instead of
-// seq_off[n] .. seq_off[n + 1].  outputs = false: no o is written, and Q and
-// A are not streamed.
+// seq_off[n] .. seq_off[n + 1].  outputs = false: no output is written, and
+// Q and A are not streamed.
 hipError_t launch_walk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             int32_t num_seqs, int32_t heads, const int32_t* rec,
                             const int32_t* seq_off, const int32_t* num_chunks,
-                            const unsigned char* factors, float* o, const WalkJob* jobs,
+                            const unsigned char* factors, OutSink out, const WalkJob* jobs,
                             int32_t num_jobs, int32_t seg_chunks, bool outputs,
                             hipStream_t stream, const WalkPrep* extra = nullptr);
 

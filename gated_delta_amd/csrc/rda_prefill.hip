@@ -50,6 +50,7 @@
 #include "rda_device.h"
 #include "rda_internal.h"
 #include "rda_lds.h"
+#include "rda_out.h"
 #include "rda_solve.h"
 
 namespace rda {
@@ -542,7 +543,7 @@ template <typename TIn, int kPar>
 __device__ __forceinline__ void output_step(WalkOps<WalkIn<TIn>::kSplit>& cur, f32x4& acc,
                                             const WalkCtx<TIn>& x, int next,
                                             WalkLds<WalkIn<TIn>::kSplit>& S,
-                                            float* __restrict__ o) {
+                                            const OutSink& out) {
     constexpr bool kSplit = WalkIn<TIn>::kSplit;
     const int w = x.w, l = x.l, g = l >> 4, c = l & 15, tt = w & 3;
     // P1
@@ -602,12 +603,7 @@ __device__ __forceinline__ void output_step(WalkOps<WalkIn<TIn>::kSplit>& cur, f
             p2 = mfma_bf16(cur.al[m], bh, p2);
         }
         const f32x4 ov = z * cur.gam + (p0 + p1 + p2);
-        const int t0 = cur.t0, len = cur.len;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tok = 16 * tt + 4 * g + i;
-            if (tok < len) o[((size_t(t0) + tok) * x.H + x.h) * kD + 16 * x.s + c] = ov[i];
-        }
+        store_out_tile(out, ov, cur.t0, 16 * tt, cur.len, x.H, x.h, x.s, g, c);
     }
     load_f(cur, x, next);
     load_rec(cur, x, next);
@@ -617,17 +613,17 @@ __device__ __forceinline__ void output_step(WalkOps<WalkIn<TIn>::kSplit>& cur, f
 template <typename TIn, bool kState>
 __device__ __forceinline__ void walk_loop(f32x4& acc, const WalkCtx<TIn>& x, int c_begin,
                                           int c_end, WalkLds<WalkIn<TIn>::kSplit>& S,
-                                          float* __restrict__ o) {
+                                          const OutSink& out) {
     WalkOps<WalkIn<TIn>::kSplit> A, B;
     const int last = c_end - 1;
     load_all(A, x, c_begin);
     load_all(B, x, c_begin + 1 < c_end ? c_begin + 1 : last);
     for (int ch = c_begin; ch < c_end; ch += 2) {
         if constexpr (kState) state_step<TIn, 0>(A, acc, x, ch + 2 < c_end ? ch + 2 : last, S);
-        else output_step<TIn, 0>(A, acc, x, ch + 2 < c_end ? ch + 2 : last, S, o);
+        else output_step<TIn, 0>(A, acc, x, ch + 2 < c_end ? ch + 2 : last, S, out);
         if (ch + 1 >= c_end) break;
         if constexpr (kState) state_step<TIn, 1>(B, acc, x, ch + 3 < c_end ? ch + 3 : last, S);
-        else output_step<TIn, 1>(B, acc, x, ch + 3 < c_end ? ch + 3 : last, S, o);
+        else output_step<TIn, 1>(B, acc, x, ch + 3 < c_end ? ch + 3 : last, S, out);
     }
 }
 
@@ -636,7 +632,7 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v, int N, int H,
     const int32_t* __restrict__ rec, const int32_t* __restrict__ seq_off,
     const int32_t* __restrict__ num_chunks, const unsigned char* __restrict__ factors,
-    const float* __restrict__ S0, float* __restrict__ o, float* __restrict__ S_final) {
+    const float* __restrict__ S0, OutSink out, float* __restrict__ S_final) {
     // XCD-aware mapping: the 8 value slices of one (sequence, head) share the
     // same blockIdx.x % 8, hence the same XCD and L2, which holds the chunk's
     // K, Q and factors that all 8 of them read.
@@ -661,8 +657,8 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(
     const size_t srow = ((size_t(n) * H + h) * kD + 16 * s + c) * kD + 16 * w + 4 * g;
     f32x4 acc = S0 ? *reinterpret_cast<const f32x4*>(S0 + srow) : zero4();
     if (c_begin < c_end) {
-        if (w < 4) walk_loop<TIn, true>(acc, x, c_begin, c_end, lds, o);
-        else walk_loop<TIn, false>(acc, x, c_begin, c_end, lds, o);
+        if (w < 4) walk_loop<TIn, true>(acc, x, c_begin, c_end, lds, out);
+        else walk_loop<TIn, false>(acc, x, c_begin, c_end, lds, out);
     }
     if (S_final) *reinterpret_cast<f32x4*>(S_final + srow) = acc;
 }
@@ -689,20 +685,20 @@ hipError_t launch_prep(const void* q, const void* k, rda_dtype dt, const float* 
 hipError_t launch_walk(const void* q, const void* k, const void* v, rda_dtype dt,
                        int32_t num_seqs, int32_t heads, const int32_t* rec,
                        const int32_t* seq_off, const int32_t* num_chunks,
-                       const unsigned char* factors, const float* S0, float* o, float* S_final,
-                       hipStream_t stream) {
+                       const unsigned char* factors, const float* S0, OutSink out,
+                       float* S_final, hipStream_t stream) {
     const int64_t pairs = int64_t(num_seqs) * heads;
     const unsigned grid = unsigned(64 * ((pairs + 7) / 8));
     if (dt == RDA_BF16) {
         const WalkJob job{S0, S_final, 0, 0};
         return launch_walk_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                 static_cast<const uint16_t*>(v), num_seqs, heads, rec, seq_off,
-                                num_chunks, factors, o, &job, 1, 0, true, stream);
+                                num_chunks, factors, out, &job, 1, 0, true, stream);
     } else {
         hipLaunchKernelGGL(walk_kernel<float>, dim3(grid), dim3(kWalkThreads), 0, stream,
                            static_cast<const float*>(q), static_cast<const float*>(k),
                            static_cast<const float*>(v), num_seqs, heads, rec, seq_off,
-                           num_chunks, factors, S0, o, S_final);
+                           num_chunks, factors, S0, out, S_final);
     }
     return hipGetLastError();
 }

@@ -51,6 +51,7 @@
 // output; they only need to be finite, which copies of real rows are.
 #include "rda_internal.h"
 #include "rda_lds.h"
+#include "rda_out.h"
 #include "rda_prep.h"
 
 namespace rda {
@@ -372,7 +373,7 @@ __device__ __forceinline__ void state_step(const Ctx& x, int w, const Stage& st,
 // ---- output waves ------------------------------------------------------------------
 
 __device__ __forceinline__ void output_step(const Ctx& x, int tt, int ch, const Stage& st, Lds& S,
-                                            float* __restrict__ o) {
+                                            const OutSink& out) {
     const int l = x.l, g = l >> 4, c = l & 15;
     const int nb = (tt >> 1) + 1;
     const int t0 = x.rec[4 * ch + 1], len = x.rec[4 * ch + 2];
@@ -424,11 +425,7 @@ __device__ __forceinline__ void output_step(const Ctx& x, int tt, int ch, const 
             mma3(ah[m], al[m], xh[m], xl[m], p0, p1, p2);
         }
         const f32x4 ov = z + (p0 + p1 + p2);
-        float* orow = o + (size_t(t0 + 16 * tt + 4 * g) * x.H + x.h) * kD + 16 * x.s + c;
-        const size_t tstride = size_t(x.H) * kD;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (16 * tt + 4 * g + e < len) orow[e * tstride] = ov[e];
+        store_out_tile(out, ov, t0, 16 * tt, len, x.H, x.h, x.s, g, c);
     }
 }
 
@@ -461,7 +458,7 @@ __global__ __launch_bounds__(kThreads) void walk_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int N, int H, const int32_t* __restrict__ rec,
     const int32_t* __restrict__ seq_off, const int32_t* __restrict__ num_chunks,
-    const unsigned char* __restrict__ factors, float* __restrict__ o, WalkJob j0, WalkJob j1,
+    const unsigned char* __restrict__ factors, OutSink out, WalkJob j0, WalkJob j1,
     int seg_chunks, WalkPrep X) {
     __shared__ __attribute__((aligned(16))) WalkOrPrepLds shm;
     if (int(blockIdx.x) >= X.walk_blocks) {
@@ -518,7 +515,7 @@ __global__ __launch_bounds__(kThreads) void walk_bf16_kernel(
     if (w >= kStateWaves) {
         for (int ch = c0; ch < c_end; ++ch) {
             if constexpr (kOut) {
-                output_step(x, w - kStateWaves, ch, lds.st[(ch - c0) & 1], lds, o);
+                output_step(x, w - kStateWaves, ch, lds.st[(ch - c0) & 1], lds, out);
             } else {
                 __syncthreads();   // A
                 __syncthreads();   // B
@@ -555,7 +552,7 @@ __global__ __launch_bounds__(kThreads) void walk_bf16_kernel(
 hipError_t launch_walk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             int32_t num_seqs, int32_t heads, const int32_t* rec,
                             const int32_t* seq_off, const int32_t* num_chunks,
-                            const unsigned char* factors, float* o, const WalkJob* jobs,
+                            const unsigned char* factors, OutSink out, const WalkJob* jobs,
                             int32_t num_jobs, int32_t seg_chunks, bool outputs,
                             hipStream_t stream, const WalkPrep* extra) {
     const int64_t pairs = int64_t(num_seqs) * heads;
@@ -568,11 +565,11 @@ hipError_t launch_walk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t
     const WalkJob j1 = num_jobs > 1 ? jobs[1] : none;
     if (outputs)
         hipLaunchKernelGGL(walk_bf16_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, q, k, v,
-                           num_seqs, heads, rec, seq_off, num_chunks, factors, o, jobs[0], j1,
+                           num_seqs, heads, rec, seq_off, num_chunks, factors, out, jobs[0], j1,
                            seg_chunks, X);
     else
         hipLaunchKernelGGL(walk_bf16_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, q, k,
-                           v, num_seqs, heads, rec, seq_off, num_chunks, factors, o, jobs[0], j1,
+                           v, num_seqs, heads, rec, seq_off, num_chunks, factors, out, jobs[0], j1,
                            seg_chunks, X);
     return hipGetLastError();
 }

@@ -93,6 +93,11 @@ def _load():
         lib.rda_decode_step_diag.argtypes = [p, p, p, ctypes.c_int, p, p, i32, i32, i32, i32,
                                              p, p, p]
         lib.rda_decode_step_diag.restype = ctypes.c_int
+        lib.rda_prefill_norm_gate_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        lib.rda_prefill_norm_gate_workspace_bytes.restype = sz
+        lib.rda_prefill_norm_gate.argtypes = pre[:13] + [p, ctypes.c_int, p, ctypes.c_float, i32,
+                                                         p, ctypes.c_int, p, p, sz, p]
+        lib.rda_prefill_norm_gate.restype = ctypes.c_int
         lib.rda_chunk_table.argtypes = [p, i32, i32, p, p, p, p]
         lib.rda_chunk_table.restype = ctypes.c_int
         _lib = lib
@@ -456,6 +461,81 @@ def rda_output_norm_gate(o: torch.Tensor, g: Optional[torch.Tensor], *,
     if st != 0:
         raise RdaError(st, "rda_output_norm_gate")
     return out
+
+
+def rda_prefill_norm_gate_workspace_bytes(num_seqs: int, total_tokens: int, num_heads: int,
+                                          dk: int = 128, dv: int = 128) -> int:
+    return _load().rda_prefill_norm_gate_workspace_bytes(num_seqs, total_tokens, num_heads, dk,
+                                                         dv)
+
+
+def rda_prefill_norm_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, a: torch.Tensor,
+                          b: torch.Tensor, g: Optional[torch.Tensor], cu_seqlens=None,
+                          S0: Optional[torch.Tensor] = None, *,
+                          weight: Optional[torch.Tensor] = None, eps: float = 1e-5,
+                          act: str = "sigmoid", out: Optional[torch.Tensor] = None,
+                          out_dtype=torch.bfloat16, S_final: Optional[torch.Tensor] = None,
+                          want_state: bool = True, workspace: Optional[torch.Tensor] = None,
+                          stream=None):
+    """Prefill with the output norm and gate fused (C entry point
+    ``rda_prefill_norm_gate``): the arguments of rda_prefill and of
+    rda_output_norm_gate (g [T, H, 128] bf16 or fp32, or None with
+    act="none").  Returns (out [T, H, 128] in out_dtype, S_final or None);
+    no fp32 o is formed."""
+    lib_ = _load()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a GPU tensor")
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _qkv_dtype(q)
+    _need(q, "q", q.dtype, (T, H, dk), dev)
+    _need(k, "k", q.dtype, (T, H, dk), dev)
+    _need(v, "v", q.dtype, (T, H, dv), dev)
+    _need(a, "a", torch.float32, (T, H), dev)
+    _need(b, "b", torch.float32, (T, H), dev)
+    if cu_seqlens is not None:
+        cu_host = check_cu_seqlens(cu_seqlens, T)
+        N = cu_host.shape[0] - 1
+        cu_dev = torch.from_numpy(cu_host).to(dev)
+    else:
+        N, cu_dev = 1, None
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (N, H, dv, dk), dev)
+    if act not in _GATE_ACTS:
+        raise ValueError(f"act must be one of {sorted(_GATE_ACTS)}")
+    g_dt = RDA_BF16
+    if act != "none":
+        if g is None:
+            raise ValueError("g is required unless act='none'")
+        g_dt = _qkv_dtype(g)
+        _need(g, "g", g.dtype, (T, H, dv), dev)
+    else:
+        g = None
+    if weight is not None:
+        _need(weight, "weight", torch.float32, (dv,), dev)
+    o_dt = {torch.bfloat16: RDA_BF16, torch.float32: RDA_FP32}.get(out_dtype)
+    if o_dt is None:
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=out_dtype, device=dev)
+    _need(out, "out", out_dtype, (T, H, dv), dev)
+    if S_final is None and want_state:
+        S_final = torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev)
+    if S_final is not None:
+        _need(S_final, "S_final", torch.float32, (N, H, dv, dk), dev)
+    need = rda_prefill_norm_gate_workspace_bytes(N, T, H, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    st = lib_.rda_prefill_norm_gate(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(a), _ptr(b),
+                                    _ptr(cu_dev), N, T, H, dk, dv, _ptr(S0), _ptr(g), g_dt,
+                                    _ptr(weight), float(eps), _GATE_ACTS[act], _ptr(out), o_dt,
+                                    _ptr(S_final), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(),
+                                    _stream_handle(stream))
+    if st != 0:
+        raise RdaError(st, "rda_prefill_norm_gate")
+    return out, S_final
 
 
 def rda_prologue(x_q: torch.Tensor, x_k: torch.Tensor, x_v: torch.Tensor,

@@ -421,6 +421,44 @@ rda_status rda_output_norm_gate(const float* o, const void* g, rda_dtype g_dtype
                                 const float* weight, float eps, int32_t act, int64_t rows,
                                 int32_t dv, void* out, rda_dtype out_dtype, hipStream_t stream);
 
+/* Workspace bytes rda_prefill_norm_gate needs (0 on bad sizes): that of
+ * rda_prefill plus 2 bytes per output element for the 16-bit form below. */
+size_t rda_prefill_norm_gate_workspace_bytes(int32_t num_seqs, int32_t total_tokens,
+                                             int32_t num_heads, int32_t dk, int32_t dv);
+
+/*
+ * rda_prefill followed by rda_output_norm_gate on its output, without the
+ * fp32 output: the block's mixer and its o_norm / gate (the
+ * tiny-random/raon-1-mini model card, section "Printing the model") in one
+ * call.  The walk stores each token-head row in 16 bits per channel, in the
+ * workspace: each 16-channel slice scaled by a power of two that puts its
+ * largest magnitude in [0.5, 1), as fp16, with the scale's exponent carried
+ * in the lowest bit of the slice's first 8 values.  A pass over that form
+ * restores the values, takes the RMS norm and applies the weight and the
+ * gate.
+ *
+ *   q, k, v, a, b, cu_seqlens, num_seqs, total_tokens, num_heads, dk, dv,
+ *   S0, S_final   as for rda_prefill
+ *   g, g_dtype, weight, eps, act, out, out_dtype
+ *                 as for rda_output_norm_gate with rows = total_tokens x
+ *                 num_heads; out [total_tokens, H, dv] may not overlap any
+ *                 other argument or the workspace
+ *   workspace     at least rda_prefill_norm_gate_workspace_bytes(...)
+ * Errors: those of both entry points, checked before anything is enqueued.
+ * The result differs from the two calls' by the 16-bit form: at most 2^-11
+ * relative per value from the fp16 rounding, plus 2^-10 on the 8 values of a
+ * slice that carry its exponent, below the output's bf16 rounding.  A slice
+ * whose largest magnitude is an fp32 subnormal counts as zeros.
+ */
+rda_status rda_prefill_norm_gate(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
+                                 const float* a, const float* b,
+                                 const int32_t* cu_seqlens, int32_t num_seqs,
+                                 int32_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
+                                 const float* S0, const void* g, rda_dtype g_dtype,
+                                 const float* weight, float eps, int32_t act, void* out,
+                                 rda_dtype out_dtype, float* S_final, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
 /*
  * Test hook: the chunk table rda_prefill builds from cu_seqlens.
  *   out               device int32 [rda_max_chunks(...), 4]; row c =

@@ -38,7 +38,8 @@ def test_header_declares_the_entry_points():
     for n in ("rda_prefill", "rda_decode_step", "rda_decode_tokens", "rda_prefill_diag",
               "rda_decode_step_diag", "rda_decode_tokens_diag", "rda_prologue", "rda_output_norm_gate",
               "rda_prefill_workspace_bytes", "rda_prefill_noalloc", "rda_decode_step_prologue",
-              "rda_chunk_table", "rda_abi_version", "rda_status_string"):
+              "rda_chunk_table", "rda_abi_version", "rda_status_string", "rda_prefill_norm_gate",
+              "rda_prefill_norm_gate_workspace_bytes"):
         assert n in names
 
 
@@ -285,6 +286,43 @@ def test_output_norm_gate_rejects_bad_arguments(lib):
     assert ng(out=P + 2 * GiB) == ALIAS           # out over the weight
     assert ng(out=P, odt=0) == ALIAS              # bf16 out over fp32 o
     assert ng(rows=1 << 40) == SHAPE              # grid beyond int32 blocks
+
+
+def test_prefill_norm_gate_rejects_bad_arguments(lib):
+    """Every check of both halves before anything is enqueued (host-side
+    pointers that are never dereferenced)."""
+    rda.lib()     # the binding sets the argument types
+
+    def png(q=P, k=P + GiB, v=P + 2 * GiB, dt=0, a=P + 3 * GiB, b=P + 4 * GiB, cu=None, N=1,
+            T=128, H=2, dk=128, dv=128, S0=None, g=P + 5 * GiB, gdt=0, w=P + 6 * GiB, eps=1e-5,
+            act=0, out=P + 7 * GiB, odt=0, Sf=P + 8 * GiB, ws=P + 9 * GiB, wsb=None):
+        if wsb is None:
+            wsb = rda.rda_prefill_norm_gate_workspace_bytes(N, T, H, 128, 128)
+        return lib.rda_prefill_norm_gate(q, k, v, dt, a, b, cu, N, T, H, dk, dv, S0, g, gdt, w,
+                                         eps, act, out, odt, Sf, ws, wsb, None)
+    base = rda.rda_prefill_workspace_bytes(1, 128, 2)
+    assert rda.rda_prefill_norm_gate_workspace_bytes(1, 128, 2) == base + 128 * 2 * 128 * 2
+    assert rda.rda_prefill_norm_gate_workspace_bytes(1, 128, 2, 64, 64) == 0
+    assert png(q=None) == NULL
+    assert png(out=None) == NULL
+    assert png(g=None) == NULL                    # the gate is read
+    assert png(dt=7) == DTYPE
+    assert png(gdt=7) == DTYPE
+    assert png(odt=5) == DTYPE
+    assert png(act=3) == VALUE
+    assert png(eps=-1.0) == VALUE
+    assert png(eps=float("nan")) == VALUE
+    assert png(T=-1) == SHAPE
+    assert png(dk=64) == UNSUP
+    assert png(ws=None) == WS
+    assert png(wsb=rda.rda_prefill_workspace_bytes(1, 128, 2)) == WS   # no room for the slices
+    assert png(out=P + 7 * GiB + 8) == ALIGN
+    assert png(g=P + 5 * GiB + 4) == ALIGN
+    assert png(out=P + 16) == ALIAS               # out over q
+    assert png(out=P + 5 * GiB + 1024) == ALIAS   # out inside g
+    assert png(out=P + 9 * GiB + 512) == ALIAS    # out inside the workspace
+    assert png(Sf=P + 5 * GiB) == ALIAS           # S_final over g
+    assert png(ws=P + 5 * GiB - 256) == ALIAS     # workspace over g
 
 
 def test_prologue_rejects_bad_arguments(lib):
