@@ -152,8 +152,12 @@ def read_profile(fname: str, key: str):
 
 
 def read_traffic(kernel: str):
-    """HBM bytes per launch of one kernel (FETCH_SIZE + WRITE_SIZE, calibrated)."""
-    return read_profile("hbm_traffic.txt", f"{kernel}.bytes_per_launch")
+    """HBM bytes of one kernel (FETCH_SIZE + WRITE_SIZE, calibrated) per
+    prefill call when the summary has that figure (every launch in a call),
+    else per launch."""
+    per_call = read_profile("hbm_traffic.txt", f"{kernel}.bytes_per_call")
+    return per_call if per_call is not None else read_profile("hbm_traffic.txt",
+                                                              f"{kernel}.bytes_per_launch")
 
 
 def main():
@@ -303,9 +307,10 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # per-kernel breakdown: the same prefill with its stages one after another
-    # (rda_prefill_profiled), each stage between its own event pair; a decode
-    # step between calls streams 512 MiB, as in the timed loop
+    # per-stage breakdown: the same calls with an event pair around each
+    # stage (rda_prefill_profiled runs the same kernels), after the timed
+    # steps because the events between launches add about 6 us to a call; a
+    # decode step between calls streams 512 MiB, as in the timed loop
     KB = min(K, 20)
     stage_evs = [make_events(2 * rda.RDA_NUM_STAGES) for _ in range(KB)]
     if do_prefill:
@@ -332,14 +337,12 @@ def main():
     if do_prefill:
         st = np.array([[stage_evs[i][2 * s].elapsed_time(stage_evs[i][2 * s + 1])
                         for s in range(rda.RDA_NUM_STAGES)] for i in range(KB)])   # ms
-        seq = np.array([stage_evs[i][0].elapsed_time(stage_evs[i][-1]) for i in range(KB)])
         call = np.array([call_evs[i][0].elapsed_time(call_evs[i][1]) for i in range(K)])
         units = T * H
         call_s = float(np.mean(call)) * 1e-3
         out["value"] = T / call_s
         out["unit"] = "tokens/s"
         out["prefill"] = {"ms_per_call": call_s * 1e3, "tokens_per_s": T / call_s,
-                          "ms_per_call_stages_in_sequence": float(np.mean(seq)),
                           "hbm_roofline_tokens_per_s": PEAK_HBM_GBPS * 1e9 / (PREFILL_BYTES * H),
                           "algorithmic_TFLOPs": PREFILL_FLOPS * units / call_s / 1e12,
                           "mfma_frac_algorithmic": PREFILL_FLOPS * units / call_s / 1e12
@@ -348,7 +351,7 @@ def main():
                           / call_s / 1e9 / PEAK_HBM_GBPS}
         # MFMA work rocprofv3 counted per launch (hi/lo split products
         # included), over this run's call time
-        mf = [read_profile("mfma_rda_prefill_T16384_H16.txt", f"{n}.mfma_{t}_flops")
+        mf = [read_profile("mfma_rda_prefill_T16384_H16.txt", f"{n}.mfma_{t}_flops_per_call")
               for n in ("rda_prep", "rda_walk") for t in ("bf16", "f32")]
         if all(x is not None for x in mf):
             out["prefill"]["mfma_frac_executed_rocprof"] = sum(mf) / call_s / 1e12 / PEAK_BF16_TFLOPS
@@ -358,14 +361,19 @@ def main():
         # the walk streams q, k, v again and writes o and the states, so it is
         # charged the whole path's algorithmic bytes (1288 B per token-head
         # plus S0 and S_final); the prep's figure is the inputs it reads
-        # itself (q, k, a, b)
+        # itself (q, k, a, b).  Times are per call: in the plan that preps
+        # the later chunks beside the walk, the prep stage is the prep of the
+        # first chunks and the walk stage both walk launches (the first of
+        # which also preps the rest on the CUs the walk leaves idle).
         kb = {0: 0.0, 1: (2 * D * 2 + 2 * 4) * units,
               2: PREFILL_BYTES * units + 2 * H * STATE_BYTES}
         for s in range(rda.RDA_NUM_STAGES):
             if s == rda.RDA_STAGE_TABLE:
                 continue    # no cu_seqlens: the table is written by the prep kernel
             ms = float(np.mean(st[:, s]))
-            kernels[names[s]] = {"avg_us": ms * 1e3, "alg_bytes": kb[s]}
+            kernels[names[s]] = {"us_per_call": ms * 1e3, "alg_bytes": kb[s],
+                                 "launches_per_call": read_profile(
+                                     "hbm_traffic.txt", f"{names[s]}.launches_per_call")}
     if do_decode:
         dms = np.array([dec_evs[i][0].elapsed_time(dec_evs[i][1]) for i in range(K)])
         dsec = float(np.mean(dms)) * 1e-3
@@ -374,7 +382,8 @@ def main():
         out["decode"] = {"value": gbps, "unit": "GB/s", "us_per_step": dsec * 1e6,
                          "frac_of_peak": gbps / PEAK_HBM_GBPS, "bytes_per_step": dbytes,
                          "tokens_per_s": B / dsec}
-        kernels["rda_decode_step"] = {"avg_us": dsec * 1e6, "alg_bytes": dbytes}
+        kernels["rda_decode_step"] = {"us_per_call": dsec * 1e6, "alg_bytes": dbytes,
+                                      "launches_per_call": 1}
         if "value" not in out:
             out["value"], out["unit"] = gbps, "GB/s"
         if not args.no_extras:
@@ -395,14 +404,16 @@ def main():
                                                  / PEAK_HBM_GBPS}
     out["kernels"] = kernels
 
-    # roofline of the kernel with the largest time per step
-    dom = max(kernels, key=lambda n: kernels[n]["avg_us"])
+    # roofline of the kernel with the largest time per step (per call: all
+    # of its launches in one call)
+    dom = max(kernels, key=lambda n: kernels[n]["us_per_call"])
     kd = kernels[dom]
-    ach = kd["alg_bytes"] / (kd["avg_us"] * 1e-6) / 1e9
+    ach = kd["alg_bytes"] / (kd["us_per_call"] * 1e-6) / 1e9
     tr = read_traffic(dom)
     out["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS,
                        "unit": "GB/s", "frac": ach / PEAK_HBM_GBPS, "traffic": tr,
-                       "alg_bytes_per_launch": kd["alg_bytes"], "avg_us": kd["avg_us"]}
+                       "alg_bytes_per_call": kd["alg_bytes"], "us_per_call": kd["us_per_call"],
+                       "launches_per_call": kd["launches_per_call"]}
     if do_prefill:
         # the whole call (every kernel of rda_prefill) against the same bytes
         whole = (PREFILL_BYTES * T * H + 2 * H * STATE_BYTES) / (out["prefill"]["ms_per_call"]
@@ -449,7 +460,16 @@ def main():
         t = time.perf_counter()
         oracle.prefill(sl(p.q), sl(p.k), sl(p.v), sl(p.a), sl(p.b), S0=p.S0, threads=1)
         one_s = time.perf_counter() - t
+        cpu_model = None
+        try:
+            for line in open("/proc/cpuinfo"):
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
         out["cpu_baseline"] = {"value": T / cpu_s, "unit": "tokens/s", "cores": thr,
+                               "cpu_model": cpu_model, "visible_cpus": os.cpu_count(),
                                "kind": "oracle",
                                "sample": f"the full long-prompt prefill (T={T}, H={H}, d={D}, "
                                          f"fp64 sequential recurrence, OpenMP over the {H} "

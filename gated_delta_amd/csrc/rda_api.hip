@@ -224,8 +224,11 @@ rda_status check_prefill(const void* q, const void* k, const void* v, rda_dtype 
     return RDA_OK;
 }
 
-// The overlapped plan (see overlap_plan), all on `stream`.
-rda_status prefill_overlapped(const Prefill& P, hipStream_t stream) {
+// The overlapped plan (see overlap_plan), all on `stream`.  Stage events
+// (when `ev` is given): the table stage is empty (the prep writes the
+// table), the prep stage is the first launch, and the walk stage spans the
+// two walk launches (the first of which also preps the later chunks).
+rda_status prefill_overlapped(const Prefill& P, hipStream_t stream, hipEvent_t const* ev) {
     const auto* q16 = static_cast<const uint16_t*>(P.q);
     const auto* k16 = static_cast<const uint16_t*>(P.k);
     const auto* v16 = static_cast<const uint16_t*>(P.v);
@@ -248,21 +251,30 @@ rda_status prefill_overlapped(const Prefill& P, hipStream_t stream) {
     Y.c_hi = nch;
     const WalkJob first{P.S0, P.S_mid, 0, 0};
     const WalkJob second{P.S_mid, P.S_final, 0, 0};
+    rda_status st;
+    if ((st = record(ev, 2 * RDA_STAGE_TABLE, stream)) != RDA_OK ||
+        (st = record(ev, 2 * RDA_STAGE_TABLE + 1, stream)) != RDA_OK ||
+        (st = record(ev, 2 * RDA_STAGE_PREP, stream)) != RDA_OK)
+        return st;
     if (launch_prep_bf16(q16, k16, P.a, P.b, P.H, P.mc, nullptr, nullptr, P.factors, P.T, P.rec,
-                         P.seq_off, P.nch, stream, 0, c1) != hipSuccess ||
-        launch_walk_bf16(q16, k16, v16, 1, P.H, P.rec, P.seq_off, P.nch, P.factors, P.out, &first,
+                         P.seq_off, P.nch, stream, 0, c1) != hipSuccess)
+        return RDA_ERR_HIP;
+    if ((st = record(ev, 2 * RDA_STAGE_PREP + 1, stream)) != RDA_OK ||
+        (st = record(ev, 2 * RDA_STAGE_WALK, stream)) != RDA_OK)
+        return st;
+    if (launch_walk_bf16(q16, k16, v16, 1, P.H, P.rec, P.seq_off, P.nch, P.factors, P.out, &first,
                          1, 0, true, stream, &X) != hipSuccess ||
         launch_walk_bf16(q16, k16, v16, 1, P.H, P.rec, P.seq_off, P.nch, P.factors, P.out, &second,
                          1, 0, true, stream, &Y) != hipSuccess)
         return RDA_ERR_HIP;
-    return RDA_OK;
+    return record(ev, 2 * RDA_STAGE_WALK + 1, stream);
 }
 
 // Table, prep and walk one after another on `stream`, each stage bracketed
-// by its event pair when `ev` is given; without events, one bf16 sequence
-// whose walk leaves CUs idle takes the overlapped plan instead.
+// by its event pair when `ev` is given; one bf16 sequence whose walk leaves
+// CUs idle takes the overlapped plan instead.
 rda_status prefill_sequential(const Prefill& P, hipStream_t stream, hipEvent_t const* ev) {
-    if (ev == nullptr && P.ovl.c1 > 0) return prefill_overlapped(P, stream);
+    if (P.ovl.c1 > 0) return prefill_overlapped(P, stream, ev);
     rda_status st;
     // one bf16 sequence without offsets: the prep kernel derives each chunk's
     // record itself and writes the table, which saves the table launch

@@ -2,7 +2,8 @@
 # Collects the rocprofv3 kernel summaries and the counter passes behind
 # profiles/: kernel trace + stats of the bench's timed steps (and, in passes
 # of their own, of the one-pass multi-token decode, the output norm and gate,
-# the prologue, the per-channel-decay prefill and the segmented state pass),
+# the prologue, the per-channel-decay prefill, the segmented state pass and
+# the prefill fused with the output norm and gate),
 # then one FETCH_SIZE and one
 # WRITE_SIZE pass over the prefill alone, each of those, and a plain device
 # copy of known size (the counter calibration), then one pass of the MFMA
@@ -39,6 +40,10 @@ echo "== kernel trace + stats: python bench.py --mode segments --steps 10 --no-c
 timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d "$OUT/prof_trace_seg" -o trace \
     -- python -u "$R/bench.py" --mode segments --steps 10 --no-cpu \
     > "$OUT/prof_trace_seg.log" 2>&1 || exit $?
+echo "== kernel trace + stats: python bench.py --mode prefill_norm_gate --steps 10 --no-cpu"
+timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d "$OUT/prof_trace_png" -o trace \
+    -- python -u "$R/bench.py" --mode prefill_norm_gate --steps 10 --no-cpu \
+    > "$OUT/prof_trace_png.log" 2>&1 || exit $?
 for ctr in FETCH_SIZE WRITE_SIZE; do
   for mode in prefill copy decode_tokens output_norm_gate prologue prefill_diag; do
     echo "== pmc $ctr: python bench.py --mode $mode --steps 2 --warmup 1 --no-cpu"

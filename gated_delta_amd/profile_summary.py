@@ -17,6 +17,9 @@ Writes
   profiles/kernels_rda_prefill_segmented_T16384_H2.txt
       the same for the segmented state pass beside the one-pass walk on the
       long prompt's first two heads (bench --mode segments);
+  profiles/kernels_rda_prefill_norm_gate_T16384_H16.txt
+      the same for the prefill alone, followed by the output norm and gate,
+      and fused with it (bench --mode prefill_norm_gate);
   profiles/hbm_traffic.txt
       FETCH_SIZE and WRITE_SIZE per dispatch of every prefill kernel, each
       scaled by what the same counter reads for a device copy of known size,
@@ -65,6 +68,9 @@ def find(d, pattern):
     return hits[0]
 
 
+PREP_KERNELS = ("prep_bf16_kernel", "prep_kernel", "prep_diag_kernel")
+
+
 def counter(d, name):
     """Average per-dispatch value of counter `name` by kernel (first launch of
     each kernel skipped when it ran more than once)."""
@@ -77,6 +83,32 @@ def counter(d, name):
     return {k: statistics.mean(v[1:] if len(v) > 1 else v) for k, v in by.items()}
 
 
+def counter_per_call(d, name):
+    """Counter `name` summed per prefill call, by kernel: a call starts at each
+    dispatch of a prep kernel (every prefill plan launches one per call); the
+    first call is skipped.  Returns ({kernel: value per call}, {kernel:
+    launches per call}), or empty dicts when the pass ran no prep kernel."""
+    rows = [r for r in csv.DictReader(open(find(d, "*counter_collection.csv")))
+            if r["Counter_Name"] == name]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    starts = [i for i, r in enumerate(rows) if short(r["Kernel_Name"]) in PREP_KERNELS]
+    if len(starts) < 2:
+        return {}, {}
+    kept = rows[starts[1]:]
+    calls = len(starts) - 1
+    tot, cnt = {}, {}
+    for r in kept:
+        k = short(r["Kernel_Name"])
+        tot[k] = tot.get(k, 0.0) + float(r["Counter_Value"])
+        cnt[k] = cnt.get(k, 0) + 1
+    return {k: v / calls for k, v in tot.items()}, {k: v / calls for k, v in cnt.items()}
+
+
+def calls_in_trace(rows):
+    """Prefill calls in a kernel-trace pass: the dispatches of its prep kernel."""
+    return sum(int(r["Calls"]) for r in rows if short(r["Name"]) in PREP_KERNELS)
+
+
 def kernel_table(trace_dir, path, header, templates=False):
     """Write the per-kernel call count / average / total of one kernel-trace
     pass to `path` under `header`; returns the stats rows.  templates: keep
@@ -87,12 +119,18 @@ def kernel_table(trace_dir, path, header, templates=False):
         def name(n):
             n = n.replace("rda::(anonymous namespace)::", "").replace("void ", "")
             return n.replace("rda::", "").split("(")[0].strip()
-    lines = header + [f"# kernel sources: {source_hash()}",
-                      f"{'kernel':40s} {'calls':>6s} {'avg_us':>10s} {'total_us':>12s} {'pct':>6s}"]
+    ncalls = calls_in_trace(rows)
+    lines = header + [f"# kernel sources: {source_hash()}"]
+    if ncalls:
+        lines.append(f"# prefill calls in the pass: {ncalls} (dispatches of the prep kernel); "
+                     "us_per_call = total_us / calls")
+    lines.append(f"{'kernel':40s} {'calls':>6s} {'avg_us':>10s} {'total_us':>12s} {'pct':>6s}"
+                 + (f" {'us_per_call':>12s}" if ncalls else ""))
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
         lines.append(f"{name(r['Name'])[:40]:40s} {int(r['Calls']):6d} "
                      f"{float(r['AverageNs']) / 1e3:10.2f} {float(r['TotalDurationNs']) / 1e3:12.1f} "
-                     f"{float(r['Percentage']):6.2f}")
+                     f"{float(r['Percentage']):6.2f}"
+                     + (f" {float(r['TotalDurationNs']) / 1e3 / ncalls:12.2f}" if ncalls else ""))
     open(path, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
     return rows
@@ -185,6 +223,20 @@ def main():
              "#     -- python bench.py --mode segments --steps 10 --no-cpu",
              "# then python gated_delta_amd/profile_summary.py OUTDIR"], templates=True)
 
+    if os.path.isdir(os.path.join(out, "prof_trace_png")):
+        kernel_table(
+            os.path.join(out, "prof_trace_png"),
+            os.path.join(prof, "kernels_rda_prefill_norm_gate_T16384_H16.txt"),
+            ["# rocprofv3 kernel trace, the long prompt (16384 x 16, bf16 q/k/v, S0 ~ N(0,",
+             "# 0.02)) three ways: rda_prefill alone, rda_prefill then rda_output_norm_gate",
+             "# (bf16 gate and out), and rda_prefill_norm_gate (the fused form, whose norm",
+             "# pass is norm_gate_kernel<..., true>); 11 calls of each, each after a 512 MiB",
+             "# read (reduce_kernel: the cache flush)",
+             "# command: gated_delta_amd/profile_run.sh OUTDIR, whose seventh pass is",
+             "#   rocprofv3 --kernel-trace --stats --output-format csv -d OUTDIR/prof_trace_png -o trace \\",
+             "#     -- python bench.py --mode prefill_norm_gate --steps 10 --no-cpu",
+             "# then python gated_delta_amd/profile_summary.py OUTDIR"], templates=True)
+
     # ---- HBM traffic -------------------------------------------------------------
     n = 1 << 30   # bytes the calibration copy reads and writes per launch
     f_copy = counter(os.path.join(out, "prof_FETCH_SIZE_copy"), "FETCH_SIZE")
@@ -195,6 +247,9 @@ def main():
     w_scale = n / (w_copy[wk] * 1024.0)
     fetch = counter(os.path.join(out, "prof_FETCH_SIZE_prefill"), "FETCH_SIZE")
     write = counter(os.path.join(out, "prof_WRITE_SIZE_prefill"), "WRITE_SIZE")
+    fetch_call, per_call = counter_per_call(os.path.join(out, "prof_FETCH_SIZE_prefill"),
+                                            "FETCH_SIZE")
+    write_call, _ = counter_per_call(os.path.join(out, "prof_WRITE_SIZE_prefill"), "WRITE_SIZE")
     # the multi-token decode and the output norm and gate, from passes of
     # their own (only their own kernel: the flush and restores are not theirs)
     for mode, kern in (("decode_tokens", "decode_tokens_kernel"),
@@ -231,6 +286,13 @@ def main():
         lines.append(f"{name}.fetch_bytes = {fb:.0f}")
         lines.append(f"{name}.write_bytes = {wb:.0f}")
         lines.append(f"{name}.bytes_per_launch = {fb + wb:.0f}")
+        if k in fetch_call and k in write_call:
+            # per prefill call (the walk runs twice per call in the plan that
+            # preps later chunks beside it)
+            fcb = fetch_call[k] * 1024.0 * f_scale
+            wcb = write_call[k] * 1024.0 * w_scale
+            lines.append(f"{name}.launches_per_call = {per_call[k]:.2f}")
+            lines.append(f"{name}.bytes_per_call = {fcb + wcb:.0f}")
     path = os.path.join(prof, "hbm_traffic.txt")
     open(path, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -265,6 +327,11 @@ def mfma_summary(mdir, rows, path, what1, what2, bench_args, dname):
     with its rate over the kernel's average duration in `rows` (the kernel
     trace of the same workload)."""
     avg_us = {short(r["Name"]): float(r["AverageNs"]) / 1e3 for r in rows}
+    ncalls = calls_in_trace(rows)
+    call_us = {short(r["Name"]): float(r["TotalDurationNs"]) / 1e3 / ncalls for r in rows} \
+        if ncalls else {}
+    m16_call, per_call = counter_per_call(mdir, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    m32_call, _ = counter_per_call(mdir, "SQ_INSTS_VALU_MFMA_MOPS_F32")
     mops16 = counter(mdir, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
     mops32 = counter(mdir, "SQ_INSTS_VALU_MFMA_MOPS_F32")
     inst16 = counter(mdir, "SQ_INSTS_VALU_MFMA_BF16")
@@ -278,9 +345,11 @@ def mfma_summary(mdir, rows, path, what1, what2, bench_args, dname):
              f"#     -- python bench.py {bench_args}",
              "# (part of gated_delta_amd/profile_run.sh OUTDIR; then",
              "# python gated_delta_amd/profile_summary.py OUTDIR).  MOPS count 512 flops each;",
-             "# the executed work includes the hi/lo split products.  The rate divides by",
-             "# the kernel's average duration in the kernel trace summary; the fraction is",
-             "# of the 2.5 PFLOP/s dense bf16 peak.  mfma_busy_per_simd = MFMA busy cycles",
+             "# the executed work includes the hi/lo split products.  Per call: every launch",
+             "# of the kernel in one prefill call (a call starts at its prep kernel; the",
+             "# first call skipped).  The rate divides the work per call by the kernel's",
+             "# time per call in the kernel trace summary (its total over the calls); the",
+             "# fraction is of the 2.5 PFLOP/s dense bf16 peak.  mfma_busy_per_simd = MFMA busy cycles",
              "# (summed over a CU's four SIMDs) / (4 x CU busy cycles).",
              f"source_hash = {source_hash()}"]
     for k in sorted(mops16):
@@ -291,7 +360,20 @@ def mfma_summary(mdir, rows, path, what1, what2, bench_args, dname):
         lines.append(f"{name}.mfma_bf16_instructions = {inst16.get(k, 0.0):.0f}")
         lines.append(f"{name}.mfma_bf16_flops = {f16:.0f}")
         lines.append(f"{name}.mfma_f32_flops = {f32:.0f}")
-        if k in avg_us and avg_us[k] > 0:
+        if k in m16_call:
+            # per prefill call: every launch of the kernel in one call, over
+            # the kernel's time per call in the trace
+            c16 = m16_call[k] * 512.0
+            c32 = m32_call.get(k, 0.0) * 512.0
+            lines.append(f"{name}.launches_per_call = {per_call[k]:.2f}")
+            lines.append(f"{name}.mfma_bf16_flops_per_call = {c16:.0f}")
+            lines.append(f"{name}.mfma_f32_flops_per_call = {c32:.0f}")
+            if call_us.get(k, 0) > 0:
+                rate = (c16 + c32) / (call_us[k] * 1e-6) / 1e12
+                lines.append(f"{name}.us_per_call = {call_us[k]:.2f}")
+                lines.append(f"{name}.mfma_tflops = {rate:.2f}")
+                lines.append(f"{name}.mfma_frac_of_bf16_peak = {rate / 2500.0:.4f}")
+        elif k in avg_us and avg_us[k] > 0:
             rate = (f16 + f32) / (avg_us[k] * 1e-6) / 1e12
             lines.append(f"{name}.mfma_tflops = {rate:.2f}")
             lines.append(f"{name}.mfma_frac_of_bf16_peak = {rate / 2500.0:.4f}")

@@ -160,8 +160,12 @@ rda_status rda_prefill(const void* q, const void* k, const void* v, rda_dtype qk
 /*
  * rda_prefill with per-stage timing events: when `stage_events` is non-NULL
  * it points to 2 * RDA_NUM_STAGES events; stage s records stage_events[2s]
- * before its kernel and stage_events[2s+1] after it, on `stream` (NULL
- * entries are skipped).  Results are identical to rda_prefill.
+ * before its first kernel and stage_events[2s+1] after its last, on
+ * `stream` (NULL entries are skipped).  The kernels are those rda_prefill
+ * runs: in the plan that preps later chunks beside the walk, the table
+ * stage is empty, the prep stage is the prep of the first chunks and the
+ * walk stage spans both walk launches.  Results are identical to
+ * rda_prefill.
  */
 rda_status rda_prefill_profiled(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
                                 const float* a, const float* b,
