@@ -100,6 +100,20 @@ OverlapPlan overlap_plan(int32_t num_seqs, int32_t total_tokens, int32_t heads) 
     return op;
 }
 
+// With the fused output norm the last walk launch of the overlapped plan is
+// cut at c2: the walk of [c1, c2) carries the norm of the rows of [0, c1)
+// and the walk of [c2, nch) that of [c1, c2), on the idle CUs, so that only
+// the norm of the last nch - c2 chunks runs after the walk.  nch - c2 is
+// nch / 8 (at least 16): enough walk time to hide the norm of [c1, c2) on
+// half the chip.  0: no cut.
+int fused_norm_cut(const OverlapPlan& op, int32_t total_tokens) {
+    if (op.c1 <= 0) return 0;
+    const int nch = (total_tokens + kC - 1) / kC;
+    const int tail = nch / 8 > 16 ? nch / 8 : 16;
+    const int c2 = nch - tail;
+    return c2 >= op.c1 + 8 ? c2 : 0;
+}
+
 size_t overlap_state_bytes(const OverlapPlan& op, int32_t heads) {
     return op.c1 > 0 ? size_t(heads) * kD * kD * sizeof(float) : 0;
 }
@@ -150,6 +164,7 @@ struct Prefill {
     OverlapPlan ovl;      // likewise, when no segmented pass runs
     float* S_mid;         // overlapped plan: the state after chunk c1
     OutSink out;          // where the walk's outputs go (o, or the slice form)
+    WalkNorm norm;        // fused output norm (norm.y set): its arguments
 };
 
 rda_status check_prefill(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
@@ -205,7 +220,7 @@ rda_status check_prefill(const void* q, const void* k, const void* v, rda_dtype 
                 reinterpret_cast<int32_t*>(ws + tl.seq_off_off),
                 reinterpret_cast<int32_t*>(ws + tl.num_off), ws + align256(tl.bytes),
                 SegPlan{}, nullptr, nullptr, nullptr, OverlapPlan{}, nullptr,
-                OutSink{o, nullptr}};
+                OutSink{o, nullptr}, WalkNorm{}};
     const SegPlan sp = seg_plan(num_seqs, total_tokens, num_heads);
     const OverlapPlan op = overlap_plan(num_seqs, total_tokens, num_heads);
     unsigned char* tail = P.factors + size_t(mc) * num_heads * kChunkHeadBytes;
@@ -246,10 +261,26 @@ rda_status prefill_overlapped(const Prefill& P, hipStream_t stream, hipEvent_t c
     X.rec_out = P.rec;
     X.seq_off_out = P.seq_off;
     X.num_out = P.nch;
-    WalkPrep Y{};
+    // the fused output norm: the rows of chunks already walked, on the CUs a
+    // later walk launch leaves idle (see fused_norm_cut)
+    const int c2 = P.norm.y ? fused_norm_cut(P.ovl, P.T) : 0;
+    auto norm_rows = [&](WalkPrep& Z, int lo, int hi) {
+        Z.norm = P.norm;
+        Z.norm.row_lo = int64_t(kC) * lo * P.H;
+        Z.norm.row_hi = int64_t(kC) * hi * P.H;
+        Z.norm.blocks = P.ovl.prep_blocks;
+    };
+    WalkPrep Y{}, Y2{};
     Y.c_lo = c1;
-    Y.c_hi = nch;
+    Y.c_hi = c2 > 0 ? c2 : nch;
+    if (P.norm.y) norm_rows(Y, 0, c1);
+    Y2.c_lo = c2;
+    Y2.c_hi = nch;
+    if (c2 > 0) norm_rows(Y2, c1, c2);
     const WalkJob first{P.S0, P.S_mid, 0, 0};
+    // each walk workgroup reads its slice of the saved state before it
+    // writes it back, so the middle state may stay in place
+    const WalkJob middle{P.S_mid, P.S_mid, 0, 0};
     const WalkJob second{P.S_mid, P.S_final, 0, 0};
     rda_status st;
     if ((st = record(ev, 2 * RDA_STAGE_TABLE, stream)) != RDA_OK ||
@@ -263,10 +294,18 @@ rda_status prefill_overlapped(const Prefill& P, hipStream_t stream, hipEvent_t c
         (st = record(ev, 2 * RDA_STAGE_WALK, stream)) != RDA_OK)
         return st;
     if (launch_walk_bf16(q16, k16, v16, 1, P.H, P.rec, P.seq_off, P.nch, P.factors, P.out, &first,
-                         1, 0, true, stream, &X) != hipSuccess ||
-        launch_walk_bf16(q16, k16, v16, 1, P.H, P.rec, P.seq_off, P.nch, P.factors, P.out, &second,
-                         1, 0, true, stream, &Y) != hipSuccess)
+                         1, 0, true, stream, &X) != hipSuccess)
         return RDA_ERR_HIP;
+    if (c2 > 0) {
+        if (launch_walk_bf16(q16, k16, v16, 1, P.H, P.rec, P.seq_off, P.nch, P.factors, P.out,
+                             &middle, 1, 0, true, stream, &Y) != hipSuccess ||
+            launch_walk_bf16(q16, k16, v16, 1, P.H, P.rec, P.seq_off, P.nch, P.factors, P.out,
+                             &second, 1, 0, true, stream, &Y2) != hipSuccess)
+            return RDA_ERR_HIP;
+    } else if (launch_walk_bf16(q16, k16, v16, 1, P.H, P.rec, P.seq_off, P.nch, P.factors, P.out,
+                                &second, 1, 0, true, stream, &Y) != hipSuccess) {
+        return RDA_ERR_HIP;
+    }
     return record(ev, 2 * RDA_STAGE_WALK + 1, stream);
 }
 
@@ -824,9 +863,19 @@ rda_status rda_prefill_norm_gate(const void* q, const void* k, const void* v, rd
     }
     unsigned char* slices = static_cast<unsigned char*>(workspace) + align256(base);
     P.out = OutSink{nullptr, reinterpret_cast<uint16_t*>(slices)};
+    P.norm = WalkNorm{P.out.y, g, g_dtype == RDA_BF16 ? 1 : 0, weight, eps, act, out,
+                      out_dtype == RDA_BF16 ? 1 : 0, 0, 0, 0};
     if ((st = prefill_sequential(P, stream, nullptr)) != RDA_OK) return st;
-    if (launch_norm_gate(nullptr, g, g_dtype, weight, eps, act, rows, out, out_dtype, stream,
-                         P.out.y) != hipSuccess)
+    // the overlapped plan's later walk launches have done the rows of the
+    // chunks before the last walk launch's; the rest here
+    const int c2 = fused_norm_cut(P.ovl, total_tokens);
+    const int64_t done = int64_t(kC) * (c2 > 0 ? c2 : P.ovl.c1 > 0 ? P.ovl.c1 : 0) * num_heads;
+    const size_t gsz = g_dtype == RDA_BF16 ? 2 : 4, osz = out_dtype == RDA_BF16 ? 2 : 4;
+    const size_t off = size_t(done) * kD;
+    if (launch_norm_gate(nullptr, g ? static_cast<const unsigned char*>(g) + off * gsz : nullptr,
+                         g_dtype, weight, eps, act, rows - done,
+                         static_cast<unsigned char*>(out) + off * osz, out_dtype, stream,
+                         P.out.y + off) != hipSuccess)
         return RDA_ERR_HIP;
     return RDA_OK;
 }

@@ -227,6 +227,21 @@ struct WalkPrepArgs {
     int H;
     unsigned char* factors;
 };
+// The output norm and gate that norm workgroups of a walk launch may run
+// (after the walk's and the prep's workgroups) over rows [row_lo, row_hi)
+// of the 16-bit form y (OutSink) whose walk is already done.
+struct WalkNorm {
+    const uint16_t* y;
+    const void* g;
+    int g16;                // g is bf16 (else fp32)
+    const float* w;
+    float eps;
+    int act;                // an rda_gate_act
+    void* out;
+    int o16;                // out is bf16 (else fp32)
+    int64_t row_lo, row_hi;
+    int blocks;             // norm workgroups (0: none)
+};
 struct WalkPrep {
     int c_lo, c_hi;
     int prep_blocks;        // prep workgroups (0: none)
@@ -234,6 +249,7 @@ struct WalkPrep {
     int single_T, nch;
     WalkPrepArgs args;
     int32_t *rec_out, *seq_off_out, *num_out;
+    WalkNorm norm;
     int walk_blocks;        // set by the launcher
 };
 

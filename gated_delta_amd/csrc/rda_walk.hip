@@ -51,6 +51,7 @@
 // output; they only need to be finite, which copies of real rows are.
 #include "rda_internal.h"
 #include "rda_lds.h"
+#include "rda_norm.h"
 #include "rda_out.h"
 #include "rda_prep.h"
 
@@ -436,7 +437,7 @@ __device__ void prep_role(const WalkPrep& X, PrepLds (&S)[4]) {
     const int sub = wave_id() >> 2;          // which of the four groups
     const int w = wave_id() & 3;             // wave within the group
     const int tid = threadIdx.x & 255;
-    const int nprep = int(gridDim.x) - X.walk_blocks;
+    const int nprep = X.prep_blocks;
     const int wg = int(blockIdx.x) - X.walk_blocks;
     const int H = X.args.H;
     for (int base = X.item_lo + 4 * wg; base < X.item_hi; base += 4 * nprep) {
@@ -453,6 +454,35 @@ __device__ void prep_role(const WalkPrep& X, PrepLds (&S)[4]) {
     }
 }
 
+// The norm workgroups of a launch: 64 rows at a time, 16 lanes per row,
+// over rows [row_lo, row_hi) of the 16-bit form.
+template <typename TG, typename TO, int kAct>
+__device__ void norm_rows(const WalkNorm& N, int wg, int nwg) {
+    const int c = threadIdx.x & 15, grp = threadIdx.x >> 4;
+    for (int64_t base = N.row_lo + 64 * int64_t(wg); base < N.row_hi; base += 64 * int64_t(nwg)) {
+        const int64_t r0 = base + grp;
+        norm_gate_row<TG, TO, kAct, true>(nullptr, N.y, static_cast<const TG*>(N.g), N.w, N.eps,
+                                          min(r0, N.row_hi - 1), r0 < N.row_hi,
+                                          static_cast<TO*>(N.out), c);
+    }
+}
+
+template <int kAct>
+__device__ void norm_rows_act(const WalkNorm& N, int wg, int nwg) {
+    if (N.g16 && N.o16) norm_rows<uint16_t, uint16_t, kAct>(N, wg, nwg);
+    else if (N.g16) norm_rows<uint16_t, float, kAct>(N, wg, nwg);
+    else if (N.o16) norm_rows<float, uint16_t, kAct>(N, wg, nwg);
+    else norm_rows<float, float, kAct>(N, wg, nwg);
+}
+
+__device__ void norm_role(const WalkPrep& X) {
+    const int wg = int(blockIdx.x) - X.walk_blocks - X.prep_blocks;
+    const WalkNorm& N = X.norm;
+    if (N.act == RDA_GATE_SIGMOID) norm_rows_act<RDA_GATE_SIGMOID>(N, wg, N.blocks);
+    else if (N.act == RDA_GATE_SILU) norm_rows_act<RDA_GATE_SILU>(N, wg, N.blocks);
+    else norm_rows_act<RDA_GATE_NONE>(N, wg, N.blocks);
+}
+
 template <bool kOut>
 __global__ __launch_bounds__(kThreads) void walk_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -461,6 +491,10 @@ __global__ __launch_bounds__(kThreads) void walk_bf16_kernel(
     const unsigned char* __restrict__ factors, OutSink out, WalkJob j0, WalkJob j1,
     int seg_chunks, WalkPrep X) {
     __shared__ __attribute__((aligned(16))) WalkOrPrepLds shm;
+    if (int(blockIdx.x) >= X.walk_blocks + X.prep_blocks) {
+        norm_role(X);
+        return;
+    }
     if (int(blockIdx.x) >= X.walk_blocks) {
         prep_role(X, shm.prep);
         return;
@@ -560,7 +594,8 @@ hipError_t launch_walk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t
     WalkPrep X{};
     if (extra) X = *extra;
     X.walk_blocks = int(walk_grid);
-    const unsigned grid = walk_grid + unsigned(extra ? extra->prep_blocks : 0);
+    const unsigned grid =
+        walk_grid + unsigned(extra ? extra->prep_blocks + extra->norm.blocks : 0);
     const WalkJob none{nullptr, nullptr, 0, 0};
     const WalkJob j1 = num_jobs > 1 ? jobs[1] : none;
     if (outputs)

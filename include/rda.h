@@ -439,7 +439,8 @@ size_t rda_prefill_norm_gate_workspace_bytes(int32_t num_seqs, int32_t total_tok
  * largest magnitude in [0.5, 1), as fp16, with the scale's exponent carried
  * in the lowest bit of the slice's first 8 values.  A pass over that form
  * restores the values, takes the RMS norm and applies the weight and the
- * gate.
+ * gate; for one bf16 sequence whose walk leaves CUs idle, most of that pass
+ * runs beside the walk over the rows already walked.
  *
  *   q, k, v, a, b, cu_seqlens, num_seqs, total_tokens, num_heads, dk, dv,
  *   S0, S_final   as for rda_prefill

@@ -109,6 +109,10 @@ CASES = {
                                                     key=(604,)), "sigmoid", True, True),
     "overlapped 2048x16": (lambda: synth.make_prefill(2048, 16, bf16=True, s0_std=0.02,
                                                       key=(605,)), "silu", True, True),
+    # long enough that the last walk launch is cut in two, each part running
+    # the norm of rows already walked beside it
+    "overlapped, cut 4100x16": (lambda: synth.make_prefill(4100, 16, bf16=True, s0_std=0.02,
+                                                           key=(612,)), "sigmoid", True, True),
     # outputs far outside fp16's range, and far below its normal range: each
     # slice's power-of-two scale must bring them into (-1, 1) either way
     "values x 2^20": (lambda: scaled(synth.make_prefill(300, 2, bf16=True, key=(608,)), 2.0 ** 20),
