@@ -75,10 +75,13 @@ def test_decode_steps(dev):
         busy(dev)
 
 
-@pytest.mark.parametrize("T,H,bf16", [(64, 1, False), (300, 4, True), (4096, 4, True)])
+@pytest.mark.parametrize("T,H,bf16", [(64, 1, False), (300, 4, True), (4096, 4, True),
+                                      (2048, 16, True)])
 def test_prefill(dev, T, H, bf16):
-    """A short prefill (launch-bound), a packed-size one, and one that takes
-    the segmented state pass (4096 tokens x 4 heads)."""
+    """A short prefill (launch-bound), a packed-size one, one that takes the
+    segmented state pass (4096 tokens x 4 heads) and one that takes the
+    overlapped plan (2048 x 16: prep of the first chunks, then their walk
+    beside the prep of the rest, then the rest of the walk)."""
     p = synth.make_prefill(T, H, bf16=bf16, s0_std=0.02, key=(801, T, H))
     q, k, v = (dev_tokens(getattr(p, n), bf16, dev) for n in "qkv")
     a, b = dev_f32(p.a, dev), dev_f32(p.b, dev)
@@ -97,6 +100,37 @@ def test_prefill(dev, T, H, bf16):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(o_g, o_e), f"replay {r}: o"
+        assert torch.equal(S_g, S_e), f"replay {r}: S_final"
+        busy(dev)
+
+
+@pytest.mark.parametrize("T,H", [(300, 4), (4100, 16)])
+def test_prefill_norm_gate(dev, T, H):
+    """The prefill fused with the output norm and gate; 4100 x 16 takes the
+    overlapped plan with its last walk launch cut in two, the norm of walked
+    rows running beside the walk."""
+    p = synth.make_prefill(T, H, bf16=True, s0_std=0.02, key=(803, T, H))
+    x = synth.epilogue_inputs(T * H, key=(803, T))
+    q, k, v = (dev_tokens(getattr(p, n), True, dev) for n in "qkv")
+    a, b = dev_f32(p.a, dev), dev_f32(p.b, dev)
+    S0 = dev_f32(p.S0, dev)
+    g = dev_tokens(x.g.reshape(T, H, 128), True, dev)
+    w = dev_f32(x.weight, dev)
+    say(f"[graph] prefill_norm_gate T={T} H={H}")
+    o_e, S_e = rda.rda_prefill_norm_gate(q, k, v, a, b, g, S0=S0, weight=w)
+    torch.cuda.synchronize()
+    o_g = torch.empty_like(o_e)
+    S_g = torch.empty_like(S_e)
+    ws = torch.empty(rda.rda_prefill_norm_gate_workspace_bytes(1, T, H), dtype=torch.uint8,
+                     device=dev)
+    gr = warm_then_capture(lambda: rda.rda_prefill_norm_gate(q, k, v, a, b, g, S0=S0, weight=w,
+                                                             out=o_g, S_final=S_g, workspace=ws))
+    for r in range(REPLAYS):
+        o_g.fill_(float("nan"))
+        S_g.fill_(float("nan"))
+        gr.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_e), f"replay {r}: out"
         assert torch.equal(S_g, S_e), f"replay {r}: S_final"
         busy(dev)
 
