@@ -31,12 +31,18 @@
 // exceeds e^60 on some channel (possible only for decays below e^-3.75 per
 // token), the block is computed elementwise with exact exponents instead.
 //
-// WALK (sequential over the chunks of a sequence): one 8-wave workgroup per
-// (sequence, head, 16-channel value slice).  Wave w keeps the state's key
-// tile w (16 keys x 16 values) in an MFMA accumulator.  Every operand comes
-// pre-packed from the prep, so each wave loads its MFMA operands straight
-// into registers, two chunks ahead; LDS only carries the state, the errors
-// and U between waves.  Per chunk, wave tt = w % 4:
+// WALK (sequential over the chunks of a sequence): one 16-wave workgroup per
+// (sequence, head, 16-channel value slice).  Compute wave w (0..7) keeps
+// the state's key tile w (16 keys x 16 values) in an MFMA accumulator; eight
+// loader waves stream every operand the prep packed into LDS with LDS-DMA,
+// so the compute waves issue no global loads.  The chunk's operands do not
+// fit twice in LDS (130 KiB), so they are held once, in three parts that
+// are each streamed for the next chunk right after the barrier that ends
+// their last read: the decayed K and Q tiles and V after barrier B, T_b
+// after barrier C, (K e^{G_C - G})^T, A and e^{G_C} after the next chunk's
+// barrier A.  Loaders 0 and 1 also touch the factor lines four chunks ahead
+// so that they sit in L2 when the DMA asks for them.  Per chunk, wave
+// tt = w % 4:
 //   P1  every wave publishes its state tile (bf16 hi/lo B operand)
 //   P2  waves 0-3: Y = (K e^G)[tt] S^T, E = V - Y published;
 //       waves 4-7: Z = (Q e^G)[tt] S^T
@@ -338,28 +344,50 @@ __global__ __launch_bounds__(kPrepThreads) void prep_diag_kernel(
 // ---------------------------------------------------------------------------
 // WALK
 // ---------------------------------------------------------------------------
-constexpr int kDWaves = 8;
+constexpr int kDCompute = 8;                          // compute waves
+constexpr int kDLoaders = 8;                          // loader waves
+constexpr int kDThreads = (kDCompute + kDLoaders) * 64;
+constexpr int kDPfAhead = 4;                          // L2 touch distance (chunks)
 
-// One wave's operands of one chunk.
+// One chunk's operands in LDS, in three parts with lifetimes of their own,
+// each streamed for the next chunk right after the barrier that ends its
+// last read:
+//   XA  the decayed K and Q tiles and this slice's V columns: read in P2,
+//       streamed after barrier B;
+//   FT  T_b: read in P3, streamed after barrier C;
+//   FK  (K e^{G_C - G})^T, A and e^{G_C}: read in P4, streamed after the next
+//       chunk's barrier A.
+// The packed operands keep the prep's layout: 1 KiB blocks of one 16-byte
+// MFMA operand per lane.
 template <typename TIn>
-struct DiagOps {
-    bf16x8 xa[4][2];   // (K e^G) (waves 0-3) or (Q e^G) (waves 4-7), token tile tt: [key block][hi/lo]
-    bf16x8 fa[2][2];   // T_b (waves 0-3) or A (waves 4-7), token tile tt: [token block][hi/lo]
-    bf16x8 kh[2][2];   // (K e^{G_C - G})^T, key tile w: [token block][hi/lo]
-    f32x4 gc;          // e^{G_C} of keys 16w + 4g .. +3
-    TIn vraw[4];       // V at tokens 16tt + 4g + i, value 16s + c (waves 0-3), as loaded:
-                       // widened where used, so the prefetch is never waited on here
-    int t0, len;
+struct DiagStage {
+    u32x4 Kt[32][64];    // (K e^G): [(token tile * 4 + key block) * 2 + hi/lo][lane]
+    u32x4 Qt[32][64];    // (Q e^G), the same
+    TIn V[kC * 16];      // this slice's 16 value channels, one row per token
+    u32x4 Tb[16][64];    // T_b: [(token tile * 2 + token block) * 2 + hi/lo][lane]
+    u32x4 Kh[32][64];    // (K e^{G_C - G})^T: [(key tile * 2 + token block) * 2 + hi/lo][lane]
+    u32x4 Am[16][64];    // A, as T_b
+    float GC[kD];        // e^{G_C} per key
 };
+
+template <typename TIn>
+struct DiagLds {
+    DiagStage<TIn> st;
+    u32x4 Sx[4][2][64];  // state tiles (hi/lo) as B operands, key blocks 0..3
+    u32x4 Ex[2][2][64];  // E (hi/lo), token blocks 0, 1
+    u32x4 Ux[2][2][64];  // U (hi/lo)
+    float sink[64];      // landing words of the L2 touches
+};
+static_assert(sizeof(DiagLds<float>) <= 160 * 1024, "LDS budget of one workgroup");
 
 // The chunks of one sequence are consecutive and full but for the last, so
 // a chunk's first token and length follow from the first chunk's start and
-// the sequence's end without a dependent load in the chunk loop.
+// the sequence's end.
 template <typename TIn>
 struct DiagCtx {
     const TIn* v;
     const unsigned char* factors;
-    int H, h, s, w, l;
+    int H, h, s, l;
     int c_begin, t_begin, t_end;
 };
 
@@ -368,80 +396,137 @@ __device__ __forceinline__ const unsigned char* diag_factors(const DiagCtx<TIn>&
     return x.factors + (size_t(chunk) * x.H + x.h) * kDiagChunkHeadBytes;
 }
 
+// ---- loader waves ------------------------------------------------------------
+// Blocks per chunk, by part: XA = K e^G (32), Q e^G (32, with outputs only),
+// V (2 bf16 or 4 fp32 blocks of 32 or 16 token rows); FT = T_b (16); FK =
+// (K e^{G_C - G})^T (32), A (16, with outputs only), e^{G_C} (half a block).
+// Loader i issues the blocks i, i + 8, ... of each part.
 template <typename TIn>
-__device__ __forceinline__ void load_xa(DiagOps<TIn>& o, const DiagCtx<TIn>& x, int chunk) {
-    const bf16x8* P =
-        reinterpret_cast<const bf16x8*>(diag_factors(x, chunk) + (x.w < 4 ? kDOffKt : kDOffQt));
-    const int tt = x.w & 3;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int base = ((tt * 4 + m) * 2) * 64 + x.l;
-        o.xa[m][0] = P[base];
-        o.xa[m][1] = P[base + 64];
-    }
-}
+constexpr int kVBlocks = sizeof(TIn) == 2 ? 2 : 4;
+template <bool kOut, typename TIn>
+constexpr int kXABlocks = (kOut ? 64 : 32) + kVBlocks<TIn>;
+constexpr int kFTBlocks = 16;
+template <bool kOut>
+constexpr int kFKBlocks = (kOut ? 48 : 32) + 1;
 
-template <typename TIn>
-__device__ __forceinline__ void load_fa(DiagOps<TIn>& o, const DiagCtx<TIn>& x, int chunk) {
-    const bf16x8* P =
-        reinterpret_cast<const bf16x8*>(diag_factors(x, chunk) + (x.w < 4 ? kDOffTb : kDOffA));
-    const int tt = x.w & 3;
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        const int base = ((tt * 2 + m) * 2) * 64 + x.l;
-        o.fa[m][0] = P[base];
-        o.fa[m][1] = P[base + 64];
-    }
-}
+constexpr int loader_share(int n, int i) { return i < n ? (n - i + 7) / 8 : 0; }
 
-template <typename TIn>
-__device__ __forceinline__ void load_kh(DiagOps<TIn>& o, const DiagCtx<TIn>& x, int chunk) {
+template <bool kOut, typename TIn>
+__device__ __forceinline__ void issue_xa_block(const DiagCtx<TIn>& x, int chunk, int j,
+                                               DiagStage<TIn>& st) {
+    const int L = x.l;
     const unsigned char* F = diag_factors(x, chunk);
-    const bf16x8* P = reinterpret_cast<const bf16x8*>(F + kDOffKh);
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        const int base = ((x.w * 2 + m) * 2) * 64 + x.l;
-        o.kh[m][0] = P[base];
-        o.kh[m][1] = P[base + 64];
-    }
-    o.gc = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(F + kDOffGC) +
-                                           16 * x.w + 4 * (x.l >> 4));
-}
-
-template <typename TIn>
-__device__ __forceinline__ void load_rec_v(DiagOps<TIn>& o, const DiagCtx<TIn>& x, int chunk) {
-    o.t0 = x.t_begin + kC * (chunk - x.c_begin);
-    o.len = min(kC, x.t_end - o.t0);
-    // every wave loads (output waves do not use it): the same loads in the same
-    // order in every wave keeps the compiler's load counting exact
-    const int tt = x.w & 3, g = x.l >> 4, c = x.l & 15;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 16 * tt + 4 * g + i;
-        const int rr = r < o.len ? r : o.len - 1;   // rows past the end: any valid row
-        o.vraw[i] = x.v[((size_t(o.t0) + rr) * x.H + x.h) * kD + 16 * x.s + c];
+    constexpr int kQ = kOut ? 32 : 0;
+    if (j < 32) {
+        dma16(F + kDOffKt + 1024 * j + 16 * L, reinterpret_cast<char*>(st.Kt) + 1024 * j);
+    } else if (j < 32 + kQ) {
+        dma16(F + kDOffQt + 1024 * (j - 32) + 16 * L,
+              reinterpret_cast<char*>(st.Qt) + 1024 * (j - 32));
+    } else {
+        // V rows: 16 bytes per lane, 2 (bf16) or 4 (fp32) lanes per row; rows
+        // past the chunk's end duplicate its last row (only finite values are
+        // needed there: T_b is zero on those rows and columns)
+        const int n = j - 32 - kQ;
+        constexpr int kLanesPerRow = int(sizeof(TIn));   // a row is 16 values: 32 or 64 bytes
+        constexpr int kRows = 64 / kLanesPerRow;         // rows per block: 32 or 16
+        const int t0 = x.t_begin + kC * (chunk - x.c_begin);
+        const int len = min(kC, x.t_end - t0);
+        const int r = kRows * n + L / kLanesPerRow;
+        const int rr = r < len ? r : len - 1;
+        const TIn* src = x.v + (size_t(t0 + rr) * x.H + x.h) * kD + 16 * x.s +
+                         (16 / int(sizeof(TIn))) * (L % kLanesPerRow);
+        dma16(src, reinterpret_cast<char*>(st.V) + 1024 * n);
     }
 }
 
-// the order of the in-loop refills, so the pending loads at the loop head are
-// the same on entry and on the back edge
-template <typename TIn>
-__device__ __forceinline__ void load_all(DiagOps<TIn>& o, const DiagCtx<TIn>& x, int chunk) {
-    load_xa(o, x, chunk);
-    load_fa(o, x, chunk);
-    load_kh(o, x, chunk);
-    load_rec_v(o, x, chunk);
+template <bool kOut, typename TIn>
+__device__ __forceinline__ void issue_fk_block(const DiagCtx<TIn>& x, int chunk, int j,
+                                               DiagStage<TIn>& st) {
+    const int L = x.l;
+    const unsigned char* F = diag_factors(x, chunk);
+    constexpr int kA = kOut ? 16 : 0;
+    if (j < 32) {
+        dma16(F + kDOffKh + 1024 * j + 16 * L, reinterpret_cast<char*>(st.Kh) + 1024 * j);
+    } else if (j < 32 + kA) {
+        dma16(F + kDOffA + 1024 * (j - 32) + 16 * L,
+              reinterpret_cast<char*>(st.Am) + 1024 * (j - 32));
+    } else if (L < 32) {
+        dma16(F + kDOffGC + 16 * L, st.GC);   // 128 floats: lanes 0..31
+    }
 }
 
-struct DiagLds {
-    u32x4 Sx[4][2][64];   // state tiles (hi/lo) as B operands, key blocks 0..3
-    u32x4 Ex[2][2][64];   // E (hi/lo), token blocks 0, 1
-    u32x4 Ux[2][2][64];   // U (hi/lo)
-};
+template <int kI, bool kOut, typename TIn>
+__device__ __forceinline__ void issue_xa(const DiagCtx<TIn>& x, int chunk, DiagStage<TIn>& st) {
+#pragma unroll
+    for (int j = kI; j < kXABlocks<kOut, TIn>; j += kDLoaders) issue_xa_block<kOut>(x, chunk, j, st);
+}
+template <int kI, typename TIn>
+__device__ __forceinline__ void issue_ft(const DiagCtx<TIn>& x, int chunk, DiagStage<TIn>& st) {
+    const unsigned char* F = diag_factors(x, chunk);
+#pragma unroll
+    for (int j = kI; j < kFTBlocks; j += kDLoaders)
+        dma16(F + kDOffTb + 1024 * j + 16 * x.l, reinterpret_cast<char*>(st.Tb) + 1024 * j);
+}
+template <int kI, bool kOut, typename TIn>
+__device__ __forceinline__ void issue_fk(const DiagCtx<TIn>& x, int chunk, DiagStage<TIn>& st) {
+#pragma unroll
+    for (int j = kI; j < kFKBlocks<kOut>; j += kDLoaders) issue_fk_block<kOut>(x, chunk, j, st);
+}
 
-// hi*hi + hi*lo + lo*hi over `nb` k blocks: A from registers, B from LDS
+// Touch this slice's eighth of a chunk's factor lines (the 8 slices of a
+// head share them through their XCD's L2): lines s + 8 u, u in 64 kHalf ..
+// 64 kHalf + 63, one per lane.
+template <int kHalf, typename TIn>
+__device__ __forceinline__ void touch_diag(const DiagCtx<TIn>& x, int chunk, float* sink) {
+    const int u = 64 * kHalf + x.l;
+    dma4(diag_factors(x, chunk) + 128 * (x.s + 8 * u), sink);
+}
+
+// Before each barrier a loader waits until only what it issued after the
+// part read next may still be in flight (loads complete in issue order):
+// loaders 0 and 1 also issue one L2 touch right after each XA part.
+template <int kI, bool kOut, typename TIn>
+__device__ void diag_loader(const DiagCtx<TIn>& x, int c0, int c_end, DiagLds<TIn>& S) {
+    constexpr int kT = kI < 2 ? 1 : 0;
+    constexpr int nXA = loader_share(kXABlocks<kOut, TIn>, kI);
+    constexpr int nFT = loader_share(kFTBlocks, kI);
+    constexpr int nFK = loader_share(kFKBlocks<kOut>, kI);
+    const int last = c_end - 1;
+    auto cl = [last](int c) { return c < last ? c : last; };
+    if constexpr (kI < 2) {
+#pragma unroll
+        for (int d = 1; d < kDPfAhead; ++d) touch_diag<kI>(x, cl(c0 + d), S.sink);
+    }
+    issue_xa<kI, kOut>(x, c0, S.st);
+    if constexpr (kI < 2) touch_diag<kI>(x, cl(c0 + kDPfAhead), S.sink);
+    issue_ft<kI>(x, c0, S.st);
+    for (int c = c0; c < c_end; ++c) {
+        wait_vm<kT + nFT>();               // XA(c) has landed
+        __builtin_amdgcn_s_barrier();      // A
+        issue_fk<kI, kOut>(x, c, S.st);    // FK was last read in the previous P4
+        wait_vm<nFK>();                    // FT(c) has landed
+        __builtin_amdgcn_s_barrier();      // B
+        issue_xa<kI, kOut>(x, cl(c + 1), S.st);
+        if constexpr (kI < 2) touch_diag<kI>(x, cl(c + 1 + kDPfAhead), S.sink);
+        wait_vm<nXA + kT>();               // FK(c) has landed
+        __builtin_amdgcn_s_barrier();      // C
+        issue_ft<kI>(x, cl(c + 1), S.st);
+    }
+    wait_vm<0>();   // nothing may land in LDS after the workgroup ends
+}
+
+// ---- compute waves -------------------------------------------------------------
+
+// hi*hi + hi*lo + lo*hi over `nb` k blocks: A operands from the packed stage
+// blocks P[(base + m) * 2 + hl], B operands from an exchange buffer
 template <int nb>
-__device__ __forceinline__ f32x4 prod3(const bf16x8 (*a)[2], u32x4 (*B)[2][64], int l) {
+__device__ __forceinline__ f32x4 prod3(const u32x4 (*P)[64], int base, u32x4 (*B)[2][64], int l) {
+    bf16x8 a[nb][2];
+#pragma unroll
+    for (int m = 0; m < nb; ++m) {
+        a[m][0] = __builtin_bit_cast(bf16x8, P[(base + m) * 2][l]);
+        a[m][1] = __builtin_bit_cast(bf16x8, P[(base + m) * 2 + 1][l]);
+    }
     f32x4 p0 = zero4(), p1 = zero4(), p2 = zero4();
 #pragma unroll
     for (int m = 0; m < nb; ++m) {
@@ -453,54 +538,53 @@ __device__ __forceinline__ f32x4 prod3(const bf16x8 (*a)[2], u32x4 (*B)[2][64], 
     return p0 + p1 + p2;
 }
 
-// One chunk; `cur` holds its operands and is refilled with chunk `next`
-// as each part is consumed.  Without outputs (kOut false) the output waves
-// only carry their state tiles; zero_v takes every value as zero (the walk
-// then applies the chunks' transition alone).
+// One chunk.  Wave w keeps the state's key tile w (16 keys x 16 values) in
+// an MFMA accumulator; waves 0-3 also take token tile w through the errors
+// and U, waves 4-7 token tile w - 4 through the outputs.  Without outputs
+// (kOut false) the output waves only carry their state tiles; zero_v takes
+// every value as zero (the walk then applies the chunks' transition alone).
 template <bool kOut, typename TIn>
-__device__ __forceinline__ void diag_step(DiagOps<TIn>& cur, f32x4& acc, const DiagCtx<TIn>& x,
-                                          int next, DiagLds& S, float* __restrict__ o,
+__device__ __forceinline__ void diag_step(const DiagCtx<TIn>& x, int w, int t0, int len,
+                                          DiagLds<TIn>& S, f32x4& acc, float* __restrict__ o,
                                           bool zero_v) {
-    const int w = x.w, l = x.l, g = l >> 4, c = l & 15, tt = w & 3;
+    const int l = x.l, g = l >> 4, c = l & 15, tt = w & 3;
     const bool state = w < 4;
     // P1
     publish4(S.Sx, w, l, acc);
-    __syncthreads();
+    __syncthreads();   // A
     // P2
     f32x4 yz = zero4();
-    if (kOut || state) yz = prod3<4>(cur.xa, S.Sx, l);
     if (state) {
-        const f32x4 vv = zero_v ? zero4()
-                                : f32x4{in_f32(cur.vraw[0]), in_f32(cur.vraw[1]),
-                                        in_f32(cur.vraw[2]), in_f32(cur.vraw[3])};
+        yz = prod3<4>(S.st.Kt, tt * 4, S.Sx, l);
+        f32x4 vv = zero4();
+        if (!zero_v) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vv[i] = in_f32(S.st.V[(16 * tt + 4 * g + i) * 16 + c]);
+        }
         publish4(S.Ex, tt, l, vv - yz);
+    } else if (kOut) {
+        yz = prod3<4>(S.st.Qt, tt * 4, S.Sx, l);
     }
-    load_xa(cur, x, next);
-    __builtin_amdgcn_sched_barrier(0);   // keep the prefetch here: never sink it to its use
-    __syncthreads();
+    __syncthreads();   // B
     // P3
-    if (state) publish4(S.Ux, tt, l, prod3<2>(cur.fa, S.Ex, l));
-    __syncthreads();
+    if (state) publish4(S.Ux, tt, l, prod3<2>(S.st.Tb, tt * 2, S.Ex, l));
+    __syncthreads();   // C
     // P4
-    const f32x4 upd = prod3<2>(cur.kh, S.Ux, l);
-    acc = acc * cur.gc + upd;
+    const f32x4 upd = prod3<2>(S.st.Kh, w * 2, S.Ux, l);
+    const f32x4 gc = *reinterpret_cast<const f32x4*>(S.st.GC + 16 * w + 4 * g);
+    acc = acc * gc + upd;
     if (kOut && !state) {
-        const f32x4 ov = yz + prod3<2>(cur.fa, S.Ux, l);
-        const int t0 = cur.t0, len = cur.len;
+        const f32x4 ov = yz + prod3<2>(S.st.Am, tt * 2, S.Ux, l);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int tok = 16 * tt + 4 * g + i;
             if (tok < len) o[((size_t(t0) + tok) * x.H + x.h) * kD + 16 * x.s + c] = ov[i];
         }
     }
-    load_fa(cur, x, next);
-    load_kh(cur, x, next);
-    load_rec_v(cur, x, next);
-    __builtin_amdgcn_sched_barrier(0);
 }
 
 template <bool kOut, typename TIn>
-__global__ __launch_bounds__(kDWaves * 64) void walk_diag_kernel(
+__global__ __launch_bounds__(kDThreads) void walk_diag_kernel(
     const TIn* __restrict__ v, int N, int H, const int32_t* __restrict__ rec,
     const int32_t* __restrict__ seq_off, const int32_t* __restrict__ num_chunks,
     const unsigned char* __restrict__ factors, float* __restrict__ o, WalkJob j0, WalkJob j1,
@@ -520,7 +604,7 @@ __global__ __launch_bounds__(kDWaves * 64) void walk_diag_kernel(
     const int n = p / H, h = p - n * H;
     const int tid = threadIdx.x;
     const int w = wave_id(), l = tid & 63, g = l >> 4, c = l & 15;
-    __shared__ __attribute__((aligned(16))) DiagLds lds;
+    __shared__ __attribute__((aligned(16))) DiagLds<TIn> lds;
 
     // sequence n's chunks: from the table, or the n-th run of seg_chunks
     const int nch = num_chunks[0];
@@ -537,7 +621,23 @@ __global__ __launch_bounds__(kDWaves * 64) void walk_diag_kernel(
         t_begin = rec[4 * c_begin + 1];
         t_end = rec[4 * (c_end - 1) + 1] + rec[4 * (c_end - 1) + 2];
     }
-    const DiagCtx<TIn> x{v, factors, H, h, s, w, l, c_begin, t_begin, t_end};
+    const DiagCtx<TIn> x{v, factors, H, h, s, l, c_begin, t_begin, t_end};
+
+    if (w >= kDCompute) {
+        if (c_begin < c_end) {
+            switch (w - kDCompute) {
+                case 0: diag_loader<0, kOut>(x, c_begin, c_end, lds); break;
+                case 1: diag_loader<1, kOut>(x, c_begin, c_end, lds); break;
+                case 2: diag_loader<2, kOut>(x, c_begin, c_end, lds); break;
+                case 3: diag_loader<3, kOut>(x, c_begin, c_end, lds); break;
+                case 4: diag_loader<4, kOut>(x, c_begin, c_end, lds); break;
+                case 5: diag_loader<5, kOut>(x, c_begin, c_end, lds); break;
+                case 6: diag_loader<6, kOut>(x, c_begin, c_end, lds); break;
+                default: diag_loader<7, kOut>(x, c_begin, c_end, lds); break;
+            }
+        }
+        return;
+    }
 
     // state: lane holds S^T[key 16w + 4g + i][value 16s + c] = S[value][key .. key+3]
     const size_t srow = ((size_t(n) * H + h) * kD + 16 * s + c) * kD + 16 * w + 4 * g;
@@ -549,21 +649,9 @@ __global__ __launch_bounds__(kDWaves * 64) void walk_diag_kernel(
         acc = *reinterpret_cast<const f32x4*>(J.S0 + srow);
     }
     const bool zero_v = J.zero_v != 0;
-    if (c_begin < c_end) {
-        // two operand sets in turn, a pair of chunks per iteration (no exit
-        // between the two steps, so the loads pending at the loop head are
-        // the same on every path and the compiler's waits stay exact), and
-        // an odd last chunk after the loop
-        DiagOps<TIn> A, B;
-        const int last = c_end - 1;
-        load_all(A, x, c_begin);
-        load_all(B, x, c_begin + 1 < c_end ? c_begin + 1 : last);
-        int ch = c_begin;
-        for (; ch + 1 < c_end; ch += 2) {
-            diag_step<kOut>(A, acc, x, ch + 2 < c_end ? ch + 2 : last, lds, o, zero_v);
-            diag_step<kOut>(B, acc, x, ch + 3 < c_end ? ch + 3 : last, lds, o, zero_v);
-        }
-        if (ch < c_end) diag_step<kOut>(A, acc, x, last, lds, o, zero_v);
+    for (int ch = c_begin; ch < c_end; ++ch) {
+        const int t0 = t_begin + kC * (ch - c_begin);
+        diag_step<kOut>(x, w, t0, min(kC, t_end - t0), lds, acc, o, zero_v);
     }
     if (J.S_final) *reinterpret_cast<f32x4*>(J.S_final + srow) = acc;
 }
@@ -594,7 +682,7 @@ static void launch_walk_diag_t(const void* v, int32_t num_seqs, int32_t heads, c
                                const int32_t* seq_off, const int32_t* num_chunks,
                                const unsigned char* factors, float* o, WalkJob j0, WalkJob j1,
                                int32_t seg_chunks, unsigned wgrid, hipStream_t stream) {
-    hipLaunchKernelGGL((walk_diag_kernel<kOut, TIn>), dim3(wgrid), dim3(kDWaves * 64), 0, stream,
+    hipLaunchKernelGGL((walk_diag_kernel<kOut, TIn>), dim3(wgrid), dim3(kDThreads), 0, stream,
                        static_cast<const TIn*>(v), num_seqs, heads, rec, seq_off, num_chunks,
                        factors, o, j0, j1, seg_chunks);
 }
