@@ -73,26 +73,31 @@ size_t seg_state_bytes(const SegPlan& sp, int32_t heads) {
 // on the whole chip, (2) one launch whose walk workgroups walk chunks
 // [0, c1) and save the state while prep workgroups on the idle CUs prep the
 // remaining chunks, (3) the walk of chunks [c1, nch) from the saved state.
-// c1 balances (2): a walk chunk step costs about as long as 3 prep items on
-// one CU, so the walk of c1 chunks and the prep of (nch - c1) H items on
-// `idle` CUs take the same time when c1 = nch 3H / (idle + 3H).
+// c1 balances (2): when a walk chunk step costs about as long as r prep
+// items on one CU, the walk of c1 chunks and the prep of (nch - c1) H items
+// on `idle` CUs take the same time when c1 = nch rH / (idle + rH).  r is
+// about 3 for the scalar decay and about 2/11 for the per-channel one (a
+// per-channel prep item takes about 5.5 walk steps).
 constexpr int kOverlapMinChunks = 32;
 constexpr int kOverlapMinIdleCUs = 64;
 constexpr int kPrepItemsPerWalkStep = 3;
+constexpr int kDiagWalkStepsPerPrepItem2 = 11;   // walk steps per per-channel prep item, x 2
 
 struct OverlapPlan {
     int c1 = 0;           // chunks walked in the middle launch (0: no overlap)
     int prep_blocks = 0;  // prep workgroups beside them
 };
 
-OverlapPlan overlap_plan(int32_t num_seqs, int32_t total_tokens, int32_t heads) {
+// rn / rd: r of the comment above as a ratio
+OverlapPlan overlap_plan(int32_t num_seqs, int32_t total_tokens, int32_t heads, int64_t rn = 3,
+                         int64_t rd = 1) {
     OverlapPlan op;
     if (num_seqs != 1 || total_tokens <= 0 || heads <= 0) return op;
     const int64_t nch = (int64_t(total_tokens) + kC - 1) / kC;
     const int64_t idle = kSegCUs - int64_t(kWalkSlices) * heads;
     if (nch < kOverlapMinChunks || idle < kOverlapMinIdleCUs) return op;
-    const int64_t r = int64_t(kPrepItemsPerWalkStep) * heads;
-    int64_t c1 = (nch * r + (idle + r) / 2) / (idle + r);
+    const int64_t r = rn * heads, den = rd * idle + r;
+    int64_t c1 = (nch * r + den / 2) / den;
     c1 = c1 < 8 ? 8 : c1;
     c1 = c1 > nch - 8 ? nch - 8 : c1;
     op.c1 = int(c1);
@@ -112,6 +117,10 @@ int fused_norm_cut(const OverlapPlan& op, int32_t total_tokens) {
     const int tail = nch / 8 > 16 ? nch / 8 : 16;
     const int c2 = nch - tail;
     return c2 >= op.c1 + 8 ? c2 : 0;
+}
+
+OverlapPlan diag_overlap_plan(int32_t num_seqs, int32_t total_tokens, int32_t heads) {
+    return overlap_plan(num_seqs, total_tokens, heads, kDiagWalkStepsPerPrepItem2, 2);
 }
 
 size_t overlap_state_bytes(const OverlapPlan& op, int32_t heads) {
@@ -557,9 +566,13 @@ size_t rda_prefill_diag_workspace_bytes(int32_t num_seqs, int32_t total_tokens,
     const int32_t mc = rda_max_chunks(num_seqs, total_tokens);
     if (mc < 0) return 0;
     const TableLayout tl = table_layout(mc, num_seqs);
-    // one sequence: room for the segmented pass's three state arrays
+    // one sequence: room for the segmented pass's three state arrays or the
+    // overlapped plan's middle state
+    const size_t seg = 3 * seg_state_bytes(seg_plan(num_seqs, total_tokens, num_heads), num_heads);
+    const size_t mid =
+        overlap_state_bytes(diag_overlap_plan(num_seqs, total_tokens, num_heads), num_heads);
     return align256(tl.bytes) + size_t(mc) * size_t(num_heads) * kDiagChunkHeadBytes +
-           3 * seg_state_bytes(seg_plan(num_seqs, total_tokens, num_heads), num_heads);
+           (seg > mid ? seg : mid);
 }
 
 rda_status rda_prefill_diag(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
@@ -629,6 +642,38 @@ rda_status rda_prefill_diag(const void* q, const void* k, const void* v, rda_dty
                 hipSuccess ||
             launch_walk_diag(v, qkv_dtype, sp.P, num_heads, rec, seq_off, nch, factors, o, &last,
                              1, sp.cps, true, stream) != hipSuccess)
+            return RDA_ERR_HIP;
+        return RDA_OK;
+    }
+    const OverlapPlan op = diag_overlap_plan(num_seqs, total_tokens, num_heads);
+    if (op.c1 > 0 && cu_seqlens == nullptr) {
+        // the overlapped plan, as for rda_prefill: the prep of the first c1
+        // chunks; their walk beside the prep of the rest on the idle CUs;
+        // the walk of the rest from the state saved in between
+        float* S_mid = reinterpret_cast<float*>(factors + size_t(mc) * num_heads *
+                                                              kDiagChunkHeadBytes);
+        const int nchunks = (total_tokens + kC - 1) / kC;
+        DiagSide X{};
+        X.c_lo = 0;
+        X.c_hi = op.c1;
+        X.prep_blocks = op.prep_blocks;
+        X.item_lo = op.c1 * num_heads;
+        X.item_hi = nchunks * num_heads;
+        X.q = q;
+        X.k = k;
+        X.alpha = alpha;
+        X.b = b;
+        DiagSide Y{};
+        Y.c_lo = op.c1;
+        Y.c_hi = nchunks;
+        const WalkJob first{S0, S_mid, 0, 0};
+        const WalkJob second{S_mid, S_final, 0, 0};
+        if (launch_prep_diag(q, k, qkv_dtype, alpha, b, num_heads, mc, rec, nch, factors, stream,
+                             op.c1 * num_heads) != hipSuccess ||
+            launch_walk_diag(v, qkv_dtype, 1, num_heads, rec, seq_off, nch, factors, o, &first, 1,
+                             0, true, stream, &X) != hipSuccess ||
+            launch_walk_diag(v, qkv_dtype, 1, num_heads, rec, seq_off, nch, factors, o, &second,
+                             1, 0, true, stream, &Y) != hipSuccess)
             return RDA_ERR_HIP;
         return RDA_OK;
     }

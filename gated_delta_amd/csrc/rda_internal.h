@@ -150,17 +150,31 @@ hipError_t launch_prefill_diag(const void* q, const void* k, const void* v, rda_
                                unsigned char* factors, const float* S0, float* o,
                                float* S_final, hipStream_t stream);
 // Its two stages apart (the segmented state pass runs the walk three times
-// over one prep): the prep, and the walk with jobs, segment runs and the
-// instantiation without outputs as for launch_walk_bf16.
+// over one prep): the prep (of the first item_end (chunk, head) items, all
+// when negative), and the walk with jobs, segment runs and the
+// instantiation without outputs as for launch_walk_bf16.  A walk launch may
+// carry a DiagSide: a chunk range for one sequence (c_hi > 0: walk chunks
+// [c_lo, c_hi) only) and prep workgroups after the walk's that prep items
+// [item_lo, item_hi) of the table on the CUs the walk leaves idle.
+struct DiagSide {
+    int c_lo, c_hi;
+    int prep_blocks;        // prep workgroups (0: none)
+    int item_lo, item_hi;
+    const void* q;
+    const void* k;
+    const float* alpha;
+    const float* b;
+    int walk_blocks;        // set by the launcher
+};
 hipError_t launch_prep_diag(const void* q, const void* k, rda_dtype dt, const float* alpha,
                             const float* b, int32_t heads, int32_t max_chunks, const int32_t* rec,
                             const int32_t* num_chunks, unsigned char* factors,
-                            hipStream_t stream);
+                            hipStream_t stream, int32_t item_end = -1);
 hipError_t launch_walk_diag(const void* v, rda_dtype dt, int32_t num_seqs, int32_t heads,
                             const int32_t* rec, const int32_t* seq_off,
-                            const int32_t* num_chunks, const unsigned char* factors, float* o,
+                            const int32_t* num_chunks, unsigned char* factors, float* o,
                             const WalkJob* jobs, int32_t num_jobs, int32_t seg_chunks,
-                            bool outputs, hipStream_t stream);
+                            bool outputs, hipStream_t stream, const DiagSide* side = nullptr);
 hipError_t launch_decode_diag(const void* q, const void* k, const void* v, rda_dtype dt,
                               const float* alpha, const float* b, int32_t batch, int32_t heads,
                               float* S, float* o, hipStream_t stream);

@@ -137,18 +137,16 @@ struct Row8<float> {
     }
 };
 
+// The prep of items (chunk, head) first, first + stride, ... below `total`
+// (item = chunk * H + head) by one 1024-thread workgroup, which loads the
+// next item's inputs into registers while it works on the current one (one
+// workgroup fills a CU, so nothing else would hide that load's latency).
 template <typename TIn>
-__global__ __launch_bounds__(kPrepThreads) void prep_diag_kernel(
+__device__ __forceinline__ void prep_diag_items(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ alpha,
-    const float* __restrict__ b, int H, const int32_t* __restrict__ rec,
-    const int32_t* __restrict__ num_chunks, unsigned char* __restrict__ factors) {
-    __shared__ __attribute__((aligned(16))) PrepDiagLds<TIn> S;
-    // Persistent: the workgroup takes items (chunk, head) blockIdx.x,
-    // blockIdx.x + gridDim.x, ... and loads the next item's inputs into
-    // registers while it works on the current one (one workgroup fills a CU,
-    // so nothing else would hide that load's latency).
-    const int total = num_chunks[0] * H;
-    int item = blockIdx.x;
+    const float* __restrict__ b, int H, const int32_t* __restrict__ rec, int first, int stride,
+    int total, unsigned char* __restrict__ factors, PrepDiagLds<TIn>& S) {
+    int item = first;
     if (item >= total) return;
 
     // K, Q rows, b, and alpha for (channel, eighth of 8 tokens) of one item;
@@ -187,7 +185,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_diag_kernel(
     const int chunk = item / H;
     const int h = item - chunk * H;
     unsigned char* F = factors + (size_t(chunk) * H + h) * kDiagChunkHeadBytes;
-    const int next = item + int(gridDim.x);
+    const int next = item + stride;
     // ---- stage K, Q (rows past the chunk's end are zero), b; zero T and A;
     //      G = running sum of log2(alpha) per channel, each eighth of the
     //      chunk first on its own, then offset by the eighths before it
@@ -339,6 +337,20 @@ __global__ __launch_bounds__(kPrepThreads) void prep_diag_kernel(
     item = next;
     __syncthreads();   // T, A and the staged rows are rewritten next
     }
+}
+
+// Persistent: workgroup i takes items i, i + gridDim.x, ... of the first
+// item_end items (item_end < 0: all of them).
+template <typename TIn>
+__global__ __launch_bounds__(kPrepThreads) void prep_diag_kernel(
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ alpha,
+    const float* __restrict__ b, int H, const int32_t* __restrict__ rec,
+    const int32_t* __restrict__ num_chunks, unsigned char* __restrict__ factors, int item_end) {
+    __shared__ __attribute__((aligned(16))) PrepDiagLds<TIn> S;
+    int total = num_chunks[0] * H;
+    if (item_end >= 0 && item_end < total) total = item_end;
+    prep_diag_items<TIn>(q, k, alpha, b, H, rec, int(blockIdx.x), int(gridDim.x), total, factors,
+                         S);
 }
 
 // ---------------------------------------------------------------------------
@@ -583,12 +595,29 @@ __device__ __forceinline__ void diag_step(const DiagCtx<TIn>& x, int w, int t0, 
     }
 }
 
+// A walk launch's LDS: the walk's, or (its prep workgroups) the prep's.
+template <typename TIn>
+union DiagWalkOrPrepLds {
+    DiagLds<TIn> walk;
+    PrepDiagLds<TIn> prep;
+};
+
 template <bool kOut, typename TIn>
 __global__ __launch_bounds__(kDThreads) void walk_diag_kernel(
     const TIn* __restrict__ v, int N, int H, const int32_t* __restrict__ rec,
     const int32_t* __restrict__ seq_off, const int32_t* __restrict__ num_chunks,
-    const unsigned char* __restrict__ factors, float* __restrict__ o, WalkJob j0, WalkJob j1,
-    int seg_chunks) {
+    unsigned char* __restrict__ factors, float* __restrict__ o, WalkJob j0, WalkJob j1,
+    int seg_chunks, DiagSide X) {
+    __shared__ __attribute__((aligned(16))) DiagWalkOrPrepLds<TIn> shm;
+    if (int(blockIdx.x) >= X.walk_blocks) {
+        // the prep of later chunks, on the CUs the walk leaves idle
+        prep_diag_items<TIn>(static_cast<const TIn*>(X.q), static_cast<const TIn*>(X.k),
+                             X.alpha, X.b, H, rec,
+                             X.item_lo + int(blockIdx.x) - X.walk_blocks, X.prep_blocks,
+                             X.item_hi, factors, shm.prep);
+        return;
+    }
+    DiagLds<TIn>& lds = shm.walk;
     // Jobs split the grid in halves.  Within a job the mapping is XCD-aware:
     // the 8 value slices of one (sequence, head) share the same
     // blockIdx.x % 8, hence one XCD and its L2, which holds the chunk
@@ -604,7 +633,6 @@ __global__ __launch_bounds__(kDThreads) void walk_diag_kernel(
     const int n = p / H, h = p - n * H;
     const int tid = threadIdx.x;
     const int w = wave_id(), l = tid & 63, g = l >> 4, c = l & 15;
-    __shared__ __attribute__((aligned(16))) DiagLds<TIn> lds;
 
     // sequence n's chunks: from the table, or the n-th run of seg_chunks
     const int nch = num_chunks[0];
@@ -615,6 +643,10 @@ __global__ __launch_bounds__(kDThreads) void walk_diag_kernel(
     } else {
         c_begin = seq_off[n];
         c_end = seq_off[n + 1] < nch ? seq_off[n + 1] : nch;
+    }
+    if (X.c_hi > 0) {   // one sequence walked over chunks [c_lo, c_hi) only
+        c_begin = X.c_lo < nch ? X.c_lo : nch;
+        c_end = X.c_hi < nch ? X.c_hi : nch;
     }
     int t_begin = 0, t_end = 0;
     if (c_begin < c_end) {
@@ -661,55 +693,64 @@ __global__ __launch_bounds__(kDThreads) void walk_diag_kernel(
 hipError_t launch_prep_diag(const void* q, const void* k, rda_dtype dt, const float* alpha,
                             const float* b, int32_t heads, int32_t max_chunks, const int32_t* rec,
                             const int32_t* num_chunks, unsigned char* factors,
-                            hipStream_t stream) {
+                            hipStream_t stream, int32_t item_end) {
     // one persistent workgroup per CU at most (each holds a CU's LDS)
-    const int64_t items = int64_t(max_chunks) * heads;
+    int64_t items = int64_t(max_chunks) * heads;
+    if (item_end >= 0 && item_end < items) items = item_end;
     const unsigned pgrid = unsigned(items < kPrepDiagGrid ? items : kPrepDiagGrid);
     if (pgrid == 0) return hipSuccess;
     if (dt == RDA_BF16)
         hipLaunchKernelGGL(prep_diag_kernel<uint16_t>, dim3(pgrid), dim3(kPrepThreads), 0, stream,
                            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), alpha,
-                           b, heads, rec, num_chunks, factors);
+                           b, heads, rec, num_chunks, factors, item_end);
     else
         hipLaunchKernelGGL(prep_diag_kernel<float>, dim3(pgrid), dim3(kPrepThreads), 0, stream,
                            static_cast<const float*>(q), static_cast<const float*>(k), alpha, b,
-                           heads, rec, num_chunks, factors);
+                           heads, rec, num_chunks, factors, item_end);
     return hipGetLastError();
 }
 
 template <bool kOut, typename TIn>
 static void launch_walk_diag_t(const void* v, int32_t num_seqs, int32_t heads, const int32_t* rec,
                                const int32_t* seq_off, const int32_t* num_chunks,
-                               const unsigned char* factors, float* o, WalkJob j0, WalkJob j1,
-                               int32_t seg_chunks, unsigned wgrid, hipStream_t stream) {
-    hipLaunchKernelGGL((walk_diag_kernel<kOut, TIn>), dim3(wgrid), dim3(kDThreads), 0, stream,
+                               unsigned char* factors, float* o, WalkJob j0, WalkJob j1,
+                               int32_t seg_chunks, unsigned grid, const DiagSide& X,
+                               hipStream_t stream) {
+    hipLaunchKernelGGL((walk_diag_kernel<kOut, TIn>), dim3(grid), dim3(kDThreads), 0, stream,
                        static_cast<const TIn*>(v), num_seqs, heads, rec, seq_off, num_chunks,
-                       factors, o, j0, j1, seg_chunks);
+                       factors, o, j0, j1, seg_chunks, X);
 }
 
 hipError_t launch_walk_diag(const void* v, rda_dtype dt, int32_t num_seqs, int32_t heads,
                             const int32_t* rec, const int32_t* seq_off,
-                            const int32_t* num_chunks, const unsigned char* factors, float* o,
+                            const int32_t* num_chunks, unsigned char* factors, float* o,
                             const WalkJob* jobs, int32_t num_jobs, int32_t seg_chunks,
-                            bool outputs, hipStream_t stream) {
+                            bool outputs, hipStream_t stream, const DiagSide* side) {
     const int64_t pairs = int64_t(num_seqs) * heads;
     const unsigned wgrid = unsigned(num_jobs * 64 * ((pairs + 7) / 8));
+    DiagSide X{};
+    if (side) X = *side;
+    X.walk_blocks = int(wgrid);
+    const unsigned grid = wgrid + unsigned(side ? side->prep_blocks : 0);
     const WalkJob none{nullptr, nullptr, 0, 0};
     const WalkJob j1 = num_jobs > 1 ? jobs[1] : none;
     if (dt == RDA_BF16) {
         if (outputs)
             launch_walk_diag_t<true, uint16_t>(v, num_seqs, heads, rec, seq_off, num_chunks,
-                                               factors, o, jobs[0], j1, seg_chunks, wgrid, stream);
+                                               factors, o, jobs[0], j1, seg_chunks, grid, X,
+                                               stream);
         else
             launch_walk_diag_t<false, uint16_t>(v, num_seqs, heads, rec, seq_off, num_chunks,
-                                                factors, o, jobs[0], j1, seg_chunks, wgrid, stream);
+                                                factors, o, jobs[0], j1, seg_chunks, grid, X,
+                                                stream);
     } else {
         if (outputs)
             launch_walk_diag_t<true, float>(v, num_seqs, heads, rec, seq_off, num_chunks, factors,
-                                            o, jobs[0], j1, seg_chunks, wgrid, stream);
+                                            o, jobs[0], j1, seg_chunks, grid, X, stream);
         else
             launch_walk_diag_t<false, float>(v, num_seqs, heads, rec, seq_off, num_chunks,
-                                             factors, o, jobs[0], j1, seg_chunks, wgrid, stream);
+                                             factors, o, jobs[0], j1, seg_chunks, grid, X,
+                                             stream);
     }
     return hipGetLastError();
 }

@@ -142,6 +142,28 @@ def test_decay_regimes(dev, kind):
     assert_parity("S_final", to_host(S), rS)
 
 
+@pytest.mark.parametrize("T,H,bf16", [(2048, 16, True), (4097, 8, True), (3000, 12, True),
+                                      (2100, 16, False)])
+def test_overlapped_plan_matches_one_pass(dev, T, H, bf16):
+    """One sequence without offsets whose walk leaves CUs idle runs the
+    overlapped plan (the prep of the first chunks, then their walk beside
+    the prep of the rest on the idle CUs, then the rest of the walk); with
+    cu_seqlens = {0, T} the same sizes run prep then one walk.  Both give the
+    same bits, and the plan meets the oracle."""
+    import dataclasses
+    p = synth.make_prefill(T, H, bf16=bf16, s0_std=0.02, key=(613, T, H))
+    alpha = synth.diag_alpha(T, H, key=(613, T, H))
+    say(f"[prefill_diag] overlapped plan vs one pass T={T} H={H} bf16={bf16}")
+    o1, S1 = (to_host(x) for x in run_gpu(p, alpha, dev))
+    one = dataclasses.replace(p, cu_seqlens=np.array([0, T], np.int32))
+    o2, S2 = (to_host(x) for x in run_gpu(one, alpha, dev))
+    assert np.array_equal(o1, o2), "o differs from the one-pass walk"
+    assert np.array_equal(S1, S2), "S_final differs from the one-pass walk"
+    ro, rS = oracle.prefill_diag(p.q, p.k, p.v, alpha, p.b, S0=p.S0)
+    assert_parity("overlapped o", o1, ro)
+    assert_parity("overlapped S_final", S1, rS)
+
+
 def test_long_prompt(dev):
     """The long prompt with per-channel decay: T = 16384, H = 16."""
     p, alpha = case(16384, 16, (604,))
