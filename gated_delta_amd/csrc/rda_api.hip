@@ -324,9 +324,9 @@ rda_status prefill_overlapped(const Prefill& P, hipStream_t stream, hipEvent_t c
 rda_status prefill_sequential(const Prefill& P, hipStream_t stream, hipEvent_t const* ev) {
     if (P.ovl.c1 > 0) return prefill_overlapped(P, stream, ev);
     rda_status st;
-    // one bf16 sequence without offsets: the prep kernel derives each chunk's
+    // one sequence without offsets: the prep kernel derives each chunk's
     // record itself and writes the table, which saves the table launch
-    const bool table_in_prep = P.cu == nullptr && P.dt == RDA_BF16 && P.T > 0;
+    const bool table_in_prep = P.cu == nullptr && P.T > 0;
     if ((st = record(ev, 2 * RDA_STAGE_TABLE, stream)) != RDA_OK) return st;
     if (!table_in_prep &&
         launch_chunk_table(P.cu, P.N, P.T, P.mc, P.rec, P.seq_off, P.nch, stream) != hipSuccess)
@@ -334,9 +334,8 @@ rda_status prefill_sequential(const Prefill& P, hipStream_t stream, hipEvent_t c
     if ((st = record(ev, 2 * RDA_STAGE_TABLE + 1, stream)) != RDA_OK) return st;
     if ((st = record(ev, 2 * RDA_STAGE_PREP, stream)) != RDA_OK) return st;
     if (table_in_prep) {
-        if (launch_prep_bf16(static_cast<const uint16_t*>(P.q), static_cast<const uint16_t*>(P.k),
-                             P.a, P.b, P.H, P.mc, nullptr, nullptr, P.factors, P.T, P.rec,
-                             P.seq_off, P.nch, stream) != hipSuccess)
+        if (launch_prep(P.q, P.k, P.dt, P.a, P.b, P.H, P.mc, nullptr, nullptr, P.factors, stream,
+                        P.T, P.rec, P.seq_off, P.nch) != hipSuccess)
             return RDA_ERR_HIP;
     } else if (P.mc > 0 && P.T > 0) {
         if (launch_prep(P.q, P.k, P.dt, P.a, P.b, P.H, P.mc, P.rec, P.nch, P.factors, stream) !=

@@ -199,16 +199,37 @@ hipError_t launch_norm_gate(const float* o, const void* g, rda_dtype g_dtype, co
                             float eps, int32_t act, int64_t rows, void* out, rda_dtype out_dtype,
                             hipStream_t stream, const uint16_t* o_enc = nullptr);
 
+// The prep for either input type.  single_T >= 0: one sequence of single_T
+// tokens without offsets, whose table the prep writes (rec_out,
+// seq_off_out, num_out) instead of reading rec / num_chunks.
 hipError_t launch_prep(const void* q, const void* k, rda_dtype dt,
                        const float* a, const float* b, int32_t heads, int32_t max_chunks,
                        const int32_t* rec, const int32_t* num_chunks, unsigned char* factors,
-                       hipStream_t stream);
+                       hipStream_t stream, int32_t single_T = -1, int32_t* rec_out = nullptr,
+                       int32_t* seq_off_out = nullptr, int32_t* num_out = nullptr);
 
 hipError_t launch_walk(const void* q, const void* k, const void* v, rda_dtype dt,
                        int32_t num_seqs, int32_t heads, const int32_t* rec,
                        const int32_t* seq_off, const int32_t* num_chunks,
                        const unsigned char* factors, const float* S0, OutSink out,
                        float* S_final, hipStream_t stream);
+
+// Chunk `chunk`'s record for one sequence of single_T tokens and no offsets
+// (plain arithmetic), written by the prep of head 0 of each chunk; chunk 0's
+// also writes the sequence offsets and the chunk count nch.
+__device__ __forceinline__ void prep_table_entry(int chunk, int t0, int len, int nch, int tid,
+                                                 int32_t* rec_out, int32_t* seq_off_out,
+                                                 int32_t* num_out) {
+    if (tid < 4) {
+        const int32_t field[4] = {0, t0, len, chunk};
+        rec_out[4 * chunk + tid] = field[tid];
+        if (chunk == 0) {
+            if (tid == 0) seq_off_out[0] = 0;
+            if (tid == 1) seq_off_out[1] = nch;
+            if (tid == 2) num_out[0] = nch;
+        }
+    }
+}
 
 // bf16 prep (factors from LDS-DMA'd tiles, four workgroups per CU).  With
 // single_T >= 0 the input is one sequence of single_T tokens without offsets:

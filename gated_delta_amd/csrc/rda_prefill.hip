@@ -124,15 +124,28 @@ template <bool kSplit>
 __global__ __launch_bounds__(256) void prep_kernel(
     const typename PrepIn<kSplit>::T* __restrict__ q, const typename PrepIn<kSplit>::T* __restrict__ k,
     const float* __restrict__ a, const float* __restrict__ b, int H, const int32_t* __restrict__ rec,
-    const int32_t* __restrict__ num_chunks, unsigned char* __restrict__ factors) {
+    const int32_t* __restrict__ num_chunks, unsigned char* __restrict__ factors, int32_t single_T,
+    int32_t* __restrict__ rec_out, int32_t* __restrict__ seq_off_out, int32_t* __restrict__ num_out) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[kSplit ? kPrepSmemSplit : kPrepSmemBf16];
     const int chunk = blockIdx.x / H;
     const int h = blockIdx.x - chunk * H;
-    if (chunk >= num_chunks[0]) return;
-    const int64_t t0 = rec[4 * chunk + 1];
-    const int len = rec[4 * chunk + 2];
-
     const int tid = threadIdx.x;
+    int64_t t0;
+    int len;
+    if (single_T >= 0) {
+        // one sequence of single_T tokens and no offsets: the records are
+        // plain arithmetic, and the head-0 workgroups write the table
+        const int nch = (single_T + kC - 1) / kC;
+        if (chunk >= nch) return;
+        t0 = int64_t(kC) * chunk;
+        len = single_T - int(t0) < kC ? single_T - int(t0) : kC;
+        if (h == 0) prep_table_entry(chunk, int(t0), len, nch, tid, rec_out, seq_off_out, num_out);
+    } else {
+        if (chunk >= num_chunks[0]) return;
+        t0 = rec[4 * chunk + 1];
+        len = rec[4 * chunk + 2];
+    }
+
     const int w = wave_id(), l = tid & 63, g = l >> 4, c = l & 15;
 
     uint16_t* Ks = reinterpret_cast<uint16_t*>(smem + kSmK);
@@ -667,17 +680,20 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(
 
 hipError_t launch_prep(const void* q, const void* k, rda_dtype dt, const float* a,
                        const float* b, int32_t heads, int32_t max_chunks, const int32_t* rec,
-                       const int32_t* num_chunks, unsigned char* factors, hipStream_t stream) {
+                       const int32_t* num_chunks, unsigned char* factors, hipStream_t stream,
+                       int32_t single_T, int32_t* rec_out, int32_t* seq_off_out,
+                       int32_t* num_out) {
     const unsigned grid = unsigned(int64_t(max_chunks) * heads);
     if (grid == 0) return hipSuccess;
     if (dt == RDA_BF16) {
         return launch_prep_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), a,
-                                b, heads, max_chunks, rec, num_chunks, factors, -1, nullptr,
-                                nullptr, nullptr, stream);
+                                b, heads, max_chunks, rec, num_chunks, factors, single_T, rec_out,
+                                seq_off_out, num_out, stream);
     } else {
         hipLaunchKernelGGL(prep_kernel<true>, dim3(grid), dim3(256), 0, stream,
                            static_cast<const float*>(q), static_cast<const float*>(k), a, b,
-                           heads, rec, num_chunks, factors);
+                           heads, rec, num_chunks, factors, single_T, rec_out, seq_off_out,
+                           num_out);
     }
     return hipGetLastError();
 }

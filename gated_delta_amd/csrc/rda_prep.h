@@ -42,23 +42,6 @@ static_assert(sizeof(PrepLds) <= 40 * 1024, "four workgroups per CU");
 
 typedef WalkPrepArgs PrepArgs;   // inputs and the factors' base
 
-// Chunk `chunk`'s record for one sequence of single_T tokens and no offsets
-// (plain arithmetic), written by the head-0 item of each chunk; chunk 0's
-// also writes the sequence offsets and the chunk count nch.
-__device__ __forceinline__ void prep_table_entry(int chunk, int t0, int len, int nch, int tid,
-                                                 int32_t* rec_out, int32_t* seq_off_out,
-                                                 int32_t* num_out) {
-    if (tid < 4) {
-        const int32_t field[4] = {0, t0, len, chunk};
-        rec_out[4 * chunk + tid] = field[tid];
-        if (chunk == 0) {
-            if (tid == 0) seq_off_out[0] = 0;
-            if (tid == 1) seq_off_out[1] = nch;
-            if (tid == 2) num_out[0] = nch;
-        }
-    }
-}
-
 // One item by one 256-thread group: `tid` 0..255 and `w` = tid / 64 (a
 // wave-uniform value).  With valid false the group loads and stores nothing
 // but passes the same workgroup barriers (the walk's prep workgroups run

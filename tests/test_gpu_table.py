@@ -65,17 +65,19 @@ def _align256(x):
 
 
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 1000, 16384])
-def test_prep_written_table_single_sequence(dev, T):
-    """One bf16 sequence without offsets: the prep kernel writes the chunk
-    table itself (no table kernel runs).  Read it back from the workspace
+@pytest.mark.parametrize("bf16", [True, False])
+def test_prep_written_table_single_sequence(dev, T, bf16):
+    """One sequence without offsets (bf16 or fp32 inputs): the prep kernel
+    writes the chunk table itself (no table kernel runs).  Read it back from the workspace
     (library-internal layout: records at 0, then sequence offsets and the
     chunk count at the next 256-byte boundaries) and compare with the integer
     reference; the workspace starts filled with a byte pattern so that a
     missing write shows."""
     H = 2
-    say(f"[table] prep-written T={T}")
-    p = synth.make_prefill(T, H, bf16=True, key=(900, T))
-    q, k, v = (torch.from_numpy(getattr(p, n)).to(dev).to(torch.bfloat16) for n in "qkv")
+    say(f"[table] prep-written T={T} bf16={bf16}")
+    p = synth.make_prefill(T, H, bf16=bf16, key=(900, T))
+    dt = torch.bfloat16 if bf16 else torch.float32
+    q, k, v = (torch.from_numpy(getattr(p, n)).to(dev).to(dt) for n in "qkv")
     a, b = (torch.from_numpy(x).to(dev) for x in (p.a, p.b))
     mc = table_ref.max_chunks(1, T)
     ws = torch.full((rda.rda_prefill_workspace_bytes(1, T, H),), 0x5A, dtype=torch.uint8,
