@@ -258,7 +258,7 @@ rda_status prefill_overlapped(const Prefill& P, hipStream_t stream, hipEvent_t c
     const auto* v16 = static_cast<const uint16_t*>(P.v);
     const int nch = (P.T + kC - 1) / kC;
     const int c1 = P.ovl.c1;
-    WalkPrep X{};
+    WalkSide X{};
     X.c_lo = 0;
     X.c_hi = c1;
     X.prep_blocks = P.ovl.prep_blocks;
@@ -266,20 +266,20 @@ rda_status prefill_overlapped(const Prefill& P, hipStream_t stream, hipEvent_t c
     X.item_hi = nch * P.H;
     X.single_T = P.T;
     X.nch = nch;
-    X.args = WalkPrepArgs{q16, k16, P.a, P.b, P.H, P.factors};
+    X.args = PrepItemArgs{q16, k16, P.a, P.b, P.H, P.factors};
     X.rec_out = P.rec;
     X.seq_off_out = P.seq_off;
     X.num_out = P.nch;
     // the fused output norm: the rows of chunks already walked, on the CUs a
     // later walk launch leaves idle (see fused_norm_cut)
     const int c2 = P.norm.y ? fused_norm_cut(P.ovl, P.T) : 0;
-    auto norm_rows = [&](WalkPrep& Z, int lo, int hi) {
+    auto norm_rows = [&](WalkSide& Z, int lo, int hi) {
         Z.norm = P.norm;
         Z.norm.row_lo = int64_t(kC) * lo * P.H;
         Z.norm.row_hi = int64_t(kC) * hi * P.H;
         Z.norm.blocks = P.ovl.prep_blocks;
     };
-    WalkPrep Y{}, Y2{};
+    WalkSide Y{}, Y2{};
     Y.c_lo = c1;
     Y.c_hi = c2 > 0 ? c2 : nch;
     if (P.norm.y) norm_rows(Y, 0, c1);

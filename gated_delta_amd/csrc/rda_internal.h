@@ -249,12 +249,8 @@ hipError_t launch_prep_bf16(const uint16_t* q, const uint16_t* k, const float* a
 
 // bf16 walk (operands streamed into LDS by loader waves)
 
-// Extra work a walk launch may carry (rda_prep.h's args, so forward-declared
-// as plain pointers here): a chunk range for one sequence (c_hi > 0: walk
-// chunks [c_lo, c_hi) only), and prep workgroups after the walk's that run
-// the prep items [item_lo, item_hi) of one sequence of single_T tokens and
-// write their table entries (nch = the sequence's chunk count).
-struct WalkPrepArgs {
+// The inputs of one bf16 prep item (rda_prep.h) and the factors' base.
+struct PrepItemArgs {
     const uint16_t* q;
     const uint16_t* k;
     const float* a;
@@ -277,12 +273,17 @@ struct WalkNorm {
     int64_t row_lo, row_hi;
     int blocks;             // norm workgroups (0: none)
 };
-struct WalkPrep {
+// Extra work a walk launch may carry: a chunk range for one sequence
+// (c_hi > 0: walk chunks [c_lo, c_hi) only); prep workgroups after the
+// walk's that run the prep items [item_lo, item_hi) of one sequence of
+// single_T tokens and write their table entries (nch = the sequence's chunk
+// count); and norm workgroups after those (WalkNorm).
+struct WalkSide {
     int c_lo, c_hi;
     int prep_blocks;        // prep workgroups (0: none)
     int item_lo, item_hi;
     int single_T, nch;
-    WalkPrepArgs args;
+    PrepItemArgs args;
     int32_t *rec_out, *seq_off_out, *num_out;
     WalkNorm norm;
     int walk_blocks;        // set by the launcher
@@ -298,7 +299,7 @@ hipError_t launch_walk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t
                             const int32_t* seq_off, const int32_t* num_chunks,
                             const unsigned char* factors, OutSink out, const WalkJob* jobs,
                             int32_t num_jobs, int32_t seg_chunks, bool outputs,
-                            hipStream_t stream, const WalkPrep* extra = nullptr);
+                            hipStream_t stream, const WalkSide* extra = nullptr);
 
 // The segment combine of the segmented state pass, per head and value row:
 // S_in[0] = S0 (zero when null); for p < P: with E_p = segment p's final

@@ -40,13 +40,11 @@ struct PrepLds {
 
 static_assert(sizeof(PrepLds) <= 40 * 1024, "four workgroups per CU");
 
-typedef WalkPrepArgs PrepArgs;   // inputs and the factors' base
-
 // One item by one 256-thread group: `tid` 0..255 and `w` = tid / 64 (a
 // wave-uniform value).  With valid false the group loads and stores nothing
 // but passes the same workgroup barriers (the walk's prep workgroups run
 // four groups in step).
-__device__ __forceinline__ void prep_item(const PrepArgs& A, int chunk, int h, int t0, int len,
+__device__ __forceinline__ void prep_item(const PrepItemArgs& A, int chunk, int h, int t0, int len,
                                           bool valid, PrepLds& S, int tid, int w) {
     const uint16_t* __restrict__ q = A.q;
     const uint16_t* __restrict__ k = A.k;

@@ -8,7 +8,7 @@ namespace rda {
 
 namespace {
 
-__global__ __launch_bounds__(256) void prep_bf16_kernel(PrepArgs A,
+__global__ __launch_bounds__(256) void prep_bf16_kernel(PrepItemArgs A,
                                                         const int32_t* __restrict__ rec,
                                                         const int32_t* __restrict__ num_chunks,
                                                         int32_t single_T, int32_t chunk_begin,
@@ -54,7 +54,7 @@ hipError_t launch_prep_bf16(const uint16_t* q, const uint16_t* k, const float* a
     }
     const unsigned grid = unsigned(int64_t(chunk_count) * heads);
     if (grid == 0) return hipSuccess;
-    const PrepArgs A{q, k, a, b, heads, factors};
+    const PrepItemArgs A{q, k, a, b, heads, factors};
     hipLaunchKernelGGL(prep_bf16_kernel, dim3(grid), dim3(256), 0, stream, A, rec, num_chunks,
                        single_T, chunk_begin, nch_total, rec_out, seq_off_out, num_out);
     return hipGetLastError();

@@ -433,7 +433,7 @@ __device__ __forceinline__ void output_step(const Ctx& x, int tt, int ch, const 
 // The prep workgroups of a launch: prep items [item_lo, item_hi) (item =
 // chunk * H + head) of one sequence of single_T tokens without offsets, four
 // consecutive items per round, writing their chunks' table entries too.
-__device__ void prep_role(const WalkPrep& X, PrepLds (&S)[4]) {
+__device__ void prep_role(const WalkSide& X, PrepLds (&S)[4]) {
     const int sub = wave_id() >> 2;          // which of the four groups
     const int w = wave_id() & 3;             // wave within the group
     const int tid = threadIdx.x & 255;
@@ -475,7 +475,7 @@ __device__ void norm_rows_act(const WalkNorm& N, int wg, int nwg) {
     else norm_rows<float, float, kAct>(N, wg, nwg);
 }
 
-__device__ void norm_role(const WalkPrep& X) {
+__device__ void norm_role(const WalkSide& X) {
     const int wg = int(blockIdx.x) - X.walk_blocks - X.prep_blocks;
     const WalkNorm& N = X.norm;
     if (N.act == RDA_GATE_SIGMOID) norm_rows_act<RDA_GATE_SIGMOID>(N, wg, N.blocks);
@@ -489,7 +489,7 @@ __global__ __launch_bounds__(kThreads) void walk_bf16_kernel(
     const uint16_t* __restrict__ v, int N, int H, const int32_t* __restrict__ rec,
     const int32_t* __restrict__ seq_off, const int32_t* __restrict__ num_chunks,
     const unsigned char* __restrict__ factors, OutSink out, WalkJob j0, WalkJob j1,
-    int seg_chunks, WalkPrep X) {
+    int seg_chunks, WalkSide X) {
     __shared__ __attribute__((aligned(16))) WalkOrPrepLds shm;
     if (int(blockIdx.x) >= X.walk_blocks + X.prep_blocks) {
         norm_role(X);
@@ -588,10 +588,10 @@ hipError_t launch_walk_bf16(const uint16_t* q, const uint16_t* k, const uint16_t
                             const int32_t* seq_off, const int32_t* num_chunks,
                             const unsigned char* factors, OutSink out, const WalkJob* jobs,
                             int32_t num_jobs, int32_t seg_chunks, bool outputs,
-                            hipStream_t stream, const WalkPrep* extra) {
+                            hipStream_t stream, const WalkSide* extra) {
     const int64_t pairs = int64_t(num_seqs) * heads;
     const unsigned walk_grid = unsigned(num_jobs * 64 * ((pairs + 7) / 8));
-    WalkPrep X{};
+    WalkSide X{};
     if (extra) X = *extra;
     X.walk_blocks = int(walk_grid);
     const unsigned grid =
