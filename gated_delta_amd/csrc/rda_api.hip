@@ -69,62 +69,87 @@ size_t seg_state_bytes(const SegPlan& sp, int32_t heads) {
 }
 
 // The overlapped plan for one long sequence whose walk leaves many CUs idle
-// (8 workgroups per head, one per CU): (1) the prep of the first c1 chunks
-// on the whole chip, (2) one launch whose walk workgroups walk chunks
-// [0, c1) and save the state while prep workgroups on the idle CUs prep the
-// remaining chunks, (3) the walk of chunks [c1, nch) from the saved state.
-// c1 balances (2): when a walk chunk step costs about as long as r prep
-// items on one CU, the walk of c1 chunks and the prep of (nch - c1) H items
-// on `idle` CUs take the same time when c1 = nch rH / (idle + rH).  r is
-// about 3 for the scalar decay and about 2/11 for the per-channel one (a
-// per-channel prep item takes about 5.5 walk steps).
+// (8 workgroups per head, one per CU), in chunk ranges: (1) the prep of the
+// first range on the whole chip, (2) one launch per range whose walk
+// workgroups walk it, from the state the launch before saved, while prep
+// workgroups on the idle CUs prep later chunks.  When one prep item takes
+// about r walk steps on one CU, the walk of L chunks hides the prep of
+// g L = L idle / (r H) chunks, so each range may be g times the one before
+// and the launch preps the next: the first range is short (its prep runs
+// alone), the ranges grow until the last takes the rest.  r is about 3 for
+// the scalar decay and about 6 for the per-channel one.  Each walk launch
+// costs a ramp, and a walk slows while prep runs beside it, so growing
+// ranges pay only where the prep is dear: for the per-channel decay (at
+// 16384 x 16, 0.68 ms against 0.73 with two ranges).  Otherwise, and with g
+// below 5/4 (many heads), two ranges: the first walk launch preps
+// everything after its range, c1 = nch / (1 + g) balancing it (for the
+// scalar decay at 16384 x 16 growing ranges measured 0.376-0.385 ms
+// against 0.372-0.378).
+//
+// The fused output norm runs the norm of range i - 1 beside the walk of
+// range i, on the same idle CUs, and the norm of the last range after the
+// walk; for it the plan ends with a range of nch / 8 chunks (at least 16),
+// long enough to hide the norm of the one before on the idle CUs.
 constexpr int kOverlapMinChunks = 32;
 constexpr int kOverlapMinIdleCUs = 64;
-constexpr int kPrepItemsPerWalkStep = 3;
-constexpr int kDiagWalkStepsPerPrepItem2 = 11;   // walk steps per per-channel prep item, x 2
+constexpr int kOverlapMaxRanges = 16;
+constexpr int kOverlapMinRange = 8;
+constexpr int kDiagWalkStepsPerPrepItem = 6;   // walk steps per per-channel prep item
 
 struct OverlapPlan {
-    int c1 = 0;           // chunks walked in the middle launch (0: no overlap)
-    int prep_blocks = 0;  // prep workgroups beside them
+    int m = 0;            // walk launches, one per range (0: no overlap)
+    int prep_blocks = 0;  // prep (or norm) workgroups beside each walk launch
+    int cut[kOverlapMaxRanges + 1] = {};   // range i: chunks [cut[i], cut[i + 1])
+    int pend[kOverlapMaxRanges] = {};      // chunks prepped once walk launch i ends
 };
 
-// rn / rd: r of the comment above as a ratio
-OverlapPlan overlap_plan(int32_t num_seqs, int32_t total_tokens, int32_t heads, int64_t rn = 3,
-                         int64_t rd = 1) {
+// The fused norm's last range: nch / 8 chunks, at least 16.
+int64_t norm_tail_chunks(int64_t nch) { return nch / 8 > 16 ? nch / 8 : 16; }
+
+// r walk steps per prep item; `grow`: growing ranges, the first nch / 8
+// chunks; `fused`: end with the fused norm's tail range.
+OverlapPlan overlap_plan(int32_t num_seqs, int32_t total_tokens, int32_t heads, bool fused,
+                         int64_t r = 3, bool grow = false) {
     OverlapPlan op;
     if (num_seqs != 1 || total_tokens <= 0 || heads <= 0) return op;
     const int64_t nch = (int64_t(total_tokens) + kC - 1) / kC;
     const int64_t idle = kSegCUs - int64_t(kWalkSlices) * heads;
     if (nch < kOverlapMinChunks || idle < kOverlapMinIdleCUs) return op;
-    const int64_t r = rn * heads, den = rd * idle + r;
-    int64_t c1 = (nch * r + den / 2) / den;
-    c1 = c1 < 8 ? 8 : c1;
-    c1 = c1 > nch - 8 ? nch - 8 : c1;
-    op.c1 = int(c1);
+    const int64_t gn = idle, gd = r * heads;   // g = gn / gd
+    const int64_t limit = nch - (fused ? norm_tail_chunks(nch) : 0);
     op.prep_blocks = int(idle);
+    int m = 0;
+    if (!grow || 4 * gn < 5 * gd) {
+        int64_t c1 = (nch * gd + (gn + gd) / 2) / (gn + gd);
+        c1 = c1 < kOverlapMinRange ? kOverlapMinRange : c1;
+        c1 = c1 > nch - kOverlapMinRange ? nch - kOverlapMinRange : c1;
+        op.cut[++m] = int(c1);
+        if (limit >= c1 + kOverlapMinRange && limit < nch) op.cut[++m] = int(limit);
+        op.cut[++m] = int(nch);
+        for (int i = 0; i < m; ++i) op.pend[i] = int(nch);
+        op.m = m;
+        return op;
+    }
+    int64_t len = nch / 8 > kOverlapMinRange ? nch / 8 : kOverlapMinRange;
+    while (op.cut[m] < limit) {
+        int64_t next = op.cut[m] + len;
+        // a short remainder joins the range before
+        if (next + kOverlapMinRange > limit || m + 2 >= kOverlapMaxRanges) next = limit;
+        op.cut[++m] = int(next);
+        len = len * gn / gd;
+    }
+    if (limit < nch) op.cut[++m] = int(nch);
+    for (int i = 0; i < m; ++i) op.pend[i] = op.cut[i + 2 <= m ? i + 2 : m];
+    op.m = m;
     return op;
 }
 
-// With the fused output norm the last walk launch of the overlapped plan is
-// cut at c2: the walk of [c1, c2) carries the norm of the rows of [0, c1)
-// and the walk of [c2, nch) that of [c1, c2), on the idle CUs, so that only
-// the norm of the last nch - c2 chunks runs after the walk.  nch - c2 is
-// nch / 8 (at least 16): enough walk time to hide the norm of [c1, c2) on
-// half the chip.  0: no cut.
-int fused_norm_cut(const OverlapPlan& op, int32_t total_tokens) {
-    if (op.c1 <= 0) return 0;
-    const int nch = (total_tokens + kC - 1) / kC;
-    const int tail = nch / 8 > 16 ? nch / 8 : 16;
-    const int c2 = nch - tail;
-    return c2 >= op.c1 + 8 ? c2 : 0;
-}
-
 OverlapPlan diag_overlap_plan(int32_t num_seqs, int32_t total_tokens, int32_t heads) {
-    return overlap_plan(num_seqs, total_tokens, heads, kDiagWalkStepsPerPrepItem2, 2);
+    return overlap_plan(num_seqs, total_tokens, heads, false, kDiagWalkStepsPerPrepItem, true);
 }
 
 size_t overlap_state_bytes(const OverlapPlan& op, int32_t heads) {
-    return op.c1 > 0 ? size_t(heads) * kD * kD * sizeof(float) : 0;
+    return op.m > 0 ? size_t(heads) * kD * kD * sizeof(float) : 0;
 }
 
 // The 16-bit output form of the fused output norm: [T, H, 128] 16-bit values.
@@ -171,7 +196,7 @@ struct Prefill {
     SegPlan seg;          // used when the input is one bf16 sequence without offsets
     float *E, *F, *S_in;  // segmented pass: end states from zero, transitions, starts
     OverlapPlan ovl;      // likewise, when no segmented pass runs
-    float* S_mid;         // overlapped plan: the state after chunk c1
+    float* S_mid;         // overlapped plan: the state between walk launches
     OutSink out;          // where the walk's outputs go (o, or the slice form)
     WalkNorm norm;        // fused output norm (norm.y set): its arguments
 };
@@ -231,7 +256,7 @@ rda_status check_prefill(const void* q, const void* k, const void* v, rda_dtype 
                 SegPlan{}, nullptr, nullptr, nullptr, OverlapPlan{}, nullptr,
                 OutSink{o, nullptr}, WalkNorm{}};
     const SegPlan sp = seg_plan(num_seqs, total_tokens, num_heads);
-    const OverlapPlan op = overlap_plan(num_seqs, total_tokens, num_heads);
+    const OverlapPlan op = overlap_plan(num_seqs, total_tokens, num_heads, fused);
     unsigned char* tail = P.factors + size_t(mc) * num_heads * kChunkHeadBytes;
     if (cu_seqlens == nullptr && qkv_dtype == RDA_BF16) {
         if (sp.P > 0) {
@@ -240,7 +265,7 @@ rda_status check_prefill(const void* q, const void* k, const void* v, rda_dtype 
             P.E = reinterpret_cast<float*>(tail);
             P.F = reinterpret_cast<float*>(tail + sb);
             P.S_in = reinterpret_cast<float*>(tail + 2 * sb);
-        } else if (op.c1 > 0) {
+        } else if (op.m > 0) {
             P.ovl = op;
             P.S_mid = reinterpret_cast<float*>(tail);
         }
@@ -257,63 +282,48 @@ rda_status prefill_overlapped(const Prefill& P, hipStream_t stream, hipEvent_t c
     const auto* k16 = static_cast<const uint16_t*>(P.k);
     const auto* v16 = static_cast<const uint16_t*>(P.v);
     const int nch = (P.T + kC - 1) / kC;
-    const int c1 = P.ovl.c1;
-    WalkSide X{};
-    X.c_lo = 0;
-    X.c_hi = c1;
-    X.prep_blocks = P.ovl.prep_blocks;
-    X.item_lo = c1 * P.H;
-    X.item_hi = nch * P.H;
-    X.single_T = P.T;
-    X.nch = nch;
-    X.args = PrepItemArgs{q16, k16, P.a, P.b, P.H, P.factors};
-    X.rec_out = P.rec;
-    X.seq_off_out = P.seq_off;
-    X.num_out = P.nch;
-    // the fused output norm: the rows of chunks already walked, on the CUs a
-    // later walk launch leaves idle (see fused_norm_cut)
-    const int c2 = P.norm.y ? fused_norm_cut(P.ovl, P.T) : 0;
-    auto norm_rows = [&](WalkSide& Z, int lo, int hi) {
-        Z.norm = P.norm;
-        Z.norm.row_lo = int64_t(kC) * lo * P.H;
-        Z.norm.row_hi = int64_t(kC) * hi * P.H;
-        Z.norm.blocks = P.ovl.prep_blocks;
-    };
-    WalkSide Y{}, Y2{};
-    Y.c_lo = c1;
-    Y.c_hi = c2 > 0 ? c2 : nch;
-    if (P.norm.y) norm_rows(Y, 0, c1);
-    Y2.c_lo = c2;
-    Y2.c_hi = nch;
-    if (c2 > 0) norm_rows(Y2, c1, c2);
-    const WalkJob first{P.S0, P.S_mid, 0, 0};
-    // each walk workgroup reads its slice of the saved state before it
-    // writes it back, so the middle state may stay in place
-    const WalkJob middle{P.S_mid, P.S_mid, 0, 0};
-    const WalkJob second{P.S_mid, P.S_final, 0, 0};
+    const OverlapPlan& op = P.ovl;
     rda_status st;
     if ((st = record(ev, 2 * RDA_STAGE_TABLE, stream)) != RDA_OK ||
         (st = record(ev, 2 * RDA_STAGE_TABLE + 1, stream)) != RDA_OK ||
         (st = record(ev, 2 * RDA_STAGE_PREP, stream)) != RDA_OK)
         return st;
     if (launch_prep_bf16(q16, k16, P.a, P.b, P.H, P.mc, nullptr, nullptr, P.factors, P.T, P.rec,
-                         P.seq_off, P.nch, stream, 0, c1) != hipSuccess)
+                         P.seq_off, P.nch, stream, 0, op.cut[1]) != hipSuccess)
         return RDA_ERR_HIP;
     if ((st = record(ev, 2 * RDA_STAGE_PREP + 1, stream)) != RDA_OK ||
         (st = record(ev, 2 * RDA_STAGE_WALK, stream)) != RDA_OK)
         return st;
-    if (launch_walk_bf16(q16, k16, v16, 1, P.H, P.rec, P.seq_off, P.nch, P.factors, P.out, &first,
-                         1, 0, true, stream, &X) != hipSuccess)
-        return RDA_ERR_HIP;
-    if (c2 > 0) {
+    for (int i = 0; i < op.m; ++i) {
+        // range i; beside it the prep of the chunks up to pend[i] (and their
+        // table entries) and, for the fused norm, the norm of range i - 1
+        WalkSide X{};
+        X.c_lo = op.cut[i];
+        X.c_hi = op.cut[i + 1];
+        const int p_lo = i == 0 ? op.cut[1] : op.pend[i - 1];
+        if (op.pend[i] > p_lo) {
+            X.prep_blocks = op.prep_blocks;
+            X.item_lo = p_lo * P.H;
+            X.item_hi = op.pend[i] * P.H;
+            X.single_T = P.T;
+            X.nch = nch;
+            X.args = PrepItemArgs{q16, k16, P.a, P.b, P.H, P.factors};
+            X.rec_out = P.rec;
+            X.seq_off_out = P.seq_off;
+            X.num_out = P.nch;
+        }
+        if (P.norm.y && i > 0) {
+            X.norm = P.norm;
+            X.norm.row_lo = int64_t(kC) * op.cut[i - 1] * P.H;
+            X.norm.row_hi = int64_t(kC) * op.cut[i] * P.H;
+            X.norm.blocks = op.prep_blocks;
+        }
+        // each walk workgroup reads its slice of the saved state before it
+        // writes it back, so the state between launches stays in place
+        const WalkJob job{i == 0 ? P.S0 : P.S_mid, i + 1 == op.m ? P.S_final : P.S_mid, 0, 0};
         if (launch_walk_bf16(q16, k16, v16, 1, P.H, P.rec, P.seq_off, P.nch, P.factors, P.out,
-                             &middle, 1, 0, true, stream, &Y) != hipSuccess ||
-            launch_walk_bf16(q16, k16, v16, 1, P.H, P.rec, P.seq_off, P.nch, P.factors, P.out,
-                             &second, 1, 0, true, stream, &Y2) != hipSuccess)
+                             &job, 1, 0, true, stream, &X) != hipSuccess)
             return RDA_ERR_HIP;
-    } else if (launch_walk_bf16(q16, k16, v16, 1, P.H, P.rec, P.seq_off, P.nch, P.factors, P.out,
-                                &second, 1, 0, true, stream, &Y) != hipSuccess) {
-        return RDA_ERR_HIP;
     }
     return record(ev, 2 * RDA_STAGE_WALK + 1, stream);
 }
@@ -322,7 +332,7 @@ rda_status prefill_overlapped(const Prefill& P, hipStream_t stream, hipEvent_t c
 // by its event pair when `ev` is given; one bf16 sequence whose walk leaves
 // CUs idle takes the overlapped plan instead.
 rda_status prefill_sequential(const Prefill& P, hipStream_t stream, hipEvent_t const* ev) {
-    if (P.ovl.c1 > 0) return prefill_overlapped(P, stream, ev);
+    if (P.ovl.m > 0) return prefill_overlapped(P, stream, ev);
     rda_status st;
     // one sequence without offsets: the prep kernel derives each chunk's
     // record itself and writes the table, which saves the table launch
@@ -434,7 +444,8 @@ size_t rda_prefill_workspace_bytes(int32_t num_seqs, int32_t total_tokens, int32
     // one sequence: room for the segmented pass's three state arrays or the
     // overlapped plan's middle state
     const size_t seg = 3 * seg_state_bytes(seg_plan(num_seqs, total_tokens, num_heads), num_heads);
-    const size_t mid = overlap_state_bytes(overlap_plan(num_seqs, total_tokens, num_heads), num_heads);
+    const size_t mid =
+        overlap_state_bytes(overlap_plan(num_seqs, total_tokens, num_heads, false), num_heads);
     return align256(tl.bytes) + size_t(mc) * size_t(num_heads) * kChunkHeadBytes +
            (seg > mid ? seg : mid);
 }
@@ -645,35 +656,34 @@ rda_status rda_prefill_diag(const void* q, const void* k, const void* v, rda_dty
         return RDA_OK;
     }
     const OverlapPlan op = diag_overlap_plan(num_seqs, total_tokens, num_heads);
-    if (op.c1 > 0 && cu_seqlens == nullptr) {
-        // the overlapped plan, as for rda_prefill: the prep of the first c1
-        // chunks; their walk beside the prep of the rest on the idle CUs;
-        // the walk of the rest from the state saved in between
+    if (op.m > 0 && cu_seqlens == nullptr) {
+        // the overlapped plan (see overlap_plan): the prep of the first range,
+        // then the walk of each range beside the prep of the next on the
+        // idle CUs, the state handed on in place between the walk launches
         float* S_mid = reinterpret_cast<float*>(factors + size_t(mc) * num_heads *
                                                               kDiagChunkHeadBytes);
-        const int nchunks = (total_tokens + kC - 1) / kC;
-        DiagSide X{};
-        X.c_lo = 0;
-        X.c_hi = op.c1;
-        X.prep_blocks = op.prep_blocks;
-        X.item_lo = op.c1 * num_heads;
-        X.item_hi = nchunks * num_heads;
-        X.q = q;
-        X.k = k;
-        X.alpha = alpha;
-        X.b = b;
-        DiagSide Y{};
-        Y.c_lo = op.c1;
-        Y.c_hi = nchunks;
-        const WalkJob first{S0, S_mid, 0, 0};
-        const WalkJob second{S_mid, S_final, 0, 0};
         if (launch_prep_diag(q, k, qkv_dtype, alpha, b, num_heads, mc, rec, nch, factors, stream,
-                             op.c1 * num_heads) != hipSuccess ||
-            launch_walk_diag(v, qkv_dtype, 1, num_heads, rec, seq_off, nch, factors, o, &first, 1,
-                             0, true, stream, &X) != hipSuccess ||
-            launch_walk_diag(v, qkv_dtype, 1, num_heads, rec, seq_off, nch, factors, o, &second,
-                             1, 0, true, stream, &Y) != hipSuccess)
+                             op.cut[1] * num_heads) != hipSuccess)
             return RDA_ERR_HIP;
+        for (int i = 0; i < op.m; ++i) {
+            DiagSide X{};
+            X.c_lo = op.cut[i];
+            X.c_hi = op.cut[i + 1];
+            const int p_lo = i == 0 ? op.cut[1] : op.pend[i - 1];
+            if (op.pend[i] > p_lo) {
+                X.prep_blocks = op.prep_blocks;
+                X.item_lo = p_lo * num_heads;
+                X.item_hi = op.pend[i] * num_heads;
+                X.q = q;
+                X.k = k;
+                X.alpha = alpha;
+                X.b = b;
+            }
+            const WalkJob job{i == 0 ? S0 : S_mid, i + 1 == op.m ? S_final : S_mid, 0, 0};
+            if (launch_walk_diag(v, qkv_dtype, 1, num_heads, rec, seq_off, nch, factors, o, &job,
+                                 1, 0, true, stream, &X) != hipSuccess)
+                return RDA_ERR_HIP;
+        }
         return RDA_OK;
     }
     if (launch_prefill_diag(q, k, v, qkv_dtype, alpha, b, num_seqs, num_heads,
@@ -912,8 +922,7 @@ rda_status rda_prefill_norm_gate(const void* q, const void* k, const void* v, rd
     if ((st = prefill_sequential(P, stream, nullptr)) != RDA_OK) return st;
     // the overlapped plan's later walk launches have done the rows of the
     // chunks before the last walk launch's; the rest here
-    const int c2 = fused_norm_cut(P.ovl, total_tokens);
-    const int64_t done = int64_t(kC) * (c2 > 0 ? c2 : P.ovl.c1 > 0 ? P.ovl.c1 : 0) * num_heads;
+    const int64_t done = int64_t(kC) * (P.ovl.m > 0 ? P.ovl.cut[P.ovl.m - 1] : 0) * num_heads;
     const size_t gsz = g_dtype == RDA_BF16 ? 2 : 4, osz = out_dtype == RDA_BF16 ? 2 : 4;
     const size_t off = size_t(done) * kD;
     if (launch_norm_gate(nullptr, g ? static_cast<const unsigned char*>(g) + off * gsz : nullptr,

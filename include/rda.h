@@ -276,7 +276,11 @@ rda_status rda_decode_tokens(const void* q, const void* k, const void* v, rda_dt
  * forms a decay factor above e^60 (it falls back to exact per-element
  * factors where a 16-token block decays by more than that).  One sequence
  * without offsets with few heads takes the segmented state pass described
- * at rda_prefill (same plan; its workspace size includes the state arrays).
+ * at rda_prefill (same plan; its workspace size includes the state arrays);
+ * with more heads, the overlapped plan described there, in growing chunk
+ * ranges: the prep of the first range, then one walk launch per range beside
+ * the prep of the next on the idle CUs (bitwise the one-pass result; the
+ * workspace includes one [H, dv, dk] state).
  */
 size_t rda_prefill_diag_workspace_bytes(int32_t num_seqs, int32_t total_tokens,
                                         int32_t num_heads, int32_t dk, int32_t dv);

@@ -146,10 +146,11 @@ def test_decay_regimes(dev, kind):
                                       (2100, 16, False)])
 def test_overlapped_plan_matches_one_pass(dev, T, H, bf16):
     """One sequence without offsets whose walk leaves CUs idle runs the
-    overlapped plan (the prep of the first chunks, then their walk beside
-    the prep of the rest on the idle CUs, then the rest of the walk); with
-    cu_seqlens = {0, T} the same sizes run prep then one walk.  Both give the
-    same bits, and the plan meets the oracle."""
+    overlapped plan in chunk ranges (the prep of the first range, then the
+    walk of each range beside the prep of the next on the idle CUs, the
+    state handed on between walk launches; 2048 tokens make 3 ranges, 4097
+    make 5); with cu_seqlens = {0, T} the same sizes run prep then one walk.
+    Both give the same bits, and the plan meets the oracle."""
     import dataclasses
     p = synth.make_prefill(T, H, bf16=bf16, s0_std=0.02, key=(613, T, H))
     alpha = synth.diag_alpha(T, H, key=(613, T, H))
