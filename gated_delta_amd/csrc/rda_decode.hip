@@ -368,35 +368,43 @@ __global__ __launch_bounds__(256) void decode_diag_kernel(const TIn* __restrict_
 
 // ---------------------------------------------------------------------------
 // One decode step with the block's prologue in front, one 512-thread
-// workgroup per (batch, head).  Lane groups 0, 1, 2 of wave 0 run the
-// prologue for q, k and v in the prologue kernel's own lane layout (a lane
-// 8 channels, 4c.. and 64+4c..) and per-channel arithmetic
-// (rda_prologue_math.h): the short convolution over the history and the
-// raw token, the activation, the q / k L2 norm or the write gate on v, the
-// rounding to bf16.  They put q, k, v (768 bytes) in LDS and move the
-// history on by one token; every wave then reads its operands after one
-// barrier and runs the decode step's single pass over its 16 state rows
-// (decode_rows, wave w rows 16w + 4p + g).  The result is that of
-// rda_prologue (one-token layout) followed by rda_decode_step, bit for bit,
-// and q, k, v, a, b never reach memory.  A lane reads its history slots
-// before it writes the shifted ones, and no other lane touches them, so the
-// history may be updated in place.
+// workgroup per (batch, head).  Lanes 0..383 load the short convolution's
+// operands for one channel each of q, k, v (lane 128x + ch: tensor x,
+// channel ch) -- its weights, its history slots and the raw token -- and then
+// every lane sends out its state loads (the decode step's layout: wave w
+// holds rows 16w + 4p + g).  The convolution lanes run the taps in the
+// prologue's order and the activation, leave the fp32 result in LDS and move
+// their channel's history on by one token.  After a barrier lane groups 0
+// and 1 of wave 0 take the L2 scales of q and k in the prologue kernel's
+// lane layout (a lane 8 channels, 4c.. and 64+4c..) and leave q and k in
+// bf16 in LDS; after a second barrier every wave reads them, rounds its rows
+// of the gated v to bf16 and runs the decode step's single pass over its
+// rows (decode_rows).  The result is that of rda_prologue (one-token layout)
+// followed by rda_decode_step, bit for bit (the per-channel arithmetic is
+// the shared code of rda_prologue_math.h), and q, k, v, a, b never reach
+// memory.  A lane reads its channel's history slots before it writes the
+// shifted ones, and no other lane touches them, so the history may be
+// updated in place.
 //
 // That the history may be updated in place is what fixes one workgroup per
 // (batch, head): both halves of the state need every q and k channel, hence
-// the whole q / k history.  On 256 x 16 states this step takes about 93 us,
-// as long as rda_prologue followed by rda_decode_step (about 13 + 80.5 us);
-// the plain decode step keeps twice the bytes in flight per CU with two
-// 32 KiB workgroups per (batch, head).  Measured and not kept: every lane
-// group running the whole prologue for itself (173 us: 157 registers and
-// all the conv weights loaded by every group), eight waves per SIMD (2
-// registers spilled: 99 us), a
-// ninth wave for the prologue (94 us), and persistent workgroups with the
-// prologue one item ahead in a second LDS buffer (88 registers: 100 us).
+// the whole q / k history.  The gates go to scalar registers, which keeps
+// the kernel at 64 registers, 8 waves per SIMD: 4 workgroups, as many state
+// bytes in flight per CU as the plain decode step.  On 256 x 16 states this
+// step takes 87 us against 80.5 us for the plain decode step, which moves
+// 3.5 % fewer bytes (no history read and written); 6 waves per SIMD measure
+// the same.  Measured and not kept: lane groups 0-2 of wave 0 running the
+// prologue 8 channels per lane and loading their state only after it (93
+// us, as long as rda_prologue followed by rda_decode_step), every lane group
+// running the whole prologue for itself (173 us), a ninth wave for the
+// prologue (94 us), persistent workgroups with the prologue one item ahead
+// in a second LDS buffer (100 us), and the gates in vector registers, which
+// spills a state load at 8 waves per SIMD (101 us).
 template <int K, int kAct>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(8)))
 void decode_prologue_kernel(const DecodePrologueArgs P) {
-    __shared__ __attribute__((aligned(16))) uint16_t qkv[3][kD];
+    __shared__ __attribute__((aligned(16))) float u[4][kD];        // q, k, v; row 3 unused
+    __shared__ __attribute__((aligned(16))) uint16_t qk[2][kD];    // q, k in bf16
     const int64_t bh = blockIdx.x;
     const int64_t n = bh / P.H;
     const int h = int(bh - n * P.H);
@@ -407,90 +415,95 @@ void decode_prologue_kernel(const DecodePrologueArgs P) {
     const int rbase = 16 * w + g;
     float* __restrict__ Sb = P.S + bh * (kD * kD);
 
-    const int ch0 = 4 * c, ch1 = 64 + 4 * c;
-    const float br = P.beta[bh];
+    // the convolution's loads first (waves 6, 7 load v's channels again and
+    // keep nothing: all of this stays straight-line code), so that it waits
+    // for them alone (loads return in order)
+    const bool conv = t < 3 * kD;
+    const int xr = __builtin_amdgcn_readfirstlane(t >> 7);   // 3 in waves 6, 7
+    const int x = xr < 3 ? xr : 2;
+    const uint32_t ch = uint32_t(t) & (kD - 1);
+    const uint32_t hd = uint32_t(P.H) * kD;
+    // history slots of tensor x for this (sequence, head): [N][3][K-1][H][128]
+    const size_t hslots = (size_t(n) * 3 + x) * (K - 1) * hd + size_t(h) * kD;
+    const float* wb = P.w + (size_t(x) * P.H + h) * kD * K;
+    const uint16_t* xb = (x == 0 ? P.x[0] : x == 1 ? P.x[1] : P.x[2]) + bh * kD;
+    float wt[K];
+    uint32_t win[K];   // taps 0 .. K-2 from the history, tap K-1 the current token
+#pragma unroll
+    for (int i = 0; i < K; ++i) wt[i] = wb[ch * K + i];
+    win[K - 1] = xb[ch];
+    // without a history the taps read the current token and are masked to
+    // zero further down (no branch)
+    const uint32_t keep = P.hin ? 0xffffu : 0u;
+    {
+        const uint16_t* hb = P.hin ? P.hin + hslots : xb;
+        const uint32_t hstep = P.hin ? hd : 0u;
+#pragma unroll
+        for (int i = 0; i < K - 1; ++i) win[i] = hb[ch + uint32_t(i) * hstep];
+    }
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 s[4][2];
-    auto load_state = [&]() {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int row = rbase + 4 * p;
-            s[p][0] = *reinterpret_cast<const f32x4*>(Sb + row * kD + 4 * c);
-            s[p][1] = *reinterpret_cast<const f32x4*>(Sb + row * kD + 64 + 4 * c);
-        }
-    };
-    // the state loads go out first everywhere except in the prologue's lanes,
-    // which load theirs once the convolution is done (their registers then
-    // hold either the convolution's operands or the state, never both, which
-    // keeps the kernel at 6 waves per SIMD without spills)
-    if (!(w == 0 && g < 3)) load_state();
-    if (w == 0 && g < 3) {
-        const int x = g;   // 0 = q, 1 = k, 2 = v
-        const size_t hd = size_t(P.H) * kD;
-        // history slot m of tensor x for this (sequence, head): [N][3][K-1][H][128]
-        auto slot = [&](int m) { return ((size_t(n) * 3 + x) * (K - 1) + m) * hd + size_t(h) * kD; };
-        float wt[K][8];
-        const float* wb = P.w + (size_t(x) * P.H + h) * kD * K;
+    for (int p = 0; p < 4; ++p) {
+        const int row = rbase + 4 * p;
+        s[p][0] = *reinterpret_cast<const f32x4*>(Sb + row * kD + 4 * c);
+        s[p][1] = *reinterpret_cast<const f32x4*>(Sb + row * kD + 64 + 4 * c);
+    }
+    float acc[1] = {0.f};
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int i = 0; i < K; ++i) {
-                wt[i][j] = wb[(ch0 + j) * K + i];
-                wt[i][4 + j] = wb[(ch1 + j) * K + i];
-            }
-        u32x2 win[K][2];   // taps 0 .. K-2 from the history, tap K-1 the current token
-#pragma unroll
-        for (int i = 0; i < K - 1; ++i) {
-            win[i][0] = u32x2{0u, 0u};
-            win[i][1] = u32x2{0u, 0u};
-            if (P.hin) {
-                win[i][0] = *reinterpret_cast<const u32x2*>(P.hin + slot(i) + ch0);
-                win[i][1] = *reinterpret_cast<const u32x2*>(P.hin + slot(i) + ch1);
-            }
-        }
-        const uint16_t* xp = P.x[x] + bh * kD;
-        win[K - 1][0] = *reinterpret_cast<const u32x2*>(xp + ch0);
-        win[K - 1][1] = *reinterpret_cast<const u32x2*>(xp + ch1);
-        float acc[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-#pragma unroll
-        for (int i = 0; i < K; ++i) {
-            float xv[8];
-            widen8(win[i], xv);
-            conv_tap(acc, wt[i], xv);
-        }
-        conv_activation<kAct>(acc);
-        const float scale =
-            x < 2 ? l2_scale(acc, P.l2eps) : write_gate(br, P.delta ? P.delta[bh] : 0.f);
-        *reinterpret_cast<u32x2*>(&qkv[x][ch0]) =
-            u32x2{pack_bf16(acc[0] * scale, acc[1] * scale), pack_bf16(acc[2] * scale, acc[3] * scale)};
-        *reinterpret_cast<u32x2*>(&qkv[x][ch1]) =
-            u32x2{pack_bf16(acc[4] * scale, acc[5] * scale), pack_bf16(acc[6] * scale, acc[7] * scale)};
+    for (int i = 0; i < K; ++i) {
+        const float xv[1] = {__uint_as_float((i < K - 1 ? win[i] & keep : win[i]) << 16)};
+        const float wv[1] = {wt[i]};
+        conv_tap(acc, wv, xv);
+    }
+    conv_activation<kAct>(acc);
+    u[xr][ch] = acc[0];
+    if (conv && P.hout) {
         // the history moves on by one token: slot m takes the old slot m + 1,
         // the newest slot the current raw token (read above by this lane)
-        if (P.hout) {
+        uint16_t* ho = P.hout + hslots;
 #pragma unroll
-            for (int m = 0; m < K - 1; ++m) {
-                *reinterpret_cast<u32x2*>(P.hout + slot(m) + ch0) = win[m + 1][0];
-                *reinterpret_cast<u32x2*>(P.hout + slot(m) + ch1) = win[m + 1][1];
-            }
-        }
-        load_state();
+        for (int m = 0; m < K - 1; ++m)
+            ho[ch + uint32_t(m) * hd] = uint16_t(m + 1 < K - 1 ? win[m + 1] & keep : win[m + 1]);
     }
-    const float av = floored_decay(P.glog[bh], P.floor_log);
-    const float bv = erase_gate(br);
+    const float br = P.beta[bh];
+    // the gates are the same in every lane: kept in scalar registers
+    const float av = uniform_f32(floored_decay(P.glog[bh], P.floor_log));
+    const float bv = uniform_f32(erase_gate(br));
+    const float vg = uniform_f32(write_gate(br, P.delta ? P.delta[bh] : 0.f));
     __syncthreads();
 
+    // q and k as rda_prologue leaves them: times their L2 scale, rounded to bf16
+    const int ch0 = 4 * c, ch1 = 64 + 4 * c;
+    if (w == 0 && g < 2) {
+        float a8[8];
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(&u[g][ch0]);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(&u[g][ch1]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a8[e] = x0[e];
+            a8[4 + e] = x1[e];
+        }
+        const float sc = l2_scale(a8, P.l2eps);
+        *reinterpret_cast<u32x2*>(&qk[g][ch0]) =
+            u32x2{pack_bf16(a8[0] * sc, a8[1] * sc), pack_bf16(a8[2] * sc, a8[3] * sc)};
+        *reinterpret_cast<u32x2*>(&qk[g][ch1]) =
+            u32x2{pack_bf16(a8[4] * sc, a8[5] * sc), pack_bf16(a8[6] * sc, a8[7] * sc)};
+    }
+    __syncthreads();
+
+    // every wave: q and k from LDS; its rows of v times the write gate, in bf16
     float kx[8], qx[8], vr[4];
     {
-        const u32x2 kr[2] = {*reinterpret_cast<const u32x2*>(&qkv[1][ch0]),
-                             *reinterpret_cast<const u32x2*>(&qkv[1][ch1])};
-        const u32x2 qr[2] = {*reinterpret_cast<const u32x2*>(&qkv[0][ch0]),
-                             *reinterpret_cast<const u32x2*>(&qkv[0][ch1])};
+        const u32x2 kr[2] = {*reinterpret_cast<const u32x2*>(&qk[1][ch0]),
+                             *reinterpret_cast<const u32x2*>(&qk[1][ch1])};
+        const u32x2 qr[2] = {*reinterpret_cast<const u32x2*>(&qk[0][ch0]),
+                             *reinterpret_cast<const u32x2*>(&qk[0][ch1])};
         widen8(kr, kx);
         widen8(qr, qx);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) vr[p] = bf16_bits_to_f32(qkv[2][rbase + 4 * p]);
+        for (int p = 0; p < 4; ++p)
+            vr[p] = __uint_as_float(pack_bf16(u[2][rbase + 4 * p] * vg, 0.f) << 16);
     }
     const float o_mine = decode_rows(s, kx, qx, av, bv, vr, c, Sb, rbase);
     if (c < 4) P.o[bh * kD + rbase + 4 * c] = o_mine;

@@ -84,6 +84,12 @@ __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
 }
 
+// A float that every lane of the wave holds alike, moved to a scalar
+// register (its bits, not a conversion).
+__device__ __forceinline__ float uniform_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
