@@ -23,7 +23,10 @@
 // shares with the neighbouring workgroup come from L2.  TT is 8 when that
 // still gives 512 workgroups, else 1 (a decode batch).  Where a
 // sequence starts inside a token's window the history of that sequence
-// replaces the raw tokens before it.  The q and k norms are 16-lane DPP
+// replaces the raw tokens before it; a block whose tokens and windows all
+// lie inside one sequence, away from the last K-1 tokens of a sequence whose
+// history is kept, takes a plain path without those per-token lookups and
+// branches (16384 x 16: 96 us against 103).  The q and k norms are 16-lane DPP
 // reductions.  The arithmetic (about 160 VALU instructions per token and
 // lane, a third of them the SiLU's exp and reciprocal) is of the same order
 // as the memory time, and the two overlap only in part.  Measured and not
@@ -74,7 +77,7 @@ __device__ __forceinline__ int32_t find_seq(const PrologueArgs& P, int32_t t) {
 }
 
 template <int K, int kAct, int kTT>
-__global__ __launch_bounds__(256) void prologue_kernel(const PrologueArgs P) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void prologue_kernel(const PrologueArgs P) {
     const int x = blockIdx.z;        // 0 = q, 1 = k, 2 = v
     const int lane = threadIdx.x;
     const int grp = lane >> 4;
@@ -128,6 +131,53 @@ __global__ __launch_bounds__(256) void prologue_kernel(const PrologueArgs P) {
     }
 
     int32_t n_hint = find_seq(P, t_first);
+    {
+        // The common block: its tokens and their windows inside one
+        // sequence, and (with a history out) none of them among the
+        // sequence's last K-1 tokens, whose raw values become the history.
+        // Then every tap reads the raw window and nothing else is written:
+        // the same arithmetic without the per-token lookups and branches.
+        const Seq s0 = seq_of(P, t_first, n_hint);
+        const int32_t t_last = min(t_first + kTT, P.T) - 1;
+        const bool plain = t_first - (K - 1) >= s0.s && t_last < s0.e &&
+                           (!P.hout || K == 1 || t_last < s0.e - (K - 1));
+        if (plain) {
+#pragma unroll
+            for (int j = 0; j < kTT; ++j) {
+                const int32_t t = t_first + j;
+                if (t > t_last) break;
+                float acc[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+                for (int i = 0; i < K; ++i) {
+                    float xv[8];
+                    widen8(raw[j + i], xv);
+                    conv_tap(acc, wt[i], xv);
+                }
+                conv_activation<kAct>(acc);
+                const size_t th = size_t(t) * P.H + h;
+                float scale;
+                if (x < 2) {
+                    scale = l2_scale(acc, P.l2eps);
+                } else {
+                    const float br = P.beta[th];
+                    const float dl = P.delta ? P.delta[th] : 0.f;
+                    scale = write_gate(br, dl);
+                }
+                uint16_t* ob = P.out[x] + th * kD;
+                *reinterpret_cast<u32x2*>(ob + ch0) = u32x2{pack_bf16(acc[0] * scale, acc[1] * scale),
+                                                            pack_bf16(acc[2] * scale, acc[3] * scale)};
+                *reinterpret_cast<u32x2*>(ob + ch1) = u32x2{pack_bf16(acc[4] * scale, acc[5] * scale),
+                                                            pack_bf16(acc[6] * scale, acc[7] * scale)};
+                if (x == 0 && c == 0) {
+                    P.b[th] = erase_gate(P.beta[th]);
+                    P.a[th] = floored_decay(P.glog[th], P.floor_log);
+                }
+            }
+            return;
+        }
+    }
 #pragma unroll
     for (int j = 0; j < kTT; ++j) {
         const int32_t t = t_first + j;
