@@ -2,9 +2,9 @@
 # Collects the rocprofv3 kernel summaries and the counter passes behind
 # profiles/: kernel trace + stats of the bench's timed steps (and, in passes
 # of their own, of the one-pass multi-token decode, the output norm and gate,
-# the prologue, the per-channel-decay prefill, the segmented state pass and
-# the prefill fused with the output norm and gate),
-# then one FETCH_SIZE and one
+# the prologue, the decode step with the prologue in front, the
+# per-channel-decay prefill, the segmented state pass and the prefill fused
+# with the output norm and gate), then one FETCH_SIZE and one
 # WRITE_SIZE pass over the prefill alone, each of those, and a plain device
 # copy of known size (the counter calibration), then one pass of the MFMA
 # counters over the prefill.
@@ -32,6 +32,10 @@ echo "== kernel trace + stats: python bench.py --mode prologue --steps 20 --no-c
 timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d "$OUT/prof_trace_pro" -o trace \
     -- python -u "$R/bench.py" --mode prologue --steps 20 --no-cpu \
     > "$OUT/prof_trace_pro.log" 2>&1 || exit $?
+echo "== kernel trace + stats: python bench.py --mode decode_prologue --steps 10 --no-cpu"
+timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d "$OUT/prof_trace_dp" -o trace \
+    -- python -u "$R/bench.py" --mode decode_prologue --steps 10 --no-cpu \
+    > "$OUT/prof_trace_dp.log" 2>&1 || exit $?
 echo "== kernel trace + stats: python bench.py --mode prefill_diag --steps 10 --no-cpu"
 timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d "$OUT/prof_trace_diag" -o trace \
     -- python -u "$R/bench.py" --mode prefill_diag --steps 10 --no-cpu \
@@ -45,7 +49,7 @@ timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d "$OUT/
     -- python -u "$R/bench.py" --mode prefill_norm_gate --steps 10 --no-cpu \
     > "$OUT/prof_trace_png.log" 2>&1 || exit $?
 for ctr in FETCH_SIZE WRITE_SIZE; do
-  for mode in prefill copy decode_tokens output_norm_gate prologue prefill_diag; do
+  for mode in prefill copy decode_tokens output_norm_gate prologue decode_prologue prefill_diag; do
     echo "== pmc $ctr: python bench.py --mode $mode --steps 2 --warmup 1 --no-cpu"
     timeout -s KILL 120 rocprofv3 --pmc $ctr --output-format csv -d "$OUT/prof_${ctr}_$mode" -o pmc \
         -- python -u "$R/bench.py" --mode $mode --steps 2 --warmup 1 --no-cpu \

@@ -12,6 +12,9 @@ Writes
       the same for the output norm and gate (bench --mode output_norm_gate);
   profiles/kernels_rda_prologue_T16384_H16.txt
       the same for the prologue (bench --mode prologue);
+  profiles/kernels_rda_decode_step_prologue_B256_H16.txt
+      the same for the decode step with the prologue in front, beside the
+      plain decode step (bench --mode decode_prologue);
   profiles/kernels_rda_prefill_diag_T16384_H16.txt
       the same for the per-channel-decay prefill (bench --mode prefill_diag);
   profiles/kernels_rda_prefill_segmented_T16384_H2.txt
@@ -191,14 +194,30 @@ def main():
              "#     -- python bench.py --mode prologue --steps 20 --no-cpu",
              "# then python gated_delta_amd/profile_summary.py OUTDIR"])
 
+    if os.path.isdir(os.path.join(out, "prof_trace_dp")):
+        kernel_table(
+            os.path.join(out, "prof_trace_dp"),
+            os.path.join(prof, "kernels_rda_decode_step_prologue_B256_H16.txt"),
+            ["# rocprofv3 kernel trace, the decode step with the prologue in front:",
+             "# rda_decode_step_prologue on B=256 sequences x H=16 heads (bf16 raw q, k, v;",
+             "# conv width 4, SiLU, the history updated in place; fp32 states in place),",
+             "# then rda_decode_step on the same states; 11 calls of each, each after a",
+             "# 512 MiB read (reduce_kernel: the cache flush)",
+             "# command: gated_delta_amd/profile_run.sh OUTDIR, whose pass for it is",
+             "#   rocprofv3 --kernel-trace --stats --output-format csv -d OUTDIR/prof_trace_dp -o trace \\",
+             "#     -- python bench.py --mode decode_prologue --steps 10 --no-cpu",
+             "# then python gated_delta_amd/profile_summary.py OUTDIR"])
+
     if os.path.isdir(os.path.join(out, "prof_trace_diag")):
         kernel_table(
             os.path.join(out, "prof_trace_diag"),
             os.path.join(prof, "kernels_rda_prefill_diag_T16384_H16.txt"),
             ["# rocprofv3 kernel trace, the per-channel-decay prefill: rda_prefill_diag on the",
              "# long prompt, 16384 tokens x 16 heads (bf16 q/k/v, a decay per key channel,",
-             "# S0 ~ N(0, 0.02)): chunk table, prep_diag, walk_diag; 10 calls, each after a",
-             "# 512 MiB read (reduce_kernel: the cache flush)",
+             "# S0 ~ N(0, 0.02)), the overlapped plan in chunk ranges: chunk table, prep_diag",
+             "# (the first range), walk_diag once per range (each launch also preps the next",
+             "# range on the CUs the walk leaves idle); 11 calls, each after a 512 MiB read",
+             "# (reduce_kernel: the cache flush); us_per_call sums a call's launches",
              "# command: gated_delta_amd/profile_run.sh OUTDIR, whose fifth pass is",
              "#   rocprofv3 --kernel-trace --stats --output-format csv -d OUTDIR/prof_trace_diag -o trace \\",
              "#     -- python bench.py --mode prefill_diag --steps 10 --no-cpu",
@@ -254,6 +273,7 @@ def main():
     # their own (only their own kernel: the flush and restores are not theirs)
     for mode, kern in (("decode_tokens", "decode_tokens_kernel"),
                        ("output_norm_gate", "norm_gate_kernel"), ("prologue", "prologue_kernel"),
+                       ("decode_prologue", "decode_prologue_kernel"),
                        ("prefill_diag", "prep_diag_kernel"), ("prefill_diag", "walk_diag_kernel")):
         fd = os.path.join(out, f"prof_FETCH_SIZE_{mode}")
         wd = os.path.join(out, f"prof_WRITE_SIZE_{mode}")
@@ -261,10 +281,17 @@ def main():
             fm, wm = counter(fd, "FETCH_SIZE"), counter(wd, "WRITE_SIZE")
             if kern in fm and kern in wm:
                 fetch[kern], write[kern] = fm[kern], wm[kern]
+            # a prefill mode: also per call (the per-channel walk runs once per
+            # chunk range of the overlapped plan)
+            fcm, pcm = counter_per_call(fd, "FETCH_SIZE")
+            wcm, _ = counter_per_call(wd, "WRITE_SIZE")
+            if kern in fcm and kern in wcm:
+                fetch_call[kern], write_call[kern], per_call[kern] = fcm[kern], wcm[kern], pcm[kern]
     lines = ["# HBM bytes per launch of the prefill kernels, RDA prefill T=16384 H=16 d=128",
              "# (bf16 q/k/v), of the one-pass multi-token decode (B=256 T=3 H=16), of the",
              "# output norm and gate (262144 rows), of the prologue (T=16384 H=16, conv",
-             "# width 4) and of the per-channel-decay prefill's two kernels (T=16384 H=16).",
+             "# width 4), of the decode step with the prologue in front (B=256 H=16) and of",
+             "# the per-channel-decay prefill's two kernels (T=16384 H=16).",
              "# FETCH_SIZE and WRITE_SIZE (KiB per",
              "# dispatch) from one rocprofv3 --pmc pass each, scaled by what the same counter",
              "# reads for a plain device copy of 1 GiB (bench.py --mode copy):",
@@ -272,7 +299,8 @@ def main():
              f" copy WRITE_SIZE = {w_copy[wk]:.0f} KiB -> scale {w_scale:.3f}",
              "# command: gated_delta_amd/profile_run.sh OUTDIR (passes",
              "#   rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE --output-format csv -d OUTDIR/prof_<ctr>_<mode> -o pmc \\",
-             "#     -- python bench.py --mode prefill|copy|decode_tokens|output_norm_gate|prologue|prefill_diag \\",
+             "#     -- python bench.py --mode prefill|copy|decode_tokens|output_norm_gate|prologue|\\",
+             "#        decode_prologue|prefill_diag \\",
              "#        --steps 2 --warmup 1 --no-cpu)",
              "# then python gated_delta_amd/profile_summary.py OUTDIR",
              f"source_hash = {source_hash()}",
