@@ -363,8 +363,8 @@ def main():
         # plus S0 and S_final); the prep's figure is the inputs it reads
         # itself (q, k, a, b).  Times are per call: in the plan that preps
         # the later chunks beside the walk, the prep stage is the prep of the
-        # first chunks and the walk stage both walk launches (the first of
-        # which also preps the rest on the CUs the walk leaves idle).
+        # first chunks and the walk stage the walk launches (the first also
+        # preps the rest on the CUs the walk leaves idle).
         kb = {0: 0.0, 1: (2 * D * 2 + 2 * 4) * units,
               2: PREFILL_BYTES * units + 2 * H * STATE_BYTES}
         for s in range(rda.RDA_NUM_STAGES):

@@ -276,7 +276,7 @@ rda_status check_prefill(const void* q, const void* k, const void* v, rda_dtype 
 // The overlapped plan (see overlap_plan), all on `stream`.  Stage events
 // (when `ev` is given): the table stage is empty (the prep writes the
 // table), the prep stage is the first launch, and the walk stage spans the
-// two walk launches (the first of which also preps the later chunks).
+// walk launches (all but the last also prep later chunks).
 rda_status prefill_overlapped(const Prefill& P, hipStream_t stream, hipEvent_t const* ev) {
     const auto* q16 = static_cast<const uint16_t*>(P.q);
     const auto* k16 = static_cast<const uint16_t*>(P.k);

@@ -164,7 +164,7 @@ rda_status rda_prefill(const void* q, const void* k, const void* v, rda_dtype qk
  * `stream` (NULL entries are skipped).  The kernels are those rda_prefill
  * runs: in the plan that preps later chunks beside the walk, the table
  * stage is empty, the prep stage is the prep of the first chunks and the
- * walk stage spans both walk launches.  Results are identical to
+ * walk stage spans the walk launches.  Results are identical to
  * rda_prefill.
  */
 rda_status rda_prefill_profiled(const void* q, const void* k, const void* v, rda_dtype qkv_dtype,
