@@ -26,7 +26,8 @@
 // replaces the raw tokens before it; a block whose tokens and windows all
 // lie inside one sequence, away from the last K-1 tokens of a sequence whose
 // history is kept, takes a plain path without those per-token lookups and
-// branches (16384 x 16: 96 us against 103).  The q and k norms are 16-lane DPP
+// branches, and its per-token gates are computed once per token by one lane
+// each (16384 x 16: 83 us against 103).  The q and k norms are 16-lane DPP
 // reductions.  The arithmetic (about 160 VALU instructions per token and
 // lane, a third of them the SiLU's exp and reciprocal) is of the same order
 // as the memory time, and the two overlap only in part.  Measured and not
@@ -142,6 +143,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void p
         const bool plain = t_first - (K - 1) >= s0.s && t_last < s0.e &&
                            (!P.hout || K == 1 || t_last < s0.e - (K - 1));
         if (plain) {
+            // the per-token gates, lane c of each group taking token c of
+            // the block (the same arithmetic as the token loop's, once per
+            // token instead of once per token and lane): a and b by the q
+            // workgroups, the write gate by the v workgroups, handed to the
+            // group's lanes per token
+            const bool gl = c < kTT && t_first + c <= t_last;
+            const int32_t tg = gl ? t_first + c : t_last;   // a token of the block either way
+            const size_t thg = size_t(tg) * P.H + h;
+            float vgate = 0.f;
+            if (x == 0 && gl) {
+                P.b[thg] = erase_gate(P.beta[thg]);
+                P.a[thg] = floored_decay(P.glog[thg], P.floor_log);
+            }
+            if (x == 2) vgate = write_gate(P.beta[thg], P.delta ? P.delta[thg] : 0.f);
 #pragma unroll
             for (int j = 0; j < kTT; ++j) {
                 const int32_t t = t_first + j;
@@ -157,23 +172,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void p
                 }
                 conv_activation<kAct>(acc);
                 const size_t th = size_t(t) * P.H + h;
-                float scale;
-                if (x < 2) {
-                    scale = l2_scale(acc, P.l2eps);
-                } else {
-                    const float br = P.beta[th];
-                    const float dl = P.delta ? P.delta[th] : 0.f;
-                    scale = write_gate(br, dl);
-                }
+                const float scale = x < 2 ? l2_scale(acc, P.l2eps)
+                                          : __shfl(vgate, (lane & ~15) + j, 64);
                 uint16_t* ob = P.out[x] + th * kD;
                 *reinterpret_cast<u32x2*>(ob + ch0) = u32x2{pack_bf16(acc[0] * scale, acc[1] * scale),
                                                             pack_bf16(acc[2] * scale, acc[3] * scale)};
                 *reinterpret_cast<u32x2*>(ob + ch1) = u32x2{pack_bf16(acc[4] * scale, acc[5] * scale),
                                                             pack_bf16(acc[6] * scale, acc[7] * scale)};
-                if (x == 0 && c == 0) {
-                    P.b[th] = erase_gate(P.beta[th]);
-                    P.a[th] = floored_decay(P.glog[th], P.floor_log);
-                }
             }
             return;
         }
