@@ -143,13 +143,15 @@ def test_decay_regimes(dev, kind):
 
 
 @pytest.mark.parametrize("T,H,bf16", [(2048, 16, True), (4097, 8, True), (3000, 12, True),
-                                      (2100, 16, False)])
+                                      (2100, 16, False), (2048, 20, True)])
 def test_overlapped_plan_matches_one_pass(dev, T, H, bf16):
     """One sequence without offsets whose walk leaves CUs idle runs the
     overlapped plan in chunk ranges (the prep of the first range, then the
     walk of each range beside the prep of the next on the idle CUs, the
     state handed on between walk launches; 2048 tokens make 3 ranges, 4097
-    make 5); with cu_seqlens = {0, T} the same sizes run prep then one walk.
+    make 5; with 20 heads the ranges could not grow by 5/4, so two ranges,
+    the first launch prepping all the rest); with cu_seqlens = {0, T} the
+    same sizes run prep then one walk.
     Both give the same bits, and the plan meets the oracle."""
     import dataclasses
     p = synth.make_prefill(T, H, bf16=bf16, s0_std=0.02, key=(613, T, H))
