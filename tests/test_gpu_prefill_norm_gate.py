@@ -113,6 +113,9 @@ CASES = {
     # the norm of rows already walked beside it
     "overlapped, cut 4100x16": (lambda: synth.make_prefill(4100, 16, bf16=True, s0_std=0.02,
                                                            key=(612,)), "sigmoid", True, True),
+    # 8 heads: a short first range (8 chunks) and a cut last range
+    "overlapped 3000x8": (lambda: synth.make_prefill(3000, 8, bf16=True, s0_std=0.02,
+                                                     key=(613,)), "silu", True, True),
     # outputs far outside fp16's range, and far below its normal range: each
     # slice's power-of-two scale must bring them into (-1, 1) either way
     "values x 2^20": (lambda: scaled(synth.make_prefill(300, 2, bf16=True, key=(608,)), 2.0 ** 20),
