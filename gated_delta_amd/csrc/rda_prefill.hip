@@ -47,6 +47,8 @@
 //   block m of 32:  lane group g holds k = 32m + 4g + i and 32m + 16 + 4g + i
 // which is exactly the union of D-layout rows of tiles 2m and 2m + 1: an
 // accumulator tile pair is then a ready B operand with no data movement.
+#include <type_traits>
+
 #include "rda_device.h"
 #include "rda_internal.h"
 #include "rda_lds.h"
@@ -82,30 +84,46 @@ struct PrepIn<false> { using T = uint16_t; };
 template <>
 struct PrepIn<true> { using T = float; };
 
-// Stage one [64 x 128] token tile of head h into LDS as bf16 (hi, and lo for
-// fp32 inputs).  Rows >= len are zero.
+// One [64 x 128] token tile of head h as this thread's share of loads (8
+// bf16 or 4 fp32 elements per load), every load issued before any is used:
+// rows past the chunk's end read its last row and are zeroed when stored.
 template <bool kSplit>
-__device__ __forceinline__ void stage_tile(const typename PrepIn<kSplit>::T* __restrict__ src,
-                                           int64_t t0, int len, int H, int h, uint16_t* hi,
+struct TileLoads {
+    using V = typename std::conditional<kSplit, f32x4, u16x8>::type;
+    static constexpr int kN = kSplit ? 8 : 4;   // loads per thread
+    V x[kN];
+};
+
+template <bool kSplit>
+__device__ __forceinline__ void load_tile(const typename PrepIn<kSplit>::T* __restrict__ src,
+                                          int64_t t0, int len, int H, int h, int tid,
+                                          TileLoads<kSplit>& L) {
+#pragma unroll
+    for (int qq = 0; qq < TileLoads<kSplit>::kN; ++qq) {
+        const int p = tid + 256 * qq;
+        const int r = kSplit ? p >> 5 : p >> 4;
+        const int col = kSplit ? (p & 31) * 4 : (p & 15) * 8;
+        const int rr = r < len ? r : len - 1;
+        L.x[qq] = *reinterpret_cast<const typename TileLoads<kSplit>::V*>(
+            src + ((t0 + rr) * H + h) * kD + col);
+    }
+}
+
+// Store a loaded tile into LDS as bf16 (hi, and lo for fp32 inputs); rows
+// >= len are zero.
+template <bool kSplit>
+__device__ __forceinline__ void store_tile(const TileLoads<kSplit>& L, int len, uint16_t* hi,
                                            uint16_t* lo, int tid) {
-    if constexpr (!kSplit) {
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-            const int p = tid + 256 * qq;
+    for (int qq = 0; qq < TileLoads<kSplit>::kN; ++qq) {
+        const int p = tid + 256 * qq;
+        if constexpr (!kSplit) {
             const int r = p >> 4, c8 = (p & 15) * 8;
-            u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (r < len)
-                x = *reinterpret_cast<const u16x8*>(src + ((t0 + r) * H + h) * kD + c8);
-            *reinterpret_cast<u16x8*>(hi + r * kTS + c8) = x;
-        }
-    } else {
-#pragma unroll
-        for (int qq = 0; qq < 8; ++qq) {
-            const int p = tid + 256 * qq;
+            const u16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
+            *reinterpret_cast<u16x8*>(hi + r * kTS + c8) = r < len ? L.x[qq] : zero;
+        } else {
             const int r = p >> 5, c4 = (p & 31) * 4;
-            f32x4 x = zero4();
-            if (r < len)
-                x = *reinterpret_cast<const f32x4*>(src + ((t0 + r) * H + h) * kD + c4);
+            const f32x4 x = r < len ? L.x[qq] : zero4();
             u16x4 xh, xl;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -164,8 +182,13 @@ __global__ __launch_bounds__(256) void prep_kernel(
     unsigned char* F = factors + (size_t(chunk) * H + h) * kChunkHeadBytes;
 
     // ---- stage inputs; zero T and A (their upper triangles stay zero) ------
-    stage_tile<kSplit>(k, t0, len, H, h, Ks, Kl, tid);
-    stage_tile<kSplit>(q, t0, len, H, h, Qs, Ql, tid);
+    {
+        TileLoads<kSplit> lk, lq;
+        load_tile<kSplit>(k, t0, len, H, h, tid, lk);
+        load_tile<kSplit>(q, t0, len, H, h, tid, lq);
+        store_tile<kSplit>(lk, len, Ks, Kl, tid);
+        store_tile<kSplit>(lq, len, Qs, Ql, tid);
+    }
     for (int e = tid; e < kC * kFS; e += 256) {
         Ts[e] = 0.f;
         As[e] = 0.f;
@@ -192,39 +215,69 @@ __global__ __launch_bounds__(256) void prep_kernel(
     }
     __syncthreads();
 
-    // ---- Gram tiles: L = strict-lower(diag(b) K K^T . Gamma), A = lower(Q K^T . Gamma)
+    // ---- Gram tiles: L = strict-lower(diag(b) K K^T . Gamma), A = lower(Q K^T . Gamma).
+    //      Wave w: the L tiles (t, w) for t >= w and the transposed A tiles
+    //      (t, w) for t <= w, i.e. A's row tile w, with its own K and Q rows
+    //      read once and K rows 16t.. for each t (fp32 inputs: hi*hi + hi*lo +
+    //      lo*hi).  A transposed tile leaves each lane 4 consecutive entries
+    //      of one row of A.
     {
-        for (int task = w; task < 20; task += 4) {
-            // lower-triangular tile (ti, tj), ti >= tj, enumerated row by row
-            const bool isq = task >= 10;
-            const int idx = isq ? task - 10 : task;
-            const int ti = (idx >= 1) + (idx >= 3) + (idx >= 6);
-            const int tj = idx - ti * (ti + 1) / 2;
-            const uint16_t* X = isq ? Qs : Ks;
-            const uint16_t* Xl = isq ? Ql : Kl;
-            f32x4 acc = zero4();
+        auto rowop = [&](const uint16_t* X, int r, int m) {
+            return *reinterpret_cast<const bf16x8*>(X + r * kTS + 32 * m + 8 * g);
+        };
+        bf16x8 kwh[4], kwl[4], qwh[4], qwl[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            kwh[m] = rowop(Ks, 16 * w + c, m);
+            qwh[m] = rowop(Qs, 16 * w + c, m);
+            if constexpr (kSplit) {
+                kwl[m] = rowop(Kl, 16 * w + c, m);
+                qwl[m] = rowop(Ql, 16 * w + c, m);
+            }
+        }
+        const int s = 16 * w + c;   // key token of the L tiles, query token of the A tiles
+        const float gs = gg[s];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            bf16x8 kth[4], ktl[4];
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const int kk = 32 * m + 8 * g;
-                const bf16x8 ah = *reinterpret_cast<const bf16x8*>(X + (16 * ti + c) * kTS + kk);
-                const bf16x8 bh = *reinterpret_cast<const bf16x8*>(Ks + (16 * tj + c) * kTS + kk);
-                acc = mfma_bf16(ah, bh, acc);
-                if constexpr (kSplit) {
-                    const bf16x8 al = *reinterpret_cast<const bf16x8*>(Xl + (16 * ti + c) * kTS + kk);
-                    const bf16x8 bl = *reinterpret_cast<const bf16x8*>(Kl + (16 * tj + c) * kTS + kk);
-                    acc = mfma_bf16(ah, bl, acc);
-                    acc = mfma_bf16(al, bh, acc);
+                kth[m] = rowop(Ks, 16 * t + c, m);
+                if constexpr (kSplit) ktl[m] = rowop(Kl, 16 * t + c, m);
+            }
+            if (t >= w) {   // L tile (t, w): rows 16t + 4g + e, column s
+                f32x4 d = zero4();
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    d = mfma_bf16(kth[m], kwh[m], d);
+                    if constexpr (kSplit) {
+                        d = mfma_bf16(kth[m], kwl[m], d);
+                        d = mfma_bf16(ktl[m], kwh[m], d);
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * t + 4 * g + e;
+                    Ls[r * kFS + s] = r > s ? bb[r] * d[e] * __expf(gg[r] - gs) : 0.f;
                 }
             }
-            const int s_ = 16 * tj + c;
+            if (t <= w) {   // transposed A tile (t, w): A[s][16t + 4g + e]
+                f32x4 d = zero4();
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * ti + 4 * g + i;
-                if (isq) {
-                    As[r * kFS + s_] = r >= s_ ? acc[i] * expf(gg[r] - gg[s_]) : 0.f;
-                } else {
-                    Ls[r * kFS + s_] = r > s_ ? bb[r] * acc[i] * expf(gg[r] - gg[s_]) : 0.f;
+                for (int m = 0; m < 4; ++m) {
+                    d = mfma_bf16(kth[m], qwh[m], d);
+                    if constexpr (kSplit) {
+                        d = mfma_bf16(kth[m], qwl[m], d);
+                        d = mfma_bf16(ktl[m], qwh[m], d);
+                    }
                 }
+                f32x4 out;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 16 * t + 4 * g + e;
+                    out[e] = j <= s ? d[e] * __expf(gs - gg[j]) : 0.f;
+                }
+                *reinterpret_cast<f32x4*>(As + s * kFS + 16 * t + 4 * g) = out;
             }
         }
     }
